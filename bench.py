@@ -1,0 +1,168 @@
+"""Decode throughput of a stack of quantised MoE layers on one MI355X.
+
+One step = one token through the whole stack (router, top-k, packed gate|up dequant-GEMV with
+SwiGLU, down dequant-GEMV, weighted combine with the shared expert, for every layer, the layers
+chained by the RMS glue), i.e. one moe_stack_decode call. The default workload is the
+Qwen3.6-35B-A3B-shaped 4-bit stack: 40 layers, H 2048, 256 experts, top-8, I 512, shared
+expert 512, group-64 bf16 scale/bias, seeded synthetic weights resident in HBM; each step gets a
+fresh seeded input so routing changes every step.
+
+Prints one JSON line with the throughput, the HBM roofline of the decode kernel (algorithmic
+bytes per launch / measured launch time) and the fp64 CPU oracle timed on a bounded sample.
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer decode tokens/s and achieved HBM GB/s (% of peak), 4-bit 35B shape"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "quantized_moe_decode_router_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """Per-launch HBM bytes from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(stack, wl, budget_s: float):
+    """The oracle as it stands, on this host's cores, on a bounded sample: the first
+    `n` layers of the same stack, tokens chained through them until ~budget_s has elapsed."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from tests.helpers import host_layer
+
+    n = min(8, wl.n_layers)
+    layers = [host_layer(stack, l) for l in range(n)]
+    threads = oracle.num_threads()
+    import synth
+    layer_tokens = 0
+    tokens = 0
+    t0 = time.perf_counter()
+    while True:
+        xb = synth.make_x(wl.shape, 1, wl.seed, step=10_000 + tokens).view(torch.int16).numpy().view(np.uint16)
+        for L in layers:
+            out = oracle.layer_forward(L, xb)
+            xb = oracle.rms_glue(out["y"][0], 1e-6)[None, :]
+            layer_tokens += 1
+        tokens += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s and tokens >= 2:
+            break
+    per_layer_token = el / layer_tokens
+    return {"value": 1.0 / (per_layer_token * wl.n_layers), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{tokens} tokens x first {n} of {wl.n_layers} layers (T=1, chained by the glue), "
+                      f"{el:.1f} s; tokens/s = 1 / (time per layer-token x {wl.n_layers} layers)"}
+
+
+def main():
+    import synth
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=synth.QWEN35B_4BIT.name,
+                    choices=[w.name for w in synth.ALL.values() if w.tokens <= 8 and w.n_layers > 1])
+    ap.add_argument("--phased", action="store_true", help="one launch per phase instead of the persistent kernel")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the MoE decode path here is single-GPU (no sharding or "
+              "collectives are built); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_moe_decode_router_amd as moe
+
+    dev = torch.device("cuda:0")
+    wl = synth.ALL[args.workload]
+    shape, T, L = wl.shape, wl.tokens, wl.n_layers
+    t0 = time.perf_counter()
+    stack = synth.make_workload(wl, dev)
+    torch.cuda.synchronize()
+    print(f"[bench] {wl.describe()}: {stack.nbytes() / 1e9:.2f} GB generated in "
+          f"{time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    nsteps = args.warmup + args.steps
+    xs = torch.stack([synth.make_x(shape, T, wl.seed, step=s, device=dev) for s in range(nsteps)])
+    y = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
+    ws = moe.workspace(shape, T, moe.MOE_WS_STACK, dev)
+    fn = moe.moe_stack_decode_phased if args.phased else moe.moe_stack_decode
+    stream = torch.cuda.current_stream()
+
+    def step(s):
+        fn(shape, stack, L, xs[s], T, y, workspace=ws, stream=stream)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    assert moe.moe_read_status(ws) == 0
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.warmup, nsteps):
+        step(s)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    status = moe.moe_read_status(ws)
+    if status != 0:
+        raise SystemExit(f"device status {moe.status_string(status)} after the timed steps")
+    ev_ms = start.elapsed_time(end)
+    ms_per_step = ev_ms / args.steps
+    tokens_per_s = args.steps * T / (ev_ms / 1e3)
+
+    bytes_per_launch = L * synth.algorithmic_decode_bytes(shape) * T
+    achieved = bytes_per_launch / (ms_per_step / 1e3) / 1e9
+    kernel = "decode_phase" if args.phased else "decode_persistent"
+    traffic = recorded_traffic(wl.name, kernel)
+    result = {
+        "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded counter-based weights and inputs; no checkpoints)",
+        "config": {"workload": wl.name, "layers": L, "tokens_per_step": T, "hidden": shape.hidden,
+                   "experts": shape.num_experts, "top_k": shape.top_k, "inter": shape.inter,
+                   "shared_inter": shape.shared_inter, "bits": shape.bits, "group": shape.group_size,
+                   "stack_gb": round(stack.nbytes() / 1e9, 2), "kernel": kernel},
+        "hbm_gbps": round(achieved, 1), "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "wall_s": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": bytes_per_launch,
+                     "avg_launch_us": round(ms_per_step * 1e3, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(stack, wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

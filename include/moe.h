@@ -1,0 +1,183 @@
+/*
+ * moe.h -- C ABI of the quantised sparse Mixture-of-Experts FFN layer (MI355X / gfx950).
+ *
+ * The layer (per token, x a bf16 row of H values):
+ *   logits  l[e] = x . R[e] (+ bias[e])                      router, fp32 weights [E][H]
+ *   select  S    = the top_k experts by logit, ties to the lower index, ordered by
+ *                  (logit descending, index ascending)
+ *   weights w_k  = softmax(l)[S_k] / sum_{j in S} softmax(l)[j]   (renormalised top-k softmax)
+ *   expert  d_e  = W2_e ( silu(Wg_e x) * (Wu_e x) ),  gate|up packed as one matrix W13_e
+ *   shared  gamma = sigmoid(x . g_s),  d_s = the shared expert's MLP, same form
+ *   output  y    = sum_k w_k d_{S_k} + gamma d_s   (fp32)
+ * Sources on the pages: each token goes to 8 of 256 experts (35B-A3B) or 10 of 512
+ * (80B-A3B), beside an always-on shared expert (xix.ai Swiftlet article, paragraph on
+ * scheduling; Runnel README, "Target"); experts are MLX-style int4/int8 group-quantised with
+ * byte-addressable kernels and 64-bit offsets (xix.ai Swiftlet article, paragraph on lineage);
+ * routed gate and up are packed into one projection (Runnel README, intro and "Streaming CLI").
+ * The pages print no routing, SwiGLU or gate formula; the forms above are the plainest reading.
+ *
+ * Quantised matrices (moe_qweight), each [n_exp][rows][cols], row-major, expert-major with a
+ * fixed stride per expert (expert e at base + e * stride, 64-bit arithmetic):
+ *   codes  : uint8 [n_exp][rows][cols*bits/8]; 4-bit: input column 2j is the LOW nibble of
+ *            byte j; 8-bit: one code per byte
+ *   scales : bf16 bit patterns [n_exp][rows][cols/group_size]
+ *   biases : bf16 bit patterns, same shape; weight = scale * code + bias
+ *   W13 (routed gate|up): rows 2*inter (0..inter-1 gate, inter..2*inter-1 up), cols hidden
+ *   W2  (routed down)   : rows hidden, cols inter
+ *   S13 / S2 (shared)   : as W13 / W2 with n_exp = 1 and shared_inter in place of inter
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library allocates
+ *     nothing, keeps no state between calls and never synchronises the stream.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work is enqueued
+ *     asynchronously; results are valid once the stream reaches that point.
+ *   - Arguments are checked on the host before anything is enqueued; on a failed check the
+ *     call returns the error and writes nothing.
+ *   - Every pointer must be 16-byte aligned (4-byte for the small fp32 vectors router_bias,
+ *     shared_gate and all optional outputs).
+ *   - Supported: bits in {4, 8}; group_size 64; hidden, inter, shared_inter powers of two with
+ *     256 <= hidden <= 4096 and 64 <= inter, shared_inter <= 4096; 1 <= top_k <= 16,
+ *     top_k <= num_experts <= 1024. Other shapes return MOE_ERR_UNSUPPORTED.
+ *   - A workspace is device memory of at least moe_workspace_bytes() for the same arguments.
+ *     Its first 4 bytes are a device status word: 0 after a successful run, or a moe_status
+ *     a kernel set (MOE_ERR_TIMEOUT). moe_read_status() reads it.
+ *   - Two calls that share a workspace must not run concurrently.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* NULL required pointer, misaligned pointer, bad count or shape   */
+    MOE_ERR_UNSUPPORTED = 2, /* valid layer that this build has no kernel for (see above)     */
+    MOE_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than moe_workspace_bytes()          */
+    MOE_ERR_HIP = 4,         /* the HIP runtime refused a launch (hipGetLastError)            */
+    MOE_ERR_TIMEOUT = 5      /* device status only: a grid-wide wait exceeded its spin bound;
+                                outputs are undefined (never seen on a healthy device)        */
+} moe_status;
+
+typedef struct {
+    int32_t hidden;       /* H */
+    int32_t num_experts;  /* E */
+    int32_t top_k;        /* K */
+    int32_t inter;        /* I, routed expert intermediate size */
+    int32_t shared_inter; /* Is, shared expert intermediate size; 0 = no shared expert */
+    int32_t bits;         /* 4 or 8 */
+    int32_t group_size;   /* 64 */
+} moe_shape;
+
+typedef struct {
+    const uint8_t *codes;
+    const uint16_t *scales;
+    const uint16_t *biases;
+} moe_qweight;
+
+/* One layer. For moe_stack_decode the same struct describes a stack of L layers: every
+ * pointer is the base of an [L][...] array whose per-layer stride is the size above. */
+typedef struct {
+    const float *router;      /* [E][H] fp32                                             */
+    const float *router_bias; /* [E] fp32 added to the logits, or NULL                   */
+    const float *shared_gate; /* [H] fp32 (gamma = sigmoid(x . shared_gate)); required iff
+                                 shared_inter > 0                                          */
+    moe_qweight w13;          /* routed gate|up  */
+    moe_qweight w2;           /* routed down     */
+    moe_qweight s13;          /* shared gate|up  (ignored when shared_inter == 0) */
+    moe_qweight s2;           /* shared down     */
+} moe_layer;
+
+/* moe_route flags */
+#define MOE_ROUTE_LOGITS_IN 1u /* `logits` is an input [T][E]; the router GEMV is skipped and
+                                  layer->router may be NULL. Used to decide routing from given
+                                  logits (ties, +-0, duplicates) exactly as the layer does.    */
+
+/* Which call a workspace is sized for */
+#define MOE_WS_DECODE 0
+#define MOE_WS_BATCHED 1
+#define MOE_WS_STACK 2
+
+/*
+ * Router: logits, top-k selection and renormalised weights for T tokens (1 <= T <= 65536).
+ *   x       : bf16 [T][H] (unused with MOE_ROUTE_LOGITS_IN, may be NULL)
+ *   logits  : fp32 [T][E]; output, or input with MOE_ROUTE_LOGITS_IN; required
+ *   topk_idx: int32 [T][K] out; topk_w: fp32 [T][K] out; gamma: fp32 [T] out or NULL
+ *             (needs shared_inter > 0 and no MOE_ROUTE_LOGITS_IN)
+ * Needs no workspace.
+ */
+moe_status moe_route(const moe_shape *shape, const moe_layer *layer, const uint16_t *x, int32_t T,
+                     float *logits, int32_t *topk_idx, float *topk_w, float *gamma, uint32_t flags,
+                     void *stream);
+
+/*
+ * One layer at decode for 1 <= T <= 8 tokens: router, top-k, packed gate|up dequant-GEMV with
+ * SwiGLU, down dequant-GEMV and the fixed-order combine (k = 0..K-1, then the shared expert),
+ * as one persistent grid-synchronised kernel.
+ *   x : bf16 [T][H]   y : fp32 [T][H]
+ *   topk_idx_opt [T][K], topk_w_opt [T][K], logits_opt [T][E]: routing outputs or NULL
+ */
+moe_status moe_layer_decode(const moe_shape *shape, const moe_layer *layer, const uint16_t *x,
+                            int32_t T, float *y, int32_t *topk_idx_opt, float *topk_w_opt,
+                            float *logits_opt, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/*
+ * L chained layers at decode (1 <= T <= 8) in one launch. Layer 0 takes x; layer l+1 takes
+ *   x_{l+1} = bf16_rne( y_l / sqrt(mean(y_l^2) + 1e-6) )   per token
+ * (a weightless RMS normalisation standing in for the norm and mixer between the MoE layers of
+ * a model; it is not part of the MoE method). `stack` holds [L]-stacked arrays (see moe_layer).
+ *   y            : fp32 [T][H], output of the last layer
+ *   x_all_opt    : bf16 [L][T][H] inputs of every layer (x_all[0] = x), or NULL
+ *   y_all_opt    : fp32 [L][T][H], or NULL
+ *   topk_idx_all_opt [L][T][K], topk_w_all_opt [L][T][K], logits_all_opt [L][T][E], or NULL
+ */
+moe_status moe_stack_decode(const moe_shape *shape, const moe_layer *stack, int32_t n_layers,
+                            const uint16_t *x, int32_t T, float *y, uint16_t *x_all_opt,
+                            float *y_all_opt, int32_t *topk_idx_all_opt, float *topk_w_all_opt,
+                            float *logits_all_opt, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/*
+ * Same computation and arguments as moe_stack_decode, enqueued as three kernel launches per
+ * layer (one per phase) instead of one persistent launch with grid-wide barriers. Results are
+ * bit-identical; it exists to measure what the barriers cost against kernel boundaries.
+ */
+moe_status moe_stack_decode_phased(const moe_shape *shape, const moe_layer *stack,
+                                   int32_t n_layers, const uint16_t *x, int32_t T, float *y,
+                                   uint16_t *x_all_opt, float *y_all_opt,
+                                   int32_t *topk_idx_all_opt, float *topk_w_all_opt,
+                                   float *logits_all_opt, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/*
+ * One layer for a batch of 1 <= T <= 65536 tokens (prefill or batched decode): router, then a
+ * histogram / exclusive-scan / stable scatter that groups (token, slot) pairs by expert, an
+ * MFMA grouped GEMM for gate|up with SwiGLU, one for down scaled by the routing weight, the
+ * shared expert as one dense group, and a fixed-order un-permute combine.
+ * Arguments as moe_layer_decode.
+ */
+moe_status moe_layer_batched(const moe_shape *shape, const moe_layer *layer, const uint16_t *x,
+                             int32_t T, float *y, int32_t *topk_idx_opt, float *topk_w_opt,
+                             float *logits_opt, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* Workspace bytes for `kind` (MOE_WS_DECODE, MOE_WS_BATCHED or MOE_WS_STACK) and T tokens;
+ * 0 if the shape or T is invalid or unsupported. */
+size_t moe_workspace_bytes(const moe_shape *shape, int32_t T, int32_t kind);
+
+/* Synchronises `stream`, then copies the workspace's device status word into *status. */
+moe_status moe_read_status(const void *workspace, void *stream, int32_t *status);
+
+/* Static, human-readable name of a status code. */
+const char *moe_status_string(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

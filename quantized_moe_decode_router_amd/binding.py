@@ -1,0 +1,210 @@
+"""ctypes binding of libmoe_amd.so (include/moe.h): argument marshalling only.
+
+Every function has the C entry point's name and argument order, takes torch tensors for the
+pointer arguments, and raises MoeError on a non-OK status. All compute happens in the HIP
+library; torch only provides device memory and the current stream. Tensors must be contiguous
+and on the GPU: a host pointer handed to a kernel would fault the device, so that is checked
+here before the call.
+
+Layer arguments are duck-typed: any object with the attributes router, router_bias,
+shared_gate and {w13,w2,s13,s2}_{codes,scales,biases} (torch tensors or None). For the stack
+call the tensors carry a leading layer dimension and the base pointers describe layer 0.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libmoe_amd.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_TIMEOUT = range(6)
+MOE_ROUTE_LOGITS_IN = 1
+MOE_WS_DECODE, MOE_WS_BATCHED, MOE_WS_STACK = 0, 1, 2
+
+EXPORTED = ("moe_route", "moe_layer_decode", "moe_stack_decode", "moe_stack_decode_phased",
+            "moe_layer_batched", "moe_workspace_bytes", "moe_read_status", "moe_status_string")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("hidden", "num_experts", "top_k", "inter", "shared_inter", "bits", "group_size")]
+
+
+class MoeQWeight(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+
+
+class MoeLayer(ctypes.Structure):
+    _fields_ = [("router", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+                ("shared_gate", ctypes.c_void_p), ("w13", MoeQWeight), ("w2", MoeQWeight),
+                ("s13", MoeQWeight), ("s2", MoeQWeight)]
+
+
+_lib = None
+
+
+def lib():
+    """Load the built library; fails loudly if it is missing (there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run quantized_moe_decode_router_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, U32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+        PS, PL = ctypes.POINTER(MoeShape), ctypes.POINTER(MoeLayer)
+        L.moe_route.argtypes = [PS, PL, P, I32, P, P, P, P, U32, P]
+        L.moe_layer_decode.argtypes = [PS, PL, P, I32, P, P, P, P, P, SZ, P]
+        L.moe_layer_batched.argtypes = [PS, PL, P, I32, P, P, P, P, P, SZ, P]
+        for fn in (L.moe_stack_decode, L.moe_stack_decode_phased):
+            fn.argtypes = [PS, PL, I32, P, I32, P, P, P, P, P, P, P, SZ, P]
+        L.moe_workspace_bytes.argtypes = [PS, I32, I32]
+        L.moe_workspace_bytes.restype = SZ
+        L.moe_read_status.argtypes = [P, P, ctypes.POINTER(I32)]
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        for name in ("moe_route", "moe_layer_decode", "moe_layer_batched", "moe_stack_decode",
+                     "moe_stack_decode_phased", "moe_read_status"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor (the library takes device pointers)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def shape_struct(shape) -> MoeShape:
+    return MoeShape(shape.hidden, shape.num_experts, shape.top_k, shape.inter, shape.shared_inter,
+                    shape.bits, getattr(shape, "group_size", 64))
+
+
+_BF16_BITS = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def layer_struct(layer) -> MoeLayer:
+    def q(prefix):
+        c = getattr(layer, prefix + "_codes", None)
+        if c is None:
+            return MoeQWeight(None, None, None)
+        return MoeQWeight(_ptr(c, prefix + "_codes", torch.uint8),
+                          _ptr(getattr(layer, prefix + "_scales"), prefix + "_scales", _BF16_BITS),
+                          _ptr(getattr(layer, prefix + "_biases"), prefix + "_biases", _BF16_BITS))
+    return MoeLayer(_ptr(getattr(layer, "router", None), "router", torch.float32),
+                    _ptr(getattr(layer, "router_bias", None), "router_bias", torch.float32),
+                    _ptr(getattr(layer, "shared_gate", None), "shared_gate", torch.float32),
+                    q("w13"), q("w2"), q("s13"), q("s2"))
+
+
+# ---- entry points ----------------------------------------------------------------------------
+
+def moe_workspace_bytes(shape, T: int, kind: int) -> int:
+    s = shape_struct(shape)
+    return int(lib().moe_workspace_bytes(ctypes.byref(s), int(T), int(kind)))
+
+
+def moe_route(shape, layer, x, T: int, logits, topk_idx, topk_w, gamma=None, flags: int = 0,
+              stream=None) -> None:
+    s = shape_struct(shape)
+    L = layer_struct(layer) if layer is not None else None
+    st = lib().moe_route(ctypes.byref(s), ctypes.byref(L) if L is not None else None,
+                         _ptr(x, "x", _BF16_BITS), int(T), _ptr(logits, "logits", torch.float32),
+                         _ptr(topk_idx, "topk_idx", torch.int32), _ptr(topk_w, "topk_w", torch.float32),
+                         _ptr(gamma, "gamma", torch.float32), int(flags), _stream(stream))
+    _check(st, "moe_route")
+
+
+def moe_layer_decode(shape, layer, x, T: int, y, topk_idx=None, topk_w=None, logits=None,
+                     workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+    s, L = shape_struct(shape), layer_struct(layer)
+    wsb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    st = lib().moe_layer_decode(ctypes.byref(s), ctypes.byref(L), _ptr(x, "x", _BF16_BITS), int(T),
+                                _ptr(y, "y", torch.float32), _ptr(topk_idx, "topk_idx", torch.int32),
+                                _ptr(topk_w, "topk_w", torch.float32), _ptr(logits, "logits", torch.float32),
+                                _ptr(workspace, "workspace"), int(wsb), _stream(stream))
+    _check(st, "moe_layer_decode")
+
+
+def _stack_call(fn, name, shape, stack, n_layers, x, T, y, x_all, y_all, idx_all, w_all, logits_all,
+                workspace, workspace_bytes, stream):
+    s, L = shape_struct(shape), layer_struct(stack)
+    wsb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    st = fn(ctypes.byref(s), ctypes.byref(L), int(n_layers), _ptr(x, "x", _BF16_BITS), int(T),
+            _ptr(y, "y", torch.float32), _ptr(x_all, "x_all", _BF16_BITS),
+            _ptr(y_all, "y_all", torch.float32), _ptr(idx_all, "topk_idx_all", torch.int32),
+            _ptr(w_all, "topk_w_all", torch.float32), _ptr(logits_all, "logits_all", torch.float32),
+            _ptr(workspace, "workspace"), int(wsb), _stream(stream))
+    _check(st, name)
+
+
+def moe_stack_decode(shape, stack, n_layers: int, x, T: int, y, x_all=None, y_all=None, topk_idx_all=None,
+                     topk_w_all=None, logits_all=None, workspace=None, workspace_bytes=None, stream=None):
+    _stack_call(lib().moe_stack_decode, "moe_stack_decode", shape, stack, n_layers, x, T, y, x_all, y_all,
+                topk_idx_all, topk_w_all, logits_all, workspace, workspace_bytes, stream)
+
+
+def moe_stack_decode_phased(shape, stack, n_layers: int, x, T: int, y, x_all=None, y_all=None,
+                            topk_idx_all=None, topk_w_all=None, logits_all=None, workspace=None,
+                            workspace_bytes=None, stream=None):
+    _stack_call(lib().moe_stack_decode_phased, "moe_stack_decode_phased", shape, stack, n_layers, x, T, y,
+                x_all, y_all, topk_idx_all, topk_w_all, logits_all, workspace, workspace_bytes, stream)
+
+
+def moe_layer_batched(shape, layer, x, T: int, y, topk_idx=None, topk_w=None, logits=None,
+                      workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+    s, L = shape_struct(shape), layer_struct(layer)
+    wsb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    st = lib().moe_layer_batched(ctypes.byref(s), ctypes.byref(L), _ptr(x, "x", _BF16_BITS), int(T),
+                                 _ptr(y, "y", torch.float32), _ptr(topk_idx, "topk_idx", torch.int32),
+                                 _ptr(topk_w, "topk_w", torch.float32), _ptr(logits, "logits", torch.float32),
+                                 _ptr(workspace, "workspace"), int(wsb), _stream(stream))
+    _check(st, "moe_layer_batched")
+
+
+def moe_read_status(workspace, stream=None) -> int:
+    out = ctypes.c_int32(-1)
+    st = lib().moe_read_status(_ptr(workspace, "workspace"), _stream(stream), ctypes.byref(out))
+    _check(st, "moe_read_status")
+    return int(out.value)
+
+
+def workspace(shape, T: int, kind: int, device="cuda") -> torch.Tensor:
+    """Allocate (through torch) a workspace of moe_workspace_bytes() bytes."""
+    n = moe_workspace_bytes(shape, T, kind)
+    if n == 0:
+        raise MoeError(MOE_ERR_UNSUPPORTED, "moe_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)

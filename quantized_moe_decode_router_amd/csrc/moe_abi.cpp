@@ -1,0 +1,252 @@
+// moe_abi.cpp -- the extern "C" entry points of include/moe.h: host-side argument checks,
+// workspace carving and kernel dispatch. Nothing here allocates device memory or synchronises,
+// except moe_read_status, which exists to read the device status word.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "moe_internal.hpp"
+
+namespace {
+
+using moe::align_up;
+
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool al4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr size_t kCtrlBytes = 256;
+constexpr int kMaxDecodeT = 8;
+constexpr int kMaxBatchT = 65536;
+
+// Shape checks shared by every entry point.
+moe_status check_shape(const moe_shape *s) {
+    if (!s) return MOE_ERR_INVALID_ARG;
+    if (s->hidden <= 0 || s->num_experts <= 0 || s->top_k <= 0 || s->inter <= 0 ||
+        s->shared_inter < 0 || s->bits <= 0 || s->group_size <= 0)
+        return MOE_ERR_INVALID_ARG;
+    if (s->top_k > s->num_experts) return MOE_ERR_INVALID_ARG;
+    if (s->hidden % s->group_size || s->inter % s->group_size ||
+        (s->shared_inter && s->shared_inter % s->group_size))
+        return MOE_ERR_INVALID_ARG;
+    if (s->bits != 4 && s->bits != 8) return MOE_ERR_UNSUPPORTED;
+    if (s->group_size != 64) return MOE_ERR_UNSUPPORTED;
+    if (!pow2(s->hidden) || s->hidden < 256 || s->hidden > 4096) return MOE_ERR_UNSUPPORTED;
+    if (!pow2(s->inter) || s->inter < 64 || s->inter > 4096) return MOE_ERR_UNSUPPORTED;
+    if (s->shared_inter && (!pow2(s->shared_inter) || s->shared_inter < 64 || s->shared_inter > 4096))
+        return MOE_ERR_UNSUPPORTED;
+    if (s->top_k > 16 || s->num_experts > 1024) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status check_qweight(const moe_qweight &q) {
+    if (!q.codes || !q.scales || !q.biases) return MOE_ERR_INVALID_ARG;
+    if (!al16(q.codes) || !al16(q.scales) || !al16(q.biases)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+moe_status check_layer(const moe_shape *s, const moe_layer *L) {
+    if (!L || !L->router || !al16(L->router)) return MOE_ERR_INVALID_ARG;
+    if (L->router_bias && !al4(L->router_bias)) return MOE_ERR_INVALID_ARG;
+    moe_status st;
+    if ((st = check_qweight(L->w13)) != MOE_OK) return st;
+    if ((st = check_qweight(L->w2)) != MOE_OK) return st;
+    if (s->shared_inter) {
+        if (!L->shared_gate || !al16(L->shared_gate)) return MOE_ERR_INVALID_ARG;
+        if ((st = check_qweight(L->s13)) != MOE_OK) return st;
+        if ((st = check_qweight(L->s2)) != MOE_OK) return st;
+    }
+    return MOE_OK;
+}
+
+size_t decode_ws_bytes(const moe_shape *s, int T) {
+    const int Imax = s->inter > s->shared_inter ? s->inter : s->shared_inter;
+    size_t b = kCtrlBytes;
+    b += align_up(sizeof(float) * (size_t)T * (s->num_experts + 1), 256);
+    b += align_up(sizeof(float) * (size_t)T * (s->top_k + 1) * Imax, 256);
+    b += align_up(sizeof(float) * (size_t)T * s->hidden, 256);
+    return b;
+}
+
+int rows_per_wg(int H, int grid) { return (H + grid - 1) / grid; }
+
+moe_status decode_common(const moe_shape *s, const moe_layer *L, int32_t n_layers, const uint16_t *x,
+                         int32_t T, float *y, uint16_t *x_all, float *y_all, int32_t *idx_all,
+                         float *w_all, float *logits_all, void *ws, size_t ws_bytes, void *stream,
+                         int persistent) {
+    moe_status st = check_shape(s);
+    if (st != MOE_OK) return st;
+    if ((st = check_layer(s, L)) != MOE_OK) return st;
+    if (n_layers < 1 || T < 1 || T > kMaxDecodeT) return MOE_ERR_INVALID_ARG;
+    if (!x || !y || !al16(x) || !al16(y)) return MOE_ERR_INVALID_ARG;
+    if ((x_all && !al16(x_all)) || (y_all && !al16(y_all)) || (idx_all && !al4(idx_all)) ||
+        (w_all && !al4(w_all)) || (logits_all && !al4(logits_all)))
+        return MOE_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < decode_ws_bytes(s, T) || !al16(ws)) return MOE_ERR_WORKSPACE;
+    const int grid = moe::device_cu_count();
+    if (grid <= 0) return MOE_ERR_HIP;
+    const int RB = rows_per_wg(s->hidden, grid);
+    const moe::DecodeLds lds = moe::decode_lds_layout(T, s->hidden, s->num_experts, s->top_k, RB);
+    if (lds.total > 160 * 1024) return MOE_ERR_UNSUPPORTED;
+
+    const size_t H = s->hidden, E = s->num_experts, I = s->inter, Is = s->shared_inter;
+    const size_t bits = s->bits;
+    moe::DecodeParams p;
+    memset(&p, 0, sizeof p);
+    p.H = s->hidden; p.E = s->num_experts; p.K = s->top_k; p.I = s->inter; p.Is = s->shared_inter;
+    p.bits = s->bits; p.T = T; p.L = n_layers; p.glue = 1;
+    p.Imax = s->inter > s->shared_inter ? s->inter : s->shared_inter;
+    p.rows_per_wg = RB;
+    p.spin_limit = 1u << 22;
+    p.eps = 1e-6f;
+    p.router = L->router; p.rbias = L->router_bias; p.sgate = Is ? L->shared_gate : nullptr;
+    p.w13 = {L->w13.codes, L->w13.scales, L->w13.biases};
+    p.w2 = {L->w2.codes, L->w2.scales, L->w2.biases};
+    if (Is) {
+        p.s13 = {L->s13.codes, L->s13.scales, L->s13.biases};
+        p.s2 = {L->s2.codes, L->s2.scales, L->s2.biases};
+    }
+    p.ls_router = (long long)(E * H);
+    p.ls_rbias = (long long)E;
+    p.ls_sgate = (long long)H;
+    p.ls_w13c = (long long)(E * 2 * I * H * bits / 8);
+    p.ls_w13s = (long long)(E * 2 * I * H / 64);
+    p.ls_w2c = (long long)(E * H * I * bits / 8);
+    p.ls_w2s = (long long)(E * H * I / 64);
+    p.ls_s13c = (long long)(2 * Is * H * bits / 8);
+    p.ls_s13s = (long long)(2 * Is * H / 64);
+    p.ls_s2c = (long long)(H * Is * bits / 8);
+    p.ls_s2s = (long long)(H * Is / 64);
+    p.x_in = x; p.y_out = y;
+    p.x_all = x_all; p.y_all = y_all; p.idx_all = idx_all; p.w_all = w_all; p.logits_all = logits_all;
+    char *w = static_cast<char *>(ws);
+    p.ctrl = reinterpret_cast<int *>(w);
+    size_t o = kCtrlBytes;
+    p.logits = reinterpret_cast<float *>(w + o);
+    o += align_up(sizeof(float) * (size_t)T * (E + 1), 256);
+    p.hbuf = reinterpret_cast<float *>(w + o);
+    o += align_up(sizeof(float) * (size_t)T * (s->top_k + 1) * p.Imax, 256);
+    p.ybuf = reinterpret_cast<float *>(w + o);
+    hipError_t err = moe::launch_decode(p, grid, static_cast<hipStream_t>(stream), persistent);
+    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace
+
+namespace moe {
+
+int device_cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    if (dev >= 0 && dev < 64) cache[dev] = n;
+    return n;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+const char *moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        case MOE_ERR_TIMEOUT: return "MOE_ERR_TIMEOUT";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+size_t moe_workspace_bytes(const moe_shape *s, int32_t T, int32_t kind) {
+    if (check_shape(s) != MOE_OK || T < 1) return 0;
+    if (kind == MOE_WS_DECODE || kind == MOE_WS_STACK) {
+        if (T > kMaxDecodeT) return 0;
+        return decode_ws_bytes(s, T);
+    }
+    if (kind == MOE_WS_BATCHED) {
+        if (T > kMaxBatchT) return 0;
+        return decode_ws_bytes(s, 1);  // placeholder until the batched path lands
+    }
+    return 0;
+}
+
+moe_status moe_read_status(const void *ws, void *stream, int32_t *status) {
+    if (!ws || !status) return MOE_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (hipStreamSynchronize(st) != hipSuccess) return MOE_ERR_HIP;
+    if (hipMemcpy(status, ws, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+moe_status moe_route(const moe_shape *s, const moe_layer *L, const uint16_t *x, int32_t T,
+                     float *logits, int32_t *topk_idx, float *topk_w, float *gamma, uint32_t flags,
+                     void *stream) {
+    moe_status st = check_shape(s);
+    if (st != MOE_OK) return st;
+    if (flags & ~MOE_ROUTE_LOGITS_IN) return MOE_ERR_INVALID_ARG;
+    const bool lin = (flags & MOE_ROUTE_LOGITS_IN) != 0;
+    if (T < 1 || T > kMaxBatchT) return MOE_ERR_INVALID_ARG;
+    if (!logits || !topk_idx || !topk_w || !al4(logits) || !al4(topk_idx) || !al4(topk_w))
+        return MOE_ERR_INVALID_ARG;
+    if (gamma && (lin || !s->shared_inter || !al4(gamma))) return MOE_ERR_INVALID_ARG;
+    if (!lin) {
+        if (!L || !L->router || !al16(L->router) || !x || !al16(x)) return MOE_ERR_INVALID_ARG;
+        if (L->router_bias && !al4(L->router_bias)) return MOE_ERR_INVALID_ARG;
+        if (gamma && (!L->shared_gate || !al16(L->shared_gate))) return MOE_ERR_INVALID_ARG;
+    }
+    moe::RouteParams p;
+    memset(&p, 0, sizeof p);
+    p.H = s->hidden; p.E = s->num_experts; p.K = s->top_k; p.T = T;
+    p.logits_in = lin ? 1 : 0;
+    p.has_gate = gamma ? 1 : 0;
+    p.x = x;
+    if (!lin) {
+        p.router = L->router;
+        p.rbias = L->router_bias;
+        p.sgate = gamma ? L->shared_gate : nullptr;
+    }
+    p.logits = logits; p.idx = topk_idx; p.w = topk_w; p.gamma = gamma;
+    hipError_t err = moe::launch_route(p, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_layer_decode(const moe_shape *s, const moe_layer *L, const uint16_t *x, int32_t T,
+                            float *y, int32_t *topk_idx_opt, float *topk_w_opt, float *logits_opt,
+                            void *ws, size_t ws_bytes, void *stream) {
+    return decode_common(s, L, 1, x, T, y, nullptr, nullptr, topk_idx_opt, topk_w_opt, logits_opt,
+                         ws, ws_bytes, stream, 1);
+}
+
+moe_status moe_stack_decode(const moe_shape *s, const moe_layer *stack, int32_t n_layers,
+                            const uint16_t *x, int32_t T, float *y, uint16_t *x_all_opt,
+                            float *y_all_opt, int32_t *idx_all_opt, float *w_all_opt,
+                            float *logits_all_opt, void *ws, size_t ws_bytes, void *stream) {
+    return decode_common(s, stack, n_layers, x, T, y, x_all_opt, y_all_opt, idx_all_opt, w_all_opt,
+                         logits_all_opt, ws, ws_bytes, stream, 1);
+}
+
+moe_status moe_stack_decode_phased(const moe_shape *s, const moe_layer *stack, int32_t n_layers,
+                                   const uint16_t *x, int32_t T, float *y, uint16_t *x_all_opt,
+                                   float *y_all_opt, int32_t *idx_all_opt, float *w_all_opt,
+                                   float *logits_all_opt, void *ws, size_t ws_bytes, void *stream) {
+    return decode_common(s, stack, n_layers, x, T, y, x_all_opt, y_all_opt, idx_all_opt, w_all_opt,
+                         logits_all_opt, ws, ws_bytes, stream, 0);
+}
+
+moe_status moe_layer_batched(const moe_shape *s, const moe_layer *L, const uint16_t *x, int32_t T,
+                             float *y, int32_t *topk_idx_opt, float *topk_w_opt, float *logits_opt,
+                             void *ws, size_t ws_bytes, void *stream) {
+    (void)L; (void)x; (void)y; (void)topk_idx_opt; (void)topk_w_opt; (void)logits_opt;
+    (void)ws; (void)ws_bytes; (void)stream; (void)T;
+    moe_status st = check_shape(s);
+    if (st != MOE_OK) return st;
+    return MOE_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"
