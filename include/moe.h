@@ -38,10 +38,14 @@
  *   - Supported: bits in {4, 8}; group_size 64; hidden, inter, shared_inter powers of two with
  *     256 <= hidden <= 4096 and 64 <= inter, shared_inter <= 4096; 1 <= top_k <= 16,
  *     top_k <= num_experts <= 1024. Other shapes return MOE_ERR_UNSUPPORTED.
- *   - A workspace is device memory of at least moe_workspace_bytes() for the same arguments.
- *     Its first 4 bytes are a device status word: 0 after a successful run, or a moe_status
- *     a kernel set (MOE_ERR_TIMEOUT). moe_read_status() reads it.
+ *   - A workspace is device memory of at least moe_workspace_bytes() for the same arguments,
+ *     zero-filled before its first use; calls leave it ready for the next call. Its first 4
+ *     bytes are a sticky device status word: 0 after successful runs, or a moe_status a kernel
+ *     set (MOE_ERR_TIMEOUT). A decode kernel that finds it non-zero does nothing; zero-fill the
+ *     workspace again to recover. moe_read_status() reads it.
  *   - Two calls that share a workspace must not run concurrently.
+ *   - The decode calls additionally need hidden, inter, shared_inter <= 2048 and an LDS footprint
+ *     within 160 KiB (it grows with T); other shapes return MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -126,8 +130,13 @@ moe_status moe_layer_decode(const moe_shape *shape, const moe_layer *layer, cons
                             float *logits_opt, void *workspace, size_t workspace_bytes,
                             void *stream);
 
+/* moe_stack_decode flags */
+#define MOE_STACK_INDEPENDENT 1u /* every layer takes x (no chaining); used to check every layer of
+                                    a stack against a reference on identical inputs             */
+
 /*
- * L chained layers at decode (1 <= T <= 8) in one launch. Layer 0 takes x; layer l+1 takes
+ * L layers at decode (1 <= T <= 8, 1 <= L <= 4096) in one persistent launch. Layer 0 takes x;
+ * unless MOE_STACK_INDEPENDENT, layer l+1 takes
  *   x_{l+1} = bf16_rne( y_l / sqrt(mean(y_l^2) + 1e-6) )   per token
  * (a weightless RMS normalisation standing in for the norm and mixer between the MoE layers of
  * a model; it is not part of the MoE method). `stack` holds [L]-stacked arrays (see moe_layer).
@@ -137,22 +146,10 @@ moe_status moe_layer_decode(const moe_shape *shape, const moe_layer *layer, cons
  *   topk_idx_all_opt [L][T][K], topk_w_all_opt [L][T][K], logits_all_opt [L][T][E], or NULL
  */
 moe_status moe_stack_decode(const moe_shape *shape, const moe_layer *stack, int32_t n_layers,
-                            const uint16_t *x, int32_t T, float *y, uint16_t *x_all_opt,
-                            float *y_all_opt, int32_t *topk_idx_all_opt, float *topk_w_all_opt,
-                            float *logits_all_opt, void *workspace, size_t workspace_bytes,
-                            void *stream);
-
-/*
- * Same computation and arguments as moe_stack_decode, enqueued as three kernel launches per
- * layer (one per phase) instead of one persistent launch with grid-wide barriers. Results are
- * bit-identical; it exists to measure what the barriers cost against kernel boundaries.
- */
-moe_status moe_stack_decode_phased(const moe_shape *shape, const moe_layer *stack,
-                                   int32_t n_layers, const uint16_t *x, int32_t T, float *y,
-                                   uint16_t *x_all_opt, float *y_all_opt,
-                                   int32_t *topk_idx_all_opt, float *topk_w_all_opt,
-                                   float *logits_all_opt, void *workspace,
-                                   size_t workspace_bytes, void *stream);
+                            uint32_t flags, const uint16_t *x, int32_t T, float *y,
+                            uint16_t *x_all_opt, float *y_all_opt, int32_t *topk_idx_all_opt,
+                            float *topk_w_all_opt, float *logits_all_opt, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /*
  * One layer for a batch of 1 <= T <= 65536 tokens (prefill or batched decode): router, then a
@@ -166,9 +163,9 @@ moe_status moe_layer_batched(const moe_shape *shape, const moe_layer *layer, con
                              float *logits_opt, void *workspace, size_t workspace_bytes,
                              void *stream);
 
-/* Workspace bytes for `kind` (MOE_WS_DECODE, MOE_WS_BATCHED or MOE_WS_STACK) and T tokens;
- * 0 if the shape or T is invalid or unsupported. */
-size_t moe_workspace_bytes(const moe_shape *shape, int32_t T, int32_t kind);
+/* Workspace bytes for `kind` (MOE_WS_DECODE, MOE_WS_BATCHED or MOE_WS_STACK), T tokens and, for
+ * MOE_WS_STACK, n_layers layers (ignored otherwise); 0 if the arguments are invalid. */
+size_t moe_workspace_bytes(const moe_shape *shape, int32_t T, int32_t n_layers, int32_t kind);
 
 /* Synchronises `stream`, then copies the workspace's device status word into *status. */
 moe_status moe_read_status(const void *workspace, void *stream, int32_t *status);

@@ -25,8 +25,10 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_ROUTE_LOGITS_IN = 1
 MOE_WS_DECODE, MOE_WS_BATCHED, MOE_WS_STACK = 0, 1, 2
 
-EXPORTED = ("moe_route", "moe_layer_decode", "moe_stack_decode", "moe_stack_decode_phased",
-            "moe_layer_batched", "moe_workspace_bytes", "moe_read_status", "moe_status_string")
+MOE_STACK_INDEPENDENT = 1
+
+EXPORTED = ("moe_route", "moe_layer_decode", "moe_stack_decode", "moe_layer_batched",
+            "moe_workspace_bytes", "moe_read_status", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -65,15 +67,14 @@ def lib():
         L.moe_route.argtypes = [PS, PL, P, I32, P, P, P, P, U32, P]
         L.moe_layer_decode.argtypes = [PS, PL, P, I32, P, P, P, P, P, SZ, P]
         L.moe_layer_batched.argtypes = [PS, PL, P, I32, P, P, P, P, P, SZ, P]
-        for fn in (L.moe_stack_decode, L.moe_stack_decode_phased):
-            fn.argtypes = [PS, PL, I32, P, I32, P, P, P, P, P, P, P, SZ, P]
-        L.moe_workspace_bytes.argtypes = [PS, I32, I32]
+        L.moe_stack_decode.argtypes = [PS, PL, I32, U32, P, I32, P, P, P, P, P, P, P, SZ, P]
+        L.moe_workspace_bytes.argtypes = [PS, I32, I32, I32]
         L.moe_workspace_bytes.restype = SZ
         L.moe_read_status.argtypes = [P, P, ctypes.POINTER(I32)]
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         for name in ("moe_route", "moe_layer_decode", "moe_layer_batched", "moe_stack_decode",
-                     "moe_stack_decode_phased", "moe_read_status"):
+                     "moe_read_status"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -132,9 +133,9 @@ def layer_struct(layer) -> MoeLayer:
 
 # ---- entry points ----------------------------------------------------------------------------
 
-def moe_workspace_bytes(shape, T: int, kind: int) -> int:
+def moe_workspace_bytes(shape, T: int, kind: int, n_layers: int = 1) -> int:
     s = shape_struct(shape)
-    return int(lib().moe_workspace_bytes(ctypes.byref(s), int(T), int(kind)))
+    return int(lib().moe_workspace_bytes(ctypes.byref(s), int(T), int(n_layers), int(kind)))
 
 
 def moe_route(shape, layer, x, T: int, logits, topk_idx, topk_w, gamma=None, flags: int = 0,
@@ -159,29 +160,19 @@ def moe_layer_decode(shape, layer, x, T: int, y, topk_idx=None, topk_w=None, log
     _check(st, "moe_layer_decode")
 
 
-def _stack_call(fn, name, shape, stack, n_layers, x, T, y, x_all, y_all, idx_all, w_all, logits_all,
-                workspace, workspace_bytes, stream):
+def moe_stack_decode(shape, stack, n_layers: int, x, T: int, y, x_all=None, y_all=None, topk_idx_all=None,
+                     topk_w_all=None, logits_all=None, workspace=None, workspace_bytes=None, stream=None,
+                     flags: int = 0) -> None:
     s, L = shape_struct(shape), layer_struct(stack)
     wsb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
-    st = fn(ctypes.byref(s), ctypes.byref(L), int(n_layers), _ptr(x, "x", _BF16_BITS), int(T),
-            _ptr(y, "y", torch.float32), _ptr(x_all, "x_all", _BF16_BITS),
-            _ptr(y_all, "y_all", torch.float32), _ptr(idx_all, "topk_idx_all", torch.int32),
-            _ptr(w_all, "topk_w_all", torch.float32), _ptr(logits_all, "logits_all", torch.float32),
-            _ptr(workspace, "workspace"), int(wsb), _stream(stream))
-    _check(st, name)
-
-
-def moe_stack_decode(shape, stack, n_layers: int, x, T: int, y, x_all=None, y_all=None, topk_idx_all=None,
-                     topk_w_all=None, logits_all=None, workspace=None, workspace_bytes=None, stream=None):
-    _stack_call(lib().moe_stack_decode, "moe_stack_decode", shape, stack, n_layers, x, T, y, x_all, y_all,
-                topk_idx_all, topk_w_all, logits_all, workspace, workspace_bytes, stream)
-
-
-def moe_stack_decode_phased(shape, stack, n_layers: int, x, T: int, y, x_all=None, y_all=None,
-                            topk_idx_all=None, topk_w_all=None, logits_all=None, workspace=None,
-                            workspace_bytes=None, stream=None):
-    _stack_call(lib().moe_stack_decode_phased, "moe_stack_decode_phased", shape, stack, n_layers, x, T, y,
-                x_all, y_all, topk_idx_all, topk_w_all, logits_all, workspace, workspace_bytes, stream)
+    st = lib().moe_stack_decode(ctypes.byref(s), ctypes.byref(L), int(n_layers), int(flags),
+                                _ptr(x, "x", _BF16_BITS), int(T), _ptr(y, "y", torch.float32),
+                                _ptr(x_all, "x_all", _BF16_BITS), _ptr(y_all, "y_all", torch.float32),
+                                _ptr(topk_idx_all, "topk_idx_all", torch.int32),
+                                _ptr(topk_w_all, "topk_w_all", torch.float32),
+                                _ptr(logits_all, "logits_all", torch.float32), _ptr(workspace, "workspace"),
+                                int(wsb), _stream(stream))
+    _check(st, "moe_stack_decode")
 
 
 def moe_layer_batched(shape, layer, x, T: int, y, topk_idx=None, topk_w=None, logits=None,
@@ -202,9 +193,9 @@ def moe_read_status(workspace, stream=None) -> int:
     return int(out.value)
 
 
-def workspace(shape, T: int, kind: int, device="cuda") -> torch.Tensor:
-    """Allocate (through torch) a workspace of moe_workspace_bytes() bytes."""
-    n = moe_workspace_bytes(shape, T, kind)
+def workspace(shape, T: int, kind: int, device="cuda", n_layers: int = 1) -> torch.Tensor:
+    """Allocate (through torch) a zero-filled workspace of moe_workspace_bytes() bytes."""
+    n = moe_workspace_bytes(shape, T, kind, n_layers)
     if n == 0:
         raise MoeError(MOE_ERR_UNSUPPORTED, "moe_workspace_bytes")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)

@@ -16,8 +16,8 @@ bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool al4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-constexpr size_t kCtrlBytes = 256;
 constexpr int kMaxDecodeT = 8;
+constexpr int kMaxLayers = 4096;
 constexpr int kMaxBatchT = 65536;
 
 // Shape checks shared by every entry point.
@@ -60,45 +60,51 @@ moe_status check_layer(const moe_shape *s, const moe_layer *L) {
     return MOE_OK;
 }
 
-size_t decode_ws_bytes(const moe_shape *s, int T) {
-    const int Imax = s->inter > s->shared_inter ? s->inter : s->shared_inter;
-    size_t b = kCtrlBytes;
-    b += align_up(sizeof(float) * (size_t)T * (s->num_experts + 1), 256);
-    b += align_up(sizeof(float) * (size_t)T * (s->top_k + 1) * Imax, 256);
-    b += align_up(sizeof(float) * (size_t)T * s->hidden, 256);
-    return b;
+size_t decode_ws_bytes(const moe_shape *s, int T, int L) {
+    return moe::decode_ws_layout(L, T, s->hidden, s->num_experts, s->top_k, s->inter, s->shared_inter).total;
 }
 
 int rows_per_wg(int H, int grid) { return (H + grid - 1) / grid; }
 
-moe_status decode_common(const moe_shape *s, const moe_layer *L, int32_t n_layers, const uint16_t *x,
-                         int32_t T, float *y, uint16_t *x_all, float *y_all, int32_t *idx_all,
-                         float *w_all, float *logits_all, void *ws, size_t ws_bytes, void *stream,
-                         int persistent) {
+// Shapes the decode kernel handles (beyond check_shape): rows of at most 64 slices of 32 columns,
+// router rows spread over at most 3 per workgroup, and LDS within the compute unit's 160 KiB.
+moe_status decode_supported(const moe_shape *s, int T, int grid) {
+    if (s->hidden > 2048 || s->inter > 2048 || s->shared_inter > 2048) return MOE_ERR_UNSUPPORTED;
+    if (s->num_experts + 1 > 3 * grid) return MOE_ERR_UNSUPPORTED;
+    const size_t lds = moe::decode_lds_bytes(T, s->hidden, s->num_experts, s->top_k, s->inter, s->shared_inter,
+                                             s->bits, rows_per_wg(s->hidden, grid));
+    if (lds > 160 * 1024) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status decode_common(const moe_shape *s, const moe_layer *L, int32_t n_layers, uint32_t flags,
+                         const uint16_t *x, int32_t T, float *y, uint16_t *x_all, float *y_all,
+                         int32_t *idx_all, float *w_all, float *logits_all, void *ws, size_t ws_bytes,
+                         void *stream) {
     moe_status st = check_shape(s);
     if (st != MOE_OK) return st;
     if ((st = check_layer(s, L)) != MOE_OK) return st;
-    if (n_layers < 1 || T < 1 || T > kMaxDecodeT) return MOE_ERR_INVALID_ARG;
+    if (flags & ~MOE_STACK_INDEPENDENT) return MOE_ERR_INVALID_ARG;
+    if (n_layers < 1 || n_layers > kMaxLayers || T < 1 || T > kMaxDecodeT) return MOE_ERR_INVALID_ARG;
     if (!x || !y || !al16(x) || !al16(y)) return MOE_ERR_INVALID_ARG;
     if ((x_all && !al16(x_all)) || (y_all && !al16(y_all)) || (idx_all && !al4(idx_all)) ||
         (w_all && !al4(w_all)) || (logits_all && !al4(logits_all)))
         return MOE_ERR_INVALID_ARG;
-    if (!ws || ws_bytes < decode_ws_bytes(s, T) || !al16(ws)) return MOE_ERR_WORKSPACE;
+    if (!ws || ws_bytes < decode_ws_bytes(s, T, n_layers) || !al16(ws)) return MOE_ERR_WORKSPACE;
     const int grid = moe::device_cu_count();
     if (grid <= 0) return MOE_ERR_HIP;
-    const int RB = rows_per_wg(s->hidden, grid);
-    const moe::DecodeLds lds = moe::decode_lds_layout(T, s->hidden, s->num_experts, s->top_k, RB);
-    if (lds.total > 160 * 1024) return MOE_ERR_UNSUPPORTED;
+    if (grid > moe::kMaxGrid) return MOE_ERR_UNSUPPORTED;
+    if ((st = decode_supported(s, T, grid)) != MOE_OK) return st;
 
     const size_t H = s->hidden, E = s->num_experts, I = s->inter, Is = s->shared_inter;
     const size_t bits = s->bits;
     moe::DecodeParams p;
     memset(&p, 0, sizeof p);
     p.H = s->hidden; p.E = s->num_experts; p.K = s->top_k; p.I = s->inter; p.Is = s->shared_inter;
-    p.bits = s->bits; p.T = T; p.L = n_layers; p.glue = 1;
-    p.Imax = s->inter > s->shared_inter ? s->inter : s->shared_inter;
-    p.rows_per_wg = RB;
-    p.spin_limit = 1u << 22;
+    p.bits = s->bits; p.T = T; p.L = n_layers;
+    p.chained = (flags & MOE_STACK_INDEPENDENT) ? 0 : 1;
+    p.rows_per_wg = rows_per_wg(s->hidden, grid);
+    p.spin_limit = 1u << 20;
     p.eps = 1e-6f;
     p.router = L->router; p.rbias = L->router_bias; p.sgate = Is ? L->shared_gate : nullptr;
     p.w13 = {L->w13.codes, L->w13.scales, L->w13.biases};
@@ -121,14 +127,15 @@ moe_status decode_common(const moe_shape *s, const moe_layer *L, int32_t n_layer
     p.x_in = x; p.y_out = y;
     p.x_all = x_all; p.y_all = y_all; p.idx_all = idx_all; p.w_all = w_all; p.logits_all = logits_all;
     char *w = static_cast<char *>(ws);
+    const moe::DecodeWs lay = moe::decode_ws_layout(n_layers, T, s->hidden, s->num_experts, s->top_k, s->inter,
+                                                    s->shared_inter);
     p.ctrl = reinterpret_cast<int *>(w);
-    size_t o = kCtrlBytes;
-    p.logits = reinterpret_cast<float *>(w + o);
-    o += align_up(sizeof(float) * (size_t)T * (E + 1), 256);
-    p.hbuf = reinterpret_cast<float *>(w + o);
-    o += align_up(sizeof(float) * (size_t)T * (s->top_k + 1) * p.Imax, 256);
-    p.ybuf = reinterpret_cast<float *>(w + o);
-    hipError_t err = moe::launch_decode(p, grid, static_cast<hipStream_t>(stream), persistent);
+    p.ll_start = reinterpret_cast<uint64_t *>(w + lay.start);
+    p.ll_logits = reinterpret_cast<uint64_t *>(w + lay.logits);
+    p.ll_h = reinterpret_cast<uint64_t *>(w + lay.h);
+    p.ll_hs = reinterpret_cast<uint64_t *>(w + lay.hs);
+    p.ll_y = reinterpret_cast<uint64_t *>(w + lay.y);
+    hipError_t err = moe::launch_decode(p, grid, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -163,15 +170,16 @@ const char *moe_status_string(moe_status s) {
     return "MOE_ERR_UNKNOWN";
 }
 
-size_t moe_workspace_bytes(const moe_shape *s, int32_t T, int32_t kind) {
+size_t moe_workspace_bytes(const moe_shape *s, int32_t T, int32_t n_layers, int32_t kind) {
     if (check_shape(s) != MOE_OK || T < 1) return 0;
     if (kind == MOE_WS_DECODE || kind == MOE_WS_STACK) {
-        if (T > kMaxDecodeT) return 0;
-        return decode_ws_bytes(s, T);
+        const int L = kind == MOE_WS_DECODE ? 1 : n_layers;
+        if (T > kMaxDecodeT || L < 1 || L > kMaxLayers) return 0;
+        return decode_ws_bytes(s, T, L);
     }
     if (kind == MOE_WS_BATCHED) {
         if (T > kMaxBatchT) return 0;
-        return decode_ws_bytes(s, 1);  // placeholder until the batched path lands
+        return 256;  // placeholder until the batched path lands
     }
     return 0;
 }
@@ -219,24 +227,16 @@ moe_status moe_route(const moe_shape *s, const moe_layer *L, const uint16_t *x, 
 moe_status moe_layer_decode(const moe_shape *s, const moe_layer *L, const uint16_t *x, int32_t T,
                             float *y, int32_t *topk_idx_opt, float *topk_w_opt, float *logits_opt,
                             void *ws, size_t ws_bytes, void *stream) {
-    return decode_common(s, L, 1, x, T, y, nullptr, nullptr, topk_idx_opt, topk_w_opt, logits_opt,
-                         ws, ws_bytes, stream, 1);
+    return decode_common(s, L, 1, 0, x, T, y, nullptr, nullptr, topk_idx_opt, topk_w_opt, logits_opt, ws,
+                         ws_bytes, stream);
 }
 
-moe_status moe_stack_decode(const moe_shape *s, const moe_layer *stack, int32_t n_layers,
+moe_status moe_stack_decode(const moe_shape *s, const moe_layer *stack, int32_t n_layers, uint32_t flags,
                             const uint16_t *x, int32_t T, float *y, uint16_t *x_all_opt,
                             float *y_all_opt, int32_t *idx_all_opt, float *w_all_opt,
                             float *logits_all_opt, void *ws, size_t ws_bytes, void *stream) {
-    return decode_common(s, stack, n_layers, x, T, y, x_all_opt, y_all_opt, idx_all_opt, w_all_opt,
-                         logits_all_opt, ws, ws_bytes, stream, 1);
-}
-
-moe_status moe_stack_decode_phased(const moe_shape *s, const moe_layer *stack, int32_t n_layers,
-                                   const uint16_t *x, int32_t T, float *y, uint16_t *x_all_opt,
-                                   float *y_all_opt, int32_t *idx_all_opt, float *w_all_opt,
-                                   float *logits_all_opt, void *ws, size_t ws_bytes, void *stream) {
-    return decode_common(s, stack, n_layers, x, T, y, x_all_opt, y_all_opt, idx_all_opt, w_all_opt,
-                         logits_all_opt, ws, ws_bytes, stream, 0);
+    return decode_common(s, stack, n_layers, flags, x, T, y, x_all_opt, y_all_opt, idx_all_opt, w_all_opt,
+                         logits_all_opt, ws, ws_bytes, stream);
 }
 
 moe_status moe_layer_batched(const moe_shape *s, const moe_layer *L, const uint16_t *x, int32_t T,

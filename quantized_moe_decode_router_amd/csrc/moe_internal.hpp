@@ -13,13 +13,13 @@ struct QMat {
     const uint16_t *b;  // bf16 biases
 };
 
-// Decode of L chained layers (L = 1 for a single layer). Every weight pointer is the layer-0
-// base of an [L]-stacked array; ls_* are the per-layer strides in elements.
+// Decode of L layers (L = 1 for a single layer). Every weight pointer is the layer-0 base of an
+// [L]-stacked array; ls_* are the per-layer strides in elements.
 struct DecodeParams {
-    int H, E, K, I, Is, bits, T, L, glue;
-    int Imax;         // max(I, Is): row stride of the h buffer
-    int rows_per_wg;  // down-projection rows owned by each workgroup
-    unsigned spin_limit;
+    int H, E, K, I, Is, bits, T, L;
+    int chained;          // layer l+1 takes the RMS glue of y_l (else every layer takes x_in)
+    int rows_per_wg;      // rows of y owned by each workgroup
+    unsigned spin_limit;  // bound on every wait
     float eps;
     const float *router, *rbias, *sgate;
     QMat w13, w2, s13, s2;
@@ -32,38 +32,41 @@ struct DecodeParams {
     int *idx_all;          // [L][T][K] or null
     float *w_all;          // [L][T][K] or null
     float *logits_all;     // [L][T][E] or null
-    // workspace
-    int *ctrl;      // [0] status, [1] barrier arrivals, [2] barrier generation
-    float *logits;  // [T][E+1]: router logits, column E = shared-gate logit
-    float *hbuf;    // [T][K+1][Imax]: routed h at slot k, shared h at slot K
-    float *ybuf;    // [T][H]
+    // workspace (zero-filled before first use)
+    int *ctrl;               // [0] status, [1] call sequence number
+    uint64_t *ll_start;      // [grid]            one word per workgroup: "this call has started"
+    uint64_t *ll_logits;     // [L][T][E+1]       router logits, column E = shared-gate logit
+    uint64_t *ll_h;          // [L][T][K][I]      routed h
+    uint64_t *ll_hs;         // [L][T][Is]        shared-expert h
+    uint64_t *ll_y;          // [L][T][H]
 };
 
-struct DecodeLds {
-    size_t xs, lg, sidx, sw, gam, part, red, total;
-};
+constexpr int kDecodeThreads = 512;
+constexpr size_t kCtrlBytes = 256;
 
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-__host__ __device__ inline DecodeLds decode_lds_layout(int T, int H, int E, int K, int rows_per_wg) {
-    DecodeLds d;
-    size_t o = 0;
-    d.xs = o;   o = align_up(o + sizeof(float) * (size_t)T * H, 16);
-    d.lg = o;   o = align_up(o + sizeof(float) * (size_t)T * (E + 1), 16);
-    d.sidx = o; o = align_up(o + sizeof(int) * (size_t)T * K, 16);
-    d.sw = o;   o = align_up(o + sizeof(float) * (size_t)T * K, 16);
-    d.gam = o;  o = align_up(o + sizeof(float) * (size_t)T, 16);
-    d.part = o; o = align_up(o + sizeof(float) * (size_t)T * (K + 1) * rows_per_wg, 16);
-    d.red = o;  o = align_up(o + sizeof(float) * 64, 16);
-    d.total = o;
-    return d;
+// Workspace layout of the decode kernel (bytes from the workspace base).
+struct DecodeWs {
+    size_t start, logits, h, hs, y, total;
+};
+constexpr int kMaxGrid = 1024;
+__host__ __device__ inline DecodeWs decode_ws_layout(int L, int T, int H, int E, int K, int I, int Is) {
+    DecodeWs w;
+    size_t o = kCtrlBytes;
+    w.start = o;  o = align_up(o + 8 * (size_t)kMaxGrid, 256);
+    w.logits = o; o = align_up(o + 8 * (size_t)L * T * (E + 1), 256);
+    w.h = o;      o = align_up(o + 8 * (size_t)L * T * K * I, 256);
+    w.hs = o;     o = align_up(o + 8 * (size_t)L * T * (Is > 0 ? Is : 1), 256);
+    w.y = o;      o = align_up(o + 8 * (size_t)L * T * H, 256);
+    w.total = o;
+    return w;
 }
 
-constexpr int kDecodeThreads = 512;
-
-// Enqueue the decode kernel(s). persistent != 0: one cooperative launch with grid barriers;
-// persistent == 0: one launch per phase (3 per layer). Returns a hipError_t.
-hipError_t launch_decode(const DecodeParams &p, int grid, hipStream_t stream, int persistent);
+// Enqueue the decode kernel. Returns a hipError_t.
+hipError_t launch_decode(const DecodeParams &p, int grid, hipStream_t stream);
+// Dynamic LDS bytes the decode kernel needs (0 if the shape does not fit).
+size_t decode_lds_bytes(int T, int H, int E, int K, int I, int Is, int bits, int rows_per_wg);
 
 // Router for T tokens: logits (or given logits), top-k, renormalised weights, optional gamma.
 struct RouteParams {

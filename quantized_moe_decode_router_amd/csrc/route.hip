@@ -1,5 +1,6 @@
 // route.hip -- router for T tokens: fp32 router GEMV (or given logits), top-k selection under
-// (logit descending, index ascending) and renormalised softmax weights. One workgroup per token.
+// (logit descending, index ascending) and renormalised softmax weights. One workgroup per token;
+// its first wave selects (wave_topk).
 // Each token goes to 8 of 256 experts (35B-A3B) or 10 of 512 (80B-A3B) (xix.ai Swiftlet article,
 // paragraph on scheduling); the selection rule and renormalisation are the plainest reading of
 // top-k routing, and softmax-then-renormalise over the kept experts equals the softmax of the
@@ -36,30 +37,17 @@ __global__ void __launch_bounds__(kRouteThreads) route_kernel(RouteParams p) {
         for (int e = threadIdx.x; e < E; e += blockDim.x) lg[e] = p.logits[(size_t)t * E + e];
         __syncthreads();
     }
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        const float v = lg[e];
-        int rank = 0;
-        for (int e2 = 0; e2 < E; ++e2) {
-            const float v2 = lg[e2];
-            rank += (v2 > v) || (v2 == v && e2 < e);
-        }
-        if (rank < K) sidx[rank] = e;
-    }
+    if (wave == 0) wave_topk(lg, E, K, sidx + 2 * K, reinterpret_cast<float *>(sidx + 3 * K), sidx);
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const float m = lg[sidx[0]];
-        float z = 0.0f;
-        for (int k = 0; k < K; ++k) z += expf(lg[sidx[k]] - m);
-        for (int k = 0; k < K; ++k) {
-            p.idx[(size_t)t * K + k] = sidx[k];
-            p.w[(size_t)t * K + k] = expf(lg[sidx[k]] - m) / z;
-        }
-        if (p.gamma) p.gamma[t] = 1.0f / (1.0f + expf(-gate_logit));
+    if (threadIdx.x < K) {
+        p.idx[(size_t)t * K + threadIdx.x] = sidx[2 * K + threadIdx.x];
+        p.w[(size_t)t * K + threadIdx.x] = reinterpret_cast<float *>(sidx + 3 * K)[threadIdx.x];
     }
+    if (threadIdx.x == 0 && p.gamma) p.gamma[t] = 1.0f / (1.0f + expf(-gate_logit));
 }
 
 hipError_t launch_route(const RouteParams &p, hipStream_t stream) {
-    const size_t lds = sizeof(float) * ((size_t)p.H + p.E + 1) + sizeof(int) * (size_t)p.K;
+    const size_t lds = sizeof(float) * ((size_t)p.H + p.E + 1) + sizeof(int) * 4 * (size_t)p.K;
     if (lds > 65536) {
         hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&route_kernel),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) >= 8, names
+    assert len(names) >= 7, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding.EXPORTED)
@@ -46,8 +46,8 @@ def S(**kw):
     return binding.MoeShape(**d)
 
 
-def ws(shape, T=1, kind=0):
-    return binding.lib().moe_workspace_bytes(ctypes.byref(shape), T, kind)
+def ws(shape, T=1, kind=0, L=1):
+    return binding.lib().moe_workspace_bytes(ctypes.byref(shape), T, L, kind)
 
 
 def test_workspace_bytes_and_shape_checks(L):
@@ -55,6 +55,8 @@ def test_workspace_bytes_and_shape_checks(L):
     assert ws(S(), T=8) > ws(S(), T=1)
     assert ws(S(), T=9, kind=0) == 0  # decode takes at most 8 tokens
     assert ws(S(), T=512, kind=1) > 0
+    assert ws(S(), kind=2, L=40) > ws(S(), kind=2, L=1) == ws(S(), kind=0)
+    assert ws(S(), kind=2, L=0) == 0
     assert ws(S(bits=3)) == 0
     assert ws(S(group_size=32)) == 0
     assert ws(S(top_k=300)) == 0  # K > E

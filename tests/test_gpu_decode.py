@@ -100,9 +100,9 @@ def test_route_own_logits(name, T):
     gamma = torch.empty(T, dtype=torch.float32, device=dev)
     moe.moe_route(shape, sd, x.to(dev), T, logits, idx, w, gamma)
     torch.cuda.synchronize()
-    amb = check_routing_against_oracle(idx.cpu().numpy(), w.cpu().numpy(), logits.cpu().numpy(), ref,
-                                       bf16_bits(x), Lh, shape.top_k)
-    assert amb == 0
+    differ = check_routing_against_oracle(idx.cpu().numpy(), w.cpu().numpy(), logits.cpu().numpy(), ref,
+                                          bf16_bits(x), Lh, shape.top_k)
+    assert not differ
     np.testing.assert_allclose(gamma.cpu().numpy(), ref["gamma"], rtol=0, atol=1e-6)
 
 
@@ -130,10 +130,11 @@ def test_layer_decode_parity(name, shape, T, seed):
     Lh = host_layer(st, 0)
     ref = oracle_layer(st, 0, bf16_bits(x))
     y, idx, w, lg = run_decode(shape, st.layer(0), x, T, dev)
-    amb = check_routing_against_oracle(idx, w, lg, ref, bf16_bits(x), Lh, shape.top_k)
-    assert amb == 0, "seed gives a near-tie in routing; pick another"
-    err = check_y(y, ref["y"])
-    print(f"{name}: max|err|/RMS = {err:.2e}")
+    differ = check_routing_against_oracle(idx, w, lg, ref, bf16_bits(x), Lh, shape.top_k)
+    keep = [t for t in range(T) if t not in differ]
+    assert keep, "every token's routing is legitimately ambiguous; pick another seed"
+    err = check_y(y[keep], ref["y"][keep])
+    print(f"{name}: max|err|/RMS = {err:.2e} over {len(keep)}/{T} tokens")
 
 
 def test_decode_edge_values():
@@ -165,7 +166,7 @@ def test_decode_tokens_are_independent():
 
 # ------------------------------------------------------------------------------ stacks
 
-def _stack_run(shape, st, n_layers, x, T, dev, phased=False):
+def _stack_run(shape, st, n_layers, x, T, dev, flags=0):
     moe = _moe()
     H, K, E = shape.hidden, shape.top_k, shape.num_experts
     out = dict(y=torch.empty(T, H, dtype=torch.float32, device=dev),
@@ -174,23 +175,45 @@ def _stack_run(shape, st, n_layers, x, T, dev, phased=False):
                idx_all=torch.empty(n_layers, T, K, dtype=torch.int32, device=dev),
                w_all=torch.empty(n_layers, T, K, dtype=torch.float32, device=dev),
                logits_all=torch.empty(n_layers, T, E, dtype=torch.float32, device=dev))
-    ws = moe.workspace(shape, T, moe.MOE_WS_STACK, dev)
-    fn = moe.moe_stack_decode_phased if phased else moe.moe_stack_decode
-    fn(shape, st, n_layers, x, T, out["y"], out["x_all"], out["y_all"], out["idx_all"], out["w_all"],
-       out["logits_all"], workspace=ws)
+    ws = moe.workspace(shape, T, moe.MOE_WS_STACK, dev, n_layers=n_layers)
+    moe.moe_stack_decode(shape, st, n_layers, x, T, out["y"], out["x_all"], out["y_all"], out["idx_all"],
+                         out["w_all"], out["logits_all"], workspace=ws, flags=flags)
     assert moe.moe_read_status(ws) == 0
     return out
 
 
-def test_stack_phased_equals_persistent():
+def test_stack_layers_equal_single_layer_calls():
+    """An unchained stack computes, for every layer, exactly what a one-layer call computes."""
     dev = need_gpu()
+    moe = _moe()
     shape = synth.QWEN35B_4BIT.shape
     st = synth.make_stack(shape, 3, 5, dev)
     x = synth.make_x(shape, 2, 1, device=dev)
-    a = _stack_run(shape, st, 3, x, 2, dev)
-    b = _stack_run(shape, st, 3, x, 2, dev, phased=True)
-    for k in a:
-        assert torch.equal(a[k], b[k]), k
+    out = _stack_run(shape, st, 3, x, 2, dev, flags=moe.MOE_STACK_INDEPENDENT)
+    for l in range(3):
+        y, idx, w, lg = run_decode(shape, st.layer(l), x, 2, dev)
+        assert np.array_equal(out["y_all"][l].cpu().numpy(), y), l
+        assert np.array_equal(out["idx_all"][l].cpu().numpy(), idx), l
+        assert torch.equal(out["x_all"][l], x)
+    assert torch.equal(out["y"], out["y_all"][2])
+
+
+def test_repeated_calls_reuse_the_workspace():
+    """Back-to-back calls on one workspace (the call counter advances) give identical results."""
+    dev = need_gpu()
+    moe = _moe()
+    shape = synth.QWEN35B_4BIT.shape
+    st = synth.make_stack(shape, 4, 6, dev)
+    x = synth.make_x(shape, 1, 2, device=dev)
+    ws = moe.workspace(shape, 1, moe.MOE_WS_STACK, dev, n_layers=4)
+    ys = []
+    for _ in range(5):
+        y = torch.empty(1, shape.hidden, dtype=torch.float32, device=dev)
+        moe.moe_stack_decode(shape, st, 4, x, 1, y, workspace=ws)
+        ys.append(y)
+    assert moe.moe_read_status(ws) == 0
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
 
 
 def _glue_ref(y):
@@ -200,36 +223,41 @@ def _glue_ref(y):
     return bf16_bits(torch.from_numpy(y * inv).to(torch.bfloat16))
 
 
-def _stack_layer_check(l, gx, xo, out, ref, Lh, K):
-    """One layer of the chained comparison. The two chains' inputs may differ by one bf16 ulp in
-    a few elements (fp32 vs fp64 glue); that difference is added to the logit bound and loosens
-    the weight tolerance. Returns False when the routing is legitimately ambiguous and differs."""
-    from tests.gpu_common import W_TOL, logit_bound, topk_margin
-    from tests.helpers import bits_to_f32
-    xg = bits_to_f32(gx[0]).astype(np.float64)
-    xr = bits_to_f32(xo[0]).astype(np.float64)
-    R = Lh.arrays["router"].astype(np.float64)
-    bnd = logit_bound(xr, Lh.arrays["router"], Lh.arrays.get("router_bias")).max()
-    bnd += float((np.abs(R) @ np.abs(xg - xr)).max())
-    idx = out["idx_all"][l].cpu().numpy()[0]
-    w = out["w_all"][l].cpu().numpy()[0]
-    if topk_margin(ref["logits"][0], K) > 2 * bnd:
-        assert list(idx) == list(ref["idx"][0]), f"layer {l}: {idx} vs {ref['idx'][0]}"
-    elif list(idx) != list(ref["idx"][0]):
-        return False
-    tol = W_TOL if np.array_equal(gx, xo) else 2.0 * bnd
-    np.testing.assert_allclose(w, ref["w"][0], rtol=0, atol=tol)
-    assert abs(float(w.astype(np.float64).sum()) - 1.0) <= 1e-6
-    return True
+STACKS = [synth.QWEN35B_4BIT, synth.QWEN80B_4BIT, synth.QWEN35B_8BIT]
+STACK_IDS = ["35b_4bit", "80b_4bit", "35b_8bit"]
 
 
-@pytest.mark.parametrize("wl", [synth.QWEN35B_4BIT, synth.QWEN80B_4BIT, synth.QWEN35B_8BIT],
-                         ids=["35b_4bit", "80b_4bit", "35b_8bit"])
-def test_full_stack_against_chained_oracle(wl):
-    """The full stack in the configuration the benchmark times (T = 1, every layer chained by the
-    glue) against the oracle run layer by layer on its own chain (its own fp64 glue; no GPU value
-    feeds the oracle). Every layer's input, routing and output are compared; the comparison stops
-    at the first layer whose routing is legitimately ambiguous between the two chains."""
+@pytest.mark.parametrize("wl", STACKS, ids=STACK_IDS)
+def test_full_stack_every_layer(wl):
+    """The full stack in one launch with every layer taking the same input (unchained): every
+    layer's routing and output against the oracle on identical inputs."""
+    import oracle
+    dev = need_gpu()
+    moe = _moe()
+    shape = wl.shape
+    st = synth.make_workload(wl, dev)
+    x = synth.make_x(shape, 1, 0, device=dev)
+    out = _stack_run(shape, st, wl.n_layers, x, 1, dev, flags=moe.MOE_STACK_INDEPENDENT)
+    xo = bf16_bits(x)
+    worst = 0.0
+    for l in range(wl.n_layers):
+        Lh = host_layer(st, l)
+        ref = oracle.layer_forward(Lh, xo)
+        differ = check_routing_against_oracle(out["idx_all"][l].cpu().numpy(), out["w_all"][l].cpu().numpy(),
+                                              out["logits_all"][l].cpu().numpy(), ref, xo, Lh, shape.top_k)
+        if not differ:
+            worst = max(worst, check_y(out["y_all"][l].cpu().numpy(), ref["y"]))
+    print(f"{wl.name}: {wl.n_layers} layers, worst max|err|/RMS {worst:.2e}")
+
+
+@pytest.mark.parametrize("wl", STACKS, ids=STACK_IDS)
+def test_full_stack_chained(wl):
+    """The chained stack exactly as the benchmark runs it (T = 1, layers joined by the glue)
+    against the oracle run on its own chain with its own fp64 glue (no GPU value feeds the
+    oracle). While the two chains' layer inputs are bitwise identical each layer is held to the
+    layer tolerance; rounding can later make the chains' bf16 inputs differ, after which a
+    per-layer tolerance no longer bounds the difference, so from there on only the GPU's own glue
+    (against numpy fp32, to one bf16 ulp) and finiteness are checked."""
     import oracle
     dev = need_gpu()
     shape = wl.shape
@@ -237,25 +265,26 @@ def test_full_stack_against_chained_oracle(wl):
     x = synth.make_x(shape, 1, 0, device=dev)
     out = _stack_run(shape, st, wl.n_layers, x, 1, dev)
     xo = bf16_bits(x)
-    compared, worst, ndiff = 0, 0.0, 0
+    strict = 0
     for l in range(wl.n_layers):
+        gx = bf16_bits(out["x_all"][l])
+        if not np.array_equal(gx, xo):
+            break
         Lh = host_layer(st, l)
         ref = oracle.layer_forward(Lh, xo)
-        gx = bf16_bits(out["x_all"][l])
-        d = np.abs(gx.astype(np.int32) - xo.astype(np.int32))
-        assert d.max() <= 1, f"layer {l}: inputs differ by more than one bf16 ulp"
-        ndiff += int((d > 0).sum())
-        if not _stack_layer_check(l, gx, xo, out, ref, Lh, shape.top_k):
-            print(f"layer {l}: routing legitimately ambiguous between the chains; stopping")
+        differ = check_routing_against_oracle(out["idx_all"][l].cpu().numpy(), out["w_all"][l].cpu().numpy(),
+                                              out["logits_all"][l].cpu().numpy(), ref, xo, Lh, shape.top_k)
+        if differ:
             break
-        worst = max(worst, check_y(out["y_all"][l].cpu().numpy(), ref["y"]))
-        if l + 1 < wl.n_layers:  # the GPU glue itself, against numpy fp32, to one ulp
-            g = _glue_ref(out["y_all"][l].cpu().numpy()[0])
-            nx = bf16_bits(out["x_all"][l + 1])[0]
-            assert np.max(np.abs(g.astype(np.int32) - nx.astype(np.int32))) <= 1
+        check_y(out["y_all"][l].cpu().numpy(), ref["y"])
         xo = oracle.rms_glue(ref["y"][0], 1e-6)[None, :]
-        compared += 1
-    print(f"{wl.name}: {compared}/{wl.n_layers} layers compared, worst max|err|/RMS {worst:.2e}, "
-          f"{ndiff} input elements 1 ulp apart")
-    assert compared >= wl.n_layers // 2
+        strict += 1
+    y_all = out["y_all"].cpu().numpy()
+    assert np.all(np.isfinite(y_all))
+    for l in range(wl.n_layers - 1):
+        g = _glue_ref(y_all[l][0])
+        nx = bf16_bits(out["x_all"][l + 1])[0]
+        assert np.max(np.abs(g.astype(np.int32) - nx.astype(np.int32))) <= 1, f"glue after layer {l}"
     assert torch.equal(out["y"], out["y_all"][-1])
+    print(f"{wl.name}: {strict}/{wl.n_layers} chained layers on bitwise-identical inputs")
+    assert strict >= 1
