@@ -163,6 +163,23 @@ moe_status moe_layer_batched(const moe_shape *shape, const moe_layer *layer, con
                              float *logits_opt, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/*
+ * The grouping step of moe_layer_batched on its own: histogram, exclusive scan and stable
+ * scatter of the T*K (token, slot) pairs of a top-k selection by expert (the "scatter" that turns
+ * per-token routing into per-expert row lists in the grouped evaluation of the layer).
+ *   topk_idx : int32 [T][K] in, every value in [0, E) (values outside are clamped into it, so
+ *              nothing is accessed out of bounds, but the result is then meaningless)
+ *   counts   : int32 [E] out, pairs per expert
+ *   offsets  : int32 [E+1] out, exclusive prefix sums of counts (offsets[E] = T*K)
+ *   perm     : int32 [T*K] out, perm[offsets[e] + r] = the r-th pair q = t*K + k, in increasing
+ *              q, whose expert is e
+ *   pos      : int32 [T*K] out, pos[q] = row of pair q in perm (perm[pos[q]] == q)
+ * Workspace: moe_workspace_bytes(shape, T, 0, MOE_WS_BATCHED) bytes.
+ */
+moe_status moe_group_pairs(const moe_shape *shape, const int32_t *topk_idx, int32_t T, int32_t *counts,
+                           int32_t *offsets, int32_t *perm, int32_t *pos, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 /* Workspace bytes for `kind` (MOE_WS_DECODE, MOE_WS_BATCHED or MOE_WS_STACK), T tokens and, for
  * MOE_WS_STACK, n_layers layers (ignored otherwise); 0 if the arguments are invalid. */
 size_t moe_workspace_bytes(const moe_shape *shape, int32_t T, int32_t n_layers, int32_t kind);

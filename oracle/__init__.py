@@ -237,3 +237,21 @@ def layer_forward(layer: HostLayer, x_bf16_bits, logits_in=None):
     if rc != 0:
         raise ValueError("oracle rejected the layer shape")
     return out
+
+
+# ---- grouping of (token, slot) pairs by expert ------------------------------------------------
+
+def group_pairs(idx, E: int):
+    """Plain definition of the expert grouping used by a batched layer (no arithmetic of the
+    method; a bookkeeping step of the grouped evaluation the spec layer describes):
+    pairs q = t*K + k are ordered by (expert idx[t, k], q) with a stable sort.
+    Returns counts[E], offsets[E+1] (exclusive prefix sums), perm[T*K] (pair at each row) and
+    pos[T*K] (row of each pair)."""
+    flat = np.asarray(idx, dtype=np.int64).reshape(-1)
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    perm = np.argsort(flat, kind="stable").astype(np.int32)
+    pos = np.empty_like(perm)
+    pos[perm] = np.arange(perm.shape[0], dtype=np.int32)
+    return counts, offsets, perm, pos

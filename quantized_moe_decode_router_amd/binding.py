@@ -27,7 +27,7 @@ MOE_WS_DECODE, MOE_WS_BATCHED, MOE_WS_STACK = 0, 1, 2
 
 MOE_STACK_INDEPENDENT = 1
 
-EXPORTED = ("moe_route", "moe_layer_decode", "moe_stack_decode", "moe_layer_batched",
+EXPORTED = ("moe_route", "moe_layer_decode", "moe_stack_decode", "moe_layer_batched", "moe_group_pairs",
             "moe_workspace_bytes", "moe_read_status", "moe_status_string")
 
 
@@ -67,6 +67,7 @@ def lib():
         L.moe_route.argtypes = [PS, PL, P, I32, P, P, P, P, U32, P]
         L.moe_layer_decode.argtypes = [PS, PL, P, I32, P, P, P, P, P, SZ, P]
         L.moe_layer_batched.argtypes = [PS, PL, P, I32, P, P, P, P, P, SZ, P]
+        L.moe_group_pairs.argtypes = [PS, P, I32, P, P, P, P, P, SZ, P]
         L.moe_stack_decode.argtypes = [PS, PL, I32, U32, P, I32, P, P, P, P, P, P, P, SZ, P]
         L.moe_workspace_bytes.argtypes = [PS, I32, I32, I32]
         L.moe_workspace_bytes.restype = SZ
@@ -184,6 +185,17 @@ def moe_layer_batched(shape, layer, x, T: int, y, topk_idx=None, topk_w=None, lo
                                  _ptr(topk_w, "topk_w", torch.float32), _ptr(logits, "logits", torch.float32),
                                  _ptr(workspace, "workspace"), int(wsb), _stream(stream))
     _check(st, "moe_layer_batched")
+
+
+def moe_group_pairs(shape, topk_idx, T: int, counts, offsets, perm, pos, workspace=None,
+                    workspace_bytes: Optional[int] = None, stream=None) -> None:
+    s = shape_struct(shape)
+    wsb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    st = lib().moe_group_pairs(ctypes.byref(s), _ptr(topk_idx, "topk_idx", torch.int32), int(T),
+                               _ptr(counts, "counts", torch.int32), _ptr(offsets, "offsets", torch.int32),
+                               _ptr(perm, "perm", torch.int32), _ptr(pos, "pos", torch.int32),
+                               _ptr(workspace, "workspace"), int(wsb), _stream(stream))
+    _check(st, "moe_group_pairs")
 
 
 def moe_read_status(workspace, stream=None) -> int:

@@ -64,6 +64,10 @@ size_t decode_ws_bytes(const moe_shape *s, int T, int L) {
     return moe::decode_ws_layout(L, T, s->hidden, s->num_experts, s->top_k, s->inter, s->shared_inter).total;
 }
 
+size_t batched_ws_bytes(const moe_shape *s, int T) {
+    return moe::batched_ws_layout(T, s->hidden, s->num_experts, s->top_k, s->inter, s->shared_inter).total;
+}
+
 int rows_per_wg(int H, int grid) { return (H + grid - 1) / grid; }
 
 // Shapes the decode kernel handles (beyond check_shape): rows of at most 64 slices of 32 columns,
@@ -179,7 +183,7 @@ size_t moe_workspace_bytes(const moe_shape *s, int32_t T, int32_t n_layers, int3
     }
     if (kind == MOE_WS_BATCHED) {
         if (T > kMaxBatchT) return 0;
-        return 256;  // placeholder until the batched path lands
+        return batched_ws_bytes(s, T);
     }
     return 0;
 }
@@ -242,11 +246,80 @@ moe_status moe_stack_decode(const moe_shape *s, const moe_layer *stack, int32_t 
 moe_status moe_layer_batched(const moe_shape *s, const moe_layer *L, const uint16_t *x, int32_t T,
                              float *y, int32_t *topk_idx_opt, float *topk_w_opt, float *logits_opt,
                              void *ws, size_t ws_bytes, void *stream) {
-    (void)L; (void)x; (void)y; (void)topk_idx_opt; (void)topk_w_opt; (void)logits_opt;
-    (void)ws; (void)ws_bytes; (void)stream; (void)T;
     moe_status st = check_shape(s);
     if (st != MOE_OK) return st;
-    return MOE_ERR_UNSUPPORTED;
+    if ((st = check_layer(s, L)) != MOE_OK) return st;
+    if (T < 1 || T > kMaxBatchT) return MOE_ERR_INVALID_ARG;
+    if (!x || !y || !al16(x) || !al16(y)) return MOE_ERR_INVALID_ARG;
+    if ((topk_idx_opt && !al4(topk_idx_opt)) || (topk_w_opt && !al4(topk_w_opt)) ||
+        (logits_opt && !al4(logits_opt)))
+        return MOE_ERR_INVALID_ARG;
+    if (!ws || !al16(ws) || ws_bytes < batched_ws_bytes(s, T)) return MOE_ERR_WORKSPACE;
+    const moe::BatchedWs lay = moe::batched_ws_layout(T, s->hidden, s->num_experts, s->top_k, s->inter,
+                                                      s->shared_inter);
+    char *w = static_cast<char *>(ws);
+    moe::BatchedParams p;
+    memset(&p, 0, sizeof p);
+    p.H = s->hidden; p.E = s->num_experts; p.K = s->top_k; p.I = s->inter; p.Is = s->shared_inter;
+    p.Imax = p.I > p.Is ? p.I : p.Is;
+    p.bits = s->bits; p.T = T;
+    p.x = x;
+    p.router = L->router; p.rbias = L->router_bias;
+    p.sgate = p.Is ? L->shared_gate : nullptr;
+    p.w13 = {L->w13.codes, L->w13.scales, L->w13.biases};
+    p.w2 = {L->w2.codes, L->w2.scales, L->w2.biases};
+    if (p.Is) {
+        p.s13 = {L->s13.codes, L->s13.scales, L->s13.biases};
+        p.s2 = {L->s2.codes, L->s2.scales, L->s2.biases};
+    }
+    p.logits = logits_opt ? logits_opt : reinterpret_cast<float *>(w + lay.logits);
+    p.gate = reinterpret_cast<float *>(w + lay.gate);
+    p.idx = topk_idx_opt ? topk_idx_opt : reinterpret_cast<int *>(w + lay.idx);
+    p.w = topk_w_opt ? topk_w_opt : reinterpret_cast<float *>(w + lay.w);
+    p.gamma = reinterpret_cast<float *>(w + lay.gamma);
+    p.blkcnt = reinterpret_cast<int *>(w + lay.blkcnt);
+    p.rank = reinterpret_cast<int *>(w + lay.rank);
+    p.gcnt = reinterpret_cast<int *>(w + lay.gcnt);
+    p.goff = reinterpret_cast<int *>(w + lay.goff);
+    p.ntiles = reinterpret_cast<int *>(w + lay.ntiles);
+    p.tiles = reinterpret_cast<int2 *>(w + lay.tiles);
+    p.perm = reinterpret_cast<int *>(w + lay.perm);
+    p.pos = reinterpret_cast<int *>(w + lay.pos);
+    p.hh = reinterpret_cast<_Float16 *>(w + lay.hh);
+    p.hl = reinterpret_cast<_Float16 *>(w + lay.hl);
+    p.out = reinterpret_cast<float *>(w + lay.out);
+    p.y = y;
+    hipError_t err = moe::launch_batched(p, lay.max_tiles, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_group_pairs(const moe_shape *s, const int32_t *topk_idx, int32_t T, int32_t *counts,
+                           int32_t *offsets, int32_t *perm, int32_t *pos, void *ws, size_t ws_bytes,
+                           void *stream) {
+    moe_status st = check_shape(s);
+    if (st != MOE_OK) return st;
+    if (T < 1 || T > kMaxBatchT) return MOE_ERR_INVALID_ARG;
+    if (!topk_idx || !counts || !offsets || !perm || !pos) return MOE_ERR_INVALID_ARG;
+    if (!al4(topk_idx) || !al4(counts) || !al4(offsets) || !al4(perm) || !al4(pos)) return MOE_ERR_INVALID_ARG;
+    if (!ws || !al16(ws) || ws_bytes < batched_ws_bytes(s, T)) return MOE_ERR_WORKSPACE;
+    const moe::BatchedWs lay = moe::batched_ws_layout(T, s->hidden, s->num_experts, s->top_k, s->inter,
+                                                      s->shared_inter);
+    char *w = static_cast<char *>(ws);
+    moe::BatchedParams p;
+    memset(&p, 0, sizeof p);
+    p.H = s->hidden; p.E = s->num_experts; p.K = s->top_k; p.I = s->inter; p.Is = 0;
+    p.Imax = p.I; p.bits = s->bits; p.T = T;
+    p.idx = const_cast<int *>(topk_idx);
+    p.blkcnt = reinterpret_cast<int *>(w + lay.blkcnt);
+    p.rank = reinterpret_cast<int *>(w + lay.rank);
+    p.gcnt = counts;
+    p.goff = offsets;
+    p.ntiles = reinterpret_cast<int *>(w + lay.ntiles);
+    p.tiles = reinterpret_cast<int2 *>(w + lay.tiles);
+    p.perm = perm;
+    p.pos = pos;
+    hipError_t err = moe::launch_bucket(p, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 }  // extern "C"

@@ -80,6 +80,68 @@ struct RouteParams {
 };
 hipError_t launch_route(const RouteParams &p, hipStream_t stream);
 
+// One batched layer (T tokens). Pointers into the workspace are carved by the host.
+struct BatchedParams {
+    int H, E, K, I, Is, Imax, bits, T;
+    const uint16_t *x;  // [T][H] bf16
+    const float *router, *rbias, *sgate;
+    QMat w13, w2, s13, s2;
+    float *logits;      // [T][E]
+    float *gate;        // [T] shared-gate logit
+    int *idx;           // [T][K]
+    float *w;           // [T][K]
+    float *gamma;       // [T]
+    int *blkcnt;        // [ceil(T/64)][E] per-block counts, then per-block exclusive prefixes
+    int *rank;          // [T*K] rank of a pair among its 64-token block's pairs of the same expert
+    int *gcnt;          // [E+1] rows per group (group E = shared expert, T rows)
+    int *goff;          // [E+2] first row of each group
+    int *ntiles;        // [1]
+    int2 *tiles;        // [max_tiles] (group, first row in group)
+    int *perm;          // [R] pair index t*K+k of each row (shared rows: t*K)
+    int *pos;           // [T*K] row of each pair
+    _Float16 *hh, *hl;  // [R][Imax] SwiGLU output, fp16 hi and lo halves
+    float *out;         // [R][H] scaled down-projection rows
+    float *y;           // [T][H]
+};
+
+// Workspace layout of the batched path (bytes from the workspace base); R = T*K (+ T with a
+// shared expert) rows.
+struct BatchedWs {
+    size_t logits, gate, idx, w, gamma, blkcnt, rank, gcnt, goff, ntiles, tiles, perm, pos, hh, hl, out, total;
+    int max_tiles;
+};
+__host__ inline BatchedWs batched_ws_layout(int T, int H, int E, int K, int I, int Is) {
+    BatchedWs w;
+    const size_t TK = (size_t)T * K, R = TK + (Is ? (size_t)T : 0);
+    const size_t Imax = I > Is ? I : Is, nblk = ((size_t)T + 63) / 64;
+    const size_t touched = TK < (size_t)E ? TK : (size_t)E;
+    w.max_tiles = (int)(TK / 64 + touched + (Is ? ((size_t)T + 63) / 64 : 0) + 1);
+    size_t o = kCtrlBytes;
+    w.logits = o; o = align_up(o + 4 * (size_t)T * E, 256);
+    w.gate = o;   o = align_up(o + 4 * (size_t)T, 256);
+    w.idx = o;    o = align_up(o + 4 * TK, 256);
+    w.w = o;      o = align_up(o + 4 * TK, 256);
+    w.gamma = o;  o = align_up(o + 4 * (size_t)T, 256);
+    w.blkcnt = o; o = align_up(o + 4 * nblk * E, 256);
+    w.rank = o;   o = align_up(o + 4 * TK, 256);
+    w.gcnt = o;   o = align_up(o + 4 * ((size_t)E + 2), 256);
+    w.goff = o;   o = align_up(o + 4 * ((size_t)E + 2), 256);
+    w.ntiles = o; o = align_up(o + 16, 256);
+    w.tiles = o;  o = align_up(o + 8 * (size_t)w.max_tiles, 256);
+    w.perm = o;   o = align_up(o + 4 * R, 256);
+    w.pos = o;    o = align_up(o + 4 * TK, 256);
+    w.hh = o;     o = align_up(o + 2 * R * Imax, 256);
+    w.hl = o;     o = align_up(o + 2 * R * Imax, 256);
+    w.out = o;    o = align_up(o + 4 * R * (size_t)H, 256);
+    w.total = o;
+    return w;
+}
+hipError_t launch_batched(const BatchedParams &p, int max_tiles, hipStream_t stream);
+// Histogram / scan / stable scatter of the batched path (fills gcnt, goff, tiles, perm, pos).
+hipError_t launch_bucket(const BatchedParams &p, hipStream_t stream);
+// Router GEMM + per-token top-k of the batched path (fills logits, gate, idx, w, gamma).
+hipError_t launch_router_topk(const BatchedParams &p, hipStream_t stream);
+
 // Query (and cache per device) the compute-unit count.
 int device_cu_count();
 

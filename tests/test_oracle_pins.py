@@ -371,3 +371,39 @@ def test_rms_glue(oracle_lib):
                     .to(torch.bfloat16))
     # fp64 vs fp32 quotient may straddle a rounding boundary: at most 1 ulp apart
     assert np.max(np.abs(got.astype(np.int32) - ref.astype(np.int32))) <= 1
+
+
+@pytest.mark.parametrize("T,K,E,seed", [(1, 1, 1, 0), (4, 2, 16, 1), (33, 8, 256, 2), (130, 10, 512, 3), (7, 4, 4, 4)])
+def test_group_pairs_properties(oracle_lib, T, K, E, seed):
+    """The grouping is pinned by properties that determine it uniquely, checked with plain loops
+    (no sort): counts are the histogram, offsets its exclusive prefix, perm a permutation whose
+    segment e holds exactly the pairs selecting e in increasing pair order, pos its inverse."""
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.choice(E, size=K, replace=False) for _ in range(T)]).astype(np.int32)
+    counts, offsets, perm, pos = oracle_lib.group_pairs(idx, E)
+    flat = idx.reshape(-1)
+    hist = [0] * E
+    for e in flat:
+        hist[int(e)] += 1
+    assert list(counts) == hist
+    run = 0
+    for e in range(E):
+        assert offsets[e] == run
+        run += hist[e]
+    assert offsets[E] == T * K
+    assert sorted(perm.tolist()) == list(range(T * K))
+    for e in range(E):
+        seg = perm[offsets[e]:offsets[e + 1]].tolist()
+        assert all(flat[q] == e for q in seg)
+        assert all(a < b for a, b in zip(seg, seg[1:]))
+    for q in range(T * K):
+        assert perm[pos[q]] == q
+
+
+def test_group_pairs_planted_order_mistake(oracle_lib):
+    """A grouping that is not stable (pairs of one expert out of pair order) violates the
+    segment-order property the test above checks."""
+    idx = np.array([[0, 1], [1, 0], [0, 1]], dtype=np.int32)
+    counts, offsets, perm, pos = oracle_lib.group_pairs(idx, 2)
+    assert perm[offsets[0]:offsets[1]].tolist() == [0, 3, 4]
+    assert perm[offsets[1]:offsets[2]].tolist() == [1, 2, 5]
