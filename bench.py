@@ -8,7 +8,10 @@ expert 512, group-64 bf16 scale/bias, seeded synthetic weights resident in HBM; 
 fresh seeded input so routing changes every step.
 
 Prints one JSON line with the throughput, the HBM roofline of the decode kernel (algorithmic
-bytes per launch / measured launch time) and the fp64 CPU oracle timed on a bounded sample.
+bytes per launch / its average launch duration, timed with HIP events on the launch stream),
+the fp64 CPU oracle timed on a bounded sample, and a "batched" leg: the same weights with a
+Zipf(1.1) router bias, T = 512 tokens per layer call through moe_layer_batched, reporting its
+MFMA utilisation against the fp16 dense peak.
 """
 import argparse
 import glob
@@ -22,7 +25,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer decode tokens/s and achieved HBM GB/s (% of peak), 4-bit 35B shape"
-HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
+FP16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, published
 
 
 def kernel_source_hash() -> str:
@@ -79,6 +83,55 @@ def cpu_baseline(stack, wl, budget_s: float):
                       f"{el:.1f} s; tokens/s = 1 / (time per layer-token x {wl.n_layers} layers)"}
 
 
+def batched_leg(stack, steps: int, warmup: int):
+    """T = 512 tokens through every layer of the stack (each layer called on the step's input)
+    with moe_layer_batched; the Zipf(1.1) router bias of the batched workload is attached to the
+    same weights."""
+    import torch
+
+    import quantized_moe_decode_router_amd as moe
+    import synth
+
+    wl = synth.QWEN35B_BATCHED
+    shape, T, L = wl.shape, wl.tokens, stack.n_layers
+    dev = stack.router.device
+    sb = synth.with_zipf_bias(stack, wl.seed, wl.zipf_s)
+    layers = [sb.layer(l) for l in range(L)]
+    n = warmup + steps
+    xs = [synth.make_x(shape, T, wl.seed, step=s, device=dev) for s in range(n)]
+    y = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
+    idx = torch.empty(T, shape.top_k, dtype=torch.int32, device=dev)
+    ws = moe.workspace(shape, T, moe.MOE_WS_BATCHED, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(s):
+        for l in range(L):
+            moe.moe_layer_batched(shape, layers[l], xs[s], T, y, idx, workspace=ws, stream=stream)
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for s in range(warmup, n):
+        step(s)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    per_layer_us = ms * 1e3 / L
+    flops = 2.0 * T * shape.top_k * 3 * shape.inter * shape.hidden + 2.0 * T * 3 * shape.shared_inter * shape.hidden
+    tflops = flops / (per_layer_us * 1e-6) / 1e12
+    counts = torch.bincount(idx.view(-1).long(), minlength=shape.num_experts)
+    return {"workload": wl.name, "tokens_per_call": T, "layers": L, "steps": steps,
+            "ms_per_step": round(ms, 4), "us_per_layer": round(per_layer_us, 2),
+            "layer_tokens_per_s": round(T * L / (ms / 1e3), 1),
+            "mfma": {"dtype": "fp16", "algorithmic_tflop_per_layer": round(flops / 1e12, 4),
+                     "achieved_tflops": round(tflops, 1), "peak_tflops": FP16_PEAK_TFLOPS,
+                     "utilisation": round(tflops / FP16_PEAK_TFLOPS, 4)},
+            "last_layer_experts_touched": int((counts > 0).sum().item()),
+            "last_layer_max_load": int(counts.max().item())}
+
+
 def main():
     import synth
     ap = argparse.ArgumentParser()
@@ -91,6 +144,8 @@ def main():
                     help="unchained layers (every layer takes the step's input): an upper bound, not decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--batched-steps", type=int, default=10,
+                    help="steps of the batched leg (0 skips it)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -123,24 +178,27 @@ def main():
         step(s)
     torch.cuda.synchronize()
     assert moe.moe_read_status(ws) == 0
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event pair around every launch: their mean is the kernel's average launch duration
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    start.record(stream)
-    for s in range(args.warmup, nsteps):
+    for i, s in enumerate(range(args.warmup, nsteps)):
+        evs[i][0].record(stream)
         step(s)
-    end.record(stream)
+        evs[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     status = moe.moe_read_status(ws)
     if status != 0:
         raise SystemExit(f"device status {moe.status_string(status)} after the timed steps")
-    ev_ms = start.elapsed_time(end)
-    ms_per_step = ev_ms / args.steps
-    tokens_per_s = args.steps * T / (ev_ms / 1e3)
+    total_ms = evs[0][0].elapsed_time(evs[-1][1])
+    launch_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    ms_per_step = total_ms / args.steps
+    tokens_per_s = args.steps * T / (total_ms / 1e3)
 
     bytes_per_launch = L * synth.algorithmic_decode_bytes(shape) * T
-    achieved = bytes_per_launch / (ms_per_step / 1e3) / 1e9
+    achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
     kernel = "decode_kernel"
     traffic = recorded_traffic(wl.name, kernel)
     result = {
@@ -158,9 +216,12 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": bytes_per_launch,
-                     "avg_launch_us": round(ms_per_step * 1e3, 3)},
+                     "avg_launch_us": round(launch_ms * 1e3, 3)},
         "cpu_baseline": None,
+        "batched": None,
     }
+    if args.batched_steps > 0 and shape == synth.QWEN35B_BATCHED.shape:
+        result["batched"] = batched_leg(stack, args.batched_steps, 2)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(stack, wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -5,4 +5,4 @@ none of the MoE layer's arithmetic lives here."""
 from . import rng, workloads  # noqa: F401
 from .workloads import (ALL, QWEN35B_4BIT, QWEN35B_8BIT, QWEN35B_BATCHED, QWEN80B_4BIT, TINY,  # noqa: F401
                         LayerStack, MoeShape, Workload, algorithmic_decode_bytes, make_stack,
-                        make_workload, make_x)
+                        make_workload, make_x, with_zipf_bias, zipf_bias)

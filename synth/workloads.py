@@ -187,6 +187,21 @@ def _fill_scales_biases(scales: torch.Tensor, biases: torch.Tensor, key: int, bi
     biases.view(-1).copy_(s * (-zero_point))  # exact: power-of-two multiple of a bf16 value
 
 
+def zipf_bias(shape: MoeShape, l: int, seed: int, zipf_s: float, device="cpu") -> torch.Tensor:
+    """fp32 [E] router bias of layer l: -s * ln(rank_e), ranks a seeded permutation of 1..E."""
+    perm = rng.permutation(rng.derive_key(seed, l, T_ROUTER_BIAS), shape.num_experts, device)
+    rank = torch.empty_like(perm)
+    rank[perm] = torch.arange(1, shape.num_experts + 1, device=device)
+    return (-zipf_s * torch.log(rank.to(torch.float64))).to(torch.float32)
+
+
+def with_zipf_bias(stack: LayerStack, seed: int, zipf_s: float) -> LayerStack:
+    """The same weights (no copy) with the Zipf router bias of every layer attached."""
+    dev = stack.router.device
+    bias = torch.stack([zipf_bias(stack.shape, l, seed, zipf_s, dev) for l in range(stack.n_layers)])
+    return dataclasses.replace(stack, router_bias=bias.contiguous())
+
+
 def fill_layer(stack: LayerStack, l: int, seed: int, zipf_s: Optional[float] = None) -> None:
     """Fill layer l of `stack` in place from (seed, l)."""
     sh = stack.shape
@@ -198,10 +213,7 @@ def fill_layer(stack: LayerStack, l: int, seed: int, zipf_s: Optional[float] = N
         if zipf_s is None:
             stack.router_bias[l].zero_()
         else:
-            perm = rng.permutation(k(T_ROUTER_BIAS), sh.num_experts, dev)
-            rank = torch.empty_like(perm)
-            rank[perm] = torch.arange(1, sh.num_experts + 1, device=dev)
-            stack.router_bias[l].copy_((-zipf_s * torch.log(rank.to(torch.float64))).to(torch.float32))
+            stack.router_bias[l].copy_(zipf_bias(sh, l, seed, zipf_s, dev))
     if stack.shared_gate is not None:
         stack.shared_gate[l].copy_((0.02 * rng.normal(k(T_SHARED_GATE), sh.hidden, dev)).to(torch.float32))
     rng.fill_bytes(stack.w13_codes[l], k(T_W13_CODES))
