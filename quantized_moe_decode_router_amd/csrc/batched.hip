@@ -98,13 +98,12 @@ __global__ void __launch_bounds__(kTopkWaves * kWave) topk_kernel(BatchedParams 
     const int E = p.E, K = p.K;
     const int t = blockIdx.x * kTopkWaves + wave;
     float *lt = reinterpret_cast<float *>(smem) + (size_t)wave * E;
-    int *scratch = reinterpret_cast<int *>(reinterpret_cast<float *>(smem) + (size_t)kTopkWaves * E) + wave * 16;
     if (t >= p.T) return;  // whole wave leaves together; no workgroup barrier follows
     for (int e = lane; e < E; e += kWave) lt[e] = p.logits[(size_t)t * E + e];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    wave_topk(lt, E, K, p.idx + (size_t)t * K, p.w + (size_t)t * K, scratch);
+    wave_topk(lt, E, K, p.idx + (size_t)t * K, p.w + (size_t)t * K);
     if (lane == 0 && p.gamma) p.gamma[t] = p.sgate ? 1.0f / (1.0f + expf(-p.gate[t])) : 0.0f;
 }
 
@@ -532,7 +531,7 @@ hipError_t launch_router_topk(const BatchedParams &p, hipStream_t stream) {
                        stream, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const size_t lds = sizeof(float) * (size_t)kTopkWaves * p.E + sizeof(int) * kTopkWaves * 16;
+    const size_t lds = sizeof(float) * (size_t)kTopkWaves * p.E;
     hipLaunchKernelGGL(topk_kernel, dim3((p.T + kTopkWaves - 1) / kTopkWaves), dim3(kTopkWaves * kWave), lds, stream,
                        p);
     return hipGetLastError();

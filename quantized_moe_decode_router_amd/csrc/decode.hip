@@ -8,132 +8,238 @@
 // the current epoch in a word has that word's value, so no grid barrier, no cache-maintenance
 // fence and no separate flag is needed, and each workgroup waits only for the words it reads.
 //
-// Per layer and workgroup b:
-//   R  (after x is known) router logits of the experts e = b (mod grid) [+ the shared-gate row E]
-//      and gate|up + SwiGLU of the shared expert's pairs j = b (mod grid)  -> logits, shared h
-//   G  every workgroup reads all E logits, ranks them (logit desc, index asc) and keeps the top-k
-//      with renormalised weights; then issues the loads of its share of the routed gate|up rows
-//      and of its routed down rows together, computes gate|up + SwiGLU -> routed h; then the
-//      shared expert's down projection for its rows of y
-//   D  reads the routed h of every (token, slot), computes its rows of every routed down
-//      projection from the already-loaded codes and combines them in a fixed order
-//      (k = 0..K-1, then the shared expert) -> y
-// Between layers each workgroup recomputes the same RMS-normalised bf16 input from all of y.
+// Per layer and workgroup b (grid = number of CUs):
+//   input   x of every token: x_in, or the RMS glue of all of y_{l-1} (chained stacks)
+//   R       router rows e = b (mod grid) [row E = the shared-expert gate] and the shared
+//           expert's gate|up pairs j = b (mod grid), both from LDS (staged during the previous
+//           layer) -> logit words, shared h words
+//   G       all logits -> top-k by rank counting (identical in every workgroup) -> this
+//           workgroup's share of the flattened (token, slot, j) routed gate|up pairs, loaded
+//           straight into registers -> routed h words
+//   D       per token: all K routed h vectors and the shared h -> the workgroup's H/grid rows of
+//           every routed down projection (rows staged into LDS while h is in flight) and of the
+//           shared one -> fixed-order combine (k = 0..K-1, then the shared expert) -> y
+// Weights that do not depend on the routing (router rows, shared expert rows) are copied into
+// LDS by the LDS-DMA form of the global load (global_load_lds_dwordx4 / _dword) while the
+// workgroup waits for an exchange, so they cost neither registers nor time on the chain.
 //
 // Quantised rows are split into 32-column slices (16 bytes of 4-bit or 32 bytes of 8-bit codes,
-// always inside one 64-column quantisation group); lane l of a wave always takes slice l % SPR of
-// its row (SPR = slices per row), so its slice of the activation vector stays in registers as
-// bf16 pairs. Codes become the bf16 values 128 + nibble with one v_and_or (exact), feed
-// v_dot2_f32_bf16 against the bf16 activations (products exact, fp32 sums), and the 128 * sum(x)
-// offset folds into the group bias: s * sum(q x) + b * sum(x) = s * sum((128+q) x) + (b - 128 s) * sum(x).
-// The fp32 h of the down projection is split into bf16 hi + lo halves (16 significant bits).
-// All address arithmetic into the weights is 64-bit.
+// always inside one 64-column quantisation group). Codes become the bf16 values 128 + nibble with
+// one v_and_or (exact), feed v_dot2_f32_bf16 against bf16 activations (products exact, fp32
+// sums), and the zero point folds into the group bias (see SliceRef). The fp32 h of the down
+// projection is split into bf16 hi + lo halves (16 significant bits). All address arithmetic
+// into the weights is 64-bit.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
 namespace moe {
 
 constexpr int kWaves = kDecodeThreads / kWave;  // 8
-constexpr int kMaxWL = 4;                       // gate|up wave-loads of codes a wave holds at once
-constexpr int kDnWL = 2;                        // down-projection wave-loads a wave holds at once
-constexpr int kShWL = 2;                        // shared gate|up wave-loads prefetched per wave
+constexpr int kGuWL = 4;                        // routed gate|up wave-loads a wave holds at once
 constexpr uint32_t kMagic = 0x43004300u;        // bf16 pair (128, 128)
-constexpr int kGatherWords = 8;                 // exchange words one thread waits for at once
+constexpr int kMaxGather = 16;                  // exchange words one thread waits for at once
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
                                            false);
 }
 
+// Global-memory view of a pointer. The parameter block is re-read word by word inside the layer
+// loop (see fresh_params), which hides from the compiler that its pointers are global; accesses
+// through G() stay global loads and stores instead of flat ones (a flat access counts against the
+// LDS wait counter too, which would couple every LDS wait to outstanding global loads).
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T *G(T *p) {
+    return (__attribute__((address_space(1))) T *)p;
+}
+
 // ---- exchange words ---------------------------------------------------------------------------
 __device__ __forceinline__ void ll_put(uint64_t *p, float v, uint32_t ep) {
     const uint64_t w = (static_cast<uint64_t>(ep) << 32) | __float_as_uint(v);
-    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(G(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t ll_get(const uint64_t *p) {
-    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(G(const_cast<uint64_t *>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int status_of(const int *ctrl) {
-    return __hip_atomic_load(const_cast<int *>(ctrl), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(G(const_cast<int *>(ctrl)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void fail(int *ctrl) {
-    __hip_atomic_store(ctrl, 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(G(ctrl), 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait until words src[0..n) (n <= kGatherWords * 512) carry epoch ep and copy their values to dst (LDS).
-// Called by the whole workgroup. All of a thread's loads are in flight together; only the words
-// not yet current are polled again. Returns false on timeout or when any workgroup has failed.
+// Wait until words src[0..n) carry epoch ep and copy their values into LDS: word i goes to
+// dst[i] (PAD = false) or to dst[i + 4 (i / 32)] (PAD = true: 36-word stride per 32 words).
+// Called by the whole workgroup; n may be any size (passes of kMaxGather words per thread). All of
+// a pass's loads are in flight together; only words not yet current are polled again.
+// Returns false on timeout or when any workgroup has failed.
+template <bool PAD>
 __device__ bool ll_gather(const uint64_t *src, int n, uint32_t ep, float *dst, int *ctrl, unsigned spin) {
-    constexpr int kMax = kGatherWords;
+    constexpr int kPass = kMaxGather * kDecodeThreads;
     const int tid = threadIdx.x;
-    uint32_t pending = 0;
-#pragma unroll
-    for (int k = 0; k < kMax; ++k)
-        if (tid + k * kDecodeThreads < n) pending |= 1u << k;
     bool ok = true;
-    unsigned it = 0;
-    while (pending) {
-        uint64_t w[kMax];
+    for (int base = 0; base < n && ok; base += kPass) {
+        const int m = min(n - base, kPass);
+        uint32_t pending = 0;
 #pragma unroll
-        for (int k = 0; k < kMax; ++k) {
-            const int i = tid + k * kDecodeThreads;
-            w[k] = ((pending >> k) & 1u) ? ll_get(src + i) : 0;
-        }
+        for (int k = 0; k < kMaxGather; ++k)
+            if (tid + k * kDecodeThreads < m) pending |= 1u << k;
+        unsigned it = 0;
+        while (pending) {
+            uint64_t w[kMaxGather];
 #pragma unroll
-        for (int k = 0; k < kMax; ++k) {
-            if (((pending >> k) & 1u) && static_cast<uint32_t>(w[k] >> 32) == ep) {
-                dst[tid + k * kDecodeThreads] = __uint_as_float(static_cast<uint32_t>(w[k]));
-                pending &= ~(1u << k);
+            for (int k = 0; k < kMaxGather; ++k)
+                w[k] = ((pending >> k) & 1u) ? ll_get(src + base + tid + k * kDecodeThreads) : 0;
+#pragma unroll
+            for (int k = 0; k < kMaxGather; ++k) {
+                if (((pending >> k) & 1u) && static_cast<uint32_t>(w[k] >> 32) == ep) {
+                    const int i = base + tid + k * kDecodeThreads;
+                    dst[PAD ? i + 4 * (i >> 5) : i] = __uint_as_float(static_cast<uint32_t>(w[k]));
+                    pending &= ~(1u << k);
+                }
             }
+            if (!pending) break;
+            if (++it > spin) { fail(ctrl); ok = false; break; }
+            if ((it & 31u) == 0 && status_of(ctrl) != 0) { ok = false; break; }
+            __builtin_amdgcn_s_sleep(1);
         }
-        if (!pending) break;
-        if (++it > spin) { fail(ctrl); ok = false; break; }
-        if ((it & 31u) == 0 && status_of(ctrl) != 0) { ok = false; break; }
-        __builtin_amdgcn_s_sleep(1);
     }
     // workgroup-wide AND of ok through LDS (slots written, read, then released again)
-    __shared__ int vote[kDecodeThreads / kWave];
+    __shared__ int vote[kWaves];
     const unsigned long long bad = __ballot(!ok);
     if ((threadIdx.x % kWave) == 0) vote[threadIdx.x / kWave] = bad ? 0 : 1;
     lds_barrier();
     int all = 1;
 #pragma unroll
-    for (int w = 0; w < kDecodeThreads / kWave; ++w) all &= vote[w];
+    for (int w = 0; w < kWaves; ++w) all &= vote[w];
     lds_barrier();
     return all != 0;
 }
 
+// ---- LDS DMA ------------------------------------------------------------------------------------
+// The LDS-DMA form of the global load writes lane l's 16 (or 4) bytes to LDS address
+// M0 + 16 l (4 l), M0 wave-uniform. It is issued from inline assembly so that the compiler does
+// not treat it as an LDS store it must wait for at every barrier; every consumer therefore waits
+// explicitly (dma_wait: all of this wave's vector-memory loads, then a workgroup barrier).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    // a generic pointer into LDS converted to its 32-bit LDS address (address space 3)
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char *)p));
+}
+__device__ __forceinline__ void dma16(const void *g, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void *g, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most n of this wave's vector-memory loads are outstanding (n wave-uniform). Loads
+// complete in issue order, so this waits for everything issued before the last n loads; values
+// of n above 15 wait for more than needed (still correct).
+__device__ __forceinline__ void dma_wait_but(int n) {
+    switch (n < 0 ? 0 : (n > 15 ? 15 : n)) {
+        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+        case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+        case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+        case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+        case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+        case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+        case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+        case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+        case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+        case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
+        case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+    }
+}
+
+// Copy n rows of `bytes` bytes each (a power of two, a multiple of U = 16 or 4; src_of(r) aligned
+// to U) into LDS at dst + r * bytes. Unit u = r * (bytes / U) + c is lane u % 64 of instruction
+// u / 64; wave w issues instructions w, w + 8, ...
+template <int U, typename SrcOf>
+__device__ __forceinline__ void dma_rows(int n, int bytes, SrcOf src_of, char *dst) {
+    const int sh = __builtin_ctz(static_cast<unsigned>(bytes / U)), total = n << sh;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    for (int i = wave; i * kWave < total; i += kWaves) {
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(dst + (size_t)i * kWave * U));
+        const int u = i * kWave + lane;
+        if (u < total) {
+            const int r = u >> sh, c = u & ((1 << sh) - 1);
+            const char *g = src_of(r) + (size_t)c * U;
+            if constexpr (U == 16) dma16(g, m0);
+            else dma4(g, m0);
+        }
+    }
+}
+
+// DMA instructions this wave issues in dma_rows for `total` units (instruction i goes to wave i % 8).
+__device__ __forceinline__ int dma_count(int total) {
+    const int wave = threadIdx.x / kWave, n = (total + kWave - 1) / kWave;
+    return n > wave ? (n - wave + kWaves - 1) / kWaves : 0;
+}
+
+// Rows of a quantised matrix staged in LDS: codes [n][cb], scales [n][sb], biases [n][sb].
+struct Rows {
+    char *c, *s, *b;
+    int cb, sb;
+};
+__device__ __forceinline__ Rows rows_at(char *base, int n, int cols, int bits) {
+    const int cb = cols * bits / 8, sb = cols / 32;
+    return Rows{base, base + (size_t)n * cb, base + (size_t)n * (cb + sb), cb, sb};
+}
+// DMA instructions this wave issues in dma_qrows for n rows of `cols` columns.
+__device__ __forceinline__ int dma_qrows_count(int n, int cols, int bits) {
+    return dma_count(n * (cols * bits / 8) / 16) + 2 * dma_count(n * (cols / 32) / 4);
+}
+// Stage n rows; row r of the matrix family q is matrix row row_of(r) (64-bit), cols columns.
+template <typename RowOf>
+__device__ __forceinline__ void dma_qrows(const QMat &q, int cols, int bits, int n, RowOf row_of, const Rows &dst) {
+    const size_t cb = (size_t)cols * bits / 8, gpr = cols / 64;
+    dma_rows<16>(n, dst.cb, [&](int r) { return reinterpret_cast<const char *>(q.c + row_of(r) * cb); }, dst.c);
+    dma_rows<4>(n, dst.sb, [&](int r) { return reinterpret_cast<const char *>(q.s + row_of(r) * gpr); }, dst.s);
+    dma_rows<4>(n, dst.sb, [&](int r) { return reinterpret_cast<const char *>(q.b + row_of(r) * gpr); }, dst.b);
+}
+
 // ---- slice dot products -------------------------------------------------------------------------
+// Each product chain is split into four independent accumulators (one per code dword, or per
+// dword mod 4), summed in a fixed order at the end: a single chain is bound by the latency of
+// v_dot2 (about 9 cycles per step), four interleaved chains by its issue rate.
 // 4-bit slice: 16 bytes = 32 codes; dword d holds columns 8d..8d+7 (nibble i = column 8d+i).
-// xp[4d+p] = bf16 pair (x[8d+p], x[8d+p+4]). Returns acc + sum((128+q) x).
-__device__ __forceinline__ float slice_dot4(const uint4 c, const uint32_t *xp, float acc) {
+// xp[4d+p] = bf16 pair (x[8d+p], x[8d+p+4]). a[d] += sum over dword d of (128+q) x.
+__device__ __forceinline__ void slice_dot4(const uint4 c, const uint32_t *xp, float (&a)[4]) {
     const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         const uint32_t w = wd[d];
-        acc = dot2((w & 0x000F000Fu) | kMagic, xp[4 * d + 0], acc);
-        acc = dot2(((w >> 4) & 0x000F000Fu) | kMagic, xp[4 * d + 1], acc);
-        acc = dot2(((w >> 8) & 0x000F000Fu) | kMagic, xp[4 * d + 2], acc);
-        acc = dot2(((w >> 12) & 0x000F000Fu) | kMagic, xp[4 * d + 3], acc);
+        a[d] = dot2((w & 0x000F000Fu) | kMagic, xp[4 * d + 0], a[d]);
+        a[d] = dot2(((w >> 4) & 0x000F000Fu) | kMagic, xp[4 * d + 1], a[d]);
+        a[d] = dot2(((w >> 8) & 0x000F000Fu) | kMagic, xp[4 * d + 2], a[d]);
+        a[d] = dot2(((w >> 12) & 0x000F000Fu) | kMagic, xp[4 * d + 3], a[d]);
     }
-    return acc;
 }
 // 8-bit slice: 32 bytes = 32 codes in two uint4; dword d holds columns 4d..4d+3.
 // xp[2d+p] = bf16 pair (x[4d+p], x[4d+p+2]). Each byte q = lo + 16 hi is split into nibbles:
-// lo += sum((128+lo) x), hi += sum((128+hi) x).
-__device__ __forceinline__ void slice_dot8(const uint4 c0, const uint4 c1, const uint32_t *xp, float &lo, float &hi) {
+// lo[d % 4] += sum((128+lo) x), hi[d % 4] += sum((128+hi) x).
+__device__ __forceinline__ void slice_dot8(const uint4 c0, const uint4 c1, const uint32_t *xp, float (&lo)[4],
+                                           float (&hi)[4]) {
     const uint32_t wd[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
         const uint32_t w = wd[d];
-        lo = dot2((w & 0x000F000Fu) | kMagic, xp[2 * d + 0], lo);
-        lo = dot2(((w >> 8) & 0x000F000Fu) | kMagic, xp[2 * d + 1], lo);
-        hi = dot2(((w >> 4) & 0x000F000Fu) | kMagic, xp[2 * d + 0], hi);
-        hi = dot2(((w >> 12) & 0x000F000Fu) | kMagic, xp[2 * d + 1], hi);
+        const int j = d & 3;
+        lo[j] = dot2((w & 0x000F000Fu) | kMagic, xp[2 * d + 0], lo[j]);
+        lo[j] = dot2(((w >> 8) & 0x000F000Fu) | kMagic, xp[2 * d + 1], lo[j]);
+        hi[j] = dot2(((w >> 4) & 0x000F000Fu) | kMagic, xp[2 * d + 0], hi[j]);
+        hi[j] = dot2(((w >> 12) & 0x000F000Fu) | kMagic, xp[2 * d + 1], hi[j]);
     }
 }
+__device__ __forceinline__ float sum4(const float (&a)[4]) { return (a[0] + a[1]) + (a[2] + a[3]); }
 
 // Column (within a 32-column slice) of the two halves of pair slot q.
 template <int BITS>
@@ -144,10 +250,20 @@ template <int BITS>
 __device__ __forceinline__ int pair_col_b(int q) {
     return pair_col_a<BITS>(q) + (BITS == 4 ? 4 : 2);
 }
+// Inverse: pair slot and half (0 = low 16 bits) holding column c of a slice.
+template <int BITS>
+__device__ __forceinline__ void col_pair(int c, int &q, int &half) {
+    if constexpr (BITS == 4) {
+        q = 4 * (c >> 3) + (c & 3);
+        half = (c >> 2) & 1;
+    } else {
+        q = 2 * (c >> 2) + (c & 1);
+        half = (c >> 1) & 1;
+    }
+}
 
 // Codes of one lane for one row slice (16 bytes at 4-bit, 32 at 8-bit) and its group's scale and
-// bias bf16 bit patterns, held exactly as loaded: no arithmetic touches them until the math, so
-// the loads of many rows stay in flight together instead of each waiting for its own scale.
+// bias bf16 bit patterns, read from a row set staged in LDS.
 template <int BITS>
 struct SliceCodes;
 template <>
@@ -161,13 +277,12 @@ struct SliceCodes<8> {
     uint32_t s16, b16;
 };
 template <int BITS>
-__device__ __forceinline__ void load_slice(SliceCodes<BITS> &sc, const uint8_t *crow, const uint16_t *srow,
-                                           const uint16_t *brow, int slice) {
-    const uint4 *cp = reinterpret_cast<const uint4 *>(crow + (size_t)slice * (BITS == 4 ? 16 : 32));
+__device__ __forceinline__ void lds_slice(SliceCodes<BITS> &sc, const Rows &R, int row, int slice) {
+    const uint4 *cp = reinterpret_cast<const uint4 *>(R.c + (size_t)row * R.cb + slice * (BITS == 4 ? 16 : 32));
     sc.c0 = cp[0];
     if constexpr (BITS == 8) sc.c1 = cp[1];
-    sc.s16 = srow[slice >> 1];
-    sc.b16 = brow[slice >> 1];
+    sc.s16 = reinterpret_cast<const uint16_t *>(R.s + (size_t)row * R.sb)[slice >> 1];
+    sc.b16 = reinterpret_cast<const uint16_t *>(R.b + (size_t)row * R.sb)[slice >> 1];
 }
 template <int BITS>
 __device__ __forceinline__ float sc_scale(const SliceCodes<BITS> &sc) { return __uint_as_float(sc.s16 << 16); }
@@ -184,10 +299,10 @@ __device__ __forceinline__ float sc_bias(const SliceCodes<BITS> &sc) { return __
 struct SliceRef {
     float sum, z0, z1;
 };
-constexpr uint32_t kZero4 = 0x43084308u;  // bf16 pair (136, 136) = 128 + 8
+static_assert(sizeof(SliceRef) == 12, "LDS plan assumes 12-byte slice constants");
 template <int BITS>
 __device__ __forceinline__ SliceRef slice_ref(const uint32_t *vp, int npass, const uint32_t *vp2) {
-    // npass = 1: one pair set; npass = 2: chain continues over a second pair set (hi then lo)
+    // npass = 1: one pair set; npass = 2: the chains continue over a second pair set (hi then lo)
     SliceRef r;
     float sum = 0.0f;
     const uint32_t *sets[2] = {vp, vp2};
@@ -197,47 +312,49 @@ __device__ __forceinline__ SliceRef slice_ref(const uint32_t *vp, int npass, con
     r.sum = sum;
     if constexpr (BITS == 4) {
         const uint4 zc = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-        float acc = 0.0f;
-        for (int ps = 0; ps < npass; ++ps) acc = slice_dot4(zc, sets[ps], acc);
-        r.z0 = acc;
+        float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int ps = 0; ps < npass; ++ps) slice_dot4(zc, sets[ps], a);
+        r.z0 = sum4(a);
         r.z1 = 0.0f;
     } else {
         const uint4 zc = make_uint4(0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u);
-        float lo = 0.0f, hi = 0.0f;
+        float lo[4] = {0.0f, 0.0f, 0.0f, 0.0f}, hi[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int ps = 0; ps < npass; ++ps) slice_dot8(zc, zc, sets[ps], lo, hi);
-        r.z0 = lo;
-        r.z1 = hi;
+        r.z0 = sum4(lo);
+        r.z1 = sum4(hi);
     }
     return r;
 }
 // Partial row value of one lane: sum over its slice of (s q + b) v, with vp the slice's bf16
-// pairs of v and ref its SliceRef.
+// pairs of v and ref its SliceRef (the same chains as slice_ref, so zero-point rows give 0).
 template <int BITS>
 __device__ __forceinline__ float slice_value(const SliceCodes<BITS> &sc, const uint32_t *vp, const SliceRef &ref) {
     const float sv = sc_scale(sc), bv = sc_bias(sc);
     if constexpr (BITS == 4) {
-        const float acc = slice_dot4(sc.c0, vp, 0.0f);
-        return sv * (acc - ref.z0) + fmaf(8.0f, sv, bv) * ref.sum;
+        float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        slice_dot4(sc.c0, vp, a);
+        return sv * (sum4(a) - ref.z0) + fmaf(8.0f, sv, bv) * ref.sum;
     } else {
-        float lo = 0.0f, hi = 0.0f;
+        float lo[4] = {0.0f, 0.0f, 0.0f, 0.0f}, hi[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         slice_dot8(sc.c0, sc.c1, vp, lo, hi);
-        return sv * ((lo - ref.z0) + 16.0f * (hi - ref.z1)) + fmaf(128.0f, sv, bv) * ref.sum;
+        return sv * ((sum4(lo) - ref.z0) + 16.0f * (sum4(hi) - ref.z1)) + fmaf(128.0f, sv, bv) * ref.sum;
     }
 }
-// Same with v split into bf16 hi and lo pair sets (one chain over hi, then lo).
+// Same with v split into bf16 hi and lo pair sets (the chains run over hi, then lo).
 template <int BITS>
 __device__ __forceinline__ float slice_value2(const SliceCodes<BITS> &sc, const uint32_t *vhi, const uint32_t *vlo,
                                               const SliceRef &ref) {
     const float sv = sc_scale(sc), bv = sc_bias(sc);
     if constexpr (BITS == 4) {
-        float acc = slice_dot4(sc.c0, vhi, 0.0f);
-        acc = slice_dot4(sc.c0, vlo, acc);
-        return sv * (acc - ref.z0) + fmaf(8.0f, sv, bv) * ref.sum;
+        float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        slice_dot4(sc.c0, vhi, a);
+        slice_dot4(sc.c0, vlo, a);
+        return sv * (sum4(a) - ref.z0) + fmaf(8.0f, sv, bv) * ref.sum;
     } else {
-        float lo = 0.0f, hi = 0.0f;
+        float lo[4] = {0.0f, 0.0f, 0.0f, 0.0f}, hi[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         slice_dot8(sc.c0, sc.c1, vhi, lo, hi);
         slice_dot8(sc.c0, sc.c1, vlo, lo, hi);
-        return sv * ((lo - ref.z0) + 16.0f * (hi - ref.z1)) + fmaf(128.0f, sv, bv) * ref.sum;
+        return sv * ((sum4(lo) - ref.z0) + 16.0f * (sum4(hi) - ref.z1)) + fmaf(128.0f, sv, bv) * ref.sum;
     }
 }
 
@@ -247,28 +364,28 @@ __device__ __forceinline__ size_t expert_at(int e, int E) {
     return (size_t)min((unsigned)e, (unsigned)(E - 1));
 }
 
-// Sum over aligned groups of n lanes (n a power of two <= 64, runtime).
-__device__ __forceinline__ float seg_sum(float v, int n) {
-    for (int o = n >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
-
 // ---- layer pointers --------------------------------------------------------------------------
 struct LayerPtrs {
     const float *router, *rbias, *sgate;
     QMat w13, w2, s13, s2;
 };
 
+// Layer l's arrays: per-layer strides follow from the shape ([L]-stacked arrays, each layer one
+// contiguous block).
 __device__ __forceinline__ LayerPtrs layer_ptrs(const DecodeParams &p, int l) {
+    const size_t H = p.H, E = p.E, I = p.I, Is = p.Is, bits = p.bits, L = l;
     LayerPtrs q;
-    q.router = p.router + (size_t)l * p.ls_router;
-    q.rbias = p.rbias ? p.rbias + (size_t)l * p.ls_rbias : nullptr;
-    q.sgate = p.sgate ? p.sgate + (size_t)l * p.ls_sgate : nullptr;
-    q.w13 = {p.w13.c + (size_t)l * p.ls_w13c, p.w13.s + (size_t)l * p.ls_w13s, p.w13.b + (size_t)l * p.ls_w13s};
-    q.w2 = {p.w2.c + (size_t)l * p.ls_w2c, p.w2.s + (size_t)l * p.ls_w2s, p.w2.b + (size_t)l * p.ls_w2s};
-    if (p.Is) {
-        q.s13 = {p.s13.c + (size_t)l * p.ls_s13c, p.s13.s + (size_t)l * p.ls_s13s, p.s13.b + (size_t)l * p.ls_s13s};
-        q.s2 = {p.s2.c + (size_t)l * p.ls_s2c, p.s2.s + (size_t)l * p.ls_s2s, p.s2.b + (size_t)l * p.ls_s2s};
+    q.router = p.router + L * E * H;
+    q.rbias = p.rbias ? p.rbias + L * E : nullptr;
+    q.sgate = p.sgate ? p.sgate + L * H : nullptr;
+    const size_t w13c = E * 2 * I * H * bits / 8, w13s = E * 2 * I * H / 64;
+    const size_t w2c = E * H * I * bits / 8, w2s = E * H * I / 64;
+    q.w13 = {p.w13.c + L * w13c, p.w13.s + L * w13s, p.w13.b + L * w13s};
+    q.w2 = {p.w2.c + L * w2c, p.w2.s + L * w2s, p.w2.b + L * w2s};
+    if (Is) {
+        const size_t s13c = 2 * Is * H * bits / 8, s13s = 2 * Is * H / 64, s2c = H * Is * bits / 8, s2s = H * Is / 64;
+        q.s13 = {p.s13.c + L * s13c, p.s13.s + L * s13s, p.s13.b + L * s13s};
+        q.s2 = {p.s2.c + L * s2c, p.s2.s + L * s2s, p.s2.b + L * s2s};
     } else {
         q.s13 = {nullptr, nullptr, nullptr};
         q.s2 = {nullptr, nullptr, nullptr};
@@ -276,113 +393,169 @@ __device__ __forceinline__ LayerPtrs layer_ptrs(const DecodeParams &p, int l) {
     return q;
 }
 
-// ---- LDS layout --------------------------------------------------------------------------------
+// The kernel's parameter block, re-read from the kernel-argument segment (scalar loads) through a
+// pointer the compiler cannot prove invariant: without it every field would be hoisted out of
+// the layer loop and held in scalar registers for the whole kernel.
+__device__ __forceinline__ DecodeParams fresh_params() {
+    typedef const __attribute__((address_space(4))) uint32_t *KP;
+    static_assert(sizeof(DecodeParams) % 4 == 0, "parameter block is copied in 32-bit words");
+    uint64_t a = reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr());
+    asm volatile("" : "+s"(a));
+    const KP src = reinterpret_cast<KP>(a);
+    DecodeParams out;
+    uint32_t *dst = reinterpret_cast<uint32_t *>(&out);
+#pragma unroll
+    for (size_t i = 0; i < sizeof(DecodeParams) / 4; ++i) dst[i] = src[i];
+    return out;
+}
+
+// ---- LDS ---------------------------------------------------------------------------------------
 // Pair tables are stored per 32-column slice with 4 dwords of padding (20 or 36 dwords per slice)
 // so that lanes reading consecutive slices with 16-byte loads spread over the banks.
 struct Lds {
-    uint16_t *xb;   // [T][H] bf16 input of the layer
-    uint32_t *xp;   // [T][H/32][20] bf16 pairs of x (16 used)
-    SliceRef *xref; // [T][H/32] per-slice constants of x
-    float *fbuf;    // gathered words / per-row results: max(H, K*I, T*Is, grid) floats
-    uint32_t *hp;   // [max(K,T)][Imax/32][36] bf16 hi pairs (16), lo pairs (16), padding
-    SliceRef *href; // [max(K,T)][Imax/32] per-slice constants of h (hi then lo)
-    float *lg;      // [T][E+1]
-    int *sidx;      // [T][K]
-    float *sw;      // [T][K]
-    float *gam;     // [T]
-    float *rowv;    // [kRowv] row results of one gate|up batch
-    float *part;    // [T][K+1][RB] down-projection rows of this workgroup (slot K = shared)
-    float *red;     // [T * kMaxRR * kWaves] block-reduction scratch
-    int *tks;       // [kWaves][32] top-k scratch, one slice per wave
+    uint32_t *xp;    // [T][H/32][20] bf16 pairs of x (16 used)
+    SliceRef *xref;  // [T][H/32]
+    float *lg;       // [T][E+1] logits (column E = shared-gate logit)
+    int *sidx;       // [T][K]
+    float *sw;       // [T][K]
+    float *gam;      // [T]
+    float *rt;       // [nrr][H] router rows, chunk-transposed (see stage_router)
+    char *sg;        // shared gate|up rows (pairs of this workgroup), staged
+    char *sd;        // shared down rows of this workgroup, staged
+    char *rd;        // routed down rows of this workgroup for one token, staged
+    char *rg;        // routed gate|up rows of one chunk of this workgroup's pairs, staged
+    uint32_t *hp;    // [(K*I + Is)/32][36] h of one token: gathered fp32, then bf16 hi (16) + lo (16) pairs
+    SliceRef *href;  // [(K*I + Is)/32]
+    float *part;     // [T][K+1][RB] down-projection rows of this workgroup (slot K = shared)
+    float *red;      // [64] reduction scratch
 };
-constexpr int kRowv = kWaves * kMaxWL * 8;  // rows per wave-load <= 8 since H >= 256
-constexpr int kMaxRR = 3;                   // router rows per workgroup: (E + 1) / grid <= 3
-constexpr int kMaxQ = 1;                    // float4 of a router row per thread: H / 4 <= 512
-
-__host__ __device__ inline size_t lds_offsets(int T, int H, int E, int K, int I, int Is, int RB, size_t *o) {
-    const int Imax = I > Is ? I : Is;
-    const int nh = K > T ? K : T;
-    size_t fb = (size_t)H;
-    if ((size_t)K * I > fb) fb = (size_t)K * I;
-    if ((size_t)T * Is > fb) fb = (size_t)T * Is;
-    if ((size_t)T * (K + 1) * RB > fb) fb = (size_t)T * (K + 1) * RB;
-    if (fb < kMaxGrid) fb = kMaxGrid;
-    size_t off = 0;
-    const size_t sz[14] = {2 * (size_t)T * H,
-                           4 * (size_t)T * (H / 32) * 20,
-                           sizeof(SliceRef) * (size_t)T * (H / 32),
-                           4 * fb,
-                           4 * (size_t)nh * (Imax / 32) * 36,
-                           sizeof(SliceRef) * (size_t)nh * (Imax / 32),
-                           4 * (size_t)T * (E + 1),
-                           4 * (size_t)T * K,
-                           4 * (size_t)T * K,
-                           4 * (size_t)T,
-                           4 * (size_t)kRowv,
-                           4 * (size_t)T * (K + 1) * RB,
-                           4 * (size_t)T * kMaxRR * kWaves,
-                           4 * (size_t)kWaves * 32};
-    for (int i = 0; i < 14; ++i) {
-        o[i] = off;
-        off = align_up(off + sz[i], 16);
-    }
-    return off;
-}
-
 __device__ __forceinline__ Lds carve(const DecodeParams &p, char *smem) {
-    size_t o[14];
-    lds_offsets(p.T, p.H, p.E, p.K, p.I, p.Is, p.rows_per_wg, o);
+    const DecodeLds &o = p.lds;
     Lds s;
-    s.xb = reinterpret_cast<uint16_t *>(smem + o[0]);
-    s.xp = reinterpret_cast<uint32_t *>(smem + o[1]);
-    s.xref = reinterpret_cast<SliceRef *>(smem + o[2]);
-    s.fbuf = reinterpret_cast<float *>(smem + o[3]);
-    s.hp = reinterpret_cast<uint32_t *>(smem + o[4]);
-    s.href = reinterpret_cast<SliceRef *>(smem + o[5]);
-    s.lg = reinterpret_cast<float *>(smem + o[6]);
-    s.sidx = reinterpret_cast<int *>(smem + o[7]);
-    s.sw = reinterpret_cast<float *>(smem + o[8]);
-    s.gam = reinterpret_cast<float *>(smem + o[9]);
-    s.rowv = reinterpret_cast<float *>(smem + o[10]);
-    s.part = reinterpret_cast<float *>(smem + o[11]);
-    s.red = reinterpret_cast<float *>(smem + o[12]);
-    s.tks = reinterpret_cast<int *>(smem + o[13]);
+    s.xp = reinterpret_cast<uint32_t *>(smem + o.xp);
+    s.xref = reinterpret_cast<SliceRef *>(smem + o.xref);
+    s.lg = reinterpret_cast<float *>(smem + o.lg);
+    s.sidx = reinterpret_cast<int *>(smem + o.sidx);
+    s.sw = reinterpret_cast<float *>(smem + o.sw);
+    s.gam = reinterpret_cast<float *>(smem + o.gam);
+    s.rt = reinterpret_cast<float *>(smem + o.rt);
+    s.sg = smem + o.sg;
+    s.sd = smem + o.sd;
+    s.rd = smem + o.rd;
+    s.rg = smem + o.rg;
+    s.hp = reinterpret_cast<uint32_t *>(smem + o.hp);
+    s.href = reinterpret_cast<SliceRef *>(smem + o.href);
+    s.part = reinterpret_cast<float *>(smem + o.part);
+    s.red = reinterpret_cast<float *>(smem + o.red);
     return s;
 }
 
-// Build the bf16 pair table and per-slice sums of x (from s.xb) for all T tokens.
-template <int BITS>
-__device__ void build_x_pairs(const DecodeParams &p, const Lds &s) {
-    const int H = p.H, T = p.T, nsl = H / 32;
-    for (int i = threadIdx.x; i < T * nsl * 16; i += blockDim.x) {
-        const int t = i / (nsl * 16), r = i - t * nsl * 16, sl = r >> 4, q = r & 15;
-        const uint16_t *xr = s.xb + t * H + sl * 32;
-        const uint32_t a = xr[pair_col_a<BITS>(q)], c = xr[pair_col_b<BITS>(q)];
-        s.xp[(t * nsl + sl) * 20 + q] = a | (c << 16);
-    }
-    lds_barrier();
-    for (int i = threadIdx.x; i < T * nsl; i += blockDim.x) {
-        uint32_t v[16];
-        for (int q = 0; q < 16; ++q) v[q] = s.xp[i * 20 + q];
-        s.xref[i] = slice_ref<BITS>(v, 1, v);
-    }
-    lds_barrier();
+// What this workgroup b owns, computed once per call (integer divisions by the grid included):
+//   rows r0 .. r0 + nr - 1 of y (nrm = div_magic(nr)); nrr router rows e = b + r * grid <= E (row E
+//   only with a shared expert); nps shared pairs j = b + r * grid < Is; routed gate|up pairs
+//   [q0, q1) of the T*K*I flattened (token, slot, j) pairs.
+struct WgShare {
+    int r0, nr, nrr, nps, q0, q1;
+    uint32_t nrm;
+};
+__device__ __forceinline__ WgShare wg_share(const DecodeParams &p) {
+    WgShare w;
+    const int b = blockIdx.x, g = gridDim.x;
+    w.r0 = b * p.rows_per_wg;
+    w.nr = w.r0 >= p.H ? 0 : min(p.rows_per_wg, p.H - w.r0);
+    w.nrm = div_magic(static_cast<uint32_t>(w.nr));
+    const int n = p.E + (p.Is ? 1 : 0);
+    w.nrr = b < n ? min(p.nrr, (n - 1 - b) / g + 1) : 0;
+    w.nps = (p.Is && b < p.Is) ? min(p.nps, (p.Is - 1 - b) / g + 1) : 0;
+    const unsigned long long total = (unsigned long long)p.T * p.K * p.I;
+    w.q0 = (int)(total * b / g);
+    w.q1 = (int)(total * (b + 1) / g);
+    return w;
 }
 
-// Input of layer l into s.xb: x_in for l == 0 (or unchained), else the RMS glue of y_{l-1}:
-// x = bf16_rne(y / sqrt(mean(y^2) + eps)). Every workgroup computes the same bits.
+// ---- staging of the weights that do not depend on routing ----------------------------------------
+// Router rows are stored chunk-transposed: 16-byte chunk k (k < 8) of 32-column slice sl of a row
+// goes to chunk position k * (H/32) + sl, so that lane sl reading its k-th chunk is one
+// conflict-free 16-byte LDS read per wave.
+__device__ __forceinline__ void stage_router(const DecodeParams &p, int l, const Lds &s, const WgShare &w) {
+    const LayerPtrs L = layer_ptrs(p, l);
+    const int nr = w.nrr, H = p.H, nsl = H / 32, b = blockIdx.x, g = gridDim.x;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int cs = __builtin_ctz(static_cast<unsigned>(H / 4)), ss = __builtin_ctz(static_cast<unsigned>(nsl));
+    const int total = nr << cs;  // 16-byte chunks
+    for (int i = wave; i * kWave < total; i += kWaves) {
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(s.rt + (size_t)i * kWave * 4));
+        const int u = i * kWave + lane;
+        if (u < total) {
+            const int r = u >> cs, pos = u & ((1 << cs) - 1);
+            const int k = pos >> ss, sl = pos & (nsl - 1);
+            const int e = b + r * g;
+            const float *row = e < p.E ? L.router + (size_t)e * H : L.sgate;
+            dma16(row + sl * 32 + k * 4, m0);
+        }
+    }
+}
+__device__ __forceinline__ Rows sg_rows(const DecodeParams &p, const Lds &s) {
+    return rows_at(s.sg, 2 * p.nps, p.H, p.bits);
+}
+__device__ __forceinline__ Rows sd_rows(const DecodeParams &p, const Lds &s) {
+    return rows_at(s.sd, p.rows_per_wg, p.Is, p.bits);
+}
+__device__ __forceinline__ Rows rd_rows(const DecodeParams &p, const Lds &s) {
+    return rows_at(s.rd, p.K * p.rows_per_wg, p.I, p.bits);
+}
+// Shared gate|up rows of this workgroup's pairs: staged row 2r = gate row j, 2r+1 = up row Is + j,
+// j = b + r * grid.
+__device__ __forceinline__ void stage_shared_gu(const DecodeParams &p, int l, const Lds &s, const WgShare &w) {
+    const int np = w.nps, b = blockIdx.x, g = gridDim.x, Is = p.Is;
+    if (np == 0) return;
+    const LayerPtrs L = layer_ptrs(p, l);
+    dma_qrows(L.s13, p.H, p.bits, 2 * np,
+              [&](int r) -> size_t { return (size_t)((r & 1) * Is + b + (r >> 1) * g); }, sg_rows(p, s));
+}
+__device__ __forceinline__ void stage_shared_down(const DecodeParams &p, int l, const Lds &s, int r0, int nr) {
+    if (!p.Is || nr <= 0) return;
+    const LayerPtrs L = layer_ptrs(p, l);
+    dma_qrows(L.s2, p.Is, p.bits, nr, [&](int r) -> size_t { return (size_t)(r0 + r); }, sd_rows(p, s));
+}
+// Routed down rows r0..r0+nr-1 of token t's K experts: staged row k * nr + rl.
+__device__ __forceinline__ void stage_routed_down(const DecodeParams &p, int l, const Lds &s, int t, int r0,
+                                                  int nr, uint32_t nrm) {
+    if (nr <= 0) return;
+    const LayerPtrs L = layer_ptrs(p, l);
+    const int K = p.K, E = p.E;
+    const size_t H = p.H;
+    dma_qrows(L.w2, p.I, p.bits, K * nr,
+              [&](int r) -> size_t {
+                  const int k = div_by(r, nrm), rl = r - k * nr;
+                  return expert_at(s.sidx[t * K + k], E) * H + (size_t)(r0 + rl);
+              },
+              rd_rows(p, s));
+}
+
+// ---- layer input ---------------------------------------------------------------------------------
+// x of every token into the pair table s.xp (and its slice constants): x_in for l == 0 (or
+// unchained), else the RMS glue of y_{l-1}: x = bf16_rne(y / sqrt(mean(y^2) + eps)); every
+// workgroup computes the same bits.
 template <int BITS>
 __device__ bool layer_input(const DecodeParams &p, int l, uint32_t ep, const Lds &s) {
-    const int T = p.T, H = p.H;
+    const int T = p.T, H = p.H, nsl = H / 32;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     if (l == 0 || !p.chained) {
-        for (int i = threadIdx.x; i < T * H; i += blockDim.x) s.xb[i] = p.x_in[i];
+        for (int i = threadIdx.x; i < T * nsl * 16; i += blockDim.x) {
+            const int sh = __builtin_ctz(static_cast<unsigned>(nsl * 16));
+            const int t = i >> sh, r = i & ((nsl * 16) - 1), sl = r >> 4, q = r & 15;
+            const auto xr = G(p.x_in + (size_t)t * H + sl * 32);
+            const uint32_t a = xr[pair_col_a<BITS>(q)], c = xr[pair_col_b<BITS>(q)];
+            s.xp[(t * nsl + sl) * 20 + q] = a | (c << 16);
+        }
     } else {
         const uint64_t *ysrc = p.ll_y + (size_t)(l - 1) * T * H;
+        float *yb = reinterpret_cast<float *>(s.hp);
         for (int t = 0; t < T; ++t) {
-            if (!ll_gather(ysrc + (size_t)t * H, H, ep, s.fbuf, p.ctrl, p.spin_limit)) return false;
+            if (!ll_gather<false>(ysrc + (size_t)t * H, H, ep, yb, p.ctrl, p.spin_limit)) return false;
             float ss = 0.0f;
-            for (int h = threadIdx.x; h < H; h += blockDim.x) ss += s.fbuf[h] * s.fbuf[h];
+            for (int h = threadIdx.x; h < H; h += blockDim.x) ss += yb[h] * yb[h];
             ss = wave_sum(ss);
             if (lane == 0) s.red[wave] = ss;
             lds_barrier();
@@ -390,115 +563,155 @@ __device__ bool layer_input(const DecodeParams &p, int l, uint32_t ep, const Lds
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) ss += s.red[w];
             const float inv = 1.0f / sqrtf(ss / (float)H + p.eps);
-            for (int h = threadIdx.x; h < H; h += blockDim.x) s.xb[t * H + h] = f32_to_bf16_rne(s.fbuf[h] * inv);
+            for (int i = threadIdx.x; i < nsl * 16; i += blockDim.x) {
+                const int sl = i >> 4, q = i & 15;
+                const float *yr = yb + sl * 32;
+                const uint32_t a = f32_to_bf16_rne(yr[pair_col_a<BITS>(q)] * inv);
+                const uint32_t c = f32_to_bf16_rne(yr[pair_col_b<BITS>(q)] * inv);
+                s.xp[(t * nsl + sl) * 20 + q] = a | (c << 16);
+            }
             lds_barrier();
         }
     }
     lds_barrier();
     if (p.x_all && blockIdx.x == 0)
-        for (int i = threadIdx.x; i < T * H; i += blockDim.x) p.x_all[(size_t)l * T * H + i] = s.xb[i];
-    build_x_pairs<BITS>(p, s);
+        for (int i = threadIdx.x; i < T * H; i += blockDim.x) {
+            const int t = i >> __builtin_ctz(static_cast<unsigned>(H)), h = i & (H - 1), sl = h >> 5;
+            int q, half;
+            col_pair<BITS>(h & 31, q, half);
+            G(p.x_all)[(size_t)l * T * H + i] = static_cast<uint16_t>(s.xp[(t * nsl + sl) * 20 + q] >> (16 * half));
+        }
+    for (int i = threadIdx.x; i < T * nsl; i += blockDim.x) {
+        uint32_t v[16];
+        for (int q = 0; q < 16; ++q) v[q] = s.xp[i * 20 + q];
+        s.xref[i] = slice_ref<BITS>(v, 1, v);
+    }
+    lds_barrier();
     return true;
 }
 
-// Gate|up + SwiGLU for `npairs` row pairs. Pair i: gate row row_of(i, m) of matrix m, up row
-// gate row + inter, token tok_of(i); h = silu(gate) * up goes to the word dst_of(i).
-// Row slots 2i (gate) and 2i+1 (up) are processed rpw per wave-load, wave-loads round-robin over
-// the waves, in batches of kWaves * kMaxWL wave-loads whose loads are all issued before any math:
-// gu_load issues one batch's loads, gu_finish does its math and publishes its h.
-struct GuPlan {
-    int spr, rpw, nslots, nwl;
-};
-__device__ __forceinline__ GuPlan gu_plan(int H, int npairs) {
-    GuPlan g;
-    g.spr = H / 32;
-    g.rpw = kWave / g.spr;
-    g.nslots = 2 * npairs;
-    g.nwl = (g.nslots + g.rpw - 1) / g.rpw;
-    return g;
-}
-// A batch is kWaves * NK wave-loads; wave w takes wave-loads base + w + k * kWaves, k < NK.
-template <int BITS, int NK, typename RowOf>
-__device__ __forceinline__ void gu_load(const DecodeParams &p, const GuPlan &g, int base, int inter, RowOf row_of,
-                                        SliceCodes<BITS> *sc) {
+// ---- router --------------------------------------------------------------------------------------
+// (row r, token t) combinations round-robin over the waves; lane sl takes 32-column slice sl.
+template <int BITS>
+__device__ void router_logits(const DecodeParams &p, int l, const Lds &s, const WgShare &w, uint64_t *ll_lg,
+                              uint32_t ep) {
+    const float *rbias = p.rbias ? p.rbias + (size_t)l * p.E : nullptr;
+    const int T = p.T, H = p.H, E = p.E, nsl = H / 32, b = blockIdx.x, g = gridDim.x;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int H = p.H, seg = lane / g.spr, sl = lane % g.spr;
-    const size_t cpr = (size_t)H * BITS / 8;
+    const int nr = w.nrr;
+    for (int c = wave; c < nr * T; c += kWaves) {
+        const int r = div_by(c, p.tdiv), t = c - r * T;
+        const float4 *row = reinterpret_cast<const float4 *>(s.rt + (size_t)r * H);
+        float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int sl = lane; sl < nsl; sl += kWave) {
+            const uint32_t *xw = s.xp + (t * nsl + sl) * 20;
+            float rv[32];
 #pragma unroll
-    for (int k = 0; k < NK; ++k) {
-        const int wl = base + wave + k * kWaves;
-        const int slot = wl * g.rpw + seg;
-        if (wl < g.nwl && slot < g.nslots) {
-            QMat m;
-            const size_t row = row_of(slot >> 1, m) + (size_t)(slot & 1) * inter;
-            load_slice<BITS>(sc[k], m.c + row * cpr, m.s + row * (H / 64), m.b + row * (H / 64), sl);
-        }
-    }
-}
-template <int BITS, int NK, typename TokOf, typename DstOf>
-__device__ __forceinline__ void gu_finish(const DecodeParams &p, const Lds &s, const GuPlan &g, int base, int npairs,
-                                          const SliceCodes<BITS> *sc, TokOf tok_of, DstOf dst_of, uint32_t ep) {
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int seg = lane / g.spr, sl = lane % g.spr;
-#pragma unroll
-    for (int k = 0; k < NK; ++k) {
-        const int wl = base + wave + k * kWaves;
-        const int slot = wl * g.rpw + seg;
-        if (wl < g.nwl) {
-            float v = 0.0f;
-            if (slot < g.nslots) {
-                const int t = tok_of(slot >> 1);
-                v = slice_value<BITS>(sc[k], s.xp + (t * g.spr + sl) * 20, s.xref[t * g.spr + sl]);
+            for (int k = 0; k < 8; ++k) {
+                const float4 f = row[k * nsl + sl];
+                rv[4 * k] = f.x; rv[4 * k + 1] = f.y; rv[4 * k + 2] = f.z; rv[4 * k + 3] = f.w;
             }
-            v = seg_sum(v, g.spr);
-            if (sl == 0 && slot < g.nslots) s.rowv[slot - base * g.rpw] = v;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const uint32_t w = xw[q];
+                a4[q & 3] = fmaf(rv[pair_col_a<BITS>(q)], bf16_to_f32(w & 0xFFFF), a4[q & 3]);
+                a4[q & 3] = fmaf(rv[pair_col_b<BITS>(q)], bf16_to_f32(w >> 16), a4[q & 3]);
+            }
         }
-    }
-    lds_barrier();
-    const int lo = base * g.rpw / 2;
-    const int hi = min(npairs, (base + kWaves * NK) * g.rpw / 2);
-    for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
-        const float gv = s.rowv[2 * i - base * g.rpw], uv = s.rowv[2 * i + 1 - base * g.rpw];
-        ll_put(dst_of(i), silu(gv) * uv, ep);
-    }
-    lds_barrier();
-}
-// Batches from `first` on (the batches before it were handled by the caller).
-template <int BITS, typename RowOf, typename TokOf, typename DstOf>
-__device__ void gate_up_pairs(const DecodeParams &p, const Lds &s, int npairs, int inter, RowOf row_of,
-                              TokOf tok_of, DstOf dst_of, uint32_t ep, int first = 0) {
-    const GuPlan g = gu_plan(p.H, npairs);
-    for (int base = first; base < g.nwl; base += kWaves * kMaxWL) {
-        SliceCodes<BITS> sc[kMaxWL];
-        gu_load<BITS, kMaxWL>(p, g, base, inter, row_of, sc);
-        gu_finish<BITS, kMaxWL>(p, s, g, base, npairs, sc, tok_of, dst_of, ep);
+        float acc = wave_sum(sum4(a4));
+        if (lane == 0) {
+            const int e = b + r * g;
+            if (e < E && rbias) acc += G(rbias)[e];
+            ll_put(ll_lg + (size_t)t * (E + 1) + e, acc, ep);
+        }
     }
 }
 
-// Gather `nvec` h vectors of length len (vector v from src_of(v)) into the LDS pair table:
-// hp[v][slice][0..15] = bf16 hi pairs, [16..31] = bf16 lo pairs; href[v][slice] its constants.
-// src_of(v) must be contiguous in v with stride len (one gather covers them all).
-template <int BITS>
-__device__ bool stage_h(const DecodeParams &p, const Lds &s, const uint64_t *src, int nvec, int len, uint32_t ep) {
-    const int nsl = len / 32, n = nvec * len;
-    for (int c0 = 0; c0 < n; c0 += kGatherWords * kDecodeThreads)
-        if (!ll_gather(src + c0, min(n - c0, kGatherWords * kDecodeThreads), ep, s.fbuf + c0, p.ctrl, p.spin_limit))
-            return false;
-    for (int i = threadIdx.x; i < nvec * nsl * 16; i += blockDim.x) {
-        const int vs = i >> 4, q = i & 15;  // vs = v * nsl + slice
-        const float a = s.fbuf[vs * 32 + pair_col_a<BITS>(q)], c = s.fbuf[vs * 32 + pair_col_b<BITS>(q)];
-        const uint16_t ah = f32_to_bf16_rne(a), ch = f32_to_bf16_rne(c);
-        const uint16_t al = f32_to_bf16_rne(a - bf16_to_f32(ah)), cl = f32_to_bf16_rne(c - bf16_to_f32(ch));
-        uint32_t *dst = s.hp + (size_t)vs * 36;
-        dst[q] = (uint32_t)ah | ((uint32_t)ch << 16);
-        dst[16 + q] = (uint32_t)al | ((uint32_t)cl << 16);
+// ---- gate|up + SwiGLU ------------------------------------------------------------------------------
+// A pair is the gate row and the up row of one (token, expert, j). With H/32 = 64 slices per row
+// (wide rows) a pair is two wave-loads (gate, then up) and lane l takes slice l; with at most 32
+// slices a pair is one wave-load, lanes [0, spr) on the gate row and [spr, 2 spr) on the up row.
+// Wave w takes the contiguous pairs [np w / 8, np (w + 1) / 8), kGuWL wave-loads at a time: all of
+// a batch's loads are issued before any of its math.
+//   load(i, half, sc)   fetch this lane's slice of pair i's gate (half 0) or up (half 1) row
+//   tok_of(i)           token of pair i;   dst_of(i) its h word
+template <int BITS, typename Load, typename TokOf, typename DstOf>
+__device__ __forceinline__ void gate_up(const DecodeParams &p, const Lds &s, int np, Load load, TokOf tok_of,
+                                        DstOf dst_of, uint32_t ep) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int nsl = p.H / 32;
+    const bool wide = nsl == kWave;
+    const int spr = nsl;
+    const int half = wide ? 0 : lane / spr, sl = wide ? lane : lane % spr;
+    const bool active = wide || half < 2;
+    constexpr int kPPB = kGuWL / 2;  // pairs per batch for wide rows (kGuWL for narrow rows)
+    const int ppb = wide ? kPPB : kGuWL;
+    const int i0 = (int)((long long)np * wave / kWaves), i1 = (int)((long long)np * (wave + 1) / kWaves);
+    int cur_t = -1;
+    uint32_t xr[16];
+    SliceRef xf = {0.0f, 0.0f, 0.0f};
+    for (int ib = i0; ib < i1; ib += ppb) {
+        SliceCodes<BITS> sc[kGuWL];
+#pragma unroll
+        for (int k = 0; k < kGuWL; ++k) {
+            const int i = ib + (wide ? k / 2 : k);
+            const int hf = wide ? (k & 1) : half;
+            if (i < i1 && active) load(i, hf, sl, sc[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < kGuWL; ++k) {
+            const int i = ib + (wide ? k / 2 : k);
+            if (i >= i1) continue;  // uniform across the wave
+            const int t = tok_of(i);
+            if (t != cur_t) {
+                const uint4 *src = reinterpret_cast<const uint4 *>(s.xp + (t * nsl + sl) * 20);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint4 u = src[q];
+                    xr[4 * q] = u.x; xr[4 * q + 1] = u.y; xr[4 * q + 2] = u.z; xr[4 * q + 3] = u.w;
+                }
+                xf = s.xref[t * nsl + sl];
+                cur_t = t;
+            }
+            if (wide) {
+                if (k & 1) continue;
+                const float g = wave_sum(slice_value<BITS>(sc[k], xr, xf));
+                const float u = wave_sum(slice_value<BITS>(sc[k + 1], xr, xf));
+                if (lane == 0) ll_put(dst_of(i), silu(g) * u, ep);
+            } else {
+                float v = active ? slice_value<BITS>(sc[k], xr, xf) : 0.0f;
+                v = seg_sum(v, spr);
+                const float g = __shfl(v, 0, kWave), u = __shfl(v, spr, kWave);
+                if (lane == 0) ll_put(dst_of(i), silu(g) * u, ep);
+            }
+        }
     }
-    lds_barrier();
-    for (int i = threadIdx.x; i < nvec * nsl; i += blockDim.x) {
+}
+
+// ---- h of one token: gather, bf16 hi/lo pair table, slice constants --------------------------------
+template <int BITS>
+__device__ bool stage_h(const DecodeParams &p, const Lds &s, const uint64_t *src, uint32_t ep) {
+    const int n = p.K * p.I + p.Is, nsl = n / 32;
+    if (!ll_gather<true>(src, n, ep, reinterpret_cast<float *>(s.hp), p.ctrl, p.spin_limit)) return false;
+    // one thread per slice: read its 32 floats, write 16 hi pairs and 16 lo pairs in place
+    for (int i = threadIdx.x; i < nsl; i += blockDim.x) {
+        uint32_t *row = s.hp + (size_t)i * 36;
+        float v[32];
+#pragma unroll
+        for (int c = 0; c < 32; ++c) v[c] = __uint_as_float(row[c]);
         uint32_t hi[16], lo[16];
+#pragma unroll
         for (int q = 0; q < 16; ++q) {
-            hi[q] = s.hp[(size_t)i * 36 + q];
-            lo[q] = s.hp[(size_t)i * 36 + 16 + q];
+            const float a = v[pair_col_a<BITS>(q)], c = v[pair_col_b<BITS>(q)];
+            const uint16_t ah = f32_to_bf16_rne(a), ch = f32_to_bf16_rne(c);
+            const uint16_t al = f32_to_bf16_rne(a - bf16_to_f32(ah)), cl = f32_to_bf16_rne(c - bf16_to_f32(ch));
+            hi[q] = (uint32_t)ah | ((uint32_t)ch << 16);
+            lo[q] = (uint32_t)al | ((uint32_t)cl << 16);
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            row[q] = hi[q];
+            row[16 + q] = lo[q];
         }
         s.href[i] = slice_ref<BITS>(hi, 2, lo);
     }
@@ -506,266 +719,225 @@ __device__ bool stage_h(const DecodeParams &p, const Lds &s, const uint64_t *src
     return true;
 }
 
-// Down projection of `nvec` h vectors (staged in s.hp) for this workgroup's rows r0..r0+nr-1:
-// out[v * RB + rl] = W_v[r0 + rl] . h_v. A wave-load puts vectors g*rpw .. g*rpw+rpw-1 (one per
-// lane segment) at one row rl; wave-load wl covers g = wl / nr, rl = wl % nr, and wave w takes the
-// contiguous wave-loads [w*nwl/8, (w+1)*nwl/8), so a lane's h slice changes rarely.
-struct DownPlan {
-    int spr, rpw, nwl, wl0, nwl_w;
-};
-__device__ __forceinline__ DownPlan down_plan(int len, int nvec, int nr) {
-    DownPlan d;
-    const int wave = threadIdx.x / kWave;
-    d.spr = len / 32;
-    d.rpw = kWave / d.spr;
-    d.nwl = ((nvec + d.rpw - 1) / d.rpw) * nr;
-    d.wl0 = (int)((long long)wave * d.nwl / kWaves);
-    d.nwl_w = (int)((long long)(wave + 1) * d.nwl / kWaves) - d.wl0;
-    return d;
-}
-template <int BITS, typename MatOf>
-__device__ __forceinline__ void down_load(const DownPlan &d, int len, int r0, int nr, int nvec, MatOf mat_of,
-                                          SliceCodes<BITS> *sc, int first, int count) {
-    const int lane = threadIdx.x % kWave;
-    const int seg = lane / d.spr, sl = lane % d.spr;
-    const size_t cpr = (size_t)len * BITS / 8;
-#pragma unroll
-    for (int k = 0; k < kDnWL; ++k) {
-        if (k < count) {
-            const int wl = d.wl0 + first + k;
-            const int g = wl / nr, rl = wl - g * nr;
-            const int v = g * d.rpw + seg;
-            if (v < nvec) {
-                const QMat m = mat_of(v);
-                const size_t row = (size_t)(r0 + rl);
-                load_slice<BITS>(sc[k], m.c + row * cpr, m.s + row * (len / 64), m.b + row * (len / 64), sl);
-            }
-        }
-    }
-}
+// ---- down projection of this workgroup's rows --------------------------------------------------------
+// nv vectors of length len (h slices starting at slice sl0, vector v at sl0 + v * len / 32), rows
+// from R (row v * nr + rl) -> out[v * RB + rl]. Jobs (v, rl) v-major; a wave-load holds
+// rpw = 64 / (len / 32) jobs; wave w takes the contiguous wave-loads [nwl w / 8, nwl (w + 1) / 8),
+// so a lane's h slice changes rarely (kept in registers).
 template <int BITS>
-__device__ __forceinline__ void down_compute(const DownPlan &d, const Lds &s, int len, int nr, int nvec,
-                                             const SliceCodes<BITS> *sc, int first, int count, float *out, int RB) {
-    const int lane = threadIdx.x % kWave;
-    const int seg = lane / d.spr, sl = lane % d.spr;
-    const int nsl = len / 32;
+__device__ void down_rows(const Lds &s, const Rows &R, int nv, int len, int nr, uint32_t nrm, int sl0, float *out,
+                          int RB) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int spr = len / 32, rpw = kWave / spr;
+    const int seg = lane / spr, sl = lane % spr;
+    const int njobs = nv * nr, nwl = (njobs + rpw - 1) / rpw;
+    const int w0 = (int)((long long)nwl * wave / kWaves), w1 = (int)((long long)nwl * (wave + 1) / kWaves);
     int cur = -1;
     uint32_t hv[32];
-    SliceRef hr;
+    SliceRef hr = {0.0f, 0.0f, 0.0f};
+    constexpr int kU = 4;  // wave-loads whose codes are read before any of their math
+    for (int wb = w0; wb < w1; wb += kU) {
+        SliceCodes<BITS> sc[kU];
 #pragma unroll
-    for (int k = 0; k < kDnWL; ++k) {
-        if (k < count) {
-            const int wl = d.wl0 + first + k;
-            const int g = wl / nr, rl = wl - g * nr;
-            const int v = g * d.rpw + seg;
+        for (int u = 0; u < kU; ++u) {
+            const int job = (wb + u) * rpw + seg;
+            if (wb + u < w1 && job < njobs) lds_slice<BITS>(sc[u], R, job, sl);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (wb + u >= w1) break;  // uniform across the wave
+            const int job = (wb + u) * rpw + seg;
+            const bool ok = job < njobs;
             float val = 0.0f;
-            if (v < nvec) {
+            int v = 0, rl = 0;
+            if (ok) {
+                v = div_by(job, nrm);
+                rl = job - v * nr;
                 if (v != cur) {
-                    const uint4 *src = reinterpret_cast<const uint4 *>(s.hp + ((size_t)v * nsl + sl) * 36);
+                    const int si = sl0 + v * spr + sl;
+                    const uint4 *src = reinterpret_cast<const uint4 *>(s.hp + (size_t)si * 36);
 #pragma unroll
                     for (int q = 0; q < 8; ++q) {
-                        const uint4 u = src[q];
-                        hv[4 * q] = u.x;
-                        hv[4 * q + 1] = u.y;
-                        hv[4 * q + 2] = u.z;
-                        hv[4 * q + 3] = u.w;
+                        const uint4 h4 = src[q];
+                        hv[4 * q] = h4.x; hv[4 * q + 1] = h4.y; hv[4 * q + 2] = h4.z; hv[4 * q + 3] = h4.w;
                     }
-                    hr = s.href[v * nsl + sl];
+                    hr = s.href[si];
                     cur = v;
                 }
-                val = slice_value2<BITS>(sc[k], hv, hv + 16, hr);
+                val = slice_value2<BITS>(sc[u], hv, hv + 16, hr);
             }
-            val = seg_sum(val, d.spr);
-            if (sl == 0 && v < nvec) out[v * RB + rl] = val;
+            val = seg_sum(val, spr);
+            if (ok && sl == 0) out[v * RB + rl] = val;
         }
     }
 }
 
-template <int BITS>
-__global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams p) {
-    extern __shared__ __align__(16) char smem[];
-    const Lds s = carve(p, smem);
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int nb = gridDim.x, b = blockIdx.x;
-    const int T = p.T, H = p.H, E = p.E, K = p.K, I = p.I, Is = p.Is, RB = p.rows_per_wg;
-    if (p.ctrl[0] != 0) return;  // sticky failure of an earlier call: do nothing
-    uint32_t ep = static_cast<uint32_t>(p.ctrl[1]) + 1u;
-    if (ep == 0) ep = 1;
-    if (tid == 0) ll_put(p.ll_start + b, 0.0f, ep);
-    const int r0 = b * RB;
-    const int nr = r0 >= H ? 0 : min(RB, H - r0);
-    const int nlg = E + (Is ? 1 : 0);  // logit words per token (column E = shared gate)
+// ---- routing of every token (identical in every workgroup) ---------------------------------------
+// Wave t selects token t's experts (wave_topk); gamma from the shared-gate logit (column E).
+__device__ void route_tokens(const DecodeParams &p, const Lds &s) {
+    const int T = p.T, E = p.E, K = p.K, wave = threadIdx.x / kWave;
+    if (wave < T) wave_topk(s.lg + wave * (E + 1), E, K, s.sidx + wave * K, s.sw + wave * K);
+    for (int t = threadIdx.x; t < T; t += blockDim.x)
+        s.gam[t] = p.Is ? 1.0f / (1.0f + expf(-s.lg[t * (E + 1) + E])) : 0.0f;
+    lds_barrier();
+}
 
-    for (int l = 0; l < p.L; ++l) {
-        const LayerPtrs L = layer_ptrs(p, l);
+template <int BITS>
+__global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams p0) {
+    extern __shared__ __align__(16) char smem[];
+    const int tid = threadIdx.x;
+    const int nb = gridDim.x, b = blockIdx.x;
+    if (p0.ctrl[0] != 0) return;  // sticky failure of an earlier call: do nothing
+    uint32_t ep = static_cast<uint32_t>(p0.ctrl[1]) + 1u;
+    if (ep == 0) ep = 1;
+    if (tid == 0) ll_put(p0.ll_start + b, 0.0f, ep);
+    const WgShare w = wg_share(p0);
+    {
+        const Lds s = carve(p0, smem);
+        stage_router(p0, 0, s, w);
+        stage_shared_gu(p0, 0, s, w);
+        stage_shared_down(p0, 0, s, w.r0, w.nr);
+    }
+    const int nlayers = p0.L;
+    for (int l = 0; l < nlayers; ++l) {
+        const DecodeParams p = fresh_params();
+        const Lds s = carve(p, smem);
+        const int T = p.T, H = p.H, E = p.E, K = p.K, I = p.I, Is = p.Is, RB = p.rows_per_wg;
+        const int KI = K * I, HW = KI + Is;  // h words per token
+        const int r0 = w.r0, nr = w.nr;
+        const bool has_next = l + 1 < nlayers;
         uint64_t *ll_lg = p.ll_logits + (size_t)l * T * (E + 1);
-        uint64_t *ll_h = p.ll_h + (size_t)l * T * K * I;
-        uint64_t *ll_hs = p.ll_hs + (size_t)l * T * (Is > 0 ? Is : 1);
+        uint64_t *ll_h = p.ll_h + (size_t)l * T * HW;
         uint64_t *ll_y = p.ll_y + (size_t)l * T * H;
 
-        // ---- R: the router rows e = b (mod nb) and the shared-gate row E, and the shared expert's
-        // gate|up and down rows of this workgroup: none depends on the layer input, so their loads
-        // are issued before the input is awaited.
-        float4 rv[kMaxRR];
-        const int nq = H / 4;
-#pragma unroll
-        for (int r = 0; r < kMaxRR; ++r) {
-            const int e = b + r * nb;
-            const float *row = e < E ? L.router + (size_t)e * H : (e == E && Is ? L.sgate : nullptr);
-            rv[r] = (row && tid < nq) ? reinterpret_cast<const float4 *>(row)[tid] : make_float4(0, 0, 0, 0);
-        }
-        const int nps = (Is && b < Is) ? (Is - 1 - b) / nb + 1 : 0;  // shared pairs j = b (mod nb)
-        auto sh_row = [&](int i, QMat &m) -> size_t { m = L.s13; return (size_t)(b + (i / T) * nb); };
-        const GuPlan sg = gu_plan(H, nps * T);
-        SliceCodes<BITS> shsc[kShWL];
-        if (nps) gu_load<BITS, kShWL>(p, sg, 0, Is, sh_row, shsc);
-        const DownPlan sp = down_plan(Is > 0 ? Is : 64, T, nr);
-        SliceCodes<BITS> ssc[kDnWL];
-        const int spre = min(kDnWL, sp.nwl_w);
-        if (Is && nr > 0) down_load<BITS>(sp, Is, r0, nr, T, [&](int) { return L.s2; }, ssc, 0, spre);
+        if (!layer_input<BITS>(p, l, ep, s)) { dma_wait(); return; }
+        dma_wait();  // this layer's router and shared rows (staged during the previous layer)
+        lds_barrier();
 
-        if (!layer_input<BITS>(p, l, ep, s)) return;
-        for (int t = 0; t < T; ++t) {
-            float xv[4] = {0, 0, 0, 0};
-            if (tid < nq) {
-                const uint16_t *xr = s.xb + t * H + 4 * tid;
-                xv[0] = bf16_to_f32(xr[0]); xv[1] = bf16_to_f32(xr[1]);
-                xv[2] = bf16_to_f32(xr[2]); xv[3] = bf16_to_f32(xr[3]);
-            }
-#pragma unroll
-            for (int r = 0; r < kMaxRR; ++r) {
-                float acc = rv[r].x * xv[0] + rv[r].y * xv[1] + rv[r].z * xv[2] + rv[r].w * xv[3];
-                acc = wave_sum(acc);
-                if (lane == 0) s.red[(t * kMaxRR + r) * kWaves + wave] = acc;
-            }
+        // ---- R: router logits and the shared expert's gate|up, from LDS
+        router_logits<BITS>(p, l, s, w, ll_lg, ep);
+        if (!Is && b == 0 && tid < T) ll_put(ll_lg + (size_t)tid * (E + 1) + E, 0.0f, ep);  // unused column
+        if (Is) {
+            const Rows sg = sg_rows(p, s);
+            const uint32_t tdiv = p.tdiv;
+            gate_up<BITS>(
+                p, s, w.nps * T,
+                [&](int i, int hf, int sl, SliceCodes<BITS> &sc) {
+                    lds_slice<BITS>(sc, sg, 2 * div_by(i, tdiv) + hf, sl);
+                },
+                [&](int i) { return i - div_by(i, tdiv) * T; },
+                [&](int i) {
+                    const int r = div_by(i, tdiv);
+                    return ll_h + (size_t)(i - r * T) * HW + KI + (b + r * nb);
+                },
+                ep);
         }
         lds_barrier();
-        if (tid < T * kMaxRR) {
-            const int t = tid / kMaxRR, r = tid - t * kMaxRR, e = b + r * nb;
-            if (e < nlg) {
-                float tot = 0.0f;
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) tot += s.red[tid * kWaves + w];
-                if (e < E && L.rbias) tot += L.rbias[e];
-                ll_put(ll_lg + (size_t)t * (E + 1) + e, tot, ep);
-            }
-        }
-        // shared expert gate|up for pairs j = b (mod nb), every token
-        if (nps) {
-            auto sh_tok = [&](int i) { return i % T; };
-            auto sh_dst = [&](int i) { return ll_hs + (size_t)(i % T) * Is + (b + (i / T) * nb); };
-            gu_finish<BITS, kShWL>(p, s, sg, 0, nps * T, shsc, sh_tok, sh_dst, ep);
-            gate_up_pairs<BITS>(p, s, nps * T, Is, sh_row, sh_tok, sh_dst, ep, kWaves * kShWL);
-        }
 
-        // ---- G: routing, identical in every workgroup (one wave per token)
-        for (int t = 0; t < T; ++t)
-            if (!ll_gather(ll_lg + (size_t)t * (E + 1), nlg, ep, s.lg + t * (E + 1), p.ctrl, p.spin_limit)) return;
-        if (wave < T) wave_topk(s.lg + wave * (E + 1), E, K, s.sidx + wave * K, s.sw + wave * K, s.tks + wave * 32);
-        if (tid < T) s.gam[tid] = Is ? 1.0f / (1.0f + expf(-s.lg[tid * (E + 1) + E])) : 0.0f;
-        lds_barrier();
+        // ---- G: routing (identical in every workgroup), then routed gate|up + SwiGLU
+        if (!ll_gather<false>(ll_lg, T * (E + 1), ep, s.lg, p.ctrl, p.spin_limit)) { dma_wait(); return; }
+        route_tokens(p, s);
         if (b == 0) {
             const size_t base = (size_t)l * T;
             if (p.idx_all)
-                for (int i = tid; i < T * K; i += blockDim.x) p.idx_all[base * K + i] = s.sidx[i];
+                for (int i = tid; i < T * K; i += blockDim.x) G(p.idx_all)[base * K + i] = s.sidx[i];
             if (p.w_all)
-                for (int i = tid; i < T * K; i += blockDim.x) p.w_all[base * K + i] = s.sw[i];
+                for (int i = tid; i < T * K; i += blockDim.x) G(p.w_all)[base * K + i] = s.sw[i];
             if (p.logits_all)
                 for (int i = tid; i < T * E; i += blockDim.x)
-                    p.logits_all[base * E + i] = s.lg[(i / E) * (E + 1) + i % E];
+                    G(p.logits_all)[base * E + i] = s.lg[(i / E) * (E + 1) + i % E];
         }
-
-        // routed down rows of token 0: their loads go out now, with the gate|up loads below
-        auto routed_mat = [&](int t) {
-            return [&, t](int k) -> QMat {
-                const size_t e = expert_at(s.sidx[t * K + k], E);
-                const size_t oc = e * H * ((size_t)I * BITS / 8), os = e * H * (I / 64);
-                return QMat{L.w2.c + oc, L.w2.s + os, L.w2.b + os};
-            };
-        };
-        const DownPlan dp = down_plan(I, K, nr);
-        SliceCodes<BITS> dsc[kDnWL];
-        const int pre = min(kDnWL, dp.nwl_w);
-        if (nr > 0) down_load<BITS>(dp, I, r0, nr, K, routed_mat(0), dsc, 0, pre);
-
-        // routed gate|up + SwiGLU: this workgroup's share of the flattened (token, slot, j) pairs
+        // routed gate|up: this workgroup's pairs [q0, q1) of the flattened (token, slot, j) pairs,
+        // staged into LDS chunk by chunk (one chunk at T = 1): LDS row 2i = gate row, 2i+1 = up row
         {
-            const long long total = (long long)T * K * I;
-            const int p0 = (int)(total * b / nb), p1 = (int)(total * (b + 1) / nb);
-            gate_up_pairs<BITS>(
-                p, s, p1 - p0, I,
-                [&](int i, QMat &m) -> size_t {
-                    const int P = p0 + i, tk = P / I, j = P - tk * I;
-                    m = L.w13;
-                    return expert_at(s.sidx[tk], E) * 2 * I + j;
-                },
-                [&](int i) { return (p0 + i) / (K * I); },
-                [&](int i) { return ll_h + (size_t)(p0 + i); }, ep);
-        }
-
-        // shared expert down for this workgroup's rows, every token -> part[t][K][rl]
-        if (Is && nr > 0) {
-            if (!stage_h<BITS>(p, s, ll_hs, T, Is, ep)) return;
-            for (int c0 = 0; c0 < sp.nwl_w; c0 += kDnWL) {
-                const int cn = min(kDnWL, sp.nwl_w - c0);
-                if (c0 > 0) down_load<BITS>(sp, Is, r0, nr, T, [&](int) { return L.s2; }, ssc, c0, cn);
-                down_compute<BITS>(sp, s, Is, nr, T, ssc, c0, cn, s.fbuf, RB);
-            }
-            lds_barrier();
-            for (int i = tid; i < T * nr; i += blockDim.x) {
-                const int t = i / nr, rl = i - t * nr;
-                s.part[(t * (K + 1) + K) * RB + rl] = s.fbuf[t * RB + rl];
-            }
-            lds_barrier();
-        }
-
-        // ---- D: routed down projections of this workgroup's rows, token by token, and the combine
-        for (int t = 0; t < T; ++t) {
-            if (!stage_h<BITS>(p, s, ll_h + (size_t)t * K * I, K, I, ep)) return;
-            if (nr > 0) {
-                for (int c0 = 0; c0 < dp.nwl_w; c0 += kDnWL) {
-                    const int cn = min(kDnWL, dp.nwl_w - c0);
-                    if (t > 0 || c0 > 0) down_load<BITS>(dp, I, r0, nr, K, routed_mat(t), dsc, c0, cn);
-                    down_compute<BITS>(dp, s, I, nr, K, dsc, c0, cn, s.part + t * (K + 1) * RB, RB);
+            const int np = w.q1 - w.q0, lgI = p.log2I, cp = p.cp;
+            const uint32_t kdiv = p.kdiv;
+            const QMat w13 = layer_ptrs(p, l).w13;
+            const Rows rg = rows_at(s.rg, 2 * cp, H, BITS);
+            const bool one_chunk = np <= cp;
+            for (int c0 = 0; c0 < np; c0 += cp) {
+                const int nc = min(cp, np - c0), pb = w.q0 + c0;
+                dma_qrows(w13, H, BITS, 2 * nc,
+                          [&](int r) -> size_t {
+                              const int P = pb + (r >> 1), tk = P >> lgI, j = P & (I - 1);
+                              return expert_at(s.sidx[tk], E) * 2 * I + (size_t)(r & 1) * I + j;
+                          },
+                          rg);
+                if (one_chunk) {
+                    // token 0's routed down rows follow right behind; wait for the gate|up rows only
+                    stage_routed_down(p, l, s, 0, r0, nr, w.nrm);
+                    dma_wait_but(nr > 0 ? dma_qrows_count(K * nr, I, BITS) : 0);
+                } else {
+                    dma_wait();
                 }
+                lds_barrier();
+                gate_up<BITS>(
+                    p, s, nc,
+                    [&](int i, int hf, int sl, SliceCodes<BITS> &sc) { lds_slice<BITS>(sc, rg, 2 * i + hf, sl); },
+                    [&](int i) { return div_by((pb + i) >> lgI, kdiv); },
+                    [&](int i) {
+                        const int P = pb + i, t = div_by(P >> lgI, kdiv);
+                        return ll_h + (size_t)t * HW + (P - t * KI);
+                    },
+                    ep);
+                lds_barrier();
+            }
+        }
+
+        // ---- D: per token, all h -> this workgroup's rows of every down projection -> combine
+        {
+            const int np = w.q1 - w.q0;
+            if (!(np > 0 && np <= p.cp))  // not staged with the gate|up rows above
+                stage_routed_down(p, l, s, 0, r0, nr, w.nrm);  // streams in during the h exchange
+        }
+        for (int t = 0; t < T; ++t) {
+            if (!stage_h<BITS>(p, s, ll_h + (size_t)t * HW, ep)) { dma_wait(); return; }
+            dma_wait();
+            lds_barrier();
+            if (nr > 0) {
+                float *pt = s.part + (size_t)t * (K + 1) * RB;
+                down_rows<BITS>(s, rd_rows(p, s), K, I, nr, w.nrm, 0, pt, RB);
+                if (Is) down_rows<BITS>(s, sd_rows(p, s), 1, Is, nr, w.nrm, KI / 32, pt + K * RB, RB);
             }
             lds_barrier();
+            if (t + 1 < T) stage_routed_down(p, l, s, t + 1, r0, nr, w.nrm);
         }
         for (int i = tid; i < T * nr; i += blockDim.x) {
-            const int t = i / nr, rl = i - t * nr;
+            const int t = div_by(i, w.nrm), rl = i - t * nr;
             const float *pt = s.part + t * (K + 1) * RB;
             float acc = 0.0f;
             for (int k = 0; k < K; ++k) acc += s.sw[t * K + k] * pt[k * RB + rl];
             if (Is) acc += s.gam[t] * pt[K * RB + rl];
             const size_t o = (size_t)t * H + r0 + rl;
-            if (l + 1 < p.L && p.chained) ll_put(ll_y + o, acc, ep);
-            if (l == p.L - 1) p.y_out[o] = acc;
-            if (p.y_all) p.y_all[(size_t)l * T * H + o] = acc;
+            if (has_next && p.chained) ll_put(ll_y + o, acc, ep);
+            if (!has_next) G(p.y_out)[o] = acc;
+            if (p.y_all) G(p.y_all)[(size_t)l * T * H + o] = acc;
         }
         lds_barrier();
+        if (has_next) {  // layer l+1's router and shared-expert rows stream in during the y exchange
+            stage_router(p, l + 1, s, w);
+            stage_shared_gu(p, l + 1, s, w);
+            stage_shared_down(p, l + 1, s, r0, nr);
+        }
     }
+    dma_wait();
     // the next call may advance the epoch once every workgroup has read it
     if (b == 0) {
-        if (!ll_gather(p.ll_start, nb, ep, s.fbuf, p.ctrl, p.spin_limit)) return;
-        if (tid == 0) p.ctrl[1] = static_cast<int>(ep);
+        if (!ll_gather<false>(p0.ll_start, nb, ep, reinterpret_cast<float *>(smem + p0.lds.hp), p0.ctrl,
+                              p0.spin_limit))
+            return;
+        if (tid == 0) p0.ctrl[1] = static_cast<int>(ep);
     }
-}
-
-size_t decode_lds_bytes(int T, int H, int E, int K, int I, int Is, int bits, int rows_per_wg) {
-    (void)bits;
-    size_t o[14];
-    return lds_offsets(T, H, E, K, I, Is, rows_per_wg, o);
 }
 
 template <int BITS>
 static hipError_t launch_bits(const DecodeParams &p, int grid, hipStream_t stream) {
-    const size_t lds = decode_lds_bytes(p.T, p.H, p.E, p.K, p.I, p.Is, p.bits, p.rows_per_wg);
     const void *fn = reinterpret_cast<const void *>(&decode_kernel<BITS>);
-    hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds.total);
     if (err != hipSuccess) return err;
     DecodeParams arg = p;
     void *args[] = {&arg};
-    return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kDecodeThreads), args, (unsigned)lds, stream);
+    return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kDecodeThreads), args, (unsigned)p.lds.total, stream);
 }
 
 hipError_t launch_decode(const DecodeParams &p, int grid, hipStream_t stream) {

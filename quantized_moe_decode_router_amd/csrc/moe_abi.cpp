@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "../../include/moe.h"
+#include "moe_device.hpp"
 #include "moe_internal.hpp"
 
 namespace {
@@ -68,16 +69,24 @@ size_t batched_ws_bytes(const moe_shape *s, int T) {
     return moe::batched_ws_layout(T, s->hidden, s->num_experts, s->top_k, s->inter, s->shared_inter).total;
 }
 
+// LDS available to the decode kernel's dynamic plan (the rest of the 160 KiB holds its small
+// static arrays).
+constexpr int kDecodeLdsBudget = 160 * 1024 - 256;
+
+int decode_chunk(const moe_shape *s, int T, int grid) {
+    return moe::decode_chunk_pairs(T, s->hidden, s->num_experts, s->top_k, s->inter, s->shared_inter, s->bits, grid,
+                                   kDecodeLdsBudget);
+}
+
 int rows_per_wg(int H, int grid) { return (H + grid - 1) / grid; }
 
 // Shapes the decode kernel handles (beyond check_shape): rows of at most 64 slices of 32 columns,
-// router rows spread over at most 3 per workgroup, and LDS within the compute unit's 160 KiB.
+// intermediates of at least 128 columns (whole dwords of scales per row for the LDS staging),
+// and an LDS plan within the compute unit's 160 KiB.
 moe_status decode_supported(const moe_shape *s, int T, int grid) {
     if (s->hidden > 2048 || s->inter > 2048 || s->shared_inter > 2048) return MOE_ERR_UNSUPPORTED;
-    if (s->num_experts + 1 > 3 * grid) return MOE_ERR_UNSUPPORTED;
-    const size_t lds = moe::decode_lds_bytes(T, s->hidden, s->num_experts, s->top_k, s->inter, s->shared_inter,
-                                             s->bits, rows_per_wg(s->hidden, grid));
-    if (lds > 160 * 1024) return MOE_ERR_UNSUPPORTED;
+    if (s->inter < 128 || (s->shared_inter && s->shared_inter < 128)) return MOE_ERR_UNSUPPORTED;
+    if (decode_chunk(s, T, grid) == 0) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -108,6 +117,15 @@ moe_status decode_common(const moe_shape *s, const moe_layer *L, int32_t n_layer
     p.bits = s->bits; p.T = T; p.L = n_layers;
     p.chained = (flags & MOE_STACK_INDEPENDENT) ? 0 : 1;
     p.rows_per_wg = rows_per_wg(s->hidden, grid);
+    p.nrr = (s->num_experts + (Is ? 1 : 0) + grid - 1) / grid;
+    p.nps = Is ? ((int)Is + grid - 1) / grid : 0;
+    p.log2I = 0;
+    while ((1 << p.log2I) < s->inter) ++p.log2I;
+    p.kdiv = moe::div_magic((unsigned)s->top_k);
+    p.tdiv = moe::div_magic((unsigned)T);
+    p.cp = decode_chunk(s, T, grid);
+    p.lds = moe::decode_lds_plan(T, s->hidden, s->num_experts, s->top_k, s->inter, s->shared_inter, s->bits, grid,
+                                 p.cp);
     p.spin_limit = 1u << 20;
     p.eps = 1e-6f;
     p.router = L->router; p.rbias = L->router_bias; p.sgate = Is ? L->shared_gate : nullptr;
@@ -117,17 +135,6 @@ moe_status decode_common(const moe_shape *s, const moe_layer *L, int32_t n_layer
         p.s13 = {L->s13.codes, L->s13.scales, L->s13.biases};
         p.s2 = {L->s2.codes, L->s2.scales, L->s2.biases};
     }
-    p.ls_router = (long long)(E * H);
-    p.ls_rbias = (long long)E;
-    p.ls_sgate = (long long)H;
-    p.ls_w13c = (long long)(E * 2 * I * H * bits / 8);
-    p.ls_w13s = (long long)(E * 2 * I * H / 64);
-    p.ls_w2c = (long long)(E * H * I * bits / 8);
-    p.ls_w2s = (long long)(E * H * I / 64);
-    p.ls_s13c = (long long)(2 * Is * H * bits / 8);
-    p.ls_s13s = (long long)(2 * Is * H / 64);
-    p.ls_s2c = (long long)(H * Is * bits / 8);
-    p.ls_s2s = (long long)(H * Is / 64);
     p.x_in = x; p.y_out = y;
     p.x_all = x_all; p.y_all = y_all; p.idx_all = idx_all; p.w_all = w_all; p.logits_all = logits_all;
     char *w = static_cast<char *>(ws);
@@ -137,7 +144,6 @@ moe_status decode_common(const moe_shape *s, const moe_layer *L, int32_t n_layer
     p.ll_start = reinterpret_cast<uint64_t *>(w + lay.start);
     p.ll_logits = reinterpret_cast<uint64_t *>(w + lay.logits);
     p.ll_h = reinterpret_cast<uint64_t *>(w + lay.h);
-    p.ll_hs = reinterpret_cast<uint64_t *>(w + lay.hs);
     p.ll_y = reinterpret_cast<uint64_t *>(w + lay.y);
     hipError_t err = moe::launch_decode(p, grid, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;

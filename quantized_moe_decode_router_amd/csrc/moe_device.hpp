@@ -33,16 +33,64 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// ---- lane reductions -------------------------------------------------------------------------
-// Sum over aligned groups of N lanes (N a power of two <= 64); every lane of a group gets the sum.
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int o = N / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+// ---- division by a runtime constant ----------------------------------------------------------------
+// n / d = mulhi(n, m) with m = ceil(2^32 / d), exact for 0 <= n < 2^32 / d (d >= 2); m = 0 stands
+// for d = 1. Integer division on the GPU is a long instruction sequence; the reciprocal is
+// computed once (on the host, or once per kernel) and every later division is one mulhi.
+__host__ __device__ inline uint32_t div_magic(uint32_t d) {
+    return d <= 1 ? 0u : static_cast<uint32_t>(0xFFFFFFFFull / d + 1ull);
+}
+__device__ __forceinline__ int div_by(int n, uint32_t m) {
+    return m == 0 ? n : static_cast<int>(__umulhi(static_cast<uint32_t>(n), m));
 }
 
-__device__ __forceinline__ float wave_sum(float v) { return group_sum<kWave>(v); }
+// ---- lane reductions (DPP) ---------------------------------------------------------------------
+// Data-parallel-primitive lane moves inside rows of 16 lanes (quad permutations, half-row and
+// row mirrors, row rotations) feed the ALU directly, without an LDS round trip; rows are then
+// combined with readlane, in a fixed order, so every lane returns the same bits.
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each half-row of 8
+constexpr int kDppRowMirror = 0x140;  // lane i <-> 15 - i within each row of 16
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+// Sum over aligned groups of n lanes (n a power of two <= 64, runtime): every lane of a group
+// gets the group's sum.
+__device__ __forceinline__ float seg_sum(float v, int n) {
+    if (n >= 2) v += dpp_f32<kDppQuadXor1>(v);
+    if (n >= 4) v += dpp_f32<kDppQuadXor2>(v);
+    if (n >= 8) v += dpp_f32<kDppHalfMirror>(v);
+    if (n >= 16) v += dpp_f32<kDppRowMirror>(v);
+    if (n >= 32) {
+        const float a = readlane_f32(v, 0) + readlane_f32(v, 16), b = readlane_f32(v, 32) + readlane_f32(v, 48);
+        v = n >= 64 ? a + b : ((threadIdx.x & 32) ? b : a);
+    }
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) { return seg_sum(v, kWave); }
+// Maximum over the wave (every lane gets it).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<kDppQuadXor1>(v));
+    v = max(v, dpp_u32<kDppQuadXor2>(v));
+    v = max(v, dpp_u32<kDppHalfMirror>(v));
+    v = max(v, dpp_u32<kDppRowMirror>(v));
+    // readlane returns int: compare as unsigned
+    const uint32_t r0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0));
+    const uint32_t r1 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16));
+    const uint32_t r2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32));
+    const uint32_t r3 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
+    return max(max(r0, r1), max(r2, r3));
+}
 
 // Partial dot product of an fp32 row with v[0..cols) (cols % 4 == 0).
 __device__ __forceinline__ float frow_dot_partial(const float *row, int cols, const float *v, int lane) {
@@ -69,113 +117,56 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 
 constexpr int kTopkMaxE = 1024;
 
-// Top-k of lt[0..E) (LDS) by one whole wave, NJ = ceil(E / 64) keys per lane: the K indices with
-// the largest values, ordered by (value descending, index ascending). Exact and deterministic:
-//   1. theta = the K-th largest key, built bit by bit from the top: a candidate bit stays set when
-//      at least K keys are >= the candidate (each lane compare is itself the wave ballot);
-//   2. every key > theta is taken, then keys == theta in increasing index order until K;
-//   3. the K winners (one per lane < K) are ranked among themselves with readlane broadcasts.
-// Writes idx[0..K) and the renormalised softmax weights w[0..K) (softmax over the kept logits
-// equals softmax-then-renormalise). `scratch` is LDS for K ints owned by this wave.
+// Top-k of lt[0..E) (LDS) by one whole wave, NJ = ceil(E / 64) keys per lane (expert e = lane +
+// 64 j in slot j): the K indices with the largest values, ordered by (value descending, index
+// ascending). Exact and deterministic: K rounds of (wave maximum of the remaining keys; the lowest
+// expert index holding it wins -- the first slot j with a match, then its lowest lane; that key is
+// removed). Writes idx[0..K) and the renormalised softmax weights w[0..K) (softmax over the kept
+// logits equals softmax-then-renormalise), the exponentials summed by a fixed lane reduction.
 template <int NJ>
-__device__ inline void wave_topk_n(const float *lt, int E, int K, int *idx, float *w, int *scratch) {
+__device__ inline void wave_topk_n(const float *lt, int E, int K, int *idx, float *w) {
     const int lane = threadIdx.x % kWave;
     uint32_t key[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int e = lane + kWave * j;
         const float v = lt[min(e, E - 1)];  // every read in flight at once; padding masked below
-        key[j] = e < E ? order_key(v) : 0u; // padding keys sort below every value
+        key[j] = e < E ? order_key(v) : 0u; // 0 sorts below the key of every finite value
     }
-    uint32_t theta = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = theta | (1u << bit);  // never 0, so padding keys never count
-        int cnt = 0;
+    int mine = 0;  // lane r < K ends with the rank-r winner
+    for (int r = 0; r < K; ++r) {
+        uint32_t m = key[0];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(key[j] >= cand));
-        if (cnt >= K) theta = cand;
-    }
-    int need = K;
+        for (int j = 1; j < NJ; ++j) m = max(m, key[j]);
+        m = wave_max_u32(m);
+        int win = -1;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) need -= __popcll(__ballot(key[j] > theta));
-    // take ties (key == theta) in increasing index order: index = lane + 64 j
-    const unsigned long long below = (1ull << lane) - 1ull;
-    int base = 0;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const unsigned long long eq = __ballot(key[j] == theta);
-        const bool sel = key[j] > theta || ((key[j] == theta) && (int)__popcll(eq & below) < need);
-        need -= min(need, (int)__popcll(eq));
-        const unsigned long long sm = __ballot(sel);
-        if (sel) scratch[base + __popcll(sm & below)] = lane + kWave * j;
-        base += __popcll(sm);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int e = lane < K ? scratch[lane] : 0;
-    const float v = lt[e];
-    const uint32_t ke = order_key(v);
-    int rank = 0;
-    for (int m = 0; m < K; ++m) {
-        const uint32_t km = __builtin_amdgcn_readlane(ke, m);
-        const int em = __builtin_amdgcn_readlane(e, m);
-        rank += (km > ke) || (km == ke && em < e);
-    }
-    // the maximum logit is the rank-0 winner's; sum the exponentials in winner order
-    const unsigned long long top = __ballot(lane < K && rank == 0);
-    const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), __ffsll((long long)top) - 1));
-    const float pe = expf(v - vmax);
-    float z = 0.0f;
-    for (int m = 0; m < K; ++m) z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), m));
-    if (lane < K) {
-        idx[rank] = e;
-        w[rank] = pe / z;
-    }
-}
-
-__device__ inline void wave_topk(const float *lt, int E, int K, int *idx, float *w, int *scratch) {
-    const int nj = (E + kWave - 1) / kWave;
-    if (nj <= 1) wave_topk_n<1>(lt, E, K, idx, w, scratch);
-    else if (nj <= 2) wave_topk_n<2>(lt, E, K, idx, w, scratch);
-    else if (nj <= 4) wave_topk_n<4>(lt, E, K, idx, w, scratch);
-    else if (nj <= 8) wave_topk_n<8>(lt, E, K, idx, w, scratch);
-    else wave_topk_n<16>(lt, E, K, idx, w, scratch);
-}
-
-// ---- grid-wide barrier for a cooperative (all workgroups co-resident) launch ------------------
-// ctrl[0] = status (0 ok, else a moe_status), ctrl[1] = arrivals, ctrl[2] = generation.
-// Bounded: after `spin_limit` polls a waiting workgroup records MOE_ERR_TIMEOUT (5) and every
-// workgroup then leaves at its next barrier, so a fault in the protocol cannot hang the GPU.
-// Returns false once the status is non-zero.
-__device__ __forceinline__ bool grid_barrier(int *ctrl, unsigned nblocks, unsigned spin_limit) {
-    __shared__ int s_ok;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int ok = 1;
-        const int gen = __hip_atomic_load(&ctrl[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned arrived = static_cast<unsigned>(
-            __hip_atomic_fetch_add(&ctrl[1], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT));
-        if (arrived == nblocks - 1) {
-            __hip_atomic_store(&ctrl[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_add(&ctrl[2], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            unsigned n = 0;
-            while (__hip_atomic_load(&ctrl[2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-                if (__hip_atomic_load(&ctrl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
-                if (++n > spin_limit) {
-                    __hip_atomic_store(&ctrl[0], 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
+        for (int j = 0; j < NJ; ++j) {
+            const unsigned long long hit = __ballot(key[j] == m);
+            if (win < 0 && hit) win = (__ffsll((long long)hit) - 1) + kWave * j;
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        if (__hip_atomic_load(&ctrl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) ok = 0;
-        s_ok = ok;
+        if (lane == r) mine = win;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            if (lane + kWave * j == win) key[j] = 0u;
     }
-    __syncthreads();
-    return s_ok != 0;
+    const float v = lt[lane < K ? mine : 0];
+    const float vmax = readlane_f32(v, 0);
+    const float pe = lane < K ? expf(v - vmax) : 0.0f;
+    const float z = wave_sum(pe);  // fixed reduction tree: the same bits every time
+    if (lane < K) {
+        idx[lane] = mine;
+        w[lane] = pe / z;
+    }
+}
+
+__device__ inline void wave_topk(const float *lt, int E, int K, int *idx, float *w) {
+    const int nj = (E + kWave - 1) / kWave;
+    if (nj <= 1) wave_topk_n<1>(lt, E, K, idx, w);
+    else if (nj <= 2) wave_topk_n<2>(lt, E, K, idx, w);
+    else if (nj <= 4) wave_topk_n<4>(lt, E, K, idx, w);
+    else if (nj <= 8) wave_topk_n<8>(lt, E, K, idx, w);
+    else wave_topk_n<16>(lt, E, K, idx, w);
 }
 
 }  // namespace moe

@@ -13,18 +13,28 @@ struct QMat {
     const uint16_t *b;  // bf16 biases
 };
 
+// LDS plan of the decode kernel: byte offsets of every region (computed once on the host).
+struct DecodeLds {
+    int xp, xref, lg, sidx, sw, gam, rt, sg, sd, rd, rg, hp, href, part, red;
+    int total;
+};
+
 // Decode of L layers (L = 1 for a single layer). Every weight pointer is the layer-0 base of an
-// [L]-stacked array; ls_* are the per-layer strides in elements.
+// [L]-stacked array (each layer one contiguous block of the shape's size).
 struct DecodeParams {
     int H, E, K, I, Is, bits, T, L;
     int chained;          // layer l+1 takes the RMS glue of y_l (else every layer takes x_in)
     int rows_per_wg;      // rows of y owned by each workgroup
+    int nrr;              // router rows per workgroup (rows e = b + r * grid, r < nrr; row E = shared gate)
+    int nps;              // shared-expert pairs per workgroup (j = b + r * grid, r < nps)
+    int cp;               // routed gate|up pairs staged in LDS at once
+    int log2I;            // log2(I)
+    unsigned kdiv, tdiv;  // div_magic(K), div_magic(T)
     unsigned spin_limit;  // bound on every wait
     float eps;
+    DecodeLds lds;
     const float *router, *rbias, *sgate;
     QMat w13, w2, s13, s2;
-    long long ls_router, ls_rbias, ls_sgate;
-    long long ls_w13c, ls_w13s, ls_w2c, ls_w2s, ls_s13c, ls_s13s, ls_s2c, ls_s2s;
     const uint16_t *x_in;  // [T][H] bf16
     float *y_out;          // [T][H] fp32, last layer
     uint16_t *x_all;       // [L][T][H] or null
@@ -34,10 +44,9 @@ struct DecodeParams {
     float *logits_all;     // [L][T][E] or null
     // workspace (zero-filled before first use)
     int *ctrl;               // [0] status, [1] call sequence number
-    uint64_t *ll_start;      // [grid]            one word per workgroup: "this call has started"
-    uint64_t *ll_logits;     // [L][T][E+1]       router logits, column E = shared-gate logit
-    uint64_t *ll_h;          // [L][T][K][I]      routed h
-    uint64_t *ll_hs;         // [L][T][Is]        shared-expert h
+    uint64_t *ll_start;      // [grid]               one word per workgroup: "this call has started"
+    uint64_t *ll_logits;     // [L][T][E+1]          router logits, column E = shared-gate logit
+    uint64_t *ll_h;          // [L][T][K*I + Is]     routed h of slots 0..K-1, then the shared expert's h
     uint64_t *ll_y;          // [L][T][H]
 };
 
@@ -48,7 +57,7 @@ __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a -
 
 // Workspace layout of the decode kernel (bytes from the workspace base).
 struct DecodeWs {
-    size_t start, logits, h, hs, y, total;
+    size_t start, logits, h, y, total;
 };
 constexpr int kMaxGrid = 1024;
 __host__ __device__ inline DecodeWs decode_ws_layout(int L, int T, int H, int E, int K, int I, int Is) {
@@ -56,17 +65,66 @@ __host__ __device__ inline DecodeWs decode_ws_layout(int L, int T, int H, int E,
     size_t o = kCtrlBytes;
     w.start = o;  o = align_up(o + 8 * (size_t)kMaxGrid, 256);
     w.logits = o; o = align_up(o + 8 * (size_t)L * T * (E + 1), 256);
-    w.h = o;      o = align_up(o + 8 * (size_t)L * T * K * I, 256);
-    w.hs = o;     o = align_up(o + 8 * (size_t)L * T * (Is > 0 ? Is : 1), 256);
+    w.h = o;      o = align_up(o + 8 * (size_t)L * T * ((size_t)K * I + Is), 256);
     w.y = o;      o = align_up(o + 8 * (size_t)L * T * H, 256);
     w.total = o;
     return w;
 }
 
+// LDS plan for a shape, token count and grid (router rows and shared pairs per workgroup and
+// the y rows per workgroup follow from the grid); cp = routed gate|up pairs per LDS chunk.
+__host__ inline DecodeLds decode_lds_plan(int T, int H, int E, int K, int I, int Is, int bits, int grid, int cp) {
+    DecodeLds d;
+    const size_t RB = ((size_t)H + grid - 1) / grid;
+    const size_t nrr = ((size_t)E + (Is ? 1 : 0) + grid - 1) / grid;
+    const size_t nps = Is ? ((size_t)Is + grid - 1) / grid : 0;
+    const size_t cbH = (size_t)H * bits / 8, sbH = (size_t)H / 32;
+    const size_t cbS = (size_t)Is * bits / 8, sbS = (size_t)Is / 32;
+    const size_t cbI = (size_t)I * bits / 8, sbI = (size_t)I / 32;
+    const size_t nsl = ((size_t)K * I + Is) / 32;
+    size_t hp = nsl * 36 * 4;
+    if ((size_t)H * 4 > hp) hp = (size_t)H * 4;
+    if ((size_t)kMaxGrid * 4 > hp) hp = (size_t)kMaxGrid * 4;
+    const size_t sz[15] = {
+        4 * (size_t)T * (H / 32) * 20,   // xp
+        12 * (size_t)T * (H / 32),       // xref
+        4 * (size_t)T * (E + 1),         // lg
+        4 * (size_t)T * K,               // sidx
+        4 * (size_t)T * K,               // sw
+        4 * (size_t)T,                   // gam
+        4 * nrr * H,                     // rt
+        2 * nps * (cbH + 2 * sbH),       // sg
+        RB * (cbS + 2 * sbS),            // sd
+        (size_t)K * RB * (cbI + 2 * sbI),  // rd
+        2 * (size_t)cp * (cbH + 2 * sbH),  // rg
+        hp,                              // hp (also the y gather buffer)
+        12 * nsl,                        // href
+        4 * (size_t)T * (K + 1) * RB,    // part
+        4 * 64};                         // red
+    int *o[15] = {&d.xp, &d.xref, &d.lg, &d.sidx, &d.sw, &d.gam, &d.rt, &d.sg, &d.sd, &d.rd, &d.rg, &d.hp, &d.href,
+                  &d.part, &d.red};
+    size_t off = 0;
+    for (int i = 0; i < 15; ++i) {
+        *o[i] = (int)off;
+        off = align_up(off + sz[i], 16);
+    }
+    d.total = off > (size_t)0x7fffffff ? 0x7fffffff : (int)off;
+    return d;
+}
+// Routed gate|up pairs per LDS chunk: every pair of the workgroup's share if that fits in
+// `budget` bytes of LDS, else the largest power of two that does (0 if not even one pair fits).
+__host__ inline int decode_chunk_pairs(int T, int H, int E, int K, int I, int Is, int bits, int grid, int budget) {
+    const long long total = (long long)T * K * I;
+    int cp = (int)((total + grid - 1) / grid);
+    int p2 = 1;
+    while (p2 < cp) p2 <<= 1;
+    for (int c = cp; c >= 1; c = (c == cp && cp != p2) ? p2 / 2 : c / 2)
+        if (decode_lds_plan(T, H, E, K, I, Is, bits, grid, c).total <= budget) return c;
+    return 0;
+}
+
 // Enqueue the decode kernel. Returns a hipError_t.
 hipError_t launch_decode(const DecodeParams &p, int grid, hipStream_t stream);
-// Dynamic LDS bytes the decode kernel needs (0 if the shape does not fit).
-size_t decode_lds_bytes(int T, int H, int E, int K, int I, int Is, int bits, int rows_per_wg);
 
 // Router for T tokens: logits (or given logits), top-k, renormalised weights, optional gamma.
 struct RouteParams {

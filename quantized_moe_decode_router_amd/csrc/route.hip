@@ -37,7 +37,7 @@ __global__ void __launch_bounds__(kRouteThreads) route_kernel(RouteParams p) {
         for (int e = threadIdx.x; e < E; e += blockDim.x) lg[e] = p.logits[(size_t)t * E + e];
         __syncthreads();
     }
-    if (wave == 0) wave_topk(lg, E, K, sidx + 2 * K, reinterpret_cast<float *>(sidx + 3 * K), sidx);
+    if (wave == 0) wave_topk(lg, E, K, sidx + 2 * K, reinterpret_cast<float *>(sidx + 3 * K));
     __syncthreads();
     if (threadIdx.x < K) {
         p.idx[(size_t)t * K + threadIdx.x] = sidx[2 * K + threadIdx.x];

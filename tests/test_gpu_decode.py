@@ -117,7 +117,7 @@ DECODE_CASES = [
     ("35b_8bit_T1", synth.QWEN35B_8BIT.shape, 1, 6),
     ("35b_8bit_T3", synth.QWEN35B_8BIT.shape, 3, 7),
     ("k1_no_shared", synth.MoeShape(512, 8, 1, 256, 0, 4), 5, 8),
-    ("k_eq_e", synth.MoeShape(256, 4, 4, 64, 64, 8), 2, 9),
+    ("k_eq_e", synth.MoeShape(256, 4, 4, 128, 128, 8), 2, 9),
     ("wide_inter", synth.MoeShape(1024, 32, 6, 1024, 256, 4), 3, 10),
 ]
 
