@@ -1,8 +1,8 @@
 // batched.hip -- one MoE layer for a batch of T tokens (prefill / batched decode) on gfx950.
 //
 // Six launches on one stream, no host synchronisation:
-//   1. router_gemm   logits[T][E] (+ shared-gate logit) = x . R^T on v_mfma_f32_16x16x4_f32
-//                    (fp32 operands: x is bf16, exact in fp32; the router stays fp32)
+//   1. router_gemm   logits[T][E] (+ shared-gate logit) = x . R^T on v_mfma_f32_16x16x32_bf16, the
+//                    fp32 router split into bf16 hi + lo (x is bf16, exact)
 //   2. topk_kernel   one wave per token: top-k by (logit desc, index asc), renormalised weights
 //                    (softmax of the kept logits), gamma = sigmoid(gate logit)
 //   3. bucket_kernel one workgroup: per-expert histogram of the (token, slot) pairs, exclusive scan,
@@ -16,8 +16,9 @@
 //                    h lo; epilogue scales by the routing weight (gamma for the shared group)
 //   6. combine       y[t] = sum_k out[pos(t, k)] + out[shared row of t], k = 0..K-1 in order
 //
-// Dequantised weights are s * q + b rounded to fp16; bf16 activations are exact in fp16 in the
-// normal range. Products are exact in the fp32 accumulators of the MFMA.
+// Dequantised weights are s * q + b rounded once to fp16 (scales and biases must lie in fp16's
+// normal range); bf16 activations are exact in fp16 in the normal range. Products are exact in
+// the fp32 accumulators of the MFMA.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -33,60 +34,104 @@ constexpr int kLdsK = 72;        // fp16 per LDS tile row: 64 + 8 padding (16 by
 __device__ __forceinline__ _Float16 bf16_to_f16(uint16_t b) { return (_Float16)bf16_to_f32(b); }
 
 // ---- 1. router GEMM ------------------------------------------------------------------------------
-// Workgroup tile: 16 tokens x 64 router rows (row E = shared gate); wave w owns rows 16w..16w+15.
-// k-step of 32 columns staged in LDS as fp32 (+1 word padding per row).
-constexpr int kRtT = 16, kRtN = 64, kRtK = 32;
+// logits = x . R^T on bf16 MFMA: x is bf16 (exact), every fp32 router weight is split into
+// bf16 hi = rne(R) and lo = rne(R - hi), so R - hi - lo is below 2^-17 |R|; both products are exact
+// in the fp32 accumulators. Tile: 32 tokens x 64 router rows (row E = shared gate), k-steps of 64;
+// wave w: tokens 16 (w & 1) .., rows 32 (w >> 1) ..
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+constexpr int kRtT = 32, kRtN = 64;
 
 __global__ void __launch_bounds__(kGemmThreads) router_gemm(BatchedParams p) {
-    __shared__ float xs[kRtT][kRtK + 1];
-    __shared__ float rs[kRtN][kRtK + 1];
+    __shared__ __align__(16) uint16_t xs[kRtT][kLdsK];
+    __shared__ __align__(16) uint16_t rh[kRtN][kLdsK];
+    __shared__ __align__(16) uint16_t rl[kRtN][kLdsK];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int t0 = blockIdx.x * kRtT, n0 = blockIdx.y * kRtN;
     const int H = p.H, E = p.E, T = p.T;
     const int N = E + (p.sgate ? 1 : 0);
-    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k0 = 0; k0 < H; k0 += kRtK) {
-        // x: 16 rows x 32 bf16 -> 64 threads x 8 values
-        if (tid < 64) {
-            const int r = tid / 4, c = (tid % 4) * 8, t = t0 + r;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (t < T) v = *reinterpret_cast<const uint4 *>(p.x + (size_t)t * H + k0 + c);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    // loads: x row xr (8 bf16 at xc); router row rr (16 floats at rc)
+    const int xr = tid / 8, xc = (tid % 8) * 8, rr = tid / 4, rc = (tid % 4) * 16;
+    const bool xok = t0 + xr < T, rok = n0 + rr < N;
+    const uint16_t *xrow = p.x + (size_t)(xok ? t0 + xr : 0) * H;
+    const float *rrow = rok ? (n0 + rr < E ? p.router + (size_t)(n0 + rr) * H : p.sgate) : p.router;
+    struct St {
+        uint4 x;
+        float4 r[4];
+    };
+    auto load = [&](int kb) {
+        St st;
+        st.x = xok ? *reinterpret_cast<const uint4 *>(xrow + kb * 64 + xc) : make_uint4(0, 0, 0, 0);
+        const float4 *src = reinterpret_cast<const float4 *>(rrow + kb * 64 + rc);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                xs[r][c + 2 * q] = bf16_to_f32(w[q] & 0xFFFF);
-                xs[r][c + 2 * q + 1] = bf16_to_f32(w[q] >> 16);
+        for (int q = 0; q < 4; ++q) st.r[q] = rok ? src[q] : make_float4(0, 0, 0, 0);
+        return st;
+    };
+    auto store = [&](const St &st) {
+        *reinterpret_cast<uint4 *>(&xs[xr][xc]) = st.x;
+        uint16_t hi[16], lo[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float f[4] = {st.r[q].x, st.r[q].y, st.r[q].z, st.r[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint16_t h = f32_to_bf16_rne(f[e]);
+                hi[4 * q + e] = h;
+                lo[4 * q + e] = f32_to_bf16_rne(f[e] - bf16_to_f32(h));
             }
         }
-        // router rows: 64 rows x 32 fp32 -> 256 threads x 8 values
-        {
-            const int r = tid / 4, c = (tid % 4) * 8, n = n0 + r;
-            float4 a = make_float4(0, 0, 0, 0), b = a;
-            if (n < N) {
-                const float *row = n < E ? p.router + (size_t)n * H : p.sgate;
-                a = *reinterpret_cast<const float4 *>(row + k0 + c);
-                b = *reinterpret_cast<const float4 *>(row + k0 + c + 4);
-            }
-            rs[r][c + 0] = a.x; rs[r][c + 1] = a.y; rs[r][c + 2] = a.z; rs[r][c + 3] = a.w;
-            rs[r][c + 4] = b.x; rs[r][c + 5] = b.y; rs[r][c + 6] = b.z; rs[r][c + 7] = b.w;
-        }
-        __syncthreads();
+        uint4 *dh = reinterpret_cast<uint4 *>(&rh[rr][rc]);
+        uint4 *dl = reinterpret_cast<uint4 *>(&rl[rr][rc]);
 #pragma unroll
-        for (int kk = 0; kk < kRtK; kk += 4) {
-            const float a = xs[lane % 16][kk + lane / 16];
-            const float b = rs[16 * wave + lane % 16][kk + lane / 16];
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+        for (int q = 0; q < 2; ++q) {
+            dh[q] = make_uint4(hi[8 * q] | (uint32_t)hi[8 * q + 1] << 16, hi[8 * q + 2] | (uint32_t)hi[8 * q + 3] << 16,
+                               hi[8 * q + 4] | (uint32_t)hi[8 * q + 5] << 16, hi[8 * q + 6] | (uint32_t)hi[8 * q + 7] << 16);
+            dl[q] = make_uint4(lo[8 * q] | (uint32_t)lo[8 * q + 1] << 16, lo[8 * q + 2] | (uint32_t)lo[8 * q + 3] << 16,
+                               lo[8 * q + 4] | (uint32_t)lo[8 * q + 5] << 16, lo[8 * q + 6] | (uint32_t)lo[8 * q + 7] << 16);
         }
+    };
+    float4_t acc[2] = {float4_t{0.0f, 0.0f, 0.0f, 0.0f}, float4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+    const int th = wave & 1, nh = wave >> 1;
+    auto mfma_step = [&]() {
+#pragma unroll
+        for (int ks = 0; ks < 64; ks += 32) {
+            const int kc = ks + 8 * (lane / 16);
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&xs[16 * th + lane % 16][kc]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&rh[32 * nh + 16 * j + lane % 16][kc]);
+                const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(&rl[32 * nh + 16 * j + lane % 16][kc]);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[j], 0, 0, 0);
+            }
+        }
+    };
+    const int nk = H / 64;
+    St S0 = load(0), S1 = load(nk > 1 ? 1 : 0);
+    for (int kb = 0; kb < nk; kb += 2) {
+        store(S0);
         __syncthreads();
+        if (kb + 2 < nk) S0 = load(kb + 2);
+        mfma_step();
+        __syncthreads();
+        if (kb + 1 < nk) {
+            store(S1);
+            __syncthreads();
+            if (kb + 3 < nk) S1 = load(kb + 3);
+            mfma_step();
+            __syncthreads();
+        }
     }
-    // lane l, register r -> token t0 + 4 (l / 16) + r, row n0 + 16 wave + l % 16
-    const int n = n0 + 16 * wave + lane % 16;
+    // lane l, register r -> token t0 + 16 th + 4 (l / 16) + r, row n0 + 32 nh + 16 j + l % 16
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int t = t0 + 4 * (lane / 16) + r;
-        if (t >= T || n >= N) continue;
-        if (n < E) p.logits[(size_t)t * E + n] = acc[r] + (p.rbias ? p.rbias[n] : 0.0f);
-        else p.gate[t] = acc[r];
+    for (int j = 0; j < 2; ++j) {
+        const int n = n0 + 32 * nh + 16 * j + lane % 16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 16 * th + 4 * (lane / 16) + r;
+            if (t >= T || n >= N) continue;
+            if (n < E) p.logits[(size_t)t * E + n] = acc[j][r] + (p.rbias ? p.rbias[n] : 0.0f);
+            else p.gate[t] = acc[j][r];
+        }
     }
 }
 
@@ -241,64 +286,78 @@ __device__ __forceinline__ GroupW group_w2(const BatchedParams &p, int g) {
     return {p.s2.c, p.s2.s, p.s2.b, p.Is};
 }
 
-// Dequantise 16 consecutive codes of one row (4-bit: 8 bytes, low nibble first; 8-bit: 16 bytes)
-// to fp16 s * q + b and store them as two 16-byte LDS writes at dst.
+// ---- fp16 tiles in pair order ----------------------------------------------------------------------
+// Inside every 8-column block (4-bit) or 4-column block (8-bit) the fp16 tiles hold their columns in
+// the order the packed dequantisation produces them: 4-bit (0,4,1,5,2,6,3,7), 8-bit (0,2,1,3).
+// Both operands of every MFMA use the same order, so each product and each k-sum is that of the
+// natural order; h is stored in this order by gu_gemm for dn_gemm's A operand.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
 template <int BITS>
-__device__ __forceinline__ void dequant16(const uint4 raw, float s, float b, _Float16 *dst) {
-    half8_t lo, hi;
-    if constexpr (BITS == 4) {
-        const uint32_t w[2] = {raw.x, raw.y};
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const uint32_t c = (w[q / 4] >> (8 * (q % 4))) & 0xFFu;
-            const float v0 = fmaf(s, (float)(c & 0xF), b), v1 = fmaf(s, (float)(c >> 4), b);
-            if (q < 4) { lo[2 * q] = (_Float16)v0; lo[2 * q + 1] = (_Float16)v1; }
-            else { hi[2 * q - 8] = (_Float16)v0; hi[2 * q - 7] = (_Float16)v1; }
-        }
-    } else {
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const float v = fmaf(s, (float)((w[q / 4] >> (8 * (q % 4))) & 0xFFu), b);
-            if (q < 8) lo[q] = (_Float16)v;
-            else hi[q - 8] = (_Float16)v;
-        }
-    }
-    reinterpret_cast<half8_t *>(dst)[0] = lo;
-    reinterpret_cast<half8_t *>(dst)[1] = hi;
+__device__ __forceinline__ int pair_pos(int c) {  // position of column c (within its 64-column step)
+    if constexpr (BITS == 4) return (c & ~7) + 2 * (c & 3) + ((c >> 2) & 1);
+    else return (c & ~3) + 2 * (c & 1) + ((c >> 1) & 1);
 }
 
-// One thread's share of a weight k-step: row r (of the tile), 16 codes at column c16 * 16 of the
-// 64-column step `kb`, and that group's scale and bias.
+// Codes -> fp16 s q + b, two per instruction: a nibble (byte) masked into the mantissa of the fp16
+// constant 1024 is exactly 1024 + q; subtracting 1024 is exact; one packed fma rounds s q + b once.
+// 4-bit: a dword holds columns 0..7 of a block and gives pairs (p, p+4), p = 0..3.
+// 8-bit: a dword holds columns 0..3 of a block and gives pairs (p, p+2), p = 0..1.
 template <int BITS>
-struct WFrag {
-    uint4 raw;
-    uint16_t s, b;
-};
+__device__ __forceinline__ void dequant_dword(uint32_t w, half2_t s2, half2_t b2, half2_t *out) {
+    const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    constexpr int NP = BITS == 4 ? 4 : 2;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const uint32_t u = BITS == 4 ? (((w >> (4 * p)) & 0x000F000Fu) | 0x64006400u)
+                                     : (((w >> (8 * p)) & 0x00FF00FFu) | 0x64006400u);
+        const half2_t q = __builtin_bit_cast(half2_t, u) - k1024;
+        out[p] = __builtin_elementwise_fma(q, s2, b2);
+    }
+}
+__device__ __forceinline__ half2_t bf16_pair_to_f16(uint16_t a, uint16_t b) {
+    return half2_t{(_Float16)bf16_to_f32(a), (_Float16)bf16_to_f32(b)};
+}
+__device__ __forceinline__ half2_t bf16_splat_f16(uint16_t v) {
+    const _Float16 h = (_Float16)bf16_to_f32(v);
+    return half2_t{h, h};
+}
+// 16 bf16 activations (natural order) -> 16 fp16 in pair order (two blocks of 8 or four of 4).
 template <int BITS>
-__device__ __forceinline__ void wfrag_load(WFrag<BITS> &f, const GroupW &w, size_t row, int cols, int kb, int c16,
-                                           bool ok) {
-    if (!ok) {
-        f.raw = make_uint4(0, 0, 0, 0);
-        f.s = 0;
-        f.b = 0;
-        return;
+__device__ __forceinline__ void act16_to_pairs(const uint4 r0, const uint4 r1, half2_t *out) {
+    const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    uint16_t x[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        x[2 * i] = w[i] & 0xFFFF;
+        x[2 * i + 1] = w[i] >> 16;
     }
-    const uint8_t *cp = w.c + row * ((size_t)cols * BITS / 8) + ((size_t)kb * 64 + c16 * 16) * BITS / 8;
-    if constexpr (BITS == 4) {
-        const uint2 v = *reinterpret_cast<const uint2 *>(cp);
-        f.raw = make_uint4(v.x, v.y, 0, 0);
-    } else {
-        f.raw = *reinterpret_cast<const uint4 *>(cp);
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const uint16_t *v = x + 8 * blk;
+        if constexpr (BITS == 4) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) out[4 * blk + p] = bf16_pair_to_f16(v[p], v[p + 4]);
+        } else {
+            out[4 * blk + 0] = bf16_pair_to_f16(v[0], v[2]);
+            out[4 * blk + 1] = bf16_pair_to_f16(v[1], v[3]);
+            out[4 * blk + 2] = bf16_pair_to_f16(v[4], v[6]);
+            out[4 * blk + 3] = bf16_pair_to_f16(v[5], v[7]);
+        }
     }
-    f.s = w.s[row * (cols / 64) + kb];
-    f.b = w.b[row * (cols / 64) + kb];
 }
 
 // ---- 4. grouped gate|up + SwiGLU -----------------------------------------------------------------
-// Tile: 64 pair rows x 64 j (128 weight rows: 64 gate then 64 up), k-steps of 64 columns of H.
-// Wave w: rows 32 (w & 1) .. +32, j 32 (w >> 1) .. +32; 2 x 2 MFMA tiles each for gate and up, so
-// a lane holds gate and up of the same (row, j) and SwiGLU needs no exchange.
+// Tile: 64 pair rows x 64 j (128 weight rows: 64 gate then 64 up), k-steps of 64 columns of H (one
+// quantisation group). Wave w: rows 32 (w & 1) .. +32, j 32 (w >> 1) .. +32; 2 x 2 MFMA tiles each
+// for gate and up, so a lane holds gate and up of the same (row, j) and SwiGLU needs no exchange.
+// Global loads run two k-steps ahead of the MFMAs (register stages S0 / S1).
+template <int BITS>
+struct GuStage {
+    uint4 a0, a1;      // 16 bf16 of activation row ar
+    uint4 c0, c1;      // 32 codes of weight row br (c1 only at 8-bit)
+    uint16_t s, b;     // that row's group scale and bias
+};
 template <int BITS>
 __global__ void __launch_bounds__(kGemmThreads) gu_gemm(BatchedParams p) {
     __shared__ __align__(16) _Float16 As[kBM][kLdsK];
@@ -314,43 +373,53 @@ __global__ void __launch_bounds__(kGemmThreads) gu_gemm(BatchedParams p) {
     const int H = p.H, K = p.K;
     const int P0 = p.goff[g] + m0;
     const int M = min(kBM, p.gcnt[g] - m0);
-    // A loads: row ar = tid / 4, 16 columns at (tid % 4) * 16
-    const int ar = tid / 4, ac = (tid % 4) * 16;
+    const int ar = tid / 4, ac = (tid % 4) * 16;  // A: row, first of 16 columns
     const bool aok = ar < M;
     const uint16_t *xrow = p.x + (size_t)(aok ? p.perm[P0 + ar] / K : 0) * H;
-    // B loads: tile row br = tid / 2 (0..127), 16 codes at columns (tid % 2) * 16 and +32
-    const int br = tid / 2, bc = tid % 2;
+    const int br = tid / 2, bc = (tid % 2) * 32;  // B: tile row, first of 32 columns
     const size_t wrow = (br < 64) ? (size_t)(j0 + br) : (size_t)(w.inter + j0 + br - 64);
+    const uint8_t *crow = w.c + wrow * ((size_t)H * BITS / 8);
+    const int gpr = H / 64;
     const int nk = H / 64;
 
-    uint4 xa0, xa1;
-    WFrag<BITS> f0, f1;
-    auto load_step = [&](int kb) {
+    auto load = [&](int kb) {
+        GuStage<BITS> st;
         if (aok) {
             const uint4 *src = reinterpret_cast<const uint4 *>(xrow + kb * 64 + ac);
-            xa0 = src[0];
-            xa1 = src[1];
+            st.a0 = src[0];
+            st.a1 = src[1];
         } else {
-            xa0 = make_uint4(0, 0, 0, 0);
-            xa1 = xa0;
+            st.a0 = make_uint4(0, 0, 0, 0);
+            st.a1 = st.a0;
         }
-        wfrag_load<BITS>(f0, w, wrow, H, kb, bc, true);
-        wfrag_load<BITS>(f1, w, wrow, H, kb, bc + 2, true);
+        const uint4 *cp = reinterpret_cast<const uint4 *>(crow + ((size_t)kb * 64 + bc) * BITS / 8);
+        st.c0 = cp[0];
+        st.c1 = BITS == 8 ? cp[1] : make_uint4(0, 0, 0, 0);
+        st.s = w.s[wrow * gpr + kb];
+        st.b = w.b[wrow * gpr + kb];
+        return st;
     };
-    auto store_step = [&]() {
-        half8_t h0, h1;
-        const uint32_t a[8] = {xa0.x, xa0.y, xa0.z, xa0.w, xa1.x, xa1.y, xa1.z, xa1.w};
+    auto store = [&](const GuStage<BITS> &st) {
+        half2_t av[8];
+        act16_to_pairs<BITS>(st.a0, st.a1, av);
+        reinterpret_cast<uint4 *>(&As[ar][ac])[0] = __builtin_bit_cast(uint4, half8_t{av[0][0], av[0][1], av[1][0], av[1][1], av[2][0], av[2][1], av[3][0], av[3][1]});
+        reinterpret_cast<uint4 *>(&As[ar][ac])[1] = __builtin_bit_cast(uint4, half8_t{av[4][0], av[4][1], av[5][0], av[5][1], av[6][0], av[6][1], av[7][0], av[7][1]});
+        const half2_t s2 = bf16_splat_f16(st.s), b2 = bf16_splat_f16(st.b);
+        half2_t bv[16];
+        const uint32_t cw[8] = {st.c0.x, st.c0.y, st.c0.z, st.c0.w, st.c1.x, st.c1.y, st.c1.z, st.c1.w};
+        if constexpr (BITS == 4) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            h0[2 * q] = bf16_to_f16(a[q] & 0xFFFF);
-            h0[2 * q + 1] = bf16_to_f16(a[q] >> 16);
-            h1[2 * q] = bf16_to_f16(a[q + 4] & 0xFFFF);
-            h1[2 * q + 1] = bf16_to_f16(a[q + 4] >> 16);
+            for (int d = 0; d < 4; ++d) dequant_dword<4>(cw[d], s2, b2, bv + 4 * d);
+        } else {
+#pragma unroll
+            for (int d = 0; d < 8; ++d) dequant_dword<8>(cw[d], s2, b2, bv + 2 * d);
         }
-        reinterpret_cast<half8_t *>(&As[ar][ac])[0] = h0;
-        reinterpret_cast<half8_t *>(&As[ar][ac])[1] = h1;
-        dequant16<BITS>(f0.raw, bf16_to_f32(f0.s), bf16_to_f32(f0.b), &Bs[br][bc * 16]);
-        dequant16<BITS>(f1.raw, bf16_to_f32(f1.s), bf16_to_f32(f1.b), &Bs[br][bc * 16 + 32]);
+        uint4 *dst = reinterpret_cast<uint4 *>(&Bs[br][bc]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            dst[q] = __builtin_bit_cast(uint4, half8_t{bv[4 * q][0], bv[4 * q][1], bv[4 * q + 1][0], bv[4 * q + 1][1],
+                                                       bv[4 * q + 2][0], bv[4 * q + 2][1], bv[4 * q + 3][0],
+                                                       bv[4 * q + 3][1]});
     };
 
     float4_t ag[2][2], au[2][2];
@@ -362,11 +431,7 @@ __global__ void __launch_bounds__(kGemmThreads) gu_gemm(BatchedParams p) {
             au[i][j] = ag[i][j];
         }
     const int mh = wave & 1, jh = wave >> 1;
-    load_step(0);
-    for (int kb = 0; kb < nk; ++kb) {
-        store_step();
-        __syncthreads();
-        if (kb + 1 < nk) load_step(kb + 1);
+    auto mfma_step = [&]() {
 #pragma unroll
         for (int ks = 0; ks < 64; ks += 32) {
             const int kc = ks + 8 * (lane / 16);
@@ -386,9 +451,24 @@ __global__ void __launch_bounds__(kGemmThreads) gu_gemm(BatchedParams p) {
                     au[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bu[j], au[i][j], 0, 0, 0);
                 }
         }
+    };
+    GuStage<BITS> S0 = load(0), S1 = load(nk > 1 ? 1 : 0);
+    for (int kb = 0; kb < nk; kb += 2) {
+        store(S0);
         __syncthreads();
+        if (kb + 2 < nk) S0 = load(kb + 2);
+        mfma_step();
+        __syncthreads();
+        if (kb + 1 < nk) {
+            store(S1);
+            __syncthreads();
+            if (kb + 3 < nk) S1 = load(kb + 3);
+            mfma_step();
+            __syncthreads();
+        }
     }
-    // epilogue: lane l, register r -> row 32 mh + 16 i + 4 (l / 16) + r, j = j0 + 32 jh + 16 j + l % 16
+    // epilogue: lane l, register r -> row 32 mh + 16 i + 4 (l / 16) + r, j = j0 + 32 jh + 16 j + l % 16;
+    // h goes to its pair-order position (dn_gemm's A operand)
     const int Imax = p.Imax;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -403,7 +483,7 @@ __global__ void __launch_bounds__(kGemmThreads) gu_gemm(BatchedParams p) {
                 const float h = gv / (1.0f + expf(-gv)) * uv;
                 const _Float16 hh = (_Float16)h;
                 const _Float16 hl = (_Float16)(h - (float)hh);
-                const size_t o = (size_t)(P0 + m) * Imax + jj;
+                const size_t o = (size_t)(P0 + m) * Imax + pair_pos<BITS>(jj & 63) + (jj & ~63);
                 p.hh[o] = hh;
                 p.hl[o] = hl;
             }
@@ -412,6 +492,12 @@ __global__ void __launch_bounds__(kGemmThreads) gu_gemm(BatchedParams p) {
 // ---- 5. grouped down projection ------------------------------------------------------------------
 // Tile: 64 pair rows x 64 output rows n, k-steps of 64 columns of the group's inter. Wave w: rows
 // 32 (w & 1) .., n 32 (w >> 1) ..; each k-step runs the MFMA once on h hi and once on h lo.
+template <int BITS>
+struct DnStage {
+    uint4 h0, h1, l0, l1;  // 16 fp16 of h hi / lo, row ar (pair order)
+    uint4 c;               // 16 codes of weight row br (8 bytes used at 4-bit)
+    uint16_t s, b;
+};
 template <int BITS>
 __global__ void __launch_bounds__(kGemmThreads) dn_gemm(BatchedParams p) {
     __shared__ __align__(16) _Float16 Ah[kBM][kLdsK];
@@ -431,30 +517,55 @@ __global__ void __launch_bounds__(kGemmThreads) dn_gemm(BatchedParams p) {
     const bool aok = ar < M;
     const _Float16 *hrow = p.hh + (size_t)(P0 + (aok ? ar : 0)) * Imax;
     const _Float16 *lrow = p.hl + (size_t)(P0 + (aok ? ar : 0)) * Imax;
-    const int br = tid / 4, bc = tid % 4;  // 64 rows x 4 chunks of 16 codes
+    const int br = tid / 4, bc = (tid % 4) * 16;  // 64 rows x 4 chunks of 16 codes
     const size_t wrow = (size_t)(n0 + br);
+    const uint8_t *crow = w.c + wrow * ((size_t)w.inter * BITS / 8);
+    const int gpr = w.inter / 64;
     const int nk = w.inter / 64;
 
-    uint4 ha0, ha1, la0, la1;
-    WFrag<BITS> f;
-    auto load_step = [&](int kb) {
+    auto load = [&](int kb) {
+        DnStage<BITS> st;
         if (aok) {
             const uint4 *hs = reinterpret_cast<const uint4 *>(hrow + kb * 64 + ac);
             const uint4 *ls = reinterpret_cast<const uint4 *>(lrow + kb * 64 + ac);
-            ha0 = hs[0]; ha1 = hs[1];
-            la0 = ls[0]; la1 = ls[1];
+            st.h0 = hs[0]; st.h1 = hs[1];
+            st.l0 = ls[0]; st.l1 = ls[1];
         } else {
-            ha0 = make_uint4(0, 0, 0, 0);
-            ha1 = ha0; la0 = ha0; la1 = ha0;
+            st.h0 = make_uint4(0, 0, 0, 0);
+            st.h1 = st.h0; st.l0 = st.h0; st.l1 = st.h0;
         }
-        wfrag_load<BITS>(f, w, wrow, w.inter, kb, bc, true);
+        const uint8_t *cp = crow + ((size_t)kb * 64 + bc) * BITS / 8;
+        if constexpr (BITS == 4) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(cp);
+            st.c = make_uint4(v.x, v.y, 0, 0);
+        } else {
+            st.c = *reinterpret_cast<const uint4 *>(cp);
+        }
+        st.s = w.s[wrow * gpr + kb];
+        st.b = w.b[wrow * gpr + kb];
+        return st;
     };
-    auto store_step = [&]() {
-        reinterpret_cast<uint4 *>(&Ah[ar][ac])[0] = ha0;
-        reinterpret_cast<uint4 *>(&Ah[ar][ac])[1] = ha1;
-        reinterpret_cast<uint4 *>(&Al[ar][ac])[0] = la0;
-        reinterpret_cast<uint4 *>(&Al[ar][ac])[1] = la1;
-        dequant16<BITS>(f.raw, bf16_to_f32(f.s), bf16_to_f32(f.b), &Bs[br][bc * 16]);
+    auto store = [&](const DnStage<BITS> &st) {
+        reinterpret_cast<uint4 *>(&Ah[ar][ac])[0] = st.h0;
+        reinterpret_cast<uint4 *>(&Ah[ar][ac])[1] = st.h1;
+        reinterpret_cast<uint4 *>(&Al[ar][ac])[0] = st.l0;
+        reinterpret_cast<uint4 *>(&Al[ar][ac])[1] = st.l1;
+        const half2_t s2 = bf16_splat_f16(st.s), b2 = bf16_splat_f16(st.b);
+        half2_t bv[8];
+        const uint32_t cw[4] = {st.c.x, st.c.y, st.c.z, st.c.w};
+        if constexpr (BITS == 4) {
+            dequant_dword<4>(cw[0], s2, b2, bv);
+            dequant_dword<4>(cw[1], s2, b2, bv + 4);
+        } else {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) dequant_dword<8>(cw[d], s2, b2, bv + 2 * d);
+        }
+        uint4 *dst = reinterpret_cast<uint4 *>(&Bs[br][bc]);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            dst[q] = __builtin_bit_cast(uint4, half8_t{bv[4 * q][0], bv[4 * q][1], bv[4 * q + 1][0], bv[4 * q + 1][1],
+                                                       bv[4 * q + 2][0], bv[4 * q + 2][1], bv[4 * q + 3][0],
+                                                       bv[4 * q + 3][1]});
     };
 
     float4_t acc[2][2];
@@ -463,11 +574,7 @@ __global__ void __launch_bounds__(kGemmThreads) dn_gemm(BatchedParams p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     const int mh = wave & 1, nh = wave >> 1;
-    load_step(0);
-    for (int kb = 0; kb < nk; ++kb) {
-        store_step();
-        __syncthreads();
-        if (kb + 1 < nk) load_step(kb + 1);
+    auto mfma_step = [&]() {
 #pragma unroll
         for (int ks = 0; ks < 64; ks += 32) {
             const int kc = ks + 8 * (lane / 16);
@@ -487,7 +594,21 @@ __global__ void __launch_bounds__(kGemmThreads) dn_gemm(BatchedParams p) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[i], b[j], acc[i][j], 0, 0, 0);
                 }
         }
+    };
+    DnStage<BITS> S0 = load(0), S1 = load(nk > 1 ? 1 : 0);
+    for (int kb = 0; kb < nk; kb += 2) {
+        store(S0);
         __syncthreads();
+        if (kb + 2 < nk) S0 = load(kb + 2);
+        mfma_step();
+        __syncthreads();
+        if (kb + 1 < nk) {
+            store(S1);
+            __syncthreads();
+            if (kb + 3 < nk) S1 = load(kb + 3);
+            mfma_step();
+            __syncthreads();
+        }
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
