@@ -161,16 +161,18 @@ __device__ __forceinline__ void dma_wait_but(int n) {
 
 // Copy n rows of `bytes` bytes each (a power of two, a multiple of U = 16 or 4; src_of(r) aligned
 // to U) into LDS at dst + r * bytes. Unit u = r * (bytes / U) + c is lane u % 64 of instruction
-// u / 64; wave w issues instructions w, w + 8, ...
+// u / 64; wave w issues instructions w, w + 8, ... With swz != 0 (U = 16 only) LDS chunk c of row r
+// receives source chunk c ^ ((r & swz) << 1): the 32-byte blocks of a row are XOR-permuted by the
+// row index, so a column block read across consecutive rows spreads over the LDS banks.
 template <int U, typename SrcOf>
-__device__ __forceinline__ void dma_rows(int n, int bytes, SrcOf src_of, char *dst) {
+__device__ __forceinline__ void dma_rows(int n, int bytes, SrcOf src_of, char *dst, int swz = 0) {
     const int sh = __builtin_ctz(static_cast<unsigned>(bytes / U)), total = n << sh;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     for (int i = wave; i * kWave < total; i += kWaves) {
         const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(dst + (size_t)i * kWave * U));
         const int u = i * kWave + lane;
         if (u < total) {
-            const int r = u >> sh, c = u & ((1 << sh) - 1);
+            const int r = u >> sh, c = (u & ((1 << sh) - 1)) ^ ((r & swz) << 1);
             const char *g = src_of(r) + (size_t)c * U;
             if constexpr (U == 16) dma16(g, m0);
             else dma4(g, m0);
@@ -197,11 +199,13 @@ __device__ __forceinline__ Rows rows_at(char *base, int n, int cols, int bits) {
 __device__ __forceinline__ int dma_qrows_count(int n, int cols, int bits) {
     return dma_count(n * (cols * bits / 8) / 16) + 2 * dma_count(n * (cols / 32) / 4);
 }
-// Stage n rows; row r of the matrix family q is matrix row row_of(r) (64-bit), cols columns.
+// Stage n rows; row r of the matrix family q is matrix row row_of(r) (64-bit), cols columns; swz
+// permutes the code blocks as in dma_rows (scales and biases are never permuted).
 template <typename RowOf>
-__device__ __forceinline__ void dma_qrows(const QMat &q, int cols, int bits, int n, RowOf row_of, const Rows &dst) {
+__device__ __forceinline__ void dma_qrows(const QMat &q, int cols, int bits, int n, RowOf row_of, const Rows &dst,
+                                          int swz = 0) {
     const size_t cb = (size_t)cols * bits / 8, gpr = cols / 64;
-    dma_rows<16>(n, dst.cb, [&](int r) { return reinterpret_cast<const char *>(q.c + row_of(r) * cb); }, dst.c);
+    dma_rows<16>(n, dst.cb, [&](int r) { return reinterpret_cast<const char *>(q.c + row_of(r) * cb); }, dst.c, swz);
     dma_rows<4>(n, dst.sb, [&](int r) { return reinterpret_cast<const char *>(q.s + row_of(r) * gpr); }, dst.s);
     dma_rows<4>(n, dst.sb, [&](int r) { return reinterpret_cast<const char *>(q.b + row_of(r) * gpr); }, dst.b);
 }
@@ -513,10 +517,14 @@ __device__ __forceinline__ void stage_shared_gu(const DecodeParams &p, int l, co
     dma_qrows(L.s13, p.H, p.bits, 2 * np,
               [&](int r) -> size_t { return (size_t)((r & 1) * Is + b + (r >> 1) * g); }, sg_rows(p, s));
 }
+// Block permutation of staged 4-bit down rows (see dma_rows): the MFMA down projection reads one
+// 64-column group of 16 consecutive staged rows at a time.
+__device__ __forceinline__ int down_swz(int bits, int cols) { return bits == 4 ? min(cols / 64, 8) - 1 : 0; }
 __device__ __forceinline__ void stage_shared_down(const DecodeParams &p, int l, const Lds &s, int r0, int nr) {
     if (!p.Is || nr <= 0) return;
     const LayerPtrs L = layer_ptrs(p, l);
-    dma_qrows(L.s2, p.Is, p.bits, nr, [&](int r) -> size_t { return (size_t)(r0 + r); }, sd_rows(p, s));
+    dma_qrows(L.s2, p.Is, p.bits, nr, [&](int r) -> size_t { return (size_t)(r0 + r); }, sd_rows(p, s),
+              down_swz(p.bits, p.Is));
 }
 // Routed down rows r0..r0+nr-1 of token t's K experts: staged row k * nr + rl.
 __device__ __forceinline__ void stage_routed_down(const DecodeParams &p, int l, const Lds &s, int t, int r0,
@@ -530,7 +538,7 @@ __device__ __forceinline__ void stage_routed_down(const DecodeParams &p, int l, 
                   const int k = div_by(r, nrm), rl = r - k * nr;
                   return expert_at(s.sidx[t * K + k], E) * H + (size_t)(r0 + rl);
               },
-              rd_rows(p, s));
+              rd_rows(p, s), down_swz(p.bits, p.I));
 }
 
 // ---- layer input ---------------------------------------------------------------------------------
@@ -772,6 +780,103 @@ __device__ void down_rows(const Lds &s, const Rows &R, int nv, int len, int nr, 
     }
 }
 
+// ---- down projection on MFMA (4-bit rows) ------------------------------------------------------------
+// v_mfma_f32_16x16x32_bf16 serves as the dot-product engine. Jobs (v, rl) of nv vectors x nr rows
+// are numbered job = v * nr + rl (the staged row); a tile is th = 16 (8 when nr == 1) consecutive
+// jobs, which touch at most 8 vectors. A row 2u / 2u + 1 = bf16 hi / lo halves of the tile's u-th
+// vector; B column i = weight row i of the tile, codes turned into the exact bf16 values 128 + q.
+// Column i uses only its own vector's two rows; the other products are never read. A second MFMA
+// with B = zero-point codes (136) gives, in the same lanes and with the same hardware summation,
+// the reference sum, so (acc - ref) is exact and an all-zero-point row gives exactly 0. Per
+// 64-column quantisation group: sum = s (acc - ref) + (b + 8 s) sum(h).
+// Operand layouts (lane l, i = l % 16, kb = l / 16): A[i][8 kb + e], B[8 kb + e][i] and
+// C[4 kb + r][i], so lane (i, kb) ends with weight row i against vectors 2 kb and 2 kb + 1: one
+// scale and bias per lane and group, hi + lo added in the lane. In k-step j of group g lane kb
+// takes code dword 2 kb + j of the group's 8 (one 8-byte read serves both k-steps) and the
+// matching 4 pair words of h; within a dword both operands hold the columns in the pair order
+// (0,4,1,5,2,6,3,7) of the h pair table.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct DnGroup {  // one lane's operands for one quantisation group
+    uint4 h0, h1;
+    uint2 q;
+    uint32_t sv, bv;
+    float sh0, sh1;  // sum(h) of the group's two slices (added only when used)
+};
+
+__device__ void down_tile_mfma4(const Lds &s, const Rows &R, int nv, int len, int nr, uint32_t nrm, int th, int tau,
+                                int sl0, float *out, int RB) {
+    const int lane = threadIdx.x % kWave, i = lane % 16, kb = lane / 16;
+    const int njobs = nv * nr, j0 = tau * th, jn = min(j0 + th, njobs);
+    const int spv = len / 32, ng = len / 64, gm = min(ng, 8) - 1;
+    const int vfirst = div_by(j0, nrm), nsp = div_by(jn - 1, nrm) - vfirst + 1;
+    // B column i: weight row j0 + i (columns past the tile repeat its first row, unused)
+    const bool wok = i < th && j0 + i < jn;
+    const int wrow = wok ? j0 + i : j0, vi = div_by(wrow, nrm), us = vi - vfirst;
+    const bool own = wok && (us >> 1) == kb;
+    const bool odd = (us & 1) != 0;
+    const char *qbase = R.c + (size_t)wrow * R.cb + kb * 8;
+    const int qswz = wrow & gm;
+    const uint16_t *sp = reinterpret_cast<const uint16_t *>(R.s + (size_t)wrow * R.sb);
+    const uint16_t *bp = reinterpret_cast<const uint16_t *>(R.b + (size_t)wrow * R.sb);
+    const SliceRef *hr = s.href + (sl0 + vi * spv);
+    // A row i: half (i & 1) of tile vector min(i / 2, nsp - 1)
+    const int V = vfirst + min(i >> 1, nsp - 1);
+    const uint32_t *hbase = s.hp + (size_t)(sl0 + V * spv + (kb >> 1)) * 36 + (i & 1) * 16 + (kb & 1) * 8;
+    auto load = [&](int g) -> DnGroup {
+        DnGroup d;
+        d.h0 = *reinterpret_cast<const uint4 *>(hbase + (size_t)g * 72);
+        d.h1 = *reinterpret_cast<const uint4 *>(hbase + (size_t)g * 72 + 4);
+        d.q = *reinterpret_cast<const uint2 *>(qbase + ((g ^ qswz) * 32));
+        d.sv = sp[g];
+        d.bv = bp[g];
+        d.sh0 = hr[2 * g].sum;
+        d.sh1 = hr[2 * g + 1].sum;
+        return d;
+    };
+    const bf16x8_t bzero = __builtin_bit_cast(bf16x8_t, make_uint4(0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u));
+    auto unpack = [](uint32_t w) -> bf16x8_t {
+        return __builtin_bit_cast(bf16x8_t, make_uint4((w & 0x000F000Fu) | kMagic, ((w >> 4) & 0x000F000Fu) | kMagic,
+                                                       ((w >> 8) & 0x000F000Fu) | kMagic,
+                                                       ((w >> 12) & 0x000F000Fu) | kMagic));
+    };
+    float acc = 0.0f;
+    auto step = [&](const DnGroup &d) {
+        const bf16x8_t h0 = __builtin_bit_cast(bf16x8_t, d.h0), h1 = __builtin_bit_cast(bf16x8_t, d.h1);
+        f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f}, z = {0.0f, 0.0f, 0.0f, 0.0f};
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h0, unpack(d.q.x), c, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h0, bzero, z, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h1, unpack(d.q.y), c, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h1, bzero, z, 0, 0, 0);
+        const float xh = odd ? c[2] - z[2] : c[0] - z[0], xl = odd ? c[3] - z[3] : c[1] - z[1];
+        const float sv = __uint_as_float(d.sv << 16), bv = __uint_as_float(d.bv << 16);
+        acc += sv * (xh + xl) + fmaf(8.0f, sv, bv) * (d.sh0 + d.sh1);
+    };
+    // two groups in flight (ng is even)
+    DnGroup ga = load(0);
+    for (int g = 0; g < ng; g += 2) {
+        const DnGroup gb = load(g + 1);
+        step(ga);
+        ga = load(min(g + 2, ng - 1));
+        step(gb);
+    }
+    if (own) out[vi * RB + (wrow - vi * nr)] = acc;
+}
+
+// Every routed vector (rows from rd) and the shared vector (rows from sd) of one token; tiles are
+// dealt round-robin over the waves.
+__device__ void down_all_mfma4(const Lds &s, const Rows &rd, const Rows &sd, int K, int I, int Is, int nr,
+                               uint32_t nrm, float *out, int RB) {
+    const int wave = threadIdx.x / kWave;
+    const int th = nr >= 2 ? 16 : 8;
+    const int nrt = (K * nr + th - 1) / th, nst = Is ? (nr + th - 1) / th : 0;
+    for (int u = wave; u < nrt + nst; u += kWaves) {
+        if (u < nrt) down_tile_mfma4(s, rd, K, I, nr, nrm, th, u, 0, out, RB);
+        else down_tile_mfma4(s, sd, 1, Is, nr, nrm, th, u - nrt, K * I / 32, out + K * RB, RB);
+    }
+}
+
 // ---- routing of every token (identical in every workgroup) ---------------------------------------
 // Wave t selects token t's experts (wave_topk); gamma from the shared-gate logit (column E).
 __device__ void route_tokens(const DecodeParams &p, const Lds &s) {
@@ -896,8 +1001,12 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
             lds_barrier();
             if (nr > 0) {
                 float *pt = s.part + (size_t)t * (K + 1) * RB;
-                down_rows<BITS>(s, rd_rows(p, s), K, I, nr, w.nrm, 0, pt, RB);
-                if (Is) down_rows<BITS>(s, sd_rows(p, s), 1, Is, nr, w.nrm, KI / 32, pt + K * RB, RB);
+                if constexpr (BITS == 4) {
+                    down_all_mfma4(s, rd_rows(p, s), sd_rows(p, s), K, I, Is, nr, w.nrm, pt, RB);
+                } else {
+                    down_rows<BITS>(s, rd_rows(p, s), K, I, nr, w.nrm, 0, pt, RB);
+                    if (Is) down_rows<BITS>(s, sd_rows(p, s), 1, Is, nr, w.nrm, KI / 32, pt + K * RB, RB);
+                }
             }
             lds_barrier();
             if (t + 1 < T) stage_routed_down(p, l, s, t + 1, r0, nr, w.nrm);
