@@ -432,6 +432,11 @@ struct Lds {
     SliceRef *href;  // [(K*I + Is)/32]
     float *part;     // [T][K+1][RB] down-projection rows of this workgroup (slot K = shared)
     float *red;      // [64] reduction scratch
+    // 4-bit rows only: activations as three int8 limbs per 64-column group (see build_limbs)
+    int8_t *xq;      // [T][H/64][3][64]
+    float2 *xsx;     // [T][H/64] (sum of the limb values, group scale)
+    int8_t *hq;      // [(K*I + Is)/64][3][64] h of one token (routed vectors, then the shared one)
+    float2 *hsx;     // [(K*I + Is)/64]
 };
 __device__ __forceinline__ Lds carve(const DecodeParams &p, char *smem) {
     const DecodeLds &o = p.lds;
@@ -451,6 +456,10 @@ __device__ __forceinline__ Lds carve(const DecodeParams &p, char *smem) {
     s.href = reinterpret_cast<SliceRef *>(smem + o.href);
     s.part = reinterpret_cast<float *>(smem + o.part);
     s.red = reinterpret_cast<float *>(smem + o.red);
+    s.xq = reinterpret_cast<int8_t *>(smem + o.xq);
+    s.xsx = reinterpret_cast<float2 *>(smem + o.xsx);
+    s.hq = reinterpret_cast<int8_t *>(smem + o.hq);
+    s.hsx = reinterpret_cast<float2 *>(smem + o.hsx);
     return s;
 }
 
@@ -508,6 +517,9 @@ __device__ __forceinline__ Rows sd_rows(const DecodeParams &p, const Lds &s) {
 __device__ __forceinline__ Rows rd_rows(const DecodeParams &p, const Lds &s) {
     return rows_at(s.rd, p.K * p.rows_per_wg, p.I, p.bits);
 }
+// Block permutation of staged 4-bit rows (see dma_rows): the MFMA dot products read one 64-column
+// group of 16 consecutive staged rows at a time.
+__device__ __forceinline__ int mfma_swz(int bits, int cols) { return bits == 4 ? min(cols / 64, 8) - 1 : 0; }
 // Shared gate|up rows of this workgroup's pairs: staged row 2r = gate row j, 2r+1 = up row Is + j,
 // j = b + r * grid.
 __device__ __forceinline__ void stage_shared_gu(const DecodeParams &p, int l, const Lds &s, const WgShare &w) {
@@ -515,16 +527,14 @@ __device__ __forceinline__ void stage_shared_gu(const DecodeParams &p, int l, co
     if (np == 0) return;
     const LayerPtrs L = layer_ptrs(p, l);
     dma_qrows(L.s13, p.H, p.bits, 2 * np,
-              [&](int r) -> size_t { return (size_t)((r & 1) * Is + b + (r >> 1) * g); }, sg_rows(p, s));
+              [&](int r) -> size_t { return (size_t)((r & 1) * Is + b + (r >> 1) * g); }, sg_rows(p, s),
+              mfma_swz(p.bits, p.H));
 }
-// Block permutation of staged 4-bit down rows (see dma_rows): the MFMA down projection reads one
-// 64-column group of 16 consecutive staged rows at a time.
-__device__ __forceinline__ int down_swz(int bits, int cols) { return bits == 4 ? min(cols / 64, 8) - 1 : 0; }
 __device__ __forceinline__ void stage_shared_down(const DecodeParams &p, int l, const Lds &s, int r0, int nr) {
     if (!p.Is || nr <= 0) return;
     const LayerPtrs L = layer_ptrs(p, l);
     dma_qrows(L.s2, p.Is, p.bits, nr, [&](int r) -> size_t { return (size_t)(r0 + r); }, sd_rows(p, s),
-              down_swz(p.bits, p.Is));
+              mfma_swz(p.bits, p.Is));
 }
 // Routed down rows r0..r0+nr-1 of token t's K experts: staged row k * nr + rl.
 __device__ __forceinline__ void stage_routed_down(const DecodeParams &p, int l, const Lds &s, int t, int r0,
@@ -538,7 +548,79 @@ __device__ __forceinline__ void stage_routed_down(const DecodeParams &p, int l, 
                   const int k = div_by(r, nrm), rl = r - k * nr;
                   return expert_at(s.sidx[t * K + k], E) * H + (size_t)(r0 + rl);
               },
-              rd_rows(p, s), down_swz(p.bits, p.I));
+              rd_rows(p, s), mfma_swz(p.bits, p.I));
+}
+
+// ---- activations as int8 limbs (4-bit rows) ------------------------------------------------------
+// The 4-bit dot products run on v_mfma_i32_16x16x64_i8 in exact integer arithmetic. A 64-column
+// group of activations v is held as the integers X = rint(v / 2^e), e taken from the group's
+// largest magnitude so that |X| <= 2^22, each split into three signed 8-bit limbs
+// X = L0 2^16 + L1 2^8 + L2 (L1, L2 balanced in [-128, 127], |L0| <= 65). With the codes entering
+// as the bytes 16 (q - 8), C_j = sum 16 (q - 8) L_j is an exact integer (|C_j| <= 2^20) and
+//   sum((s q + b) v) = 2^(e-4) (s comb3(C_0, C_1, C_2) + (b + 8 s) 16 comb3(sum L_0, sum L_1, sum L_2));
+// the group entry keeps (16 comb3 of the limb sums, 2^(e-4)). Codes all at the zero point with
+// b = -8 s give exactly 0 (every C_j is 0 and b + 8 s rounds to 0).
+// Position p of a 64-byte limb row holds column limb_col(p): lane kb of an MFMA takes the code
+// dwords 2 kb and 2 kb + 1 of the group, whose nibbles code_bytes turns into 16 bytes in the order
+// (0,2,4,6, 1,3,5,7, 8,10,12,14, 9,11,13,15) + 16 kb.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int limb_col(int p) {
+    const int e = p & 15;
+    return 16 * (p >> 4) + ((e >> 3) << 3) + 2 * (e & 3) + ((e >> 2) & 1);
+}
+// Codes as the signed bytes 16 (q - 8): q ^ 8 is the 4-bit two's complement of q - 8, moved to
+// the top of its byte.
+__device__ __forceinline__ i32x4_t code_bytes(uint2 q) {
+    const uint32_t w0 = q.x ^ 0x88888888u, w1 = q.y ^ 0x88888888u;
+    return i32x4_t{(int)((w0 << 4) & 0xF0F0F0F0u), (int)(w0 & 0xF0F0F0F0u), (int)((w1 << 4) & 0xF0F0F0F0u),
+                   (int)(w1 & 0xF0F0F0F0u)};
+}
+__device__ __forceinline__ float comb3(int a0, int a1, int a2) {
+    return fmaf((float)(a0 * 256 + a1), 256.0f, (float)a2);  // |a0| <= 2^20: a0 * 256 + a1 fits
+}
+__device__ __forceinline__ int row16_sum(int v) {
+    v += (int)dpp_u32<kDppQuadXor1>((uint32_t)v);
+    v += (int)dpp_u32<kDppQuadXor2>((uint32_t)v);
+    v += (int)dpp_u32<kDppHalfMirror>((uint32_t)v);
+    v += (int)dpp_u32<kDppRowMirror>((uint32_t)v);
+    return v;
+}
+// Called by the 16 lanes of one DPP row for one group: lane m holds the values of positions
+// 4m .. 4m+3 and writes limb dword m of rows 0..2 at dst; lane 0 writes the group entry.
+__device__ __forceinline__ void build_limbs(const float (&v)[4], int8_t *dst, float2 *entry) {
+    const int m = threadIdx.x & 15;
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    amax = fmaxf(amax, dpp_f32<kDppQuadXor1>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppQuadXor2>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppHalfMirror>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppRowMirror>(amax));
+    int ex = 0;
+    if (amax > 0.0f) {
+        frexpf(amax, &ex);  // amax < 2^ex
+        ex -= 22;
+    }
+    uint32_t w0 = 0, w1 = 0, w2 = 0;
+    int s0 = 0, s1 = 0, s2 = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int X = (int)rintf(ldexpf(v[e], -ex));
+        const int l2 = ((X + 128) & 255) - 128, x1 = (X - l2) >> 8;
+        const int l1 = ((x1 + 128) & 255) - 128, l0 = (x1 - l1) >> 8;
+        w0 |= (uint32_t)(l0 & 255) << (8 * e);
+        w1 |= (uint32_t)(l1 & 255) << (8 * e);
+        w2 |= (uint32_t)(l2 & 255) << (8 * e);
+        s0 += l0;
+        s1 += l1;
+        s2 += l2;
+    }
+    s0 = row16_sum(s0);
+    s1 = row16_sum(s1);
+    s2 = row16_sum(s2);
+    reinterpret_cast<uint32_t *>(dst)[m] = w0;
+    reinterpret_cast<uint32_t *>(dst + 64)[m] = w1;
+    reinterpret_cast<uint32_t *>(dst + 128)[m] = w2;
+    if (m == 0) *entry = make_float2(16.0f * comb3(s0, s1, s2), ldexpf(1.0f, ex - 4));
 }
 
 // ---- layer input ---------------------------------------------------------------------------------
@@ -589,13 +671,46 @@ __device__ bool layer_input(const DecodeParams &p, int l, uint32_t ep, const Lds
             col_pair<BITS>(h & 31, q, half);
             G(p.x_all)[(size_t)l * T * H + i] = static_cast<uint16_t>(s.xp[(t * nsl + sl) * 20 + q] >> (16 * half));
         }
-    for (int i = threadIdx.x; i < T * nsl; i += blockDim.x) {
-        uint32_t v[16];
-        for (int q = 0; q < 16; ++q) v[q] = s.xp[i * 20 + q];
-        s.xref[i] = slice_ref<BITS>(v, 1, v);
+    if constexpr (BITS == 8) {
+        for (int i = threadIdx.x; i < T * nsl; i += blockDim.x) {
+            uint32_t v[16];
+            for (int q = 0; q < 16; ++q) v[q] = s.xp[i * 20 + q];
+            s.xref[i] = slice_ref<BITS>(v, 1, v);
+        }
     }
     lds_barrier();
     return true;
+}
+
+// ---- x as limbs (4-bit rows) -------------------------------------------------------------------------
+// The limb table overwrites the bf16 pairs of x (same LDS region), so every thread first reads its
+// items into registers, then all write after a barrier; called once the router has read x.
+__device__ void build_x_limbs(const DecodeParams &p, const Lds &s) {
+    const int T = p.T, nsl = p.H / 32, ng = p.H / 64, lng = __builtin_ctz(static_cast<unsigned>(ng));
+    const int n = T * ng * 16;  // 16 lanes per group; n and the block size are multiples of 16
+    constexpr int kItems = 8;   // n <= 8 * 512 (T <= 8, H <= 2048)
+    float v[kItems][4];
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        const int it = threadIdx.x + k * kDecodeThreads;
+        if (it < n) {
+            const int tg = it >> 4, m = it & 15, t = tg >> lng, g = tg & (ng - 1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int col = 64 * g + limb_col(4 * m + e);
+                int q, half;
+                col_pair<4>(col & 31, q, half);
+                v[k][e] = bf16_to_f32((s.xp[(t * nsl + (col >> 5)) * 20 + q] >> (16 * half)) & 0xFFFFu);
+            }
+        }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        const int it = threadIdx.x + k * kDecodeThreads;
+        if (it < n) build_limbs(v[k], s.xq + (size_t)(it >> 4) * 192, s.xsx + (it >> 4));
+    }
+    lds_barrier();
 }
 
 // ---- router --------------------------------------------------------------------------------------
@@ -780,86 +895,88 @@ __device__ void down_rows(const Lds &s, const Rows &R, int nv, int len, int nr, 
     }
 }
 
+// ---- h of one token as limbs (4-bit rows) ------------------------------------------------------------
+__device__ bool stage_h4(const DecodeParams &p, const Lds &s, const uint64_t *src, uint32_t ep) {
+    const int n = p.K * p.I + p.Is;
+    const float *hf = reinterpret_cast<const float *>(s.hp);
+    if (!ll_gather<false>(src, n, ep, reinterpret_cast<float *>(s.hp), p.ctrl, p.spin_limit)) return false;
+    // 16 lanes per group; n / 4 and the block size are multiples of 16, so DPP rows stay whole
+    for (int it = threadIdx.x; it < n / 4; it += blockDim.x) {
+        const int gi = it >> 4, m = it & 15;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = hf[gi * 64 + limb_col(4 * m + e)];
+        build_limbs(v, s.hq + (size_t)gi * 192, s.hsx + gi);
+    }
+    lds_barrier();
+    return true;
+}
+
 // ---- down projection on MFMA (4-bit rows) ------------------------------------------------------------
-// v_mfma_f32_16x16x32_bf16 serves as the dot-product engine. Jobs (v, rl) of nv vectors x nr rows
-// are numbered job = v * nr + rl (the staged row); a tile is th = 16 (8 when nr == 1) consecutive
-// jobs, which touch at most 8 vectors. A row 2u / 2u + 1 = bf16 hi / lo halves of the tile's u-th
-// vector; B column i = weight row i of the tile, codes turned into the exact bf16 values 128 + q.
-// Column i uses only its own vector's two rows; the other products are never read. A second MFMA
-// with B = zero-point codes (136) gives, in the same lanes and with the same hardware summation,
-// the reference sum, so (acc - ref) is exact and an all-zero-point row gives exactly 0. Per
-// 64-column quantisation group: sum = s (acc - ref) + (b + 8 s) sum(h).
-// Operand layouts (lane l, i = l % 16, kb = l / 16): A[i][8 kb + e], B[8 kb + e][i] and
-// C[4 kb + r][i], so lane (i, kb) ends with weight row i against vectors 2 kb and 2 kb + 1: one
-// scale and bias per lane and group, hi + lo added in the lane. In k-step j of group g lane kb
-// takes code dword 2 kb + j of the group's 8 (one 8-byte read serves both k-steps) and the
-// matching 4 pair words of h; within a dword both operands hold the columns in the pair order
-// (0,4,1,5,2,6,3,7) of the h pair table.
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-struct DnGroup {  // one lane's operands for one quantisation group
-    uint4 h0, h1;
-    uint2 q;
-    uint32_t sv, bv;
-    float sh0, sh1;  // sum(h) of the group's two slices (added only when used)
-};
-
+// Jobs (v, rl) of nv vectors x nr rows are numbered job = v * nr + rl (the staged row); a tile is
+// th = min(16, 3 nr + 1) consecutive jobs, which touch at most 4 vectors. A row 4u + j = limb j of
+// the tile's u-th vector (row 4u + 3 repeats limb 2); B column i = the codes of weight row i of the
+// tile. Operand layouts (lane l, i = l % 16, kb = l / 16): A[i][16 kb + e], B[16 kb + e][i],
+// C[4 kb + r][i], so lane (i, kb) ends with weight row i against the three limbs of tile vector
+// kb: it owns row i when that is the row's vector. Groups of h: gbase + v * len / 64 + g.
 __device__ void down_tile_mfma4(const Lds &s, const Rows &R, int nv, int len, int nr, uint32_t nrm, int th, int tau,
-                                int sl0, float *out, int RB) {
+                                int gbase, float *out, int RB) {
     const int lane = threadIdx.x % kWave, i = lane % 16, kb = lane / 16;
     const int njobs = nv * nr, j0 = tau * th, jn = min(j0 + th, njobs);
-    const int spv = len / 32, ng = len / 64, gm = min(ng, 8) - 1;
+    const int ngv = len / 64, gm = min(ngv, 8) - 1;
     const int vfirst = div_by(j0, nrm), nsp = div_by(jn - 1, nrm) - vfirst + 1;
     // B column i: weight row j0 + i (columns past the tile repeat its first row, unused)
     const bool wok = i < th && j0 + i < jn;
-    const int wrow = wok ? j0 + i : j0, vi = div_by(wrow, nrm), us = vi - vfirst;
-    const bool own = wok && (us >> 1) == kb;
-    const bool odd = (us & 1) != 0;
+    const int wrow = wok ? j0 + i : j0, vi = div_by(wrow, nrm);
+    const bool own = wok && vi - vfirst == kb;
     const char *qbase = R.c + (size_t)wrow * R.cb + kb * 8;
     const int qswz = wrow & gm;
     const uint16_t *sp = reinterpret_cast<const uint16_t *>(R.s + (size_t)wrow * R.sb);
     const uint16_t *bp = reinterpret_cast<const uint16_t *>(R.b + (size_t)wrow * R.sb);
-    const SliceRef *hr = s.href + (sl0 + vi * spv);
-    // A row i: half (i & 1) of tile vector min(i / 2, nsp - 1)
-    const int V = vfirst + min(i >> 1, nsp - 1);
-    const uint32_t *hbase = s.hp + (size_t)(sl0 + V * spv + (kb >> 1)) * 36 + (i & 1) * 16 + (kb & 1) * 8;
-    auto load = [&](int g) -> DnGroup {
-        DnGroup d;
-        d.h0 = *reinterpret_cast<const uint4 *>(hbase + (size_t)g * 72);
-        d.h1 = *reinterpret_cast<const uint4 *>(hbase + (size_t)g * 72 + 4);
-        d.q = *reinterpret_cast<const uint2 *>(qbase + ((g ^ qswz) * 32));
-        d.sv = sp[g];
-        d.bv = bp[g];
-        d.sh0 = hr[2 * g].sum;
-        d.sh1 = hr[2 * g + 1].sum;
+    // A row i: limb min(i % 4, 2) of tile vector min(i / 4, nsp - 1)
+    const int va = vfirst + min(i >> 2, nsp - 1), ja = min(i & 3, 2);
+    const int8_t *abase = s.hq + ((size_t)(gbase + va * ngv) * 3 + ja) * 64 + 16 * kb;
+    // group entries of this lane's vector (tile vector kb)
+    const float2 *gsx = s.hsx + gbase + (vfirst + min(kb, nsp - 1)) * ngv;
+    // operands of the group pair (g, g + 1), g even; the next pair's loads are issued before the
+    // current pair's math (scheduling barriers keep the compiler from sinking them)
+    struct Pair {
+        i32x4_t a0, a1;
+        uint2 q0, q1;
+        uint32_t sv, bv;  // bf16 scale / bias of groups g (low half) and g + 1 (high half)
+        float4 gx;        // entries of groups g and g + 1
+    };
+    auto load = [&](int g) -> Pair {
+        Pair d;
+        d.a0 = *reinterpret_cast<const i32x4_t *>(abase + (size_t)g * 192);
+        d.a1 = *reinterpret_cast<const i32x4_t *>(abase + (size_t)g * 192 + 192);
+        d.q0 = *reinterpret_cast<const uint2 *>(qbase + ((g ^ qswz) * 32));
+        d.q1 = *reinterpret_cast<const uint2 *>(qbase + (((g + 1) ^ qswz) * 32));
+        d.sv = *reinterpret_cast<const uint32_t *>(sp + g);
+        d.bv = *reinterpret_cast<const uint32_t *>(bp + g);
+        d.gx = *reinterpret_cast<const float4 *>(gsx + g);
         return d;
     };
-    const bf16x8_t bzero = __builtin_bit_cast(bf16x8_t, make_uint4(0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u));
-    auto unpack = [](uint32_t w) -> bf16x8_t {
-        return __builtin_bit_cast(bf16x8_t, make_uint4((w & 0x000F000Fu) | kMagic, ((w >> 4) & 0x000F000Fu) | kMagic,
-                                                       ((w >> 8) & 0x000F000Fu) | kMagic,
-                                                       ((w >> 12) & 0x000F000Fu) | kMagic));
-    };
     float acc = 0.0f;
-    auto step = [&](const DnGroup &d) {
-        const bf16x8_t h0 = __builtin_bit_cast(bf16x8_t, d.h0), h1 = __builtin_bit_cast(bf16x8_t, d.h1);
-        f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f}, z = {0.0f, 0.0f, 0.0f, 0.0f};
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h0, unpack(d.q.x), c, 0, 0, 0);
-        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h0, bzero, z, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h1, unpack(d.q.y), c, 0, 0, 0);
-        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h1, bzero, z, 0, 0, 0);
-        const float xh = odd ? c[2] - z[2] : c[0] - z[0], xl = odd ? c[3] - z[3] : c[1] - z[1];
-        const float sv = __uint_as_float(d.sv << 16), bv = __uint_as_float(d.bv << 16);
-        acc += sv * (xh + xl) + fmaf(8.0f, sv, bv) * (d.sh0 + d.sh1);
+    auto step = [&](const Pair &d) {
+        const i32x4_t zero = {0, 0, 0, 0};
+        const i32x4_t c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(d.a0, code_bytes(d.q0), zero, 0, 0, 0);
+        const i32x4_t c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(d.a1, code_bytes(d.q1), zero, 0, 0, 0);
+        const float s0 = __uint_as_float(d.sv << 16), b0 = __uint_as_float(d.bv << 16);
+        const float s1 = __uint_as_float(d.sv & 0xFFFF0000u), b1 = __uint_as_float(d.bv & 0xFFFF0000u);
+        acc = fmaf(d.gx.y, fmaf(s0, comb3(c0[0], c0[1], c0[2]), fmaf(8.0f, s0, b0) * d.gx.x), acc);
+        acc = fmaf(d.gx.w, fmaf(s1, comb3(c1[0], c1[1], c1[2]), fmaf(8.0f, s1, b1) * d.gx.z), acc);
     };
-    // two groups in flight (ng is even)
-    DnGroup ga = load(0);
-    for (int g = 0; g < ng; g += 2) {
-        const DnGroup gb = load(g + 1);
-        step(ga);
-        ga = load(min(g + 2, ng - 1));
-        step(gb);
+    const int glast = ngv - 2;
+    Pair pa = load(0);
+    for (int g = 0; g < ngv; g += 4) {
+        const Pair pb = load(min(g + 2, glast));
+        __builtin_amdgcn_sched_barrier(0);
+        step(pa);
+        if (g + 2 >= ngv) break;
+        pa = load(min(g + 4, glast));
+        __builtin_amdgcn_sched_barrier(0);
+        step(pb);
     }
     if (own) out[vi * RB + (wrow - vi * nr)] = acc;
 }
@@ -869,11 +986,119 @@ __device__ void down_tile_mfma4(const Lds &s, const Rows &R, int nv, int len, in
 __device__ void down_all_mfma4(const Lds &s, const Rows &rd, const Rows &sd, int K, int I, int Is, int nr,
                                uint32_t nrm, float *out, int RB) {
     const int wave = threadIdx.x / kWave;
-    const int th = nr >= 2 ? 16 : 8;
+    const int th = min(16, 3 * nr + 1);
     const int nrt = (K * nr + th - 1) / th, nst = Is ? (nr + th - 1) / th : 0;
     for (int u = wave; u < nrt + nst; u += kWaves) {
         if (u < nrt) down_tile_mfma4(s, rd, K, I, nr, nrm, th, u, 0, out, RB);
-        else down_tile_mfma4(s, sd, 1, Is, nr, nrm, th, u - nrt, K * I / 32, out + K * RB, RB);
+        else down_tile_mfma4(s, sd, 1, Is, nr, nrm, th, u - nrt, K * I / 64, out + K * RB, RB);
+    }
+}
+
+// ---- gate|up + SwiGLU on MFMA (4-bit rows) -----------------------------------------------------------
+// The same engine with A row 4t' + j = limb j of token 4 tb + t' (token blocks tb of 4; rows past
+// T repeat token T - 1) and B column i = staged row i of a 16-row tile (rows 2m / 2m + 1 = gate /
+// up of pair m); lane (i, kb) ends with row i against token 4 tb + kb. The H columns are split into
+// ks contiguous ranges of whole groups so that tiles x ranges fill the 8 waves; each range's sum
+// goes to an LDS partial (the h staging area is idle during gate|up), and after a barrier the
+// partials are added in range order, SwiGLU applied and the result exchanged.
+//   ALL = true: every pair serves every token (the shared expert); else pair m serves tok_of(m).
+//   dst_of(m, t): the exchange word of pair m for token t.
+template <bool ALL, typename TokOf, typename DstOf>
+__device__ void gate_up_mfma4(const DecodeParams &p, const Lds &s, const Rows &R, int np, TokOf tok_of,
+                              DstOf dst_of, uint32_t ep) {
+    const int lane = threadIdx.x % kWave, i = lane % 16, kb = lane / 16, wave = threadIdx.x / kWave;
+    const int T = p.T, ng = p.H / 64, gm = min(ng, 8) - 1;
+    const int nrows = 2 * np, ntile = (nrows + 15) / 16, nslot = ALL ? T : 1;
+    const bool two = T > 4;  // a second token block (T <= 8)
+    int lks = 0;  // log2 of the number of column ranges: ranges x tiles <= 8, >= 2 groups per range
+    while ((2 << lks) * ntile <= kWaves && (4 << lks) <= ng) ++lks;
+    const int ks = 1 << lks, gpr = ng >> lks;
+    float *part = reinterpret_cast<float *>(s.hp);  // [ks][nslot][nrows]
+    const int ja = min(i & 3, 2);
+    const int ta0 = min(i >> 2, T - 1), ta1 = min(4 + (i >> 2), T - 1);
+    const int tl0 = min(kb, T - 1), tl1 = min(4 + kb, T - 1);  // this lane's tokens in blocks 0 and 1
+    for (int unit = wave; unit < (ntile << lks); unit += kWaves) {
+        const int tau = unit >> lks, kq = unit & (ks - 1), g0 = kq * gpr;
+        const int row = 16 * tau + i;
+        const bool wok = row < nrows;
+        const int wrow = wok ? row : 16 * tau;
+        const int tk = ALL ? 0 : tok_of(wrow >> 1);
+        const char *qbase = R.c + (size_t)wrow * R.cb + kb * 8;
+        const int qswz = wrow & gm;
+        const uint16_t *sp = reinterpret_cast<const uint16_t *>(R.s + (size_t)wrow * R.sb);
+        const uint16_t *bp = reinterpret_cast<const uint16_t *>(R.b + (size_t)wrow * R.sb);
+        const int8_t *a0p = s.xq + ((size_t)ta0 * ng * 3 + ja) * 64 + 16 * kb;
+        const int8_t *a1p = s.xq + ((size_t)ta1 * ng * 3 + ja) * 64 + 16 * kb;
+        const float2 *x0p = s.xsx + tl0 * ng, *x1p = s.xsx + tl1 * ng;
+        // operands of the group pair (g, g + 1), g even (token blocks 0 and 1)
+        struct Pair {
+            i32x4_t a00, a01, a10, a11;
+            uint2 q0, q1;
+            uint32_t sv, bv;
+            float4 x0, x1;
+        };
+        auto load = [&](int g) -> Pair {
+            Pair d;
+            d.a00 = *reinterpret_cast<const i32x4_t *>(a0p + (size_t)g * 192);
+            d.a01 = *reinterpret_cast<const i32x4_t *>(a0p + (size_t)g * 192 + 192);
+            d.q0 = *reinterpret_cast<const uint2 *>(qbase + ((g ^ qswz) * 32));
+            d.q1 = *reinterpret_cast<const uint2 *>(qbase + (((g + 1) ^ qswz) * 32));
+            d.sv = *reinterpret_cast<const uint32_t *>(sp + g);
+            d.bv = *reinterpret_cast<const uint32_t *>(bp + g);
+            d.x0 = *reinterpret_cast<const float4 *>(x0p + g);
+            if (two) {
+                d.a10 = *reinterpret_cast<const i32x4_t *>(a1p + (size_t)g * 192);
+                d.a11 = *reinterpret_cast<const i32x4_t *>(a1p + (size_t)g * 192 + 192);
+                d.x1 = *reinterpret_cast<const float4 *>(x1p + g);
+            }
+            return d;
+        };
+        float acc0 = 0.0f, acc1 = 0.0f;
+        auto step = [&](const Pair &d) {
+            const i32x4_t zero = {0, 0, 0, 0}, b0 = code_bytes(d.q0), b1 = code_bytes(d.q1);
+            const float s0 = __uint_as_float(d.sv << 16), z0 = fmaf(8.0f, s0, __uint_as_float(d.bv << 16));
+            const float s1 = __uint_as_float(d.sv & 0xFFFF0000u);
+            const float z1 = fmaf(8.0f, s1, __uint_as_float(d.bv & 0xFFFF0000u));
+            i32x4_t c = __builtin_amdgcn_mfma_i32_16x16x64_i8(d.a00, b0, zero, 0, 0, 0);
+            acc0 = fmaf(d.x0.y, fmaf(s0, comb3(c[0], c[1], c[2]), z0 * d.x0.x), acc0);
+            c = __builtin_amdgcn_mfma_i32_16x16x64_i8(d.a01, b1, zero, 0, 0, 0);
+            acc0 = fmaf(d.x0.w, fmaf(s1, comb3(c[0], c[1], c[2]), z1 * d.x0.z), acc0);
+            if (two) {
+                c = __builtin_amdgcn_mfma_i32_16x16x64_i8(d.a10, b0, zero, 0, 0, 0);
+                acc1 = fmaf(d.x1.y, fmaf(s0, comb3(c[0], c[1], c[2]), z0 * d.x1.x), acc1);
+                c = __builtin_amdgcn_mfma_i32_16x16x64_i8(d.a11, b1, zero, 0, 0, 0);
+                acc1 = fmaf(d.x1.w, fmaf(s1, comb3(c[0], c[1], c[2]), z1 * d.x1.z), acc1);
+            }
+        };
+        const int glast = g0 + gpr - 2;
+        Pair pa = load(g0);
+        for (int g = g0; g < g0 + gpr; g += 4) {
+            const Pair pb = load(min(g + 2, glast));
+            __builtin_amdgcn_sched_barrier(0);
+            step(pa);
+            if (g + 2 >= g0 + gpr) break;
+            pa = load(min(g + 4, glast));
+            __builtin_amdgcn_sched_barrier(0);
+            step(pb);
+        }
+        if (wok) {
+            if constexpr (ALL) {
+                if (kb < T) part[(kq * T + kb) * nrows + row] = acc0;
+                if (two && 4 + kb < T) part[(kq * T + 4 + kb) * nrows + row] = acc1;
+            } else {
+                if ((tk & 3) == kb) part[kq * nrows + row] = tk < 4 ? acc0 : acc1;
+            }
+        }
+    }
+    lds_barrier();
+    for (int e = threadIdx.x; e < np * nslot; e += blockDim.x) {
+        const int m = ALL ? div_by(e, p.tdiv) : e, t = ALL ? e - m * T : 0;
+        float gsum = 0.0f, usum = 0.0f;
+        for (int k = 0; k < ks; ++k) {
+            gsum += part[(k * nslot + t) * nrows + 2 * m];
+            usum += part[(k * nslot + t) * nrows + 2 * m + 1];
+        }
+        ll_put(dst_of(m, t), silu(gsum) * usum, ep);
     }
 }
 
@@ -922,7 +1147,12 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         // ---- R: router logits and the shared expert's gate|up, from LDS
         router_logits<BITS>(p, l, s, w, ll_lg, ep);
         if (!Is && b == 0 && tid < T) ll_put(ll_lg + (size_t)tid * (E + 1) + E, 0.0f, ep);  // unused column
-        if (Is) {
+        if constexpr (BITS == 4) build_x_limbs(p, s);
+        if (Is && BITS == 4) {
+            gate_up_mfma4<true>(
+                p, s, sg_rows(p, s), w.nps, [](int) { return 0; },
+                [&](int m, int t) { return ll_h + (size_t)t * HW + KI + (b + m * nb); }, ep);
+        } else if (Is) {
             const Rows sg = sg_rows(p, s);
             const uint32_t tdiv = p.tdiv;
             gate_up<BITS>(
@@ -967,7 +1197,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
                               const int P = pb + (r >> 1), tk = P >> lgI, j = P & (I - 1);
                               return expert_at(s.sidx[tk], E) * 2 * I + (size_t)(r & 1) * I + j;
                           },
-                          rg);
+                          rg, mfma_swz(BITS, H));
                 if (one_chunk) {
                     // token 0's routed down rows follow right behind; wait for the gate|up rows only
                     stage_routed_down(p, l, s, 0, r0, nr, w.nrm);
@@ -976,15 +1206,25 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
                     dma_wait();
                 }
                 lds_barrier();
-                gate_up<BITS>(
-                    p, s, nc,
-                    [&](int i, int hf, int sl, SliceCodes<BITS> &sc) { lds_slice<BITS>(sc, rg, 2 * i + hf, sl); },
-                    [&](int i) { return div_by((pb + i) >> lgI, kdiv); },
-                    [&](int i) {
-                        const int P = pb + i, t = div_by(P >> lgI, kdiv);
-                        return ll_h + (size_t)t * HW + (P - t * KI);
-                    },
-                    ep);
+                if constexpr (BITS == 4) {
+                    gate_up_mfma4<false>(
+                        p, s, rg, nc, [&](int i) { return div_by((pb + i) >> lgI, kdiv); },
+                        [&](int i, int) {
+                            const int P = pb + i, t = div_by(P >> lgI, kdiv);
+                            return ll_h + (size_t)t * HW + (P - t * KI);
+                        },
+                        ep);
+                } else {
+                    gate_up<BITS>(
+                        p, s, nc,
+                        [&](int i, int hf, int sl, SliceCodes<BITS> &sc) { lds_slice<BITS>(sc, rg, 2 * i + hf, sl); },
+                        [&](int i) { return div_by((pb + i) >> lgI, kdiv); },
+                        [&](int i) {
+                            const int P = pb + i, t = div_by(P >> lgI, kdiv);
+                            return ll_h + (size_t)t * HW + (P - t * KI);
+                        },
+                        ep);
+                }
                 lds_barrier();
             }
         }
@@ -996,7 +1236,10 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
                 stage_routed_down(p, l, s, 0, r0, nr, w.nrm);  // streams in during the h exchange
         }
         for (int t = 0; t < T; ++t) {
-            if (!stage_h<BITS>(p, s, ll_h + (size_t)t * HW, ep)) { dma_wait(); return; }
+            if (!(BITS == 4 ? stage_h4(p, s, ll_h + (size_t)t * HW, ep) : stage_h<BITS>(p, s, ll_h + (size_t)t * HW, ep))) {
+                dma_wait();
+                return;
+            }
             dma_wait();
             lds_barrier();
             if (nr > 0) {
