@@ -508,6 +508,10 @@ __device__ __forceinline__ void stage_router(const DecodeParams &p, int l, const
         }
     }
 }
+// DMA instructions this wave issues in stage_router.
+__device__ __forceinline__ int stage_router_count(const DecodeParams &p, const WgShare &w) {
+    return dma_count(w.nrr << __builtin_ctz(static_cast<unsigned>(p.H / 4)));
+}
 __device__ __forceinline__ Rows sg_rows(const DecodeParams &p, const Lds &s) {
     return rows_at(s.sg, 2 * p.nps, p.H, p.bits);
 }
@@ -1189,7 +1193,6 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
             const uint32_t kdiv = p.kdiv;
             const QMat w13 = layer_ptrs(p, l).w13;
             const Rows rg = rows_at(s.rg, 2 * cp, H, BITS);
-            const bool one_chunk = np <= cp;
             for (int c0 = 0; c0 < np; c0 += cp) {
                 const int nc = min(cp, np - c0), pb = w.q0 + c0;
                 dma_qrows(w13, H, BITS, 2 * nc,
@@ -1198,13 +1201,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
                               return expert_at(s.sidx[tk], E) * 2 * I + (size_t)(r & 1) * I + j;
                           },
                           rg, mfma_swz(BITS, H));
-                if (one_chunk) {
-                    // token 0's routed down rows follow right behind; wait for the gate|up rows only
-                    stage_routed_down(p, l, s, 0, r0, nr, w.nrm);
-                    dma_wait_but(nr > 0 ? dma_qrows_count(K * nr, I, BITS) : 0);
-                } else {
-                    dma_wait();
-                }
+                dma_wait();
                 lds_barrier();
                 if constexpr (BITS == 4) {
                     gate_up_mfma4<false>(
@@ -1230,17 +1227,23 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         }
 
         // ---- D: per token, all h -> this workgroup's rows of every down projection -> combine
-        {
-            const int np = w.q1 - w.q0;
-            if (!(np > 0 && np <= p.cp))  // not staged with the gate|up rows above
-                stage_routed_down(p, l, s, 0, r0, nr, w.nrm);  // streams in during the h exchange
+        // Token 0's routed down rows, then layer l+1's router rows and shared gate|up rows (their LDS
+        // was last read in phase R), stream in during the h exchange; the down projection waits for
+        // the routed down rows only.
+        stage_routed_down(p, l, s, 0, r0, nr, w.nrm);
+        int later = 0;  // DMA instructions this wave issued after the routed down rows
+        if (has_next) {
+            stage_router(p, l + 1, s, w);
+            stage_shared_gu(p, l + 1, s, w);
+            later = stage_router_count(p, w) + (w.nps ? dma_qrows_count(2 * w.nps, H, BITS) : 0);
         }
         for (int t = 0; t < T; ++t) {
             if (!(BITS == 4 ? stage_h4(p, s, ll_h + (size_t)t * HW, ep) : stage_h<BITS>(p, s, ll_h + (size_t)t * HW, ep))) {
                 dma_wait();
                 return;
             }
-            dma_wait();
+            if (t == 0) dma_wait_but(later);
+            else dma_wait();
             lds_barrier();
             if (nr > 0) {
                 float *pt = s.part + (size_t)t * (K + 1) * RB;
@@ -1266,11 +1269,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
             if (p.y_all) G(p.y_all)[(size_t)l * T * H + o] = acc;
         }
         lds_barrier();
-        if (has_next) {  // layer l+1's router and shared-expert rows stream in during the y exchange
-            stage_router(p, l + 1, s, w);
-            stage_shared_gu(p, l + 1, s, w);
-            stage_shared_down(p, l + 1, s, r0, nr);
-        }
+        if (has_next) stage_shared_down(p, l + 1, s, r0, nr);  // streams in during the y exchange
     }
     dma_wait();
     // the next call may advance the epoch once every workgroup has read it
