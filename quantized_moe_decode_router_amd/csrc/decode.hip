@@ -1007,15 +1007,19 @@ __device__ void down_all_mfma4(const Lds &s, const Rows &rd, const Rows &sd, int
 // partials are added in range order, SwiGLU applied and the result exchanged.
 //   ALL = true: every pair serves every token (the shared expert); else pair m serves tok_of(m).
 //   dst_of(m, t): the exchange word of pair m for token t.
+//   busy: waves 0 .. busy-1 arrive late (they are selecting experts), so the units go to the other
+//   waves first; max_units bounds ranges x tiles (it alone fixes the ranges, so results do not
+//   depend on busy).
 template <bool ALL, typename TokOf, typename DstOf>
 __device__ void gate_up_mfma4(const DecodeParams &p, const Lds &s, const Rows &R, int np, TokOf tok_of,
-                              DstOf dst_of, uint32_t ep) {
-    const int lane = threadIdx.x % kWave, i = lane % 16, kb = lane / 16, wave = threadIdx.x / kWave;
+                              DstOf dst_of, uint32_t ep, int busy = 0, int max_units = kWaves) {
+    const int lane = threadIdx.x % kWave, i = lane % 16, kb = lane / 16;
+    const int wave = (threadIdx.x / kWave + kWaves - busy) % kWaves;  // busy waves come last
     const int T = p.T, ng = p.H / 64, gm = min(ng, 8) - 1;
     const int nrows = 2 * np, ntile = (nrows + 15) / 16, nslot = ALL ? T : 1;
     const bool two = T > 4;  // a second token block (T <= 8)
-    int lks = 0;  // log2 of the number of column ranges: ranges x tiles <= 8, >= 2 groups per range
-    while ((2 << lks) * ntile <= kWaves && (4 << lks) <= ng) ++lks;
+    int lks = 0;  // log2 of the number of column ranges: ranges x tiles <= max_units, >= 2 groups per range
+    while ((2 << lks) * ntile <= max_units && (4 << lks) <= ng) ++lks;
     const int ks = 1 << lks, gpr = ng >> lks;
     float *part = reinterpret_cast<float *>(s.hp);  // [ks][nslot][nrows]
     const int ja = min(i & 3, 2);
@@ -1108,12 +1112,12 @@ __device__ void gate_up_mfma4(const DecodeParams &p, const Lds &s, const Rows &R
 
 // ---- routing of every token (identical in every workgroup) ---------------------------------------
 // Wave t selects token t's experts (wave_topk); gamma from the shared-gate logit (column E).
+// Wave t < T selects token t's experts; the caller publishes the results with a barrier.
 __device__ void route_tokens(const DecodeParams &p, const Lds &s) {
     const int T = p.T, E = p.E, K = p.K, wave = threadIdx.x / kWave;
     if (wave < T) wave_topk(s.lg + wave * (E + 1), E, K, s.sidx + wave * K, s.sw + wave * K);
     for (int t = threadIdx.x; t < T; t += blockDim.x)
         s.gam[t] = p.Is ? 1.0f / (1.0f + expf(-s.lg[t * (E + 1) + E])) : 0.0f;
-    lds_barrier();
 }
 
 template <int BITS>
@@ -1152,11 +1156,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         router_logits<BITS>(p, l, s, w, ll_lg, ep);
         if (!Is && b == 0 && tid < T) ll_put(ll_lg + (size_t)tid * (E + 1) + E, 0.0f, ep);  // unused column
         if constexpr (BITS == 4) build_x_limbs(p, s);
-        if (Is && BITS == 4) {
-            gate_up_mfma4<true>(
-                p, s, sg_rows(p, s), w.nps, [](int) { return 0; },
-                [&](int m, int t) { return ll_h + (size_t)t * HW + KI + (b + m * nb); }, ep);
-        } else if (Is) {
+        if (Is && BITS != 4) {
             const Rows sg = sg_rows(p, s);
             const uint32_t tdiv = p.tdiv;
             gate_up<BITS>(
@@ -1176,6 +1176,15 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         // ---- G: routing (identical in every workgroup), then routed gate|up + SwiGLU
         if (!ll_gather<false>(ll_lg, T * (E + 1), ep, s.lg, p.ctrl, p.spin_limit)) { dma_wait(); return; }
         route_tokens(p, s);
+        if (Is && BITS == 4) {
+            // the shared expert's gate|up runs on the waves not selecting experts; its barrier also
+            // publishes the routing
+            gate_up_mfma4<true>(
+                p, s, sg_rows(p, s), w.nps, [](int) { return 0; },
+                [&](int m, int t) { return ll_h + (size_t)t * HW + KI + (b + m * nb); }, ep, T, kWaves / 2);
+        } else {
+            lds_barrier();
+        }
         if (b == 0) {
             const size_t base = (size_t)l * T;
             if (p.idx_all)
