@@ -52,14 +52,15 @@ constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1, 0, 3, 2]
 constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each half-row of 8
 constexpr int kDppRowMirror = 0x140;  // lane i <-> 15 - i within each row of 16
+// Every pattern used reads a lane of the same row, so callers keep whole rows active; the plain
+// move form lets the compiler fold it into the consuming ALU instruction (one DPP-modified op).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return static_cast<uint32_t>(
-        __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xF, 0xF, false));
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float readlane_f32(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
@@ -91,6 +92,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     const uint32_t r3 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
     return max(max(r0, r1), max(r2, r3));
 }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, dpp_u32<kDppQuadXor1>(v));
+    v = min(v, dpp_u32<kDppQuadXor2>(v));
+    v = min(v, dpp_u32<kDppHalfMirror>(v));
+    v = min(v, dpp_u32<kDppRowMirror>(v));
+    const uint32_t r0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0));
+    const uint32_t r1 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16));
+    const uint32_t r2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32));
+    const uint32_t r3 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
+    return min(min(r0, r1), min(r2, r3));
+}
 
 // Partial dot product of an fp32 row with v[0..cols) (cols % 4 == 0).
 __device__ __forceinline__ float frow_dot_partial(const float *row, int cols, const float *v, int lane) {
@@ -120,8 +132,7 @@ constexpr int kTopkMaxE = 1024;
 // Top-k of lt[0..E) (LDS) by one whole wave, NJ = ceil(E / 64) keys per lane (expert e = lane +
 // 64 j in slot j): the K indices with the largest values, ordered by (value descending, index
 // ascending). Exact and deterministic: K rounds of (wave maximum of the remaining keys; the lowest
-// expert index holding it wins -- the first slot j with a match, then its lowest lane; that key is
-// removed). Writes idx[0..K) and the renormalised softmax weights w[0..K) (softmax over the kept
+// expert index holding it wins; that key is removed). Writes idx[0..K) and the renormalised softmax weights w[0..K) (softmax over the kept
 // logits equals softmax-then-renormalise), the exponentials summed by a fixed lane reduction.
 template <int NJ>
 __device__ inline void wave_topk_n(const float *lt, int E, int K, int *idx, float *w) {
@@ -139,12 +150,12 @@ __device__ inline void wave_topk_n(const float *lt, int E, int K, int *idx, floa
 #pragma unroll
         for (int j = 1; j < NJ; ++j) m = max(m, key[j]);
         m = wave_max_u32(m);
-        int win = -1;
+        // the lowest expert index holding the maximum: per lane the first matching slot, then the
+        // wave minimum (all in vector ALU; no scalar round trips)
+        uint32_t c = 0xFFFFFFFFu;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const unsigned long long hit = __ballot(key[j] == m);
-            if (win < 0 && hit) win = (__ffsll((long long)hit) - 1) + kWave * j;
-        }
+        for (int j = NJ - 1; j >= 0; --j) c = key[j] == m ? static_cast<uint32_t>(lane + kWave * j) : c;
+        const int win = static_cast<int>(wave_min_u32(c));
         if (lane == r) mine = win;
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
