@@ -164,11 +164,18 @@ __device__ __forceinline__ void dma_wait_but(int n) {
 // u / 64; wave w issues instructions w, w + 8, ... With swz != 0 (U = 16 only) LDS chunk c of row r
 // receives source chunk c ^ ((r & swz) << 1): the 32-byte blocks of a row are XOR-permuted by the
 // row index, so a column block read across consecutive rows spreads over the LDS banks.
+// Waves [first, first + n) of the workgroup that issue a DMA.
+struct DmaWaves {
+    int first, n;
+};
+constexpr DmaWaves kAllWaves = {0, kWaves};
 template <int U, typename SrcOf>
-__device__ __forceinline__ void dma_rows(int n, int bytes, SrcOf src_of, char *dst, int swz = 0) {
+__device__ __forceinline__ void dma_rows(int n, int bytes, SrcOf src_of, char *dst, int swz = 0,
+                                         DmaWaves dw = kAllWaves) {
     const int sh = __builtin_ctz(static_cast<unsigned>(bytes / U)), total = n << sh;
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    for (int i = wave; i * kWave < total; i += kWaves) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave - dw.first;
+    if (wave < 0 || wave >= dw.n) return;
+    for (int i = wave; i * kWave < total; i += dw.n) {
         const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(dst + (size_t)i * kWave * U));
         const int u = i * kWave + lane;
         if (u < total) {
@@ -490,13 +497,15 @@ __device__ __forceinline__ WgShare wg_share(const DecodeParams &p) {
 // Router rows are stored chunk-transposed: 16-byte chunk k (k < 8) of 32-column slice sl of a row
 // goes to chunk position k * (H/32) + sl, so that lane sl reading its k-th chunk is one
 // conflict-free 16-byte LDS read per wave.
-__device__ __forceinline__ void stage_router(const DecodeParams &p, int l, const Lds &s, const WgShare &w) {
+__device__ __forceinline__ void stage_router(const DecodeParams &p, int l, const Lds &s, const WgShare &w,
+                                             DmaWaves dw = kAllWaves) {
     const LayerPtrs L = layer_ptrs(p, l);
     const int nr = w.nrr, H = p.H, nsl = H / 32, b = blockIdx.x, g = gridDim.x;
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave - dw.first;
+    if (wave < 0 || wave >= dw.n) return;
     const int cs = __builtin_ctz(static_cast<unsigned>(H / 4)), ss = __builtin_ctz(static_cast<unsigned>(nsl));
     const int total = nr << cs;  // 16-byte chunks
-    for (int i = wave; i * kWave < total; i += kWaves) {
+    for (int i = wave; i * kWave < total; i += dw.n) {
         const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(s.rt + (size_t)i * kWave * 4));
         const int u = i * kWave + lane;
         if (u < total) {
@@ -507,10 +516,6 @@ __device__ __forceinline__ void stage_router(const DecodeParams &p, int l, const
             dma16(row + sl * 32 + k * 4, m0);
         }
     }
-}
-// DMA instructions this wave issues in stage_router.
-__device__ __forceinline__ int stage_router_count(const DecodeParams &p, const WgShare &w) {
-    return dma_count(w.nrr << __builtin_ctz(static_cast<unsigned>(p.H / 4)));
 }
 __device__ __forceinline__ Rows sg_rows(const DecodeParams &p, const Lds &s) {
     return rows_at(s.sg, 2 * p.nps, p.H, p.bits);
@@ -1176,6 +1181,12 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         // ---- G: routing (identical in every workgroup), then routed gate|up + SwiGLU
         if (!ll_gather<false>(ll_lg, T * (E + 1), ep, s.lg, p.ctrl, p.spin_limit)) { dma_wait(); return; }
         route_tokens(p, s);
+        // layer l+1's router rows (the LDS copy was last read before the logits exchange) stream in
+        // during the expert selection, issued by waves with nothing else to do then
+        if (has_next) {
+            const int first = min(T + kWaves / 2, kWaves - 1);
+            stage_router(p, l + 1, s, w, DmaWaves{first, kWaves - first});
+        }
         if (Is && BITS == 4) {
             // the shared expert's gate|up runs on the waves not selecting experts; its barrier also
             // publishes the routing
@@ -1236,15 +1247,14 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         }
 
         // ---- D: per token, all h -> this workgroup's rows of every down projection -> combine
-        // Token 0's routed down rows, then layer l+1's router rows and shared gate|up rows (their LDS
-        // was last read in phase R), stream in during the h exchange; the down projection waits for
-        // the routed down rows only.
+        // Token 0's routed down rows, then layer l+1's shared gate|up rows (the shared gate|up of this
+        // layer is done), stream in during the h exchange; the down projection waits for the routed
+        // down rows only.
         stage_routed_down(p, l, s, 0, r0, nr, w.nrm);
         int later = 0;  // DMA instructions this wave issued after the routed down rows
         if (has_next) {
-            stage_router(p, l + 1, s, w);
             stage_shared_gu(p, l + 1, s, w);
-            later = stage_router_count(p, w) + (w.nps ? dma_qrows_count(2 * w.nps, H, BITS) : 0);
+            later = w.nps ? dma_qrows_count(2 * w.nps, H, BITS) : 0;
         }
         for (int t = 0; t < T; ++t) {
             if (!(BITS == 4 ? stage_h4(p, s, ll_h + (size_t)t * HW, ep) : stage_h<BITS>(p, s, ll_h + (size_t)t * HW, ep))) {
