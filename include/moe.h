@@ -44,8 +44,9 @@
  *     set (MOE_ERR_TIMEOUT). A decode kernel that finds it non-zero does nothing; zero-fill the
  *     workspace again to recover. moe_read_status() reads it.
  *   - Two calls that share a workspace must not run concurrently.
- *   - The decode calls additionally need hidden, inter, shared_inter <= 2048 and an LDS footprint
- *     within 160 KiB (it grows with T); other shapes return MOE_ERR_UNSUPPORTED.
+ *   - The decode calls additionally need hidden, inter, shared_inter <= 2048, inter and a
+ *     non-zero shared_inter >= 128, and an LDS footprint within 160 KiB (it grows with T); other
+ *     shapes return MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -121,7 +122,8 @@ moe_status moe_route(const moe_shape *shape, const moe_layer *layer, const uint1
 /*
  * One layer at decode for 1 <= T <= 8 tokens: router, top-k, packed gate|up dequant-GEMV with
  * SwiGLU, down dequant-GEMV and the fixed-order combine (k = 0..K-1, then the shared expert),
- * as one persistent grid-synchronised kernel.
+ * as one persistent kernel (one workgroup per compute unit; workgroups exchange logits, h and y
+ * through epoch-tagged words in the workspace, with no grid-wide barrier).
  *   x : bf16 [T][H]   y : fp32 [T][H]
  *   topk_idx_opt [T][K], topk_w_opt [T][K], logits_opt [T][E]: routing outputs or NULL
  */
