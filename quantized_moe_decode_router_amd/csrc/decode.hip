@@ -10,42 +10,31 @@
 //
 // Per layer and workgroup b (grid = number of CUs):
 //   input   x of every token: x_in, or the RMS glue of all of y_{l-1} (chained stacks)
-//   R       router rows e = b (mod grid) [row E = the shared-expert gate] and the shared
-//           expert's gate|up pairs j = b (mod grid), both from LDS (staged during the previous
-//           layer) -> logit words, shared h words
-//   G       all logits -> top-k by rank counting (identical in every workgroup) -> this
-//           workgroup's share of the flattened (token, slot, j) routed gate|up pairs, loaded
-//           straight into registers -> routed h words
+//   R       router rows e = b (mod grid) [row E = the shared-expert gate], staged in LDS, against
+//           x -> logit words; x turned into int8 limbs
+//   G       all logits -> top-k (identical in every workgroup; one wave per token) beside the
+//           shared expert's gate|up pairs j = b (mod grid) on the other waves -> this workgroup's
+//           share of the flattened (token, slot, j) routed gate|up pairs, DMA'd into LDS -> h words
 //   D       per token: all K routed h vectors and the shared h -> the workgroup's H/grid rows of
-//           every routed down projection (rows staged into LDS while h is in flight) and of the
+//           every routed down projection (rows DMA'd into LDS while h is in flight) and of the
 //           shared one -> fixed-order combine (k = 0..K-1, then the shared expert) -> y
-// Weights that do not depend on the routing (router rows, shared expert rows) are copied into
-// LDS by the LDS-DMA form of the global load (global_load_lds_dwordx4 / _dword) while the
-// workgroup waits for an exchange, so they cost neither registers nor time on the chain.
+// Weights reach LDS through the LDS-DMA form of the global load (global_load_lds_dwordx4 /
+// _dword), issued while the workgroup waits for an exchange, so they cost neither registers nor
+// time on the chain.
 //
-// Quantised rows are split into 32-column slices (16 bytes of 4-bit or 32 bytes of 8-bit codes,
-// always inside one 64-column quantisation group). Codes become the bf16 values 128 + nibble with
-// one v_and_or (exact), feed v_dot2_f32_bf16 against bf16 activations (products exact, fp32
-// sums), and the zero point folds into the group bias (see SliceRef). The fp32 h of the down
-// projection is split into bf16 hi + lo halves (16 significant bits). All address arithmetic
-// into the weights is 64-bit.
+// Every dot product with quantised rows runs on v_mfma_i32_16x16x64_i8 in exact integer
+// arithmetic: the activations (x, or h) of each 64-column quantisation group are held as three
+// int8 limbs of a 24-bit fixed-point value, the codes enter as signed bytes relative to the zero
+// point (see build_limbs). All address arithmetic into the weights is 64-bit.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
 namespace moe {
 
 constexpr int kWaves = kDecodeThreads / kWave;  // 8
-constexpr int kGuWL = 4;                        // routed gate|up wave-loads a wave holds at once
-constexpr uint32_t kMagic = 0x43004300u;        // bf16 pair (128, 128)
 constexpr int kMaxGather = 16;                  // exchange words one thread waits for at once
 
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
-                                           false);
-}
 
 // Global-memory view of a pointer. The parameter block is re-read word by word inside the layer
 // loop (see fresh_params), which hides from the compiler that its pointers are global; accesses
@@ -159,18 +148,23 @@ __device__ __forceinline__ void dma_wait_but(int n) {
     }
 }
 
-// Copy n rows of `bytes` bytes each (a power of two, a multiple of U = 16 or 4; src_of(r) aligned
-// to U) into LDS at dst + r * bytes. Unit u = r * (bytes / U) + c is lane u % 64 of instruction
-// u / 64; wave w issues instructions w, w + 8, ... With swz != 0 (U = 16 only) LDS chunk c of row r
-// receives source chunk c ^ ((r & swz) << 1): the 32-byte blocks of a row are XOR-permuted by the
-// row index, so a column block read across consecutive rows spreads over the LDS banks.
 // Waves [first, first + n) of the workgroup that issue a DMA.
 struct DmaWaves {
     int first, n;
 };
 constexpr DmaWaves kAllWaves = {0, kWaves};
+// Block permutation of staged rows: LDS chunk c (16 bytes) of row r receives source chunk
+// c ^ ((r & mask) << shift), i.e. the 2^shift-chunk blocks of a row are XOR-permuted by the row
+// index, so a column block read across consecutive rows spreads over the LDS banks.
+struct Swz {
+    int mask, shift;
+};
+constexpr Swz kNoSwz = {0, 0};
+// Copy n rows of `bytes` bytes each (a power of two, a multiple of U = 16 or 4; src_of(r) aligned
+// to U) into LDS at dst + r * bytes. Unit u = r * (bytes / U) + c is lane u % 64 of instruction
+// u / 64; wave dw.first + w issues instructions w, w + dw.n, ... (swz only with U = 16).
 template <int U, typename SrcOf>
-__device__ __forceinline__ void dma_rows(int n, int bytes, SrcOf src_of, char *dst, int swz = 0,
+__device__ __forceinline__ void dma_rows(int n, int bytes, SrcOf src_of, char *dst, Swz swz = kNoSwz,
                                          DmaWaves dw = kAllWaves) {
     const int sh = __builtin_ctz(static_cast<unsigned>(bytes / U)), total = n << sh;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave - dw.first;
@@ -179,7 +173,7 @@ __device__ __forceinline__ void dma_rows(int n, int bytes, SrcOf src_of, char *d
         const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(dst + (size_t)i * kWave * U));
         const int u = i * kWave + lane;
         if (u < total) {
-            const int r = u >> sh, c = (u & ((1 << sh) - 1)) ^ ((r & swz) << 1);
+            const int r = u >> sh, c = (u & ((1 << sh) - 1)) ^ ((r & swz.mask) << swz.shift);
             const char *g = src_of(r) + (size_t)c * U;
             if constexpr (U == 16) dma16(g, m0);
             else dma4(g, m0);
@@ -210,47 +204,12 @@ __device__ __forceinline__ int dma_qrows_count(int n, int cols, int bits) {
 // permutes the code blocks as in dma_rows (scales and biases are never permuted).
 template <typename RowOf>
 __device__ __forceinline__ void dma_qrows(const QMat &q, int cols, int bits, int n, RowOf row_of, const Rows &dst,
-                                          int swz = 0) {
+                                          Swz swz = kNoSwz) {
     const size_t cb = (size_t)cols * bits / 8, gpr = cols / 64;
     dma_rows<16>(n, dst.cb, [&](int r) { return reinterpret_cast<const char *>(q.c + row_of(r) * cb); }, dst.c, swz);
     dma_rows<4>(n, dst.sb, [&](int r) { return reinterpret_cast<const char *>(q.s + row_of(r) * gpr); }, dst.s);
     dma_rows<4>(n, dst.sb, [&](int r) { return reinterpret_cast<const char *>(q.b + row_of(r) * gpr); }, dst.b);
 }
-
-// ---- slice dot products -------------------------------------------------------------------------
-// Each product chain is split into four independent accumulators (one per code dword, or per
-// dword mod 4), summed in a fixed order at the end: a single chain is bound by the latency of
-// v_dot2 (about 9 cycles per step), four interleaved chains by its issue rate.
-// 4-bit slice: 16 bytes = 32 codes; dword d holds columns 8d..8d+7 (nibble i = column 8d+i).
-// xp[4d+p] = bf16 pair (x[8d+p], x[8d+p+4]). a[d] += sum over dword d of (128+q) x.
-__device__ __forceinline__ void slice_dot4(const uint4 c, const uint32_t *xp, float (&a)[4]) {
-    const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const uint32_t w = wd[d];
-        a[d] = dot2((w & 0x000F000Fu) | kMagic, xp[4 * d + 0], a[d]);
-        a[d] = dot2(((w >> 4) & 0x000F000Fu) | kMagic, xp[4 * d + 1], a[d]);
-        a[d] = dot2(((w >> 8) & 0x000F000Fu) | kMagic, xp[4 * d + 2], a[d]);
-        a[d] = dot2(((w >> 12) & 0x000F000Fu) | kMagic, xp[4 * d + 3], a[d]);
-    }
-}
-// 8-bit slice: 32 bytes = 32 codes in two uint4; dword d holds columns 4d..4d+3.
-// xp[2d+p] = bf16 pair (x[4d+p], x[4d+p+2]). Each byte q = lo + 16 hi is split into nibbles:
-// lo[d % 4] += sum((128+lo) x), hi[d % 4] += sum((128+hi) x).
-__device__ __forceinline__ void slice_dot8(const uint4 c0, const uint4 c1, const uint32_t *xp, float (&lo)[4],
-                                           float (&hi)[4]) {
-    const uint32_t wd[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-        const uint32_t w = wd[d];
-        const int j = d & 3;
-        lo[j] = dot2((w & 0x000F000Fu) | kMagic, xp[2 * d + 0], lo[j]);
-        lo[j] = dot2(((w >> 8) & 0x000F000Fu) | kMagic, xp[2 * d + 1], lo[j]);
-        hi[j] = dot2(((w >> 4) & 0x000F000Fu) | kMagic, xp[2 * d + 0], hi[j]);
-        hi[j] = dot2(((w >> 12) & 0x000F000Fu) | kMagic, xp[2 * d + 1], hi[j]);
-    }
-}
-__device__ __forceinline__ float sum4(const float (&a)[4]) { return (a[0] + a[1]) + (a[2] + a[3]); }
 
 // Column (within a 32-column slice) of the two halves of pair slot q.
 template <int BITS>
@@ -273,104 +232,6 @@ __device__ __forceinline__ void col_pair(int c, int &q, int &half) {
     }
 }
 
-// Codes of one lane for one row slice (16 bytes at 4-bit, 32 at 8-bit) and its group's scale and
-// bias bf16 bit patterns, read from a row set staged in LDS.
-template <int BITS>
-struct SliceCodes;
-template <>
-struct SliceCodes<4> {
-    uint4 c0;
-    uint32_t s16, b16;
-};
-template <>
-struct SliceCodes<8> {
-    uint4 c0, c1;
-    uint32_t s16, b16;
-};
-template <int BITS>
-__device__ __forceinline__ void lds_slice(SliceCodes<BITS> &sc, const Rows &R, int row, int slice) {
-    const uint4 *cp = reinterpret_cast<const uint4 *>(R.c + (size_t)row * R.cb + slice * (BITS == 4 ? 16 : 32));
-    sc.c0 = cp[0];
-    if constexpr (BITS == 8) sc.c1 = cp[1];
-    sc.s16 = reinterpret_cast<const uint16_t *>(R.s + (size_t)row * R.sb)[slice >> 1];
-    sc.b16 = reinterpret_cast<const uint16_t *>(R.b + (size_t)row * R.sb)[slice >> 1];
-}
-template <int BITS>
-__device__ __forceinline__ float sc_scale(const SliceCodes<BITS> &sc) { return __uint_as_float(sc.s16 << 16); }
-template <int BITS>
-__device__ __forceinline__ float sc_bias(const SliceCodes<BITS> &sc) { return __uint_as_float(sc.b16 << 16); }
-
-// Per-slice constants of an activation slice v (built once per vector, shared by every row):
-//   sum = sum(v);  z0 / z1 = the dot chains of slice_dot4 / slice_dot8 evaluated with every code
-//   at the zero point (4-bit: q = 8 -> pairs (136, 136); 8-bit: q = 128 -> lo nibble 0, hi 8), in
-//   exactly the same order as for a real row. Then, exactly in algebra,
-//     sum((s q + b) v) = s * sum((q - zp) v) + (b + zp s) * sum(v)
-//   and sum((q - zp) v) = acc - z0 (4-bit) or (lo - z0) + 16 (hi - z1) (8-bit). A row whose codes
-//   all sit at the zero point gives acc == z0 bit for bit, so an all-zero expert yields exactly 0.
-struct SliceRef {
-    float sum, z0, z1;
-};
-static_assert(sizeof(SliceRef) == 12, "LDS plan assumes 12-byte slice constants");
-template <int BITS>
-__device__ __forceinline__ SliceRef slice_ref(const uint32_t *vp, int npass, const uint32_t *vp2) {
-    // npass = 1: one pair set; npass = 2: the chains continue over a second pair set (hi then lo)
-    SliceRef r;
-    float sum = 0.0f;
-    const uint32_t *sets[2] = {vp, vp2};
-    for (int ps = 0; ps < npass; ++ps)
-        for (int q = 0; q < 16; ++q)
-            sum += bf16_to_f32(sets[ps][q] & 0xFFFF) + bf16_to_f32(sets[ps][q] >> 16);
-    r.sum = sum;
-    if constexpr (BITS == 4) {
-        const uint4 zc = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-        float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int ps = 0; ps < npass; ++ps) slice_dot4(zc, sets[ps], a);
-        r.z0 = sum4(a);
-        r.z1 = 0.0f;
-    } else {
-        const uint4 zc = make_uint4(0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u);
-        float lo[4] = {0.0f, 0.0f, 0.0f, 0.0f}, hi[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int ps = 0; ps < npass; ++ps) slice_dot8(zc, zc, sets[ps], lo, hi);
-        r.z0 = sum4(lo);
-        r.z1 = sum4(hi);
-    }
-    return r;
-}
-// Partial row value of one lane: sum over its slice of (s q + b) v, with vp the slice's bf16
-// pairs of v and ref its SliceRef (the same chains as slice_ref, so zero-point rows give 0).
-template <int BITS>
-__device__ __forceinline__ float slice_value(const SliceCodes<BITS> &sc, const uint32_t *vp, const SliceRef &ref) {
-    const float sv = sc_scale(sc), bv = sc_bias(sc);
-    if constexpr (BITS == 4) {
-        float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        slice_dot4(sc.c0, vp, a);
-        return sv * (sum4(a) - ref.z0) + fmaf(8.0f, sv, bv) * ref.sum;
-    } else {
-        float lo[4] = {0.0f, 0.0f, 0.0f, 0.0f}, hi[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        slice_dot8(sc.c0, sc.c1, vp, lo, hi);
-        return sv * ((sum4(lo) - ref.z0) + 16.0f * (sum4(hi) - ref.z1)) + fmaf(128.0f, sv, bv) * ref.sum;
-    }
-}
-// Same with v split into bf16 hi and lo pair sets (the chains run over hi, then lo).
-template <int BITS>
-__device__ __forceinline__ float slice_value2(const SliceCodes<BITS> &sc, const uint32_t *vhi, const uint32_t *vlo,
-                                              const SliceRef &ref) {
-    const float sv = sc_scale(sc), bv = sc_bias(sc);
-    if constexpr (BITS == 4) {
-        float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        slice_dot4(sc.c0, vhi, a);
-        slice_dot4(sc.c0, vlo, a);
-        return sv * (sum4(a) - ref.z0) + fmaf(8.0f, sv, bv) * ref.sum;
-    } else {
-        float lo[4] = {0.0f, 0.0f, 0.0f, 0.0f}, hi[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        slice_dot8(sc.c0, sc.c1, vhi, lo, hi);
-        slice_dot8(sc.c0, sc.c1, vlo, lo, hi);
-        return sv * ((sum4(lo) - ref.z0) + 16.0f * (sum4(hi) - ref.z1)) + fmaf(128.0f, sv, bv) * ref.sum;
-    }
-}
-
-// An expert index used as an address: clamped into [0, E) so that the weights are never read out
-// of bounds, whatever the selection produced (it always produces valid indices).
 __device__ __forceinline__ size_t expert_at(int e, int E) {
     return (size_t)min((unsigned)e, (unsigned)(E - 1));
 }
@@ -425,7 +286,6 @@ __device__ __forceinline__ DecodeParams fresh_params() {
 // so that lanes reading consecutive slices with 16-byte loads spread over the banks.
 struct Lds {
     uint32_t *xp;    // [T][H/32][20] bf16 pairs of x (16 used)
-    SliceRef *xref;  // [T][H/32]
     float *lg;       // [T][E+1] logits (column E = shared-gate logit)
     int *sidx;       // [T][K]
     float *sw;       // [T][K]
@@ -435,11 +295,10 @@ struct Lds {
     char *sd;        // shared down rows of this workgroup, staged
     char *rd;        // routed down rows of this workgroup for one token, staged
     char *rg;        // routed gate|up rows of one chunk of this workgroup's pairs, staged
-    uint32_t *hp;    // [(K*I + Is)/32][36] h of one token: gathered fp32, then bf16 hi (16) + lo (16) pairs
-    SliceRef *href;  // [(K*I + Is)/32]
+    uint32_t *hp;    // gathered h of one token (fp32); also the y gather buffer and gate|up partials
     float *part;     // [T][K+1][RB] down-projection rows of this workgroup (slot K = shared)
     float *red;      // [64] reduction scratch
-    // 4-bit rows only: activations as three int8 limbs per 64-column group (see build_limbs)
+    // activations as three int8 limbs per 64-column group (see build_limbs)
     int8_t *xq;      // [T][H/64][3][64]
     float2 *xsx;     // [T][H/64] (sum of the limb values, group scale)
     int8_t *hq;      // [(K*I + Is)/64][3][64] h of one token (routed vectors, then the shared one)
@@ -449,7 +308,6 @@ __device__ __forceinline__ Lds carve(const DecodeParams &p, char *smem) {
     const DecodeLds &o = p.lds;
     Lds s;
     s.xp = reinterpret_cast<uint32_t *>(smem + o.xp);
-    s.xref = reinterpret_cast<SliceRef *>(smem + o.xref);
     s.lg = reinterpret_cast<float *>(smem + o.lg);
     s.sidx = reinterpret_cast<int *>(smem + o.sidx);
     s.sw = reinterpret_cast<float *>(smem + o.sw);
@@ -460,7 +318,6 @@ __device__ __forceinline__ Lds carve(const DecodeParams &p, char *smem) {
     s.rd = smem + o.rd;
     s.rg = smem + o.rg;
     s.hp = reinterpret_cast<uint32_t *>(smem + o.hp);
-    s.href = reinterpret_cast<SliceRef *>(smem + o.href);
     s.part = reinterpret_cast<float *>(smem + o.part);
     s.red = reinterpret_cast<float *>(smem + o.red);
     s.xq = reinterpret_cast<int8_t *>(smem + o.xq);
@@ -526,9 +383,9 @@ __device__ __forceinline__ Rows sd_rows(const DecodeParams &p, const Lds &s) {
 __device__ __forceinline__ Rows rd_rows(const DecodeParams &p, const Lds &s) {
     return rows_at(s.rd, p.K * p.rows_per_wg, p.I, p.bits);
 }
-// Block permutation of staged 4-bit rows (see dma_rows): the MFMA dot products read one 64-column
-// group of 16 consecutive staged rows at a time.
-__device__ __forceinline__ int mfma_swz(int bits, int cols) { return bits == 4 ? min(cols / 64, 8) - 1 : 0; }
+// Block permutation of staged rows (see dma_rows): the MFMA dot products read one 64-column group
+// (32 bytes of 4-bit, 64 of 8-bit codes) of 16 consecutive staged rows at a time.
+__device__ __forceinline__ Swz mfma_swz(int bits, int cols) { return Swz{min(cols / 64, 8) - 1, bits == 4 ? 1 : 2}; }
 // Shared gate|up rows of this workgroup's pairs: staged row 2r = gate row j, 2r+1 = up row Is + j,
 // j = b + r * grid.
 __device__ __forceinline__ void stage_shared_gu(const DecodeParams &p, int l, const Lds &s, const WgShare &w) {
@@ -560,30 +417,50 @@ __device__ __forceinline__ void stage_routed_down(const DecodeParams &p, int l, 
               rd_rows(p, s), mfma_swz(p.bits, p.I));
 }
 
-// ---- activations as int8 limbs (4-bit rows) ------------------------------------------------------
-// The 4-bit dot products run on v_mfma_i32_16x16x64_i8 in exact integer arithmetic. A 64-column
-// group of activations v is held as the integers X = rint(v / 2^e), e taken from the group's
-// largest magnitude so that |X| <= 2^22, each split into three signed 8-bit limbs
-// X = L0 2^16 + L1 2^8 + L2 (L1, L2 balanced in [-128, 127], |L0| <= 65). With the codes entering
-// as the bytes 16 (q - 8), C_j = sum 16 (q - 8) L_j is an exact integer (|C_j| <= 2^20) and
-//   sum((s q + b) v) = 2^(e-4) (s comb3(C_0, C_1, C_2) + (b + 8 s) 16 comb3(sum L_0, sum L_1, sum L_2));
-// the group entry keeps (16 comb3 of the limb sums, 2^(e-4)). Codes all at the zero point with
-// b = -8 s give exactly 0 (every C_j is 0 and b + 8 s rounds to 0).
-// Position p of a 64-byte limb row holds column limb_col(p): lane kb of an MFMA takes the code
-// dwords 2 kb and 2 kb + 1 of the group, whose nibbles code_bytes turns into 16 bytes in the order
-// (0,2,4,6, 1,3,5,7, 8,10,12,14, 9,11,13,15) + 16 kb.
+// ---- activations as int8 limbs -------------------------------------------------------------------
+// Dot products with quantised rows run on v_mfma_i32_16x16x64_i8 in exact integer arithmetic. A
+// 64-column group of activations v is held as the integers X = rint(v / 2^e), e taken from the
+// group's largest magnitude so that |X| <= 2^22, each split into three signed 8-bit limbs
+// X = L0 2^16 + L1 2^8 + L2 (L1, L2 balanced in [-128, 127], |L0| <= 65). The codes enter as the
+// signed bytes u (q - zp) relative to the zero point (4-bit: zp 8, u 16, the nibble at the top of
+// its byte; 8-bit: zp 128, u 1), so C_j = sum u (q - zp) L_j is an exact integer (|C_j| <= 2^20) and
+//   sum((s q + b) v) = (2^e / u) (s comb3(C_0, C_1, C_2) + (b + zp s) u comb3(sum L_0, sum L_1, sum L_2));
+// the group entry keeps (u comb3 of the limb sums, 2^e / u). Codes all at the zero point with
+// b = -zp s give exactly 0 (every C_j is 0 and b + zp s rounds to 0).
+// Position p of a 64-byte limb row holds column limb_col(p): lane kb of an MFMA takes columns
+// 16 kb .. 16 kb + 15 of the group, in the order code_bytes produces them -- 4-bit: nibbles of two
+// code dwords, (0,2,4,6, 1,3,5,7, 8,10,12,14, 9,11,13,15) + 16 kb; 8-bit: natural order.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
+template <int BITS>
+struct CodeFmt;
+template <>
+struct CodeFmt<4> {
+    static constexpr int zp = 8, unit = 16, group_bytes = 32;
+    typedef uint2 lane_t;  // one lane's codes of one group (16 columns)
+};
+template <>
+struct CodeFmt<8> {
+    static constexpr int zp = 128, unit = 1, group_bytes = 64;
+    typedef uint4 lane_t;
+};
+
+template <int BITS>
 __device__ __forceinline__ int limb_col(int p) {
+    if constexpr (BITS == 8) return p;
     const int e = p & 15;
     return 16 * (p >> 4) + ((e >> 3) << 3) + 2 * (e & 3) + ((e >> 2) & 1);
 }
-// Codes as the signed bytes 16 (q - 8): q ^ 8 is the 4-bit two's complement of q - 8, moved to
-// the top of its byte.
+// 4-bit: q ^ 8 is the 4-bit two's complement of q - 8, moved to the top of its byte (16 (q - 8)).
+// 8-bit: q ^ 0x80 is the signed byte q - 128.
 __device__ __forceinline__ i32x4_t code_bytes(uint2 q) {
     const uint32_t w0 = q.x ^ 0x88888888u, w1 = q.y ^ 0x88888888u;
     return i32x4_t{(int)((w0 << 4) & 0xF0F0F0F0u), (int)(w0 & 0xF0F0F0F0u), (int)((w1 << 4) & 0xF0F0F0F0u),
                    (int)(w1 & 0xF0F0F0F0u)};
+}
+__device__ __forceinline__ i32x4_t code_bytes(uint4 q) {
+    return i32x4_t{(int)(q.x ^ 0x80808080u), (int)(q.y ^ 0x80808080u), (int)(q.z ^ 0x80808080u),
+                   (int)(q.w ^ 0x80808080u)};
 }
 __device__ __forceinline__ float comb3(int a0, int a1, int a2) {
     return fmaf((float)(a0 * 256 + a1), 256.0f, (float)a2);  // |a0| <= 2^20: a0 * 256 + a1 fits
@@ -597,6 +474,7 @@ __device__ __forceinline__ int row16_sum(int v) {
 }
 // Called by the 16 lanes of one DPP row for one group: lane m holds the values of positions
 // 4m .. 4m+3 and writes limb dword m of rows 0..2 at dst; lane 0 writes the group entry.
+template <int BITS>
 __device__ __forceinline__ void build_limbs(const float (&v)[4], int8_t *dst, float2 *entry) {
     const int m = threadIdx.x & 15;
     float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
@@ -629,7 +507,8 @@ __device__ __forceinline__ void build_limbs(const float (&v)[4], int8_t *dst, fl
     reinterpret_cast<uint32_t *>(dst)[m] = w0;
     reinterpret_cast<uint32_t *>(dst + 64)[m] = w1;
     reinterpret_cast<uint32_t *>(dst + 128)[m] = w2;
-    if (m == 0) *entry = make_float2(16.0f * comb3(s0, s1, s2), ldexpf(1.0f, ex - 4));
+    constexpr int u = CodeFmt<BITS>::unit;
+    if (m == 0) *entry = make_float2((float)u * comb3(s0, s1, s2), ldexpf(1.0f, ex) / (float)u);
 }
 
 // ---- layer input ---------------------------------------------------------------------------------
@@ -680,20 +559,14 @@ __device__ bool layer_input(const DecodeParams &p, int l, uint32_t ep, const Lds
             col_pair<BITS>(h & 31, q, half);
             G(p.x_all)[(size_t)l * T * H + i] = static_cast<uint16_t>(s.xp[(t * nsl + sl) * 20 + q] >> (16 * half));
         }
-    if constexpr (BITS == 8) {
-        for (int i = threadIdx.x; i < T * nsl; i += blockDim.x) {
-            uint32_t v[16];
-            for (int q = 0; q < 16; ++q) v[q] = s.xp[i * 20 + q];
-            s.xref[i] = slice_ref<BITS>(v, 1, v);
-        }
-    }
     lds_barrier();
     return true;
 }
 
-// ---- x as limbs (4-bit rows) -------------------------------------------------------------------------
+// ---- x as limbs --------------------------------------------------------------------------------------
 // The limb table overwrites the bf16 pairs of x (same LDS region), so every thread first reads its
 // items into registers, then all write after a barrier; called once the router has read x.
+template <int BITS>
 __device__ void build_x_limbs(const DecodeParams &p, const Lds &s) {
     const int T = p.T, nsl = p.H / 32, ng = p.H / 64, lng = __builtin_ctz(static_cast<unsigned>(ng));
     const int n = T * ng * 16;  // 16 lanes per group; n and the block size are multiples of 16
@@ -706,9 +579,9 @@ __device__ void build_x_limbs(const DecodeParams &p, const Lds &s) {
             const int tg = it >> 4, m = it & 15, t = tg >> lng, g = tg & (ng - 1);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int col = 64 * g + limb_col(4 * m + e);
+                const int col = 64 * g + limb_col<BITS>(4 * m + e);
                 int q, half;
-                col_pair<4>(col & 31, q, half);
+                col_pair<BITS>(col & 31, q, half);
                 v[k][e] = bf16_to_f32((s.xp[(t * nsl + (col >> 5)) * 20 + q] >> (16 * half)) & 0xFFFFu);
             }
         }
@@ -717,7 +590,7 @@ __device__ void build_x_limbs(const DecodeParams &p, const Lds &s) {
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
         const int it = threadIdx.x + k * kDecodeThreads;
-        if (it < n) build_limbs(v[k], s.xq + (size_t)(it >> 4) * 192, s.xsx + (it >> 4));
+        if (it < n) build_limbs<BITS>(v[k], s.xq + (size_t)(it >> 4) * 192, s.xsx + (it >> 4));
     }
     lds_barrier();
 }
@@ -750,7 +623,7 @@ __device__ void router_logits(const DecodeParams &p, int l, const Lds &s, const 
                 a4[q & 3] = fmaf(rv[pair_col_b<BITS>(q)], bf16_to_f32(w >> 16), a4[q & 3]);
             }
         }
-        float acc = wave_sum(sum4(a4));
+        float acc = wave_sum((a4[0] + a4[1]) + (a4[2] + a4[3]));
         if (lane == 0) {
             const int e = b + r * g;
             if (e < E && rbias) acc += G(rbias)[e];
@@ -759,153 +632,9 @@ __device__ void router_logits(const DecodeParams &p, int l, const Lds &s, const 
     }
 }
 
-// ---- gate|up + SwiGLU ------------------------------------------------------------------------------
-// A pair is the gate row and the up row of one (token, expert, j). With H/32 = 64 slices per row
-// (wide rows) a pair is two wave-loads (gate, then up) and lane l takes slice l; with at most 32
-// slices a pair is one wave-load, lanes [0, spr) on the gate row and [spr, 2 spr) on the up row.
-// Wave w takes the contiguous pairs [np w / 8, np (w + 1) / 8), kGuWL wave-loads at a time: all of
-// a batch's loads are issued before any of its math.
-//   load(i, half, sc)   fetch this lane's slice of pair i's gate (half 0) or up (half 1) row
-//   tok_of(i)           token of pair i;   dst_of(i) its h word
-template <int BITS, typename Load, typename TokOf, typename DstOf>
-__device__ __forceinline__ void gate_up(const DecodeParams &p, const Lds &s, int np, Load load, TokOf tok_of,
-                                        DstOf dst_of, uint32_t ep) {
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int nsl = p.H / 32;
-    const bool wide = nsl == kWave;
-    const int spr = nsl;
-    const int half = wide ? 0 : lane / spr, sl = wide ? lane : lane % spr;
-    const bool active = wide || half < 2;
-    constexpr int kPPB = kGuWL / 2;  // pairs per batch for wide rows (kGuWL for narrow rows)
-    const int ppb = wide ? kPPB : kGuWL;
-    const int i0 = (int)((long long)np * wave / kWaves), i1 = (int)((long long)np * (wave + 1) / kWaves);
-    int cur_t = -1;
-    uint32_t xr[16];
-    SliceRef xf = {0.0f, 0.0f, 0.0f};
-    for (int ib = i0; ib < i1; ib += ppb) {
-        SliceCodes<BITS> sc[kGuWL];
-#pragma unroll
-        for (int k = 0; k < kGuWL; ++k) {
-            const int i = ib + (wide ? k / 2 : k);
-            const int hf = wide ? (k & 1) : half;
-            if (i < i1 && active) load(i, hf, sl, sc[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < kGuWL; ++k) {
-            const int i = ib + (wide ? k / 2 : k);
-            if (i >= i1) continue;  // uniform across the wave
-            const int t = tok_of(i);
-            if (t != cur_t) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(s.xp + (t * nsl + sl) * 20);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint4 u = src[q];
-                    xr[4 * q] = u.x; xr[4 * q + 1] = u.y; xr[4 * q + 2] = u.z; xr[4 * q + 3] = u.w;
-                }
-                xf = s.xref[t * nsl + sl];
-                cur_t = t;
-            }
-            if (wide) {
-                if (k & 1) continue;
-                const float g = wave_sum(slice_value<BITS>(sc[k], xr, xf));
-                const float u = wave_sum(slice_value<BITS>(sc[k + 1], xr, xf));
-                if (lane == 0) ll_put(dst_of(i), silu(g) * u, ep);
-            } else {
-                float v = active ? slice_value<BITS>(sc[k], xr, xf) : 0.0f;
-                v = seg_sum(v, spr);
-                const float g = __shfl(v, 0, kWave), u = __shfl(v, spr, kWave);
-                if (lane == 0) ll_put(dst_of(i), silu(g) * u, ep);
-            }
-        }
-    }
-}
-
-// ---- h of one token: gather, bf16 hi/lo pair table, slice constants --------------------------------
+// ---- h of one token as limbs -------------------------------------------------------------------------
 template <int BITS>
-__device__ bool stage_h(const DecodeParams &p, const Lds &s, const uint64_t *src, uint32_t ep) {
-    const int n = p.K * p.I + p.Is, nsl = n / 32;
-    if (!ll_gather<true>(src, n, ep, reinterpret_cast<float *>(s.hp), p.ctrl, p.spin_limit)) return false;
-    // one thread per slice: read its 32 floats, write 16 hi pairs and 16 lo pairs in place
-    for (int i = threadIdx.x; i < nsl; i += blockDim.x) {
-        uint32_t *row = s.hp + (size_t)i * 36;
-        float v[32];
-#pragma unroll
-        for (int c = 0; c < 32; ++c) v[c] = __uint_as_float(row[c]);
-        uint32_t hi[16], lo[16];
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const float a = v[pair_col_a<BITS>(q)], c = v[pair_col_b<BITS>(q)];
-            const uint16_t ah = f32_to_bf16_rne(a), ch = f32_to_bf16_rne(c);
-            const uint16_t al = f32_to_bf16_rne(a - bf16_to_f32(ah)), cl = f32_to_bf16_rne(c - bf16_to_f32(ch));
-            hi[q] = (uint32_t)ah | ((uint32_t)ch << 16);
-            lo[q] = (uint32_t)al | ((uint32_t)cl << 16);
-        }
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            row[q] = hi[q];
-            row[16 + q] = lo[q];
-        }
-        s.href[i] = slice_ref<BITS>(hi, 2, lo);
-    }
-    lds_barrier();
-    return true;
-}
-
-// ---- down projection of this workgroup's rows --------------------------------------------------------
-// nv vectors of length len (h slices starting at slice sl0, vector v at sl0 + v * len / 32), rows
-// from R (row v * nr + rl) -> out[v * RB + rl]. Jobs (v, rl) v-major; a wave-load holds
-// rpw = 64 / (len / 32) jobs; wave w takes the contiguous wave-loads [nwl w / 8, nwl (w + 1) / 8),
-// so a lane's h slice changes rarely (kept in registers).
-template <int BITS>
-__device__ void down_rows(const Lds &s, const Rows &R, int nv, int len, int nr, uint32_t nrm, int sl0, float *out,
-                          int RB) {
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int spr = len / 32, rpw = kWave / spr;
-    const int seg = lane / spr, sl = lane % spr;
-    const int njobs = nv * nr, nwl = (njobs + rpw - 1) / rpw;
-    const int w0 = (int)((long long)nwl * wave / kWaves), w1 = (int)((long long)nwl * (wave + 1) / kWaves);
-    int cur = -1;
-    uint32_t hv[32];
-    SliceRef hr = {0.0f, 0.0f, 0.0f};
-    constexpr int kU = 4;  // wave-loads whose codes are read before any of their math
-    for (int wb = w0; wb < w1; wb += kU) {
-        SliceCodes<BITS> sc[kU];
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int job = (wb + u) * rpw + seg;
-            if (wb + u < w1 && job < njobs) lds_slice<BITS>(sc[u], R, job, sl);
-        }
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            if (wb + u >= w1) break;  // uniform across the wave
-            const int job = (wb + u) * rpw + seg;
-            const bool ok = job < njobs;
-            float val = 0.0f;
-            int v = 0, rl = 0;
-            if (ok) {
-                v = div_by(job, nrm);
-                rl = job - v * nr;
-                if (v != cur) {
-                    const int si = sl0 + v * spr + sl;
-                    const uint4 *src = reinterpret_cast<const uint4 *>(s.hp + (size_t)si * 36);
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const uint4 h4 = src[q];
-                        hv[4 * q] = h4.x; hv[4 * q + 1] = h4.y; hv[4 * q + 2] = h4.z; hv[4 * q + 3] = h4.w;
-                    }
-                    hr = s.href[si];
-                    cur = v;
-                }
-                val = slice_value2<BITS>(sc[u], hv, hv + 16, hr);
-            }
-            val = seg_sum(val, spr);
-            if (ok && sl == 0) out[v * RB + rl] = val;
-        }
-    }
-}
-
-// ---- h of one token as limbs (4-bit rows) ------------------------------------------------------------
-__device__ bool stage_h4(const DecodeParams &p, const Lds &s, const uint64_t *src, uint32_t ep) {
+__device__ bool stage_hq(const DecodeParams &p, const Lds &s, const uint64_t *src, uint32_t ep) {
     const int n = p.K * p.I + p.Is;
     const float *hf = reinterpret_cast<const float *>(s.hp);
     if (!ll_gather<false>(src, n, ep, reinterpret_cast<float *>(s.hp), p.ctrl, p.spin_limit)) return false;
@@ -914,22 +643,25 @@ __device__ bool stage_h4(const DecodeParams &p, const Lds &s, const uint64_t *sr
         const int gi = it >> 4, m = it & 15;
         float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = hf[gi * 64 + limb_col(4 * m + e)];
-        build_limbs(v, s.hq + (size_t)gi * 192, s.hsx + gi);
+        for (int e = 0; e < 4; ++e) v[e] = hf[gi * 64 + limb_col<BITS>(4 * m + e)];
+        build_limbs<BITS>(v, s.hq + (size_t)gi * 192, s.hsx + gi);
     }
     lds_barrier();
     return true;
 }
 
-// ---- down projection on MFMA (4-bit rows) ------------------------------------------------------------
+// ---- down projection on MFMA ------------------------------------------------------------------------
 // Jobs (v, rl) of nv vectors x nr rows are numbered job = v * nr + rl (the staged row); a tile is
 // th = min(16, 3 nr + 1) consecutive jobs, which touch at most 4 vectors. A row 4u + j = limb j of
 // the tile's u-th vector (row 4u + 3 repeats limb 2); B column i = the codes of weight row i of the
 // tile. Operand layouts (lane l, i = l % 16, kb = l / 16): A[i][16 kb + e], B[16 kb + e][i],
 // C[4 kb + r][i], so lane (i, kb) ends with weight row i against the three limbs of tile vector
 // kb: it owns row i when that is the row's vector. Groups of h: gbase + v * len / 64 + g.
-__device__ void down_tile_mfma4(const Lds &s, const Rows &R, int nv, int len, int nr, uint32_t nrm, int th, int tau,
-                                int gbase, float *out, int RB) {
+template <int BITS>
+__device__ void down_tile_mfma(const Lds &s, const Rows &R, int nv, int len, int nr, uint32_t nrm, int th, int tau,
+                               int gbase, float *out, int RB) {
+    typedef CodeFmt<BITS> F;
+    typedef typename F::lane_t qv_t;
     const int lane = threadIdx.x % kWave, i = lane % 16, kb = lane / 16;
     const int njobs = nv * nr, j0 = tau * th, jn = min(j0 + th, njobs);
     const int ngv = len / 64, gm = min(ngv, 8) - 1;
@@ -938,7 +670,7 @@ __device__ void down_tile_mfma4(const Lds &s, const Rows &R, int nv, int len, in
     const bool wok = i < th && j0 + i < jn;
     const int wrow = wok ? j0 + i : j0, vi = div_by(wrow, nrm);
     const bool own = wok && vi - vfirst == kb;
-    const char *qbase = R.c + (size_t)wrow * R.cb + kb * 8;
+    const char *qbase = R.c + (size_t)wrow * R.cb + kb * (F::group_bytes / 4);
     const int qswz = wrow & gm;
     const uint16_t *sp = reinterpret_cast<const uint16_t *>(R.s + (size_t)wrow * R.sb);
     const uint16_t *bp = reinterpret_cast<const uint16_t *>(R.b + (size_t)wrow * R.sb);
@@ -951,7 +683,7 @@ __device__ void down_tile_mfma4(const Lds &s, const Rows &R, int nv, int len, in
     // current pair's math (scheduling barriers keep the compiler from sinking them)
     struct Pair {
         i32x4_t a0, a1;
-        uint2 q0, q1;
+        qv_t q0, q1;
         uint32_t sv, bv;  // bf16 scale / bias of groups g (low half) and g + 1 (high half)
         float4 gx;        // entries of groups g and g + 1
     };
@@ -959,8 +691,8 @@ __device__ void down_tile_mfma4(const Lds &s, const Rows &R, int nv, int len, in
         Pair d;
         d.a0 = *reinterpret_cast<const i32x4_t *>(abase + (size_t)g * 192);
         d.a1 = *reinterpret_cast<const i32x4_t *>(abase + (size_t)g * 192 + 192);
-        d.q0 = *reinterpret_cast<const uint2 *>(qbase + ((g ^ qswz) * 32));
-        d.q1 = *reinterpret_cast<const uint2 *>(qbase + (((g + 1) ^ qswz) * 32));
+        d.q0 = *reinterpret_cast<const qv_t *>(qbase + ((g ^ qswz) * F::group_bytes));
+        d.q1 = *reinterpret_cast<const qv_t *>(qbase + (((g + 1) ^ qswz) * F::group_bytes));
         d.sv = *reinterpret_cast<const uint32_t *>(sp + g);
         d.bv = *reinterpret_cast<const uint32_t *>(bp + g);
         d.gx = *reinterpret_cast<const float4 *>(gsx + g);
@@ -973,8 +705,9 @@ __device__ void down_tile_mfma4(const Lds &s, const Rows &R, int nv, int len, in
         const i32x4_t c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(d.a1, code_bytes(d.q1), zero, 0, 0, 0);
         const float s0 = __uint_as_float(d.sv << 16), b0 = __uint_as_float(d.bv << 16);
         const float s1 = __uint_as_float(d.sv & 0xFFFF0000u), b1 = __uint_as_float(d.bv & 0xFFFF0000u);
-        acc = fmaf(d.gx.y, fmaf(s0, comb3(c0[0], c0[1], c0[2]), fmaf(8.0f, s0, b0) * d.gx.x), acc);
-        acc = fmaf(d.gx.w, fmaf(s1, comb3(c1[0], c1[1], c1[2]), fmaf(8.0f, s1, b1) * d.gx.z), acc);
+        constexpr float zp = F::zp;
+        acc = fmaf(d.gx.y, fmaf(s0, comb3(c0[0], c0[1], c0[2]), fmaf(zp, s0, b0) * d.gx.x), acc);
+        acc = fmaf(d.gx.w, fmaf(s1, comb3(c1[0], c1[1], c1[2]), fmaf(zp, s1, b1) * d.gx.z), acc);
     };
     const int glast = ngv - 2;
     Pair pa = load(0);
@@ -992,18 +725,19 @@ __device__ void down_tile_mfma4(const Lds &s, const Rows &R, int nv, int len, in
 
 // Every routed vector (rows from rd) and the shared vector (rows from sd) of one token; tiles are
 // dealt round-robin over the waves.
-__device__ void down_all_mfma4(const Lds &s, const Rows &rd, const Rows &sd, int K, int I, int Is, int nr,
-                               uint32_t nrm, float *out, int RB) {
+template <int BITS>
+__device__ void down_all_mfma(const Lds &s, const Rows &rd, const Rows &sd, int K, int I, int Is, int nr,
+                              uint32_t nrm, float *out, int RB) {
     const int wave = threadIdx.x / kWave;
     const int th = min(16, 3 * nr + 1);
     const int nrt = (K * nr + th - 1) / th, nst = Is ? (nr + th - 1) / th : 0;
     for (int u = wave; u < nrt + nst; u += kWaves) {
-        if (u < nrt) down_tile_mfma4(s, rd, K, I, nr, nrm, th, u, 0, out, RB);
-        else down_tile_mfma4(s, sd, 1, Is, nr, nrm, th, u - nrt, K * I / 64, out + K * RB, RB);
+        if (u < nrt) down_tile_mfma<BITS>(s, rd, K, I, nr, nrm, th, u, 0, out, RB);
+        else down_tile_mfma<BITS>(s, sd, 1, Is, nr, nrm, th, u - nrt, K * I / 64, out + K * RB, RB);
     }
 }
 
-// ---- gate|up + SwiGLU on MFMA (4-bit rows) -----------------------------------------------------------
+// ---- gate|up + SwiGLU on MFMA -----------------------------------------------------------------------
 // The same engine with A row 4t' + j = limb j of token 4 tb + t' (token blocks tb of 4; rows past
 // T repeat token T - 1) and B column i = staged row i of a 16-row tile (rows 2m / 2m + 1 = gate /
 // up of pair m); lane (i, kb) ends with row i against token 4 tb + kb. The H columns are split into
@@ -1015,9 +749,11 @@ __device__ void down_all_mfma4(const Lds &s, const Rows &rd, const Rows &sd, int
 //   busy: waves 0 .. busy-1 arrive late (they are selecting experts), so the units go to the other
 //   waves first; max_units bounds ranges x tiles (it alone fixes the ranges, so results do not
 //   depend on busy).
-template <bool ALL, typename TokOf, typename DstOf>
-__device__ void gate_up_mfma4(const DecodeParams &p, const Lds &s, const Rows &R, int np, TokOf tok_of,
-                              DstOf dst_of, uint32_t ep, int busy = 0, int max_units = kWaves) {
+template <int BITS, bool ALL, typename TokOf, typename DstOf>
+__device__ void gate_up_mfma(const DecodeParams &p, const Lds &s, const Rows &R, int np, TokOf tok_of,
+                             DstOf dst_of, uint32_t ep, int busy = 0, int max_units = kWaves) {
+    typedef CodeFmt<BITS> F;
+    typedef typename F::lane_t qv_t;
     const int lane = threadIdx.x % kWave, i = lane % 16, kb = lane / 16;
     const int wave = (threadIdx.x / kWave + kWaves - busy) % kWaves;  // busy waves come last
     const int T = p.T, ng = p.H / 64, gm = min(ng, 8) - 1;
@@ -1036,7 +772,7 @@ __device__ void gate_up_mfma4(const DecodeParams &p, const Lds &s, const Rows &R
         const bool wok = row < nrows;
         const int wrow = wok ? row : 16 * tau;
         const int tk = ALL ? 0 : tok_of(wrow >> 1);
-        const char *qbase = R.c + (size_t)wrow * R.cb + kb * 8;
+        const char *qbase = R.c + (size_t)wrow * R.cb + kb * (F::group_bytes / 4);
         const int qswz = wrow & gm;
         const uint16_t *sp = reinterpret_cast<const uint16_t *>(R.s + (size_t)wrow * R.sb);
         const uint16_t *bp = reinterpret_cast<const uint16_t *>(R.b + (size_t)wrow * R.sb);
@@ -1046,7 +782,7 @@ __device__ void gate_up_mfma4(const DecodeParams &p, const Lds &s, const Rows &R
         // operands of the group pair (g, g + 1), g even (token blocks 0 and 1)
         struct Pair {
             i32x4_t a00, a01, a10, a11;
-            uint2 q0, q1;
+            qv_t q0, q1;
             uint32_t sv, bv;
             float4 x0, x1;
         };
@@ -1054,8 +790,8 @@ __device__ void gate_up_mfma4(const DecodeParams &p, const Lds &s, const Rows &R
             Pair d;
             d.a00 = *reinterpret_cast<const i32x4_t *>(a0p + (size_t)g * 192);
             d.a01 = *reinterpret_cast<const i32x4_t *>(a0p + (size_t)g * 192 + 192);
-            d.q0 = *reinterpret_cast<const uint2 *>(qbase + ((g ^ qswz) * 32));
-            d.q1 = *reinterpret_cast<const uint2 *>(qbase + (((g + 1) ^ qswz) * 32));
+            d.q0 = *reinterpret_cast<const qv_t *>(qbase + ((g ^ qswz) * F::group_bytes));
+            d.q1 = *reinterpret_cast<const qv_t *>(qbase + (((g + 1) ^ qswz) * F::group_bytes));
             d.sv = *reinterpret_cast<const uint32_t *>(sp + g);
             d.bv = *reinterpret_cast<const uint32_t *>(bp + g);
             d.x0 = *reinterpret_cast<const float4 *>(x0p + g);
@@ -1069,9 +805,10 @@ __device__ void gate_up_mfma4(const DecodeParams &p, const Lds &s, const Rows &R
         float acc0 = 0.0f, acc1 = 0.0f;
         auto step = [&](const Pair &d) {
             const i32x4_t zero = {0, 0, 0, 0}, b0 = code_bytes(d.q0), b1 = code_bytes(d.q1);
-            const float s0 = __uint_as_float(d.sv << 16), z0 = fmaf(8.0f, s0, __uint_as_float(d.bv << 16));
+            constexpr float zp = F::zp;
+            const float s0 = __uint_as_float(d.sv << 16), z0 = fmaf(zp, s0, __uint_as_float(d.bv << 16));
             const float s1 = __uint_as_float(d.sv & 0xFFFF0000u);
-            const float z1 = fmaf(8.0f, s1, __uint_as_float(d.bv & 0xFFFF0000u));
+            const float z1 = fmaf(zp, s1, __uint_as_float(d.bv & 0xFFFF0000u));
             i32x4_t c = __builtin_amdgcn_mfma_i32_16x16x64_i8(d.a00, b0, zero, 0, 0, 0);
             acc0 = fmaf(d.x0.y, fmaf(s0, comb3(c[0], c[1], c[2]), z0 * d.x0.x), acc0);
             c = __builtin_amdgcn_mfma_i32_16x16x64_i8(d.a01, b1, zero, 0, 0, 0);
@@ -1157,26 +894,10 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         dma_wait();  // this layer's router and shared rows (staged during the previous layer)
         lds_barrier();
 
-        // ---- R: router logits and the shared expert's gate|up, from LDS
+        // ---- R: router logits from LDS, then x as limbs (its barriers also end this phase)
         router_logits<BITS>(p, l, s, w, ll_lg, ep);
         if (!Is && b == 0 && tid < T) ll_put(ll_lg + (size_t)tid * (E + 1) + E, 0.0f, ep);  // unused column
-        if constexpr (BITS == 4) build_x_limbs(p, s);
-        if (Is && BITS != 4) {
-            const Rows sg = sg_rows(p, s);
-            const uint32_t tdiv = p.tdiv;
-            gate_up<BITS>(
-                p, s, w.nps * T,
-                [&](int i, int hf, int sl, SliceCodes<BITS> &sc) {
-                    lds_slice<BITS>(sc, sg, 2 * div_by(i, tdiv) + hf, sl);
-                },
-                [&](int i) { return i - div_by(i, tdiv) * T; },
-                [&](int i) {
-                    const int r = div_by(i, tdiv);
-                    return ll_h + (size_t)(i - r * T) * HW + KI + (b + r * nb);
-                },
-                ep);
-        }
-        lds_barrier();
+        build_x_limbs<BITS>(p, s);
 
         // ---- G: routing (identical in every workgroup), then routed gate|up + SwiGLU
         if (!ll_gather<false>(ll_lg, T * (E + 1), ep, s.lg, p.ctrl, p.spin_limit)) { dma_wait(); return; }
@@ -1187,10 +908,10 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
             const int first = min(T + kWaves / 2, kWaves - 1);
             stage_router(p, l + 1, s, w, DmaWaves{first, kWaves - first});
         }
-        if (Is && BITS == 4) {
+        if (Is) {
             // the shared expert's gate|up runs on the waves not selecting experts; its barrier also
             // publishes the routing
-            gate_up_mfma4<true>(
+            gate_up_mfma<BITS, true>(
                 p, s, sg_rows(p, s), w.nps, [](int) { return 0; },
                 [&](int m, int t) { return ll_h + (size_t)t * HW + KI + (b + m * nb); }, ep, T, kWaves / 2);
         } else {
@@ -1223,25 +944,13 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
                           rg, mfma_swz(BITS, H));
                 dma_wait();
                 lds_barrier();
-                if constexpr (BITS == 4) {
-                    gate_up_mfma4<false>(
-                        p, s, rg, nc, [&](int i) { return div_by((pb + i) >> lgI, kdiv); },
-                        [&](int i, int) {
-                            const int P = pb + i, t = div_by(P >> lgI, kdiv);
-                            return ll_h + (size_t)t * HW + (P - t * KI);
-                        },
-                        ep);
-                } else {
-                    gate_up<BITS>(
-                        p, s, nc,
-                        [&](int i, int hf, int sl, SliceCodes<BITS> &sc) { lds_slice<BITS>(sc, rg, 2 * i + hf, sl); },
-                        [&](int i) { return div_by((pb + i) >> lgI, kdiv); },
-                        [&](int i) {
-                            const int P = pb + i, t = div_by(P >> lgI, kdiv);
-                            return ll_h + (size_t)t * HW + (P - t * KI);
-                        },
-                        ep);
-                }
+                gate_up_mfma<BITS, false>(
+                    p, s, rg, nc, [&](int i) { return div_by((pb + i) >> lgI, kdiv); },
+                    [&](int i, int) {
+                        const int P = pb + i, t = div_by(P >> lgI, kdiv);
+                        return ll_h + (size_t)t * HW + (P - t * KI);
+                    },
+                    ep);
                 lds_barrier();
             }
         }
@@ -1257,21 +966,13 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
             later = w.nps ? dma_qrows_count(2 * w.nps, H, BITS) : 0;
         }
         for (int t = 0; t < T; ++t) {
-            if (!(BITS == 4 ? stage_h4(p, s, ll_h + (size_t)t * HW, ep) : stage_h<BITS>(p, s, ll_h + (size_t)t * HW, ep))) {
-                dma_wait();
-                return;
-            }
+            if (!stage_hq<BITS>(p, s, ll_h + (size_t)t * HW, ep)) { dma_wait(); return; }
             if (t == 0) dma_wait_but(later);
             else dma_wait();
             lds_barrier();
             if (nr > 0) {
                 float *pt = s.part + (size_t)t * (K + 1) * RB;
-                if constexpr (BITS == 4) {
-                    down_all_mfma4(s, rd_rows(p, s), sd_rows(p, s), K, I, Is, nr, w.nrm, pt, RB);
-                } else {
-                    down_rows<BITS>(s, rd_rows(p, s), K, I, nr, w.nrm, 0, pt, RB);
-                    if (Is) down_rows<BITS>(s, sd_rows(p, s), 1, Is, nr, w.nrm, KI / 32, pt + K * RB, RB);
-                }
+                down_all_mfma<BITS>(s, rd_rows(p, s), sd_rows(p, s), K, I, Is, nr, w.nrm, pt, RB);
             }
             lds_barrier();
             if (t + 1 < T) stage_routed_down(p, l, s, t + 1, r0, nr, w.nrm);

@@ -15,7 +15,7 @@ struct QMat {
 
 // LDS plan of the decode kernel: byte offsets of every region (computed once on the host).
 struct DecodeLds {
-    int xp, xref, lg, sidx, sw, gam, rt, sg, sd, rd, rg, hp, href, part, red, xq, xsx, hq, hsx;
+    int xp, lg, sidx, sw, gam, rt, sg, sd, rd, rg, hp, part, red, xq, xsx, hq, hsx;
     int total;
 };
 
@@ -75,34 +75,29 @@ __host__ __device__ inline DecodeWs decode_ws_layout(int L, int T, int H, int E,
 // the y rows per workgroup follow from the grid); cp = routed gate|up pairs per LDS chunk.
 __host__ inline DecodeLds decode_lds_plan(int T, int H, int E, int K, int I, int Is, int bits, int grid, int cp) {
     DecodeLds d;
-    const bool q4 = bits == 4;
     const size_t RB = ((size_t)H + grid - 1) / grid;
     const size_t nrr = ((size_t)E + (Is ? 1 : 0) + grid - 1) / grid;
     const size_t nps = Is ? ((size_t)Is + grid - 1) / grid : 0;
     const size_t cbH = (size_t)H * bits / 8, sbH = (size_t)H / 32;
     const size_t cbS = (size_t)Is * bits / 8, sbS = (size_t)Is / 32;
     const size_t cbI = (size_t)I * bits / 8, sbI = (size_t)I / 32;
-    const size_t nh = (size_t)K * I + Is, nsl = nh / 32;
-    // hp: gathered h (8-bit rows: then its bf16 hi/lo pair table, 36 words per slice), the y gather
-    // buffer, the exchange-start gather and (4-bit rows) the gate|up partial sums
-    size_t hp = q4 ? nh * 4 : nsl * 36 * 4;
+    const size_t nh = (size_t)K * I + Is;
+    // hp: gathered h (fp32), the y gather buffer, the exchange-start gather and the gate|up partial
+    // sums ([ranges][tokens][rows], ranges x tiles <= 8 or one range)
+    size_t hp = nh * 4;
     if ((size_t)H * 4 > hp) hp = (size_t)H * 4;
     if ((size_t)kMaxGrid * 4 > hp) hp = (size_t)kMaxGrid * 4;
     const size_t gpart = 4 * (size_t)T * (128 > 2 * cp ? 128 : 2 * cp) + 8 * (size_t)T * nps;
-    if (q4 && gpart > hp) hp = gpart;
-    // 4-bit rows: the x pairs, the x limbs and the h limbs share one region (disjoint lifetimes), as
-    // do the two limb-group tables; the slice constants are not used
+    if (gpart > hp) hp = gpart;
+    // the x pairs, the x limbs and the h limbs share one region (disjoint lifetimes), as do the two
+    // limb-group tables
     size_t xp = 4 * (size_t)T * (H / 32) * 20;
-    size_t gsx = 0;
-    if (q4) {
-        if (3 * (size_t)T * H > xp) xp = 3 * (size_t)T * H;
-        if (3 * nh > xp) xp = 3 * nh;
-        gsx = 8 * (size_t)T * (H / 64);
-        if (8 * (nh / 64) > gsx) gsx = 8 * (nh / 64);
-    }
-    const size_t sz[16] = {
-        xp,                              // xp (4-bit rows: also xq and hq)
-        q4 ? 0 : 12 * (size_t)T * (H / 32),  // xref
+    if (3 * (size_t)T * H > xp) xp = 3 * (size_t)T * H;
+    if (3 * nh > xp) xp = 3 * nh;
+    size_t gsx = 8 * (size_t)T * (H / 64);
+    if (8 * (nh / 64) > gsx) gsx = 8 * (nh / 64);
+    const size_t sz[14] = {
+        xp,                              // xp (also xq and hq)
         4 * (size_t)T * (E + 1),         // lg
         4 * (size_t)T * K,               // sidx
         4 * (size_t)T * K,               // sw
@@ -113,14 +108,13 @@ __host__ inline DecodeLds decode_lds_plan(int T, int H, int E, int K, int I, int
         (size_t)K * RB * (cbI + 2 * sbI),  // rd
         2 * (size_t)cp * (cbH + 2 * sbH),  // rg
         hp,                              // hp
-        q4 ? 0 : 12 * nsl,               // href
         4 * (size_t)T * (K + 1) * RB,    // part
         4 * 64,                          // red
         gsx};                            // xsx (also hsx)
-    int *o[16] = {&d.xp, &d.xref, &d.lg, &d.sidx, &d.sw, &d.gam, &d.rt, &d.sg, &d.sd, &d.rd, &d.rg, &d.hp, &d.href,
-                  &d.part, &d.red, &d.xsx};
+    int *o[14] = {&d.xp, &d.lg, &d.sidx, &d.sw, &d.gam, &d.rt, &d.sg, &d.sd, &d.rd, &d.rg, &d.hp, &d.part, &d.red,
+                  &d.xsx};
     size_t off = 0;
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 14; ++i) {
         *o[i] = (int)off;
         off = align_up(off + sz[i], 16);
     }
