@@ -60,41 +60,52 @@ __device__ __forceinline__ void fail(int *ctrl) {
     __hip_atomic_store(G(ctrl), 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait until words src[0..n) carry epoch ep and copy their values into LDS: word i goes to
-// dst[i] (PAD = false) or to dst[i + 4 (i / 32)] (PAD = true: 36-word stride per 32 words).
-// Called by the whole workgroup; n may be any size (passes of kMaxGather words per thread). All of
-// a pass's loads are in flight together; only words not yet current are polled again.
-// Returns false on timeout or when any workgroup has failed.
-template <bool PAD>
+// Wait until words src[0..n) carry epoch ep and copy their values into LDS (word i to dst[i]).
+// Called by the whole workgroup; n may be any size (passes of kMaxGather words per thread). Thread
+// tid holds words tid + k * blockDim (slot k) of a pass in registers; a wave re-reads all its slots
+// (every load of a poll in flight together) until one poll finds all of them current -- a current
+// word stays current, so re-reading words that were already there is harmless. The poll loop is
+// instantiated for the number of slots the wave has (rounded up to 1, 4, 12 or 16), so it stays short
+// and its period -- the delay between a word's arrival and its detection -- with it. The values
+// go to LDS once at the end. Returns false on timeout or when any workgroup has failed.
+template <int NW>
+__device__ __forceinline__ bool gather_slots(const uint64_t *src, int m, uint32_t ep, float *dst, int *ctrl,
+                                             unsigned spin) {
+    const int tid = threadIdx.x;
+    uint64_t w[NW];
+    for (unsigned it = 0;; ++it) {
+        // lanes past m read word m - 1 (it becomes current like any other), which keeps the loads
+        // unpredicated
+#pragma unroll
+        for (int k = 0; k < NW; ++k) w[k] = ll_get(src + min(tid + k * kDecodeThreads, m - 1));
+        bool done = true;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) done &= static_cast<uint32_t>(w[k] >> 32) == ep;
+        if (__ballot(!done) == 0ull) break;
+        if (it >= spin) { fail(ctrl); return false; }
+        if ((it & 31u) == 31u && status_of(ctrl) != 0) return false;
+        __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        const int i = tid + k * kDecodeThreads;
+        if (i < m) dst[i] = __uint_as_float(static_cast<uint32_t>(w[k]));
+    }
+    return true;
+}
 __device__ bool ll_gather(const uint64_t *src, int n, uint32_t ep, float *dst, int *ctrl, unsigned spin) {
     constexpr int kPass = kMaxGather * kDecodeThreads;
-    const int tid = threadIdx.x;
+    const int wbase = __builtin_amdgcn_readfirstlane(threadIdx.x & ~(kWave - 1));
     bool ok = true;
     for (int base = 0; base < n && ok; base += kPass) {
         const int m = min(n - base, kPass);
-        uint32_t pending = 0;
-#pragma unroll
-        for (int k = 0; k < kMaxGather; ++k)
-            if (tid + k * kDecodeThreads < m) pending |= 1u << k;
-        unsigned it = 0;
-        while (pending) {
-            uint64_t w[kMaxGather];
-#pragma unroll
-            for (int k = 0; k < kMaxGather; ++k)
-                w[k] = ((pending >> k) & 1u) ? ll_get(src + base + tid + k * kDecodeThreads) : 0;
-#pragma unroll
-            for (int k = 0; k < kMaxGather; ++k) {
-                if (((pending >> k) & 1u) && static_cast<uint32_t>(w[k] >> 32) == ep) {
-                    const int i = base + tid + k * kDecodeThreads;
-                    dst[PAD ? i + 4 * (i >> 5) : i] = __uint_as_float(static_cast<uint32_t>(w[k]));
-                    pending &= ~(1u << k);
-                }
-            }
-            if (!pending) break;
-            if (++it > spin) { fail(ctrl); ok = false; break; }
-            if ((it & 31u) == 0 && status_of(ctrl) != 0) { ok = false; break; }
-            __builtin_amdgcn_s_sleep(1);
-        }
+        // slots of this wave: k < kw (the wave's first word of slot k is below m); wave-uniform
+        const int kw = m > wbase ? (m - wbase + kDecodeThreads - 1) / kDecodeThreads : 0;
+        if (kw == 0) continue;
+        if (kw <= 1) ok = gather_slots<1>(src + base, m, ep, dst + base, ctrl, spin);
+        else if (kw <= 4) ok = gather_slots<4>(src + base, m, ep, dst + base, ctrl, spin);
+        else if (kw <= 12) ok = gather_slots<12>(src + base, m, ep, dst + base, ctrl, spin);
+        else ok = gather_slots<kMaxGather>(src + base, m, ep, dst + base, ctrl, spin);
     }
     // workgroup-wide AND of ok through LDS (slots written, read, then released again)
     __shared__ int vote[kWaves];
@@ -531,7 +542,7 @@ __device__ bool layer_input(const DecodeParams &p, int l, uint32_t ep, const Lds
         const uint64_t *ysrc = p.ll_y + (size_t)(l - 1) * T * H;
         float *yb = reinterpret_cast<float *>(s.hp);
         for (int t = 0; t < T; ++t) {
-            if (!ll_gather<false>(ysrc + (size_t)t * H, H, ep, yb, p.ctrl, p.spin_limit)) return false;
+            if (!ll_gather(ysrc + (size_t)t * H, H, ep, yb, p.ctrl, p.spin_limit)) return false;
             float ss = 0.0f;
             for (int h = threadIdx.x; h < H; h += blockDim.x) ss += yb[h] * yb[h];
             ss = wave_sum(ss);
@@ -637,7 +648,7 @@ template <int BITS>
 __device__ bool stage_hq(const DecodeParams &p, const Lds &s, const uint64_t *src, uint32_t ep) {
     const int n = p.K * p.I + p.Is;
     const float *hf = reinterpret_cast<const float *>(s.hp);
-    if (!ll_gather<false>(src, n, ep, reinterpret_cast<float *>(s.hp), p.ctrl, p.spin_limit)) return false;
+    if (!ll_gather(src, n, ep, reinterpret_cast<float *>(s.hp), p.ctrl, p.spin_limit)) return false;
     // 16 lanes per group; n / 4 and the block size are multiples of 16, so DPP rows stay whole
     for (int it = threadIdx.x; it < n / 4; it += blockDim.x) {
         const int gi = it >> 4, m = it & 15;
@@ -900,7 +911,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         build_x_limbs<BITS>(p, s);
 
         // ---- G: routing (identical in every workgroup), then routed gate|up + SwiGLU
-        if (!ll_gather<false>(ll_lg, T * (E + 1), ep, s.lg, p.ctrl, p.spin_limit)) { dma_wait(); return; }
+        if (!ll_gather(ll_lg, T * (E + 1), ep, s.lg, p.ctrl, p.spin_limit)) { dma_wait(); return; }
         route_tokens(p, s);
         // layer l+1's router rows (the LDS copy was last read before the logits exchange) stream in
         // during the expert selection, issued by waves with nothing else to do then
@@ -994,7 +1005,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
     dma_wait();
     // the next call may advance the epoch once every workgroup has read it
     if (b == 0) {
-        if (!ll_gather<false>(p0.ll_start, nb, ep, reinterpret_cast<float *>(smem + p0.lds.hp), p0.ctrl,
+        if (!ll_gather(p0.ll_start, nb, ep, reinterpret_cast<float *>(smem + p0.lds.hp), p0.ctrl,
                               p0.spin_limit))
             return;
         if (tid == 0) p0.ctrl[1] = static_cast<int>(ep);
