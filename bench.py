@@ -132,6 +132,61 @@ def batched_leg(stack, steps: int, warmup: int):
             "last_layer_max_load": int(counts.max().item())}
 
 
+SWEEP_TOKENS = list(range(1, 17)) + [32, 64, 128, 512]
+
+
+def crossover_sweep(stack, reps: int):
+    """One layer (layer 0 of the stack, no router bias) through moe_layer_decode (T <= 8) and
+    moe_layer_batched for every T of SWEEP_TOKENS: the mean time per call over `reps` calls after
+    a warm-up, and the largest T at which the decode path is the faster one (below it every
+    decode-capable T is faster too)."""
+    import torch
+
+    import quantized_moe_decode_router_amd as moe
+    import synth
+
+    shape, dev = stack.shape, stack.router.device
+    layer = stack.layer(0)
+    stream = torch.cuda.current_stream()
+    rows = []
+    for T in SWEEP_TOKENS:
+        x = synth.make_x(shape, T, 7, step=T, device=dev)
+        y = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
+        row = {"tokens": T}
+        paths = [("batched", moe.MOE_WS_BATCHED, moe.moe_layer_batched)]
+        if T <= 8:
+            paths.insert(0, ("decode", moe.MOE_WS_DECODE, moe.moe_layer_decode))
+        for name, kind, fn in paths:
+            ws = moe.workspace(shape, T, kind, dev)
+            for _ in range(5):
+                fn(shape, layer, x, T, y, workspace=ws, stream=stream)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                fn(shape, layer, x, T, y, workspace=ws, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / reps
+            row[name + "_us"] = round(us, 2)
+            row[name + "_us_per_token"] = round(us / T, 3)
+        rows.append(row)
+        print(f"[sweep] T={T}: " + ", ".join(f"{k} {v}" for k, v in row.items() if k != "tokens"),
+              file=sys.stderr, flush=True)
+    cross = 0
+    for row in rows:
+        if "decode_us" in row and row["decode_us"] <= row["batched_us"]:
+            cross = row["tokens"]
+        elif "decode_us" in row:
+            break
+    return {"workload": stack_name(stack), "layer": 0, "reps": reps, "rows": rows, "crossover": cross}
+
+
+def stack_name(stack) -> str:
+    s = stack.shape
+    return f"H{s.hidden}_E{s.num_experts}_K{s.top_k}_I{s.inter}_Is{s.shared_inter}_{s.bits}bit"
+
+
 def main():
     import synth
     ap = argparse.ArgumentParser()
@@ -146,6 +201,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--batched-steps", type=int, default=10,
                     help="steps of the batched leg (0 skips it)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only the decode / batched crossover sweep of one layer (one JSON line)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -164,6 +221,9 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] {wl.describe()}: {stack.nbytes() / 1e9:.2f} GB generated in "
           f"{time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    if args.sweep:
+        print(json.dumps({"sweep": crossover_sweep(stack, reps=50)}), flush=True)
+        return
     nsteps = args.warmup + args.steps
     xs = torch.stack([synth.make_x(shape, T, wl.seed, step=s, device=dev) for s in range(nsteps)])
     y = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)

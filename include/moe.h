@@ -106,6 +106,15 @@ typedef struct {
 #define MOE_WS_DECODE 0
 #define MOE_WS_BATCHED 1
 #define MOE_WS_STACK 2
+#define MOE_WS_FORWARD 3 /* moe_layer_forward: a decode part (status word first), then a batched part */
+
+/* The two evaluations of a layer, as moe_layer_path names them */
+#define MOE_PATH_DECODE 0
+#define MOE_PATH_BATCHED 1
+/* Largest token count moe_layer_forward sends to the decode path when given crossover <= 0.
+ * Measured on MI355X for one 35B-shaped 4-bit layer (H 2048, E 256, top-8, I = Is = 512): the
+ * decode call is faster than the batched one at every T it takes (T = 8: 108 vs 123 us). */
+#define MOE_DEFAULT_CROSSOVER 8
 
 /*
  * Router: logits, top-k selection and renormalised weights for T tokens (1 <= T <= 65536).
@@ -182,8 +191,32 @@ moe_status moe_group_pairs(const moe_shape *shape, const int32_t *topk_idx, int3
                            int32_t *offsets, int32_t *perm, int32_t *pos, void *workspace,
                            size_t workspace_bytes, void *stream);
 
-/* Workspace bytes for `kind` (MOE_WS_DECODE, MOE_WS_BATCHED or MOE_WS_STACK), T tokens and, for
- * MOE_WS_STACK, n_layers layers (ignored otherwise); 0 if the arguments are invalid. */
+/*
+ * The decode / batched route boundary (the per-batch-size route selection of a quantised matrix
+ * kernel that the Smelt README's "Lab workflow" section sweeps and then benchmarks on both sides of
+ * the selected boundary): the path moe_layer_forward takes for T tokens.
+ * MOE_PATH_DECODE when T <= crossover (crossover <= 0: MOE_DEFAULT_CROSSOVER), T <= 8 and the shape
+ * is one the decode call takes (the header's decode limits; its LDS plan is checked for the current
+ * device's compute-unit count, or 256 when no device is visible); MOE_PATH_BATCHED otherwise; -1
+ * for an invalid shape or T outside 1..65536. Host-only: touches no device memory.
+ */
+int32_t moe_layer_path(const moe_shape *shape, int32_t T, int32_t crossover);
+
+/*
+ * One layer for 1 <= T <= 65536 tokens through the path moe_layer_path(shape, T, crossover)
+ * names: exactly moe_layer_decode or moe_layer_batched (same outputs, bit for bit). Arguments as
+ * moe_layer_decode; workspace: moe_workspace_bytes(shape, T, 0, MOE_WS_FORWARD) bytes, zero-filled
+ * before first use: a decode workspace for 8 tokens (status word first), then a batched one for T.
+ * Calls with different T may share a workspace sized for the largest.
+ */
+moe_status moe_layer_forward(const moe_shape *shape, const moe_layer *layer, const uint16_t *x,
+                             int32_t T, int32_t crossover, float *y, int32_t *topk_idx_opt,
+                             float *topk_w_opt, float *logits_opt, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for `kind` (MOE_WS_DECODE, MOE_WS_BATCHED, MOE_WS_STACK or MOE_WS_FORWARD), T
+ * tokens and, for MOE_WS_STACK, n_layers layers (ignored otherwise); 0 if the arguments are
+ * invalid. */
 size_t moe_workspace_bytes(const moe_shape *shape, int32_t T, int32_t n_layers, int32_t kind);
 
 /* Synchronises `stream`, then copies the workspace's device status word into *status. */

@@ -23,12 +23,14 @@ LIB_PATH = os.path.join(_HERE, "_lib", "libmoe_amd.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_TIMEOUT = range(6)
 MOE_ROUTE_LOGITS_IN = 1
-MOE_WS_DECODE, MOE_WS_BATCHED, MOE_WS_STACK = 0, 1, 2
+MOE_WS_DECODE, MOE_WS_BATCHED, MOE_WS_STACK, MOE_WS_FORWARD = 0, 1, 2, 3
+MOE_PATH_DECODE, MOE_PATH_BATCHED = 0, 1
+MOE_DEFAULT_CROSSOVER = 8
 
 MOE_STACK_INDEPENDENT = 1
 
 EXPORTED = ("moe_route", "moe_layer_decode", "moe_stack_decode", "moe_layer_batched", "moe_group_pairs",
-            "moe_workspace_bytes", "moe_read_status", "moe_status_string")
+            "moe_layer_path", "moe_layer_forward", "moe_workspace_bytes", "moe_read_status", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -68,6 +70,9 @@ def lib():
         L.moe_layer_decode.argtypes = [PS, PL, P, I32, P, P, P, P, P, SZ, P]
         L.moe_layer_batched.argtypes = [PS, PL, P, I32, P, P, P, P, P, SZ, P]
         L.moe_group_pairs.argtypes = [PS, P, I32, P, P, P, P, P, SZ, P]
+        L.moe_layer_path.argtypes = [PS, I32, I32]
+        L.moe_layer_path.restype = I32
+        L.moe_layer_forward.argtypes = [PS, PL, P, I32, I32, P, P, P, P, P, SZ, P]
         L.moe_stack_decode.argtypes = [PS, PL, I32, U32, P, I32, P, P, P, P, P, P, P, SZ, P]
         L.moe_workspace_bytes.argtypes = [PS, I32, I32, I32]
         L.moe_workspace_bytes.restype = SZ
@@ -75,7 +80,7 @@ def lib():
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         for name in ("moe_route", "moe_layer_decode", "moe_layer_batched", "moe_stack_decode",
-                     "moe_read_status"):
+                     "moe_layer_forward", "moe_group_pairs", "moe_read_status"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -185,6 +190,24 @@ def moe_layer_batched(shape, layer, x, T: int, y, topk_idx=None, topk_w=None, lo
                                  _ptr(topk_w, "topk_w", torch.float32), _ptr(logits, "logits", torch.float32),
                                  _ptr(workspace, "workspace"), int(wsb), _stream(stream))
     _check(st, "moe_layer_batched")
+
+
+def moe_layer_path(shape, T: int, crossover: int = 0) -> int:
+    s = shape_struct(shape)
+    return int(lib().moe_layer_path(ctypes.byref(s), int(T), int(crossover)))
+
+
+def moe_layer_forward(shape, layer, x, T: int, y, topk_idx=None, topk_w=None, logits=None,
+                      workspace=None, workspace_bytes: Optional[int] = None, stream=None,
+                      crossover: int = 0) -> None:
+    s, L = shape_struct(shape), layer_struct(layer)
+    wsb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    st = lib().moe_layer_forward(ctypes.byref(s), ctypes.byref(L), _ptr(x, "x", _BF16_BITS), int(T),
+                                 int(crossover), _ptr(y, "y", torch.float32),
+                                 _ptr(topk_idx, "topk_idx", torch.int32), _ptr(topk_w, "topk_w", torch.float32),
+                                 _ptr(logits, "logits", torch.float32), _ptr(workspace, "workspace"), int(wsb),
+                                 _stream(stream))
+    _check(st, "moe_layer_forward")
 
 
 def moe_group_pairs(shape, topk_idx, T: int, counts, offsets, perm, pos, workspace=None,

@@ -80,6 +80,16 @@ int decode_chunk(const moe_shape *s, int T, int grid) {
 
 int rows_per_wg(int H, int grid) { return (H + grid - 1) / grid; }
 
+// Compute units assumed by moe_layer_path when no device is visible (MI355X).
+constexpr int kAssumedCus = 256;
+
+// Decode part of a moe_layer_forward workspace: a decode workspace for the largest decode T (its
+// status word at byte 0), rounded up so that the batched part after it stays aligned. Its size does
+// not depend on T, so calls with any T that share the workspace keep the decode exchange words
+// and the batched scratch apart (a batched call never writes where a later decode call looks for
+// words of its epoch).
+size_t forward_decode_part(const moe_shape *s) { return align_up(decode_ws_bytes(s, kMaxDecodeT, 1), 256); }
+
 // Shapes the decode kernel handles (beyond check_shape): rows of at most 64 slices of 32 columns,
 // intermediates of at least 128 columns (whole dwords of scales per row for the LDS staging),
 // and an LDS plan within the compute unit's 160 KiB.
@@ -182,6 +192,10 @@ const char *moe_status_string(moe_status s) {
 
 size_t moe_workspace_bytes(const moe_shape *s, int32_t T, int32_t n_layers, int32_t kind) {
     if (check_shape(s) != MOE_OK || T < 1) return 0;
+    if (kind == MOE_WS_FORWARD) {
+        if (T > kMaxBatchT) return 0;
+        return forward_decode_part(s) + batched_ws_bytes(s, T);
+    }
     if (kind == MOE_WS_DECODE || kind == MOE_WS_STACK) {
         const int L = kind == MOE_WS_DECODE ? 1 : n_layers;
         if (T > kMaxDecodeT || L < 1 || L > kMaxLayers) return 0;
@@ -297,6 +311,30 @@ moe_status moe_layer_batched(const moe_shape *s, const moe_layer *L, const uint1
     p.y = y;
     hipError_t err = moe::launch_batched(p, lay.max_tiles, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int32_t moe_layer_path(const moe_shape *s, int32_t T, int32_t crossover) {
+    if (check_shape(s) != MOE_OK || T < 1 || T > kMaxBatchT) return -1;
+    const int cross = crossover > 0 ? crossover : MOE_DEFAULT_CROSSOVER;
+    if (T > cross || T > kMaxDecodeT) return MOE_PATH_BATCHED;
+    int grid = moe::device_cu_count();
+    if (grid <= 0) grid = kAssumedCus;
+    if (grid > moe::kMaxGrid || decode_supported(s, T, grid) != MOE_OK) return MOE_PATH_BATCHED;
+    return MOE_PATH_DECODE;
+}
+
+moe_status moe_layer_forward(const moe_shape *s, const moe_layer *L, const uint16_t *x, int32_t T,
+                             int32_t crossover, float *y, int32_t *topk_idx_opt, float *topk_w_opt,
+                             float *logits_opt, void *ws, size_t ws_bytes, void *stream) {
+    moe_status st = check_shape(s);
+    if (st != MOE_OK) return st;
+    if (T < 1 || T > kMaxBatchT) return MOE_ERR_INVALID_ARG;
+    if (!ws || !al16(ws) || ws_bytes < moe_workspace_bytes(s, T, 0, MOE_WS_FORWARD)) return MOE_ERR_WORKSPACE;
+    const size_t dpart = forward_decode_part(s);
+    if (moe_layer_path(s, T, crossover) == MOE_PATH_DECODE)
+        return moe_layer_decode(s, L, x, T, y, topk_idx_opt, topk_w_opt, logits_opt, ws, dpart, stream);
+    return moe_layer_batched(s, L, x, T, y, topk_idx_opt, topk_w_opt, logits_opt, static_cast<char *>(ws) + dpart,
+                             ws_bytes - dpart, stream);
 }
 
 moe_status moe_group_pairs(const moe_shape *s, const int32_t *topk_idx, int32_t T, int32_t *counts,

@@ -116,3 +116,40 @@ def test_binding_refuses_host_tensors(L):
     with pytest.raises(ValueError, match="GPU tensor"):
         moe.moe_layer_decode(synth.TINY.shape, st.layer(0), x, 1, torch.empty(1, 256),
                              workspace=torch.empty(16, dtype=torch.uint8))
+
+
+def test_layer_path_boundary(L):
+    """moe_layer_path (host-only): decode for T up to the crossover (default 8) when the decode
+    call takes the shape, batched above it or for shapes the decode kernel does not take."""
+    path = lambda shape, T, c=0: binding.lib().moe_layer_path(ctypes.byref(shape), T, c)
+    s = S()
+    assert [path(s, T) for T in (1, 2, 7, 8)] == [moe.MOE_PATH_DECODE] * 4
+    assert [path(s, T) for T in (9, 16, 512, 65536)] == [moe.MOE_PATH_BATCHED] * 4
+    assert path(s, 3, 2) == moe.MOE_PATH_BATCHED and path(s, 2, 2) == moe.MOE_PATH_DECODE
+    assert path(s, 9, 100) == moe.MOE_PATH_BATCHED  # the decode path takes at most 8 tokens
+    assert path(s, 8, -1) == moe.MOE_PATH_DECODE == path(s, moe.MOE_DEFAULT_CROSSOVER)
+    assert path(S(hidden=4096), 1) == moe.MOE_PATH_BATCHED  # beyond the decode limits
+    assert path(S(inter=64), 1) == moe.MOE_PATH_BATCHED
+    assert path(s, 0) == -1 and path(s, 65537) == -1 and path(S(bits=3), 1) == -1
+    assert moe.moe_layer_path(synth_tiny_shape(), 4) == moe.MOE_PATH_DECODE
+
+
+def synth_tiny_shape():
+    import synth
+    return synth.TINY.shape
+
+
+def test_forward_workspace_and_host_checks(L):
+    s = S()
+    fwd = ws(s, T=512, kind=moe.MOE_WS_FORWARD)
+    # a decode part for 8 tokens (independent of T), then a batched part for T
+    assert fwd >= ws(s, T=8, kind=0) + ws(s, T=512, kind=1)
+    assert ws(s, T=1, kind=moe.MOE_WS_FORWARD) - ws(s, T=1, kind=1) == fwd - ws(s, T=512, kind=1)
+    assert ws(s, T=65537, kind=moe.MOE_WS_FORWARD) == 0
+    f = binding.lib().moe_layer_forward
+    lay, p = _fake_layer(), 1 << 20
+    assert f(ctypes.byref(s), ctypes.byref(lay), p, 0, 0, p, None, None, None, p, fwd, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(s), ctypes.byref(lay), p, 4, 0, p, None, None, None, p, 64, None) == moe.MOE_ERR_WORKSPACE
+    assert f(ctypes.byref(s), ctypes.byref(lay), p, 4, 0, p, None, None, None, None, fwd, None) == moe.MOE_ERR_WORKSPACE
+    assert f(ctypes.byref(S(bits=3)), ctypes.byref(lay), p, 4, 0, p, None, None, None, p, fwd, None) == \
+        moe.MOE_ERR_UNSUPPORTED
