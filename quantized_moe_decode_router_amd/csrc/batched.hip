@@ -1,8 +1,9 @@
 // batched.hip -- one MoE layer for a batch of T tokens (prefill / batched decode) on gfx950.
 //
-// Six launches on one stream, no host synchronisation:
-//   1. router_gemm   logits[T][E] (+ shared-gate logit) = x . R^T on v_mfma_f32_16x16x32_bf16, the
-//                    fp32 router split into bf16 hi + lo (x is bf16, exact)
+// Seven launches on one stream, no host synchronisation:
+//   1. router_split  the fp32 router (and shared gate) as bf16 hi + lo halves, once per call
+//      router_gemm   logits[T][E] (+ shared-gate logit) = x . R^T on v_mfma_f32_16x16x32_bf16 over
+//                    both halves (x is bf16, exact)
 //   2. topk_kernel   one wave per token: top-k by (logit desc, index asc), renormalised weights
 //                    (softmax of the kept logits), gamma = sigmoid(gate logit)
 //   3. bucket_kernel one workgroup: per-expert histogram of the (token, slot) pairs, exclusive scan,
@@ -36,10 +37,38 @@ __device__ __forceinline__ _Float16 bf16_to_f16(uint16_t b) { return (_Float16)b
 // ---- 1. router GEMM ------------------------------------------------------------------------------
 // logits = x . R^T on bf16 MFMA: x is bf16 (exact), every fp32 router weight is split into
 // bf16 hi = rne(R) and lo = rne(R - hi), so R - hi - lo is below 2^-17 |R|; both products are exact
-// in the fp32 accumulators. Tile: 32 tokens x 64 router rows (row E = shared gate), k-steps of 64;
-// wave w: tokens 16 (w & 1) .., rows 32 (w >> 1) ..
+// in the fp32 accumulators. The split is done once per call by router_split (rows E+1: the router,
+// then the shared gate), so that the GEMM only moves bf16 tiles.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-constexpr int kRtT = 32, kRtN = 64;
+constexpr int kSplitThreads = 256;
+
+__global__ void __launch_bounds__(kSplitThreads) router_split(BatchedParams p) {
+    const int H = p.H, N = p.E + (p.sgate ? 1 : 0);
+    const size_t i = ((size_t)blockIdx.x * kSplitThreads + threadIdx.x) * 8;  // 8 weights per thread
+    if (i >= (size_t)N * H) return;
+    const size_t row = i / H, col = i - row * H;
+    const float *src = (row < (size_t)p.E ? p.router + row * H : p.sgate) + col;
+    const float4 a = reinterpret_cast<const float4 *>(src)[0], b = reinterpret_cast<const float4 *>(src)[1];
+    const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint16_t h0 = f32_to_bf16_rne(f[2 * q]), h1 = f32_to_bf16_rne(f[2 * q + 1]);
+        const uint16_t l0 = f32_to_bf16_rne(f[2 * q] - bf16_to_f32(h0));
+        const uint16_t l1 = f32_to_bf16_rne(f[2 * q + 1] - bf16_to_f32(h1));
+        hi[q] = h0 | (uint32_t)h1 << 16;
+        lo[q] = l0 | (uint32_t)l1 << 16;
+    }
+    *reinterpret_cast<uint4 *>(p.rhi + i) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *reinterpret_cast<uint4 *>(p.rlo + i) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+}
+
+// Tile: 32 tokens x 32 router rows x one of ks contiguous ranges of H (blockIdx.z), k-steps of 64;
+// wave w: tokens 16 (w & 1) .., rows 16 (w >> 1) ... The range's partial sums go to lpart; the
+// top-k kernel adds the ranges in order (the ranges keep the k-loop of a workgroup short, so
+// that many workgroups hide each other's load latency).
+constexpr int kRtT = 32, kRtN = 32;
+__host__ __device__ inline int router_ksplit(int H) { return H / 64 < kRouterSplitK ? H / 64 : kRouterSplitK; }
 
 __global__ void __launch_bounds__(kGemmThreads) router_gemm(BatchedParams p) {
     __shared__ __align__(16) uint16_t xs[kRtT][kLdsK];
@@ -49,89 +78,63 @@ __global__ void __launch_bounds__(kGemmThreads) router_gemm(BatchedParams p) {
     const int t0 = blockIdx.x * kRtT, n0 = blockIdx.y * kRtN;
     const int H = p.H, E = p.E, T = p.T;
     const int N = E + (p.sgate ? 1 : 0);
-    // loads: x row xr (8 bf16 at xc); router row rr (16 floats at rc)
-    const int xr = tid / 8, xc = (tid % 8) * 8, rr = tid / 4, rc = (tid % 4) * 16;
-    const bool xok = t0 + xr < T, rok = n0 + rr < N;
-    const uint16_t *xrow = p.x + (size_t)(xok ? t0 + xr : 0) * H;
-    const float *rrow = rok ? (n0 + rr < E ? p.router + (size_t)(n0 + rr) * H : p.sgate) : p.router;
+    // loads: row r (8 bf16 at c) of the x tile and of both router tiles
+    const int r = tid / 8, c = (tid % 8) * 8;
+    const bool xok = t0 + r < T, rok = n0 + r < N;
+    const uint16_t *xrow = p.x + (size_t)(xok ? t0 + r : 0) * H;
+    const uint16_t *hrow = p.rhi + (size_t)(rok ? n0 + r : 0) * H, *lrow = p.rlo + (size_t)(rok ? n0 + r : 0) * H;
     struct St {
-        uint4 x;
-        float4 r[4];
+        uint4 x, h, l;
     };
     auto load = [&](int kb) {
+        const uint4 z = make_uint4(0, 0, 0, 0);
         St st;
-        st.x = xok ? *reinterpret_cast<const uint4 *>(xrow + kb * 64 + xc) : make_uint4(0, 0, 0, 0);
-        const float4 *src = reinterpret_cast<const float4 *>(rrow + kb * 64 + rc);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) st.r[q] = rok ? src[q] : make_float4(0, 0, 0, 0);
+        st.x = xok ? *reinterpret_cast<const uint4 *>(xrow + kb * 64 + c) : z;
+        st.h = rok ? *reinterpret_cast<const uint4 *>(hrow + kb * 64 + c) : z;
+        st.l = rok ? *reinterpret_cast<const uint4 *>(lrow + kb * 64 + c) : z;
         return st;
     };
     auto store = [&](const St &st) {
-        *reinterpret_cast<uint4 *>(&xs[xr][xc]) = st.x;
-        uint16_t hi[16], lo[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float f[4] = {st.r[q].x, st.r[q].y, st.r[q].z, st.r[q].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint16_t h = f32_to_bf16_rne(f[e]);
-                hi[4 * q + e] = h;
-                lo[4 * q + e] = f32_to_bf16_rne(f[e] - bf16_to_f32(h));
-            }
-        }
-        uint4 *dh = reinterpret_cast<uint4 *>(&rh[rr][rc]);
-        uint4 *dl = reinterpret_cast<uint4 *>(&rl[rr][rc]);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            dh[q] = make_uint4(hi[8 * q] | (uint32_t)hi[8 * q + 1] << 16, hi[8 * q + 2] | (uint32_t)hi[8 * q + 3] << 16,
-                               hi[8 * q + 4] | (uint32_t)hi[8 * q + 5] << 16, hi[8 * q + 6] | (uint32_t)hi[8 * q + 7] << 16);
-            dl[q] = make_uint4(lo[8 * q] | (uint32_t)lo[8 * q + 1] << 16, lo[8 * q + 2] | (uint32_t)lo[8 * q + 3] << 16,
-                               lo[8 * q + 4] | (uint32_t)lo[8 * q + 5] << 16, lo[8 * q + 6] | (uint32_t)lo[8 * q + 7] << 16);
-        }
+        *reinterpret_cast<uint4 *>(&xs[r][c]) = st.x;
+        *reinterpret_cast<uint4 *>(&rh[r][c]) = st.h;
+        *reinterpret_cast<uint4 *>(&rl[r][c]) = st.l;
     };
-    float4_t acc[2] = {float4_t{0.0f, 0.0f, 0.0f, 0.0f}, float4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     const int th = wave & 1, nh = wave >> 1;
     auto mfma_step = [&]() {
 #pragma unroll
         for (int ks = 0; ks < 64; ks += 32) {
             const int kc = ks + 8 * (lane / 16);
             const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&xs[16 * th + lane % 16][kc]);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&rh[32 * nh + 16 * j + lane % 16][kc]);
-                const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(&rl[32 * nh + 16 * j + lane % 16][kc]);
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[j], 0, 0, 0);
-            }
+            const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&rh[16 * nh + lane % 16][kc]);
+            const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(&rl[16 * nh + lane % 16][kc]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc, 0, 0, 0);
         }
     };
-    const int nk = H / 64;
-    St S0 = load(0), S1 = load(nk > 1 ? 1 : 0);
+    const int nk = H / 64 / router_ksplit(H), k0 = blockIdx.z * nk;  // this range's k-steps
+    St S0 = load(k0), S1 = load(k0 + (nk > 1 ? 1 : 0));
     for (int kb = 0; kb < nk; kb += 2) {
         store(S0);
         __syncthreads();
-        if (kb + 2 < nk) S0 = load(kb + 2);
+        if (kb + 2 < nk) S0 = load(k0 + kb + 2);
         mfma_step();
         __syncthreads();
         if (kb + 1 < nk) {
             store(S1);
             __syncthreads();
-            if (kb + 3 < nk) S1 = load(kb + 3);
+            if (kb + 3 < nk) S1 = load(k0 + kb + 3);
             mfma_step();
             __syncthreads();
         }
     }
-    // lane l, register r -> token t0 + 16 th + 4 (l / 16) + r, row n0 + 32 nh + 16 j + l % 16
+    // lane l, register q -> token t0 + 16 th + 4 (l / 16) + q, row n0 + 16 nh + l % 16
+    const int n = n0 + 16 * nh + lane % 16;
+    float *part = p.lpart + (size_t)blockIdx.z * T * N;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int n = n0 + 32 * nh + 16 * j + lane % 16;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = t0 + 16 * th + 4 * (lane / 16) + r;
-            if (t >= T || n >= N) continue;
-            if (n < E) p.logits[(size_t)t * E + n] = acc[j][r] + (p.rbias ? p.rbias[n] : 0.0f);
-            else p.gate[t] = acc[j][r];
-        }
+    for (int q = 0; q < 4; ++q) {
+        const int t = t0 + 16 * th + 4 * (lane / 16) + q;
+        if (t < T && n < N) part[(size_t)t * N + n] = acc[q];
     }
 }
 
@@ -144,12 +147,27 @@ __global__ void __launch_bounds__(kTopkWaves * kWave) topk_kernel(BatchedParams 
     const int t = blockIdx.x * kTopkWaves + wave;
     float *lt = reinterpret_cast<float *>(smem) + (size_t)wave * E;
     if (t >= p.T) return;  // whole wave leaves together; no workgroup barrier follows
-    for (int e = lane; e < E; e += kWave) lt[e] = p.logits[(size_t)t * E + e];
+    // logits: the router GEMM's range partial sums added in range order, then the bias
+    const int N = E + (p.sgate ? 1 : 0), ks = router_ksplit(p.H);
+    const float *part = p.lpart + (size_t)t * N;
+    const size_t zs = (size_t)p.T * N;
+    for (int e = lane; e < E; e += kWave) {
+        float v = part[e];
+        for (int z = 1; z < ks; ++z) v += part[z * zs + e];
+        if (p.rbias) v += p.rbias[e];
+        lt[e] = v;
+        p.logits[(size_t)t * E + e] = v;
+    }
+    float gate = 0.0f;
+    if (p.sgate) {
+        gate = part[E];
+        for (int z = 1; z < ks; ++z) gate += part[z * zs + E];
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     wave_topk(lt, E, K, p.idx + (size_t)t * K, p.w + (size_t)t * K);
-    if (lane == 0 && p.gamma) p.gamma[t] = p.sgate ? 1.0f / (1.0f + expf(-p.gate[t])) : 0.0f;
+    if (lane == 0 && p.gamma) p.gamma[t] = p.sgate ? 1.0f / (1.0f + expf(-gate)) : 0.0f;
 }
 
 // ---- 3. histogram, exclusive scan, stable scatter, tile list -------------------------------------
@@ -648,7 +666,11 @@ __global__ void __launch_bounds__(256) combine_kernel(BatchedParams p) {
 // ---- launch sequence ---------------------------------------------------------------------------------
 hipError_t launch_router_topk(const BatchedParams &p, hipStream_t stream) {
     const int N = p.E + (p.sgate ? 1 : 0);
-    hipLaunchKernelGGL(router_gemm, dim3((p.T + kRtT - 1) / kRtT, (N + kRtN - 1) / kRtN), dim3(kGemmThreads), 0,
+    const size_t nsplit = ((size_t)N * p.H / 8 + kSplitThreads - 1) / kSplitThreads;
+    hipLaunchKernelGGL(router_split, dim3((unsigned)nsplit), dim3(kSplitThreads), 0, stream, p);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL(router_gemm, dim3((p.T + kRtT - 1) / kRtT, (N + kRtN - 1) / kRtN, router_ksplit(p.H)),
+                       dim3(kGemmThreads), 0,
                        stream, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

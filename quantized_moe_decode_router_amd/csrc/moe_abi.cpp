@@ -308,6 +308,9 @@ moe_status moe_layer_batched(const moe_shape *s, const moe_layer *L, const uint1
     p.hh = reinterpret_cast<_Float16 *>(w + lay.hh);
     p.hl = reinterpret_cast<_Float16 *>(w + lay.hl);
     p.out = reinterpret_cast<float *>(w + lay.out);
+    p.rhi = reinterpret_cast<uint16_t *>(w + lay.rhi);
+    p.rlo = reinterpret_cast<uint16_t *>(w + lay.rlo);
+    p.lpart = reinterpret_cast<float *>(w + lay.lpart);
     p.y = y;
     hipError_t err = moe::launch_batched(p, lay.max_tiles, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;

@@ -172,12 +172,18 @@ struct BatchedParams {
     _Float16 *hh, *hl;  // [R][Imax] SwiGLU output, fp16 hi and lo halves
     float *out;         // [R][H] scaled down-projection rows
     float *y;           // [T][H]
+    uint16_t *rhi, *rlo;  // [E+1][H] bf16 hi / lo halves of the router rows (row E = shared gate)
+    float *lpart;         // [kRouterSplitK][T][E+1] router partial sums over quarters of H
 };
+// The batched router GEMM splits H into this many contiguous ranges (fewer when H has fewer
+// 64-column steps); the top-k kernel adds the partial sums in range order.
+constexpr int kRouterSplitK = 4;
 
 // Workspace layout of the batched path (bytes from the workspace base); R = T*K (+ T with a
 // shared expert) rows.
 struct BatchedWs {
-    size_t logits, gate, idx, w, gamma, blkcnt, rank, gcnt, goff, ntiles, tiles, perm, pos, hh, hl, out, total;
+    size_t logits, gate, idx, w, gamma, blkcnt, rank, gcnt, goff, ntiles, tiles, perm, pos, hh, hl, out, rhi, rlo,
+        lpart, total;
     int max_tiles;
 };
 __host__ inline BatchedWs batched_ws_layout(int T, int H, int E, int K, int I, int Is) {
@@ -203,6 +209,9 @@ __host__ inline BatchedWs batched_ws_layout(int T, int H, int E, int K, int I, i
     w.hh = o;     o = align_up(o + 2 * R * Imax, 256);
     w.hl = o;     o = align_up(o + 2 * R * Imax, 256);
     w.out = o;    o = align_up(o + 4 * R * (size_t)H, 256);
+    w.rhi = o;    o = align_up(o + 2 * ((size_t)E + 1) * H, 256);
+    w.rlo = o;    o = align_up(o + 2 * ((size_t)E + 1) * H, 256);
+    w.lpart = o;  o = align_up(o + 4 * (size_t)kRouterSplitK * T * ((size_t)E + 1), 256);
     w.total = o;
     return w;
 }
