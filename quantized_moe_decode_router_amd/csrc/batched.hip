@@ -517,7 +517,7 @@ struct DnStage {
     uint16_t s, b;
 };
 template <int BITS>
-__global__ void __launch_bounds__(kGemmThreads) dn_gemm(BatchedParams p) {
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(5, 5))) dn_gemm(BatchedParams p) {
     __shared__ __align__(16) _Float16 Ah[kBM][kLdsK];
     __shared__ __align__(16) _Float16 Al[kBM][kLdsK];
     __shared__ __align__(16) _Float16 Bs[64][kLdsK];
