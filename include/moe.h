@@ -214,6 +214,84 @@ moe_status moe_layer_forward(const moe_shape *shape, const moe_layer *layer, con
                              float *topk_w_opt, float *logits_opt, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/*
+ * ---- Expert residency (fixed-stride expert container + bounded HBM slot pool) ----
+ * Swiftlet's memory scheme as the Hacker News post ("How it works"), the xix.ai article
+ * (scheduling and lineage paragraphs) and the Chinese summary describe it: routed experts repacked
+ * into fixed-stride blocks so that fetching one expert is one contiguous read, and a bounded pool
+ * of popular experts with LFU + recency eviction in front of the slow tier. Here the slow tier is
+ * the container itself (host memory the GPU reads directly, or device memory), the pool lives in
+ * HBM, and the decode kernel reads every routed expert through a table of block addresses.
+ */
+
+/* Bytes of one routed expert's block in the container: its gate|up codes, scales, biases, then
+ * its down codes, scales, biases, each piece at a 256-byte aligned offset, the total rounded up
+ * to 4096. 0 for an invalid shape. */
+size_t moe_expert_stride(const moe_shape *shape);
+
+/* Copies the routed experts (w13, w2) of an [L]-stacked layer description into the container:
+ * expert (l, e) is the block at container + (l * E + e) * moe_expert_stride(shape). `container`
+ * (4096-byte aligned, at least n_layers * E * stride bytes) may be device memory or host memory
+ * allocated with hipHostMalloc; the copies are queued on `stream` (the caller synchronises). */
+moe_status moe_pack_experts(const moe_shape *shape, const moe_layer *stack, int32_t n_layers,
+                            void *container, size_t container_bytes, void *stream);
+
+/*
+ * moe_stack_decode with the routed experts read through expert_table instead of stack->w13 and
+ * stack->w2 (which may then be NULL; every other field of `stack` is used as in moe_stack_decode).
+ *   expert_table : uint64 [L][E], device memory, 8-byte aligned: the address of expert (l, e)'s
+ *                  block (layout as moe_expert_stride); each address must stay readable by the
+ *                  device, and its bytes unchanged, until the call completes
+ * Results are bit for bit those of moe_stack_decode on the same weights, wherever the blocks are.
+ */
+moe_status moe_stack_decode_table(const moe_shape *shape, const moe_layer *stack, int32_t n_layers,
+                                  const uint64_t *expert_table, uint32_t flags, const uint16_t *x,
+                                  int32_t T, float *y, uint16_t *x_all_opt, float *y_all_opt,
+                                  int32_t *topk_idx_all_opt, float *topk_w_all_opt,
+                                  float *logits_all_opt, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+/* An expert cache: host-side policy state plus a pinned staging copy of the table. Opaque. */
+typedef struct moe_cache moe_cache;
+
+/*
+ * Creates a cache over a packed container of n_layers * E experts, with `slots` (0 <= slots <=
+ * n_layers * E) pool slots of one stride each at `pool` (device memory, 4096-byte aligned, at
+ * least slots * stride bytes; may be NULL when slots is 0), and writes the initial table (every
+ * expert at its container block) to `table` (device, uint64 [L][E]), synchronously on `stream`.
+ * The caller owns container, pool and table and keeps them alive until moe_cache_destroy.
+ */
+moe_status moe_cache_create(const moe_shape *shape, int32_t n_layers, const void *container,
+                            size_t container_bytes, void *pool, size_t pool_bytes, int32_t slots,
+                            uint64_t *table, size_t table_bytes, void *stream, moe_cache **out);
+
+/*
+ * Feeds one decode call's routing (host int32 [L][T][top_k], every value in [0, E)) through the
+ * policy in order (layer, token, slot), then queues on `stream` the copy of every newly admitted
+ * expert's block into its slot and the rewrite of the table. Synchronises `stream` first (the
+ * routing must come from a call on it that has completed). hits_opt / misses_opt: this call's
+ * counts. Policy: a resident expert has a use count (1 on admission, +1 per hit) and a last-use
+ * time; a miss takes the lowest free slot, else evicts the smallest count, oldest last use first.
+ */
+moe_status moe_cache_update(moe_cache *cache, const int32_t *topk_idx_all, int32_t T, int32_t top_k,
+                            void *stream, int32_t *hits_opt, int32_t *misses_opt);
+
+/* Totals since creation: accesses that hit, that missed, and bytes copied into the pool. */
+moe_status moe_cache_stats(const moe_cache *cache, uint64_t *hits, uint64_t *misses,
+                           uint64_t *bytes_copied);
+
+/* owner[slot] = l * E + e of the expert in each slot (after the copies queued so far), or -1. */
+moe_status moe_cache_owners(const moe_cache *cache, int32_t *owner);
+
+/* Frees the cache's host state (not the caller's container, pool or table). NULL is ignored. */
+void moe_cache_destroy(moe_cache *cache);
+
+/* The cache's policy on its own, host only: n accesses of keys in [0, n_keys) against `slots`
+ * slots; per access hit (0/1), the slot the key then occupies (-1 when slots is 0) and the key it
+ * evicted (-1 if none). */
+moe_status moe_cache_policy_run(int32_t slots, int32_t n_keys, const int32_t *keys, int64_t n,
+                                int32_t *hit, int32_t *slot, int32_t *evicted);
+
 /* Workspace bytes for `kind` (MOE_WS_DECODE, MOE_WS_BATCHED, MOE_WS_STACK or MOE_WS_FORWARD), T
  * tokens and, for MOE_WS_STACK, n_layers layers (ignored otherwise); 0 if the arguments are
  * invalid. */

@@ -16,6 +16,7 @@ import ctypes
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,7 +31,9 @@ MOE_DEFAULT_CROSSOVER = 8
 MOE_STACK_INDEPENDENT = 1
 
 EXPORTED = ("moe_route", "moe_layer_decode", "moe_stack_decode", "moe_layer_batched", "moe_group_pairs",
-            "moe_layer_path", "moe_layer_forward", "moe_workspace_bytes", "moe_read_status", "moe_status_string")
+            "moe_layer_path", "moe_layer_forward", "moe_workspace_bytes", "moe_read_status", "moe_status_string",
+            "moe_expert_stride", "moe_pack_experts", "moe_stack_decode_table", "moe_cache_create",
+            "moe_cache_update", "moe_cache_stats", "moe_cache_owners", "moe_cache_destroy", "moe_cache_policy_run")
 
 
 class MoeError(RuntimeError):
@@ -74,6 +77,18 @@ def lib():
         L.moe_layer_path.restype = I32
         L.moe_layer_forward.argtypes = [PS, PL, P, I32, I32, P, P, P, P, P, SZ, P]
         L.moe_stack_decode.argtypes = [PS, PL, I32, U32, P, I32, P, P, P, P, P, P, P, SZ, P]
+        L.moe_stack_decode_table.argtypes = [PS, PL, I32, P, U32, P, I32, P, P, P, P, P, P, P, SZ, P]
+        L.moe_expert_stride.argtypes = [PS]
+        L.moe_expert_stride.restype = SZ
+        L.moe_pack_experts.argtypes = [PS, PL, I32, P, SZ, P]
+        L.moe_cache_create.argtypes = [PS, I32, P, SZ, P, SZ, I32, P, SZ, P, ctypes.POINTER(P)]
+        L.moe_cache_update.argtypes = [P, P, I32, I32, P, ctypes.POINTER(I32), ctypes.POINTER(I32)]
+        U64P = ctypes.POINTER(ctypes.c_uint64)
+        L.moe_cache_stats.argtypes = [P, U64P, U64P, U64P]
+        L.moe_cache_owners.argtypes = [P, P]
+        L.moe_cache_destroy.argtypes = [P]
+        L.moe_cache_destroy.restype = None
+        L.moe_cache_policy_run.argtypes = [I32, I32, P, ctypes.c_int64, P, P, P]
         L.moe_workspace_bytes.argtypes = [PS, I32, I32, I32]
         L.moe_workspace_bytes.restype = SZ
         L.moe_read_status.argtypes = [P, P, ctypes.POINTER(I32)]
@@ -81,7 +96,8 @@ def lib():
         L.moe_status_string.restype = ctypes.c_char_p
         for name in ("moe_route", "moe_layer_decode", "moe_layer_batched", "moe_stack_decode",
                      "moe_layer_forward", "moe_group_pairs", "moe_read_status"):
-            getattr(L, name).restype = ctypes.c_int
+            if name != "moe_cache_destroy":
+                getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -107,6 +123,21 @@ def _ptr(t: Optional[torch.Tensor], name: str, dtype=None):
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
     return t.data_ptr()
+
+
+def _dptr(t: torch.Tensor, name: str) -> int:
+    """Address the device can read: a GPU tensor, or a pinned (page-locked) host tensor."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name}: must be a GPU tensor or pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t.data_ptr()
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
 
 
 def _stream(stream) -> Optional[int]:
@@ -219,6 +250,93 @@ def moe_group_pairs(shape, topk_idx, T: int, counts, offsets, perm, pos, workspa
                                _ptr(perm, "perm", torch.int32), _ptr(pos, "pos", torch.int32),
                                _ptr(workspace, "workspace"), int(wsb), _stream(stream))
     _check(st, "moe_group_pairs")
+
+
+def moe_expert_stride(shape) -> int:
+    s = shape_struct(shape)
+    return int(lib().moe_expert_stride(ctypes.byref(s)))
+
+
+def moe_pack_experts(shape, stack, n_layers: int, container, stream=None) -> None:
+    s, L = shape_struct(shape), layer_struct(stack)
+    st = lib().moe_pack_experts(ctypes.byref(s), ctypes.byref(L), int(n_layers), _dptr(container, "container"),
+                                _nbytes(container), _stream(stream))
+    _check(st, "moe_pack_experts")
+
+
+def moe_stack_decode_table(shape, stack, n_layers: int, expert_table, x, T: int, y, x_all=None, y_all=None,
+                           topk_idx_all=None, topk_w_all=None, logits_all=None, workspace=None,
+                           workspace_bytes=None, stream=None, flags: int = 0) -> None:
+    s, L = shape_struct(shape), layer_struct(stack)
+    wsb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    st = lib().moe_stack_decode_table(ctypes.byref(s), ctypes.byref(L), int(n_layers),
+                                      _ptr(expert_table, "expert_table", (torch.int64, torch.uint64)), int(flags),
+                                      _ptr(x, "x", _BF16_BITS), int(T), _ptr(y, "y", torch.float32),
+                                      _ptr(x_all, "x_all", _BF16_BITS), _ptr(y_all, "y_all", torch.float32),
+                                      _ptr(topk_idx_all, "topk_idx_all", torch.int32),
+                                      _ptr(topk_w_all, "topk_w_all", torch.float32),
+                                      _ptr(logits_all, "logits_all", torch.float32), _ptr(workspace, "workspace"),
+                                      int(wsb), _stream(stream))
+    _check(st, "moe_stack_decode_table")
+
+
+class MoeCache:
+    """moe_cache_* over caller-owned tensors: a packed container (GPU or pinned host uint8), a GPU
+    pool of `slots` strides and a GPU int64 [L][E] expert table."""
+
+    def __init__(self, shape, n_layers: int, container, pool, slots: int, table, stream=None):
+        s = shape_struct(shape)
+        self._h = ctypes.c_void_p()
+        self._keep = (container, pool, table)
+        self.slots = int(slots)
+        st = lib().moe_cache_create(ctypes.byref(s), int(n_layers), _dptr(container, "container"),
+                                    _nbytes(container), _ptr(pool, "pool") if pool is not None else None,
+                                    _nbytes(pool) if pool is not None else 0, self.slots,
+                                    _ptr(table, "table", (torch.int64, torch.uint64)), _nbytes(table),
+                                    _stream(stream), ctypes.byref(self._h))
+        _check(st, "moe_cache_create")
+
+    def update(self, topk_idx_all, T: int, top_k: int, stream=None):
+        """topk_idx_all: host int32 [L][T][K] (tensor or array). Returns (hits, misses) of the call."""
+        a = np.ascontiguousarray(topk_idx_all.cpu().numpy() if isinstance(topk_idx_all, torch.Tensor)
+                                 else topk_idx_all, dtype=np.int32)
+        h, m = ctypes.c_int32(0), ctypes.c_int32(0)
+        st = lib().moe_cache_update(self._h, a.ctypes.data, int(T), int(top_k), _stream(stream), ctypes.byref(h),
+                                    ctypes.byref(m))
+        _check(st, "moe_cache_update")
+        return int(h.value), int(m.value)
+
+    def stats(self):
+        h, m, b = ctypes.c_uint64(0), ctypes.c_uint64(0), ctypes.c_uint64(0)
+        _check(lib().moe_cache_stats(self._h, ctypes.byref(h), ctypes.byref(m), ctypes.byref(b)), "moe_cache_stats")
+        return int(h.value), int(m.value), int(b.value)
+
+    def owners(self) -> np.ndarray:
+        out = np.full(max(self.slots, 1), -1, dtype=np.int32)
+        _check(lib().moe_cache_owners(self._h, out.ctypes.data), "moe_cache_owners")
+        return out[:self.slots]
+
+    def close(self) -> None:
+        if self._h:
+            lib().moe_cache_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def moe_cache_policy_run(slots: int, n_keys: int, keys):
+    """The cache policy on the host: per access (hit, slot, evicted) as int32 arrays."""
+    k = np.ascontiguousarray(keys, dtype=np.int32)
+    n = k.size
+    hit, slot, ev = (np.zeros(max(n, 1), dtype=np.int32) for _ in range(3))
+    st = lib().moe_cache_policy_run(int(slots), int(n_keys), k.ctypes.data if n else None, int(n),
+                                    hit.ctypes.data, slot.ctypes.data, ev.ctypes.data)
+    _check(st, "moe_cache_policy_run")
+    return hit[:n], slot[:n], ev[:n]
 
 
 def moe_read_status(workspace, stream=None) -> int:

@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libmoe_amd.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
-SOURCES = ["moe_abi.cpp", "decode.hip", "route.hip", "batched.hip"]
+SOURCES = ["moe_abi.cpp", "residency.cpp", "decode.hip", "route.hip", "batched.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

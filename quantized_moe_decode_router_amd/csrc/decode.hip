@@ -222,6 +222,30 @@ __device__ __forceinline__ void dma_qrows(const QMat &q, int cols, int bits, int
     dma_rows<4>(n, dst.sb, [&](int r) { return reinterpret_cast<const char *>(q.b + row_of(r) * gpr); }, dst.b);
 }
 
+// Expert-table form of dma_qrows: row r is row x.row of the matrix piece whose codes start at
+// address x.base (row_of(r) -> XRow); its scales and biases start off_s and off_b bytes further.
+struct XRow {
+    uint64_t base;
+    uint32_t row;
+};
+template <typename RowOf>
+__device__ __forceinline__ void dma_xrows(int cols, int bits, int n, RowOf row_of, uint32_t off_s, uint32_t off_b,
+                                          const Rows &dst, Swz swz) {
+    const uint32_t cb = (uint32_t)cols * bits / 8, sb = (uint32_t)cols / 32;
+    dma_rows<16>(n, dst.cb, [&](int r) {
+        const XRow x = row_of(r);
+        return reinterpret_cast<const char *>(x.base + (uint64_t)x.row * cb);
+    }, dst.c, swz);
+    dma_rows<4>(n, dst.sb, [&](int r) {
+        const XRow x = row_of(r);
+        return reinterpret_cast<const char *>(x.base + off_s + (uint64_t)x.row * sb);
+    }, dst.s);
+    dma_rows<4>(n, dst.sb, [&](int r) {
+        const XRow x = row_of(r);
+        return reinterpret_cast<const char *>(x.base + off_b + (uint64_t)x.row * sb);
+    }, dst.b);
+}
+
 // Column (within a 32-column slice) of the two halves of pair slot q.
 template <int BITS>
 __device__ __forceinline__ int pair_col_a(int q) {
@@ -314,6 +338,7 @@ struct Lds {
     float2 *xsx;     // [T][H/64] (sum of the limb values, group scale)
     int8_t *hq;      // [(K*I + Is)/64][3][64] h of one token (routed vectors, then the shared one)
     float2 *hsx;     // [(K*I + Is)/64]
+    uint64_t *xb;    // [T*K] expert-table mode: block address of each selected (token, slot)
 };
 __device__ __forceinline__ Lds carve(const DecodeParams &p, char *smem) {
     const DecodeLds &o = p.lds;
@@ -335,6 +360,7 @@ __device__ __forceinline__ Lds carve(const DecodeParams &p, char *smem) {
     s.xsx = reinterpret_cast<float2 *>(smem + o.xsx);
     s.hq = reinterpret_cast<int8_t *>(smem + o.hq);
     s.hsx = reinterpret_cast<float2 *>(smem + o.hsx);
+    s.xb = reinterpret_cast<uint64_t *>(smem + o.xb);
     return s;
 }
 
@@ -414,11 +440,21 @@ __device__ __forceinline__ void stage_shared_down(const DecodeParams &p, int l, 
               mfma_swz(p.bits, p.Is));
 }
 // Routed down rows r0..r0+nr-1 of token t's K experts: staged row k * nr + rl.
+template <bool XT>
 __device__ __forceinline__ void stage_routed_down(const DecodeParams &p, int l, const Lds &s, int t, int r0,
                                                   int nr, uint32_t nrm) {
     if (nr <= 0) return;
-    const LayerPtrs L = layer_ptrs(p, l);
     const int K = p.K, E = p.E;
+    if constexpr (XT) {
+        dma_xrows(p.I, p.bits, K * nr,
+                  [&](int r) -> XRow {
+                      const int k = div_by(r, nrm), rl = r - k * nr;
+                      return XRow{s.xb[t * K + k] + p.xo2c, (uint32_t)(r0 + rl)};
+                  },
+                  p.xo2s - p.xo2c, p.xo2b - p.xo2c, rd_rows(p, s), mfma_swz(p.bits, p.I));
+        return;
+    }
+    const LayerPtrs L = layer_ptrs(p, l);
     const size_t H = p.H;
     dma_qrows(L.w2, p.I, p.bits, K * nr,
               [&](int r) -> size_t {
@@ -873,7 +909,7 @@ __device__ void route_tokens(const DecodeParams &p, const Lds &s) {
         s.gam[t] = p.Is ? 1.0f / (1.0f + expf(-s.lg[t * (E + 1) + E])) : 0.0f;
 }
 
-template <int BITS>
+template <int BITS, bool XT>
 __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams p0) {
     extern __shared__ __align__(16) char smem[];
     const int tid = threadIdx.x;
@@ -938,6 +974,11 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
                 for (int i = tid; i < T * E; i += blockDim.x)
                     G(p.logits_all)[base * E + i] = s.lg[(i / E) * (E + 1) + i % E];
         }
+        if constexpr (XT) {
+            // block address of every selected expert (the routing is published by the barrier above)
+            if (tid < T * K) s.xb[tid] = G(p.xtab)[(size_t)l * E + expert_at(s.sidx[tid], E)];
+            lds_barrier();
+        }
         // routed gate|up: this workgroup's pairs [q0, q1) of the flattened (token, slot, j) pairs,
         // staged into LDS chunk by chunk (one chunk at T = 1): LDS row 2i = gate row, 2i+1 = up row
         {
@@ -947,12 +988,21 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
             const Rows rg = rows_at(s.rg, 2 * cp, H, BITS);
             for (int c0 = 0; c0 < np; c0 += cp) {
                 const int nc = min(cp, np - c0), pb = w.q0 + c0;
-                dma_qrows(w13, H, BITS, 2 * nc,
-                          [&](int r) -> size_t {
-                              const int P = pb + (r >> 1), tk = P >> lgI, j = P & (I - 1);
-                              return expert_at(s.sidx[tk], E) * 2 * I + (size_t)(r & 1) * I + j;
-                          },
-                          rg, mfma_swz(BITS, H));
+                if constexpr (XT) {
+                    dma_xrows(H, BITS, 2 * nc,
+                              [&](int r) -> XRow {
+                                  const int P = pb + (r >> 1), tk = P >> lgI, j = P & (I - 1);
+                                  return XRow{s.xb[tk], (uint32_t)((r & 1) * I + j)};
+                              },
+                              p.xo13s, p.xo13b, rg, mfma_swz(BITS, H));
+                } else {
+                    dma_qrows(w13, H, BITS, 2 * nc,
+                              [&](int r) -> size_t {
+                                  const int P = pb + (r >> 1), tk = P >> lgI, j = P & (I - 1);
+                                  return expert_at(s.sidx[tk], E) * 2 * I + (size_t)(r & 1) * I + j;
+                              },
+                              rg, mfma_swz(BITS, H));
+                }
                 dma_wait();
                 lds_barrier();
                 gate_up_mfma<BITS, false>(
@@ -970,7 +1020,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         // Token 0's routed down rows, then layer l+1's shared gate|up rows (the shared gate|up of this
         // layer is done), stream in during the h exchange; the down projection waits for the routed
         // down rows only.
-        stage_routed_down(p, l, s, 0, r0, nr, w.nrm);
+        stage_routed_down<XT>(p, l, s, 0, r0, nr, w.nrm);
         int later = 0;  // DMA instructions this wave issued after the routed down rows
         if (has_next) {
             stage_shared_gu(p, l + 1, s, w);
@@ -986,7 +1036,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
                 down_all_mfma<BITS>(s, rd_rows(p, s), sd_rows(p, s), K, I, Is, nr, w.nrm, pt, RB);
             }
             lds_barrier();
-            if (t + 1 < T) stage_routed_down(p, l, s, t + 1, r0, nr, w.nrm);
+            if (t + 1 < T) stage_routed_down<XT>(p, l, s, t + 1, r0, nr, w.nrm);
         }
         for (int i = tid; i < T * nr; i += blockDim.x) {
             const int t = div_by(i, w.nrm), rl = i - t * nr;
@@ -1012,9 +1062,9 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
     }
 }
 
-template <int BITS>
+template <int BITS, bool XT>
 static hipError_t launch_bits(const DecodeParams &p, int grid, hipStream_t stream) {
-    const void *fn = reinterpret_cast<const void *>(&decode_kernel<BITS>);
+    const void *fn = reinterpret_cast<const void *>(&decode_kernel<BITS, XT>);
     hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds.total);
     if (err != hipSuccess) return err;
     DecodeParams arg = p;
@@ -1023,7 +1073,8 @@ static hipError_t launch_bits(const DecodeParams &p, int grid, hipStream_t strea
 }
 
 hipError_t launch_decode(const DecodeParams &p, int grid, hipStream_t stream) {
-    return p.bits == 4 ? launch_bits<4>(p, grid, stream) : launch_bits<8>(p, grid, stream);
+    if (p.xtab) return p.bits == 4 ? launch_bits<4, true>(p, grid, stream) : launch_bits<8, true>(p, grid, stream);
+    return p.bits == 4 ? launch_bits<4, false>(p, grid, stream) : launch_bits<8, false>(p, grid, stream);
 }
 
 }  // namespace moe

@@ -47,12 +47,13 @@ moe_status check_qweight(const moe_qweight &q) {
     return MOE_OK;
 }
 
-moe_status check_layer(const moe_shape *s, const moe_layer *L) {
+// routed = false: the routed experts come from an expert table, so w13 and w2 are not read.
+moe_status check_layer(const moe_shape *s, const moe_layer *L, bool routed = true) {
     if (!L || !L->router || !al16(L->router)) return MOE_ERR_INVALID_ARG;
     if (L->router_bias && !al4(L->router_bias)) return MOE_ERR_INVALID_ARG;
     moe_status st;
-    if ((st = check_qweight(L->w13)) != MOE_OK) return st;
-    if ((st = check_qweight(L->w2)) != MOE_OK) return st;
+    if (routed && (st = check_qweight(L->w13)) != MOE_OK) return st;
+    if (routed && (st = check_qweight(L->w2)) != MOE_OK) return st;
     if (s->shared_inter) {
         if (!L->shared_gate || !al16(L->shared_gate)) return MOE_ERR_INVALID_ARG;
         if ((st = check_qweight(L->s13)) != MOE_OK) return st;
@@ -103,10 +104,11 @@ moe_status decode_supported(const moe_shape *s, int T, int grid) {
 moe_status decode_common(const moe_shape *s, const moe_layer *L, int32_t n_layers, uint32_t flags,
                          const uint16_t *x, int32_t T, float *y, uint16_t *x_all, float *y_all,
                          int32_t *idx_all, float *w_all, float *logits_all, void *ws, size_t ws_bytes,
-                         void *stream) {
+                         void *stream, const uint64_t *xtab = nullptr) {
     moe_status st = check_shape(s);
     if (st != MOE_OK) return st;
-    if ((st = check_layer(s, L)) != MOE_OK) return st;
+    if ((st = check_layer(s, L, xtab == nullptr)) != MOE_OK) return st;
+    if (xtab && (reinterpret_cast<uintptr_t>(xtab) & 7u)) return MOE_ERR_INVALID_ARG;
     if (flags & ~MOE_STACK_INDEPENDENT) return MOE_ERR_INVALID_ARG;
     if (n_layers < 1 || n_layers > kMaxLayers || T < 1 || T > kMaxDecodeT) return MOE_ERR_INVALID_ARG;
     if (!x || !y || !al16(x) || !al16(y)) return MOE_ERR_INVALID_ARG;
@@ -139,8 +141,15 @@ moe_status decode_common(const moe_shape *s, const moe_layer *L, int32_t n_layer
     p.spin_limit = 1u << 20;
     p.eps = 1e-6f;
     p.router = L->router; p.rbias = L->router_bias; p.sgate = Is ? L->shared_gate : nullptr;
-    p.w13 = {L->w13.codes, L->w13.scales, L->w13.biases};
-    p.w2 = {L->w2.codes, L->w2.scales, L->w2.biases};
+    if (xtab) {
+        const moe::ExpertBlock xb = moe::expert_block(s->hidden, s->inter, s->bits);
+        p.xtab = xtab;
+        p.xo13s = (uint32_t)xb.o13s; p.xo13b = (uint32_t)xb.o13b;
+        p.xo2c = (uint32_t)xb.o2c; p.xo2s = (uint32_t)xb.o2s; p.xo2b = (uint32_t)xb.o2b;
+    } else {
+        p.w13 = {L->w13.codes, L->w13.scales, L->w13.biases};
+        p.w2 = {L->w2.codes, L->w2.scales, L->w2.biases};
+    }
     if (Is) {
         p.s13 = {L->s13.codes, L->s13.scales, L->s13.biases};
         p.s2 = {L->s2.codes, L->s2.scales, L->s2.biases};
@@ -261,6 +270,49 @@ moe_status moe_stack_decode(const moe_shape *s, const moe_layer *stack, int32_t 
                             float *logits_all_opt, void *ws, size_t ws_bytes, void *stream) {
     return decode_common(s, stack, n_layers, flags, x, T, y, x_all_opt, y_all_opt, idx_all_opt, w_all_opt,
                          logits_all_opt, ws, ws_bytes, stream);
+}
+
+moe_status moe_stack_decode_table(const moe_shape *s, const moe_layer *stack, int32_t n_layers,
+                                  const uint64_t *expert_table, uint32_t flags, const uint16_t *x, int32_t T,
+                                  float *y, uint16_t *x_all_opt, float *y_all_opt, int32_t *idx_all_opt,
+                                  float *w_all_opt, float *logits_all_opt, void *ws, size_t ws_bytes,
+                                  void *stream) {
+    if (!expert_table) return MOE_ERR_INVALID_ARG;
+    return decode_common(s, stack, n_layers, flags, x, T, y, x_all_opt, y_all_opt, idx_all_opt, w_all_opt,
+                         logits_all_opt, ws, ws_bytes, stream, expert_table);
+}
+
+size_t moe_expert_stride(const moe_shape *s) {
+    if (check_shape(s) != MOE_OK) return 0;
+    return moe::expert_block(s->hidden, s->inter, s->bits).stride;
+}
+
+moe_status moe_pack_experts(const moe_shape *s, const moe_layer *stack, int32_t n_layers, void *container,
+                            size_t container_bytes, void *stream) {
+    moe_status st = check_shape(s);
+    if (st != MOE_OK) return st;
+    if (!stack || check_qweight(stack->w13) != MOE_OK || check_qweight(stack->w2) != MOE_OK)
+        return MOE_ERR_INVALID_ARG;
+    if (n_layers < 1 || n_layers > kMaxLayers || !container || (reinterpret_cast<uintptr_t>(container) & 4095u))
+        return MOE_ERR_INVALID_ARG;
+    const moe::ExpertBlock xb = moe::expert_block(s->hidden, s->inter, s->bits);
+    const size_t n = (size_t)n_layers * s->num_experts;
+    if (container_bytes < n * xb.stride) return MOE_ERR_INVALID_ARG;
+    char *dst = static_cast<char *>(container);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    // six strided copies: piece p of every expert, source rows of piece-size bytes, destination
+    // rows one block apart
+    const struct {
+        const void *src;
+        size_t off, bytes;
+    } piece[6] = {{stack->w13.codes, 0, xb.c13},   {stack->w13.scales, xb.o13s, xb.s13},
+                  {stack->w13.biases, xb.o13b, xb.s13}, {stack->w2.codes, xb.o2c, xb.c2},
+                  {stack->w2.scales, xb.o2s, xb.s2},     {stack->w2.biases, xb.o2b, xb.s2}};
+    for (const auto &pc : piece)
+        if (hipMemcpy2DAsync(dst + pc.off, xb.stride, pc.src, pc.bytes, pc.bytes, n, hipMemcpyDefault, hs) !=
+            hipSuccess)
+            return MOE_ERR_HIP;
+    return MOE_OK;
 }
 
 moe_status moe_layer_batched(const moe_shape *s, const moe_layer *L, const uint16_t *x, int32_t T,

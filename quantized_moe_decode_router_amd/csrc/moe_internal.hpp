@@ -15,7 +15,7 @@ struct QMat {
 
 // LDS plan of the decode kernel: byte offsets of every region (computed once on the host).
 struct DecodeLds {
-    int xp, lg, sidx, sw, gam, rt, sg, sd, rd, rg, hp, part, red, xq, xsx, hq, hsx;
+    int xp, lg, sidx, sw, gam, rt, sg, sd, rd, rg, hp, part, red, xq, xsx, hq, hsx, xb;
     int total;
 };
 
@@ -42,6 +42,11 @@ struct DecodeParams {
     int *idx_all;          // [L][T][K] or null
     float *w_all;          // [L][T][K] or null
     float *logits_all;     // [L][T][E] or null
+    // expert-table mode: routed expert (l, e) is the fixed-stride block at xtab[l * E + e] (device
+    // or device-visible host memory), pieces at these byte offsets (gate|up codes at 0); w13 and w2
+    // are then unused
+    const uint64_t *xtab;
+    uint32_t xo13s, xo13b, xo2c, xo2s, xo2b;
     // workspace (zero-filled before first use)
     int *ctrl;               // [0] status, [1] call sequence number
     uint64_t *ll_start;      // [grid]               one word per workgroup: "this call has started"
@@ -49,6 +54,29 @@ struct DecodeParams {
     uint64_t *ll_h;          // [L][T][K*I + Is]     routed h of slots 0..K-1, then the shared expert's h
     uint64_t *ll_y;          // [L][T][H]
 };
+
+// Fixed-stride expert container: routed expert (l, e) is one block of `stride` bytes holding its
+// gate|up codes, scales, biases, then its down codes, scales, biases, each piece at a 256-byte
+// aligned offset (the block size rounded up to 4 KiB).
+struct ExpertBlock {
+    size_t o13s, o13b, o2c, o2s, o2b, stride;
+    size_t c13, s13, c2, s2;  // piece sizes in bytes (scales and biases alike)
+};
+__host__ inline ExpertBlock expert_block(int H, int I, int bits) {
+    ExpertBlock x;
+    x.c13 = (size_t)2 * I * H * bits / 8;
+    x.s13 = (size_t)2 * I * (H / 64) * 2;
+    x.c2 = (size_t)H * I * bits / 8;
+    x.s2 = (size_t)H * (I / 64) * 2;
+    auto a = [](size_t v) { return (v + 255) / 256 * 256; };
+    x.o13s = a(x.c13);
+    x.o13b = x.o13s + a(x.s13);
+    x.o2c = x.o13b + a(x.s13);
+    x.o2s = x.o2c + a(x.c2);
+    x.o2b = x.o2s + a(x.s2);
+    x.stride = (x.o2b + x.s2 + 4095) / 4096 * 4096;
+    return x;
+}
 
 constexpr int kDecodeThreads = 512;
 constexpr size_t kCtrlBytes = 256;
@@ -96,7 +124,7 @@ __host__ inline DecodeLds decode_lds_plan(int T, int H, int E, int K, int I, int
     if (3 * nh > xp) xp = 3 * nh;
     size_t gsx = 8 * (size_t)T * (H / 64);
     if (8 * (nh / 64) > gsx) gsx = 8 * (nh / 64);
-    const size_t sz[14] = {
+    const size_t sz[15] = {
         xp,                              // xp (also xq and hq)
         4 * (size_t)T * (E + 1),         // lg
         4 * (size_t)T * K,               // sidx
@@ -110,11 +138,12 @@ __host__ inline DecodeLds decode_lds_plan(int T, int H, int E, int K, int I, int
         hp,                              // hp
         4 * (size_t)T * (K + 1) * RB,    // part
         4 * 64,                          // red
-        gsx};                            // xsx (also hsx)
-    int *o[14] = {&d.xp, &d.lg, &d.sidx, &d.sw, &d.gam, &d.rt, &d.sg, &d.sd, &d.rd, &d.rg, &d.hp, &d.part, &d.red,
-                  &d.xsx};
+        gsx,                             // xsx (also hsx)
+        8 * (size_t)T * K};              // xb (expert blocks of the selection, expert-table mode)
+    int *o[15] = {&d.xp, &d.lg, &d.sidx, &d.sw, &d.gam, &d.rt, &d.sg, &d.sd, &d.rd, &d.rg, &d.hp, &d.part, &d.red,
+                  &d.xsx, &d.xb};
     size_t off = 0;
-    for (int i = 0; i < 14; ++i) {
+    for (int i = 0; i < 15; ++i) {
         *o[i] = (int)off;
         off = align_up(off + sz[i], 16);
     }

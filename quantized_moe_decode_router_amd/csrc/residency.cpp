@@ -1,0 +1,217 @@
+// Expert residency: a bounded pool of expert slots in HBM in front of a fixed-stride expert
+// container, with least-frequently-used eviction and ties broken by least recent use.
+//
+// Swiftlet (the Hacker News / xix.ai / Chinese write-ups, "How it works" and the scheduling
+// paragraph) keeps the dense weights resident, packs the routed experts into fixed-stride blocks
+// so that one read is one fetch, and holds the popular ones in a bounded pool with LFU + recency
+// eviction (hit rates of 43-70 % on its machine). Here the container sits in host memory the GPU
+// can read (or anywhere in device memory), the pool in HBM, and the decode kernel follows a
+// per-(layer, expert) table of block addresses: a resident expert is read from its pool slot, any
+// other straight from the container. After each decode call the host feeds that call's routing
+// through the policy in order (layer, token, slot), then copies the blocks of newly admitted
+// experts into their slots and rewrites the table, all on the caller's stream behind the call.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <set>
+#include <tuple>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "moe_internal.hpp"
+
+namespace {
+
+// The eviction policy over keys 0..n_keys-1 and `slots` slots. A resident key has a use count
+// (1 at admission, +1 per hit) and the tick of its last use; the victim is the resident key with
+// the smallest count, then the oldest last use. Free slots are taken lowest index first.
+class LfuRecency {
+  public:
+    LfuRecency(int slots, int n_keys) : owner_(slots, -1), count_(slots, 0), last_(slots, 0), slot_of_(n_keys, -1) {}
+
+    struct Outcome {
+        bool hit;
+        int slot;     // slot the key occupies after the access, or -1 (no slots at all)
+        int evicted;  // key evicted by this access, or -1
+    };
+
+    Outcome access(int key) {
+        ++tick_;
+        int sl = slot_of_[key];
+        if (sl >= 0) {
+            order_.erase(std::make_tuple(count_[sl], last_[sl], sl));
+            ++count_[sl];
+            last_[sl] = tick_;
+            order_.insert(std::make_tuple(count_[sl], last_[sl], sl));
+            return {true, sl, -1};
+        }
+        const int slots = (int)owner_.size();
+        if (slots == 0) return {false, -1, -1};
+        int evicted = -1;
+        if (next_free_ < slots) {
+            sl = next_free_++;
+        } else {
+            const auto victim = *order_.begin();
+            order_.erase(order_.begin());
+            sl = std::get<2>(victim);
+            evicted = owner_[sl];
+            slot_of_[evicted] = -1;
+        }
+        owner_[sl] = key;
+        count_[sl] = 1;
+        last_[sl] = tick_;
+        slot_of_[key] = sl;
+        order_.insert(std::make_tuple(count_[sl], last_[sl], sl));
+        return {false, sl, evicted};
+    }
+    const std::vector<int> &owners() const { return owner_; }
+
+  private:
+    std::vector<int> owner_;
+    std::vector<int64_t> count_;
+    std::vector<uint64_t> last_;
+    std::vector<int> slot_of_;
+    std::set<std::tuple<int64_t, uint64_t, int>> order_;  // resident slots by (count, last use)
+    uint64_t tick_ = 0;
+    int next_free_ = 0;
+};
+
+}  // namespace
+
+struct moe_cache {
+    int L, E, slots;
+    size_t stride;
+    const char *container;
+    char *pool;
+    uint64_t *table_dev;
+    uint64_t *table_host;  // pinned staging of the whole table
+    LfuRecency policy;
+    uint64_t hits = 0, misses = 0, bytes_copied = 0;
+    moe_cache(int L_, int E_, int slots_) : L(L_), E(E_), slots(slots_), policy(slots_, L_ * E_) {}
+};
+
+extern "C" {
+
+moe_status moe_cache_create(const moe_shape *s, int32_t n_layers, const void *container, size_t container_bytes,
+                            void *pool, size_t pool_bytes, int32_t slots, uint64_t *table, size_t table_bytes,
+                            void *stream, moe_cache **out) {
+    if (!out) return MOE_ERR_INVALID_ARG;
+    *out = nullptr;
+    const size_t stride = moe_expert_stride(s);
+    if (stride == 0 || n_layers < 1 || n_layers > 4096 || slots < 0) return MOE_ERR_INVALID_ARG;
+    const size_t keys = (size_t)n_layers * s->num_experts;
+    if (keys > (size_t)INT32_MAX || (size_t)slots > keys) return MOE_ERR_INVALID_ARG;
+    if (!container || (reinterpret_cast<uintptr_t>(container) & 4095u) || container_bytes < keys * stride)
+        return MOE_ERR_INVALID_ARG;
+    if (slots > 0 && (!pool || (reinterpret_cast<uintptr_t>(pool) & 4095u) || pool_bytes < (size_t)slots * stride))
+        return MOE_ERR_INVALID_ARG;
+    if (!table || (reinterpret_cast<uintptr_t>(table) & 7u) || table_bytes < keys * 8) return MOE_ERR_INVALID_ARG;
+    // the kernel reads the container at the addresses the table holds: it must be device memory,
+    // or pinned host memory mapped at the same address (pageable memory would fault the device)
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, container) != hipSuccess) {
+        (void)hipGetLastError();
+        return MOE_ERR_INVALID_ARG;
+    }
+    if (attr.devicePointer != container) return MOE_ERR_INVALID_ARG;
+    moe_cache *c = new moe_cache(n_layers, s->num_experts, slots);
+    c->stride = stride;
+    c->container = static_cast<const char *>(container);
+    c->pool = static_cast<char *>(pool);
+    c->table_dev = table;
+    if (hipHostMalloc(reinterpret_cast<void **>(&c->table_host), keys * 8, hipHostMallocDefault) != hipSuccess) {
+        delete c;
+        return MOE_ERR_HIP;
+    }
+    for (size_t k = 0; k < keys; ++k) c->table_host[k] = reinterpret_cast<uint64_t>(c->container + k * stride);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(table, c->table_host, keys * 8, hipMemcpyHostToDevice, hs) != hipSuccess ||
+        hipStreamSynchronize(hs) != hipSuccess) {
+        hipHostFree(c->table_host);
+        delete c;
+        return MOE_ERR_HIP;
+    }
+    *out = c;
+    return MOE_OK;
+}
+
+moe_status moe_cache_update(moe_cache *c, const int32_t *topk_idx_all, int32_t T, int32_t top_k, void *stream,
+                            int32_t *hits_opt, int32_t *misses_opt) {
+    if (!c || !topk_idx_all || T < 1 || top_k < 1) return MOE_ERR_INVALID_ARG;
+    const size_t n = (size_t)c->L * T * top_k;
+    for (size_t i = 0; i < n; ++i)
+        if (topk_idx_all[i] < 0 || topk_idx_all[i] >= c->E) return MOE_ERR_INVALID_ARG;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    // the staging table and the pool slots may still be read by work queued earlier
+    if (hipStreamSynchronize(hs) != hipSuccess) return MOE_ERR_HIP;
+    const std::vector<int> before = c->policy.owners();
+    int32_t hits = 0, misses = 0;
+    for (size_t i = 0; i < n; ++i) {
+        const int l = (int)(i / ((size_t)T * top_k));
+        const LfuRecency::Outcome o = c->policy.access(l * c->E + topk_idx_all[i]);
+        if (o.hit) ++hits;
+        else ++misses;
+    }
+    c->hits += hits;
+    c->misses += misses;
+    const std::vector<int> &after = c->policy.owners();
+    for (int sl = 0; sl < c->slots; ++sl) {
+        if (after[sl] == before[sl]) continue;
+        if (before[sl] >= 0)
+            c->table_host[before[sl]] = reinterpret_cast<uint64_t>(c->container + (size_t)before[sl] * c->stride);
+        char *dst = c->pool + (size_t)sl * c->stride;
+        if (hipMemcpyAsync(dst, c->container + (size_t)after[sl] * c->stride, c->stride, hipMemcpyDefault, hs) !=
+            hipSuccess)
+            return MOE_ERR_HIP;
+        c->bytes_copied += c->stride;
+    }
+    // a key evicted from one slot may have been admitted into another within the same call
+    for (int sl = 0; sl < c->slots; ++sl)
+        if (after[sl] >= 0) c->table_host[after[sl]] = reinterpret_cast<uint64_t>(c->pool + (size_t)sl * c->stride);
+    if (hipMemcpyAsync(c->table_dev, c->table_host, (size_t)c->L * c->E * 8, hipMemcpyHostToDevice, hs) !=
+        hipSuccess)
+        return MOE_ERR_HIP;
+    if (hits_opt) *hits_opt = hits;
+    if (misses_opt) *misses_opt = misses;
+    return MOE_OK;
+}
+
+moe_status moe_cache_stats(const moe_cache *c, uint64_t *hits, uint64_t *misses, uint64_t *bytes_copied) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (hits) *hits = c->hits;
+    if (misses) *misses = c->misses;
+    if (bytes_copied) *bytes_copied = c->bytes_copied;
+    return MOE_OK;
+}
+
+moe_status moe_cache_owners(const moe_cache *c, int32_t *owner) {
+    if (!c || (!owner && c->slots > 0)) return MOE_ERR_INVALID_ARG;
+    const std::vector<int> &o = c->policy.owners();
+    for (int sl = 0; sl < c->slots; ++sl) owner[sl] = o[sl];
+    return MOE_OK;
+}
+
+void moe_cache_destroy(moe_cache *c) {
+    if (!c) return;
+    hipHostFree(c->table_host);
+    delete c;
+}
+
+moe_status moe_cache_policy_run(int32_t slots, int32_t n_keys, const int32_t *keys, int64_t n, int32_t *hit,
+                                int32_t *slot, int32_t *evicted) {
+    if (slots < 0 || n_keys < 1 || n < 0 || (n > 0 && (!keys || !hit || !slot || !evicted)))
+        return MOE_ERR_INVALID_ARG;
+    for (int64_t i = 0; i < n; ++i)
+        if (keys[i] < 0 || keys[i] >= n_keys) return MOE_ERR_INVALID_ARG;
+    LfuRecency pol(slots, n_keys);
+    for (int64_t i = 0; i < n; ++i) {
+        const LfuRecency::Outcome o = pol.access(keys[i]);
+        hit[i] = o.hit ? 1 : 0;
+        slot[i] = o.slot;
+        evicted[i] = o.evicted;
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"

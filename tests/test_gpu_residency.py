@@ -1,0 +1,204 @@
+"""GPU parity of the expert-residency tier through the C ABI: the packed container against the
+oracle's blocks, decode through an expert table (device container, pinned host container, a
+mixed table) against the plain stack decode bit for bit and against the fp64 oracle, and a
+multi-step decode loop whose cache decisions match the oracle's policy access by access while
+every step's output stays identical to the all-resident decode."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import residency as R
+from tests.gpu_common import bf16_bits, check_routing_against_oracle, check_y, host_layer, need_gpu, oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def _moe():
+    import quantized_moe_decode_router_amd as moe
+    return moe
+
+
+def _container(moe, shape, st, n_layers, where):
+    stride = moe.moe_expert_stride(shape)
+    n = n_layers * shape.num_experts * stride
+    if where == "host":
+        buf = torch.empty(n + 4096, dtype=torch.uint8, pin_memory=True)
+    else:
+        buf = torch.empty(n + 4096, dtype=torch.uint8, device="cuda")
+    off = (-buf.data_ptr()) % 4096
+    c = buf[off:off + n]
+    moe.moe_pack_experts(shape, st, n_layers, c)
+    torch.cuda.synchronize()
+    return buf, c, stride
+
+
+def _no_routed(st):
+    """The stack without its routed expert arrays: the table decode must not need them."""
+    return dataclasses.replace(st, w13_codes=None, w13_scales=None, w13_biases=None, w2_codes=None,
+                               w2_scales=None, w2_biases=None)
+
+
+def _outs(shape, n_layers, T, dev):
+    H, K, E = shape.hidden, shape.top_k, shape.num_experts
+    return dict(y=torch.empty(T, H, dtype=torch.float32, device=dev),
+                x_all=torch.empty(n_layers, T, H, dtype=torch.bfloat16, device=dev),
+                y_all=torch.empty(n_layers, T, H, dtype=torch.float32, device=dev),
+                idx_all=torch.empty(n_layers, T, K, dtype=torch.int32, device=dev),
+                w_all=torch.empty(n_layers, T, K, dtype=torch.float32, device=dev),
+                logits_all=torch.empty(n_layers, T, E, dtype=torch.float32, device=dev))
+
+
+def _run(moe, shape, st, n_layers, x, T, dev, table=None, flags=0, ws=None):
+    o = _outs(shape, n_layers, T, dev)
+    if ws is None:
+        ws = moe.workspace(shape, T, moe.MOE_WS_STACK, dev, n_layers=n_layers)
+    args = (x, T, o["y"], o["x_all"], o["y_all"], o["idx_all"], o["w_all"], o["logits_all"])
+    if table is None:
+        moe.moe_stack_decode(shape, st, n_layers, *args, workspace=ws, flags=flags)
+    else:
+        moe.moe_stack_decode_table(shape, _no_routed(st), n_layers, table, *args, workspace=ws, flags=flags)
+    assert moe.moe_read_status(ws) == 0
+    return {k: v.cpu() for k, v in o.items()}
+
+
+def _same(a, b):
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("where", ["device", "host"])
+def test_pack_experts_matches_oracle_blocks(where):
+    dev = need_gpu()
+    moe = _moe()
+    shape = synth.TINY.shape
+    Lyr = 3
+    st = synth.make_stack(shape, Lyr, 41, dev)
+    _, c, stride = _container(moe, shape, st, Lyr, where)
+    assert stride == R.expert_block_layout(shape.hidden, shape.inter, shape.bits)["stride"]
+    got = c.cpu().numpy().reshape(Lyr * shape.num_experts, stride)
+    h = {k: (v.view(torch.int16) if v.dtype == torch.bfloat16 else v).cpu().numpy() for k, v in st.tensors().items()}
+    for l in range(Lyr):
+        for e in range(shape.num_experts):
+            want = R.pack_block(h["w13_codes"][l, e], h["w13_scales"][l, e].view(np.uint16),
+                                h["w13_biases"][l, e].view(np.uint16), h["w2_codes"][l, e],
+                                h["w2_scales"][l, e].view(np.uint16), h["w2_biases"][l, e].view(np.uint16),
+                                shape.hidden, shape.inter, shape.bits)
+            assert np.array_equal(got[l * shape.num_experts + e], want), (l, e)
+
+
+TABLE_CASES = [
+    ("tiny_T4_device", synth.TINY.shape, 3, 4, "device"),
+    ("tiny_T1_host", synth.TINY.shape, 3, 1, "host"),
+    ("tiny_T8_mixed", synth.TINY.shape, 2, 8, "mixed"),
+    ("q35b_T1_mixed", synth.QWEN35B_4BIT.shape, 3, 1, "mixed"),
+    ("q35b_T3_host", synth.QWEN35B_4BIT.shape, 2, 3, "host"),
+    ("q35b_8bit_T2_mixed", synth.QWEN35B_8BIT.shape, 2, 2, "mixed"),
+]
+
+
+@pytest.mark.parametrize("name,shape,n_layers,T,where", TABLE_CASES, ids=[c[0] for c in TABLE_CASES])
+def test_table_decode_equals_stack_decode(name, shape, n_layers, T, where):
+    """Routed experts read through the table, wherever their blocks are, give the plain stack
+    decode's results bit for bit (y, every layer's x, y, routing and logits)."""
+    dev = need_gpu()
+    moe = _moe()
+    st = synth.make_stack(shape, n_layers, 77 + T, dev, zipf_s=1.1)
+    x = synth.make_x(shape, T, 5, device=dev)
+    want = _run(moe, shape, st, n_layers, x, T, dev)
+    keep = []
+    if where == "mixed":
+        _, cd, stride = _container(moe, shape, st, n_layers, "device")
+        _, ch, _ = _container(moe, shape, st, n_layers, "host")
+        keep += [cd, ch]
+        n = n_layers * shape.num_experts
+        base = torch.where(torch.arange(n) % 2 == 0, torch.tensor(cd.data_ptr()), torch.tensor(ch.data_ptr()))
+        table = (base + torch.arange(n, dtype=torch.int64) * stride).to(dev)
+    else:
+        _, c, stride = _container(moe, shape, st, n_layers, where)
+        keep.append(c)
+        n = n_layers * shape.num_experts
+        table = (c.data_ptr() + torch.arange(n, dtype=torch.int64) * stride).to(dev)
+    got = _run(moe, shape, st, n_layers, x, T, dev, table=table)
+    _same(want, got)
+    print(f"{name}: identical to the stack decode over {n_layers} layers x {T} tokens")
+
+
+def test_table_decode_against_oracle():
+    """Every layer of an unchained table decode (host container) against the fp64 oracle."""
+    dev = need_gpu()
+    moe = _moe()
+    shape = synth.TINY.shape
+    Lyr, T = 3, 4
+    st = synth.make_stack(shape, Lyr, 303, dev)
+    x = synth.make_x(shape, T, 8, device=dev)
+    _, c, stride = _container(moe, shape, st, Lyr, "host")
+    table = (c.data_ptr() + torch.arange(Lyr * shape.num_experts, dtype=torch.int64) * stride).to(dev)
+    got = _run(moe, shape, st, Lyr, x, T, dev, table=table, flags=moe.MOE_STACK_INDEPENDENT)
+    for l in range(Lyr):
+        ref = oracle_layer(st, l, bf16_bits(x))
+        idx, w, lg = got["idx_all"][l].numpy(), got["w_all"][l].numpy(), got["logits_all"][l].numpy()
+        differ = check_routing_against_oracle(idx, w, lg, ref, bf16_bits(x), host_layer(st, l), shape.top_k)
+        keep = [t for t in range(T) if t not in differ]
+        assert keep
+        check_y(got["y_all"][l].numpy()[keep], ref["y"][keep])
+
+
+@pytest.mark.parametrize("slots_frac,T", [(0.0, 1), (0.25, 1), (0.5, 2), (1.0, 1)])
+def test_cached_decode_loop(slots_frac, T):
+    """Several decode steps through a cache over a pinned host container: each step's output is
+    the all-resident decode's bit for bit, the hits and misses are the oracle policy's on the
+    same routing, and every pool slot holds its owner's block."""
+    dev = need_gpu()
+    moe = _moe()
+    shape = synth.TINY.shape
+    Lyr, steps = 4, 6
+    E, K = shape.num_experts, shape.top_k
+    st = synth.make_stack(shape, Lyr, 909, dev, zipf_s=1.1)
+    _, c, stride = _container(moe, shape, st, Lyr, "host")
+    slots = int(round(slots_frac * Lyr * E))
+    pool = torch.empty(max(slots, 1) * stride + 4096, dtype=torch.uint8, device=dev)
+    off = (-pool.data_ptr()) % 4096
+    pool_v = pool[off:off + max(slots, 1) * stride]
+    table = torch.empty(Lyr * E, dtype=torch.int64, device=dev)
+    cache = moe.MoeCache(shape, Lyr, c, pool_v if slots else None, slots, table)
+    ws_t = moe.workspace(shape, T, moe.MOE_WS_STACK, dev, n_layers=Lyr)
+    keys_all = []
+    try:
+        for step in range(steps):
+            x = synth.make_x(shape, T, 31, step=step, device=dev)
+            want = _run(moe, shape, st, Lyr, x, T, dev)
+            got = _run(moe, shape, st, Lyr, x, T, dev, table=table, ws=ws_t)
+            _same(want, got)
+            idx = got["idx_all"].numpy()
+            keys = R.routing_keys(idx, E)
+            h_o, _, _ = R.lfu_recency(slots, np.concatenate(keys_all + [keys]))
+            keys_all.append(keys)
+            hits, misses = cache.update(idx, T, K)
+            assert hits == sum(h_o[-len(keys):]) and hits + misses == len(keys), step
+        torch.cuda.synchronize()
+        h_o, slot_o, _ = R.lfu_recency(slots, np.concatenate(keys_all))
+        owners = cache.owners()
+        want_owner = [-1] * slots
+        for k, s in zip(np.concatenate(keys_all).tolist(), slot_o):
+            if s >= 0:
+                want_owner[s] = k
+        assert owners.tolist() == want_owner
+        th = table.cpu().numpy().astype(np.uint64)
+        pool_np = pool_v.cpu().numpy().reshape(-1, stride) if slots else None
+        cont = c.numpy().reshape(-1, stride)
+        for s, k in enumerate(owners.tolist()):
+            if k >= 0:
+                assert np.array_equal(pool_np[s], cont[k]), (s, k)
+                assert int(th[k]) == pool_v.data_ptr() + s * stride
+        resident = set(k for k in owners.tolist() if k >= 0)
+        for k in range(Lyr * E):
+            if k not in resident:
+                assert int(th[k]) == c.data_ptr() + k * stride
+        hits, misses, copied = cache.stats()
+        assert hits == sum(h_o) and misses == len(h_o) - sum(h_o)
+        print(f"slots {slots}: hit rate {hits / (hits + misses):.2f}, copied {copied} B")
+    finally:
+        cache.close()
