@@ -14,6 +14,7 @@ Zipf(1.1) router bias, T = 512 tokens per layer call through moe_layer_batched, 
 MFMA utilisation against the fp16 dense peak.
 """
 import argparse
+import dataclasses
 import glob
 import hashlib
 import json
@@ -182,6 +183,135 @@ def crossover_sweep(stack, reps: int):
     return {"workload": stack_name(stack), "layer": 0, "reps": reps, "rows": rows, "crossover": cross}
 
 
+RESIDENCY_FRACTIONS = [0.0, 0.05, 0.1, 0.25, 0.5, 1.0]
+
+
+def residency_sweep(stack, wl, warmup: int, steps: int, zipf_s):
+    """The decode stack with its routed experts in a fixed-stride container in pinned host memory
+    and a bounded HBM pool (LFU + recency) in front of it, for each pool size in
+    RESIDENCY_FRACTIONS (fraction of the L * E experts): per token one moe_stack_decode_table call,
+    the routing read back, and moe_cache_update (policy, admissions copied into the pool, table
+    rewritten). Reports tokens/s of that loop (host work and copies included), the kernel's own
+    time per call, the hit rate over the timed tokens and the bytes copied per token, for each
+    router bias in zipf_s: None (no bias: every expert equally likely, the least locality) or a
+    Zipf(s) bias per layer, standing in for the expert popularity skew of real text. Every layer
+    routes the step's own token (MOE_STACK_INDEPENDENT): chained through the weightless RMS glue,
+    these random-weight layers lose the token's identity within a few layers and from about the
+    ninth on route every token to the same experts, which would make any cache look perfect."""
+    import ctypes
+
+    import torch
+
+    import quantized_moe_decode_router_amd as moe
+    import synth
+
+    shape, T, L = wl.shape, wl.tokens, wl.n_layers
+    E, K = shape.num_experts, shape.top_k
+    dev = stack.router.device
+    stride = moe.moe_expert_stride(shape)
+    nbytes = L * E * stride
+    hip = ctypes.CDLL("libamdhip64.so")
+    hbuf = ctypes.c_void_p()
+    if hip.hipHostMalloc(ctypes.byref(hbuf), ctypes.c_size_t(nbytes + 4096), ctypes.c_uint(0)) != 0:
+        raise SystemExit("hipHostMalloc of the expert container failed")
+    base = (hbuf.value + 4095) // 4096 * 4096
+    container = (base, nbytes)
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    moe.moe_pack_experts(shape, stack, L, container, stream=stream)
+    torch.cuda.synchronize()
+    print(f"[residency] packed {nbytes / 1e9:.2f} GB into pinned host memory in {time.perf_counter() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+    nsteps = warmup + steps
+    xs = torch.stack([synth.make_x(shape, T, wl.seed, step=s, device=dev) for s in range(nsteps)])
+    y = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
+    idx = torch.empty(L, T, K, dtype=torch.int32, device=dev)
+    idx_h = torch.empty(L, T, K, dtype=torch.int32, pin_memory=True)
+    ws = moe.workspace(shape, T, moe.MOE_WS_STACK, dev, n_layers=L)
+    table = torch.empty(L * E, dtype=torch.int64, device=dev)
+    rows = []
+    # the same loop's decode with every expert resident in its stacked arrays (no table, no cache)
+    for s in range(warmup):
+        moe.moe_stack_decode(shape, stack, L, xs[s], T, y, workspace=ws, stream=stream, flags=moe.MOE_STACK_INDEPENDENT)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for s in range(warmup, nsteps):
+        moe.moe_stack_decode(shape, stack, L, xs[s], T, y, workspace=ws, stream=stream, flags=moe.MOE_STACK_INDEPENDENT)
+    b.record(stream)
+    torch.cuda.synchronize()
+    resident_ms = a.elapsed_time(b) / steps
+    print(f"[residency] all experts resident, no table: {resident_ms:.3f} ms per token", file=sys.stderr, flush=True)
+    # the table decode with every block in device memory: a copy of the container in HBM
+    dbuf = torch.empty(nbytes + 4096, dtype=torch.uint8, device=dev)
+    doff = (-dbuf.data_ptr()) % 4096
+    moe.moe_pack_experts(shape, stack, L, dbuf[doff:doff + nbytes], stream=stream)
+    dtab = (dbuf.data_ptr() + doff + torch.arange(L * E, dtype=torch.int64, device=dev) * stride).contiguous()
+    nost0 = dataclasses.replace(stack, w13_codes=None, w13_scales=None, w13_biases=None, w2_codes=None,
+                                w2_scales=None, w2_biases=None)
+    for s in range(warmup):
+        moe.moe_stack_decode_table(shape, nost0, L, dtab, xs[s], T, y, workspace=ws, stream=stream,
+                                   flags=moe.MOE_STACK_INDEPENDENT)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for s in range(warmup, nsteps):
+        moe.moe_stack_decode_table(shape, nost0, L, dtab, xs[s], T, y, workspace=ws, stream=stream,
+                                   flags=moe.MOE_STACK_INDEPENDENT)
+    b.record(stream)
+    torch.cuda.synchronize()
+    table_hbm_ms = a.elapsed_time(b) / steps
+    del dbuf, dtab
+    print(f"[residency] table decode, every block in HBM: {table_hbm_ms:.3f} ms per token", file=sys.stderr,
+          flush=True)
+    try:
+        for zs in zipf_s:
+            st = stack if zs is None else synth.with_zipf_bias(stack, wl.seed, zs)
+            nost = dataclasses.replace(st, w13_codes=None, w13_scales=None, w13_biases=None, w2_codes=None,
+                                       w2_scales=None, w2_biases=None)
+            for frac in RESIDENCY_FRACTIONS:
+                slots = int(round(frac * L * E))
+                pool = torch.empty(max(slots, 1) * stride + 4096, dtype=torch.uint8, device=dev)
+                off = (-pool.data_ptr()) % 4096
+                cache = moe.MoeCache(shape, L, container, pool[off:off + max(slots, 1) * stride] if slots else None,
+                                     slots, table, stream=stream)
+                kern_ms, hits, misses = 0.0, 0, 0
+                b0 = cache.stats()[2]
+                for s in range(nsteps):
+                    if s == warmup:
+                        torch.cuda.synchronize()
+                        w0 = time.perf_counter()
+                        b0 = cache.stats()[2]
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    moe.moe_stack_decode_table(shape, nost, L, table, xs[s], T, y, topk_idx_all=idx, workspace=ws,
+                                               stream=stream, flags=moe.MOE_STACK_INDEPENDENT)
+                    b.record(stream)
+                    idx_h.copy_(idx, non_blocking=True)
+                    stream.synchronize()
+                    h, m = cache.update(idx_h, T, K, stream=stream)
+                    if s >= warmup:
+                        kern_ms += a.elapsed_time(b)
+                        hits, misses = hits + h, misses + m
+                torch.cuda.synchronize()
+                wall = time.perf_counter() - w0
+                if moe.moe_read_status(ws) != 0:
+                    raise SystemExit("device status after the residency steps is not OK")
+                copied = cache.stats()[2] - b0
+                cache.close()
+                del pool
+                row = {"zipf_s": zs, "pool_fraction": frac, "slots": slots, "pool_gb": round(slots * stride / 1e9, 2),
+                       "tokens_per_s": round(steps * T / wall, 2), "ms_per_token": round(wall * 1e3 / steps, 3),
+                       "kernel_ms": round(kern_ms / steps, 3), "hit_rate": round(hits / max(hits + misses, 1), 4),
+                       "copied_mb_per_token": round(copied / steps / 1e6, 1)}
+                rows.append(row)
+                print(f"[residency] {row}", file=sys.stderr, flush=True)
+    finally:
+        torch.cuda.synchronize()
+        hip.hipHostFree(hbuf)
+    return {"workload": wl.name, "resident_kernel_ms": round(resident_ms, 3), "table_all_hbm_kernel_ms": round(table_hbm_ms, 3), "expert_stride": stride, "container_gb": round(nbytes / 1e9, 2),
+            "warmup": warmup, "steps": steps, "rows": rows}
+
+
 def stack_name(stack) -> str:
     s = stack.shape
     return f"H{s.hidden}_E{s.num_experts}_K{s.top_k}_I{s.inter}_Is{s.shared_inter}_{s.bits}bit"
@@ -201,6 +331,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--batched-steps", type=int, default=10,
                     help="steps of the batched leg (0 skips it)")
+    ap.add_argument("--residency", action="store_true",
+                    help="only the expert-residency sweep over pool sizes (one JSON line)")
+    ap.add_argument("--residency-steps", type=int, default=100)
+    ap.add_argument("--residency-warmup", type=int, default=100)
     ap.add_argument("--sweep", action="store_true",
                     help="only the decode / batched crossover sweep of one layer (one JSON line)")
     args = ap.parse_args()
@@ -223,6 +357,11 @@ def main():
           f"{time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
     if args.sweep:
         print(json.dumps({"sweep": crossover_sweep(stack, reps=50)}), flush=True)
+        return
+    if args.residency:
+        print(json.dumps({"residency": residency_sweep(stack, wl, warmup=args.residency_warmup,
+                                                       steps=args.residency_steps,
+                                                       zipf_s=[None, 0.5, 1.1])}), flush=True)
         return
     nsteps = args.warmup + args.steps
     xs = torch.stack([synth.make_x(shape, T, wl.seed, step=s, device=dev) for s in range(nsteps)])

@@ -239,7 +239,7 @@ moe_status moe_pack_experts(const moe_shape *shape, const moe_layer *stack, int3
 /*
  * moe_stack_decode with the routed experts read through expert_table instead of stack->w13 and
  * stack->w2 (which may then be NULL; every other field of `stack` is used as in moe_stack_decode).
- *   expert_table : uint64 [L][E], device memory, 8-byte aligned: the address of expert (l, e)'s
+ *   expert_table : uint64 [L][E], device memory, 16-byte aligned: the address of expert (l, e)'s
  *                  block (layout as moe_expert_stride); each address must stay readable by the
  *                  device, and its bytes unchanged, until the call completes
  * Results are bit for bit those of moe_stack_decode on the same weights, wherever the blocks are.
@@ -258,7 +258,9 @@ typedef struct moe_cache moe_cache;
  * Creates a cache over a packed container of n_layers * E experts, with `slots` (0 <= slots <=
  * n_layers * E) pool slots of one stride each at `pool` (device memory, 4096-byte aligned, at
  * least slots * stride bytes; may be NULL when slots is 0), and writes the initial table (every
- * expert at its container block) to `table` (device, uint64 [L][E]), synchronously on `stream`.
+ * expert at its container block) to `table` (device, 16-byte aligned, uint64 [L][E]),
+ * synchronously on `stream`. The container must be device memory or pinned host memory that the
+ * device sees at the same address (checked: MOE_ERR_INVALID_ARG otherwise).
  * The caller owns container, pool and table and keeps them alive until moe_cache_destroy.
  */
 moe_status moe_cache_create(const moe_shape *shape, int32_t n_layers, const void *container,

@@ -125,8 +125,11 @@ def _ptr(t: Optional[torch.Tensor], name: str, dtype=None):
     return t.data_ptr()
 
 
-def _dptr(t: torch.Tensor, name: str) -> int:
-    """Address the device can read: a GPU tensor, or a pinned (page-locked) host tensor."""
+def _dptr(t, name: str) -> int:
+    """Address the device can read: a GPU tensor, a pinned (page-locked) host tensor, or a raw
+    (address, nbytes) pair of such memory allocated elsewhere (e.g. hipHostMalloc)."""
+    if isinstance(t, tuple):
+        return int(t[0])
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name}: expected a torch.Tensor")
     if not (t.is_cuda or t.is_pinned()):
@@ -136,7 +139,9 @@ def _dptr(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
-def _nbytes(t: torch.Tensor) -> int:
+def _nbytes(t) -> int:
+    if isinstance(t, tuple):
+        return int(t[1])
     return t.numel() * t.element_size()
 
 

@@ -338,7 +338,7 @@ struct Lds {
     float2 *xsx;     // [T][H/64] (sum of the limb values, group scale)
     int8_t *hq;      // [(K*I + Is)/64][3][64] h of one token (routed vectors, then the shared one)
     float2 *hsx;     // [(K*I + Is)/64]
-    uint64_t *xb;    // [T*K] expert-table mode: block address of each selected (token, slot)
+    uint64_t *xt;    // [2][E] expert-table mode: the table rows of layers l (buffer l & 1) and l + 1
 };
 __device__ __forceinline__ Lds carve(const DecodeParams &p, char *smem) {
     const DecodeLds &o = p.lds;
@@ -360,7 +360,7 @@ __device__ __forceinline__ Lds carve(const DecodeParams &p, char *smem) {
     s.xsx = reinterpret_cast<float2 *>(smem + o.xsx);
     s.hq = reinterpret_cast<int8_t *>(smem + o.hq);
     s.hsx = reinterpret_cast<float2 *>(smem + o.hsx);
-    s.xb = reinterpret_cast<uint64_t *>(smem + o.xb);
+    s.xt = reinterpret_cast<uint64_t *>(smem + o.xt);
     return s;
 }
 
@@ -449,7 +449,8 @@ __device__ __forceinline__ void stage_routed_down(const DecodeParams &p, int l, 
         dma_xrows(p.I, p.bits, K * nr,
                   [&](int r) -> XRow {
                       const int k = div_by(r, nrm), rl = r - k * nr;
-                      return XRow{s.xb[t * K + k] + p.xo2c, (uint32_t)(r0 + rl)};
+                      return XRow{s.xt[(l & 1) * E + expert_at(s.sidx[t * K + k], E)] + p.xo2c,
+                                  (uint32_t)(r0 + rl)};
                   },
                   p.xo2s - p.xo2c, p.xo2b - p.xo2c, rd_rows(p, s), mfma_swz(p.bits, p.I));
         return;
@@ -462,6 +463,17 @@ __device__ __forceinline__ void stage_routed_down(const DecodeParams &p, int l, 
                   return expert_at(s.sidx[t * K + k], E) * H + (size_t)(r0 + rl);
               },
               rd_rows(p, s), mfma_swz(p.bits, p.I));
+}
+
+// Expert-table mode: layer l's row of the table (E block addresses) into LDS buffer l & 1.
+__device__ __forceinline__ void stage_xtab(const DecodeParams &p, int l, const Lds &s, DmaWaves dw) {
+    const int E = p.E;
+    const uint64_t *src = p.xtab + (size_t)l * E;
+    char *dst = reinterpret_cast<char *>(s.xt + (l & 1) * E);
+    if ((E & 1) == 0)
+        dma_rows<16>(E / 2, 16, [&](int r) { return reinterpret_cast<const char *>(src + 2 * r); }, dst, kNoSwz, dw);
+    else
+        dma_rows<4>(2 * E, 4, [&](int r) { return reinterpret_cast<const char *>(src) + 4 * r; }, dst, kNoSwz, dw);
 }
 
 // ---- activations as int8 limbs -------------------------------------------------------------------
@@ -922,6 +934,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
     {
         const Lds s = carve(p0, smem);
         stage_router(p0, 0, s, w);
+        if constexpr (XT) stage_xtab(p0, 0, s, kAllWaves);
         stage_shared_gu(p0, 0, s, w);
         stage_shared_down(p0, 0, s, w.r0, w.nr);
     }
@@ -954,6 +967,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         if (has_next) {
             const int first = min(T + kWaves / 2, kWaves - 1);
             stage_router(p, l + 1, s, w, DmaWaves{first, kWaves - first});
+            if constexpr (XT) stage_xtab(p, l + 1, s, DmaWaves{first, kWaves - first});
         }
         if (Is) {
             // the shared expert's gate|up runs on the waves not selecting experts; its barrier also
@@ -974,11 +988,6 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
                 for (int i = tid; i < T * E; i += blockDim.x)
                     G(p.logits_all)[base * E + i] = s.lg[(i / E) * (E + 1) + i % E];
         }
-        if constexpr (XT) {
-            // block address of every selected expert (the routing is published by the barrier above)
-            if (tid < T * K) s.xb[tid] = G(p.xtab)[(size_t)l * E + expert_at(s.sidx[tid], E)];
-            lds_barrier();
-        }
         // routed gate|up: this workgroup's pairs [q0, q1) of the flattened (token, slot, j) pairs,
         // staged into LDS chunk by chunk (one chunk at T = 1): LDS row 2i = gate row, 2i+1 = up row
         {
@@ -992,7 +1001,8 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
                     dma_xrows(H, BITS, 2 * nc,
                               [&](int r) -> XRow {
                                   const int P = pb + (r >> 1), tk = P >> lgI, j = P & (I - 1);
-                                  return XRow{s.xb[tk], (uint32_t)((r & 1) * I + j)};
+                                  return XRow{s.xt[(l & 1) * E + expert_at(s.sidx[tk], E)],
+                                              (uint32_t)((r & 1) * I + j)};
                               },
                               p.xo13s, p.xo13b, rg, mfma_swz(BITS, H));
                 } else {

@@ -74,9 +74,9 @@ size_t batched_ws_bytes(const moe_shape *s, int T) {
 // static arrays).
 constexpr int kDecodeLdsBudget = 160 * 1024 - 256;
 
-int decode_chunk(const moe_shape *s, int T, int grid) {
+int decode_chunk(const moe_shape *s, int T, int grid, bool xt = false) {
     return moe::decode_chunk_pairs(T, s->hidden, s->num_experts, s->top_k, s->inter, s->shared_inter, s->bits, grid,
-                                   kDecodeLdsBudget);
+                                   kDecodeLdsBudget, xt);
 }
 
 int rows_per_wg(int H, int grid) { return (H + grid - 1) / grid; }
@@ -94,10 +94,10 @@ size_t forward_decode_part(const moe_shape *s) { return align_up(decode_ws_bytes
 // Shapes the decode kernel handles (beyond check_shape): rows of at most 64 slices of 32 columns,
 // intermediates of at least 128 columns (whole dwords of scales per row for the LDS staging),
 // and an LDS plan within the compute unit's 160 KiB.
-moe_status decode_supported(const moe_shape *s, int T, int grid) {
+moe_status decode_supported(const moe_shape *s, int T, int grid, bool xt = false) {
     if (s->hidden > 2048 || s->inter > 2048 || s->shared_inter > 2048) return MOE_ERR_UNSUPPORTED;
     if (s->inter < 128 || (s->shared_inter && s->shared_inter < 128)) return MOE_ERR_UNSUPPORTED;
-    if (decode_chunk(s, T, grid) == 0) return MOE_ERR_UNSUPPORTED;
+    if (decode_chunk(s, T, grid, xt) == 0) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -108,7 +108,7 @@ moe_status decode_common(const moe_shape *s, const moe_layer *L, int32_t n_layer
     moe_status st = check_shape(s);
     if (st != MOE_OK) return st;
     if ((st = check_layer(s, L, xtab == nullptr)) != MOE_OK) return st;
-    if (xtab && (reinterpret_cast<uintptr_t>(xtab) & 7u)) return MOE_ERR_INVALID_ARG;
+    if (xtab && (reinterpret_cast<uintptr_t>(xtab) & 15u)) return MOE_ERR_INVALID_ARG;
     if (flags & ~MOE_STACK_INDEPENDENT) return MOE_ERR_INVALID_ARG;
     if (n_layers < 1 || n_layers > kMaxLayers || T < 1 || T > kMaxDecodeT) return MOE_ERR_INVALID_ARG;
     if (!x || !y || !al16(x) || !al16(y)) return MOE_ERR_INVALID_ARG;
@@ -119,7 +119,8 @@ moe_status decode_common(const moe_shape *s, const moe_layer *L, int32_t n_layer
     const int grid = moe::device_cu_count();
     if (grid <= 0) return MOE_ERR_HIP;
     if (grid > moe::kMaxGrid) return MOE_ERR_UNSUPPORTED;
-    if ((st = decode_supported(s, T, grid)) != MOE_OK) return st;
+    const bool xt = xtab != nullptr;
+    if ((st = decode_supported(s, T, grid, xt)) != MOE_OK) return st;
 
     const size_t H = s->hidden, E = s->num_experts, I = s->inter, Is = s->shared_inter;
     const size_t bits = s->bits;
@@ -135,9 +136,9 @@ moe_status decode_common(const moe_shape *s, const moe_layer *L, int32_t n_layer
     while ((1 << p.log2I) < s->inter) ++p.log2I;
     p.kdiv = moe::div_magic((unsigned)s->top_k);
     p.tdiv = moe::div_magic((unsigned)T);
-    p.cp = decode_chunk(s, T, grid);
+    p.cp = decode_chunk(s, T, grid, xt);
     p.lds = moe::decode_lds_plan(T, s->hidden, s->num_experts, s->top_k, s->inter, s->shared_inter, s->bits, grid,
-                                 p.cp);
+                                 p.cp, xt);
     p.spin_limit = 1u << 20;
     p.eps = 1e-6f;
     p.router = L->router; p.rbias = L->router_bias; p.sgate = Is ? L->shared_gate : nullptr;

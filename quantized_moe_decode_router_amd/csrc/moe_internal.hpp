@@ -15,7 +15,7 @@ struct QMat {
 
 // LDS plan of the decode kernel: byte offsets of every region (computed once on the host).
 struct DecodeLds {
-    int xp, lg, sidx, sw, gam, rt, sg, sd, rd, rg, hp, part, red, xq, xsx, hq, hsx, xb;
+    int xp, lg, sidx, sw, gam, rt, sg, sd, rd, rg, hp, part, red, xq, xsx, hq, hsx, xt;
     int total;
 };
 
@@ -101,7 +101,8 @@ __host__ __device__ inline DecodeWs decode_ws_layout(int L, int T, int H, int E,
 
 // LDS plan for a shape, token count and grid (router rows and shared pairs per workgroup and
 // the y rows per workgroup follow from the grid); cp = routed gate|up pairs per LDS chunk.
-__host__ inline DecodeLds decode_lds_plan(int T, int H, int E, int K, int I, int Is, int bits, int grid, int cp) {
+__host__ inline DecodeLds decode_lds_plan(int T, int H, int E, int K, int I, int Is, int bits, int grid, int cp,
+                                          bool xt = false) {
     DecodeLds d;
     const size_t RB = ((size_t)H + grid - 1) / grid;
     const size_t nrr = ((size_t)E + (Is ? 1 : 0) + grid - 1) / grid;
@@ -139,9 +140,9 @@ __host__ inline DecodeLds decode_lds_plan(int T, int H, int E, int K, int I, int
         4 * (size_t)T * (K + 1) * RB,    // part
         4 * 64,                          // red
         gsx,                             // xsx (also hsx)
-        8 * (size_t)T * K};              // xb (expert blocks of the selection, expert-table mode)
+        xt ? 16 * (size_t)E : 0};        // xt: two layers' rows of the expert table (expert-table mode)
     int *o[15] = {&d.xp, &d.lg, &d.sidx, &d.sw, &d.gam, &d.rt, &d.sg, &d.sd, &d.rd, &d.rg, &d.hp, &d.part, &d.red,
-                  &d.xsx, &d.xb};
+                  &d.xsx, &d.xt};
     size_t off = 0;
     for (int i = 0; i < 15; ++i) {
         *o[i] = (int)off;
@@ -154,13 +155,14 @@ __host__ inline DecodeLds decode_lds_plan(int T, int H, int E, int K, int I, int
 }
 // Routed gate|up pairs per LDS chunk: every pair of the workgroup's share if that fits in
 // `budget` bytes of LDS, else the largest power of two that does (0 if not even one pair fits).
-__host__ inline int decode_chunk_pairs(int T, int H, int E, int K, int I, int Is, int bits, int grid, int budget) {
+__host__ inline int decode_chunk_pairs(int T, int H, int E, int K, int I, int Is, int bits, int grid, int budget,
+                                      bool xt = false) {
     const long long total = (long long)T * K * I;
     int cp = (int)((total + grid - 1) / grid);
     int p2 = 1;
     while (p2 < cp) p2 <<= 1;
     for (int c = cp; c >= 1; c = (c == cp && cp != p2) ? p2 / 2 : c / 2)
-        if (decode_lds_plan(T, H, E, K, I, Is, bits, grid, c).total <= budget) return c;
+        if (decode_lds_plan(T, H, E, K, I, Is, bits, grid, c, xt).total <= budget) return c;
     return 0;
 }
 

@@ -106,7 +106,7 @@ moe_status moe_cache_create(const moe_shape *s, int32_t n_layers, const void *co
         return MOE_ERR_INVALID_ARG;
     if (slots > 0 && (!pool || (reinterpret_cast<uintptr_t>(pool) & 4095u) || pool_bytes < (size_t)slots * stride))
         return MOE_ERR_INVALID_ARG;
-    if (!table || (reinterpret_cast<uintptr_t>(table) & 7u) || table_bytes < keys * 8) return MOE_ERR_INVALID_ARG;
+    if (!table || (reinterpret_cast<uintptr_t>(table) & 15u) || table_bytes < keys * 8) return MOE_ERR_INVALID_ARG;
     // the kernel reads the container at the addresses the table holds: it must be device memory,
     // or pinned host memory mapped at the same address (pageable memory would fault the device)
     hipPointerAttribute_t attr;
