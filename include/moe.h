@@ -274,6 +274,9 @@ moe_status moe_cache_create(const moe_shape *shape, int32_t n_layers, const void
  * routing must come from a call on it that has completed). hits_opt / misses_opt: this call's
  * counts. Policy: a resident expert has a use count (1 on admission, +1 per hit) and a last-use
  * time; a miss takes the lowest free slot, else evicts the smallest count, oldest last use first.
+ * The table is rewritten in two steps around the copies, so that it never names a slot being
+ * overwritten; if a copy cannot be queued the table stays valid (no admitted expert in it), the
+ * call returns MOE_ERR_HIP and so does every later update of this cache (destroy and recreate it).
  */
 moe_status moe_cache_update(moe_cache *cache, const int32_t *topk_idx_all, int32_t T, int32_t top_k,
                             void *stream, int32_t *hits_opt, int32_t *misses_opt);

@@ -85,9 +85,11 @@ struct moe_cache {
     const char *container;
     char *pool;
     uint64_t *table_dev;
-    uint64_t *table_host;  // pinned staging of the whole table
+    uint64_t *table_host;  // pinned staging of the whole table (its state after the copies)
+    uint64_t *table_mid;   // pinned staging of the table while the copies run
     LfuRecency policy;
     uint64_t hits = 0, misses = 0, bytes_copied = 0;
+    bool broken = false;  // an update failed part-way: the pool no longer matches the policy
     moe_cache(int L_, int E_, int slots_) : L(L_), E(E_), slots(slots_), policy(slots_, L_ * E_) {}
 };
 
@@ -120,7 +122,10 @@ moe_status moe_cache_create(const moe_shape *s, int32_t n_layers, const void *co
     c->container = static_cast<const char *>(container);
     c->pool = static_cast<char *>(pool);
     c->table_dev = table;
-    if (hipHostMalloc(reinterpret_cast<void **>(&c->table_host), keys * 8, hipHostMallocDefault) != hipSuccess) {
+    c->table_host = c->table_mid = nullptr;
+    if (hipHostMalloc(reinterpret_cast<void **>(&c->table_host), keys * 8, hipHostMallocDefault) != hipSuccess ||
+        hipHostMalloc(reinterpret_cast<void **>(&c->table_mid), keys * 8, hipHostMallocDefault) != hipSuccess) {
+        if (c->table_host) hipHostFree(c->table_host);
         delete c;
         return MOE_ERR_HIP;
     }
@@ -129,6 +134,7 @@ moe_status moe_cache_create(const moe_shape *s, int32_t n_layers, const void *co
     if (hipMemcpyAsync(table, c->table_host, keys * 8, hipMemcpyHostToDevice, hs) != hipSuccess ||
         hipStreamSynchronize(hs) != hipSuccess) {
         hipHostFree(c->table_host);
+        hipHostFree(c->table_mid);
         delete c;
         return MOE_ERR_HIP;
     }
@@ -139,6 +145,7 @@ moe_status moe_cache_create(const moe_shape *s, int32_t n_layers, const void *co
 moe_status moe_cache_update(moe_cache *c, const int32_t *topk_idx_all, int32_t T, int32_t top_k, void *stream,
                             int32_t *hits_opt, int32_t *misses_opt) {
     if (!c || !topk_idx_all || T < 1 || top_k < 1) return MOE_ERR_INVALID_ARG;
+    if (c->broken) return MOE_ERR_HIP;
     const size_t n = (size_t)c->L * T * top_k;
     for (size_t i = 0; i < n; ++i)
         if (topk_idx_all[i] < 0 || topk_idx_all[i] >= c->E) return MOE_ERR_INVALID_ARG;
@@ -156,22 +163,30 @@ moe_status moe_cache_update(moe_cache *c, const int32_t *topk_idx_all, int32_t T
     c->hits += hits;
     c->misses += misses;
     const std::vector<int> &after = c->policy.owners();
+    const size_t tbytes = (size_t)c->L * c->E * 8;
+    auto at_container = [&](int key) { return reinterpret_cast<uint64_t>(c->container + (size_t)key * c->stride); };
+    // Three steps on the stream, so that the device table never names a slot being rewritten:
+    // (1) every expert leaving a slot points at its container block again, (2) the admitted blocks
+    // are copied into their slots, (3) the admitted experts point at their slots. If a step fails,
+    // the table on the device is (1)'s and the cache refuses further updates.
+    for (int sl = 0; sl < c->slots; ++sl)
+        if (after[sl] != before[sl] && before[sl] >= 0) c->table_host[before[sl]] = at_container(before[sl]);
+    memcpy(c->table_mid, c->table_host, tbytes);
+    c->broken = true;
+    if (hipMemcpyAsync(c->table_dev, c->table_mid, tbytes, hipMemcpyHostToDevice, hs) != hipSuccess) return MOE_ERR_HIP;
     for (int sl = 0; sl < c->slots; ++sl) {
         if (after[sl] == before[sl]) continue;
-        if (before[sl] >= 0)
-            c->table_host[before[sl]] = reinterpret_cast<uint64_t>(c->container + (size_t)before[sl] * c->stride);
-        char *dst = c->pool + (size_t)sl * c->stride;
-        if (hipMemcpyAsync(dst, c->container + (size_t)after[sl] * c->stride, c->stride, hipMemcpyDefault, hs) !=
-            hipSuccess)
+        if (hipMemcpyAsync(c->pool + (size_t)sl * c->stride, c->container + (size_t)after[sl] * c->stride, c->stride,
+                           hipMemcpyDefault, hs) != hipSuccess)
             return MOE_ERR_HIP;
         c->bytes_copied += c->stride;
     }
     // a key evicted from one slot may have been admitted into another within the same call
     for (int sl = 0; sl < c->slots; ++sl)
         if (after[sl] >= 0) c->table_host[after[sl]] = reinterpret_cast<uint64_t>(c->pool + (size_t)sl * c->stride);
-    if (hipMemcpyAsync(c->table_dev, c->table_host, (size_t)c->L * c->E * 8, hipMemcpyHostToDevice, hs) !=
-        hipSuccess)
+    if (hipMemcpyAsync(c->table_dev, c->table_host, tbytes, hipMemcpyHostToDevice, hs) != hipSuccess)
         return MOE_ERR_HIP;
+    c->broken = false;
     if (hits_opt) *hits_opt = hits;
     if (misses_opt) *misses_opt = misses;
     return MOE_OK;
@@ -195,6 +210,7 @@ moe_status moe_cache_owners(const moe_cache *c, int32_t *owner) {
 void moe_cache_destroy(moe_cache *c) {
     if (!c) return;
     hipHostFree(c->table_host);
+    hipHostFree(c->table_mid);
     delete c;
 }
 
