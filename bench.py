@@ -192,7 +192,8 @@ def residency_sweep(stack, wl, warmup: int, steps: int, zipf_s):
     RESIDENCY_FRACTIONS (fraction of the L * E experts): per token one moe_stack_decode_table call,
     the routing read back, and moe_cache_update (policy, admissions copied into the pool, table
     rewritten). Reports tokens/s of that loop (host work and copies included), the kernel's own
-    time per call, the hit rate over the timed tokens and the bytes copied per token, for each
+    time per call, the hit rate over the timed tokens and the bytes copied per token, with and
+    without a landing buffer (misses written through by the decode, admitted device to device), for each
     router bias in zipf_s: None (no bias: every expert equally likely, the least locality) or a
     Zipf(s) bias per layer, standing in for the expert popularity skew of real text. Every layer
     routes the step's own token (MOE_STACK_INDEPENDENT): chained through the weightless RMS glue,
@@ -264,7 +265,10 @@ def residency_sweep(stack, wl, warmup: int, steps: int, zipf_s):
     print(f"[residency] table decode, every block in HBM: {table_hbm_ms:.3f} ms per token", file=sys.stderr,
           flush=True)
     try:
-        for zs in zipf_s:
+        land_t = torch.empty(L * T * K * stride + 4096, dtype=torch.uint8, device=dev)
+        loff = (-land_t.data_ptr()) % 4096
+        land = land_t[loff:loff + L * T * K * stride]
+        for zs, through in [(z, f) for z in zipf_s for f in (False, True)]:
             st = stack if zs is None else synth.with_zipf_bias(stack, wl.seed, zs)
             nost = dataclasses.replace(st, w13_codes=None, w13_scales=None, w13_biases=None, w2_codes=None,
                                        w2_scales=None, w2_biases=None)
@@ -272,8 +276,9 @@ def residency_sweep(stack, wl, warmup: int, steps: int, zipf_s):
                 slots = int(round(frac * L * E))
                 pool = torch.empty(max(slots, 1) * stride + 4096, dtype=torch.uint8, device=dev)
                 off = (-pool.data_ptr()) % 4096
+                lnd = land if through else None
                 cache = moe.MoeCache(shape, L, container, pool[off:off + max(slots, 1) * stride] if slots else None,
-                                     slots, table, stream=stream)
+                                     slots, table, stream=stream, landing=lnd)
                 kern_ms, hits, misses = 0.0, 0, 0
                 b0 = cache.stats()[2]
                 for s in range(nsteps):
@@ -284,7 +289,7 @@ def residency_sweep(stack, wl, warmup: int, steps: int, zipf_s):
                     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     a.record(stream)
                     moe.moe_stack_decode_table(shape, nost, L, table, xs[s], T, y, topk_idx_all=idx, workspace=ws,
-                                               stream=stream, flags=moe.MOE_STACK_INDEPENDENT)
+                                               stream=stream, flags=moe.MOE_STACK_INDEPENDENT, landing=lnd)
                     b.record(stream)
                     idx_h.copy_(idx, non_blocking=True)
                     stream.synchronize()
@@ -299,7 +304,7 @@ def residency_sweep(stack, wl, warmup: int, steps: int, zipf_s):
                 copied = cache.stats()[2] - b0
                 cache.close()
                 del pool
-                row = {"zipf_s": zs, "pool_fraction": frac, "slots": slots, "pool_gb": round(slots * stride / 1e9, 2),
+                row = {"zipf_s": zs, "write_through": through, "pool_fraction": frac, "slots": slots, "pool_gb": round(slots * stride / 1e9, 2),
                        "tokens_per_s": round(steps * T / wall, 2), "ms_per_token": round(wall * 1e3 / steps, 3),
                        "kernel_ms": round(kern_ms / steps, 3), "hit_rate": round(hits / max(hits + misses, 1), 4),
                        "copied_mb_per_token": round(copied / steps / 1e6, 1)}

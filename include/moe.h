@@ -240,12 +240,18 @@ moe_status moe_pack_experts(const moe_shape *shape, const moe_layer *stack, int3
  * moe_stack_decode with the routed experts read through expert_table instead of stack->w13 and
  * stack->w2 (which may then be NULL; every other field of `stack` is used as in moe_stack_decode).
  *   expert_table : uint64 [L][E], device memory, 16-byte aligned: the address of expert (l, e)'s
- *                  block (layout as moe_expert_stride); each address must stay readable by the
- *                  device, and its bytes unchanged, until the call completes
+ *                  block (layout as moe_expert_stride) plus a mark in bit 0 (blocks are 4096-byte
+ *                  aligned); each address must stay readable by the device, and its bytes
+ *                  unchanged, until the call completes
+ *   landing_opt  : NULL, or device memory (4096-byte aligned, landing_bytes >= L * T * K * stride)
+ *                  for [L][T][K] blocks: every row the call reads from a marked block is also
+ *                  stored to the landing block of its (layer, token, slot), so that all pieces of
+ *                  a marked selected expert land there (the padding between pieces is not written)
  * Results are bit for bit those of moe_stack_decode on the same weights, wherever the blocks are.
  */
 moe_status moe_stack_decode_table(const moe_shape *shape, const moe_layer *stack, int32_t n_layers,
-                                  const uint64_t *expert_table, uint32_t flags, const uint16_t *x,
+                                  const uint64_t *expert_table, void *landing_opt,
+                                  size_t landing_bytes, uint32_t flags, const uint16_t *x,
                                   int32_t T, float *y, uint16_t *x_all_opt, float *y_all_opt,
                                   int32_t *topk_idx_all_opt, float *topk_w_all_opt,
                                   float *logits_all_opt, void *workspace, size_t workspace_bytes,
@@ -262,10 +268,15 @@ typedef struct moe_cache moe_cache;
  * synchronously on `stream`. The container must be device memory or pinned host memory that the
  * device sees at the same address (checked: MOE_ERR_INVALID_ARG otherwise).
  * The caller owns container, pool and table and keeps them alive until moe_cache_destroy.
+ * landing_opt: NULL, or the landing buffer the decode calls are given (landing_bytes for up to
+ * landing_bytes / (n_layers * K * stride) tokens per call). With it every expert outside the pool
+ * is marked in the table, and an expert admitted after a call is copied from its landing block
+ * (device to device) instead of from the container.
  */
 moe_status moe_cache_create(const moe_shape *shape, int32_t n_layers, const void *container,
                             size_t container_bytes, void *pool, size_t pool_bytes, int32_t slots,
-                            uint64_t *table, size_t table_bytes, void *stream, moe_cache **out);
+                            uint64_t *table, size_t table_bytes, void *landing_opt,
+                            size_t landing_bytes, void *stream, moe_cache **out);
 
 /*
  * Feeds one decode call's routing (host int32 [L][T][top_k], every value in [0, E)) through the

@@ -77,11 +77,11 @@ def lib():
         L.moe_layer_path.restype = I32
         L.moe_layer_forward.argtypes = [PS, PL, P, I32, I32, P, P, P, P, P, SZ, P]
         L.moe_stack_decode.argtypes = [PS, PL, I32, U32, P, I32, P, P, P, P, P, P, P, SZ, P]
-        L.moe_stack_decode_table.argtypes = [PS, PL, I32, P, U32, P, I32, P, P, P, P, P, P, P, SZ, P]
+        L.moe_stack_decode_table.argtypes = [PS, PL, I32, P, P, SZ, U32, P, I32, P, P, P, P, P, P, P, SZ, P]
         L.moe_expert_stride.argtypes = [PS]
         L.moe_expert_stride.restype = SZ
         L.moe_pack_experts.argtypes = [PS, PL, I32, P, SZ, P]
-        L.moe_cache_create.argtypes = [PS, I32, P, SZ, P, SZ, I32, P, SZ, P, ctypes.POINTER(P)]
+        L.moe_cache_create.argtypes = [PS, I32, P, SZ, P, SZ, I32, P, SZ, P, SZ, P, ctypes.POINTER(P)]
         L.moe_cache_update.argtypes = [P, P, I32, I32, P, ctypes.POINTER(I32), ctypes.POINTER(I32)]
         U64P = ctypes.POINTER(ctypes.c_uint64)
         L.moe_cache_stats.argtypes = [P, U64P, U64P, U64P]
@@ -271,11 +271,12 @@ def moe_pack_experts(shape, stack, n_layers: int, container, stream=None) -> Non
 
 def moe_stack_decode_table(shape, stack, n_layers: int, expert_table, x, T: int, y, x_all=None, y_all=None,
                            topk_idx_all=None, topk_w_all=None, logits_all=None, workspace=None,
-                           workspace_bytes=None, stream=None, flags: int = 0) -> None:
+                           workspace_bytes=None, stream=None, flags: int = 0, landing=None) -> None:
     s, L = shape_struct(shape), layer_struct(stack)
     wsb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
     st = lib().moe_stack_decode_table(ctypes.byref(s), ctypes.byref(L), int(n_layers),
-                                      _ptr(expert_table, "expert_table", (torch.int64, torch.uint64)), int(flags),
+                                      _ptr(expert_table, "expert_table", (torch.int64, torch.uint64)),
+                                      _ptr(landing, "landing"), _nbytes(landing) if landing is not None else 0, int(flags),
                                       _ptr(x, "x", _BF16_BITS), int(T), _ptr(y, "y", torch.float32),
                                       _ptr(x_all, "x_all", _BF16_BITS), _ptr(y_all, "y_all", torch.float32),
                                       _ptr(topk_idx_all, "topk_idx_all", torch.int32),
@@ -289,16 +290,18 @@ class MoeCache:
     """moe_cache_* over caller-owned tensors: a packed container (GPU or pinned host uint8), a GPU
     pool of `slots` strides and a GPU int64 [L][E] expert table."""
 
-    def __init__(self, shape, n_layers: int, container, pool, slots: int, table, stream=None):
+    def __init__(self, shape, n_layers: int, container, pool, slots: int, table, stream=None, landing=None):
         s = shape_struct(shape)
         self._h = ctypes.c_void_p()
-        self._keep = (container, pool, table)
+        self._keep = (container, pool, table, landing)
         self.slots = int(slots)
         st = lib().moe_cache_create(ctypes.byref(s), int(n_layers), _dptr(container, "container"),
                                     _nbytes(container), _ptr(pool, "pool") if pool is not None else None,
                                     _nbytes(pool) if pool is not None else 0, self.slots,
                                     _ptr(table, "table", (torch.int64, torch.uint64)), _nbytes(table),
-                                    _stream(stream), ctypes.byref(self._h))
+                                    _ptr(landing, "landing") if landing is not None else None,
+                                    _nbytes(landing) if landing is not None else 0, _stream(stream),
+                                    ctypes.byref(self._h))
         _check(st, "moe_cache_create")
 
     def update(self, topk_idx_all, T: int, top_k: int, stream=None):

@@ -449,7 +449,7 @@ __device__ __forceinline__ void stage_routed_down(const DecodeParams &p, int l, 
         dma_xrows(p.I, p.bits, K * nr,
                   [&](int r) -> XRow {
                       const int k = div_by(r, nrm), rl = r - k * nr;
-                      return XRow{s.xt[(l & 1) * E + expert_at(s.sidx[t * K + k], E)] + p.xo2c,
+                      return XRow{(s.xt[(l & 1) * E + expert_at(s.sidx[t * K + k], E)] & ~1ull) + p.xo2c,
                                   (uint32_t)(r0 + rl)};
                   },
                   p.xo2s - p.xo2c, p.xo2b - p.xo2c, rd_rows(p, s), mfma_swz(p.bits, p.I));
@@ -463,6 +463,41 @@ __device__ __forceinline__ void stage_routed_down(const DecodeParams &p, int l, 
                   return expert_at(s.sidx[t * K + k], E) * H + (size_t)(r0 + rl);
               },
               rd_rows(p, s), mfma_swz(p.bits, p.I));
+}
+
+// Expert-table mode with a landing buffer: rows staged in LDS from a block marked as outside HBM
+// are stored to the landing block of their (layer, token, slot), un-permuting the code chunks
+// (LDS chunk c of row r holds source chunk c ^ ((r & mask) << shift)); dst_of(r) is the row's
+// destination or null. The host then admits such an expert from device memory.
+template <typename DstOf>
+__device__ __forceinline__ void wb_rows16(int n, int bytes, const char *lds, Swz swz, DstOf dst_of) {
+    const int sh = __builtin_ctz(static_cast<unsigned>(bytes / 16)), total = n << sh;
+    for (int u = threadIdx.x; u < total; u += blockDim.x) {
+        const int r = u >> sh, g = u & ((1 << sh) - 1);
+        char *d = dst_of(r);
+        if (!d) continue;
+        const int c = g ^ ((r & swz.mask) << swz.shift);
+        *reinterpret_cast<uint4 *>(d + (size_t)g * 16) =
+            *reinterpret_cast<const uint4 *>(lds + (size_t)r * bytes + (size_t)c * 16);
+    }
+}
+template <typename DstOf>
+__device__ __forceinline__ void wb_rows4(int n, int bytes, const char *lds, DstOf dst_of) {
+    const int sh = __builtin_ctz(static_cast<unsigned>(bytes / 4)), total = n << sh;
+    for (int u = threadIdx.x; u < total; u += blockDim.x) {
+        const int r = u >> sh, g = u & ((1 << sh) - 1);
+        char *d = dst_of(r);
+        if (!d) continue;
+        *reinterpret_cast<uint32_t *>(d + (size_t)g * 4) =
+            *reinterpret_cast<const uint32_t *>(lds + (size_t)r * bytes + (size_t)g * 4);
+    }
+}
+template <typename DstOf>
+__device__ __forceinline__ void wb_qrows(int n, const Rows &src, Swz swz, uint32_t off_s, uint32_t off_b,
+                                         DstOf row_dst) {
+    wb_rows16(n, src.cb, src.c, swz, [&](int r) { return row_dst(r, 0u, src.cb); });
+    wb_rows4(n, src.sb, src.s, [&](int r) { return row_dst(r, off_s, src.sb); });
+    wb_rows4(n, src.sb, src.b, [&](int r) { return row_dst(r, off_b, src.sb); });
 }
 
 // Expert-table mode: layer l's row of the table (E block addresses) into LDS buffer l & 1.
@@ -1001,7 +1036,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
                     dma_xrows(H, BITS, 2 * nc,
                               [&](int r) -> XRow {
                                   const int P = pb + (r >> 1), tk = P >> lgI, j = P & (I - 1);
-                                  return XRow{s.xt[(l & 1) * E + expert_at(s.sidx[tk], E)],
+                                  return XRow{s.xt[(l & 1) * E + expert_at(s.sidx[tk], E)] & ~1ull,
                                               (uint32_t)((r & 1) * I + j)};
                               },
                               p.xo13s, p.xo13b, rg, mfma_swz(BITS, H));
@@ -1022,6 +1057,23 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
                         return ll_h + (size_t)t * HW + (P - t * KI);
                     },
                     ep);
+                if constexpr (XT) {
+                    // the chunk's pairs belong to (token, slot)s tk_lo .. tk_hi; write through only
+                    // if one of them is marked (wave-uniform test on LDS broadcasts)
+                    bool marked = false;
+                    if (p.landing)
+                        for (int tk = pb >> lgI; tk <= (pb + nc - 1) >> lgI; ++tk)
+                            marked |= (s.xt[(l & 1) * E + expert_at(s.sidx[tk], E)] & 1) != 0;
+                    if (marked) {
+                        wb_qrows(2 * nc, rg, mfma_swz(BITS, H), p.xo13s, p.xo13b,
+                                 [&](int r, uint32_t piece, int rowbytes) -> char * {
+                                     const int P = pb + (r >> 1), tk = P >> lgI, j = P & (I - 1);
+                                     if (!(s.xt[(l & 1) * E + expert_at(s.sidx[tk], E)] & 1)) return nullptr;
+                                     return p.landing + ((size_t)l * T * K + tk) * p.xstride + piece +
+                                            (size_t)((r & 1) * I + j) * rowbytes;
+                                 });
+                    }
+                }
                 lds_barrier();
             }
         }
@@ -1044,6 +1096,21 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
             if (nr > 0) {
                 float *pt = s.part + (size_t)t * (K + 1) * RB;
                 down_all_mfma<BITS>(s, rd_rows(p, s), sd_rows(p, s), K, I, Is, nr, w.nrm, pt, RB);
+                if constexpr (XT) {
+                    bool marked = false;
+                    if (p.landing)
+                        for (int k = 0; k < K; ++k)
+                            marked |= (s.xt[(l & 1) * E + expert_at(s.sidx[t * K + k], E)] & 1) != 0;
+                    if (marked) {
+                        wb_qrows(K * nr, rd_rows(p, s), mfma_swz(BITS, I), p.xo2s - p.xo2c, p.xo2b - p.xo2c,
+                                 [&](int r, uint32_t piece, int rowbytes) -> char * {
+                                     const int k = div_by(r, w.nrm), rl = r - k * nr;
+                                     if (!(s.xt[(l & 1) * E + expert_at(s.sidx[t * K + k], E)] & 1)) return nullptr;
+                                     return p.landing + ((size_t)l * T * K + t * K + k) * p.xstride + p.xo2c +
+                                            piece + (size_t)(r0 + rl) * rowbytes;
+                                 });
+                    }
+                }
             }
             lds_barrier();
             if (t + 1 < T) stage_routed_down<XT>(p, l, s, t + 1, r0, nr, w.nrm);

@@ -104,11 +104,16 @@ moe_status decode_supported(const moe_shape *s, int T, int grid, bool xt = false
 moe_status decode_common(const moe_shape *s, const moe_layer *L, int32_t n_layers, uint32_t flags,
                          const uint16_t *x, int32_t T, float *y, uint16_t *x_all, float *y_all,
                          int32_t *idx_all, float *w_all, float *logits_all, void *ws, size_t ws_bytes,
-                         void *stream, const uint64_t *xtab = nullptr) {
+                         void *stream, const uint64_t *xtab = nullptr, void *landing = nullptr,
+                         size_t landing_bytes = 0) {
     moe_status st = check_shape(s);
     if (st != MOE_OK) return st;
     if ((st = check_layer(s, L, xtab == nullptr)) != MOE_OK) return st;
     if (xtab && (reinterpret_cast<uintptr_t>(xtab) & 15u)) return MOE_ERR_INVALID_ARG;
+    if (landing && (!xtab || (reinterpret_cast<uintptr_t>(landing) & 4095u) ||
+                    landing_bytes < (size_t)n_layers * T * s->top_k *
+                                        moe::expert_block(s->hidden, s->inter, s->bits).stride))
+        return MOE_ERR_INVALID_ARG;
     if (flags & ~MOE_STACK_INDEPENDENT) return MOE_ERR_INVALID_ARG;
     if (n_layers < 1 || n_layers > kMaxLayers || T < 1 || T > kMaxDecodeT) return MOE_ERR_INVALID_ARG;
     if (!x || !y || !al16(x) || !al16(y)) return MOE_ERR_INVALID_ARG;
@@ -147,6 +152,8 @@ moe_status decode_common(const moe_shape *s, const moe_layer *L, int32_t n_layer
         p.xtab = xtab;
         p.xo13s = (uint32_t)xb.o13s; p.xo13b = (uint32_t)xb.o13b;
         p.xo2c = (uint32_t)xb.o2c; p.xo2s = (uint32_t)xb.o2s; p.xo2b = (uint32_t)xb.o2b;
+        p.xstride = xb.stride;
+        p.landing = static_cast<char *>(landing);
     } else {
         p.w13 = {L->w13.codes, L->w13.scales, L->w13.biases};
         p.w2 = {L->w2.codes, L->w2.scales, L->w2.biases};
@@ -274,13 +281,15 @@ moe_status moe_stack_decode(const moe_shape *s, const moe_layer *stack, int32_t 
 }
 
 moe_status moe_stack_decode_table(const moe_shape *s, const moe_layer *stack, int32_t n_layers,
-                                  const uint64_t *expert_table, uint32_t flags, const uint16_t *x, int32_t T,
+                                  const uint64_t *expert_table, void *landing_opt, size_t landing_bytes,
+                                  uint32_t flags,
+                                  const uint16_t *x, int32_t T,
                                   float *y, uint16_t *x_all_opt, float *y_all_opt, int32_t *idx_all_opt,
                                   float *w_all_opt, float *logits_all_opt, void *ws, size_t ws_bytes,
                                   void *stream) {
     if (!expert_table) return MOE_ERR_INVALID_ARG;
     return decode_common(s, stack, n_layers, flags, x, T, y, x_all_opt, y_all_opt, idx_all_opt, w_all_opt,
-                         logits_all_opt, ws, ws_bytes, stream, expert_table);
+                         logits_all_opt, ws, ws_bytes, stream, expert_table, landing_opt, landing_bytes);
 }
 
 size_t moe_expert_stride(const moe_shape *s) {

@@ -45,8 +45,11 @@ struct DecodeParams {
     // expert-table mode: routed expert (l, e) is the fixed-stride block at xtab[l * E + e] (device
     // or device-visible host memory), pieces at these byte offsets (gate|up codes at 0); w13 and w2
     // are then unused
-    const uint64_t *xtab;
+    const uint64_t *xtab;  // bit 0 of an entry: the block is outside HBM (written through, below)
     uint32_t xo13s, xo13b, xo2c, xo2s, xo2b;
+    uint64_t xstride;      // block bytes
+    char *landing;         // or null: [L][T][K] blocks; rows staged from a marked block are stored
+                           // to the block of their (layer, token, slot)
     // workspace (zero-filled before first use)
     int *ctrl;               // [0] status, [1] call sequence number
     uint64_t *ll_start;      // [grid]               one word per workgroup: "this call has started"

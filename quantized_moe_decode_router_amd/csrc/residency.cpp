@@ -14,8 +14,11 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include <set>
 #include <tuple>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/moe.h"
@@ -84,6 +87,8 @@ struct moe_cache {
     size_t stride;
     const char *container;
     char *pool;
+    char *landing = nullptr;  // [L][T][K] blocks (T of the call) written through by the decode, or null
+    int max_tokens = 0, K = 0;
     uint64_t *table_dev;
     uint64_t *table_host;  // pinned staging of the whole table (its state after the copies)
     uint64_t *table_mid;   // pinned staging of the table while the copies run
@@ -97,7 +102,7 @@ extern "C" {
 
 moe_status moe_cache_create(const moe_shape *s, int32_t n_layers, const void *container, size_t container_bytes,
                             void *pool, size_t pool_bytes, int32_t slots, uint64_t *table, size_t table_bytes,
-                            void *stream, moe_cache **out) {
+                            void *landing_opt, size_t landing_bytes, void *stream, moe_cache **out) {
     if (!out) return MOE_ERR_INVALID_ARG;
     *out = nullptr;
     const size_t stride = moe_expert_stride(s);
@@ -109,6 +114,9 @@ moe_status moe_cache_create(const moe_shape *s, int32_t n_layers, const void *co
     if (slots > 0 && (!pool || (reinterpret_cast<uintptr_t>(pool) & 4095u) || pool_bytes < (size_t)slots * stride))
         return MOE_ERR_INVALID_ARG;
     if (!table || (reinterpret_cast<uintptr_t>(table) & 15u) || table_bytes < keys * 8) return MOE_ERR_INVALID_ARG;
+    const size_t per_token = (size_t)n_layers * s->top_k * stride;  // landing bytes per token of a call
+    if (landing_opt && ((reinterpret_cast<uintptr_t>(landing_opt) & 4095u) || landing_bytes < per_token))
+        return MOE_ERR_INVALID_ARG;
     // the kernel reads the container at the addresses the table holds: it must be device memory,
     // or pinned host memory mapped at the same address (pageable memory would fault the device)
     hipPointerAttribute_t attr;
@@ -122,6 +130,9 @@ moe_status moe_cache_create(const moe_shape *s, int32_t n_layers, const void *co
     c->container = static_cast<const char *>(container);
     c->pool = static_cast<char *>(pool);
     c->table_dev = table;
+    c->landing = static_cast<char *>(landing_opt);
+    c->K = s->top_k;
+    c->max_tokens = landing_opt ? (int)std::min<size_t>(landing_bytes / per_token, 65536) : 0;
     c->table_host = c->table_mid = nullptr;
     if (hipHostMalloc(reinterpret_cast<void **>(&c->table_host), keys * 8, hipHostMallocDefault) != hipSuccess ||
         hipHostMalloc(reinterpret_cast<void **>(&c->table_mid), keys * 8, hipHostMallocDefault) != hipSuccess) {
@@ -129,7 +140,8 @@ moe_status moe_cache_create(const moe_shape *s, int32_t n_layers, const void *co
         delete c;
         return MOE_ERR_HIP;
     }
-    for (size_t k = 0; k < keys; ++k) c->table_host[k] = reinterpret_cast<uint64_t>(c->container + k * stride);
+    const uint64_t mark = c->landing ? 1u : 0u;  // bit 0: the decode writes the block's rows through
+    for (size_t k = 0; k < keys; ++k) c->table_host[k] = reinterpret_cast<uint64_t>(c->container + k * stride) | mark;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (hipMemcpyAsync(table, c->table_host, keys * 8, hipMemcpyHostToDevice, hs) != hipSuccess ||
         hipStreamSynchronize(hs) != hipSuccess) {
@@ -146,6 +158,7 @@ moe_status moe_cache_update(moe_cache *c, const int32_t *topk_idx_all, int32_t T
                             int32_t *hits_opt, int32_t *misses_opt) {
     if (!c || !topk_idx_all || T < 1 || top_k < 1) return MOE_ERR_INVALID_ARG;
     if (c->broken) return MOE_ERR_HIP;
+    if (c->landing && (T > c->max_tokens || top_k != c->K)) return MOE_ERR_INVALID_ARG;
     const size_t n = (size_t)c->L * T * top_k;
     for (size_t i = 0; i < n; ++i)
         if (topk_idx_all[i] < 0 || topk_idx_all[i] >= c->E) return MOE_ERR_INVALID_ARG;
@@ -153,10 +166,17 @@ moe_status moe_cache_update(moe_cache *c, const int32_t *topk_idx_all, int32_t T
     // the staging table and the pool slots may still be read by work queued earlier
     if (hipStreamSynchronize(hs) != hipSuccess) return MOE_ERR_HIP;
     const std::vector<int> before = c->policy.owners();
+    std::vector<char> was_resident(c->landing ? (size_t)c->L * c->E : 0, 0);
+    if (c->landing)
+        for (int k : before)
+            if (k >= 0) was_resident[k] = 1;
+    std::unordered_map<int, size_t> first;  // key -> its first access of this call (the landing block)
     int32_t hits = 0, misses = 0;
     for (size_t i = 0; i < n; ++i) {
         const int l = (int)(i / ((size_t)T * top_k));
-        const LfuRecency::Outcome o = c->policy.access(l * c->E + topk_idx_all[i]);
+        const int key = l * c->E + topk_idx_all[i];
+        first.emplace(key, i);
+        const LfuRecency::Outcome o = c->policy.access(key);
         if (o.hit) ++hits;
         else ++misses;
     }
@@ -164,7 +184,19 @@ moe_status moe_cache_update(moe_cache *c, const int32_t *topk_idx_all, int32_t T
     c->misses += misses;
     const std::vector<int> &after = c->policy.owners();
     const size_t tbytes = (size_t)c->L * c->E * 8;
-    auto at_container = [&](int key) { return reinterpret_cast<uint64_t>(c->container + (size_t)key * c->stride); };
+    const uint64_t mark = c->landing ? 1u : 0u;
+    auto at_container = [&](int key) {
+        return reinterpret_cast<uint64_t>(c->container + (size_t)key * c->stride) | mark;
+    };
+    // an admitted expert that was outside the pool during the call has its block in the landing
+    // buffer (written through by the decode); one that was in a pool slot (evicted and re-admitted
+    // within this call) is copied from the container
+    auto source = [&](int key) -> const char * {
+        if (c->landing && !was_resident[key]) {
+            return c->landing + first.at(key) * c->stride;  // block [l][t][k] of the call's T
+        }
+        return c->container + (size_t)key * c->stride;
+    };
     // Three steps on the stream, so that the device table never names a slot being rewritten:
     // (1) every expert leaving a slot points at its container block again, (2) the admitted blocks
     // are copied into their slots, (3) the admitted experts point at their slots. If a step fails,
@@ -176,8 +208,8 @@ moe_status moe_cache_update(moe_cache *c, const int32_t *topk_idx_all, int32_t T
     if (hipMemcpyAsync(c->table_dev, c->table_mid, tbytes, hipMemcpyHostToDevice, hs) != hipSuccess) return MOE_ERR_HIP;
     for (int sl = 0; sl < c->slots; ++sl) {
         if (after[sl] == before[sl]) continue;
-        if (hipMemcpyAsync(c->pool + (size_t)sl * c->stride, c->container + (size_t)after[sl] * c->stride, c->stride,
-                           hipMemcpyDefault, hs) != hipSuccess)
+        if (hipMemcpyAsync(c->pool + (size_t)sl * c->stride, source(after[sl]), c->stride, hipMemcpyDefault, hs) !=
+            hipSuccess)
             return MOE_ERR_HIP;
         c->bytes_copied += c->stride;
     }

@@ -51,7 +51,23 @@ def _outs(shape, n_layers, T, dev):
                 logits_all=torch.empty(n_layers, T, E, dtype=torch.float32, device=dev))
 
 
-def _run(moe, shape, st, n_layers, x, T, dev, table=None, flags=0, ws=None):
+def _pieces(shape, stride):
+    """Mask of the block bytes the layout defines (the padding between pieces is unspecified)."""
+    lay = R.expert_block_layout(shape.hidden, shape.inter, shape.bits)
+    m = np.zeros(stride, dtype=bool)
+    for off, n in zip(lay["offsets"], lay["sizes"]):
+        m[off:off + n] = True
+    return m
+
+
+def _landing(shape, n_layers, T, stride, dev):
+    n = n_layers * T * shape.top_k * stride
+    buf = torch.empty(n + 4096, dtype=torch.uint8, device=dev)
+    off = (-buf.data_ptr()) % 4096
+    return buf[off:off + n]
+
+
+def _run(moe, shape, st, n_layers, x, T, dev, table=None, flags=0, ws=None, landing=None):
     o = _outs(shape, n_layers, T, dev)
     if ws is None:
         ws = moe.workspace(shape, T, moe.MOE_WS_STACK, dev, n_layers=n_layers)
@@ -59,7 +75,8 @@ def _run(moe, shape, st, n_layers, x, T, dev, table=None, flags=0, ws=None):
     if table is None:
         moe.moe_stack_decode(shape, st, n_layers, *args, workspace=ws, flags=flags)
     else:
-        moe.moe_stack_decode_table(shape, _no_routed(st), n_layers, table, *args, workspace=ws, flags=flags)
+        moe.moe_stack_decode_table(shape, _no_routed(st), n_layers, table, *args, workspace=ws, flags=flags,
+                                   landing=landing)
     assert moe.moe_read_status(ws) == 0
     return {k: v.cpu() for k, v in o.items()}
 
@@ -130,6 +147,43 @@ def test_table_decode_equals_stack_decode(name, shape, n_layers, T, where):
     print(f"{name}: identical to the stack decode over {n_layers} layers x {T} tokens")
 
 
+@pytest.mark.parametrize("name,shape,n_layers,T", [("tiny_T4", synth.TINY.shape, 3, 4),
+                                                   ("q35b_T3", synth.QWEN35B_4BIT.shape, 2, 3),
+                                                   ("q35b_8bit_T1", synth.QWEN35B_8BIT.shape, 2, 1)])
+def test_landing_blocks_hold_the_marked_experts(name, shape, n_layers, T):
+    """With every table entry marked (bit 0) and a landing buffer, the call's results are unchanged
+    and landing block [l][t][k] holds every piece of the expert that (layer, token, slot) selected;
+    unmarked entries (here the odd experts, read from HBM) write nothing."""
+    dev = need_gpu()
+    moe = _moe()
+    st = synth.make_stack(shape, n_layers, 55 + T, dev, zipf_s=0.5)
+    x = synth.make_x(shape, T, 3, device=dev)
+    want = _run(moe, shape, st, n_layers, x, T, dev)
+    _, ch, stride = _container(moe, shape, st, n_layers, "host")
+    _, cd, _ = _container(moe, shape, st, n_layers, "device")
+    E, K = shape.num_experts, shape.top_k
+    n = n_layers * E
+    keys = torch.arange(n, dtype=torch.int64)
+    odd = keys % 2 == 1
+    table = torch.where(odd, cd.data_ptr() + keys * stride, (ch.data_ptr() + keys * stride) | 1).to(dev)
+    land = _landing(shape, n_layers, T, stride, dev)
+    land.fill_(0xA5)
+    got = _run(moe, shape, st, n_layers, x, T, dev, table=table, landing=land)
+    _same(want, got)
+    idx = got["idx_all"].numpy()
+    blocks = land.cpu().numpy().reshape(n_layers, T, K, stride)
+    cont = ch.numpy().reshape(n, stride)
+    m = _pieces(shape, stride)
+    for l in range(n_layers):
+        for t in range(T):
+            for k in range(K):
+                e = int(idx[l, t, k])
+                if e % 2 == 0:
+                    assert np.array_equal(blocks[l, t, k][m], cont[l * E + e][m]), (l, t, k)
+                else:
+                    assert np.all(blocks[l, t, k] == 0xA5), (l, t, k)
+
+
 def test_table_decode_against_oracle():
     """Every layer of an unchained table decode (host container) against the fp64 oracle."""
     dev = need_gpu()
@@ -150,8 +204,9 @@ def test_table_decode_against_oracle():
         check_y(got["y_all"][l].numpy()[keep], ref["y"][keep])
 
 
-@pytest.mark.parametrize("slots_frac,T", [(0.0, 1), (0.25, 1), (0.5, 2), (1.0, 1)])
-def test_cached_decode_loop(slots_frac, T):
+@pytest.mark.parametrize("slots_frac,T,landing", [(0.0, 1, False), (0.25, 1, False), (0.5, 2, False), (1.0, 1, False),
+                                                  (0.25, 1, True), (0.5, 3, True), (0.1, 2, True)])
+def test_cached_decode_loop(slots_frac, T, landing):
     """Several decode steps through a cache over a pinned host container: each step's output is
     the all-resident decode's bit for bit, the hits and misses are the oracle policy's on the
     same routing, and every pool slot holds its owner's block."""
@@ -167,14 +222,15 @@ def test_cached_decode_loop(slots_frac, T):
     off = (-pool.data_ptr()) % 4096
     pool_v = pool[off:off + max(slots, 1) * stride]
     table = torch.empty(Lyr * E, dtype=torch.int64, device=dev)
-    cache = moe.MoeCache(shape, Lyr, c, pool_v if slots else None, slots, table)
+    land = _landing(shape, Lyr, T, stride, dev) if landing else None
+    cache = moe.MoeCache(shape, Lyr, c, pool_v if slots else None, slots, table, landing=land)
     ws_t = moe.workspace(shape, T, moe.MOE_WS_STACK, dev, n_layers=Lyr)
     keys_all = []
     try:
         for step in range(steps):
             x = synth.make_x(shape, T, 31, step=step, device=dev)
             want = _run(moe, shape, st, Lyr, x, T, dev)
-            got = _run(moe, shape, st, Lyr, x, T, dev, table=table, ws=ws_t)
+            got = _run(moe, shape, st, Lyr, x, T, dev, table=table, ws=ws_t, landing=land)
             _same(want, got)
             idx = got["idx_all"].numpy()
             keys = R.routing_keys(idx, E)
@@ -193,14 +249,15 @@ def test_cached_decode_loop(slots_frac, T):
         th = table.cpu().numpy().astype(np.uint64)
         pool_np = pool_v.cpu().numpy().reshape(-1, stride) if slots else None
         cont = c.numpy().reshape(-1, stride)
+        m = _pieces(shape, stride)
         for s, k in enumerate(owners.tolist()):
             if k >= 0:
-                assert np.array_equal(pool_np[s], cont[k]), (s, k)
+                assert np.array_equal(pool_np[s][m], cont[k][m]), (s, k)
                 assert int(th[k]) == pool_v.data_ptr() + s * stride
         resident = set(k for k in owners.tolist() if k >= 0)
         for k in range(Lyr * E):
             if k not in resident:
-                assert int(th[k]) == c.data_ptr() + k * stride
+                assert int(th[k]) == (c.data_ptr() + k * stride) | (1 if landing else 0)
         hits, misses, copied = cache.stats()
         assert hits == sum(h_o) and misses == len(h_o) - sum(h_o)
         print(f"slots {slots}: hit rate {hits / (hits + misses):.2f}, copied {copied} B")

@@ -172,14 +172,14 @@ def test_residency_host_checks(L):
     n = 2 * 256
     big = n * stride
     # out missing, slots out of range, misaligned or short container, short pool or table
-    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big, 0x20000, 4 * stride, 4, 0x30000, n * 8, None, None) == inval
-    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big, 0x20000, 4 * stride, -1, 0x30000, n * 8, None, ctypes.byref(out)) == inval
-    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big, 0x20000, 4 * stride, n + 1, 0x30000, n * 8, None, ctypes.byref(out)) == inval
-    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10008, big, 0x20000, 4 * stride, 4, 0x30000, n * 8, None, ctypes.byref(out)) == inval
-    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big - 1, 0x20000, 4 * stride, 4, 0x30000, n * 8, None, ctypes.byref(out)) == inval
-    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big, 0x20000, 4 * stride - 1, 4, 0x30000, n * 8, None, ctypes.byref(out)) == inval
-    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big, 0x20000, 4 * stride, 4, 0x30000, n * 8 - 8, None, ctypes.byref(out)) == inval
-    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big, None, 0, 4, 0x30000, n * 8, None, ctypes.byref(out)) == inval
+    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big, 0x20000, 4 * stride, 4, 0x30000, n * 8, None, 0, None, None) == inval
+    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big, 0x20000, 4 * stride, -1, 0x30000, n * 8, None, 0, None, ctypes.byref(out)) == inval
+    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big, 0x20000, 4 * stride, n + 1, 0x30000, n * 8, None, 0, None, ctypes.byref(out)) == inval
+    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10008, big, 0x20000, 4 * stride, 4, 0x30000, n * 8, None, 0, None, ctypes.byref(out)) == inval
+    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big - 1, 0x20000, 4 * stride, 4, 0x30000, n * 8, None, 0, None, ctypes.byref(out)) == inval
+    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big, 0x20000, 4 * stride - 1, 4, 0x30000, n * 8, None, 0, None, ctypes.byref(out)) == inval
+    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big, 0x20000, 4 * stride, 4, 0x30000, n * 8 - 8, None, 0, None, ctypes.byref(out)) == inval
+    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big, None, 0, 4, 0x30000, n * 8, None, 0, None, ctypes.byref(out)) == inval
     assert out.value is None
     assert L.moe_cache_update(None, None, 1, 8, None, None, None) == inval
     assert L.moe_cache_stats(None, None, None, None) == inval
@@ -191,8 +191,17 @@ def test_residency_host_checks(L):
     assert L.moe_cache_policy_run(-1, 5, keys.ctypes.data, 1, buf.ctypes.data, buf.ctypes.data, buf.ctypes.data) == inval
     # table decode without a table; packing into a misaligned or short container
     lay = binding.MoeLayer()
-    assert L.moe_stack_decode_table(ctypes.byref(s), ctypes.byref(lay), 1, None, 0, 0x1000, 1, 0x2000, None, None,
-                                    None, None, None, 0x3000, 1 << 30, None) == inval
+    assert L.moe_stack_decode_table(ctypes.byref(s), ctypes.byref(lay), 1, None, None, 0, 0, 0x1000, 1, 0x2000, None,
+                                    None, None, None, None, 0x3000, 1 << 30, None) == inval
+    # a landing buffer needs a table, 4096-byte alignment and L * T * K blocks
+    tab = 0x40000
+    for landing, lb in ((0x80000, 0), (0x80010, 1 << 40)):
+        assert L.moe_stack_decode_table(ctypes.byref(s), ctypes.byref(lay), 1, tab, landing, lb, 0, 0x1000, 1, 0x2000,
+                                        None, None, None, None, None, 0x3000, 1 << 30, None) == inval
+    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big, 0x20000, 4 * stride, 4, 0x30000, n * 8, 0x80010,
+                              1 << 40, None, ctypes.byref(out)) == inval
+    assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big, 0x20000, 4 * stride, 4, 0x30000, n * 8, 0x80000,
+                              2 * 8 * stride - 1, None, ctypes.byref(out)) == inval
     q = binding.MoeQWeight(0x1000, 0x2000, 0x3000)
     lay = binding.MoeLayer(0x4000, None, 0x5000, q, q, q, q)
     assert L.moe_pack_experts(ctypes.byref(s), ctypes.byref(lay), 1, 0x10010, big, None) == inval
