@@ -27,8 +27,11 @@
  *   S13 / S2 (shared)   : as W13 / W2 with n_exp = 1 and shared_inter in place of inter
  *
  * Conventions for every entry point:
- *   - All tensor pointers are DEVICE pointers owned by the caller; the library allocates
- *     nothing, keeps no state between calls and never synchronises the stream.
+ *   - All tensor pointers are DEVICE pointers owned by the caller (an expert container may also
+ *     be pinned host memory the device reads); the library allocates nothing, keeps no state
+ *     between calls and never synchronises the stream -- except the expert cache (moe_cache_*),
+ *     which holds host state and pinned staging from create to destroy and synchronises its
+ *     stream where its declarations say so.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work is enqueued
  *     asynchronously; results are valid once the stream reaches that point.
  *   - Arguments are checked on the host before anything is enqueued; on a failed check the
