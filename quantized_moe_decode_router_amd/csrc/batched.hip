@@ -218,13 +218,19 @@ __global__ void __launch_bounds__(kBucketThreads) bucket_kernel(BatchedParams p)
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     __syncthreads();
-    // per expert: exclusive prefix over blocks (in place) and the total
+    // per expert: exclusive prefix over blocks (in place) and the total; the counts of eight blocks
+    // are loaded before any is rewritten, so that a chunk costs one memory round trip
     for (int e = tid; e < E; e += kBucketThreads) {
         int run = 0;
-        for (int blk = 0; blk < nblk; ++blk) {
-            const int c = p.blkcnt[(size_t)blk * E + e];
-            p.blkcnt[(size_t)blk * E + e] = run;
-            run += c;
+        for (int b0 = 0; b0 < nblk; b0 += 8) {
+            int c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = b0 + i < nblk ? p.blkcnt[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (b0 + i < nblk) p.blkcnt[(size_t)(b0 + i) * E + e] = run;
+                run += c[i];
+            }
         }
         gcnt[e] = run;
     }
