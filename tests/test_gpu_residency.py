@@ -117,6 +117,7 @@ TABLE_CASES = [
     ("q35b_T1_mixed", synth.QWEN35B_4BIT.shape, 3, 1, "mixed"),
     ("q35b_T3_host", synth.QWEN35B_4BIT.shape, 2, 3, "host"),
     ("q35b_8bit_T2_mixed", synth.QWEN35B_8BIT.shape, 2, 2, "mixed"),
+    ("q80b_T2_mixed", synth.QWEN80B_4BIT.shape, 2, 2, "mixed"),
     # an odd expert count stages the table row in 4-byte units
     ("odd_e15_T2_mixed", synth.MoeShape(256, 15, 3, 128, 128, 4), 3, 2, "mixed"),
 ]
@@ -151,7 +152,8 @@ def test_table_decode_equals_stack_decode(name, shape, n_layers, T, where):
 
 @pytest.mark.parametrize("name,shape,n_layers,T", [("tiny_T4", synth.TINY.shape, 3, 4),
                                                    ("q35b_T3", synth.QWEN35B_4BIT.shape, 2, 3),
-                                                   ("q35b_8bit_T1", synth.QWEN35B_8BIT.shape, 2, 1)])
+                                                   ("q35b_8bit_T1", synth.QWEN35B_8BIT.shape, 2, 1),
+                                                   ("q80b_T2", synth.QWEN80B_4BIT.shape, 2, 2)])
 def test_landing_blocks_hold_the_marked_experts(name, shape, n_layers, T):
     """With every table entry marked (bit 0) and a landing buffer, the call's results are unchanged
     and landing block [l][t][k] holds every piece of the expert that (layer, token, slot) selected;
