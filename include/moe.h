@@ -260,7 +260,8 @@ moe_status moe_stack_decode_table(const moe_shape *shape, const moe_layer *stack
                                   float *logits_all_opt, void *workspace, size_t workspace_bytes,
                                   void *stream);
 
-/* An expert cache: host-side policy state plus a pinned staging copy of the table. Opaque. */
+/* An expert cache: host-side policy state plus pinned staging copies of the table. Opaque; not
+ * thread-safe (one caller at a time per cache). */
 typedef struct moe_cache moe_cache;
 
 /*
