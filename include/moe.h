@@ -260,6 +260,19 @@ moe_status moe_stack_decode_table(const moe_shape *shape, const moe_layer *stack
                                   float *logits_all_opt, void *workspace, size_t workspace_bytes,
                                   void *stream);
 
+/*
+ * moe_layer_batched with the routed experts read through one layer's row of an expert table
+ * (uint64 [E], device memory, 8-byte aligned, entries as for moe_stack_decode_table, bit 0
+ * ignored) instead of layer->w13 and layer->w2 (which may then be NULL). For prefill or batched
+ * decode of a stack that lives in a container: blocks outside HBM are read over the bus as the
+ * grouped GEMMs load them. Results are bit for bit those of moe_layer_batched.
+ */
+moe_status moe_layer_batched_table(const moe_shape *shape, const moe_layer *layer,
+                                   const uint64_t *expert_table, const uint16_t *x, int32_t T,
+                                   float *y, int32_t *topk_idx_opt, float *topk_w_opt,
+                                   float *logits_opt, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
 /* An expert cache: host-side policy state plus pinned staging copies of the table. Opaque; not
  * thread-safe (one caller at a time per cache). */
 typedef struct moe_cache moe_cache;

@@ -8,4 +8,5 @@ from .binding import (MOE_DEFAULT_CROSSOVER, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, M
                       MOE_WS_FORWARD, MOE_WS_STACK, MoeError, lib, moe_group_pairs, moe_layer_batched,
                       moe_layer_decode, moe_layer_forward, moe_layer_path, moe_read_status, moe_route,
                       moe_stack_decode, moe_workspace_bytes, status_string, workspace, MoeCache,
-                      moe_cache_policy_run, moe_expert_stride, moe_pack_experts, moe_stack_decode_table)
+                      moe_cache_policy_run, moe_expert_stride, moe_layer_batched_table, moe_pack_experts,
+                      moe_stack_decode_table)

@@ -32,7 +32,7 @@ MOE_STACK_INDEPENDENT = 1
 
 EXPORTED = ("moe_route", "moe_layer_decode", "moe_stack_decode", "moe_layer_batched", "moe_group_pairs",
             "moe_layer_path", "moe_layer_forward", "moe_workspace_bytes", "moe_read_status", "moe_status_string",
-            "moe_expert_stride", "moe_pack_experts", "moe_stack_decode_table", "moe_cache_create",
+            "moe_expert_stride", "moe_pack_experts", "moe_stack_decode_table", "moe_layer_batched_table", "moe_cache_create",
             "moe_cache_update", "moe_cache_stats", "moe_cache_owners", "moe_cache_destroy", "moe_cache_policy_run")
 
 
@@ -78,6 +78,7 @@ def lib():
         L.moe_layer_forward.argtypes = [PS, PL, P, I32, I32, P, P, P, P, P, SZ, P]
         L.moe_stack_decode.argtypes = [PS, PL, I32, U32, P, I32, P, P, P, P, P, P, P, SZ, P]
         L.moe_stack_decode_table.argtypes = [PS, PL, I32, P, P, SZ, U32, P, I32, P, P, P, P, P, P, P, SZ, P]
+        L.moe_layer_batched_table.argtypes = [PS, PL, P, P, I32, P, P, P, P, P, SZ, P]
         L.moe_expert_stride.argtypes = [PS]
         L.moe_expert_stride.restype = SZ
         L.moe_pack_experts.argtypes = [PS, PL, I32, P, SZ, P]
@@ -284,6 +285,19 @@ def moe_stack_decode_table(shape, stack, n_layers: int, expert_table, x, T: int,
                                       _ptr(logits_all, "logits_all", torch.float32), _ptr(workspace, "workspace"),
                                       int(wsb), _stream(stream))
     _check(st, "moe_stack_decode_table")
+
+
+def moe_layer_batched_table(shape, layer, expert_table, x, T: int, y, topk_idx=None, topk_w=None, logits=None,
+                            workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+    s, L = shape_struct(shape), layer_struct(layer)
+    wsb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    st = lib().moe_layer_batched_table(ctypes.byref(s), ctypes.byref(L),
+                                       _ptr(expert_table, "expert_table", (torch.int64, torch.uint64)),
+                                       _ptr(x, "x", _BF16_BITS), int(T), _ptr(y, "y", torch.float32),
+                                       _ptr(topk_idx, "topk_idx", torch.int32), _ptr(topk_w, "topk_w", torch.float32),
+                                       _ptr(logits, "logits", torch.float32), _ptr(workspace, "workspace"), int(wsb),
+                                       _stream(stream))
+    _check(st, "moe_layer_batched_table")
 
 
 class MoeCache:

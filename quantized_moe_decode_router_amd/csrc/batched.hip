@@ -294,6 +294,11 @@ struct GroupW {
 // Weights of group g of a matrix family: routed expert g < E, or the shared expert (g == E).
 __device__ __forceinline__ GroupW group_w13(const BatchedParams &p, int g) {
     const size_t H = p.H;
+    if (g < p.E && p.xtab) {
+        const uint64_t blk = p.xtab[g] & ~1ull;
+        return {reinterpret_cast<const uint8_t *>(blk), reinterpret_cast<const uint16_t *>(blk + p.xo13s),
+                reinterpret_cast<const uint16_t *>(blk + p.xo13b), p.I};
+    }
     if (g < p.E) {
         const size_t rows = 2 * (size_t)p.I;
         return {p.w13.c + g * rows * H * p.bits / 8, p.w13.s + g * rows * (H / 64), p.w13.b + g * rows * (H / 64),
@@ -303,6 +308,11 @@ __device__ __forceinline__ GroupW group_w13(const BatchedParams &p, int g) {
 }
 __device__ __forceinline__ GroupW group_w2(const BatchedParams &p, int g) {
     const size_t H = p.H;
+    if (g < p.E && p.xtab) {
+        const uint64_t blk = p.xtab[g] & ~1ull;
+        return {reinterpret_cast<const uint8_t *>(blk + p.xo2c), reinterpret_cast<const uint16_t *>(blk + p.xo2s),
+                reinterpret_cast<const uint16_t *>(blk + p.xo2b), p.I};
+    }
     if (g < p.E) {
         const size_t cols = p.I;
         return {p.w2.c + g * H * cols * p.bits / 8, p.w2.s + g * H * (cols / 64), p.w2.b + g * H * (cols / 64), p.I};

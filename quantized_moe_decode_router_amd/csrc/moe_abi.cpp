@@ -325,12 +325,14 @@ moe_status moe_pack_experts(const moe_shape *s, const moe_layer *stack, int32_t 
     return MOE_OK;
 }
 
-moe_status moe_layer_batched(const moe_shape *s, const moe_layer *L, const uint16_t *x, int32_t T,
-                             float *y, int32_t *topk_idx_opt, float *topk_w_opt, float *logits_opt,
-                             void *ws, size_t ws_bytes, void *stream) {
+namespace {
+moe_status batched_common(const moe_shape *s, const moe_layer *L, const uint16_t *x, int32_t T, float *y,
+                          int32_t *topk_idx_opt, float *topk_w_opt, float *logits_opt, void *ws, size_t ws_bytes,
+                          void *stream, const uint64_t *xtab) {
     moe_status st = check_shape(s);
     if (st != MOE_OK) return st;
-    if ((st = check_layer(s, L)) != MOE_OK) return st;
+    if ((st = check_layer(s, L, xtab == nullptr)) != MOE_OK) return st;
+    if (xtab && (reinterpret_cast<uintptr_t>(xtab) & 7u)) return MOE_ERR_INVALID_ARG;
     if (T < 1 || T > kMaxBatchT) return MOE_ERR_INVALID_ARG;
     if (!x || !y || !al16(x) || !al16(y)) return MOE_ERR_INVALID_ARG;
     if ((topk_idx_opt && !al4(topk_idx_opt)) || (topk_w_opt && !al4(topk_w_opt)) ||
@@ -348,8 +350,15 @@ moe_status moe_layer_batched(const moe_shape *s, const moe_layer *L, const uint1
     p.x = x;
     p.router = L->router; p.rbias = L->router_bias;
     p.sgate = p.Is ? L->shared_gate : nullptr;
-    p.w13 = {L->w13.codes, L->w13.scales, L->w13.biases};
-    p.w2 = {L->w2.codes, L->w2.scales, L->w2.biases};
+    if (xtab) {
+        const moe::ExpertBlock xb = moe::expert_block(s->hidden, s->inter, s->bits);
+        p.xtab = xtab;
+        p.xo13s = (uint32_t)xb.o13s; p.xo13b = (uint32_t)xb.o13b;
+        p.xo2c = (uint32_t)xb.o2c; p.xo2s = (uint32_t)xb.o2s; p.xo2b = (uint32_t)xb.o2b;
+    } else {
+        p.w13 = {L->w13.codes, L->w13.scales, L->w13.biases};
+        p.w2 = {L->w2.codes, L->w2.scales, L->w2.biases};
+    }
     if (p.Is) {
         p.s13 = {L->s13.codes, L->s13.scales, L->s13.biases};
         p.s2 = {L->s2.codes, L->s2.scales, L->s2.biases};
@@ -376,6 +385,22 @@ moe_status moe_layer_batched(const moe_shape *s, const moe_layer *L, const uint1
     p.y = y;
     hipError_t err = moe::launch_batched(p, lay.max_tiles, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+}  // namespace
+
+moe_status moe_layer_batched(const moe_shape *s, const moe_layer *L, const uint16_t *x, int32_t T,
+                             float *y, int32_t *topk_idx_opt, float *topk_w_opt, float *logits_opt,
+                             void *ws, size_t ws_bytes, void *stream) {
+    return batched_common(s, L, x, T, y, topk_idx_opt, topk_w_opt, logits_opt, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_layer_batched_table(const moe_shape *s, const moe_layer *L, const uint64_t *expert_table,
+                                   const uint16_t *x, int32_t T, float *y, int32_t *topk_idx_opt,
+                                   float *topk_w_opt, float *logits_opt, void *ws, size_t ws_bytes,
+                                   void *stream) {
+    if (!expert_table) return MOE_ERR_INVALID_ARG;
+    return batched_common(s, L, x, T, y, topk_idx_opt, topk_w_opt, logits_opt, ws, ws_bytes, stream,
+                          expert_table);
 }
 
 int32_t moe_layer_path(const moe_shape *s, int32_t T, int32_t crossover) {

@@ -208,6 +208,10 @@ struct BatchedParams {
     float *y;           // [T][H]
     uint16_t *rhi, *rlo;  // [E+1][H] bf16 hi / lo halves of the router rows (row E = shared gate)
     float *lpart;         // [kRouterSplitK][T][E+1] router partial sums over quarters of H
+    // expert-table mode: routed expert e is the fixed-stride block at xtab[e] (bit 0 ignored),
+    // pieces at these byte offsets (gate|up codes at 0); w13 and w2 are then unused
+    const uint64_t *xtab;
+    uint32_t xo13s, xo13b, xo2c, xo2s, xo2b;
 };
 // The batched router GEMM splits H into this many contiguous ranges (fewer when H has fewer
 // 64-column steps); the top-k kernel adds the partial sums in range order.

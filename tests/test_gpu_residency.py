@@ -188,6 +188,48 @@ def test_landing_blocks_hold_the_marked_experts(name, shape, n_layers, T):
                     assert np.all(blocks[l, t, k] == 0xA5), (l, t, k)
 
 
+BATCHED_TABLE_CASES = [
+    ("tiny_T33_mixed", synth.TINY.shape, 33, "mixed", None),
+    ("q35b_T128_host_zipf", synth.QWEN35B_4BIT.shape, 128, "host", 1.1),
+    ("q35b_8bit_T64_mixed", synth.QWEN35B_8BIT.shape, 64, "mixed", None),
+    ("q80b_T40_mixed", synth.QWEN80B_4BIT.shape, 40, "mixed", 0.5),
+]
+
+
+@pytest.mark.parametrize("name,shape,T,where,zipf", BATCHED_TABLE_CASES, ids=[c[0] for c in BATCHED_TABLE_CASES])
+def test_batched_table_equals_batched(name, shape, T, where, zipf):
+    """The batched layer with its routed experts read through a table row (pinned host memory,
+    or alternating host and device blocks) gives moe_layer_batched's outputs bit for bit."""
+    dev = need_gpu()
+    moe = _moe()
+    st = synth.make_stack(shape, 1, 31 + T, dev, zipf_s=zipf)
+    x = synth.make_x(shape, T, 13, device=dev)
+    E, K = shape.num_experts, shape.top_k
+    _, ch, stride = _container(moe, shape, st, 1, "host")
+    keys = torch.arange(E, dtype=torch.int64)
+    if where == "mixed":
+        _, cd, _ = _container(moe, shape, st, 1, "device")
+        table = torch.where(keys % 2 == 0, ch.data_ptr() + keys * stride, cd.data_ptr() + keys * stride).to(dev)
+    else:
+        table = (ch.data_ptr() + keys * stride).to(dev)
+    outs = []
+    for use_table in (False, True):
+        y = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
+        idx = torch.empty(T, K, dtype=torch.int32, device=dev)
+        w = torch.empty(T, K, dtype=torch.float32, device=dev)
+        lg = torch.empty(T, E, dtype=torch.float32, device=dev)
+        ws = moe.workspace(shape, T, moe.MOE_WS_BATCHED, dev)
+        if use_table:
+            moe.moe_layer_batched_table(shape, _no_routed(st).layer(0), table, x, T, y, idx, w, lg, workspace=ws)
+        else:
+            moe.moe_layer_batched(shape, st.layer(0), x, T, y, idx, w, lg, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (y, idx, w, lg)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    print(f"{name}: identical to moe_layer_batched")
+
+
 def test_table_decode_against_oracle():
     """Every layer of an unchained table decode (host container) against the fp64 oracle."""
     dev = need_gpu()

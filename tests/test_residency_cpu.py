@@ -193,6 +193,8 @@ def test_residency_host_checks(L):
     lay = binding.MoeLayer()
     assert L.moe_stack_decode_table(ctypes.byref(s), ctypes.byref(lay), 1, None, None, 0, 0, 0x1000, 1, 0x2000, None,
                                     None, None, None, None, 0x3000, 1 << 30, None) == inval
+    assert L.moe_layer_batched_table(ctypes.byref(s), ctypes.byref(lay), None, 0x1000, 4, 0x2000, None, None, None,
+                                     0x3000, 1 << 30, None) == inval
     # a landing buffer needs a table, 4096-byte alignment and L * T * K blocks
     tab = 0x40000
     for landing, lb in ((0x80000, 0), (0x80010, 1 << 40)):
