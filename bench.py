@@ -310,10 +310,35 @@ def residency_sweep(stack, wl, warmup: int, steps: int, zipf_s):
                        "copied_mb_per_token": round(copied / steps / 1e6, 1)}
                 rows.append(row)
                 print(f"[residency] {row}", file=sys.stderr, flush=True)
+        # prefill through the table: one batched layer (T = 512, Zipf(1.1) router bias) with every
+        # routed block read from the pinned container, against the same layer resident in HBM
+        Tb = 512
+        stb = synth.with_zipf_bias(stack, wl.seed, 1.1)
+        nob = dataclasses.replace(stb, w13_codes=None, w13_scales=None, w13_biases=None, w2_codes=None,
+                                  w2_scales=None, w2_biases=None)
+        xb = synth.make_x(shape, Tb, wl.seed, step=1 << 16, device=dev)
+        yb = torch.empty(Tb, shape.hidden, dtype=torch.float32, device=dev)
+        wsb = moe.workspace(shape, Tb, moe.MOE_WS_BATCHED, dev)
+        row0 = (base + torch.arange(E, dtype=torch.int64, device=dev) * stride).contiguous()
+        prefill = {}
+        for name, fn in (("resident", lambda: moe.moe_layer_batched(shape, stb.layer(0), xb, Tb, yb, workspace=wsb,
+                                                                      stream=stream)),
+                         ("from_host", lambda: moe.moe_layer_batched_table(shape, nob.layer(0), row0, xb, Tb, yb,
+                                                                            workspace=wsb, stream=stream))):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(10):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            prefill[name + "_us_per_layer"] = round(a.elapsed_time(b) * 100, 1)
+        print(f"[residency] prefill layer T=512: {prefill}", file=sys.stderr, flush=True)
     finally:
         torch.cuda.synchronize()
         hip.hipHostFree(hbuf)
-    return {"workload": wl.name, "resident_kernel_ms": round(resident_ms, 3), "table_all_hbm_kernel_ms": round(table_hbm_ms, 3), "expert_stride": stride, "container_gb": round(nbytes / 1e9, 2),
+    return {"workload": wl.name, "resident_kernel_ms": round(resident_ms, 3), "table_all_hbm_kernel_ms": round(table_hbm_ms, 3), "prefill_T512": prefill, "expert_stride": stride, "container_gb": round(nbytes / 1e9, 2),
             "warmup": warmup, "steps": steps, "rows": rows}
 
 
