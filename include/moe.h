@@ -309,6 +309,15 @@ moe_status moe_cache_create(const moe_shape *shape, int32_t n_layers, const void
 moe_status moe_cache_update(moe_cache *cache, const int32_t *topk_idx_all, int32_t T, int32_t top_k,
                             void *stream, int32_t *hits_opt, int32_t *misses_opt);
 
+/*
+ * Feeds n keys (host int32, each l * E + e) through the policy as accesses, then queues on
+ * `stream` the admitted blocks' copies from the container and the table rewrite, as
+ * moe_cache_update does (and synchronises `stream` first). For bringing in what a call is about
+ * to read, e.g. the experts a prefill layer's routing selects before moe_layer_batched_table.
+ */
+moe_status moe_cache_admit(moe_cache *cache, const int32_t *keys, int64_t n, void *stream,
+                           int32_t *hits_opt, int32_t *misses_opt);
+
 /* Totals since creation: accesses that hit, that missed, and bytes copied into the pool. */
 moe_status moe_cache_stats(const moe_cache *cache, uint64_t *hits, uint64_t *misses,
                            uint64_t *bytes_copied);

@@ -33,7 +33,7 @@ MOE_STACK_INDEPENDENT = 1
 EXPORTED = ("moe_route", "moe_layer_decode", "moe_stack_decode", "moe_layer_batched", "moe_group_pairs",
             "moe_layer_path", "moe_layer_forward", "moe_workspace_bytes", "moe_read_status", "moe_status_string",
             "moe_expert_stride", "moe_pack_experts", "moe_stack_decode_table", "moe_layer_batched_table", "moe_cache_create",
-            "moe_cache_update", "moe_cache_stats", "moe_cache_owners", "moe_cache_destroy", "moe_cache_policy_run")
+            "moe_cache_update", "moe_cache_admit", "moe_cache_stats", "moe_cache_owners", "moe_cache_destroy", "moe_cache_policy_run")
 
 
 class MoeError(RuntimeError):
@@ -84,6 +84,7 @@ def lib():
         L.moe_pack_experts.argtypes = [PS, PL, I32, P, SZ, P]
         L.moe_cache_create.argtypes = [PS, I32, P, SZ, P, SZ, I32, P, SZ, P, SZ, P, ctypes.POINTER(P)]
         L.moe_cache_update.argtypes = [P, P, I32, I32, P, ctypes.POINTER(I32), ctypes.POINTER(I32)]
+        L.moe_cache_admit.argtypes = [P, P, ctypes.c_int64, P, ctypes.POINTER(I32), ctypes.POINTER(I32)]
         U64P = ctypes.POINTER(ctypes.c_uint64)
         L.moe_cache_stats.argtypes = [P, U64P, U64P, U64P]
         L.moe_cache_owners.argtypes = [P, P]
@@ -326,6 +327,15 @@ class MoeCache:
         st = lib().moe_cache_update(self._h, a.ctypes.data, int(T), int(top_k), _stream(stream), ctypes.byref(h),
                                     ctypes.byref(m))
         _check(st, "moe_cache_update")
+        return int(h.value), int(m.value)
+
+    def admit(self, keys, stream=None):
+        """Feed keys (l * E + e) through the policy and admit them; returns (hits, misses)."""
+        k = np.ascontiguousarray(keys, dtype=np.int32)
+        h, m = ctypes.c_int32(0), ctypes.c_int32(0)
+        st = lib().moe_cache_admit(self._h, k.ctypes.data if k.size else None, int(k.size), _stream(stream),
+                                   ctypes.byref(h), ctypes.byref(m))
+        _check(st, "moe_cache_admit")
         return int(h.value), int(m.value)
 
     def stats(self):

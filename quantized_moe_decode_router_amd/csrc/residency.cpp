@@ -98,6 +98,72 @@ struct moe_cache {
     moe_cache(int L_, int E_, int slots_) : L(L_), E(E_), slots(slots_), policy(slots_, L_ * E_) {}
 };
 
+namespace {
+// Feeds n keys through the policy, then queues the admissions' copies and the table rewrite on
+// hs (which the caller has synchronised). from_landing: access i was read by the decode call
+// whose routing this is, so a block outside the pool during that call is at landing block i.
+moe_status apply_keys(moe_cache *c, const int *keys, size_t n, hipStream_t hs, bool from_landing,
+                      int32_t *hits_opt, int32_t *misses_opt) {
+    const std::vector<int> before = c->policy.owners();
+    std::vector<char> was_resident(from_landing ? (size_t)c->L * c->E : 0, 0);
+    if (from_landing)
+        for (int k : before)
+            if (k >= 0) was_resident[k] = 1;
+    std::unordered_map<int, size_t> first;  // key -> its first access of this call (the landing block)
+    int32_t hits = 0, misses = 0;
+    for (size_t i = 0; i < n; ++i) {
+        const int key = keys[i];
+        first.emplace(key, i);
+        const LfuRecency::Outcome o = c->policy.access(key);
+        if (o.hit) ++hits;
+        else ++misses;
+    }
+    c->hits += hits;
+    c->misses += misses;
+    const std::vector<int> &after = c->policy.owners();
+    const size_t tbytes = (size_t)c->L * c->E * 8;
+    const uint64_t mark = c->landing ? 1u : 0u;
+    auto at_container = [&](int key) {
+        return reinterpret_cast<uint64_t>(c->container + (size_t)key * c->stride) | mark;
+    };
+    // an admitted expert that was outside the pool during the call has its block in the landing
+    // buffer (written through by the decode); one that was in a pool slot (evicted and re-admitted
+    // within this call) is copied from the container
+    auto source = [&](int key) -> const char * {
+        if (from_landing && !was_resident[key]) {
+            return c->landing + first.at(key) * c->stride;  // block [l][t][k] of the call's T
+        }
+        return c->container + (size_t)key * c->stride;
+    };
+    // Three steps on the stream, so that the device table never names a slot being rewritten:
+    // (1) every expert leaving a slot points at its container block again, (2) the admitted blocks
+    // are copied into their slots, (3) the admitted experts point at their slots. If a step fails,
+    // the table on the device is (1)'s and the cache refuses further updates.
+    for (int sl = 0; sl < c->slots; ++sl)
+        if (after[sl] != before[sl] && before[sl] >= 0) c->table_host[before[sl]] = at_container(before[sl]);
+    memcpy(c->table_mid, c->table_host, tbytes);
+    c->broken = true;
+    if (hipMemcpyAsync(c->table_dev, c->table_mid, tbytes, hipMemcpyHostToDevice, hs) != hipSuccess) return MOE_ERR_HIP;
+    for (int sl = 0; sl < c->slots; ++sl) {
+        if (after[sl] == before[sl]) continue;
+        if (hipMemcpyAsync(c->pool + (size_t)sl * c->stride, source(after[sl]), c->stride, hipMemcpyDefault, hs) !=
+            hipSuccess)
+            return MOE_ERR_HIP;
+        c->bytes_copied += c->stride;
+    }
+    // a key evicted from one slot may have been admitted into another within the same call
+    for (int sl = 0; sl < c->slots; ++sl)
+        if (after[sl] >= 0) c->table_host[after[sl]] = reinterpret_cast<uint64_t>(c->pool + (size_t)sl * c->stride);
+    if (hipMemcpyAsync(c->table_dev, c->table_host, tbytes, hipMemcpyHostToDevice, hs) != hipSuccess)
+        return MOE_ERR_HIP;
+    c->broken = false;
+    if (hits_opt) *hits_opt = hits;
+    if (misses_opt) *misses_opt = misses;
+    return MOE_OK;
+}
+}  // namespace
+
+
 extern "C" {
 
 moe_status moe_cache_create(const moe_shape *s, int32_t n_layers, const void *container, size_t container_bytes,
@@ -162,66 +228,23 @@ moe_status moe_cache_update(moe_cache *c, const int32_t *topk_idx_all, int32_t T
     const size_t n = (size_t)c->L * T * top_k;
     for (size_t i = 0; i < n; ++i)
         if (topk_idx_all[i] < 0 || topk_idx_all[i] >= c->E) return MOE_ERR_INVALID_ARG;
+    std::vector<int> keys(n);
+    for (size_t i = 0; i < n; ++i) keys[i] = (int)(i / ((size_t)T * top_k)) * c->E + topk_idx_all[i];
     hipStream_t hs = static_cast<hipStream_t>(stream);
     // the staging table and the pool slots may still be read by work queued earlier
     if (hipStreamSynchronize(hs) != hipSuccess) return MOE_ERR_HIP;
-    const std::vector<int> before = c->policy.owners();
-    std::vector<char> was_resident(c->landing ? (size_t)c->L * c->E : 0, 0);
-    if (c->landing)
-        for (int k : before)
-            if (k >= 0) was_resident[k] = 1;
-    std::unordered_map<int, size_t> first;  // key -> its first access of this call (the landing block)
-    int32_t hits = 0, misses = 0;
-    for (size_t i = 0; i < n; ++i) {
-        const int l = (int)(i / ((size_t)T * top_k));
-        const int key = l * c->E + topk_idx_all[i];
-        first.emplace(key, i);
-        const LfuRecency::Outcome o = c->policy.access(key);
-        if (o.hit) ++hits;
-        else ++misses;
-    }
-    c->hits += hits;
-    c->misses += misses;
-    const std::vector<int> &after = c->policy.owners();
-    const size_t tbytes = (size_t)c->L * c->E * 8;
-    const uint64_t mark = c->landing ? 1u : 0u;
-    auto at_container = [&](int key) {
-        return reinterpret_cast<uint64_t>(c->container + (size_t)key * c->stride) | mark;
-    };
-    // an admitted expert that was outside the pool during the call has its block in the landing
-    // buffer (written through by the decode); one that was in a pool slot (evicted and re-admitted
-    // within this call) is copied from the container
-    auto source = [&](int key) -> const char * {
-        if (c->landing && !was_resident[key]) {
-            return c->landing + first.at(key) * c->stride;  // block [l][t][k] of the call's T
-        }
-        return c->container + (size_t)key * c->stride;
-    };
-    // Three steps on the stream, so that the device table never names a slot being rewritten:
-    // (1) every expert leaving a slot points at its container block again, (2) the admitted blocks
-    // are copied into their slots, (3) the admitted experts point at their slots. If a step fails,
-    // the table on the device is (1)'s and the cache refuses further updates.
-    for (int sl = 0; sl < c->slots; ++sl)
-        if (after[sl] != before[sl] && before[sl] >= 0) c->table_host[before[sl]] = at_container(before[sl]);
-    memcpy(c->table_mid, c->table_host, tbytes);
-    c->broken = true;
-    if (hipMemcpyAsync(c->table_dev, c->table_mid, tbytes, hipMemcpyHostToDevice, hs) != hipSuccess) return MOE_ERR_HIP;
-    for (int sl = 0; sl < c->slots; ++sl) {
-        if (after[sl] == before[sl]) continue;
-        if (hipMemcpyAsync(c->pool + (size_t)sl * c->stride, source(after[sl]), c->stride, hipMemcpyDefault, hs) !=
-            hipSuccess)
-            return MOE_ERR_HIP;
-        c->bytes_copied += c->stride;
-    }
-    // a key evicted from one slot may have been admitted into another within the same call
-    for (int sl = 0; sl < c->slots; ++sl)
-        if (after[sl] >= 0) c->table_host[after[sl]] = reinterpret_cast<uint64_t>(c->pool + (size_t)sl * c->stride);
-    if (hipMemcpyAsync(c->table_dev, c->table_host, tbytes, hipMemcpyHostToDevice, hs) != hipSuccess)
-        return MOE_ERR_HIP;
-    c->broken = false;
-    if (hits_opt) *hits_opt = hits;
-    if (misses_opt) *misses_opt = misses;
-    return MOE_OK;
+    return apply_keys(c, keys.data(), n, hs, c->landing != nullptr, hits_opt, misses_opt);
+}
+
+moe_status moe_cache_admit(moe_cache *c, const int32_t *keys, int64_t n, void *stream, int32_t *hits_opt,
+                           int32_t *misses_opt) {
+    if (!c || n < 0 || (n > 0 && !keys)) return MOE_ERR_INVALID_ARG;
+    if (c->broken) return MOE_ERR_HIP;
+    for (int64_t i = 0; i < n; ++i)
+        if (keys[i] < 0 || keys[i] >= c->L * c->E) return MOE_ERR_INVALID_ARG;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (hipStreamSynchronize(hs) != hipSuccess) return MOE_ERR_HIP;
+    return apply_keys(c, keys, (size_t)n, hs, false, hits_opt, misses_opt);
 }
 
 moe_status moe_cache_stats(const moe_cache *c, uint64_t *hits, uint64_t *misses, uint64_t *bytes_copied) {

@@ -230,6 +230,56 @@ def test_batched_table_equals_batched(name, shape, T, where, zipf):
     print(f"{name}: identical to moe_layer_batched")
 
 
+def test_prefill_admits_the_routed_experts_first():
+    """Prefill of one layer from a pinned container: route, admit the selected experts into the
+    pool (moe_cache_admit), then the batched layer through the rewritten table: its outputs are
+    moe_layer_batched's bit for bit, the pool holds the admitted blocks, and the policy's
+    decisions match the oracle's on the same keys."""
+    dev = need_gpu()
+    moe = _moe()
+    shape = synth.QWEN35B_4BIT.shape
+    T, E, K = 96, shape.num_experts, shape.top_k
+    st = synth.make_stack(shape, 1, 4242, dev, zipf_s=1.1)
+    x = synth.make_x(shape, T, 21, device=dev)
+    _, c, stride = _container(moe, shape, st, 1, "host")
+    slots = 48
+    pool = torch.empty(slots * stride + 4096, dtype=torch.uint8, device=dev)
+    off = (-pool.data_ptr()) % 4096
+    pool_v = pool[off:off + slots * stride]
+    table = torch.empty(E, dtype=torch.int64, device=dev)
+    cache = moe.MoeCache(shape, 1, c, pool_v, slots, table)
+    try:
+        lg = torch.empty(T, E, dtype=torch.float32, device=dev)
+        idx = torch.empty(T, K, dtype=torch.int32, device=dev)
+        w = torch.empty(T, K, dtype=torch.float32, device=dev)
+        moe.moe_route(shape, st.layer(0), x, T, lg, idx, w)
+        keys = np.unique(idx.cpu().numpy())
+        hits, misses = cache.admit(keys)
+        want_hit, want_slot, _ = R.lfu_recency(slots, keys)
+        assert (hits, misses) == (sum(want_hit), len(keys) - sum(want_hit))
+        outs = []
+        for use_table in (False, True):
+            y = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
+            ws = moe.workspace(shape, T, moe.MOE_WS_BATCHED, dev)
+            if use_table:
+                moe.moe_layer_batched_table(shape, _no_routed(st).layer(0), table, x, T, y, workspace=ws)
+            else:
+                moe.moe_layer_batched(shape, st.layer(0), x, T, y, workspace=ws)
+            torch.cuda.synchronize()
+            outs.append(y.cpu())
+        assert torch.equal(outs[0], outs[1])
+        owners = cache.owners()
+        m = _pieces(shape, stride)
+        pool_np = pool_v.cpu().numpy().reshape(slots, stride)
+        cont = c.numpy().reshape(E, stride)
+        for s_, k in enumerate(owners.tolist()):
+            if k >= 0:
+                assert np.array_equal(pool_np[s_][m], cont[k][m]), (s_, k)
+        print(f"admitted {misses} of {len(keys)} selected experts into {slots} slots")
+    finally:
+        cache.close()
+
+
 def test_table_decode_against_oracle():
     """Every layer of an unchained table decode (host container) against the fp64 oracle."""
     dev = need_gpu()

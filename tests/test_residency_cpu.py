@@ -182,6 +182,7 @@ def test_residency_host_checks(L):
     assert L.moe_cache_create(ctypes.byref(s), 2, 0x10000, big, None, 0, 4, 0x30000, n * 8, None, 0, None, ctypes.byref(out)) == inval
     assert out.value is None
     assert L.moe_cache_update(None, None, 1, 8, None, None, None) == inval
+    assert L.moe_cache_admit(None, None, 0, None, None, None) == inval
     assert L.moe_cache_stats(None, None, None, None) == inval
     assert L.moe_cache_owners(None, None) == inval
     L.moe_cache_destroy(None)
