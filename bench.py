@@ -374,6 +374,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="tokens per decode step (1..8; default: the workload's own, 1)")
     ap.add_argument("--workload", default=synth.QWEN35B_4BIT.name,
                     choices=[w.name for w in synth.ALL.values() if w.tokens <= 8 and w.n_layers > 1])
     ap.add_argument("--independent", action="store_true",
@@ -401,6 +403,8 @@ def main():
     dev = torch.device("cuda:0")
     wl = synth.ALL[args.workload]
     shape, T, L = wl.shape, wl.tokens, wl.n_layers
+    if args.tokens:
+        T = args.tokens
     t0 = time.perf_counter()
     stack = synth.make_workload(wl, dev)
     torch.cuda.synchronize()
