@@ -151,6 +151,7 @@ def test_table_decode_equals_stack_decode(name, shape, n_layers, T, where):
 
 
 @pytest.mark.parametrize("name,shape,n_layers,T", [("tiny_T4", synth.TINY.shape, 3, 4),
+                                                   ("tiny_T8", synth.TINY.shape, 2, 8),
                                                    ("q35b_T3", synth.QWEN35B_4BIT.shape, 2, 3),
                                                    ("q35b_8bit_T1", synth.QWEN35B_8BIT.shape, 2, 1),
                                                    ("q80b_T2", synth.QWEN80B_4BIT.shape, 2, 2)])
@@ -301,7 +302,7 @@ def test_table_decode_against_oracle():
 
 
 @pytest.mark.parametrize("slots_frac,T,landing", [(0.0, 1, False), (0.25, 1, False), (0.5, 2, False), (1.0, 1, False),
-                                                  (0.25, 1, True), (0.5, 3, True), (0.1, 2, True)])
+                                                  (0.25, 1, True), (0.5, 3, True), (0.1, 2, True), (1.0, 8, True)])
 def test_cached_decode_loop(slots_frac, T, landing):
     """Several decode steps through a cache over a pinned host container: each step's output is
     the all-resident decode's bit for bit, the hits and misses are the oracle policy's on the
