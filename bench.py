@@ -51,18 +51,12 @@ def recorded_traffic(workload: str, kernel: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(stack, wl, budget_s: float):
-    """The oracle as it stands, on this host's cores, on a bounded sample: the first
-    `n` layers of the same stack, tokens chained through them until ~budget_s has elapsed."""
+def _oracle_rate(layers, wl, budget_s: float):
+    """Layer-tokens per second of the oracle on `layers`, tokens chained through them."""
     import numpy as np
     import torch
 
     import oracle
-    from tests.helpers import host_layer
-
-    n = min(8, wl.n_layers)
-    layers = [host_layer(stack, l) for l in range(n)]
-    threads = oracle.num_threads()
     import synth
     layer_tokens = 0
     tokens = 0
@@ -77,17 +71,39 @@ def cpu_baseline(stack, wl, budget_s: float):
         el = time.perf_counter() - t0
         if el >= budget_s and tokens >= 2:
             break
-    per_layer_token = el / layer_tokens
-    return {"value": 1.0 / (per_layer_token * wl.n_layers), "unit": "tokens/s", "cores": threads,
+    return layer_tokens / el, tokens, el
+
+
+def cpu_baseline(stack, wl, budget_s: float):
+    """The oracle as it stands, on this host's cores (every core, then one thread), on a bounded
+    sample: the first `n` layers of the same stack, tokens chained through them for ~budget_s each;
+    tokens/s = 1 / (time per layer-token x the stack's layers)."""
+    import oracle
+    from tests.helpers import host_layer
+
+    n = min(8, wl.n_layers)
+    layers = [host_layer(stack, l) for l in range(n)]
+    threads = oracle.num_threads()
+    rate, tokens, el = _oracle_rate(layers, wl, budget_s)
+    oracle.set_num_threads(1)
+    try:
+        rate1, tokens1, el1 = _oracle_rate(layers, wl, budget_s)
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": rate / wl.n_layers, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{tokens} tokens x first {n} of {wl.n_layers} layers (T=1, chained by the glue), "
-                      f"{el:.1f} s; tokens/s = 1 / (time per layer-token x {wl.n_layers} layers)"}
+                      f"{el:.1f} s on {threads} threads; tokens/s = 1 / (time per layer-token x {wl.n_layers} layers)",
+            "single_thread": {"value": rate1 / wl.n_layers, "unit": "tokens/s", "cores": 1,
+                              "sample": f"{tokens1} tokens x first {n} layers, {el1:.1f} s"}}
 
 
 def batched_leg(stack, steps: int, warmup: int):
     """T = 512 tokens through every layer of the stack (each layer called on the step's input)
     with moe_layer_batched; the Zipf(1.1) router bias of the batched workload is attached to the
-    same weights."""
+    same weights. Reports the MFMA utilisation (algorithmic flops, router included, over the fp16
+    dense peak) and the fraction of the attainable roofline max(t_HBM, t_MFMA) / t, with t_HBM the
+    algorithmic bytes (touched experts of every layer, shared expert, router, x, y) over 8 TB/s."""
     import torch
 
     import quantized_moe_decode_router_amd as moe
@@ -95,19 +111,20 @@ def batched_leg(stack, steps: int, warmup: int):
 
     wl = synth.QWEN35B_BATCHED
     shape, T, L = wl.shape, wl.tokens, stack.n_layers
+    H, E, K, I, Is = shape.hidden, shape.num_experts, shape.top_k, shape.inter, shape.shared_inter
     dev = stack.router.device
     sb = synth.with_zipf_bias(stack, wl.seed, wl.zipf_s)
     layers = [sb.layer(l) for l in range(L)]
     n = warmup + steps
     xs = [synth.make_x(shape, T, wl.seed, step=s, device=dev) for s in range(n)]
-    y = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
-    idx = torch.empty(T, shape.top_k, dtype=torch.int32, device=dev)
+    y = torch.empty(T, H, dtype=torch.float32, device=dev)
+    idx = torch.empty(L, T, K, dtype=torch.int32, device=dev)
     ws = moe.workspace(shape, T, moe.MOE_WS_BATCHED, dev)
     stream = torch.cuda.current_stream()
 
     def step(s):
         for l in range(L):
-            moe.moe_layer_batched(shape, layers[l], xs[s], T, y, idx, workspace=ws, stream=stream)
+            moe.moe_layer_batched(shape, layers[l], xs[s], T, y, idx[l], workspace=ws, stream=stream)
 
     for s in range(warmup):
         step(s)
@@ -118,18 +135,29 @@ def batched_leg(stack, steps: int, warmup: int):
         step(s)
     b.record(stream)
     torch.cuda.synchronize()
+    if moe.moe_read_status(ws) != 0:
+        raise SystemExit("batched leg: device status is not OK")
     ms = a.elapsed_time(b) / steps
     per_layer_us = ms * 1e3 / L
-    flops = 2.0 * T * shape.top_k * 3 * shape.inter * shape.hidden + 2.0 * T * 3 * shape.shared_inter * shape.hidden
+    flops = 2.0 * T * (E + 1) * H + 6.0 * T * K * I * H + 6.0 * T * Is * H
     tflops = flops / (per_layer_us * 1e-6) / 1e12
-    counts = torch.bincount(idx.view(-1).long(), minlength=shape.num_experts)
+    touched = [int((torch.bincount(idx[l].view(-1).long(), minlength=E) > 0).sum().item()) for l in range(L)]
+    counts = torch.bincount(idx[L - 1].view(-1).long(), minlength=E)
+    bytes_layer = (sum(touched) / L * shape.expert_bytes() + shape.expert_bytes(Is) + 4 * (E + 1) * H
+                   + 2 * T * H + 4 * T * H)
+    t_hbm = bytes_layer / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = flops / (FP16_PEAK_TFLOPS * 1e12)
     return {"workload": wl.name, "tokens_per_call": T, "layers": L, "steps": steps,
             "ms_per_step": round(ms, 4), "us_per_layer": round(per_layer_us, 2),
             "layer_tokens_per_s": round(T * L / (ms / 1e3), 1),
             "mfma": {"dtype": "fp16", "algorithmic_tflop_per_layer": round(flops / 1e12, 4),
                      "achieved_tflops": round(tflops, 1), "peak_tflops": FP16_PEAK_TFLOPS,
                      "utilisation": round(tflops / FP16_PEAK_TFLOPS, 4)},
-            "last_layer_experts_touched": int((counts > 0).sum().item()),
+            "roofline": {"algorithmic_bytes_per_layer": int(bytes_layer), "t_hbm_us": round(t_hbm * 1e6, 2),
+                         "t_mfma_us": round(t_mfma * 1e6, 2),
+                         "attainable_frac": round(max(t_hbm, t_mfma) / (per_layer_us * 1e-6), 4)},
+            "experts_touched_mean": round(sum(touched) / L, 1),
+            "last_layer_experts_touched": touched[-1],
             "last_layer_max_load": int(counts.max().item())}
 
 
@@ -424,9 +452,14 @@ def main():
     ws = moe.workspace(shape, T, moe.MOE_WS_STACK, dev, n_layers=L)
     flags = moe.MOE_STACK_INDEPENDENT if args.independent else 0
     stream = torch.cuda.current_stream()
+    # for T > 1 the routing of every timed step is kept: the bytes a step must move count each
+    # distinct routed expert of a layer once
+    idx_steps = (torch.empty(args.steps, L, T, shape.top_k, dtype=torch.int32, device=dev) if T > 1 else None)
 
-    def step(s):
-        moe.moe_stack_decode(shape, stack, L, xs[s], T, y, workspace=ws, stream=stream, flags=flags)
+    def step(s, i=None):
+        idx = idx_steps[i] if (idx_steps is not None and i is not None) else None
+        moe.moe_stack_decode(shape, stack, L, xs[s], T, y, topk_idx_all=idx, workspace=ws, stream=stream,
+                             flags=flags)
 
     for s in range(args.warmup):
         step(s)
@@ -439,7 +472,7 @@ def main():
     w0 = time.perf_counter()
     for i, s in enumerate(range(args.warmup, nsteps)):
         evs[i][0].record(stream)
-        step(s)
+        step(s, i)
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -447,14 +480,20 @@ def main():
     if status != 0:
         raise SystemExit(f"device status {moe.status_string(status)} after the timed steps")
     total_ms = evs[0][0].elapsed_time(evs[-1][1])
-    launch_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    launch = sorted(a.elapsed_time(b) for a, b in evs)
+    launch_ms = sum(launch) / args.steps
     ms_per_step = total_ms / args.steps
     tokens_per_s = args.steps * T / (total_ms / 1e3)
+    # trials: the timed steps in (up to) five contiguous runs, tokens/s of each
+    ntr = min(5, args.steps)
+    bounds = [round(k * args.steps / ntr) for k in range(ntr + 1)]
+    trial_tps = sorted((bounds[k + 1] - bounds[k]) * T /
+                       (evs[bounds[k]][0].elapsed_time(evs[bounds[k + 1] - 1][1]) / 1e3) for k in range(ntr))
 
-    bytes_per_launch = L * synth.algorithmic_decode_bytes(shape) * T
+    bytes_per_launch = decode_step_bytes(shape, L, T, idx_steps)
     achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
     kernel = "decode_kernel"
-    traffic = recorded_traffic(wl.name, kernel)
+    traffic = recorded_traffic(wl.name, kernel) if T == 1 else None
     result = {
         "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -469,8 +508,14 @@ def main():
         "wall_s": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": bytes_per_launch,
+                     "algorithmic_bytes_per_launch": int(bytes_per_launch),
                      "avg_launch_us": round(launch_ms * 1e3, 3)},
+        "spread": {"launch_us": {"median": round(_pct(launch, 50) * 1e3, 3), "p10": round(_pct(launch, 10) * 1e3, 3),
+                                 "p90": round(_pct(launch, 90) * 1e3, 3)},
+                   "trials_tokens_per_s": [round(v, 1) for v in trial_tps],
+                   "trial_median": round(_pct(trial_tps, 50), 1), "trial_p10": round(_pct(trial_tps, 10), 1),
+                   "trial_p90": round(_pct(trial_tps, 90), 1)},
+        "run": run_metadata(wl.seed),
         "cpu_baseline": None,
         "batched": None,
     }
@@ -479,6 +524,73 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(stack, wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _pct(sorted_vals, q: float) -> float:
+    """The q-th percentile of an ascending list (linear interpolation)."""
+    n = len(sorted_vals)
+    if n == 1:
+        return float(sorted_vals[0])
+    pos = (n - 1) * q / 100.0
+    lo = int(pos)
+    hi = min(lo + 1, n - 1)
+    return float(sorted_vals[lo] + (sorted_vals[hi] - sorted_vals[lo]) * (pos - lo))
+
+
+def decode_step_bytes(shape, L: int, T: int, idx_steps=None) -> float:
+    """Algorithmic bytes of one decode step of T tokens through L layers, averaged over the timed
+    steps: per layer the router, the shared-gate vector and the shared expert once, every distinct
+    routed expert the step's tokens selected once (K per layer at T = 1), and x (bf16) and y (fp32)
+    per token."""
+    E, H = shape.num_experts, shape.hidden
+    once = 4 * E * H
+    if shape.shared_inter:
+        once += 4 * H + shape.expert_bytes(shape.shared_inter)
+    per_token = 2 * H + 4 * H
+    if idx_steps is None:
+        distinct = L * T * shape.top_k  # T == 1: a token's K experts are distinct
+    else:
+        import torch
+        n = idx_steps.shape[0]
+        flat = idx_steps.view(n * L, -1).long()
+        seen = torch.zeros(n * L, E, dtype=torch.bool, device=flat.device)
+        seen.scatter_(1, flat, True)
+        distinct = seen.sum().item() / n
+    return L * (once + T * per_token) + distinct * shape.expert_bytes()
+
+
+def run_metadata(seed: int) -> dict:
+    """What identifies the run: source revision, device, runtime versions, clocks, seed."""
+    import subprocess
+
+    import torch
+    meta = {"seed": seed, "kernel_source_hash": kernel_source_hash(), "git": None,
+            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+    try:
+        meta["git"] = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short", "HEAD"], capture_output=True,
+                                     text=True, timeout=10).stdout.strip() or None
+    except Exception:
+        pass
+    try:
+        props = torch.cuda.get_device_properties(0)
+        meta["gpu"] = props.name
+        meta["arch"] = getattr(props, "gcnArchName", None)
+        meta["compute_units"] = props.multi_processor_count
+    except Exception:
+        pass
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            meta["rocm"] = f.read().strip()
+    except Exception:
+        pass
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                             timeout=20).stdout
+        card = next(iter(json.loads(out).values()))
+        meta["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower() or "clk" in k.lower()}
+    except Exception:
+        pass
+    return meta
 
 
 if __name__ == "__main__":

@@ -44,8 +44,21 @@
  *   - A workspace is device memory of at least moe_workspace_bytes() for the same arguments,
  *     zero-filled before its first use; calls leave it ready for the next call. Its first 4
  *     bytes are a sticky device status word: 0 after successful runs, or a moe_status a kernel
- *     set (MOE_ERR_TIMEOUT). A decode kernel that finds it non-zero does nothing; zero-fill the
- *     workspace again to recover. moe_read_status() reads it.
+ *     set (MOE_ERR_TIMEOUT from a decode wait, MOE_ERR_UNSUPPORTED from the batched path, see
+ *     below). A decode kernel that finds it non-zero does nothing and writes no output; zero-fill
+ *     the workspace again to recover. moe_read_status() reads it.
+ *   - The decode kernels' grid-wide waits are bounded: int32 word 2 of a decode, stack or forward
+ *     workspace (bytes 8..11) is the bound in polls of one wait, 0 (as zero-filled) meaning the
+ *     default 2^20 polls (well over 0.1 s). A wait that exceeds it sets MOE_ERR_TIMEOUT and every
+ *     workgroup of the launch then ends; the outputs are undefined.
+ *   - The batched path computes with fp16 MFMA operands: x converted from bf16, the dequantised
+ *     weights s * q + b rounded once to fp16, and the SwiGLU output h as fp16 high and low parts.
+ *     Each of x, s * q + b and h must therefore lie within fp16's range (|v| <= 65504);
+ *     magnitudes below 2^-14 are held as fp16 subnormals (absolute precision 2^-24). An operand
+ *     beyond the range makes a gate|up or down accumulator non-finite, and the call then sets the
+ *     status word to MOE_ERR_UNSUPPORTED (for moe_layer_forward: the forward workspace's first
+ *     word); its outputs are undefined. The decode path has no such limit (its dot products are
+ *     exact integer sums on activation limbs, scaled in fp32).
  *   - Two calls that share a workspace must not run concurrently.
  *   - The decode calls additionally need hidden, inter, shared_inter <= 2048, inter and a
  *     non-zero shared_inter >= 128, and an LDS footprint within 160 KiB (it grows with T); other
@@ -121,6 +134,11 @@ typedef struct {
 
 /*
  * Router: logits, top-k selection and renormalised weights for T tokens (1 <= T <= 65536).
+ * Pages: every layer routes each token to 8 of 256 experts (35B) or 10 of 512 (80B), the routers
+ * being among the resident dense weights (xix.ai Swiftlet article, paragraph on scheduling;
+ * AgentLens Swiftlet page, "How it works"); 256 routed experts, top-8, one shared expert (Runnel
+ * README, "Target"). The softmax / top-k / renormalise form and the tie rule are the plainest
+ * reading (the pages print no routing formula).
  *   x       : bf16 [T][H] (unused with MOE_ROUTE_LOGITS_IN, may be NULL)
  *   logits  : fp32 [T][E]; output, or input with MOE_ROUTE_LOGITS_IN; required
  *   topk_idx: int32 [T][K] out; topk_w: fp32 [T][K] out; gamma: fp32 [T] out or NULL
@@ -132,6 +150,10 @@ moe_status moe_route(const moe_shape *shape, const moe_layer *layer, const uint1
                      void *stream);
 
 /*
+ * Pages: batch-1 decode of the MoE layer (Runnel README, "Target"); MLX-style int4/int8 group
+ * quantised experts read through 64-bit offsets (xix.ai Swiftlet article, paragraph on lineage);
+ * the routed gate and up projections packed into one matrix (Runnel README, intro and "Streaming
+ * CLI"); the shared expert always on (xix.ai article, paragraph on scheduling).
  * One layer at decode for 1 <= T <= 8 tokens: router, top-k, packed gate|up dequant-GEMV with
  * SwiGLU, down dequant-GEMV and the fixed-order combine (k = 0..K-1, then the shared expert),
  * as one persistent kernel (one workgroup per compute unit; workgroups exchange logits, h and y
@@ -166,6 +188,9 @@ moe_status moe_stack_decode(const moe_shape *shape, const moe_layer *stack, int3
                             size_t workspace_bytes, void *stream);
 
 /*
+ * Pages: the same layer as moe_layer_decode (same citations), evaluated for many tokens per call;
+ * the pages pick a quantised-matmul route by batch size and sweep its boundary (Smelt README, "Lab
+ * workflow"). The grouping by expert and the grouped GEMMs are this library's design.
  * One layer for a batch of 1 <= T <= 65536 tokens (prefill or batched decode): router, then a
  * histogram / exclusive-scan / stable scatter that groups (token, slot) pairs by expert, an
  * MFMA grouped GEMM for gate|up with SwiGLU, one for down scaled by the routing weight, the
@@ -219,7 +244,7 @@ moe_status moe_layer_forward(const moe_shape *shape, const moe_layer *layer, con
 
 /*
  * ---- Expert residency (fixed-stride expert container + bounded HBM slot pool) ----
- * Swiftlet's memory scheme as the Hacker News post ("How it works"), the xix.ai article
+ * Swiftlet's memory scheme as the AgentLens project page ("How it works"), the xix.ai article
  * (scheduling and lineage paragraphs) and the Chinese summary describe it: routed experts repacked
  * into fixed-stride blocks so that fetching one expert is one contiguous read, and a bounded pool
  * of popular experts with LFU + recency eviction in front of the slow tier. Here the slow tier is

@@ -5,7 +5,7 @@ TEST INFRASTRUCTURE: only the tests, the smoke check and the benchmark's CPU-bas
 import this module. It shares no code with the HIP library or its Python binding and imports
 neither.
 
-What the pages fix (Swiftlet as the Hacker News post describes it under "How it works", the
+What the pages fix (Swiftlet as the AgentLens project page describes it under "How it works", the
 xix.ai article in its scheduling and lineage paragraphs, and the Chinese summary's highlights):
 routed experts are repacked into fixed-stride blocks so that one expert is one contiguous read;
 popular experts are kept in a bounded pool; eviction is "LFU plus recency". Readings taken where

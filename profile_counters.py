@@ -1,8 +1,8 @@
-"""HBM traffic of the decode kernel from rocprofv3 counters (a profiling aid, not part of the path).
+"""HBM traffic of a kernel from rocprofv3 counters (a measurement aid beside bench.py, not part of
+the path).
 
   copy       run a plain device-to-device copy of a known size (the calibration kernel):
-             rocprofv3 --pmc FETCH_SIZE --kernel-include-regex copy -- \
-                 python3 -m quantized_moe_decode_router_amd.profile_counters copy
+             rocprofv3 --pmc FETCH_SIZE --kernel-include-regex copy -- python3 profile_counters.py copy
   summarize  turn the counter CSVs of the decode kernel and of the copy into
              profiles/<kernel>_<workload>_counters.json: per-launch FETCH_SIZE and WRITE_SIZE, each
              scaled by (true bytes / counted bytes) of the copy, and the hash of the kernel sources
@@ -15,7 +15,7 @@ import json
 import os
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 COPY_MIB = 1024
 
 

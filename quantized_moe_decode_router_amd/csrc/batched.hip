@@ -17,9 +17,11 @@
 //                    h lo; epilogue scales by the routing weight (gamma for the shared group)
 //   6. combine       y[t] = sum_k out[pos(t, k)] + out[shared row of t], k = 0..K-1 in order
 //
-// Dequantised weights are s * q + b rounded once to fp16 (scales and biases must lie in fp16's
-// normal range); bf16 activations are exact in fp16 in the normal range. Products are exact in
-// the fp32 accumulators of the MFMA.
+// Dequantised weights are s * q + b rounded once to fp16, bf16 activations are converted to fp16
+// (exact in fp16's normal range) and h is held as fp16 hi + lo halves; products are exact in the
+// fp32 accumulators of the MFMA. So x, s * q + b and h must lie within fp16's range (+-65504):
+// an operand beyond it becomes infinite, the accumulators it reaches are not finite, and the
+// epilogues then set the status word to MOE_ERR_UNSUPPORTED (the outputs are then undefined).
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -320,6 +322,11 @@ __device__ __forceinline__ GroupW group_w2(const BatchedParams &p, int g) {
     return {p.s2.c, p.s2.s, p.s2.b, p.Is};
 }
 
+// A non-finite accumulator: an fp16 operand was out of range (see the file header).
+__device__ __forceinline__ void flag_unsupported(int *status) {
+    __hip_atomic_store(status, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---- fp16 tiles in pair order ----------------------------------------------------------------------
 // Inside every 8-column block (4-bit) or 4-column block (8-bit) the fp16 tiles hold their columns in
 // the order the packed dequantisation produces them: 4-bit (0,4,1,5,2,6,3,7), 8-bit (0,2,1,3).
@@ -504,6 +511,7 @@ __global__ void __launch_bounds__(kGemmThreads) gu_gemm(BatchedParams p) {
     // epilogue: lane l, register r -> row 32 mh + 16 i + 4 (l / 16) + r, j = j0 + 32 jh + 16 j + l % 16;
     // h goes to its pair-order position (dn_gemm's A operand)
     const int Imax = p.Imax;
+    bool finite = true;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -515,12 +523,14 @@ __global__ void __launch_bounds__(kGemmThreads) gu_gemm(BatchedParams p) {
                 const int jj = j0 + 32 * jh + 16 * j + lane % 16;
                 const float gv = ag[i][j][r], uv = au[i][j][r];
                 const float h = gv / (1.0f + expf(-gv)) * uv;
+                finite &= __builtin_isfinite(gv) && __builtin_isfinite(uv);
                 const _Float16 hh = (_Float16)h;
                 const _Float16 hl = (_Float16)(h - (float)hh);
                 const size_t o = (size_t)(P0 + m) * Imax + pair_pos<BITS>(jj & 63) + (jj & ~63);
                 p.hh[o] = hh;
                 p.hl[o] = hl;
             }
+    if (!finite) flag_unsupported(p.status);
 }
 
 // ---- 5. grouped down projection ------------------------------------------------------------------
@@ -644,6 +654,7 @@ __global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_
             __syncthreads();
         }
     }
+    bool finite = true;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -655,9 +666,11 @@ __global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int n = n0 + 32 * nh + 16 * j + lane % 16;
+                finite &= __builtin_isfinite(acc[i][j][r]);
                 p.out[(size_t)(P0 + m) * H + n] = sc * acc[i][j][r];
             }
         }
+    if (!finite) flag_unsupported(p.status);
 }
 
 // ---- 6. fixed-order combine --------------------------------------------------------------------------

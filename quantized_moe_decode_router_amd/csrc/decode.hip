@@ -610,7 +610,7 @@ __device__ __forceinline__ void build_limbs(const float (&v)[4], int8_t *dst, fl
 // unchained), else the RMS glue of y_{l-1}: x = bf16_rne(y / sqrt(mean(y^2) + eps)); every
 // workgroup computes the same bits.
 template <int BITS>
-__device__ bool layer_input(const DecodeParams &p, int l, uint32_t ep, const Lds &s) {
+__device__ bool layer_input(const DecodeParams &p, int l, uint32_t ep, const Lds &s, unsigned spin) {
     const int T = p.T, H = p.H, nsl = H / 32;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     if (l == 0 || !p.chained) {
@@ -625,7 +625,7 @@ __device__ bool layer_input(const DecodeParams &p, int l, uint32_t ep, const Lds
         const uint64_t *ysrc = p.ll_y + (size_t)(l - 1) * T * H;
         float *yb = reinterpret_cast<float *>(s.hp);
         for (int t = 0; t < T; ++t) {
-            if (!ll_gather(ysrc + (size_t)t * H, H, ep, yb, p.ctrl, p.spin_limit)) return false;
+            if (!ll_gather(ysrc + (size_t)t * H, H, ep, yb, p.ctrl, spin)) return false;
             float ss = 0.0f;
             for (int h = threadIdx.x; h < H; h += blockDim.x) ss += yb[h] * yb[h];
             ss = wave_sum(ss);
@@ -728,10 +728,10 @@ __device__ void router_logits(const DecodeParams &p, int l, const Lds &s, const 
 
 // ---- h of one token as limbs -------------------------------------------------------------------------
 template <int BITS>
-__device__ bool stage_hq(const DecodeParams &p, const Lds &s, const uint64_t *src, uint32_t ep) {
+__device__ bool stage_hq(const DecodeParams &p, const Lds &s, const uint64_t *src, uint32_t ep, unsigned spin) {
     const int n = p.K * p.I + p.Is;
     const float *hf = reinterpret_cast<const float *>(s.hp);
-    if (!ll_gather(src, n, ep, reinterpret_cast<float *>(s.hp), p.ctrl, p.spin_limit)) return false;
+    if (!ll_gather(src, n, ep, reinterpret_cast<float *>(s.hp), p.ctrl, spin)) return false;
     // 16 lanes per group; n / 4 and the block size are multiples of 16, so DPP rows stay whole
     for (int it = threadIdx.x; it < n / 4; it += blockDim.x) {
         const int gi = it >> 4, m = it & 15;
@@ -962,6 +962,8 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
     const int tid = threadIdx.x;
     const int nb = gridDim.x, b = blockIdx.x;
     if (p0.ctrl[0] != 0) return;  // sticky failure of an earlier call: do nothing
+    // bound on every wait: the workspace's control word 2 when the caller set one, else the default
+    const unsigned spin = p0.ctrl[2] > 0 ? static_cast<unsigned>(p0.ctrl[2]) : p0.spin_limit;
     uint32_t ep = static_cast<uint32_t>(p0.ctrl[1]) + 1u;
     if (ep == 0) ep = 1;
     if (tid == 0) ll_put(p0.ll_start + b, 0.0f, ep);
@@ -985,7 +987,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         uint64_t *ll_h = p.ll_h + (size_t)l * T * HW;
         uint64_t *ll_y = p.ll_y + (size_t)l * T * H;
 
-        if (!layer_input<BITS>(p, l, ep, s)) { dma_wait(); return; }
+        if (!layer_input<BITS>(p, l, ep, s, spin)) { dma_wait(); return; }
         dma_wait();  // this layer's router and shared rows (staged during the previous layer)
         lds_barrier();
 
@@ -995,7 +997,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         build_x_limbs<BITS>(p, s);
 
         // ---- G: routing (identical in every workgroup), then routed gate|up + SwiGLU
-        if (!ll_gather(ll_lg, T * (E + 1), ep, s.lg, p.ctrl, p.spin_limit)) { dma_wait(); return; }
+        if (!ll_gather(ll_lg, T * (E + 1), ep, s.lg, p.ctrl, spin)) { dma_wait(); return; }
         route_tokens(p, s);
         // layer l+1's router rows (the LDS copy was last read before the logits exchange) stream in
         // during the expert selection, issued by waves with nothing else to do then
@@ -1089,7 +1091,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
             later = w.nps ? dma_qrows_count(2 * w.nps, H, BITS) : 0;
         }
         for (int t = 0; t < T; ++t) {
-            if (!stage_hq<BITS>(p, s, ll_h + (size_t)t * HW, ep)) { dma_wait(); return; }
+            if (!stage_hq<BITS>(p, s, ll_h + (size_t)t * HW, ep, spin)) { dma_wait(); return; }
             if (t == 0) dma_wait_but(later);
             else dma_wait();
             lds_barrier();
@@ -1132,8 +1134,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
     dma_wait();
     // the next call may advance the epoch once every workgroup has read it
     if (b == 0) {
-        if (!ll_gather(p0.ll_start, nb, ep, reinterpret_cast<float *>(smem + p0.lds.hp), p0.ctrl,
-                              p0.spin_limit))
+        if (!ll_gather(p0.ll_start, nb, ep, reinterpret_cast<float *>(smem + p0.lds.hp), p0.ctrl, spin))
             return;
         if (tid == 0) p0.ctrl[1] = static_cast<int>(ep);
     }

@@ -328,7 +328,7 @@ moe_status moe_pack_experts(const moe_shape *s, const moe_layer *stack, int32_t 
 namespace {
 moe_status batched_common(const moe_shape *s, const moe_layer *L, const uint16_t *x, int32_t T, float *y,
                           int32_t *topk_idx_opt, float *topk_w_opt, float *logits_opt, void *ws, size_t ws_bytes,
-                          void *stream, const uint64_t *xtab) {
+                          void *stream, const uint64_t *xtab, int *status_word = nullptr) {
     moe_status st = check_shape(s);
     if (st != MOE_OK) return st;
     if ((st = check_layer(s, L, xtab == nullptr)) != MOE_OK) return st;
@@ -383,6 +383,7 @@ moe_status batched_common(const moe_shape *s, const moe_layer *L, const uint16_t
     p.rlo = reinterpret_cast<uint16_t *>(w + lay.rlo);
     p.lpart = reinterpret_cast<float *>(w + lay.lpart);
     p.y = y;
+    p.status = status_word ? status_word : reinterpret_cast<int *>(w);
     hipError_t err = moe::launch_batched(p, lay.max_tiles, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -423,8 +424,9 @@ moe_status moe_layer_forward(const moe_shape *s, const moe_layer *L, const uint1
     const size_t dpart = forward_decode_part(s);
     if (moe_layer_path(s, T, crossover) == MOE_PATH_DECODE)
         return moe_layer_decode(s, L, x, T, y, topk_idx_opt, topk_w_opt, logits_opt, ws, dpart, stream);
-    return moe_layer_batched(s, L, x, T, y, topk_idx_opt, topk_w_opt, logits_opt, static_cast<char *>(ws) + dpart,
-                             ws_bytes - dpart, stream);
+    // the batched part reports through the workspace's first word, as the decode part does
+    return batched_common(s, L, x, T, y, topk_idx_opt, topk_w_opt, logits_opt, static_cast<char *>(ws) + dpart,
+                          ws_bytes - dpart, stream, nullptr, static_cast<int *>(ws));
 }
 
 moe_status moe_group_pairs(const moe_shape *s, const int32_t *topk_idx, int32_t T, int32_t *counts,

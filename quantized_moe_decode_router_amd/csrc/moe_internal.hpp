@@ -212,6 +212,10 @@ struct BatchedParams {
     // pieces at these byte offsets (gate|up codes at 0); w13 and w2 are then unused
     const uint64_t *xtab;
     uint32_t xo13s, xo13b, xo2c, xo2s, xo2b;
+    // status word (the workspace's first word, or the decode part's in a moe_layer_forward
+    // workspace): set to MOE_ERR_UNSUPPORTED (2) when a grouped-GEMM accumulator is not finite, i.e.
+    // an fp16 operand (x, s*q + b or h) was beyond fp16's range
+    int *status;
 };
 // The batched router GEMM splits H into this many contiguous ranges (fewer when H has fewer
 // 64-column steps); the top-k kernel adds the partial sums in range order.

@@ -1,10 +1,10 @@
 // Expert residency: a bounded pool of expert slots in HBM in front of a fixed-stride expert
 // container, with least-frequently-used eviction and ties broken by least recent use.
 //
-// Swiftlet (the Hacker News / xix.ai / Chinese write-ups, "How it works" and the scheduling
-// paragraph) keeps the dense weights resident, packs the routed experts into fixed-stride blocks
-// so that one read is one fetch, and holds the popular ones in a bounded pool with LFU + recency
-// eviction (hit rates of 43-70 % on its machine). Here the container sits in host memory the GPU
+// Swiftlet (AgentLens project page, "How it works"; xix.ai article, scheduling paragraph; the
+// Chinese summary's highlights) keeps the dense weights resident, packs the routed experts into
+// fixed-stride blocks so that one read is one fetch, and holds the popular ones in a bounded pool
+// with LFU + recency eviction (hit rates of 43-70 % on its machine). Here the container sits in host memory the GPU
 // can read (or anywhere in device memory), the pool in HBM, and the decode kernel follows a
 // per-(layer, expert) table of block addresses: a resident expert is read from its pool slot, any
 // other straight from the container. After each decode call the host feeds that call's routing

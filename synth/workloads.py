@@ -16,7 +16,10 @@ Value recipe (all seeded, counter-based, per layer and per tensor):
   codes   : uniform random bytes, i.e. every 4-bit nibble uniform on 0..15 and
             every 8-bit code uniform on 0..255
   scales  : bf16(U[0.005, 0.02]) per row and group of 64 input columns
-  biases  : -8 * scale (4-bit) or -128 * scale (8-bit), exact in bf16
+  biases  : -8 * scale (4-bit) or -128 * scale (8-bit), exact in bf16 (the workloads' recipe);
+            with affine_bias=True (parity tests of the general affine form w = s*q + b) an
+            independent bf16(U[-0.25, 0.25]) per row and group instead, both signs, mostly far
+            from -zero_point * scale
   router  : fp32 N(0, 0.02^2), [E, H];  shared-expert gate vector: same, [H]
   x       : bf16 N(0, 1), [T, H]
   router logit bias (batched workload only): -s * ln(rank_e), rank a seeded
@@ -42,6 +45,7 @@ T_W2_CODES, T_W2_SCALES = 6, 7
 T_S13_CODES, T_S13_SCALES = 8, 9
 T_S2_CODES, T_S2_SCALES = 10, 11
 T_X = 12
+T_AFFINE_BIAS = 13  # folded into a matrix family's scale key for its independent biases
 
 
 @dataclasses.dataclass(frozen=True)
@@ -178,11 +182,16 @@ def _alloc(shape: MoeShape, n_layers: int, device, with_bias: bool) -> LayerStac
         s2_codes=s2[0], s2_scales=s2[1], s2_biases=s2[2])
 
 
-def _fill_scales_biases(scales: torch.Tensor, biases: torch.Tensor, key: int, bits: int) -> None:
+def _fill_scales_biases(scales: torch.Tensor, biases: torch.Tensor, key: int, bits: int,
+                        affine_bias: bool = False) -> None:
     n = scales.numel()
     u = rng.uniform01(key, n, scales.device)
     s = (0.005 + 0.015 * u).to(torch.float32).to(torch.bfloat16)
     scales.view(-1).copy_(s)
+    if affine_bias:
+        ub = rng.uniform01(rng.derive_key(key, T_AFFINE_BIAS), n, scales.device)
+        biases.view(-1).copy_((0.5 * ub - 0.25).to(torch.float32).to(torch.bfloat16))
+        return
     zero_point = 8.0 if bits == 4 else 128.0
     biases.view(-1).copy_(s * (-zero_point))  # exact: power-of-two multiple of a bf16 value
 
@@ -202,8 +211,10 @@ def with_zipf_bias(stack: LayerStack, seed: int, zipf_s: float) -> LayerStack:
     return dataclasses.replace(stack, router_bias=bias.contiguous())
 
 
-def fill_layer(stack: LayerStack, l: int, seed: int, zipf_s: Optional[float] = None) -> None:
-    """Fill layer l of `stack` in place from (seed, l)."""
+def fill_layer(stack: LayerStack, l: int, seed: int, zipf_s: Optional[float] = None,
+               affine_bias: bool = False) -> None:
+    """Fill layer l of `stack` in place from (seed, l); affine_bias draws every quantisation
+    bias independently of its scale (see the module recipe)."""
     sh = stack.shape
     dev = stack.router.device
     k = lambda tid: rng.derive_key(seed, l, tid)
@@ -217,24 +228,26 @@ def fill_layer(stack: LayerStack, l: int, seed: int, zipf_s: Optional[float] = N
     if stack.shared_gate is not None:
         stack.shared_gate[l].copy_((0.02 * rng.normal(k(T_SHARED_GATE), sh.hidden, dev)).to(torch.float32))
     rng.fill_bytes(stack.w13_codes[l], k(T_W13_CODES))
-    _fill_scales_biases(stack.w13_scales[l], stack.w13_biases[l], k(T_W13_SCALES), sh.bits)
+    ab = affine_bias
+    _fill_scales_biases(stack.w13_scales[l], stack.w13_biases[l], k(T_W13_SCALES), sh.bits, ab)
     rng.fill_bytes(stack.w2_codes[l], k(T_W2_CODES))
-    _fill_scales_biases(stack.w2_scales[l], stack.w2_biases[l], k(T_W2_SCALES), sh.bits)
+    _fill_scales_biases(stack.w2_scales[l], stack.w2_biases[l], k(T_W2_SCALES), sh.bits, ab)
     if stack.s13_codes is not None:
         rng.fill_bytes(stack.s13_codes[l], k(T_S13_CODES))
-        _fill_scales_biases(stack.s13_scales[l], stack.s13_biases[l], k(T_S13_SCALES), sh.bits)
+        _fill_scales_biases(stack.s13_scales[l], stack.s13_biases[l], k(T_S13_SCALES), sh.bits, ab)
         rng.fill_bytes(stack.s2_codes[l], k(T_S2_CODES))
-        _fill_scales_biases(stack.s2_scales[l], stack.s2_biases[l], k(T_S2_SCALES), sh.bits)
+        _fill_scales_biases(stack.s2_scales[l], stack.s2_biases[l], k(T_S2_SCALES), sh.bits, ab)
 
 
 def make_stack(shape: MoeShape, n_layers: int, seed: int, device="cpu",
-               zipf_s: Optional[float] = None, with_bias: Optional[bool] = None) -> LayerStack:
+               zipf_s: Optional[float] = None, with_bias: Optional[bool] = None,
+               affine_bias: bool = False) -> LayerStack:
     """Allocate and fill an n_layers stack; layer l depends only on (seed, l)."""
     if with_bias is None:
         with_bias = zipf_s is not None
     st = _alloc(shape, n_layers, device, with_bias)
     for l in range(n_layers):
-        fill_layer(st, l, seed, zipf_s)
+        fill_layer(st, l, seed, zipf_s, affine_bias)
     return st
 
 

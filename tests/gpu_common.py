@@ -112,9 +112,33 @@ def check_y(gpu_y, ref_y, tol=Y_TOL):
     return err
 
 
+CANARY = 0x5A5A5A5A  # as fp32: a NaN-free pattern no kernel produces by accident (2.9e16)
+GUARD = 256          # 4-byte words of guard band on each side (keeps 16-byte alignment)
+
+
+class Guarded:
+    """4-byte output tensors (fp32 or int32) carved from the middle of a larger buffer whose guard
+    bands hold a canary pattern; check() fails if any guard word changed (an out-of-bounds store)."""
+
+    def __init__(self, dev):
+        self.dev = dev
+        self.bufs = []
+
+    def empty(self, *shape, dtype=torch.float32):
+        n = int(np.prod(shape))
+        buf = torch.full((n + 2 * GUARD,), CANARY, dtype=torch.int32, device=self.dev)
+        self.bufs.append((buf, n))
+        return buf[GUARD:GUARD + n].view(dtype).view(*shape)
+
+    def check(self):
+        for buf, n in self.bufs:
+            h = buf.cpu().numpy()
+            assert np.all(h[:GUARD] == CANARY) and np.all(h[GUARD + n:] == CANARY), "store outside an output"
+
+
 def x_from_bits(bits: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(device)
 
 
-__all__ = ["need_gpu", "logit_bound", "topk_margin", "oracle_layer", "check_routing_against_oracle",
+__all__ = ["Guarded", "need_gpu", "logit_bound", "topk_margin", "oracle_layer", "check_routing_against_oracle",
            "check_y", "x_from_bits", "bf16_bits", "host_layer", "Y_TOL", "W_TOL"]

@@ -25,3 +25,36 @@ def test_decode_bytes_per_token():
     assert synth.algorithmic_decode_bytes(synth.QWEN35B_4BIT.shape) == 18042880
     assert synth.algorithmic_decode_bytes(synth.QWEN80B_4BIT.shape) == 23678976
     assert synth.algorithmic_decode_bytes(synth.QWEN35B_8BIT.shape) == 32198656
+
+
+def test_multi_token_step_bytes_count_shared_weights_once():
+    """bench.py's bytes of a T-token decode step: at T = 1 the per-token model times the layers;
+    for T > 1 the router, shared gate and shared expert once per layer, each distinct routed expert
+    once per layer, x and y per token."""
+    import os
+    import sys
+
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    s = synth.QWEN35B_4BIT.shape
+    L = 40
+    assert bench.decode_step_bytes(s, L, 1) == L * synth.algorithmic_decode_bytes(s)
+    T, K, E, H = 4, s.top_k, s.num_experts, s.hidden
+    same = torch.arange(K, dtype=torch.int32).repeat(2, L, T, 1)  # every token picks experts 0..K-1
+    once = 4 * E * H + 4 * H + s.expert_bytes(s.shared_inter)
+    assert bench.decode_step_bytes(s, L, T, same) == L * (once + T * 6 * H + K * s.expert_bytes())
+    disjoint = torch.arange(T * K, dtype=torch.int32).view(T, K).repeat(3, L, 1, 1)
+    assert bench.decode_step_bytes(s, L, T, disjoint) == L * (once + T * 6 * H + T * K * s.expert_bytes())
+    # the old model (per-token bytes times T) overcounts a step
+    assert bench.decode_step_bytes(s, L, T, same) < L * T * synth.algorithmic_decode_bytes(s)
+
+
+def test_pct_interpolates():
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    assert bench._pct([1.0, 2.0, 3.0, 4.0, 5.0], 50) == 3.0
+    assert abs(bench._pct([0.0, 10.0], 10) - 1.0) < 1e-12
+    assert bench._pct([7.0], 90) == 7.0

@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import synth
-from tests.gpu_common import (bf16_bits, check_routing_against_oracle, check_y, host_layer, need_gpu,
+from tests.gpu_common import (Guarded, bf16_bits, check_routing_against_oracle, check_y, host_layer, need_gpu,
                               oracle_layer)
 
 pytestmark = pytest.mark.gpu
@@ -17,15 +17,18 @@ def _moe():
 
 
 def run_batched(shape, layer, x, T, dev, ws=None):
+    """One batched call with every output inside canary guard bands (checked after the call)."""
     moe = _moe()
-    y = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
-    idx = torch.empty(T, shape.top_k, dtype=torch.int32, device=dev)
-    w = torch.empty(T, shape.top_k, dtype=torch.float32, device=dev)
-    lg = torch.empty(T, shape.num_experts, dtype=torch.float32, device=dev)
+    g = Guarded(dev)
+    y = g.empty(T, shape.hidden)
+    idx = g.empty(T, shape.top_k, dtype=torch.int32)
+    w = g.empty(T, shape.top_k)
+    lg = g.empty(T, shape.num_experts)
     if ws is None:
         ws = moe.workspace(shape, T, moe.MOE_WS_BATCHED, dev)
     moe.moe_layer_batched(shape, layer, x, T, y, idx, w, lg, workspace=ws)
-    torch.cuda.synchronize()
+    assert moe.moe_read_status(ws) == 0
+    g.check()
     return y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy()
 
 
@@ -95,7 +98,10 @@ def test_layer_batched_parity(name, shape, T, seed, zipf):
 
 def test_batched_full_size_sampled():
     """The batched workload at full size (35B-shaped 4-bit layer, T = 512, Zipf-skewed router):
-    routing of every token against the oracle's, and y of a seeded sample of tokens."""
+    the routing of all 512 tokens in given-logits mode (the oracle's selection on the GPU's fp32
+    logits: bit-exact indices, weights to 1e-6), and y against the oracle on a sample holding the
+    first and last token of every 64-row tile of the most loaded expert plus a seeded draw."""
+    import oracle
     dev = need_gpu()
     wl = synth.QWEN35B_BATCHED
     shape, T = wl.shape, wl.tokens
@@ -103,18 +109,24 @@ def test_batched_full_size_sampled():
     x = synth.make_x(shape, T, wl.seed, device=dev)
     y, idx, w, lg = run_batched(shape, st.layer(0), x, T, dev)
     assert np.all(np.isfinite(y))
+    for t in range(T):
+        want = oracle.topk(lg[t].astype(np.float64), shape.top_k)
+        assert list(idx[t]) == list(want), t
+        np.testing.assert_allclose(w[t], oracle.route_weights(lg[t].astype(np.float64), want), rtol=0, atol=1e-6)
+    counts = np.bincount(idx.reshape(-1), minlength=shape.num_experts)
+    hot = int(counts.argmax())
+    rows = [t for t in range(T) if hot in idx[t]]  # the hot expert's rows in pair (= token) order
     rng = np.random.default_rng(11)
-    sample = sorted(rng.choice(T, size=24, replace=False).tolist())
-    import oracle
+    sample = sorted(set(rows[::64]) | set(rows[63::64]) | set(rows[-1:]) |
+                    set(rng.choice(T, size=12, replace=False).tolist()))
     xb = bf16_bits(x)
     Lh = host_layer(st, 0)
     ref = oracle.layer_forward(Lh, xb[sample])
     differ = check_routing_against_oracle(idx[sample], w[sample], lg[sample], ref, xb[sample], Lh, shape.top_k)
     keep = [i for i in range(len(sample)) if i not in differ]
     err = check_y(y[sample][keep], ref["y"][keep])
-    counts = np.bincount(idx.reshape(-1), minlength=shape.num_experts)
     print(f"batched T={T}: max|err|/RMS = {err:.2e} over {len(keep)} sampled tokens; "
-          f"{int((counts > 0).sum())} experts touched, max load {int(counts.max())}")
+          f"{int((counts > 0).sum())} experts touched, max load {int(counts.max())} (expert {hot})")
 
 
 def test_batched_rows_equal_decode_tokens():

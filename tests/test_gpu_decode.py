@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import synth
-from tests.gpu_common import (bf16_bits, check_routing_against_oracle, check_y, host_layer, need_gpu,
+from tests.gpu_common import (Guarded, bf16_bits, check_routing_against_oracle, check_y, host_layer, need_gpu,
                               oracle_layer)
 
 pytestmark = pytest.mark.gpu
@@ -16,14 +16,17 @@ def _moe():
 
 
 def run_decode(shape, layer, x, T, dev):
+    """One decode call with every output inside canary guard bands (checked after the call)."""
     moe = _moe()
-    y = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
-    idx = torch.empty(T, shape.top_k, dtype=torch.int32, device=dev)
-    w = torch.empty(T, shape.top_k, dtype=torch.float32, device=dev)
-    lg = torch.empty(T, shape.num_experts, dtype=torch.float32, device=dev)
+    g = Guarded(dev)
+    y = g.empty(T, shape.hidden)
+    idx = g.empty(T, shape.top_k, dtype=torch.int32)
+    w = g.empty(T, shape.top_k)
+    lg = g.empty(T, shape.num_experts)
     ws = moe.workspace(shape, T, moe.MOE_WS_DECODE, dev)
     moe.moe_layer_decode(shape, layer, x, T, y, idx, w, lg, workspace=ws)
     assert moe.moe_read_status(ws) == 0
+    g.check()
     return y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy()
 
 

@@ -48,3 +48,17 @@ def test_zipf_bias_is_log_rank():
     b = st.router_bias[0].double()
     ranks = torch.exp(-b / 1.1).round()
     assert sorted(ranks.long().tolist()) == list(range(1, 17))
+
+
+def test_affine_bias_recipe():
+    """affine_bias draws the biases independently of the scales: both signs, within [-0.25, 0.25],
+    mostly far from the zero point -zp * scale; scales and codes are those of the default recipe."""
+    base = synth.make_stack(synth.TINY.shape, 1, 9)
+    st = synth.make_stack(synth.TINY.shape, 1, 9, affine_bias=True)
+    assert torch.equal(st.w13_scales, base.w13_scales) and torch.equal(st.w13_codes, base.w13_codes)
+    for b, s in ((st.w13_biases, st.w13_scales), (st.w2_biases, st.w2_scales), (st.s2_biases, st.s2_scales)):
+        bf = b.float()
+        assert float(bf.min()) >= -0.25 and float(bf.max()) <= 0.25
+        assert float((bf > 0).float().mean()) > 0.4 and float((bf < 0).float().mean()) > 0.4
+        far = (bf + 8.0 * s.float()).abs() > 0.05
+        assert float(far.float().mean()) > 0.7
