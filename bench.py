@@ -391,6 +391,66 @@ def residency_sweep(stack, wl, warmup: int, steps: int, zipf_s):
             "warmup": warmup, "steps": steps, "rows": rows}
 
 
+PHASE_NAMES = ["layer", "input", "router_rows", "logits_put", "x_limbs", "logits_got", "topk", "shared_gu",
+               "routed_issued", "routed_landed", "routed_done", "down_issued", "h_got", "down_done", "y_put",
+               "layer_end"]
+REALTIME_HZ = 100e6  # s_memrealtime counts at 100 MHz
+
+
+def phase_profile(stack, wl, T: int, warmup: int, steps: int, chained: bool):
+    """Per-phase timing of the decode kernel from the phase-timer build of the library: every
+    workgroup's wave 0 stamps the 100 MHz real-time counter at each phase mark of every layer. For a
+    mark m of a layer, crit(m) is the time the last workgroup passed it; the critical-path share of
+    phase m is crit(m) - crit(m - 1) (from crit(layer_end) of the previous layer for the first mark),
+    the typical share the median over workgroups of their own t(m) - t(m - 1), and the skew the
+    spread of the workgroups' t(m). Medians over the steps and the layers 1 .. L-1."""
+    import numpy as np
+    import torch
+
+    import quantized_moe_decode_router_amd as moe
+    import synth
+
+    assert moe.LIB_PATH.endswith("libmoe_amd_phase.so"), "the phase-timer library is not loaded"
+    shape, L = wl.shape, stack.n_layers
+    dev = stack.router.device
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    ws = moe.workspace(shape, T, moe.MOE_WS_STACK, dev, n_layers=L)
+    nm = len(PHASE_NAMES)
+    ph = ws[256:256 + 8 * L * 1024 * nm].view(torch.int64)[: L * grid * nm]
+    y = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
+    flags = 0 if chained else moe.MOE_STACK_INDEPENDENT
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    crit, typ, skew, layer_us, ratio = [], [], [], [], []
+    for s in range(warmup + steps):
+        x = synth.make_x(shape, T, wl.seed, step=s, device=dev)
+        a.record(stream)
+        moe.moe_stack_decode(shape, stack, L, x, T, y, workspace=ws, stream=stream, flags=flags)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if s < warmup:
+            continue
+        t = ph.cpu().numpy().reshape(L, grid, nm).astype(np.float64) / REALTIME_HZ * 1e6  # us
+        c = t.max(axis=1)  # [L][nm]: the last workgroup at each mark
+        span = t[L - 1, :, nm - 1].max() - t[0, :, 0].min()
+        ratio.append(span / (a.elapsed_time(b) * 1e3))
+        for l in range(1, L):
+            prev = c[l - 1, nm - 1]
+            cl = np.concatenate([[prev], c[l]])
+            crit.append(np.diff(cl))
+            d = np.diff(t[l], axis=1)
+            typ.append(np.concatenate([[np.median(t[l, :, 0] - t[l - 1, :, nm - 1])], np.median(d, axis=0)]))
+            skew.append(t[l].max(axis=0) - t[l].min(axis=0))
+            layer_us.append(c[l, nm - 1] - prev)
+    crit, typ, skew = np.median(crit, axis=0), np.median(typ, axis=0), np.median(skew, axis=0)
+    rows = [{"phase": f"{PHASE_NAMES[m - 1] if m else 'layer_end(prev)'} -> {PHASE_NAMES[m]}",
+             "critical_us": round(float(crit[m]), 3), "typical_us": round(float(typ[m]), 3),
+             "skew_at_mark_us": round(float(skew[m]), 3)} for m in range(nm)]
+    return {"workload": wl.name, "tokens_per_step": T, "layers": L, "chained": chained, "grid": grid,
+            "steps": steps, "layer_us_median": round(float(np.median(layer_us)), 3),
+            "stamp_span_over_event_time": round(float(np.median(ratio)), 4), "phases": rows}
+
+
 def stack_name(stack) -> str:
     s = stack.shape
     return f"H{s.hidden}_E{s.num_experts}_K{s.top_k}_I{s.inter}_Is{s.shared_inter}_{s.bits}bit"
@@ -418,6 +478,8 @@ def main():
     ap.add_argument("--residency-warmup", type=int, default=100)
     ap.add_argument("--sweep", action="store_true",
                     help="only the decode / batched crossover sweep of one layer (one JSON line)")
+    ap.add_argument("--phases", action="store_true",
+                    help="only the per-phase timing of the decode kernel, from the phase-timer build (one JSON line)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -425,6 +487,8 @@ def main():
               "collectives are built); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.phases:
+        os.environ["MOE_AMD_PHASE_TIMER"] = "1"  # before the binding is imported
     import torch
     import quantized_moe_decode_router_amd as moe
 
@@ -440,6 +504,10 @@ def main():
           f"{time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
     if args.sweep:
         print(json.dumps({"sweep": crossover_sweep(stack, reps=50)}), flush=True)
+        return
+    if args.phases:
+        print(json.dumps({"phases": phase_profile(stack, wl, T, warmup=args.warmup, steps=args.steps,
+                                                  chained=not args.independent)}), flush=True)
         return
     if args.residency:
         print(json.dumps({"residency": residency_sweep(stack, wl, warmup=args.residency_warmup,

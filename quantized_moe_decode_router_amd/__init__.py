@@ -2,7 +2,7 @@
 
 The Python surface is the ctypes binding of include/moe.h (same names, marshalling only).
 Build the library with `quantized_moe_decode_router_amd.build.build()`."""
-from .binding import (MOE_DEFAULT_CROSSOVER, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_TIMEOUT,  # noqa: F401
+from .binding import (LIB_PATH, MOE_DEFAULT_CROSSOVER, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_TIMEOUT,  # noqa: F401
                       MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_OK, MOE_PATH_BATCHED, MOE_PATH_DECODE,
                       MOE_ROUTE_LOGITS_IN, MOE_STACK_INDEPENDENT, MOE_WS_BATCHED, MOE_WS_DECODE,
                       MOE_WS_FORWARD, MOE_WS_STACK, MoeError, lib, moe_group_pairs, moe_layer_batched,

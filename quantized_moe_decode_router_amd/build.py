@@ -1,7 +1,11 @@
 """Compile the HIP library (libmoe_amd.so) for gfx950 with hipcc, in-tree.
 
 Every kernel and the C ABI live under csrc/; the result is a plain C-ABI shared object that the
-ctypes binding loads. Compiled with packed-FP32 instructions disabled."""
+ctypes binding loads. Compiled with packed-FP32 instructions disabled.
+
+build(phase_timer=True) compiles the same sources with MOE_PHASE_TIMER into libmoe_amd_phase.so:
+the decode kernel then stamps the real-time counter at the phase marks of every layer into the
+workspace (bench.py --phases loads that library and summarises the stamps)."""
 from __future__ import annotations
 
 import os
@@ -12,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libmoe_amd.so")
+PHASE_LIB = os.path.join(LIBDIR, "libmoe_amd_phase.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 SOURCES = ["moe_abi.cpp", "residency.cpp", "decode.hip", "route.hip", "batched.hip"]
 ARCH = "gfx950"
@@ -30,15 +35,18 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, phase_timer: bool = False) -> str:
     """Compile every source (always; callers rely on this being a real build check) and link."""
-    os.makedirs(LIBDIR, exist_ok=True)
+    objdir = os.path.join(LIBDIR, "phase") if phase_timer else LIBDIR
+    lib = PHASE_LIB if phase_timer else LIB
+    extra = ["-DMOE_PHASE_TIMER"] if phase_timer else []
+    os.makedirs(objdir, exist_ok=True)
     objs = []
     procs = []
     for src in SOURCES:
-        obj = os.path.join(LIBDIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [_hipcc()] + HIPCC_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [_hipcc()] + HIPCC_FLAGS + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), file=sys.stderr)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -54,12 +62,12 @@ def build(verbose: bool = False) -> str:
             print(out, file=sys.stderr)
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, phase_timer="--phase-timer" in sys.argv))

@@ -45,6 +45,39 @@ __device__ __forceinline__ __attribute__((address_space(1))) T *G(T *p) {
     return (__attribute__((address_space(1))) T *)p;
 }
 
+// ---- phase timer (compile-time option MOE_PHASE_TIMER) -------------------------------------------
+// Wave 0 of every workgroup stamps the 100 MHz real-time counter at each of kPhaseMarks marks of a
+// layer into the workspace (p.phase[l][block][mark]); bench.py --phases reads and summarises them.
+// In the default build the marks compile to nothing.
+enum PhaseMark {
+    kMarkLayer = 0,      // top of the layer
+    kMarkInput,          // x of every token in LDS (y of the previous layer gathered, RMS glue)
+    kMarkRouterRows,     // this layer's router and shared rows landed
+    kMarkLogitsPut,      // this workgroup's logits published
+    kMarkXLimbs,         // x as limbs
+    kMarkLogitsGot,      // every logit gathered
+    kMarkTopk,           // expert selection done (wave 0: token 0)
+    kMarkSharedGu,       // shared gate|up done, routing published to the workgroup
+    kMarkRoutedIssued,   // first chunk of routed gate|up rows issued
+    kMarkRoutedLanded,   // first chunk landed
+    kMarkRoutedDone,     // every routed gate|up pair computed, h published
+    kMarkDownIssued,     // routed down rows (and next shared gate|up rows) issued
+    kMarkHGot,           // every h of token 0 gathered, down rows landed
+    kMarkDownDone,       // down projections of every token done
+    kMarkYPut,           // y published
+    kMarkLayerEnd        // next layer's shared down rows issued
+};
+#ifdef MOE_PHASE_TIMER
+__device__ __forceinline__ void phase_mark(uint64_t *ph, int l, int m) {
+    if (threadIdx.x == 0 && ph) {
+        const uint64_t t = __builtin_amdgcn_s_memrealtime();
+        ((__attribute__((address_space(1))) uint64_t *)ph)[((size_t)l * gridDim.x + blockIdx.x) * kPhaseMarks + m] = t;
+    }
+}
+#else
+__device__ __forceinline__ void phase_mark(uint64_t *, int, int) {}
+#endif
+
 // ---- exchange words ---------------------------------------------------------------------------
 __device__ __forceinline__ void ll_put(uint64_t *p, float v, uint32_t ep) {
     const uint64_t w = (static_cast<uint64_t>(ep) << 32) | __float_as_uint(v);
@@ -987,18 +1020,25 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         uint64_t *ll_h = p.ll_h + (size_t)l * T * HW;
         uint64_t *ll_y = p.ll_y + (size_t)l * T * H;
 
+        phase_mark(p.phase, l, kMarkLayer);
         if (!layer_input<BITS>(p, l, ep, s, spin)) { dma_wait(); return; }
+        phase_mark(p.phase, l, kMarkInput);
         dma_wait();  // this layer's router and shared rows (staged during the previous layer)
         lds_barrier();
+        phase_mark(p.phase, l, kMarkRouterRows);
 
         // ---- R: router logits from LDS, then x as limbs (its barriers also end this phase)
         router_logits<BITS>(p, l, s, w, ll_lg, ep);
         if (!Is && b == 0 && tid < T) ll_put(ll_lg + (size_t)tid * (E + 1) + E, 0.0f, ep);  // unused column
+        phase_mark(p.phase, l, kMarkLogitsPut);
         build_x_limbs<BITS>(p, s);
+        phase_mark(p.phase, l, kMarkXLimbs);
 
         // ---- G: routing (identical in every workgroup), then routed gate|up + SwiGLU
         if (!ll_gather(ll_lg, T * (E + 1), ep, s.lg, p.ctrl, spin)) { dma_wait(); return; }
+        phase_mark(p.phase, l, kMarkLogitsGot);
         route_tokens(p, s);
+        phase_mark(p.phase, l, kMarkTopk);
         // layer l+1's router rows (the LDS copy was last read before the logits exchange) stream in
         // during the expert selection, issued by waves with nothing else to do then
         if (has_next) {
@@ -1015,6 +1055,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         } else {
             lds_barrier();
         }
+        phase_mark(p.phase, l, kMarkSharedGu);
         if (b == 0) {
             const size_t base = (size_t)l * T;
             if (p.idx_all)
@@ -1050,8 +1091,10 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
                               },
                               rg, mfma_swz(BITS, H));
                 }
+                if (c0 == 0) phase_mark(p.phase, l, kMarkRoutedIssued);
                 dma_wait();
                 lds_barrier();
+                if (c0 == 0) phase_mark(p.phase, l, kMarkRoutedLanded);
                 gate_up_mfma<BITS, false>(
                     p, s, rg, nc, [&](int i) { return div_by((pb + i) >> lgI, kdiv); },
                     [&](int i, int) {
@@ -1084,17 +1127,20 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         // Token 0's routed down rows, then layer l+1's shared gate|up rows (the shared gate|up of this
         // layer is done), stream in during the h exchange; the down projection waits for the routed
         // down rows only.
+        phase_mark(p.phase, l, kMarkRoutedDone);
         stage_routed_down<XT>(p, l, s, 0, r0, nr, w.nrm);
         int later = 0;  // DMA instructions this wave issued after the routed down rows
         if (has_next) {
             stage_shared_gu(p, l + 1, s, w);
             later = w.nps ? dma_qrows_count(2 * w.nps, H, BITS) : 0;
         }
+        phase_mark(p.phase, l, kMarkDownIssued);
         for (int t = 0; t < T; ++t) {
             if (!stage_hq<BITS>(p, s, ll_h + (size_t)t * HW, ep, spin)) { dma_wait(); return; }
             if (t == 0) dma_wait_but(later);
             else dma_wait();
             lds_barrier();
+            if (t == 0) phase_mark(p.phase, l, kMarkHGot);
             if (nr > 0) {
                 float *pt = s.part + (size_t)t * (K + 1) * RB;
                 down_all_mfma<BITS>(s, rd_rows(p, s), sd_rows(p, s), K, I, Is, nr, w.nrm, pt, RB);
@@ -1117,6 +1163,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
             lds_barrier();
             if (t + 1 < T) stage_routed_down<XT>(p, l, s, t + 1, r0, nr, w.nrm);
         }
+        phase_mark(p.phase, l, kMarkDownDone);
         for (int i = tid; i < T * nr; i += blockDim.x) {
             const int t = div_by(i, w.nrm), rl = i - t * nr;
             const float *pt = s.part + t * (K + 1) * RB;
@@ -1128,8 +1175,10 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
             if (!has_next) G(p.y_out)[o] = acc;
             if (p.y_all) G(p.y_all)[(size_t)l * T * H + o] = acc;
         }
+        phase_mark(p.phase, l, kMarkYPut);
         lds_barrier();
         if (has_next) stage_shared_down(p, l + 1, s, r0, nr);  // streams in during the y exchange
+        phase_mark(p.phase, l, kMarkLayerEnd);
     }
     dma_wait();
     // the next call may advance the epoch once every workgroup has read it

@@ -168,6 +168,7 @@ moe_status decode_common(const moe_shape *s, const moe_layer *L, int32_t n_layer
     const moe::DecodeWs lay = moe::decode_ws_layout(n_layers, T, s->hidden, s->num_experts, s->top_k, s->inter,
                                                     s->shared_inter);
     p.ctrl = reinterpret_cast<int *>(w);
+    p.phase = lay.phase ? reinterpret_cast<uint64_t *>(w + lay.phase) : nullptr;
     p.ll_start = reinterpret_cast<uint64_t *>(w + lay.start);
     p.ll_logits = reinterpret_cast<uint64_t *>(w + lay.logits);
     p.ll_h = reinterpret_cast<uint64_t *>(w + lay.h);

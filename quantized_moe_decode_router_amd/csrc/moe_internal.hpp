@@ -50,8 +50,10 @@ struct DecodeParams {
     uint64_t xstride;      // block bytes
     char *landing;         // or null: [L][T][K] blocks; rows staged from a marked block are stored
                            // to the block of their (layer, token, slot)
+    // phase-timer build only (MOE_PHASE_TIMER): [L][grid][kPhaseMarks] real-time stamps, else null
+    uint64_t *phase;
     // workspace (zero-filled before first use)
-    int *ctrl;               // [0] status, [1] call sequence number
+    int *ctrl;               // [0] status, [1] call sequence number, [2] wait bound (0 = default)
     uint64_t *ll_start;      // [grid]               one word per workgroup: "this call has started"
     uint64_t *ll_logits;     // [L][T][E+1]          router logits, column E = shared-gate logit
     uint64_t *ll_h;          // [L][T][K*I + Is]     routed h of slots 0..K-1, then the shared expert's h
@@ -86,14 +88,21 @@ constexpr size_t kCtrlBytes = 256;
 
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace layout of the decode kernel (bytes from the workspace base).
+// Workspace layout of the decode kernel (bytes from the workspace base). A library built with
+// MOE_PHASE_TIMER keeps the per-layer phase stamps of every workgroup right after the control block.
 struct DecodeWs {
-    size_t start, logits, h, y, total;
+    size_t phase, start, logits, h, y, total;
 };
 constexpr int kMaxGrid = 1024;
+constexpr int kPhaseMarks = 16;
 __host__ __device__ inline DecodeWs decode_ws_layout(int L, int T, int H, int E, int K, int I, int Is) {
     DecodeWs w;
     size_t o = kCtrlBytes;
+#ifdef MOE_PHASE_TIMER
+    w.phase = o;  o = align_up(o + 8 * (size_t)L * kMaxGrid * kPhaseMarks, 256);
+#else
+    w.phase = 0;
+#endif
     w.start = o;  o = align_up(o + 8 * (size_t)kMaxGrid, 256);
     w.logits = o; o = align_up(o + 8 * (size_t)L * T * (E + 1), 256);
     w.h = o;      o = align_up(o + 8 * (size_t)L * T * ((size_t)K * I + Is), 256);
