@@ -187,6 +187,27 @@ moe_status moe_stack_decode(const moe_shape *shape, const moe_layer *stack, int3
                             float *topk_w_all_opt, float *logits_all_opt, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* moe_stack_decode_static flag: clear the fixed scratch (and with it a sticky status) first */
+#define MOE_STATIC_RESET 2u
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. moe_stack_decode (same arguments, same results bit for
+ * bit) with no workspace argument: the call's exchange words and status live in a fixed scratch
+ * array of 32 MiB per device that the library holds from its first use on that device until the
+ * process ends (the stack's moe_workspace_bytes(..., MOE_WS_STACK) must fit: MOE_ERR_WORKSPACE
+ * otherwise). The call allocates nothing and calls no allocating routine. The scratch is cleared
+ * on the stream by a fill kernel at the first call on each device, and again when flags holds
+ * MOE_STATIC_RESET; otherwise it keeps the previous call's contents, as a workspace does (a sticky
+ * MOE_ERR_TIMEOUT stays until a call with MOE_STATIC_RESET). Every call on one device shares the
+ * same scratch: calls that overlap on one device (different streams or threads) race and give
+ * undefined results. flags: MOE_STACK_INDEPENDENT and/or MOE_STATIC_RESET.
+ */
+moe_status moe_stack_decode_static(const moe_shape *shape, const moe_layer *stack, int32_t n_layers,
+                                   uint32_t flags, const uint16_t *x, int32_t T, float *y,
+                                   uint16_t *x_all_opt, float *y_all_opt, int32_t *topk_idx_all_opt,
+                                   float *topk_w_all_opt, float *logits_all_opt, void *stream);
+
 /*
  * Pages: the same layer as moe_layer_decode (same citations), evaluated for many tokens per call;
  * the pages pick a quantised-matmul route by batch size and sweep its boundary (Smelt README, "Lab

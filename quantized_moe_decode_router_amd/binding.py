@@ -31,11 +31,13 @@ MOE_PATH_DECODE, MOE_PATH_BATCHED = 0, 1
 MOE_DEFAULT_CROSSOVER = 8
 
 MOE_STACK_INDEPENDENT = 1
+MOE_STATIC_RESET = 2
 
 EXPORTED = ("moe_route", "moe_layer_decode", "moe_stack_decode", "moe_layer_batched", "moe_group_pairs",
             "moe_layer_path", "moe_layer_forward", "moe_workspace_bytes", "moe_read_status", "moe_status_string",
             "moe_expert_stride", "moe_pack_experts", "moe_stack_decode_table", "moe_layer_batched_table", "moe_cache_create",
-            "moe_cache_update", "moe_cache_admit", "moe_cache_stats", "moe_cache_owners", "moe_cache_destroy", "moe_cache_policy_run")
+            "moe_cache_update", "moe_cache_admit", "moe_cache_stats", "moe_cache_owners", "moe_cache_destroy", "moe_cache_policy_run",
+            "moe_stack_decode_static")
 
 
 class MoeError(RuntimeError):
@@ -79,6 +81,7 @@ def lib():
         L.moe_layer_path.restype = I32
         L.moe_layer_forward.argtypes = [PS, PL, P, I32, I32, P, P, P, P, P, SZ, P]
         L.moe_stack_decode.argtypes = [PS, PL, I32, U32, P, I32, P, P, P, P, P, P, P, SZ, P]
+        L.moe_stack_decode_static.argtypes = [PS, PL, I32, U32, P, I32, P, P, P, P, P, P, P]
         L.moe_stack_decode_table.argtypes = [PS, PL, I32, P, P, SZ, U32, P, I32, P, P, P, P, P, P, P, SZ, P]
         L.moe_layer_batched_table.argtypes = [PS, PL, P, P, I32, P, P, P, P, P, SZ, P]
         L.moe_expert_stride.argtypes = [PS]
@@ -219,6 +222,18 @@ def moe_stack_decode(shape, stack, n_layers: int, x, T: int, y, x_all=None, y_al
                                 _ptr(logits_all, "logits_all", torch.float32), _ptr(workspace, "workspace"),
                                 int(wsb), _stream(stream))
     _check(st, "moe_stack_decode")
+
+
+def moe_stack_decode_static(shape, stack, n_layers: int, x, T: int, y, x_all=None, y_all=None, topk_idx_all=None,
+                            topk_w_all=None, logits_all=None, stream=None, flags: int = 0) -> None:
+    s, L = shape_struct(shape), layer_struct(stack)
+    st = lib().moe_stack_decode_static(ctypes.byref(s), ctypes.byref(L), int(n_layers), int(flags),
+                                       _ptr(x, "x", _BF16_BITS), int(T), _ptr(y, "y", torch.float32),
+                                       _ptr(x_all, "x_all", _BF16_BITS), _ptr(y_all, "y_all", torch.float32),
+                                       _ptr(topk_idx_all, "topk_idx_all", torch.int32),
+                                       _ptr(topk_w_all, "topk_w_all", torch.float32),
+                                       _ptr(logits_all, "logits_all", torch.float32), _stream(stream))
+    _check(st, "moe_stack_decode_static")
 
 
 def moe_layer_batched(shape, layer, x, T: int, y, topk_idx=None, topk_w=None, logits=None,

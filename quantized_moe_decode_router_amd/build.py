@@ -18,7 +18,7 @@ LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libmoe_amd.so")
 PHASE_LIB = os.path.join(LIBDIR, "libmoe_amd_phase.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
-SOURCES = ["moe_abi.cpp", "residency.cpp", "decode.hip", "route.hip", "batched.hip"]
+SOURCES = ["moe_abi.cpp", "residency.cpp", "decode.hip", "route.hip", "batched.hip", "static_scratch.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -281,6 +281,23 @@ moe_status moe_stack_decode(const moe_shape *s, const moe_layer *stack, int32_t 
                          logits_all_opt, ws, ws_bytes, stream);
 }
 
+moe_status moe_stack_decode_static(const moe_shape *s, const moe_layer *stack, int32_t n_layers, uint32_t flags,
+                                   const uint16_t *x, int32_t T, float *y, uint16_t *x_all_opt, float *y_all_opt,
+                                   int32_t *idx_all_opt, float *w_all_opt, float *logits_all_opt, void *stream) {
+    if (flags & ~(MOE_STACK_INDEPENDENT | MOE_STATIC_RESET)) return MOE_ERR_INVALID_ARG;
+    moe_status st = check_shape(s);
+    if (st != MOE_OK) return st;
+    if (n_layers < 1 || n_layers > kMaxLayers || T < 1 || T > kMaxDecodeT) return MOE_ERR_INVALID_ARG;
+    const size_t need = decode_ws_bytes(s, T, n_layers);
+    if (need > moe::kStaticScratchBytes) return MOE_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (moe::static_scratch(need, (flags & MOE_STATIC_RESET) != 0, static_cast<hipStream_t>(stream), &ws) !=
+        hipSuccess)
+        return MOE_ERR_HIP;
+    return decode_common(s, stack, n_layers, flags & MOE_STACK_INDEPENDENT, x, T, y, x_all_opt, y_all_opt,
+                         idx_all_opt, w_all_opt, logits_all_opt, ws, need, stream);
+}
+
 moe_status moe_stack_decode_table(const moe_shape *s, const moe_layer *stack, int32_t n_layers,
                                   const uint64_t *expert_table, void *landing_opt, size_t landing_bytes,
                                   uint32_t flags,

@@ -275,4 +275,10 @@ hipError_t launch_router_topk(const BatchedParams &p, hipStream_t stream);
 // Query (and cache per device) the compute-unit count.
 int device_cu_count();
 
+// The fixed device scratch of moe_stack_decode_static (one per device, held until the process
+// ends): its device address on the current device, cleared on the stream on its first use on that
+// device or when `reset` is set. hipErrorInvalidValue if `need` exceeds it. Allocates nothing.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch(size_t need, bool reset, hipStream_t stream, void **out);
+
 }  // namespace moe
