@@ -104,6 +104,32 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
     return min(min(r0, r1), min(r2, r3));
 }
 
+// Maximum / minimum over the wave left in every lane's VGPR, with no scalar round trip: rows of 16
+// lanes reduced by DPP, then row pairs and wave halves combined by the gfx950 lane swaps
+// (permlane16_swap: odd rows of the first operand <-> even rows of the second; permlane32_swap:
+// upper half of the first <-> lower half of the second; with both operands the same value, the
+// maximum of the two results combines row r with row r ^ 1, then half h with half h ^ 1).
+__device__ __forceinline__ uint32_t wave_max_vgpr(uint32_t v) {
+    v = max(v, dpp_u32<kDppQuadXor1>(v));
+    v = max(v, dpp_u32<kDppQuadXor2>(v));
+    v = max(v, dpp_u32<kDppHalfMirror>(v));
+    v = max(v, dpp_u32<kDppRowMirror>(v));
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max(static_cast<uint32_t>(a[0]), static_cast<uint32_t>(a[1]));
+    const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max(static_cast<uint32_t>(c[0]), static_cast<uint32_t>(c[1]));
+}
+__device__ __forceinline__ uint32_t wave_min_vgpr(uint32_t v) {
+    v = min(v, dpp_u32<kDppQuadXor1>(v));
+    v = min(v, dpp_u32<kDppQuadXor2>(v));
+    v = min(v, dpp_u32<kDppHalfMirror>(v));
+    v = min(v, dpp_u32<kDppRowMirror>(v));
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = min(static_cast<uint32_t>(a[0]), static_cast<uint32_t>(a[1]));
+    const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return min(static_cast<uint32_t>(c[0]), static_cast<uint32_t>(c[1]));
+}
+
 // Partial dot product of an fp32 row with v[0..cols) (cols % 4 == 0).
 __device__ __forceinline__ float frow_dot_partial(const float *row, int cols, const float *v, int lane) {
     float acc = 0.0f;
@@ -132,8 +158,11 @@ constexpr int kTopkMaxE = 1024;
 // Top-k of lt[0..E) (LDS) by one whole wave, NJ = ceil(E / 64) keys per lane (expert e = lane +
 // 64 j in slot j): the K indices with the largest values, ordered by (value descending, index
 // ascending). Exact and deterministic: K rounds of (wave maximum of the remaining keys; the lowest
-// expert index holding it wins; that key is removed). Writes idx[0..K) and the renormalised softmax weights w[0..K) (softmax over the kept
-// logits equals softmax-then-renormalise), the exponentials summed by a fixed lane reduction.
+// expert index holding it wins; that key is removed). Each lane names the lowest index it holds
+// at the maximum; when one lane alone holds it (the usual case) a ballot finds that lane and its
+// index is read from it, else the wave minimum of the named indices decides. Writes idx[0..K) and
+// the renormalised softmax weights w[0..K) (softmax over the kept logits equals
+// softmax-then-renormalise), the exponentials summed by a fixed lane reduction.
 template <int NJ>
 __device__ inline void wave_topk_n(const float *lt, int E, int K, int *idx, float *w) {
     const int lane = threadIdx.x % kWave;
@@ -149,13 +178,17 @@ __device__ inline void wave_topk_n(const float *lt, int E, int K, int *idx, floa
         uint32_t m = key[0];
 #pragma unroll
         for (int j = 1; j < NJ; ++j) m = max(m, key[j]);
-        m = wave_max_u32(m);
-        // the lowest expert index holding the maximum: per lane the first matching slot, then the
-        // wave minimum (all in vector ALU; no scalar round trips)
+        m = wave_max_vgpr(m);
+        // the lowest expert index holding the maximum: per lane its first matching slot
         uint32_t c = 0xFFFFFFFFu;
 #pragma unroll
         for (int j = NJ - 1; j >= 0; --j) c = key[j] == m ? static_cast<uint32_t>(lane + kWave * j) : c;
-        const int win = static_cast<int>(wave_min_u32(c));
+        const unsigned long long holders = __ballot(c != 0xFFFFFFFFu);
+        int win;
+        if (__popcll(holders) == 1)
+            win = __builtin_amdgcn_readlane(static_cast<int>(c), __builtin_amdgcn_readfirstlane(__ffsll(holders) - 1));
+        else
+            win = static_cast<int>(wave_min_vgpr(c));
         if (lane == r) mine = win;
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
