@@ -51,14 +51,17 @@
  *     workspace (bytes 8..11) is the bound in polls of one wait, 0 (as zero-filled) meaning the
  *     default 2^20 polls (well over 0.1 s). A wait that exceeds it sets MOE_ERR_TIMEOUT and every
  *     workgroup of the launch then ends; the outputs are undefined.
- *   - The batched path computes with fp16 MFMA operands: x converted from bf16, the dequantised
- *     weights s * q + b rounded once to fp16, and the SwiGLU output h as fp16 high and low parts.
- *     Each of x, s * q + b and h must therefore lie within fp16's range (|v| <= 65504);
- *     magnitudes below 2^-14 are held as fp16 subnormals (absolute precision 2^-24). An operand
- *     beyond the range makes a gate|up or down accumulator non-finite, and the call then sets the
- *     status word to MOE_ERR_UNSUPPORTED (for moe_layer_forward: the forward workspace's first
- *     word); its outputs are undefined. The decode path has no such limit (its dot products are
- *     exact integer sums on activation limbs, scaled in fp32).
+ *   - The batched path computes with fp16 MFMA operands: x scaled by a power of two per token (any
+ *     bf16 x fits), the dequantised weights s * q + b rounded once to fp16, and the SwiGLU output h
+ *     as fp16 high and low parts, scaled down by a power of two per 128-row tile and 64-column group
+ *     where its magnitude needs it (folded into that group's down weights, so products are
+ *     unchanged). So s, b and s * q + b must lie within fp16's range (|v| <= 65504), and |W2| times
+ *     the largest |h| of a tile must stay below about 2^31; weights and h below 2^-14 in magnitude
+ *     are held as fp16 subnormals (absolute precision 2^-24). A weight beyond the range makes a
+ *     gate|up or down accumulator non-finite, and the call then sets the status word to
+ *     MOE_ERR_UNSUPPORTED (for moe_layer_forward: the forward workspace's first word); its
+ *     outputs are undefined. The decode path has no such limit (its dot products are exact
+ *     integer sums on activation limbs, scaled in fp32).
  *   - Two calls that share a workspace must not run concurrently.
  *   - The decode calls additionally need hidden, inter, shared_inter <= 2048, inter and a
  *     non-zero shared_inter >= 128, and an LDS footprint within 160 KiB (it grows with T); other

@@ -17,11 +17,15 @@
 //                    h lo; epilogue scales by the routing weight (gamma for the shared group)
 //   6. combine       y[t] = sum_k out[pos(t, k)] + out[shared row of t], k = 0..K-1 in order
 //
-// Dequantised weights are s * q + b rounded once to fp16, bf16 activations are converted to fp16
-// (exact in fp16's normal range) and h is held as fp16 hi + lo halves; products are exact in the
-// fp32 accumulators of the MFMA. So x, s * q + b and h must lie within fp16's range (+-65504):
-// an operand beyond it becomes infinite, the accumulators it reaches are not finite, and the
-// epilogues then set the status word to MOE_ERR_UNSUPPORTED (the outputs are then undefined).
+// MFMA operands are fp16, products exact in the fp32 accumulators: x scaled by a power of two per
+// token (x16_kernel: any bf16 x fits), the dequantised weights s * q + b rounded once, and h as fp16
+// hi + lo halves scaled down by a power of two per tile and 64-column group where its magnitude
+// needs it (the down GEMM scales that k-step's dequantised weights up by the same power, so each
+// product is unchanged). So s, b and s * q + b must lie within fp16's range (+-65504), and so must a
+// down weight times that power (|W2| max|h| below ~2^31); a weight beyond it becomes infinite, the
+// accumulators it reaches are not finite, and the epilogues then set the status word to
+// MOE_ERR_UNSUPPORTED (the outputs are then undefined). Weights and h below 2^-14 in magnitude are
+// held as fp16 subnormals.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -30,8 +34,9 @@ namespace moe {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 64;          // pair rows per tile
+constexpr int kBM = kTileRows;   // pair rows per tile
 constexpr int kGemmThreads = 256;
+constexpr int kRing = 4;         // k-steps of operand loads in flight per thread in the grouped GEMMs
 constexpr int kLdsK = 72;        // fp16 per LDS tile row: 64 + 8 padding (16 bytes)
 
 __device__ __forceinline__ _Float16 bf16_to_f16(uint16_t b) { return (_Float16)bf16_to_f32(b); }
@@ -192,6 +197,8 @@ __global__ void __launch_bounds__(kBucketThreads) bucket_kernel(BatchedParams p)
     int *gcnt = reinterpret_cast<int *>(reinterpret_cast<unsigned long long *>(smem) + (size_t)kBucketWaves * E);
     int *goff = gcnt + (E + 1);
     int *gtoff = goff + (E + 2);
+    int *guoff = gtoff + (E + 2);  // first gate|up work item of each group
+    int *dnoff = guoff + (E + 2);  // first down work item of each group
     const unsigned long long below = (1ull << lane) - 1ull;
 
     for (int blk = wave; blk < nblk; blk += kBucketWaves) {
@@ -238,31 +245,45 @@ __global__ void __launch_bounds__(kBucketThreads) bucket_kernel(BatchedParams p)
     }
     if (tid == 0 && p.Is) gcnt[E] = T;
     __syncthreads();
-    // exclusive scans of the group sizes and of their tile counts, by wave 0: lane l owns a chunk
+    // exclusive scans of the group sizes, their tile counts and their gate|up and down work items
+    // (tiles x column blocks), by wave 0: lane l owns a chunk
+    const int ndn = p.H / kDnCols;
+    auto ngu_of = [&](int g) { return (g < E ? p.I : p.Is) / kGuCols; };
     if (wave == 0) {
         const int chunk = (ng + kWave - 1) / kWave;
         const int g0 = min(ng, lane * chunk), g1 = min(ng, g0 + chunk);
-        int s = 0, st = 0;
+        int s = 0, st = 0, su = 0, sd = 0;
         for (int g = g0; g < g1; ++g) {
+            const int nt = (gcnt[g] + kBM - 1) / kBM;
             s += gcnt[g];
-            st += (gcnt[g] + kBM - 1) / kBM;
+            st += nt;
+            su += nt * ngu_of(g);
+            sd += nt * ndn;
         }
-        int is = s, ist = st;  // inclusive wave scans
+        int is = s, ist = st, isu = su, isd = sd;  // inclusive wave scans
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) {
             const int a = __shfl_up(is, o, kWave), b = __shfl_up(ist, o, kWave);
-            if (lane >= o) { is += a; ist += b; }
+            const int c = __shfl_up(isu, o, kWave), d = __shfl_up(isd, o, kWave);
+            if (lane >= o) { is += a; ist += b; isu += c; isd += d; }
         }
-        int run = is - s, trun = ist - st;
+        int run = is - s, trun = ist - st, urun = isu - su, drun = isd - sd;
         for (int g = g0; g < g1; ++g) {
+            const int nt = (gcnt[g] + kBM - 1) / kBM;
             goff[g] = run;
             gtoff[g] = trun;
+            guoff[g] = urun;
+            dnoff[g] = drun;
             run += gcnt[g];
-            trun += (gcnt[g] + kBM - 1) / kBM;
+            trun += nt;
+            urun += nt * ngu_of(g);
+            drun += nt * ndn;
         }
         if (lane == kWave - 1) {
             goff[ng] = is;
             gtoff[ng] = ist;
+            guoff[ng] = isu;
+            dnoff[ng] = isd;
         }
     }
     __syncthreads();
@@ -270,10 +291,56 @@ __global__ void __launch_bounds__(kBucketThreads) bucket_kernel(BatchedParams p)
         p.goff[g] = goff[g];
         if (g < ng) p.gcnt[g] = gcnt[g];
     }
-    if (tid == 0) p.ntiles[0] = gtoff[ng];
+    if (tid == 0) {
+        p.ntiles[0] = gtoff[ng];
+        p.ntiles[1] = guoff[ng];
+        p.ntiles[2] = dnoff[ng];
+    }
     for (int g = tid; g < ng; g += kBucketThreads) {
         const int nt = (gcnt[g] + kBM - 1) / kBM;
         for (int i = 0; i < nt; ++i) p.tiles[gtoff[g] + i] = make_int2(g, i * kBM);
+    }
+    // work items of the grouped GEMMs, longest first: bucketed by the tile's row count (a counting
+    // sort, 128 rows down to 1), so that the workgroups taken in list order fill the compute units
+    // greedily and the heavy tiles do not form the tail. Within a bucket the order is arbitrary
+    // (each item writes its own block of the output, so it does not change any result).
+    if (p.wgu) {
+        int *hgu = dnoff + (E + 2), *hdn = hgu + (kBM + 1);  // [kBM + 1] each: counts, then cursors
+        for (int i = tid; i <= kBM; i += kBucketThreads) hgu[i] = hdn[i] = 0;
+        __syncthreads();
+        for (int g = tid; g < ng; g += kBucketThreads) {
+            const int nt = (gcnt[g] + kBM - 1) / kBM, ngu = ngu_of(g);
+            for (int i = 0; i < nt; ++i) {
+                const int rows = min(kBM, gcnt[g] - i * kBM);
+                atomicAdd(&hgu[rows], ngu);
+                atomicAdd(&hdn[rows], ndn);
+            }
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int ru = 0, rd = 0;
+            for (int r = kBM; r >= 1; --r) {
+                const int cu = hgu[r], cd = hdn[r];
+                hgu[r] = ru;
+                hdn[r] = rd;
+                ru += cu;
+                rd += cd;
+            }
+        }
+        __syncthreads();
+        for (int g = wave; g < ng; g += kBucketWaves) {
+            const int nt = (gcnt[g] + kBM - 1) / kBM, ngu = ngu_of(g);
+            for (int i = lane; i < nt * max(ngu, ndn); i += kWave) {
+                const int mi = i % nt, col = i / nt, m0 = mi * kBM;
+                const int rows = min(kBM, gcnt[g] - m0);
+                if (col < ngu)
+                    p.wgu[atomicAdd(&hgu[rows], 1)] =
+                        make_int4(g, goff[g] + m0, rows | (col * kGuCols) << 16, gtoff[g] + mi);
+                if (col < ndn)
+                    p.wdn[atomicAdd(&hdn[rows], 1)] =
+                        make_int4(g, goff[g] + m0, rows | (col * kDnCols) << 16, gtoff[g] + mi);
+            }
+        }
     }
     // scatter
     for (int q = tid; q < T * K; q += kBucketThreads) {
@@ -322,6 +389,21 @@ __device__ __forceinline__ GroupW group_w2(const BatchedParams &p, int g) {
     return {p.s2.c, p.s2.s, p.s2.b, p.Is};
 }
 
+// Global-memory view of a pointer: loads through it compile to global (not flat) instructions,
+// which count against the vector-memory counter only, so waiting for a load never also waits for
+// LDS traffic (and LDS waits never wait for the weight loads in flight).
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T *gp(const T *p) {
+    return (const __attribute__((address_space(1))) T *)p;
+}
+
+// A 16-byte global load (through a native vector type: HIP's uint4 has no address-space load).
+typedef unsigned int u32x4n_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gload16(const void *p) {
+    const u32x4n_t v = *(const __attribute__((address_space(1))) u32x4n_t *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // A non-finite accumulator: an fp16 operand was out of range (see the file header).
 __device__ __forceinline__ void flag_unsupported(int *status) {
     __hip_atomic_store(status, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -363,309 +445,425 @@ __device__ __forceinline__ half2_t bf16_splat_f16(uint16_t v) {
     const _Float16 h = (_Float16)bf16_to_f32(v);
     return half2_t{h, h};
 }
-// 16 bf16 activations (natural order) -> 16 fp16 in pair order (two blocks of 8 or four of 4).
+// 8 bf16 activations (natural order) times 2^sh -> 8 fp16 in pair order (4-bit: one block of 8;
+// 8-bit: two blocks of 4).
 template <int BITS>
-__device__ __forceinline__ void act16_to_pairs(const uint4 r0, const uint4 r1, half2_t *out) {
-    const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-    uint16_t x[16];
+__device__ __forceinline__ void act16_to_pairs8(const uint4 r, int sh, half2_t *out) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        x[2 * i] = w[i] & 0xFFFF;
-        x[2 * i + 1] = w[i] >> 16;
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = ldexpf(bf16_to_f32(w[i] & 0xFFFF), sh);
+        v[2 * i + 1] = ldexpf(bf16_to_f32(w[i] >> 16), sh);
     }
+    if constexpr (BITS == 4) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-        const uint16_t *v = x + 8 * blk;
-        if constexpr (BITS == 4) {
-#pragma unroll
-            for (int p = 0; p < 4; ++p) out[4 * blk + p] = bf16_pair_to_f16(v[p], v[p + 4]);
-        } else {
-            out[4 * blk + 0] = bf16_pair_to_f16(v[0], v[2]);
-            out[4 * blk + 1] = bf16_pair_to_f16(v[1], v[3]);
-            out[4 * blk + 2] = bf16_pair_to_f16(v[4], v[6]);
-            out[4 * blk + 3] = bf16_pair_to_f16(v[5], v[7]);
-        }
+        for (int q = 0; q < 4; ++q) out[q] = half2_t{(_Float16)v[q], (_Float16)v[q + 4]};
+    } else {
+        out[0] = half2_t{(_Float16)v[0], (_Float16)v[2]};
+        out[1] = half2_t{(_Float16)v[1], (_Float16)v[3]};
+        out[2] = half2_t{(_Float16)v[4], (_Float16)v[6]};
+        out[3] = half2_t{(_Float16)v[5], (_Float16)v[7]};
     }
 }
 
-// ---- 4. grouped gate|up + SwiGLU -----------------------------------------------------------------
-// Tile: 64 pair rows x 64 j (128 weight rows: 64 gate then 64 up), k-steps of 64 columns of H (one
-// quantisation group). Wave w: rows 32 (w & 1) .. +32, j 32 (w >> 1) .. +32; 2 x 2 MFMA tiles each
-// for gate and up, so a lane holds gate and up of the same (row, j) and SwiGLU needs no exchange.
-// Global loads run two k-steps ahead of the MFMAs (register stages S0 / S1).
+// ---- x as fp16 -------------------------------------------------------------------------------------
+// x16[t] = x[t] * 2^-xe[t] in fp16, columns in pair order (the order of dequant_dword's output),
+// with xe[t] = E - 15 for the token's largest magnitude in [2^(E-1), 2^E): the token's values fill
+// fp16's range up to 2^15 whatever their bf16 magnitude (only values more than 2^29 below the
+// token's largest become fp16 subnormals); the power-of-two scaling is exact and the gate|up
+// epilogue multiplies it back. One workgroup per token.
+constexpr int kX16Threads = 256;
 template <int BITS>
-struct GuStage {
-    uint4 a0, a1;      // 16 bf16 of activation row ar
-    uint4 c0, c1;      // 32 codes of weight row br (c1 only at 8-bit)
-    uint16_t s, b;     // that row's group scale and bias
+__global__ void __launch_bounds__(kX16Threads) x16_kernel(BatchedParams p) {
+    __shared__ float red[kX16Threads / kWave];
+    const int t = blockIdx.x, H = p.H, tid = threadIdx.x;
+    const uint16_t *xr = p.x + (size_t)t * H;
+    float amax = 0.0f;
+    for (int c = tid * 8; c < H; c += kX16Threads * 8) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(xr + c);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(w[i] & 0xFFFF)), fabsf(bf16_to_f32(w[i] >> 16))));
+    }
+    amax = __int_as_float((int)wave_max_u32(__float_as_uint(amax)));  // non-negative floats order as integers
+    if (tid % kWave == 0) red[tid / kWave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    int e = 0;
+    if (amax > 0.0f) {
+        frexpf(amax, &e);
+        e -= 15;
+    }
+    for (int c = tid * 8; c < H; c += kX16Threads * 8) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(xr + c);
+        half2_t hv[4];
+        act16_to_pairs8<BITS>(v, -e, hv);
+        *reinterpret_cast<uint4 *>(p.x16 + (size_t)t * H + c) = __builtin_bit_cast(uint4, hv);
+    }
+    if (tid == 0) p.xe[t] = e;
+}
+
+// ---- 4 / 5. grouped GEMMs --------------------------------------------------------------------------
+// Both GEMMs run one work item per workgroup of 256 threads (4 waves): a tile of up to 128 pair rows
+// of one group against a block of the group's weight rows, k-steps of 64 columns (one quantisation
+// group). Operands are fp16 in LDS, each tile row 64 values = eight 16-byte chunks stored at
+// chunk ^ (row & 7), so the 16 rows an MFMA fragment read takes at one chunk spread over the banks.
+// The LDS tiles are double buffered, with one LDS-only barrier per k-step (a full workgroup barrier
+// would also wait for every global load in flight, draining the register prefetch each k-step). Block b runs work item b of a list ordered longest first (see bucket_kernel).
+__device__ __forceinline__ int list_item(int n) { return (int)blockIdx.x < n ? (int)blockIdx.x : -1; }
+__device__ __forceinline__ int chunk_pos(int row, int c) { return c ^ (row & 7); }
+
+// The fp16 value of a bf16 scale or bias times 2^e (exact for finite in-range results).
+__device__ __forceinline__ half2_t bf16_splat_f16_scaled(uint16_t v, float f) {
+    const _Float16 h = (_Float16)(bf16_to_f32(v) * f);
+    return half2_t{h, h};
+}
+
+// One thread's share of a 64-column k-step of 64 weight rows' codes: 32 columns (4-bit: 16 bytes,
+// 8-bit: 32 bytes), plus that row's scale and bias.
+template <int BITS>
+struct BLoad {
+    uint4 c0, c1;
+    uint16_t s, b;
 };
 template <int BITS>
-__global__ void __launch_bounds__(kGemmThreads) gu_gemm(BatchedParams p) {
-    __shared__ __align__(16) _Float16 As[kBM][kLdsK];
-    __shared__ __align__(16) _Float16 Bs[128][kLdsK];
-    const int tile = blockIdx.x;
-    if (tile >= p.ntiles[0]) return;
-    const int2 tg = p.tiles[tile];
-    const int g = tg.x, m0 = tg.y;
-    const GroupW w = group_w13(p, g);
-    const int j0 = blockIdx.y * 64;
-    if (j0 >= w.inter) return;
+__device__ __forceinline__ BLoad<BITS> b_load(const uint8_t *crow, const uint16_t *srow, const uint16_t *brow,
+                                               int kb, int half) {
+    BLoad<BITS> L;
+    const uint8_t *cp = crow + ((size_t)kb * 64 + half * 32) * BITS / 8;
+    L.c0 = gload16(cp);
+    if constexpr (BITS == 8) L.c1 = gload16(cp + 16);
+    else L.c1 = make_uint4(0, 0, 0, 0);
+    L.s = gp(srow)[kb];
+    L.b = gp(brow)[kb];
+    return L;
+}
+// Dequantise a BLoad (scale and bias times f) into four 16-byte chunks of fp16 in pair order.
+template <int BITS>
+__device__ __forceinline__ void b_dequant(const BLoad<BITS> &L, float f, uint4 *out) {
+    const half2_t s2 = bf16_splat_f16_scaled(L.s, f), b2 = bf16_splat_f16_scaled(L.b, f);
+    half2_t bv[16];
+    const uint32_t cw[8] = {L.c0.x, L.c0.y, L.c0.z, L.c0.w, L.c1.x, L.c1.y, L.c1.z, L.c1.w};
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) dequant_dword<4>(cw[d], s2, b2, bv + 4 * d);
+    } else {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) dequant_dword<8>(cw[d], s2, b2, bv + 2 * d);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[q] = __builtin_bit_cast(uint4, half8_t{bv[4 * q][0], bv[4 * q][1], bv[4 * q + 1][0],
+                                                                          bv[4 * q + 1][1], bv[4 * q + 2][0],
+                                                                          bv[4 * q + 2][1], bv[4 * q + 3][0],
+                                                                          bv[4 * q + 3][1]});
+}
+
+// gate|up + SwiGLU. Item: rows P0 .. P0+M-1 of group g against gate rows j0 .. j0+63 and up rows
+// inter + j0 .. +63 (B tile rows 0..63 gate, 64..127 up). Wave w: rows 64 (w & 1) .. +64, j
+// 32 (w >> 1) .. +32 of both gate and up, so a lane holds gate and up of the same (row, j).
+template <int BITS>
+__global__ void __launch_bounds__(kGemmThreads, 2) gu_gemm(BatchedParams p) {
+    __shared__ __align__(16) uint4 As[2][kBM][8];
+    __shared__ __align__(16) uint4 Bs[2][128][8];
+    __shared__ float tmax[kGemmThreads / kWave];
+    const int w = list_item(gp(p.ntiles)[1]);
+    if (w < 0) return;
+    const auto wq = gp(reinterpret_cast<const int *>(p.wgu + w));
+    const int4 wi = make_int4(wq[0], wq[1], wq[2], wq[3]);
+    const int g = wi.x, P0 = wi.y, M = wi.z & 0xFFFF, j0 = wi.z >> 16, tile = wi.w;
+    const GroupW W = group_w13(p, g);
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int H = p.H, K = p.K;
-    const int P0 = p.goff[g] + m0;
-    const int M = min(kBM, p.gcnt[g] - m0);
-    const int ar = tid / 4, ac = (tid % 4) * 16;  // A: row, first of 16 columns
+    const int H = p.H, K = p.K, nk = H / 64;
+    // A: thread row ar, chunks 4 ah .. 4 ah + 3 (x16 row of the pair's token)
+    const int ar = tid >> 1, ah = tid & 1;
     const bool aok = ar < M;
-    const uint16_t *xrow = p.x + (size_t)(aok ? p.perm[P0 + ar] / K : 0) * H;
-    const int br = tid / 2, bc = (tid % 2) * 32;  // B: tile row, first of 32 columns
-    const size_t wrow = (br < 64) ? (size_t)(j0 + br) : (size_t)(w.inter + j0 + br - 64);
-    const uint8_t *crow = w.c + wrow * ((size_t)H * BITS / 8);
-    const int gpr = H / 64;
-    const int nk = H / 64;
-
-    auto load = [&](int kb) {
-        GuStage<BITS> st;
-        if (aok) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(xrow + kb * 64 + ac);
-            st.a0 = src[0];
-            st.a1 = src[1];
-        } else {
-            st.a0 = make_uint4(0, 0, 0, 0);
-            st.a1 = st.a0;
-        }
-        const uint4 *cp = reinterpret_cast<const uint4 *>(crow + ((size_t)kb * 64 + bc) * BITS / 8);
-        st.c0 = cp[0];
-        st.c1 = BITS == 8 ? cp[1] : make_uint4(0, 0, 0, 0);
-        st.s = w.s[wrow * gpr + kb];
-        st.b = w.b[wrow * gpr + kb];
-        return st;
+    const _Float16 *xrow = p.x16 + (size_t)(aok ? gp(p.perm)[P0 + ar] / K : 0) * H + ah * 32;
+    // B: thread tile row br (0..63 gate, 64..127 up), columns 32 bh .. +31
+    const int br = tid >> 1, bh = tid & 1;
+    const size_t wrow = br < 64 ? (size_t)(j0 + br) : (size_t)(W.inter + j0 + br - 64);
+    const uint8_t *crow = W.c + wrow * ((size_t)H * BITS / 8);
+    const uint16_t *srow = W.s + wrow * (H / 64), *brow = W.b + wrow * (H / 64);
+    // A: 64 bytes of one x16 row per thread and k-step; rows past the tile read a valid row (of token
+    // 0) whose LDS store is skipped, so the loads stay unconditional. B: the codes, scale and bias of
+    // one weight row, dequantised into LDS one k-step ahead of the MFMAs.
+    struct AReg {
+        uint4 a0, a1, a2, a3;
     };
-    auto store = [&](const GuStage<BITS> &st) {
-        half2_t av[8];
-        act16_to_pairs<BITS>(st.a0, st.a1, av);
-        reinterpret_cast<uint4 *>(&As[ar][ac])[0] = __builtin_bit_cast(uint4, half8_t{av[0][0], av[0][1], av[1][0], av[1][1], av[2][0], av[2][1], av[3][0], av[3][1]});
-        reinterpret_cast<uint4 *>(&As[ar][ac])[1] = __builtin_bit_cast(uint4, half8_t{av[4][0], av[4][1], av[5][0], av[5][1], av[6][0], av[6][1], av[7][0], av[7][1]});
-        const half2_t s2 = bf16_splat_f16(st.s), b2 = bf16_splat_f16(st.b);
-        half2_t bv[16];
-        const uint32_t cw[8] = {st.c0.x, st.c0.y, st.c0.z, st.c0.w, st.c1.x, st.c1.y, st.c1.z, st.c1.w};
-        if constexpr (BITS == 4) {
-#pragma unroll
-            for (int d = 0; d < 4; ++d) dequant_dword<4>(cw[d], s2, b2, bv + 4 * d);
-        } else {
-#pragma unroll
-            for (int d = 0; d < 8; ++d) dequant_dword<8>(cw[d], s2, b2, bv + 2 * d);
-        }
-        uint4 *dst = reinterpret_cast<uint4 *>(&Bs[br][bc]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            dst[q] = __builtin_bit_cast(uint4, half8_t{bv[4 * q][0], bv[4 * q][1], bv[4 * q + 1][0], bv[4 * q + 1][1],
-                                                       bv[4 * q + 2][0], bv[4 * q + 2][1], bv[4 * q + 3][0],
-                                                       bv[4 * q + 3][1]});
+    auto a_load = [&](int kb) __attribute__((always_inline)) {
+        const _Float16 *src = xrow + (size_t)kb * 64;
+        return AReg{gload16(src), gload16(src + 8), gload16(src + 16), gload16(src + 24)};
     };
-
-    float4_t ag[2][2], au[2][2];
+    auto a_store = [&](const AReg &v, int buf) __attribute__((always_inline)) {
+        if (!aok) return;
+        As[buf][ar][chunk_pos(ar, 4 * ah + 0)] = v.a0;
+        As[buf][ar][chunk_pos(ar, 4 * ah + 1)] = v.a1;
+        As[buf][ar][chunk_pos(ar, 4 * ah + 2)] = v.a2;
+        As[buf][ar][chunk_pos(ar, 4 * ah + 3)] = v.a3;
+    };
+    auto b_store = [&](const BLoad<BITS> &v, int buf) __attribute__((always_inline)) {
+        uint4 bq[4];
+        b_dequant<BITS>(v, 1.0f, bq);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int q = 0; q < 4; ++q) Bs[buf][br][chunk_pos(br, 4 * bh + q)] = bq[q];
+    };
+    auto b_fetch = [&](int kb) __attribute__((always_inline)) {
+        return b_load<BITS>(crow, srow, brow, min(kb, nk - 1), bh);
+    };
+    float4_t ag[4][2], au[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             ag[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
             au[i][j] = ag[i][j];
         }
-    const int mh = wave & 1, jh = wave >> 1;
-    auto mfma_step = [&]() {
+    const int mh = wave & 1, jh = wave >> 1, fi = lane % 16, fk = lane / 16;
+    // row tiles of this wave that hold any of the M rows (the others are skipped)
+    const int mt = min(4, max(0, (M - 64 * mh + 15) / 16));
+    auto mfma_step = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < 64; ks += 32) {
-            const int kc = ks + 8 * (lane / 16);
-            half8_t a[2], bg[2], bu[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const half8_t *>(&As[32 * mh + 16 * i + lane % 16][kc]);
+        for (int q = 0; q < 2; ++q) {
+            const int c = 4 * q + fk;
+            half8_t bg[2], bu[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                bg[j] = *reinterpret_cast<const half8_t *>(&Bs[32 * jh + 16 * j + lane % 16][kc]);
-                bu[j] = *reinterpret_cast<const half8_t *>(&Bs[64 + 32 * jh + 16 * j + lane % 16][kc]);
+                const int rg = 32 * jh + 16 * j + fi, ru = 64 + rg;
+                bg[j] = __builtin_bit_cast(half8_t, Bs[buf][rg][chunk_pos(rg, c)]);
+                bu[j] = __builtin_bit_cast(half8_t, Bs[buf][ru][chunk_pos(ru, c)]);
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 4; ++i) {
+                if (i >= mt) break;
+                const int ra = 64 * mh + 16 * i + fi;
+                const half8_t a = __builtin_bit_cast(half8_t, As[buf][ra][chunk_pos(ra, c)]);
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    ag[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bg[j], ag[i][j], 0, 0, 0);
-                    au[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bu[j], au[i][j], 0, 0, 0);
+                    ag[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bg[j], ag[i][j], 0, 0, 0);
+                    au[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bu[j], au[i][j], 0, 0, 0);
                 }
+            }
         }
     };
-    GuStage<BITS> S0 = load(0), S1 = load(nk > 1 ? 1 : 0);
-    for (int kb = 0; kb < nk; kb += 2) {
-        store(S0);
-        __syncthreads();
-        if (kb + 2 < nk) S0 = load(kb + 2);
-        mfma_step();
-        __syncthreads();
-        if (kb + 1 < nk) {
-            store(S1);
-            __syncthreads();
-            if (kb + 3 < nk) S1 = load(kb + 3);
-            mfma_step();
-            __syncthreads();
+    // k-step kb lives in LDS stage kb & 1 and, kRing k-steps ahead, in register ring slot kb % kRing
+    // (kb0 below is a multiple of kRing, so every slot index is static): each k-step consumes the
+    // oldest slot into LDS and refills it with the loads of k-step kb + kRing + 1, all issued
+    // together, so a wait for the oldest slot leaves the kRing - 1 younger ones in flight.
+    AReg ra[kRing];
+    BLoad<BITS> rb[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) {
+        ra[j] = a_load(min(j, nk - 1));
+        rb[j] = b_fetch(j);
+    }
+    a_store(ra[0], 0);
+    b_store(rb[0], 0);
+    ra[0] = a_load(min(kRing, nk - 1));
+    rb[0] = b_fetch(kRing);
+    lds_barrier();
+    for (int kb0 = 0; kb0 < nk; kb0 += kRing) {
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) {
+            const int kb = kb0 + j;
+            if (kb >= nk) break;
+            mfma_step(j & 1);
+            if (kb + 1 < nk) {
+                const int s1 = (j + 1) % kRing;  // static once the loop is unrolled
+                a_store(ra[s1], (j + 1) & 1);
+                b_store(rb[s1], (j + 1) & 1);
+                ra[s1] = a_load(min(kb + 1 + kRing, nk - 1));
+                rb[s1] = b_fetch(kb + 1 + kRing);
+            }
+            lds_barrier();
         }
     }
-    // epilogue: lane l, register r -> row 32 mh + 16 i + 4 (l / 16) + r, j = j0 + 32 jh + 16 j + l % 16;
-    // h goes to its pair-order position (dn_gemm's A operand)
-    const int Imax = p.Imax;
+    // epilogue: lane l, register r of tile (i, j) -> row 64 mh + 16 i + 4 (l / 16) + r, j = j0 + 32 jh +
+    // 16 j + l % 16. The accumulators are scaled back by the token's 2^xe, SwiGLU applied, and h
+    // stored as fp16 hi + lo halves of h * 2^-e, e = max(0, E - 15) for the tile's largest |h| in
+    // [2^(E-1), 2^E), in its pair-order position (the down GEMM's A operand).
     bool finite = true;
+    float hmax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int r = 0; r < 4; ++r) {
+            const int m = 64 * mh + 16 * i + 4 * fk + r;
+            const float sc = m < M ? ldexpf(1.0f, gp(p.xe)[gp(p.perm)[P0 + m] / K]) : 0.0f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = 32 * mh + 16 * i + 4 * (lane / 16) + r;
-                if (m >= M) continue;
-                const int jj = j0 + 32 * jh + 16 * j + lane % 16;
-                const float gv = ag[i][j][r], uv = au[i][j][r];
-                const float h = gv / (1.0f + expf(-gv)) * uv;
-                finite &= __builtin_isfinite(gv) && __builtin_isfinite(uv);
+            for (int j = 0; j < 2; ++j) {
+                const float gv = ag[i][j][r] * sc, uv = au[i][j][r] * sc;
+                const float h = m < M ? gv / (1.0f + expf(-gv)) * uv : 0.0f;
+                finite &= m >= M || (__builtin_isfinite(gv) && __builtin_isfinite(uv));  // rows past M: stale
+                hmax = fmaxf(hmax, fabsf(h));
+                ag[i][j][r] = h;
+            }
+        }
+    hmax = __int_as_float((int)wave_max_u32(__float_as_uint(hmax)));
+    if (lane == 0) tmax[wave] = hmax;
+    lds_barrier();
+    hmax = fmaxf(fmaxf(tmax[0], tmax[1]), fmaxf(tmax[2], tmax[3]));
+    int e = 0;
+    if (hmax > 0.0f && __builtin_isfinite(hmax)) {
+        frexpf(hmax, &e);
+        e = max(0, e - 15);
+    }
+    const float hs = ldexpf(1.0f, -e);
+    const int Imax = p.Imax;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 64 * mh + 16 * i + 4 * fk + r;
+            if (m >= M) continue;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int jj = j0 + 32 * jh + 16 * j + fi;
+                const float h = ag[i][j][r] * hs;
                 const _Float16 hh = (_Float16)h;
                 const _Float16 hl = (_Float16)(h - (float)hh);
                 const size_t o = (size_t)(P0 + m) * Imax + pair_pos<BITS>(jj & 63) + (jj & ~63);
                 p.hh[o] = hh;
                 p.hl[o] = hl;
             }
+        }
+    if (tid == 0) p.hexp[(size_t)tile * (Imax / 64) + j0 / 64] = e;
     if (!finite) flag_unsupported(p.status);
 }
 
-// ---- 5. grouped down projection ------------------------------------------------------------------
-// Tile: 64 pair rows x 64 output rows n, k-steps of 64 columns of the group's inter. Wave w: rows
-// 32 (w & 1) .., n 32 (w >> 1) ..; each k-step runs the MFMA once on h hi and once on h lo.
+// down projection x routing weight. Item: rows P0 .. P0+M-1 of group g (h hi and lo halves)
+// against output rows n0 .. n0+127, k-steps of 64 over the group's inter. Wave w: rows 64 (w & 1) ..
+// +64, output rows 64 (w >> 1) .. +64; each k-step runs the MFMAs once on h hi and once on h lo. The
+// k-step's weights are dequantised with scale and bias times 2^e, e the exponent of the h halves
+// of this (tile, k-step), so that every product is the unscaled one.
 template <int BITS>
-struct DnStage {
-    uint4 h0, h1, l0, l1;  // 16 fp16 of h hi / lo, row ar (pair order)
-    uint4 c;               // 16 codes of weight row br (8 bytes used at 4-bit)
-    uint16_t s, b;
-};
-template <int BITS>
-__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(5, 5))) dn_gemm(BatchedParams p) {
-    __shared__ __align__(16) _Float16 Ah[kBM][kLdsK];
-    __shared__ __align__(16) _Float16 Al[kBM][kLdsK];
-    __shared__ __align__(16) _Float16 Bs[64][kLdsK];
-    const int tile = blockIdx.x;
-    if (tile >= p.ntiles[0]) return;
-    const int2 tg = p.tiles[tile];
-    const int g = tg.x, m0 = tg.y;
-    const GroupW w = group_w2(p, g);
-    const int n0 = blockIdx.y * 64;
+__global__ void __launch_bounds__(kGemmThreads, 1) dn_gemm(BatchedParams p) {
+    __shared__ __align__(16) uint4 Ah[2][kBM][8];
+    __shared__ __align__(16) uint4 Al[2][kBM][8];
+    __shared__ __align__(16) uint4 Bs[2][kDnCols][8];
+    const int w = list_item(gp(p.ntiles)[2]);
+    if (w < 0) return;
+    const auto wq = gp(reinterpret_cast<const int *>(p.wdn + w));
+    const int4 wi = make_int4(wq[0], wq[1], wq[2], wq[3]);
+    const int g = wi.x, P0 = wi.y, M = wi.z & 0xFFFF, n0 = wi.z >> 16, tile = wi.w;
+    const GroupW W = group_w2(p, g);
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int H = p.H, Imax = p.Imax;
-    const int P0 = p.goff[g] + m0;
-    const int M = min(kBM, p.gcnt[g] - m0);
-    const int ar = tid / 4, ac = (tid % 4) * 16;
+    const int H = p.H, Imax = p.Imax, nk = W.inter / 64;
+    const int ar = tid >> 1, ah = tid & 1;
     const bool aok = ar < M;
-    const _Float16 *hrow = p.hh + (size_t)(P0 + (aok ? ar : 0)) * Imax;
-    const _Float16 *lrow = p.hl + (size_t)(P0 + (aok ? ar : 0)) * Imax;
-    const int br = tid / 4, bc = (tid % 4) * 16;  // 64 rows x 4 chunks of 16 codes
+    const _Float16 *hrow = p.hh + (size_t)(P0 + (aok ? ar : 0)) * Imax + ah * 32;
+    const _Float16 *lrow = p.hl + (size_t)(P0 + (aok ? ar : 0)) * Imax + ah * 32;
+    const int br = tid >> 1, bh = tid & 1;  // output row n0 + br, columns 32 bh .. +31
     const size_t wrow = (size_t)(n0 + br);
-    const uint8_t *crow = w.c + wrow * ((size_t)w.inter * BITS / 8);
-    const int gpr = w.inter / 64;
-    const int nk = w.inter / 64;
-
-    auto load = [&](int kb) {
-        DnStage<BITS> st;
-        if (aok) {
-            const uint4 *hs = reinterpret_cast<const uint4 *>(hrow + kb * 64 + ac);
-            const uint4 *ls = reinterpret_cast<const uint4 *>(lrow + kb * 64 + ac);
-            st.h0 = hs[0]; st.h1 = hs[1];
-            st.l0 = ls[0]; st.l1 = ls[1];
-        } else {
-            st.h0 = make_uint4(0, 0, 0, 0);
-            st.h1 = st.h0; st.l0 = st.h0; st.l1 = st.h0;
-        }
-        const uint8_t *cp = crow + ((size_t)kb * 64 + bc) * BITS / 8;
-        if constexpr (BITS == 4) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(cp);
-            st.c = make_uint4(v.x, v.y, 0, 0);
-        } else {
-            st.c = *reinterpret_cast<const uint4 *>(cp);
-        }
-        st.s = w.s[wrow * gpr + kb];
-        st.b = w.b[wrow * gpr + kb];
-        return st;
+    const uint8_t *crow = W.c + wrow * ((size_t)W.inter * BITS / 8);
+    const uint16_t *srow = W.s + wrow * (W.inter / 64), *brow = W.b + wrow * (W.inter / 64);
+    const int *hexp = p.hexp + (size_t)tile * (Imax / 64);
+    // A: h hi and lo halves (rows past the tile read the tile's first row, store skipped); B: codes,
+    // scale and bias of one output row, dequantised with the k-step's h exponent into LDS one k-step
+    // ahead of the MFMAs.
+    struct AReg {
+        uint4 h0, h1, h2, h3, l0, l1, l2, l3;
     };
-    auto store = [&](const DnStage<BITS> &st) {
-        reinterpret_cast<uint4 *>(&Ah[ar][ac])[0] = st.h0;
-        reinterpret_cast<uint4 *>(&Ah[ar][ac])[1] = st.h1;
-        reinterpret_cast<uint4 *>(&Al[ar][ac])[0] = st.l0;
-        reinterpret_cast<uint4 *>(&Al[ar][ac])[1] = st.l1;
-        const half2_t s2 = bf16_splat_f16(st.s), b2 = bf16_splat_f16(st.b);
-        half2_t bv[8];
-        const uint32_t cw[4] = {st.c.x, st.c.y, st.c.z, st.c.w};
-        if constexpr (BITS == 4) {
-            dequant_dword<4>(cw[0], s2, b2, bv);
-            dequant_dword<4>(cw[1], s2, b2, bv + 4);
-        } else {
-#pragma unroll
-            for (int d = 0; d < 4; ++d) dequant_dword<8>(cw[d], s2, b2, bv + 2 * d);
-        }
-        uint4 *dst = reinterpret_cast<uint4 *>(&Bs[br][bc]);
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-            dst[q] = __builtin_bit_cast(uint4, half8_t{bv[4 * q][0], bv[4 * q][1], bv[4 * q + 1][0], bv[4 * q + 1][1],
-                                                       bv[4 * q + 2][0], bv[4 * q + 2][1], bv[4 * q + 3][0],
-                                                       bv[4 * q + 3][1]});
+    auto a_load = [&](int kb) __attribute__((always_inline)) {
+        const _Float16 *hs = hrow + (size_t)kb * 64, *ls = lrow + (size_t)kb * 64;
+        return AReg{gload16(hs), gload16(hs + 8), gload16(hs + 16), gload16(hs + 24),
+                    gload16(ls), gload16(ls + 8), gload16(ls + 16), gload16(ls + 24)};
     };
-
-    float4_t acc[2][2];
+    auto a_store = [&](const AReg &v, int buf) __attribute__((always_inline)) {
+        if (!aok) return;
+        Ah[buf][ar][chunk_pos(ar, 4 * ah + 0)] = v.h0;
+        Ah[buf][ar][chunk_pos(ar, 4 * ah + 1)] = v.h1;
+        Ah[buf][ar][chunk_pos(ar, 4 * ah + 2)] = v.h2;
+        Ah[buf][ar][chunk_pos(ar, 4 * ah + 3)] = v.h3;
+        Al[buf][ar][chunk_pos(ar, 4 * ah + 0)] = v.l0;
+        Al[buf][ar][chunk_pos(ar, 4 * ah + 1)] = v.l1;
+        Al[buf][ar][chunk_pos(ar, 4 * ah + 2)] = v.l2;
+        Al[buf][ar][chunk_pos(ar, 4 * ah + 3)] = v.l3;
+    };
+    auto b_store = [&](const BLoad<BITS> &v, int kb, int buf) __attribute__((always_inline)) {
+        uint4 bq[4];
+        b_dequant<BITS>(v, ldexpf(1.0f, gp(hexp)[kb]), bq);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int q = 0; q < 4; ++q) Bs[buf][br][chunk_pos(br, 4 * bh + q)] = bq[q];
+    };
+    auto b_fetch = [&](int kb) __attribute__((always_inline)) {
+        return b_load<BITS>(crow, srow, brow, min(kb, nk - 1), bh);
+    };
+    float4_t acc[4][4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    const int mh = wave & 1, nh = wave >> 1;
-    auto mfma_step = [&]() {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int ks = 0; ks < 64; ks += 32) {
-            const int kc = ks + 8 * (lane / 16);
-            half8_t ah[2], al[2], b[2];
+        for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const int mh = wave & 1, nh = wave >> 1, fi = lane % 16, fk = lane / 16;
+    const int mt = min(4, max(0, (M - 64 * mh + 15) / 16));
+    auto mfma_step = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                ah[i] = *reinterpret_cast<const half8_t *>(&Ah[32 * mh + 16 * i + lane % 16][kc]);
-                al[i] = *reinterpret_cast<const half8_t *>(&Al[32 * mh + 16 * i + lane % 16][kc]);
+        for (int q = 0; q < 2; ++q) {
+            const int c = 4 * q + fk;
+            half8_t b[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int rb = 64 * nh + 16 * j + fi;
+                b[j] = __builtin_bit_cast(half8_t, Bs[buf][rb][chunk_pos(rb, c)]);
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const half8_t *>(&Bs[32 * nh + 16 * j + lane % 16][kc]);
+            for (int i = 0; i < 4; ++i) {
+                if (i >= mt) break;
+                const int ra = 64 * mh + 16 * i + fi;
+                const half8_t a = __builtin_bit_cast(half8_t, Ah[buf][ra][chunk_pos(ra, c)]);
+                const half8_t al = __builtin_bit_cast(half8_t, Al[buf][ra][chunk_pos(ra, c)]);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], b[j], acc[i][j], 0, 0, 0);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[i], b[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 4; ++j) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, b[j], acc[i][j], 0, 0, 0);
                 }
+            }
         }
     };
-    DnStage<BITS> S0 = load(0), S1 = load(nk > 1 ? 1 : 0);
-    for (int kb = 0; kb < nk; kb += 2) {
-        store(S0);
-        __syncthreads();
-        if (kb + 2 < nk) S0 = load(kb + 2);
-        mfma_step();
-        __syncthreads();
-        if (kb + 1 < nk) {
-            store(S1);
-            __syncthreads();
-            if (kb + 3 < nk) S1 = load(kb + 3);
-            mfma_step();
-            __syncthreads();
+    // k-step kb lives in LDS stage kb & 1 and, kRing k-steps ahead, in register ring slot kb % kRing
+    // (kb0 below is a multiple of kRing, so every slot index is static): each k-step consumes the
+    // oldest slot into LDS and refills it with the loads of k-step kb + kRing + 1, all issued
+    // together, so a wait for the oldest slot leaves the kRing - 1 younger ones in flight.
+    AReg ra[kRing];
+    BLoad<BITS> rb[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) {
+        ra[j] = a_load(min(j, nk - 1));
+        rb[j] = b_fetch(j);
+    }
+    a_store(ra[0], 0);
+    b_store(rb[0], 0, 0);
+    ra[0] = a_load(min(kRing, nk - 1));
+    rb[0] = b_fetch(kRing);
+    lds_barrier();
+    for (int kb0 = 0; kb0 < nk; kb0 += kRing) {
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) {
+            const int kb = kb0 + j;
+            if (kb >= nk) break;
+            mfma_step(j & 1);
+            if (kb + 1 < nk) {
+                const int s1 = (j + 1) % kRing;  // static once the loop is unrolled
+                a_store(ra[s1], (j + 1) & 1);
+                b_store(rb[s1], kb + 1, (j + 1) & 1);
+                ra[s1] = a_load(min(kb + 1 + kRing, nk - 1));
+                rb[s1] = b_fetch(kb + 1 + kRing);
+            }
+            lds_barrier();
         }
     }
     bool finite = true;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = 32 * mh + 16 * i + 4 * (lane / 16) + r;
+            const int m = 64 * mh + 16 * i + 4 * fk + r;
             if (m >= M) continue;
-            const int q = p.perm[P0 + m];
-            const float sc = g < p.E ? p.w[q] : p.gamma[q / p.K];
+            const int q = gp(p.perm)[P0 + m];
+            const float sc = g < p.E ? gp(p.w)[q] : gp(p.gamma)[q / p.K];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int n = n0 + 32 * nh + 16 * j + lane % 16;
+            for (int j = 0; j < 4; ++j) {
+                const int n = n0 + 64 * nh + 16 * j + fi;
                 finite &= __builtin_isfinite(acc[i][j][r]);
                 p.out[(size_t)(P0 + m) * H + n] = sc * acc[i][j][r];
             }
@@ -710,7 +908,7 @@ hipError_t launch_router_topk(const BatchedParams &p, hipStream_t stream) {
 }
 
 size_t bucket_lds_bytes(int E) {
-    return 8 * (size_t)kBucketWaves * E + 4 * (size_t)(3 * E + 5);
+    return 8 * (size_t)kBucketWaves * E + 4 * (size_t)(5 * E + 9 + 2 * (kBM + 1));
 }
 
 hipError_t launch_bucket(const BatchedParams &p, hipStream_t stream) {
@@ -722,19 +920,24 @@ hipError_t launch_bucket(const BatchedParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_batched(const BatchedParams &p, int max_tiles, hipStream_t stream) {
+hipError_t launch_batched(const BatchedParams &p, const BatchedWs &lay, hipStream_t stream) {
     hipError_t err = launch_router_topk(p, stream);
     if (err != hipSuccess) return err;
     if ((err = launch_bucket(p, stream)) != hipSuccess) return err;
-    const dim3 ggu(max_tiles, p.Imax / 64), gdn(max_tiles, p.H / 64);
+    // grids cover the work lists' upper bounds (blocks past the list's length return at once)
+    const unsigned ggu = (unsigned)lay.max_wgu, gdn = (unsigned)lay.max_wdn;
     if (p.bits == 4) {
-        hipLaunchKernelGGL(gu_gemm<4>, ggu, dim3(kGemmThreads), 0, stream, p);
+        hipLaunchKernelGGL(x16_kernel<4>, dim3(p.T), dim3(kX16Threads), 0, stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL(dn_gemm<4>, gdn, dim3(kGemmThreads), 0, stream, p);
+        hipLaunchKernelGGL(gu_gemm<4>, dim3(ggu), dim3(kGemmThreads), 0, stream, p);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL(dn_gemm<4>, dim3(gdn), dim3(kGemmThreads), 0, stream, p);
     } else {
-        hipLaunchKernelGGL(gu_gemm<8>, ggu, dim3(kGemmThreads), 0, stream, p);
+        hipLaunchKernelGGL(x16_kernel<8>, dim3(p.T), dim3(kX16Threads), 0, stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL(dn_gemm<8>, gdn, dim3(kGemmThreads), 0, stream, p);
+        hipLaunchKernelGGL(gu_gemm<8>, dim3(ggu), dim3(kGemmThreads), 0, stream, p);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL(dn_gemm<8>, dim3(gdn), dim3(kGemmThreads), 0, stream, p);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const long long n = (long long)p.T * (p.H / 4);

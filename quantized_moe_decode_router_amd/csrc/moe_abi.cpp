@@ -400,9 +400,14 @@ moe_status batched_common(const moe_shape *s, const moe_layer *L, const uint16_t
     p.rhi = reinterpret_cast<uint16_t *>(w + lay.rhi);
     p.rlo = reinterpret_cast<uint16_t *>(w + lay.rlo);
     p.lpart = reinterpret_cast<float *>(w + lay.lpart);
+    p.wgu = reinterpret_cast<int4 *>(w + lay.wgu);
+    p.wdn = reinterpret_cast<int4 *>(w + lay.wdn);
+    p.x16 = reinterpret_cast<_Float16 *>(w + lay.x16);
+    p.xe = reinterpret_cast<int *>(w + lay.xe);
+    p.hexp = reinterpret_cast<int *>(w + lay.hexp);
     p.y = y;
     p.status = status_word ? status_word : reinterpret_cast<int *>(w);
-    hipError_t err = moe::launch_batched(p, lay.max_tiles, static_cast<hipStream_t>(stream));
+    hipError_t err = moe::launch_batched(p, lay, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 }  // namespace

@@ -208,8 +208,14 @@ struct BatchedParams {
     int *rank;          // [T*K] rank of a pair among its 64-token block's pairs of the same expert
     int *gcnt;          // [E+1] rows per group (group E = shared expert, T rows)
     int *goff;          // [E+2] first row of each group
-    int *ntiles;        // [1]
+    int *ntiles;        // [4]: tiles, gate|up work items, down work items
     int2 *tiles;        // [max_tiles] (group, first row in group)
+    int4 *wgu, *wdn;    // work items of the grouped GEMMs: {group, first row P0, rows | first column << 16,
+                        // tile index}, ordered by group, then column block, then row tile
+    _Float16 *x16;      // [T][H] x as fp16 in pair order, scaled by 2^-xe[t]
+    int *xe;            // [T] per-token exponent of that scaling
+    int *hexp;          // [max_tiles][Imax/64] exponent e of h's fp16 halves in (tile, 64-column group):
+                        // they hold h * 2^-e
     int *perm;          // [R] pair index t*K+k of each row (shared rows: t*K)
     int *pos;           // [T*K] row of each pair
     _Float16 *hh, *hl;  // [R][Imax] SwiGLU output, fp16 hi and lo halves
@@ -234,15 +240,22 @@ constexpr int kRouterSplitK = 4;
 // shared expert) rows.
 struct BatchedWs {
     size_t logits, gate, idx, w, gamma, blkcnt, rank, gcnt, goff, ntiles, tiles, perm, pos, hh, hl, out, rhi, rlo,
-        lpart, total;
-    int max_tiles;
+        lpart, wgu, wdn, x16, xe, hexp, total;
+    int max_tiles, max_wgu, max_wdn;
 };
+// Rows per tile of the grouped GEMMs, and the column blocks of one gate|up (j) and down (output row)
+// work item.
+constexpr int kTileRows = 128;
+constexpr int kGuCols = 64;
+constexpr int kDnCols = 128;
 __host__ inline BatchedWs batched_ws_layout(int T, int H, int E, int K, int I, int Is) {
     BatchedWs w;
     const size_t TK = (size_t)T * K, R = TK + (Is ? (size_t)T : 0);
     const size_t Imax = I > Is ? I : Is, nblk = ((size_t)T + 63) / 64;
     const size_t touched = TK < (size_t)E ? TK : (size_t)E;
-    w.max_tiles = (int)(TK / 64 + touched + (Is ? ((size_t)T + 63) / 64 : 0) + 1);
+    w.max_tiles = (int)(TK / kTileRows + touched + (Is ? ((size_t)T + kTileRows - 1) / kTileRows : 0) + 1);
+    w.max_wgu = w.max_tiles * (int)(Imax / kGuCols);
+    w.max_wdn = w.max_tiles * (int)((size_t)H / kDnCols);
     size_t o = kCtrlBytes;
     w.logits = o; o = align_up(o + 4 * (size_t)T * E, 256);
     w.gate = o;   o = align_up(o + 4 * (size_t)T, 256);
@@ -263,10 +276,15 @@ __host__ inline BatchedWs batched_ws_layout(int T, int H, int E, int K, int I, i
     w.rhi = o;    o = align_up(o + 2 * ((size_t)E + 1) * H, 256);
     w.rlo = o;    o = align_up(o + 2 * ((size_t)E + 1) * H, 256);
     w.lpart = o;  o = align_up(o + 4 * (size_t)kRouterSplitK * T * ((size_t)E + 1), 256);
+    w.wgu = o;    o = align_up(o + 16 * (size_t)w.max_wgu, 256);
+    w.wdn = o;    o = align_up(o + 16 * (size_t)w.max_wdn, 256);
+    w.x16 = o;    o = align_up(o + 2 * (size_t)T * H, 256);
+    w.xe = o;     o = align_up(o + 4 * (size_t)T, 256);
+    w.hexp = o;   o = align_up(o + 4 * (size_t)w.max_tiles * (Imax / 64), 256);
     w.total = o;
     return w;
 }
-hipError_t launch_batched(const BatchedParams &p, int max_tiles, hipStream_t stream);
+hipError_t launch_batched(const BatchedParams &p, const BatchedWs &lay, hipStream_t stream);
 // Histogram / scan / stable scatter of the batched path (fills gcnt, goff, tiles, perm, pos).
 hipError_t launch_bucket(const BatchedParams &p, hipStream_t stream);
 // Router GEMM + per-token top-k of the batched path (fills logits, gate, idx, w, gamma).

@@ -90,14 +90,12 @@ def test_stack_affine_bias_every_layer(bits, T):
 
 BATCHED = [
     ("35b_4bit_T33_zipf", synth.QWEN35B_4BIT.shape, 33, 21, 1.1),
-    pytest.param("35b_8bit_T33", synth.QWEN35B_8BIT.shape, 33, 22, None,
-                 marks=pytest.mark.xfail(reason="h = silu(g) u of this layer exceeds fp16's range in the batched "
-                                                "path's h operand (status MOE_ERR_UNSUPPORTED)", strict=True)),
+    ("35b_8bit_T33", synth.QWEN35B_8BIT.shape, 33, 22, None),  # h reaches ~1e5 here: scaled h halves
     ("tiny_T9", synth.TINY.shape, 9, 23, None),
 ]
 
 
-@pytest.mark.parametrize("name,shape,T,seed,zipf", BATCHED, ids=["35b_4bit_T33_zipf", "35b_8bit_T33", "tiny_T9"])
+@pytest.mark.parametrize("name,shape,T,seed,zipf", BATCHED, ids=[c[0] for c in BATCHED])
 def test_batched_affine_bias(name, shape, T, seed, zipf):
     dev = need_gpu()
     moe = _moe()

@@ -104,11 +104,12 @@ def _batched(moe, shape, st, x, T, dev):
     return moe.moe_read_status(ws), y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy()
 
 
-@pytest.mark.parametrize("scale_exp,x_exp", [(10, -10), (-6, 6), (0, 3)])
+@pytest.mark.parametrize("scale_exp,x_exp", [(10, -10), (-6, 6), (0, 3), (-6, 15)])
 def test_batched_fp16_range_inside(scale_exp, x_exp):
-    """Scales scaled by 2^10 (weights up to ~140, x ~ 1e-3) or by 2^-6 (weights ~ 2e-3, x ~ 64),
-    and x ~ 8 at the recipe's weights (h ~ 64x): every fp16 operand in range, status 0, y within the layer
-    tolerance of the oracle."""
+    """Scales times 2^10 (weights up to ~140, x ~ 1e-3) or 2^-6 (weights ~ 2e-3, x ~ 64); x ~ 8 at
+    the recipe's weights (h ~ 64 times the recipe's); weights times 2^-6 with x ~ 3e4 (|x| up to
+    ~1e5, beyond fp16's 65504: scaled per token; h ~ 1e6: scaled per tile and group): status 0, y
+    within the layer tolerance of the oracle."""
     dev = need_gpu()
     moe = _moe()
     shape, T = synth.QWEN35B_4BIT.shape, 12
@@ -122,16 +123,14 @@ def test_batched_fp16_range_inside(scale_exp, x_exp):
     check_y(y[keep], ref["y"][keep])
 
 
-@pytest.mark.parametrize("what", ["weights", "x"])
-def test_batched_fp16_range_beyond(what):
-    """Scales times 2^19 (weights s*q + b up to ~7e4 and biases to ~-8e4, beyond fp16's 65504), or
-    x times 2^15 (|x| up to ~1e5): the batched call reports MOE_ERR_UNSUPPORTED (through
-    moe_layer_forward too), and the decode path, which has no fp16 operands, computes the layer
-    within the tolerance."""
+def test_batched_fp16_range_beyond():
+    """Scales times 2^19 (weights s*q + b up to ~7e4 and biases to ~-8e4, beyond fp16's 65504): the
+    batched call reports MOE_ERR_UNSUPPORTED (through moe_layer_forward too), and the decode path,
+    which has no fp16 operands, computes the layer within the tolerance."""
     dev = need_gpu()
     moe = _moe()
     shape, T = synth.TINY.shape, 4
-    scale_exp, x_exp = (19, -19) if what == "weights" else (-15, 15)
+    scale_exp, x_exp = 19, -19
     st, x = _scaled_layer(shape, 6200, dev, scale_exp, x_exp, T)
     status = _batched(moe, shape, st, x, T, dev)[0]
     assert status == moe.MOE_ERR_UNSUPPORTED
