@@ -66,6 +66,8 @@
  *   - The decode calls additionally need hidden, inter, shared_inter <= 2048, inter and a
  *     non-zero shared_inter >= 128, and an LDS footprint within 160 KiB (it grows with T); other
  *     shapes return MOE_ERR_UNSUPPORTED.
+ *   - The batched calls additionally need hidden, inter, shared_inter <= 2048 and inter and a
+ *     non-zero shared_inter >= 128; other shapes return MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_H
 #define MOE_H

@@ -26,6 +26,8 @@
 // accumulators it reaches are not finite, and the epilogues then set the status word to
 // MOE_ERR_UNSUPPORTED (the outputs are then undefined). Weights and h below 2^-14 in magnitude are
 // held as fp16 subnormals.
+#include <type_traits>
+
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -36,7 +38,6 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = kTileRows;   // pair rows per tile
 constexpr int kGemmThreads = 256;
-constexpr int kRing = 4;         // k-steps of operand loads in flight per thread in the grouped GEMMs
 constexpr int kLdsK = 72;        // fp16 per LDS tile row: 64 + 8 padding (16 bytes)
 
 __device__ __forceinline__ _Float16 bf16_to_f16(uint16_t b) { return (_Float16)bf16_to_f32(b); }
@@ -409,42 +410,19 @@ __device__ __forceinline__ void flag_unsupported(int *status) {
     __hip_atomic_store(status, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---- fp16 tiles in pair order ----------------------------------------------------------------------
-// Inside every 8-column block (4-bit) or 4-column block (8-bit) the fp16 tiles hold their columns in
-// the order the packed dequantisation produces them: 4-bit (0,4,1,5,2,6,3,7), 8-bit (0,2,1,3).
-// Both operands of every MFMA use the same order, so each product and each k-sum is that of the
-// natural order; h is stored in this order by gu_gemm for dn_gemm's A operand.
+// ---- fp16 tiles: column order --------------------------------------------------------------------
+// Inside every 8-column block (4-bit) or 4-column block (8-bit) the A operands of the grouped GEMMs
+// (x for gate|up, h for down) hold their columns in the order the packed dequantisation produces
+// them: 4-bit (0,4,1,5,2,6,3,7), 8-bit (0,2,1,3). Both operands of every MFMA use the same order,
+// so each product and each k-sum is that of the natural order.
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 template <int BITS>
-__device__ __forceinline__ int pair_pos(int c) {  // position of column c (within its 64-column step)
+__device__ __forceinline__ int pair_pos(int c) {  // stored position of column c (blocks stay in place)
     if constexpr (BITS == 4) return (c & ~7) + 2 * (c & 3) + ((c >> 2) & 1);
     else return (c & ~3) + 2 * (c & 1) + ((c >> 1) & 1);
 }
 
-// Codes -> fp16 s q + b, two per instruction: a nibble (byte) masked into the mantissa of the fp16
-// constant 1024 is exactly 1024 + q; subtracting 1024 is exact; one packed fma rounds s q + b once.
-// 4-bit: a dword holds columns 0..7 of a block and gives pairs (p, p+4), p = 0..3.
-// 8-bit: a dword holds columns 0..3 of a block and gives pairs (p, p+2), p = 0..1.
-template <int BITS>
-__device__ __forceinline__ void dequant_dword(uint32_t w, half2_t s2, half2_t b2, half2_t *out) {
-    const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-    constexpr int NP = BITS == 4 ? 4 : 2;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const uint32_t u = BITS == 4 ? (((w >> (4 * p)) & 0x000F000Fu) | 0x64006400u)
-                                     : (((w >> (8 * p)) & 0x00FF00FFu) | 0x64006400u);
-        const half2_t q = __builtin_bit_cast(half2_t, u) - k1024;
-        out[p] = __builtin_elementwise_fma(q, s2, b2);
-    }
-}
-__device__ __forceinline__ half2_t bf16_pair_to_f16(uint16_t a, uint16_t b) {
-    return half2_t{(_Float16)bf16_to_f32(a), (_Float16)bf16_to_f32(b)};
-}
-__device__ __forceinline__ half2_t bf16_splat_f16(uint16_t v) {
-    const _Float16 h = (_Float16)bf16_to_f32(v);
-    return half2_t{h, h};
-}
 // 8 bf16 activations (natural order) times 2^sh -> 8 fp16 in pair order (4-bit: one block of 8;
 // 8-bit: two blocks of 4).
 template <int BITS>
@@ -468,11 +446,11 @@ __device__ __forceinline__ void act16_to_pairs8(const uint4 r, int sh, half2_t *
 }
 
 // ---- x as fp16 -------------------------------------------------------------------------------------
-// x16[t] = x[t] * 2^-xe[t] in fp16, columns in pair order (the order of dequant_dword's output),
-// with xe[t] = E - 15 for the token's largest magnitude in [2^(E-1), 2^E): the token's values fill
-// fp16's range up to 2^15 whatever their bf16 magnitude (only values more than 2^29 below the
-// token's largest become fp16 subnormals); the power-of-two scaling is exact and the gate|up
-// epilogue multiplies it back. One workgroup per token.
+// x16[t] = x[t] * 2^-xe[t] in fp16, columns in pair order, with xe[t] = E - 15 for the token's
+// largest magnitude in [2^(E-1), 2^E): the token's values fill fp16's range up to 2^15 whatever
+// their bf16 magnitude (only values more than 2^29 below the token's largest become fp16
+// subnormals); the power-of-two scaling is exact and the gate|up epilogue multiplies it back. One
+// workgroup per token.
 constexpr int kX16Threads = 256;
 template <int BITS>
 __global__ void __launch_bounds__(kX16Threads) x16_kernel(BatchedParams p) {
@@ -506,203 +484,351 @@ __global__ void __launch_bounds__(kX16Threads) x16_kernel(BatchedParams p) {
 }
 
 // ---- 4 / 5. grouped GEMMs --------------------------------------------------------------------------
-// Both GEMMs run one work item per workgroup of 256 threads (4 waves): a tile of up to 128 pair rows
-// of one group against a block of the group's weight rows, k-steps of 64 columns (one quantisation
-// group). Operands are fp16 in LDS, each tile row 64 values = eight 16-byte chunks stored at
-// chunk ^ (row & 7), so the 16 rows an MFMA fragment read takes at one chunk spread over the banks.
-// The LDS tiles are double buffered, with one LDS-only barrier per k-step (a full workgroup barrier
-// would also wait for every global load in flight, draining the register prefetch each k-step). Block b runs work item b of a list ordered longest first (see bucket_kernel).
+// Both GEMMs run one work item per workgroup of 512 threads (8 waves, one workgroup per compute
+// unit): a tile of up to 128 pair rows of one group (A, fp16) against a block of the group's weight
+// rows (B), in k-steps of 64 columns (one quantisation group). Each wave owns 32 weight rows and
+// every row of the tile; a lane holds the MFMA B fragments of one weight row (row l % 16 of a
+// 16-row block): the 16 columns [16 (l / 16), +16) of the group, which in pair order are its k
+// values of both 32-column fragments. It dequantises them in registers, one k-step ahead of the
+// MFMAs, so each code is dequantised once per tile and the dequantised weights never pass through
+// LDS.
+//
+// Every operand reaches LDS through the LDS-DMA form of the global load, issued from inline
+// assembly: per k-step the tile's A rows (shared by the waves; chunk c of row r stored at
+// c ^ (r & 7), so the 16 rows of a fragment read spread over the banks), and each wave's own
+// weight codes (whole 64-column groups of its 32 rows) with their scales and biases. The
+// loop therefore holds no load the compiler tracks: the vector-memory counter completes in issue
+// order, so a compiler wait for one load would also wait for every DMA issued before it. Batch kb
+// = {A(kb), B(kb + 1)} is issued L k-steps ahead into rings of L + 1 stages; at the top of k-step
+// kb each wave waits until only the L - 1 younger batches are outstanding, then an LDS-only
+// barrier makes every wave's A(kb) visible and frees the stages read in k-step kb - 1. Loads past
+// the last k-step are clamped to it, so that every batch has the same number of DMAs and the
+// counts in the waits hold; the workgroup drains its DMAs before it leaves.
+//
+// The k-loop is compiled once per count MT of 16-row subtiles that hold rows of the tile, so that
+// a k-step has no branches inside and the MFMAs of one k-step interleave with the dequantisation of
+// the next. Block b runs work item b of a list ordered longest first (see bucket_kernel).
 __device__ __forceinline__ int list_item(int n) { return (int)blockIdx.x < n ? (int)blockIdx.x : -1; }
 __device__ __forceinline__ int chunk_pos(int row, int c) { return c ^ (row & 7); }
 
-// The fp16 value of a bf16 scale or bias times 2^e (exact for finite in-range results).
-__device__ __forceinline__ half2_t bf16_splat_f16_scaled(uint16_t v, float f) {
-    const _Float16 h = (_Float16)(bf16_to_f32(v) * f);
+constexpr int kGW = kGemmWavesG;           // waves per grouped-GEMM workgroup
+constexpr int kGT = kGW * kWave;           // threads per grouped-GEMM workgroup
+
+// ---- LDS DMA --------------------------------------------------------------------------------------
+// The LDS-DMA load writes lane l's 16 (4) bytes to LDS address M0 + 16 l (4 l), M0 wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    // a generic pointer into LDS converted to its 32-bit LDS address (address space 3)
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char *)p));
+}
+// The scalar copy of a value the caller knows to be wave-uniform (for scalar-register operands).
+// (readfirstlane returns int: each half goes through uint32_t so that the low half is not
+// sign-extended into the high one)
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const void *uniform(const void *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const void *>(lo | hi << 32);
+}
+// 16 bytes per lane from the wave-uniform base sbase plus the lane's 32-bit byte offset voff.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void *sbase, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(uniform(sbase)),
+                 "s"(uniform(m0))
+                 : "memory", "m0");
+}
+// 4 bytes per lane from the lane's own address.
+__device__ __forceinline__ void dma4v(const void *g, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(uniform(m0))
+                 : "memory", "m0");
+}
+// Wait until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// (a & m) | o in one instruction (for constant operands the compiler emits an AND and an OR)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+    uint32_t d;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(o));
+    return d;
+}
+
+// Codes -> fp16 s q + b, two per packed instruction: a code masked into the mantissa of the fp16
+// constant 1024 reads as 1024 + q; the subtraction of 1024 is exact and one packed fma rounds
+// s q + b once. 4-bit: a dword holds columns 0..7 of a block, giving pairs (0,4) (1,5) (2,6) (3,7);
+// 8-bit: a dword holds columns 0..3, giving pairs (0,2) (1,3) -- the pair order of the A tiles.
+// One fragment (8 columns): 4-bit from one dword, 8-bit from two.
+template <int BITS>
+__device__ __forceinline__ half8_t dequant_frag(uint32_t d0, uint32_t d1, half2_t s2, half2_t b2) {
+    const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    half2_t h0, h1, h2, h3;
+    if constexpr (BITS == 4) {
+        const uint32_t M = 0x64006400u;
+        h0 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, and_or(d0, 0x000F000Fu, M)) - k1024, s2, b2);
+        h1 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, and_or(d0 >> 4, 0x000F000Fu, M)) - k1024, s2, b2);
+        h2 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, and_or(d0 >> 8, 0x000F000Fu, M)) - k1024, s2, b2);
+        h3 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, and_or(d0 >> 12, 0x000F000Fu, M)) - k1024, s2, b2);
+    } else {
+        const uint32_t K64 = 0x64646464u;
+        h0 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(K64, d0, 0x04020400u)) - k1024, s2, b2);
+        h1 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(K64, d0, 0x04030401u)) - k1024, s2, b2);
+        h2 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(K64, d1, 0x04020400u)) - k1024, s2, b2);
+        h3 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(K64, d1, 0x04030401u)) - k1024, s2, b2);
+    }
+    return half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+__device__ __forceinline__ half2_t f16_splat(uint16_t bf, float f) {
+    const _Float16 h = (_Float16)(bf16_to_f32(bf) * f);
     return half2_t{h, h};
 }
 
-// One thread's share of a 64-column k-step of 64 weight rows' codes: 32 columns (4-bit: 16 bytes,
-// 8-bit: 32 bytes), plus that row's scale and bias.
-template <int BITS>
-struct BLoad {
-    uint4 c0, c1;
-    uint16_t s, b;
-};
-template <int BITS>
-__device__ __forceinline__ BLoad<BITS> b_load(const uint8_t *crow, const uint16_t *srow, const uint16_t *brow,
-                                               int kb, int half) {
-    BLoad<BITS> L;
-    const uint8_t *cp = crow + ((size_t)kb * 64 + half * 32) * BITS / 8;
-    L.c0 = gload16(cp);
-    if constexpr (BITS == 8) L.c1 = gload16(cp + 16);
-    else L.c1 = make_uint4(0, 0, 0, 0);
-    L.s = gp(srow)[kb];
-    L.b = gp(brow)[kb];
-    return L;
-}
-// Dequantise a BLoad (scale and bias times f) into four 16-byte chunks of fp16 in pair order.
-template <int BITS>
-__device__ __forceinline__ void b_dequant(const BLoad<BITS> &L, float f, uint4 *out) {
-    const half2_t s2 = bf16_splat_f16_scaled(L.s, f), b2 = bf16_splat_f16_scaled(L.b, f);
-    half2_t bv[16];
-    const uint32_t cw[8] = {L.c0.x, L.c0.y, L.c0.z, L.c0.w, L.c1.x, L.c1.y, L.c1.z, L.c1.w};
-    if constexpr (BITS == 4) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) dequant_dword<4>(cw[d], s2, b2, bv + 4 * d);
-    } else {
-#pragma unroll
-        for (int d = 0; d < 8; ++d) dequant_dword<8>(cw[d], s2, b2, bv + 2 * d);
+// Pipeline parameters of the grouped GEMMs (gate|up: DN = false; down: DN = true).
+//   BB    bytes of a weight row per B block (a whole 128-byte cache line for gate|up)
+//   SB    k-steps per B block
+//   L     k-steps of lookahead: batch t = {A(t + L), and every SB k-steps one B block} is issued at
+//         k-step t, and k-step kb waits for the batches issued up to k-step kb - L
+//   NBUF  B block buffers per wave, (NBUF - 1) SB >= L so that a block's buffer is free when the
+//         block two (or three) ahead is issued into it
+//   RA    A stages (L + 1)
+//   NBC   DMAs per B block and wave (32 rows x BB bytes)
+template <int BITS, bool DN>
+struct GCfg {
+    static constexpr int BB = DN ? 64 : 128;
+    static constexpr int SB = BB / (8 * BITS);
+    static constexpr int L = DN ? (BITS == 4 ? 2 : 1) : (BITS == 4 ? 3 : 2);
+    static constexpr int NBUF = (L + SB - 1) / SB + 1;
+    static constexpr int RA = L + 1;
+    static constexpr int NBC = 32 * BB / 1024;
+    static constexpr int A_STAGE = (DN ? 2 : 1) * kBM * 128;  // A bytes per stage (h: hi and lo)
+    static constexpr int B_BLOCK = 32 * BB;                    // B bytes per block and wave
+    // LDS bytes for ng groups per weight row: A stages, B buffers, then each wave's scale and bias
+    // quarters (16 rows x ng groups x 2 bytes each)
+    __host__ __device__ static constexpr int lds_bytes(int ng) {
+        return RA * A_STAGE + kGW * NBUF * B_BLOCK + kGW * 4 * 32 * ng;
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) out[q] = __builtin_bit_cast(uint4, half8_t{bv[4 * q][0], bv[4 * q][1], bv[4 * q + 1][0],
-                                                                          bv[4 * q + 1][1], bv[4 * q + 2][0],
-                                                                          bv[4 * q + 2][1], bv[4 * q + 3][0],
-                                                                          bv[4 * q + 3][1]});
+    __host__ __device__ static constexpr int b_off() { return RA * A_STAGE; }
+    __host__ __device__ static constexpr int s_off() { return RA * A_STAGE + kGW * NBUF * B_BLOCK; }
+};
+
+// Outstanding DMAs allowed at the top of k-step kb (kb % SB = j): those of the batches issued at
+// k-steps kb - L + 1 .. kb - 1 (NA each, plus NBC in the k-steps that issue a B block).
+template <int L, int SB, int NA, int NBC>
+__host__ __device__ constexpr int wait_count(int j) {
+    int n = 0;
+    for (int d = 1; d <= L - 1; ++d) {
+        const int tm = ((j - d) % SB + SB) % SB;
+        n += NA + ((tm + 1 + L) % SB == 0 ? NBC : 0);
+    }
+    return n;
+}
+template <int L, int SB, int NA, int NBC, int J>
+__device__ __forceinline__ void wait_step() {
+    vm_wait<wait_count<L, SB, NA, NBC>(J)>();
 }
 
-// gate|up + SwiGLU. Item: rows P0 .. P0+M-1 of group g against gate rows j0 .. j0+63 and up rows
-// inter + j0 .. +63 (B tile rows 0..63 gate, 64..127 up). Wave w: rows 64 (w & 1) .. +64, j
-// 32 (w >> 1) .. +32 of both gate and up, so a lane holds gate and up of the same (row, j).
-template <int BITS>
-__global__ void __launch_bounds__(kGemmThreads, 2) gu_gemm(BatchedParams p) {
-    __shared__ __align__(16) uint4 As[2][kBM][8];
-    __shared__ __align__(16) uint4 Bs[2][128][8];
-    __shared__ float tmax[kGemmThreads / kWave];
-    const int w = list_item(gp(p.ntiles)[1]);
-    if (w < 0) return;
-    const auto wq = gp(reinterpret_cast<const int *>(p.wgu + w));
-    const int4 wi = make_int4(wq[0], wq[1], wq[2], wq[3]);
-    const int g = wi.x, P0 = wi.y, M = wi.z & 0xFFFF, j0 = wi.z >> 16, tile = wi.w;
+// Both 16-row blocks' fragments of one k-step.
+struct BQ {
+    half8_t r0q0, r0q1, r1q0, r1q1;
+};
+
+// A wave's weight DMA lanes. The wave's 32 rows are rowof(0..31); rows 0..15 form its first 16-row
+// block, 16..31 its second. B block b of the wave: 32 rows x BB bytes (row r's bytes [b BB, +BB)),
+// stored row-major with 16-byte piece p of row r at piece p ^ (r & (BB / 16 - 1)). DMA u, lane l
+// fills LDS slot 1024 u + 16 l (row r = slot / BB, piece p) from the row's piece p ^ (r & ...).
+// Scales: four quarters per wave (scales of rows 0..15, of rows 16..31, biases of rows 0..15, of
+// rows 16..31), each 16 rows x ng groups x 2 bytes, contiguous in memory and in LDS.
+template <int BITS, bool DN>
+struct WDma {
+    uint32_t coff[GCfg<BITS, DN>::NBC];  // per DMA: the lane's byte offset from the block's base
+    const uint16_t *q[4];                // the four quarters' first elements
+};
+template <int BITS, bool DN, typename RowOf>
+__device__ __forceinline__ WDma<BITS, DN> wdma_lanes(const GroupW &W, int ng, int lane, RowOf rowof) {
+    using C = GCfg<BITS, DN>;
+    WDma<BITS, DN> d;
+    const size_t rowbytes = (size_t)ng * 8 * BITS;
+#pragma unroll
+    for (int u = 0; u < C::NBC; ++u) {
+        const int f = 1024 * u + 16 * lane, r = f / C::BB, pc = (f % C::BB) / 16;
+        d.coff[u] = (uint32_t)(rowof(r) * rowbytes + (pc ^ (r & (C::BB / 16 - 1))) * 16);
+    }
+    d.q[0] = W.s + rowof(0) * (size_t)ng;
+    d.q[1] = W.s + rowof(16) * (size_t)ng;
+    d.q[2] = W.b + rowof(0) * (size_t)ng;
+    d.q[3] = W.b + rowof(16) * (size_t)ng;
+    return d;
+}
+// The four scale quarters of the wave (32 ng bytes each; lanes past a quarter's end do not load).
+template <int BITS, bool DN>
+__device__ __forceinline__ void wdma_scales(const WDma<BITS, DN> &d, int ng, int lane, char *sq) {
+    const int qbytes = 32 * ng;  // <= 1024: ng <= 32
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t m0 = lds_addr(sq + k * qbytes);
+        if (16 * lane < qbytes) dma16s(16 * lane, d.q[k], m0);
+    }
+}
+template <int BITS, bool DN>
+__device__ __forceinline__ void wdma_block(const WDma<BITS, DN> &d, const GroupW &W, int b, char *buf) {
+    using C = GCfg<BITS, DN>;
+    const uint8_t *base = W.c + (size_t)b * C::BB;
+#pragma unroll
+    for (int u = 0; u < C::NBC; ++u) dma16s(d.coff[u], base, lds_addr(buf + 1024 * u));
+}
+// The lane's fragments of k-step kb (slice kb % SB of the block in buf; f scales s and b).
+template <int BITS, bool DN>
+__device__ __forceinline__ BQ dequant_step(const char *buf, const char *sq, int ng, int kb, float f, int fi, int fj) {
+    using C = GCfg<BITS, DN>;
+    constexpr int m = C::BB / 16 - 1;
+    const int s = kb % C::SB, qb = 32 * ng;
+    const uint16_t *sg = reinterpret_cast<const uint16_t *>(sq);
+    const half2_t s0 = f16_splat(sg[fi * ng + kb], f);
+    const half2_t s1 = f16_splat(sg[qb / 2 + fi * ng + kb], f);
+    const half2_t b0 = f16_splat(sg[qb + fi * ng + kb], f);
+    const half2_t b1 = f16_splat(sg[3 * qb / 2 + fi * ng + kb], f);
+    const int r0 = fi, r1 = 16 + fi;
+    BQ q;
+    if constexpr (BITS == 4) {
+        const int P = 2 * s + (fj >> 1), o = (fj & 1) * 8;
+        const uint2 c0 = *reinterpret_cast<const uint2 *>(buf + r0 * C::BB + ((P ^ (r0 & m)) * 16) + o);
+        const uint2 c1 = *reinterpret_cast<const uint2 *>(buf + r1 * C::BB + ((P ^ (r1 & m)) * 16) + o);
+        q.r0q0 = dequant_frag<4>(c0.x, 0, s0, b0);
+        q.r0q1 = dequant_frag<4>(c0.y, 0, s0, b0);
+        q.r1q0 = dequant_frag<4>(c1.x, 0, s1, b1);
+        q.r1q1 = dequant_frag<4>(c1.y, 0, s1, b1);
+    } else {
+        const int P = 4 * s + fj;
+        const uint4 c0 = *reinterpret_cast<const uint4 *>(buf + r0 * C::BB + ((P ^ (r0 & m)) * 16));
+        const uint4 c1 = *reinterpret_cast<const uint4 *>(buf + r1 * C::BB + ((P ^ (r1 & m)) * 16));
+        q.r0q0 = dequant_frag<8>(c0.x, c0.y, s0, b0);
+        q.r0q1 = dequant_frag<8>(c0.z, c0.w, s0, b0);
+        q.r1q0 = dequant_frag<8>(c1.x, c1.y, s1, b1);
+        q.r1q1 = dequant_frag<8>(c1.z, c1.w, s1, b1);
+    }
+    return q;
+}
+
+// f(integral_constant<J>) for J = B .. E - 1, each with J a constant expression.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// The k-loop shared by both GEMMs, unrolled by SB so that every wait count is a constant.
+// issue_a(kb): the A DMAs of k-step kb (NA per wave); mfma(stage, bq): the MFMAs of one k-step on
+// A stage `stage`; dq(kb, buf): the fragments of k-step kb from B buffer `buf`.
+template <int BITS, bool DN, int NA, typename IssueA, typename IssueB, typename Mfma, typename Dq>
+__device__ __forceinline__ void kloop(int nk, IssueA issue_a, IssueB issue_b, Mfma mfma, Dq dq) {
+    using C = GCfg<BITS, DN>;
+    constexpr int L = C::L, SB = C::SB, NBC = C::NBC;
+    // the batches of k-steps -1 - L .. -1 (A only from A(0) on)
+#pragma unroll
+    for (int t = -1 - L; t <= -1; ++t) {
+        if (t + L >= 0) issue_a(t + L);
+        if ((t + 1 + L) % SB == 0) issue_b((t + 1 + L) / SB);
+    }
+    wait_step<L, SB, NA, NBC, 0>();
+    BQ bq = dq(0, 0);
+    for (int kb0 = 0; kb0 < nk; kb0 += SB) {
+        static_for<0, SB>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value;
+            const int kb = kb0 + j;
+            wait_step<L, SB, NA, NBC, j>();
+            lds_barrier();
+            issue_a(kb + L);
+            if constexpr ((j + 1 + L) % SB == 0) issue_b((kb + 1 + L) / SB);
+            mfma(kb % C::RA, bq);
+            bq = dq(kb + 1, ((kb + 1) / SB) % C::NBUF);
+        });
+    }
+    vm_wait<0>();  // no DMA may still write this workgroup's LDS once it leaves
+}
+
+// gate|up + SwiGLU. Item: rows P0 .. P0+M-1 of group g against gate rows j0 .. j0+127 and up rows
+// inter + j0 .. +127. Wave w: gate rows j0 + 16 w + (0..15) (its first row block) and the up rows
+// of the same j (its second), so a lane's accumulators hold gate and up of the same (row, j).
+template <int BITS, int MT>
+__device__ __forceinline__ void gu_body(const BatchedParams &p, char *lds, int g, int P0, int M, int j0, int tile) {
+    using C = GCfg<BITS, false>;
+    constexpr int NA = (MT + 3) / 4;  // A DMAs per wave and k-step: 8 NA waves x 8 rows >= 16 MT
     const GroupW W = group_w13(p, g);
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int H = p.H, K = p.K, nk = H / 64;
-    // A: thread row ar, chunks 4 ah .. 4 ah + 3 (x16 row of the pair's token)
-    const int ar = tid >> 1, ah = tid & 1;
-    const bool aok = ar < M;
-    const _Float16 *xrow = p.x16 + (size_t)(aok ? gp(p.perm)[P0 + ar] / K : 0) * H + ah * 32;
-    // B: thread tile row br (0..63 gate, 64..127 up), columns 32 bh .. +31
-    const int br = tid >> 1, bh = tid & 1;
-    const size_t wrow = br < 64 ? (size_t)(j0 + br) : (size_t)(W.inter + j0 + br - 64);
-    const uint8_t *crow = W.c + wrow * ((size_t)H * BITS / 8);
-    const uint16_t *srow = W.s + wrow * (H / 64), *brow = W.b + wrow * (H / 64);
-    // A: 64 bytes of one x16 row per thread and k-step; rows past the tile read a valid row (of token
-    // 0) whose LDS store is skipped, so the loads stay unconditional. B: the codes, scale and bias of
-    // one weight row, dequantised into LDS one k-step ahead of the MFMAs.
-    struct AReg {
-        uint4 a0, a1, a2, a3;
-    };
-    auto a_load = [&](int kb) __attribute__((always_inline)) {
-        const _Float16 *src = xrow + (size_t)kb * 64;
-        return AReg{gload16(src), gload16(src + 8), gload16(src + 16), gload16(src + 24)};
-    };
-    auto a_store = [&](const AReg &v, int buf) __attribute__((always_inline)) {
-        if (!aok) return;
-        As[buf][ar][chunk_pos(ar, 4 * ah + 0)] = v.a0;
-        As[buf][ar][chunk_pos(ar, 4 * ah + 1)] = v.a1;
-        As[buf][ar][chunk_pos(ar, 4 * ah + 2)] = v.a2;
-        As[buf][ar][chunk_pos(ar, 4 * ah + 3)] = v.a3;
-    };
-    auto b_store = [&](const BLoad<BITS> &v, int buf) __attribute__((always_inline)) {
-        uint4 bq[4];
-        b_dequant<BITS>(v, 1.0f, bq);
+    const int tid = threadIdx.x, lane = tid % kWave, wave = (int)uniform(tid / kWave), fi = lane % 16, fj = lane / 16;
+    const int H = p.H, K = p.K, nk = H / 64, ng = nk;
+    uint4(*As)[kBM][8] = reinterpret_cast<uint4(*)[kBM][8]>(lds);
+    char *bbuf = lds + C::b_off() + wave * C::NBUF * C::B_BLOCK;
+    char *sq = lds + C::s_off() + wave * 4 * 32 * ng;
+    // A DMA lanes: DMA u of wave w covers tile rows 8 d .. 8 d + 7, d = w + 8 u; lane l -> row
+    // 8 d + l / 8, LDS slot l % 8 = chunk (l % 8) ^ (row & 7). Rows past M read row 0's token.
+    uint32_t aoff[NA];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) Bs[buf][br][chunk_pos(br, 4 * bh + q)] = bq[q];
-    };
-    auto b_fetch = [&](int kb) __attribute__((always_inline)) {
-        return b_load<BITS>(crow, srow, brow, min(kb, nk - 1), bh);
-    };
-    float4_t ag[4][2], au[4][2];
+    for (int u = 0; u < NA; ++u) {
+        const int d = wave + kGW * u, r = 8 * d + lane / 8, c = (lane % 8) ^ (r & 7);
+        const int tok = gp(p.perm)[P0 + (r < M ? r : 0)] / K;
+        aoff[u] = (uint32_t)(((size_t)tok * H + c * 8) * 2);
+    }
+    const WDma<BITS, false> wd = wdma_lanes<BITS, false>(W, ng, lane, [&](int r) {
+        return (size_t)(r < 16 ? j0 + 16 * wave + r : W.inter + j0 + 16 * wave + r - 16);
+    });
+    wdma_scales<BITS, false>(wd, ng, lane, sq);
+    const int nblk = nk / C::SB;
+    auto issue_a = [&](int kb) __attribute__((always_inline)) {
+        const _Float16 *base = p.x16 + (size_t)min(kb, nk - 1) * 64;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int u = 0; u < NA; ++u) dma16s(aoff[u], base, lds_addr(&As[kb % C::RA][8 * (wave + kGW * u)][0]));
+    };
+    auto issue_b = [&](int b) __attribute__((always_inline)) {
+        wdma_block<BITS, false>(wd, W, min(b, nblk - 1), bbuf + (b % C::NBUF) * C::B_BLOCK);
+    };
+    float4_t ag[MT], au[MT];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            ag[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            au[i][j] = ag[i][j];
-        }
-    const int mh = wave & 1, jh = wave >> 1, fi = lane % 16, fk = lane / 16;
-    // row tiles of this wave that hold any of the M rows (the others are skipped)
-    const int mt = min(4, max(0, (M - 64 * mh + 15) / 16));
-    auto mfma_step = [&](int buf) __attribute__((always_inline)) {
+    for (int i = 0; i < MT; ++i) ag[i] = au[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    auto mfma = [&](int stage, const BQ &bq) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const int c = 4 * q + fk;
-            half8_t bg[2], bu[2];
+            const half8_t bg = q ? bq.r0q1 : bq.r0q0, bu = q ? bq.r1q1 : bq.r1q0;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int rg = 32 * jh + 16 * j + fi, ru = 64 + rg;
-                bg[j] = __builtin_bit_cast(half8_t, Bs[buf][rg][chunk_pos(rg, c)]);
-                bu[j] = __builtin_bit_cast(half8_t, Bs[buf][ru][chunk_pos(ru, c)]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (i >= mt) break;
-                const int ra = 64 * mh + 16 * i + fi;
-                const half8_t a = __builtin_bit_cast(half8_t, As[buf][ra][chunk_pos(ra, c)]);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    ag[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bg[j], ag[i][j], 0, 0, 0);
-                    au[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bu[j], au[i][j], 0, 0, 0);
-                }
+            for (int i = 0; i < MT; ++i) {
+                const int ra = 16 * i + fi;
+                const half8_t a = __builtin_bit_cast(half8_t, As[stage][ra][chunk_pos(ra, 2 * fj + q)]);
+                ag[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bg, ag[i], 0, 0, 0);
+                au[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bu, au[i], 0, 0, 0);
             }
         }
     };
-    // k-step kb lives in LDS stage kb & 1 and, kRing k-steps ahead, in register ring slot kb % kRing
-    // (kb0 below is a multiple of kRing, so every slot index is static): each k-step consumes the
-    // oldest slot into LDS and refills it with the loads of k-step kb + kRing + 1, all issued
-    // together, so a wait for the oldest slot leaves the kRing - 1 younger ones in flight.
-    AReg ra[kRing];
-    BLoad<BITS> rb[kRing];
-#pragma unroll
-    for (int j = 0; j < kRing; ++j) {
-        ra[j] = a_load(min(j, nk - 1));
-        rb[j] = b_fetch(j);
-    }
-    a_store(ra[0], 0);
-    b_store(rb[0], 0);
-    ra[0] = a_load(min(kRing, nk - 1));
-    rb[0] = b_fetch(kRing);
-    lds_barrier();
-    for (int kb0 = 0; kb0 < nk; kb0 += kRing) {
-#pragma unroll
-        for (int j = 0; j < kRing; ++j) {
-            const int kb = kb0 + j;
-            if (kb >= nk) break;
-            mfma_step(j & 1);
-            if (kb + 1 < nk) {
-                const int s1 = (j + 1) % kRing;  // static once the loop is unrolled
-                a_store(ra[s1], (j + 1) & 1);
-                b_store(rb[s1], (j + 1) & 1);
-                ra[s1] = a_load(min(kb + 1 + kRing, nk - 1));
-                rb[s1] = b_fetch(kb + 1 + kRing);
-            }
-            lds_barrier();
-        }
-    }
-    // epilogue: lane l, register r of tile (i, j) -> row 64 mh + 16 i + 4 (l / 16) + r, j = j0 + 32 jh +
-    // 16 j + l % 16. The accumulators are scaled back by the token's 2^xe, SwiGLU applied, and h
-    // stored as fp16 hi + lo halves of h * 2^-e, e = max(0, E - 15) for the tile's largest |h| in
-    // [2^(E-1), 2^E), in its pair-order position (the down GEMM's A operand).
+    auto dq = [&](int kb, int buf) __attribute__((always_inline)) {
+        return dequant_step<BITS, false>(bbuf + buf * C::B_BLOCK, sq, ng, min(kb, nk - 1), 1.0f, fi, fj);
+    };
+    kloop<BITS, false, NA>(nk, issue_a, issue_b, mfma, dq);
+    // epilogue: lane l, register r of subtile i -> row 16 i + 4 (l / 16) + r, j = j0 + 16 w + l % 16.
+    // The accumulators are scaled back by the token's 2^xe, SwiGLU applied, and h stored as fp16
+    // hi + lo halves of h * 2^-e, e = max(0, E - 15) for the largest |h| of the tile in this
+    // 64-column group (waves 0..3: j0 .., 4..7: j0 + 64 ..) in [2^(E-1), 2^E), in pair order.
     bool finite = true;
     float hmax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = 64 * mh + 16 * i + 4 * fk + r;
+            const int m = 16 * i + 4 * fj + r;
             const float sc = m < M ? ldexpf(1.0f, gp(p.xe)[gp(p.perm)[P0 + m] / K]) : 0.0f;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const float gv = ag[i][j][r] * sc, uv = au[i][j][r] * sc;
-                const float h = m < M ? gv / (1.0f + expf(-gv)) * uv : 0.0f;
-                finite &= m >= M || (__builtin_isfinite(gv) && __builtin_isfinite(uv));  // rows past M: stale
-                hmax = fmaxf(hmax, fabsf(h));
-                ag[i][j][r] = h;
-            }
+            const float gv = ag[i][r] * sc, uv = au[i][r] * sc;
+            const float h = m < M ? gv / (1.0f + expf(-gv)) * uv : 0.0f;
+            finite &= m >= M || (__builtin_isfinite(gv) && __builtin_isfinite(uv));  // rows past M: stale
+            hmax = fmaxf(hmax, fabsf(h));
+            ag[i][r] = h;
         }
     hmax = __int_as_float((int)wave_max_u32(__float_as_uint(hmax)));
+    float *tmax = reinterpret_cast<float *>(lds);  // A stage 0, no longer read by any wave
+    lds_barrier();
     if (lane == 0) tmax[wave] = hmax;
     lds_barrier();
-    hmax = fmaxf(fmaxf(tmax[0], tmax[1]), fmaxf(tmax[2], tmax[3]));
+    const int half = wave / 4;
+    hmax = fmaxf(fmaxf(tmax[4 * half], tmax[4 * half + 1]), fmaxf(tmax[4 * half + 2], tmax[4 * half + 3]));
     int e = 0;
     if (hmax > 0.0f && __builtin_isfinite(hmax)) {
         frexpf(hmax, &e);
@@ -710,165 +836,154 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gu_gemm(BatchedParams p) {
     }
     const float hs = ldexpf(1.0f, -e);
     const int Imax = p.Imax;
+    const int jj = j0 + 16 * wave + fi;
+    const size_t col = (size_t)pair_pos<BITS>(jj);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = 64 * mh + 16 * i + 4 * fk + r;
+            const int m = 16 * i + 4 * fj + r;
             if (m >= M) continue;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int jj = j0 + 32 * jh + 16 * j + fi;
-                const float h = ag[i][j][r] * hs;
-                const _Float16 hh = (_Float16)h;
-                const _Float16 hl = (_Float16)(h - (float)hh);
-                const size_t o = (size_t)(P0 + m) * Imax + pair_pos<BITS>(jj & 63) + (jj & ~63);
-                p.hh[o] = hh;
-                p.hl[o] = hl;
-            }
+            const float h = ag[i][r] * hs;
+            const _Float16 hh = (_Float16)h;
+            const _Float16 hl = (_Float16)(h - (float)hh);
+            const size_t o = (size_t)(P0 + m) * Imax + col;
+            p.hh[o] = hh;
+            p.hl[o] = hl;
         }
-    if (tid == 0) p.hexp[(size_t)tile * (Imax / 64) + j0 / 64] = e;
+    if (lane == 0 && (wave & 3) == 0) p.hexp[(size_t)tile * (Imax / 64) + j0 / 64 + half] = e;
     if (!finite) flag_unsupported(p.status);
 }
 
-// down projection x routing weight. Item: rows P0 .. P0+M-1 of group g (h hi and lo halves)
-// against output rows n0 .. n0+127, k-steps of 64 over the group's inter. Wave w: rows 64 (w & 1) ..
-// +64, output rows 64 (w >> 1) .. +64; each k-step runs the MFMAs once on h hi and once on h lo. The
-// k-step's weights are dequantised with scale and bias times 2^e, e the exponent of the h halves
-// of this (tile, k-step), so that every product is the unscaled one.
 template <int BITS>
-__global__ void __launch_bounds__(kGemmThreads, 1) dn_gemm(BatchedParams p) {
-    __shared__ __align__(16) uint4 Ah[2][kBM][8];
-    __shared__ __align__(16) uint4 Al[2][kBM][8];
-    __shared__ __align__(16) uint4 Bs[2][kDnCols][8];
-    const int w = list_item(gp(p.ntiles)[2]);
+__global__ void __launch_bounds__(kGT, 1) gu_gemm(BatchedParams p) {
+    extern __shared__ __align__(16) char smem[];
+    const int w = list_item(gp(p.ntiles)[1]);
     if (w < 0) return;
-    const auto wq = gp(reinterpret_cast<const int *>(p.wdn + w));
-    const int4 wi = make_int4(wq[0], wq[1], wq[2], wq[3]);
-    const int g = wi.x, P0 = wi.y, M = wi.z & 0xFFFF, n0 = wi.z >> 16, tile = wi.w;
+    const auto wq = gp(reinterpret_cast<const int *>(p.wgu + w));
+    const int g = wq[0], P0 = wq[1], M = wq[2] & 0xFFFF, j0 = wq[2] >> 16, tile = wq[3];
+    switch ((M + 15) / 16) {
+        case 1: gu_body<BITS, 1>(p, smem, g, P0, M, j0, tile); break;
+        case 2: gu_body<BITS, 2>(p, smem, g, P0, M, j0, tile); break;
+        case 3: gu_body<BITS, 3>(p, smem, g, P0, M, j0, tile); break;
+        case 4: gu_body<BITS, 4>(p, smem, g, P0, M, j0, tile); break;
+        case 5: gu_body<BITS, 5>(p, smem, g, P0, M, j0, tile); break;
+        case 6: gu_body<BITS, 6>(p, smem, g, P0, M, j0, tile); break;
+        case 7: gu_body<BITS, 7>(p, smem, g, P0, M, j0, tile); break;
+        default: gu_body<BITS, 8>(p, smem, g, P0, M, j0, tile); break;
+    }
+}
+
+// down projection x routing weight. Item: rows P0 .. P0+M-1 of group g (h hi and lo halves)
+// against output rows n0 .. n0+255, k-steps of 64 over the group's inter. Wave w: output rows
+// n0 + 32 w + (0..31) as two 16-row blocks; each k-step runs the MFMAs once on h hi and once on
+// h lo. The k-step's weights are dequantised with scale and bias times 2^e, e the exponent of the
+// h halves of this tile in this group, so that every product is the unscaled one.
+template <int BITS, int MT>
+__device__ __forceinline__ void dn_body(const BatchedParams &p, char *lds, int g, int P0, int M, int n0, int tile) {
+    using C = GCfg<BITS, true>;
+    constexpr int NA = (MT + 3) / 4;
     const GroupW W = group_w2(p, g);
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int H = p.H, Imax = p.Imax, nk = W.inter / 64;
-    const int ar = tid >> 1, ah = tid & 1;
-    const bool aok = ar < M;
-    const _Float16 *hrow = p.hh + (size_t)(P0 + (aok ? ar : 0)) * Imax + ah * 32;
-    const _Float16 *lrow = p.hl + (size_t)(P0 + (aok ? ar : 0)) * Imax + ah * 32;
-    const int br = tid >> 1, bh = tid & 1;  // output row n0 + br, columns 32 bh .. +31
-    const size_t wrow = (size_t)(n0 + br);
-    const uint8_t *crow = W.c + wrow * ((size_t)W.inter * BITS / 8);
-    const uint16_t *srow = W.s + wrow * (W.inter / 64), *brow = W.b + wrow * (W.inter / 64);
-    const int *hexp = p.hexp + (size_t)tile * (Imax / 64);
-    // A: h hi and lo halves (rows past the tile read the tile's first row, store skipped); B: codes,
-    // scale and bias of one output row, dequantised with the k-step's h exponent into LDS one k-step
-    // ahead of the MFMAs.
-    struct AReg {
-        uint4 h0, h1, h2, h3, l0, l1, l2, l3;
-    };
-    auto a_load = [&](int kb) __attribute__((always_inline)) {
-        const _Float16 *hs = hrow + (size_t)kb * 64, *ls = lrow + (size_t)kb * 64;
-        return AReg{gload16(hs), gload16(hs + 8), gload16(hs + 16), gload16(hs + 24),
-                    gload16(ls), gload16(ls + 8), gload16(ls + 16), gload16(ls + 24)};
-    };
-    auto a_store = [&](const AReg &v, int buf) __attribute__((always_inline)) {
-        if (!aok) return;
-        Ah[buf][ar][chunk_pos(ar, 4 * ah + 0)] = v.h0;
-        Ah[buf][ar][chunk_pos(ar, 4 * ah + 1)] = v.h1;
-        Ah[buf][ar][chunk_pos(ar, 4 * ah + 2)] = v.h2;
-        Ah[buf][ar][chunk_pos(ar, 4 * ah + 3)] = v.h3;
-        Al[buf][ar][chunk_pos(ar, 4 * ah + 0)] = v.l0;
-        Al[buf][ar][chunk_pos(ar, 4 * ah + 1)] = v.l1;
-        Al[buf][ar][chunk_pos(ar, 4 * ah + 2)] = v.l2;
-        Al[buf][ar][chunk_pos(ar, 4 * ah + 3)] = v.l3;
-    };
-    auto b_store = [&](const BLoad<BITS> &v, int kb, int buf) __attribute__((always_inline)) {
-        uint4 bq[4];
-        b_dequant<BITS>(v, ldexpf(1.0f, gp(hexp)[kb]), bq);
+    const int tid = threadIdx.x, lane = tid % kWave, wave = (int)uniform(tid / kWave), fi = lane % 16, fj = lane / 16;
+    const int H = p.H, Imax = p.Imax, nk = W.inter / 64, ng = nk;
+    // A stage s: hi tile at s * A_STAGE, lo tile 16 KiB after it
+    uint4(*Ah)[kBM][8] = reinterpret_cast<uint4(*)[kBM][8]>(lds);
+    char *bbuf = lds + C::b_off() + wave * C::NBUF * C::B_BLOCK;
+    char *sq = lds + C::s_off() + wave * 4 * 32 * ng;
+    const int hexp0 = (int)((size_t)tile * (Imax / 64));
+    uint32_t aoff[NA];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) Bs[buf][br][chunk_pos(br, 4 * bh + q)] = bq[q];
-    };
-    auto b_fetch = [&](int kb) __attribute__((always_inline)) {
-        return b_load<BITS>(crow, srow, brow, min(kb, nk - 1), bh);
-    };
-    float4_t acc[4][4];
+    for (int u = 0; u < NA; ++u) {
+        const int d = wave + kGW * u, r = 8 * d + lane / 8, c = (lane % 8) ^ (r & 7);
+        aoff[u] = (uint32_t)(((size_t)(P0 + (r < M ? r : 0)) * Imax + c * 8) * 2);
+    }
+    // the tile's h exponents of every group, in registers of lanes 0..ng-1 (read with readlane)
+    const int hexp_lane = lane < ng ? gp(p.hexp)[hexp0 + lane] : 0;
+    asm volatile("" ::"v"(hexp_lane));  // the load completes here, before the first DMA is issued
+    const WDma<BITS, true> wd =
+        wdma_lanes<BITS, true>(W, ng, lane, [&](int r) { return (size_t)(n0 + 32 * wave + r); });
+    wdma_scales<BITS, true>(wd, ng, lane, sq);
+    const int nblk = nk / C::SB;
+    auto issue_a = [&](int kb) __attribute__((always_inline)) {
+        const size_t o = (size_t)min(kb, nk - 1) * 64;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int u = 0; u < NA; ++u) {
+            const int st = kb % C::RA, row = 8 * (wave + kGW * u);
+            dma16s(aoff[u], p.hh + o, lds_addr(&Ah[2 * st][row][0]));
+            dma16s(aoff[u], p.hl + o, lds_addr(&Ah[2 * st + 1][row][0]));
+        }
+    };
+    auto issue_b = [&](int b) __attribute__((always_inline)) {
+        wdma_block<BITS, true>(wd, W, min(b, nblk - 1), bbuf + (b % C::NBUF) * C::B_BLOCK);
+    };
+    float4_t a0[MT], a1[MT];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    const int mh = wave & 1, nh = wave >> 1, fi = lane % 16, fk = lane / 16;
-    const int mt = min(4, max(0, (M - 64 * mh + 15) / 16));
-    auto mfma_step = [&](int buf) __attribute__((always_inline)) {
+    for (int i = 0; i < MT; ++i) a0[i] = a1[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    auto mfma = [&](int stage, const BQ &bq) __attribute__((always_inline)) {
+        const uint4(*Hh)[8] = Ah[2 * stage];
+        const uint4(*Hl)[8] = Ah[2 * stage + 1];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const int c = 4 * q + fk;
-            half8_t b[4];
+            const half8_t b0 = q ? bq.r0q1 : bq.r0q0, b1 = q ? bq.r1q1 : bq.r1q0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int rb = 64 * nh + 16 * j + fi;
-                b[j] = __builtin_bit_cast(half8_t, Bs[buf][rb][chunk_pos(rb, c)]);
+            for (int i = 0; i < MT; ++i) {
+                const int ra = 16 * i + fi;
+                const half8_t ah = __builtin_bit_cast(half8_t, Hh[ra][chunk_pos(ra, 2 * fj + q)]);
+                a0[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, b0, a0[i], 0, 0, 0);
+                a1[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, b1, a1[i], 0, 0, 0);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (i >= mt) break;
-                const int ra = 64 * mh + 16 * i + fi;
-                const half8_t a = __builtin_bit_cast(half8_t, Ah[buf][ra][chunk_pos(ra, c)]);
-                const half8_t al = __builtin_bit_cast(half8_t, Al[buf][ra][chunk_pos(ra, c)]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], acc[i][j], 0, 0, 0);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, b[j], acc[i][j], 0, 0, 0);
-                }
+            for (int i = 0; i < MT; ++i) {
+                const int ra = 16 * i + fi;
+                const half8_t al = __builtin_bit_cast(half8_t, Hl[ra][chunk_pos(ra, 2 * fj + q)]);
+                a0[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, b0, a0[i], 0, 0, 0);
+                a1[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, b1, a1[i], 0, 0, 0);
             }
         }
     };
-    // k-step kb lives in LDS stage kb & 1 and, kRing k-steps ahead, in register ring slot kb % kRing
-    // (kb0 below is a multiple of kRing, so every slot index is static): each k-step consumes the
-    // oldest slot into LDS and refills it with the loads of k-step kb + kRing + 1, all issued
-    // together, so a wait for the oldest slot leaves the kRing - 1 younger ones in flight.
-    AReg ra[kRing];
-    BLoad<BITS> rb[kRing];
-#pragma unroll
-    for (int j = 0; j < kRing; ++j) {
-        ra[j] = a_load(min(j, nk - 1));
-        rb[j] = b_fetch(j);
-    }
-    a_store(ra[0], 0);
-    b_store(rb[0], 0, 0);
-    ra[0] = a_load(min(kRing, nk - 1));
-    rb[0] = b_fetch(kRing);
-    lds_barrier();
-    for (int kb0 = 0; kb0 < nk; kb0 += kRing) {
-#pragma unroll
-        for (int j = 0; j < kRing; ++j) {
-            const int kb = kb0 + j;
-            if (kb >= nk) break;
-            mfma_step(j & 1);
-            if (kb + 1 < nk) {
-                const int s1 = (j + 1) % kRing;  // static once the loop is unrolled
-                a_store(ra[s1], (j + 1) & 1);
-                b_store(rb[s1], kb + 1, (j + 1) & 1);
-                ra[s1] = a_load(min(kb + 1 + kRing, nk - 1));
-                rb[s1] = b_fetch(kb + 1 + kRing);
-            }
-            lds_barrier();
-        }
-    }
+    auto dq = [&](int kb, int buf) __attribute__((always_inline)) {
+        const int k = min(kb, nk - 1);
+        const float f = ldexpf(1.0f, __builtin_amdgcn_readlane(hexp_lane, k));
+        return dequant_step<BITS, true>(bbuf + buf * C::B_BLOCK, sq, ng, k, f, fi, fj);
+    };
+    kloop<BITS, true, 2 * NA>(nk, issue_a, issue_b, mfma, dq);
+    // epilogue: lane l, register r of subtile i, block nb -> row 16 i + 4 (l / 16) + r, output row
+    // n0 + 32 w + 16 nb + l % 16; scaled by the routing weight (gamma for the shared group)
     bool finite = true;
+    const int n = n0 + 32 * wave + fi;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = 64 * mh + 16 * i + 4 * fk + r;
+            const int m = 16 * i + 4 * fj + r;
             if (m >= M) continue;
             const int q = gp(p.perm)[P0 + m];
             const float sc = g < p.E ? gp(p.w)[q] : gp(p.gamma)[q / p.K];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = n0 + 64 * nh + 16 * j + fi;
-                finite &= __builtin_isfinite(acc[i][j][r]);
-                p.out[(size_t)(P0 + m) * H + n] = sc * acc[i][j][r];
-            }
+            finite &= __builtin_isfinite(a0[i][r]) && __builtin_isfinite(a1[i][r]);
+            float *o = p.out + (size_t)(P0 + m) * H + n;
+            o[0] = sc * a0[i][r];
+            o[16] = sc * a1[i][r];
         }
     if (!finite) flag_unsupported(p.status);
+}
+
+template <int BITS>
+__global__ void __launch_bounds__(kGT, 1) dn_gemm(BatchedParams p) {
+    extern __shared__ __align__(16) char smem[];
+    const int w = list_item(gp(p.ntiles)[2]);
+    if (w < 0) return;
+    const auto wq = gp(reinterpret_cast<const int *>(p.wdn + w));
+    const int g = wq[0], P0 = wq[1], M = wq[2] & 0xFFFF, n0 = wq[2] >> 16, tile = wq[3];
+    switch ((M + 15) / 16) {
+        case 1: dn_body<BITS, 1>(p, smem, g, P0, M, n0, tile); break;
+        case 2: dn_body<BITS, 2>(p, smem, g, P0, M, n0, tile); break;
+        case 3: dn_body<BITS, 3>(p, smem, g, P0, M, n0, tile); break;
+        case 4: dn_body<BITS, 4>(p, smem, g, P0, M, n0, tile); break;
+        case 5: dn_body<BITS, 5>(p, smem, g, P0, M, n0, tile); break;
+        case 6: dn_body<BITS, 6>(p, smem, g, P0, M, n0, tile); break;
+        case 7: dn_body<BITS, 7>(p, smem, g, P0, M, n0, tile); break;
+        default: dn_body<BITS, 8>(p, smem, g, P0, M, n0, tile); break;
+    }
 }
 
 // ---- 6. fixed-order combine --------------------------------------------------------------------------
@@ -920,26 +1035,36 @@ hipError_t launch_bucket(const BatchedParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// A grouped-GEMM launch with `lds` bytes of dynamic LDS (above the default limit: the attribute
+// first). The shapes that reach here keep lds within the compute unit's 160 KiB.
+hipError_t launch_gemm(void (*kern)(BatchedParams), unsigned grid, int lds, hipStream_t stream, const BatchedParams &p) {
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGT), (size_t)lds, stream, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_batched(const BatchedParams &p, const BatchedWs &lay, hipStream_t stream) {
     hipError_t err = launch_router_topk(p, stream);
     if (err != hipSuccess) return err;
     if ((err = launch_bucket(p, stream)) != hipSuccess) return err;
     // grids cover the work lists' upper bounds (blocks past the list's length return at once)
     const unsigned ggu = (unsigned)lay.max_wgu, gdn = (unsigned)lay.max_wdn;
+    const int gu_lds4 = GCfg<4, false>::lds_bytes(p.H / 64), dn_lds4 = GCfg<4, true>::lds_bytes(p.Imax / 64);
+    const int gu_lds8 = GCfg<8, false>::lds_bytes(p.H / 64), dn_lds8 = GCfg<8, true>::lds_bytes(p.Imax / 64);
     if (p.bits == 4) {
         hipLaunchKernelGGL(x16_kernel<4>, dim3(p.T), dim3(kX16Threads), 0, stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL(gu_gemm<4>, dim3(ggu), dim3(kGemmThreads), 0, stream, p);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL(dn_gemm<4>, dim3(gdn), dim3(kGemmThreads), 0, stream, p);
+        if ((err = launch_gemm(gu_gemm<4>, ggu, gu_lds4, stream, p)) != hipSuccess) return err;
+        if ((err = launch_gemm(dn_gemm<4>, gdn, dn_lds4, stream, p)) != hipSuccess) return err;
     } else {
         hipLaunchKernelGGL(x16_kernel<8>, dim3(p.T), dim3(kX16Threads), 0, stream, p);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL(gu_gemm<8>, dim3(ggu), dim3(kGemmThreads), 0, stream, p);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL(dn_gemm<8>, dim3(gdn), dim3(kGemmThreads), 0, stream, p);
+        if ((err = launch_gemm(gu_gemm<8>, ggu, gu_lds8, stream, p)) != hipSuccess) return err;
+        if ((err = launch_gemm(dn_gemm<8>, gdn, dn_lds8, stream, p)) != hipSuccess) return err;
     }
-    if ((err = hipGetLastError()) != hipSuccess) return err;
     const long long n = (long long)p.T * (p.H / 4);
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p);
     return hipGetLastError();

@@ -97,6 +97,8 @@ size_t forward_decode_part(const moe_shape *s) { return align_up(decode_ws_bytes
 moe_status decode_supported(const moe_shape *s, int T, int grid, bool xt = false) {
     if (s->hidden > 2048 || s->inter > 2048 || s->shared_inter > 2048) return MOE_ERR_UNSUPPORTED;
     if (s->inter < 128 || (s->shared_inter && s->shared_inter < 128)) return MOE_ERR_UNSUPPORTED;
+    // a grouped-GEMM workgroup stages every scale and bias of its rows in LDS (at most 32 groups)
+    if (s->hidden > 2048 || s->inter > 2048 || s->shared_inter > 2048) return MOE_ERR_UNSUPPORTED;
     if (decode_chunk(s, T, grid, xt) == 0) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -352,6 +354,11 @@ moe_status batched_common(const moe_shape *s, const moe_layer *L, const uint16_t
     if ((st = check_layer(s, L, xtab == nullptr)) != MOE_OK) return st;
     if (xtab && (reinterpret_cast<uintptr_t>(xtab) & 7u)) return MOE_ERR_INVALID_ARG;
     if (T < 1 || T > kMaxBatchT) return MOE_ERR_INVALID_ARG;
+    // gate|up work items span 128 intermediate columns, and a k-step's scale DMA reads a dword
+    // (two groups) of every row
+    if (s->inter < 128 || (s->shared_inter && s->shared_inter < 128)) return MOE_ERR_UNSUPPORTED;
+    // a grouped-GEMM workgroup stages every scale and bias of its rows in LDS (at most 32 groups)
+    if (s->hidden > 2048 || s->inter > 2048 || s->shared_inter > 2048) return MOE_ERR_UNSUPPORTED;
     if (!x || !y || !al16(x) || !al16(y)) return MOE_ERR_INVALID_ARG;
     if ((topk_idx_opt && !al4(topk_idx_opt)) || (topk_w_opt && !al4(topk_w_opt)) ||
         (logits_opt && !al4(logits_opt)))

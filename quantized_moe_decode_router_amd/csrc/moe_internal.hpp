@@ -246,8 +246,9 @@ struct BatchedWs {
 // Rows per tile of the grouped GEMMs, and the column blocks of one gate|up (j) and down (output row)
 // work item.
 constexpr int kTileRows = 128;
-constexpr int kGuCols = 64;
-constexpr int kDnCols = 128;
+constexpr int kGuCols = 128;     // gate|up work item: 128 j (8 waves x 16)
+constexpr int kDnCols = 256;     // down work item: 256 output rows (8 waves x 32)
+constexpr int kGemmWavesG = 8;   // waves per grouped-GEMM workgroup
 __host__ inline BatchedWs batched_ws_layout(int T, int H, int E, int K, int I, int Is) {
     BatchedWs w;
     const size_t TK = (size_t)T * K, R = TK + (Is ? (size_t)T : 0);

@@ -75,7 +75,7 @@ BATCHED_CASES = [
     ("80b_4bit_T12", synth.QWEN80B_4BIT.shape, 12, 6, None),
     ("35b_8bit_T9", synth.QWEN35B_8BIT.shape, 9, 7, None),
     ("k1_no_shared", synth.MoeShape(512, 8, 1, 256, 0, 4), 5, 8, None),
-    ("k_eq_e", synth.MoeShape(256, 4, 4, 64, 64, 8), 2, 9, None),
+    ("k_eq_e", synth.MoeShape(256, 4, 4, 128, 128, 8), 2, 9, None),
     ("wide_inter", synth.MoeShape(1024, 32, 6, 1024, 256, 4), 17, 10, None),
     ("shared_wider", synth.MoeShape(512, 16, 3, 128, 512, 4), 130, 11, 1.1),
 ]
@@ -174,3 +174,20 @@ def test_batched_deterministic():
     a = run_batched(shape, st.layer(0), x, 200, dev)[0]
     b = run_batched(shape, st.layer(0), x, 200, dev)[0]
     np.testing.assert_array_equal(a, b)
+
+
+def test_batched_narrow_inter_unsupported():
+    """Intermediate sizes below 128 (a gate|up work item spans 128 columns) are refused with
+    MOE_ERR_UNSUPPORTED before any launch; y is left as it was."""
+    dev = need_gpu()
+    moe = _moe()
+    shape = synth.MoeShape(256, 4, 2, 64, 64, 4)
+    st = synth.make_stack(shape, 1, 3400, dev)
+    T = 5
+    x = synth.make_x(shape, T, 4, device=dev)
+    y = torch.full((T, shape.hidden), 7.0, dtype=torch.float32, device=dev)
+    ws = moe.workspace(shape, T, moe.MOE_WS_BATCHED, dev)
+    with pytest.raises(moe.MoeError) as err:
+        moe.moe_layer_batched(shape, st.layer(0), x, T, y, workspace=ws)
+    assert err.value.status == moe.MOE_ERR_UNSUPPORTED
+    assert torch.all(y == 7.0)
