@@ -1,24 +1,25 @@
 // batched.hip -- one MoE layer for a batch of T tokens (prefill / batched decode) on gfx950.
 //
-// Seven launches on one stream, no host synchronisation:
-//   1. router_split  the fp32 router (and shared gate) as bf16 hi + lo halves, once per call
-//      router_gemm   logits[T][E] (+ shared-gate logit) = x . R^T on v_mfma_f32_16x16x32_bf16 over
-//                    both halves (x is bf16, exact)
+// Six launches on one stream, no host synchronisation:
+//   1. router_gemm   logits[T][E] (+ shared-gate logit) = x . R^T on v_mfma_f32_16x16x32_bf16, the
+//                    fp32 router split into bf16 hi + lo halves on its way into LDS (x is bf16,
+//                    exact)
 //   2. topk_kernel   one wave per token: top-k by (logit desc, index asc), renormalised weights
-//                    (softmax of the kept logits), gamma = sigmoid(gate logit)
-//   3. bucket_kernel one workgroup: per-expert histogram of the (token, slot) pairs, exclusive scan,
-//                    stable scatter (pairs of one expert stay in pair order), the inverse map and
-//                    the list of 64-row tiles of every group (routed experts, then the shared
-//                    expert as group E with one row per token)
-//   4. gu_gemm       per tile: [64 pairs x H] . [H x (64 gate + 64 up) rows] on
-//                    v_mfma_f32_16x16x32_f16, codes dequantised to fp16 in LDS, SwiGLU epilogue;
-//                    h is stored as fp16 hi + lo halves (22 significant bits)
-//   5. dn_gemm       per tile: [64 pairs x I] . [I x 64 output rows], once with h hi and once with
-//                    h lo; epilogue scales by the routing weight (gamma for the shared group)
+//                    (softmax of the kept logits), gamma = sigmoid(gate logit); x as scaled fp16
+//   3. bucket_count  per block of 64 tokens: per-expert counts and every pair's rank in its block
+//      bucket_plan   one workgroup: exclusive scans, stable scatter (pairs of one expert stay in
+//                    pair order), the inverse map, the list of 128-row tiles of every group
+//                    (routed experts, then the shared expert as group E with one row per token)
+//                    and the two GEMMs' work lists, longest first
+//   4. gu_gemm       per item: [<=128 pairs x H] . [H x (128 gate + 128 up) rows] on
+//                    v_mfma_f32_16x16x32_f16, codes dequantised to fp16 in registers, SwiGLU
+//                    epilogue; h is stored as fp16 hi + lo halves (22 significant bits)
+//   5. dn_gemm       per item: [<=128 pairs x I] . [I x 256 output rows], once with h hi and once
+//                    with h lo; epilogue scales by the routing weight (gamma for the shared group)
 //   6. combine       y[t] = sum_k out[pos(t, k)] + out[shared row of t], k = 0..K-1 in order
 //
 // MFMA operands are fp16, products exact in the fp32 accumulators: x scaled by a power of two per
-// token (x16_kernel: any bf16 x fits), the dequantised weights s * q + b rounded once, and h as fp16
+// token (any bf16 x fits), the dequantised weights s * q + b rounded once, and h as fp16
 // hi + lo halves scaled down by a power of two per tile and 64-column group where its magnitude
 // needs it (the down GEMM scales that k-step's dequantised weights up by the same power, so each
 // product is unchanged). So s, b and s * q + b must lie within fp16's range (+-65504), and so must a
@@ -45,37 +46,15 @@ __device__ __forceinline__ _Float16 bf16_to_f16(uint16_t b) { return (_Float16)b
 // ---- 1. router GEMM ------------------------------------------------------------------------------
 // logits = x . R^T on bf16 MFMA: x is bf16 (exact), every fp32 router weight is split into
 // bf16 hi = rne(R) and lo = rne(R - hi), so R - hi - lo is below 2^-17 |R|; both products are exact
-// in the fp32 accumulators. The split is done once per call by router_split (rows E+1: the router,
-// then the shared gate), so that the GEMM only moves bf16 tiles.
+// in the fp32 accumulators. Rows E+1: the router, then the shared gate.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-constexpr int kSplitThreads = 256;
-
-__global__ void __launch_bounds__(kSplitThreads) router_split(BatchedParams p) {
-    const int H = p.H, N = p.E + (p.sgate ? 1 : 0);
-    const size_t i = ((size_t)blockIdx.x * kSplitThreads + threadIdx.x) * 8;  // 8 weights per thread
-    if (i >= (size_t)N * H) return;
-    const size_t row = i / H, col = i - row * H;
-    const float *src = (row < (size_t)p.E ? p.router + row * H : p.sgate) + col;
-    const float4 a = reinterpret_cast<const float4 *>(src)[0], b = reinterpret_cast<const float4 *>(src)[1];
-    const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint16_t h0 = f32_to_bf16_rne(f[2 * q]), h1 = f32_to_bf16_rne(f[2 * q + 1]);
-        const uint16_t l0 = f32_to_bf16_rne(f[2 * q] - bf16_to_f32(h0));
-        const uint16_t l1 = f32_to_bf16_rne(f[2 * q + 1] - bf16_to_f32(h1));
-        hi[q] = h0 | (uint32_t)h1 << 16;
-        lo[q] = l0 | (uint32_t)l1 << 16;
-    }
-    *reinterpret_cast<uint4 *>(p.rhi + i) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    *reinterpret_cast<uint4 *>(p.rlo + i) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-}
 
 // Tile: 32 tokens x 32 router rows x one of ks contiguous ranges of H (blockIdx.z), k-steps of 64;
 // wave w: tokens 16 (w & 1) .., rows 16 (w >> 1) ... The range's partial sums go to lpart; the
 // top-k kernel adds the ranges in order (the ranges keep the k-loop of a workgroup short, so
 // that many workgroups hide each other's load latency).
 constexpr int kRtT = 32, kRtN = 32;
+constexpr int kRtSteps = 8;  // k-steps per range: H / 64 / router_ksplit(H) <= 2048 / 64 / 4
 __host__ __device__ inline int router_ksplit(int H) { return H / 64 < kRouterSplitK ? H / 64 : kRouterSplitK; }
 
 __global__ void __launch_bounds__(kGemmThreads) router_gemm(BatchedParams p) {
@@ -90,22 +69,34 @@ __global__ void __launch_bounds__(kGemmThreads) router_gemm(BatchedParams p) {
     const int r = tid / 8, c = (tid % 8) * 8;
     const bool xok = t0 + r < T, rok = n0 + r < N;
     const uint16_t *xrow = p.x + (size_t)(xok ? t0 + r : 0) * H;
-    const uint16_t *hrow = p.rhi + (size_t)(rok ? n0 + r : 0) * H, *lrow = p.rlo + (size_t)(rok ? n0 + r : 0) * H;
+    const float *frow = !rok ? p.router : (n0 + r < E ? p.router + (size_t)(n0 + r) * H : p.sgate);
     struct St {
-        uint4 x, h, l;
+        uint4 x;
+        float4 f0, f1;
     };
+    // rows past T or N read row 0 (their results are not stored), so every load is unconditional
     auto load = [&](int kb) {
-        const uint4 z = make_uint4(0, 0, 0, 0);
         St st;
-        st.x = xok ? *reinterpret_cast<const uint4 *>(xrow + kb * 64 + c) : z;
-        st.h = rok ? *reinterpret_cast<const uint4 *>(hrow + kb * 64 + c) : z;
-        st.l = rok ? *reinterpret_cast<const uint4 *>(lrow + kb * 64 + c) : z;
+        st.x = *reinterpret_cast<const uint4 *>(xrow + kb * 64 + c);
+        st.f0 = *reinterpret_cast<const float4 *>(frow + kb * 64 + c);
+        st.f1 = *reinterpret_cast<const float4 *>(frow + kb * 64 + c + 4);
         return st;
     };
+    // the fp32 router weights split into bf16 hi = rne(R) and lo = rne(R - hi) on the way into LDS
     auto store = [&](const St &st) {
         *reinterpret_cast<uint4 *>(&xs[r][c]) = st.x;
-        *reinterpret_cast<uint4 *>(&rh[r][c]) = st.h;
-        *reinterpret_cast<uint4 *>(&rl[r][c]) = st.l;
+        auto split2 = [](float a, float b, uint32_t &hi, uint32_t &lo) __attribute__((always_inline)) {
+            const uint16_t h0 = f32_to_bf16_rne(a), h1 = f32_to_bf16_rne(b);
+            hi = h0 | (uint32_t)h1 << 16;
+            lo = f32_to_bf16_rne(a - bf16_to_f32(h0)) | (uint32_t)f32_to_bf16_rne(b - bf16_to_f32(h1)) << 16;
+        };
+        uint4 hi, lo;
+        split2(st.f0.x, st.f0.y, hi.x, lo.x);
+        split2(st.f0.z, st.f0.w, hi.y, lo.y);
+        split2(st.f1.x, st.f1.y, hi.z, lo.z);
+        split2(st.f1.z, st.f1.w, hi.w, lo.w);
+        *reinterpret_cast<uint4 *>(&rh[r][c]) = hi;
+        *reinterpret_cast<uint4 *>(&rl[r][c]) = lo;
     };
     float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     const int th = wave & 1, nh = wave >> 1;
@@ -120,20 +111,20 @@ __global__ void __launch_bounds__(kGemmThreads) router_gemm(BatchedParams p) {
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc, 0, 0, 0);
         }
     };
-    const int nk = H / 64 / router_ksplit(H), k0 = blockIdx.z * nk;  // this range's k-steps
-    St S0 = load(k0), S1 = load(k0 + (nk > 1 ? 1 : 0));
-    for (int kb = 0; kb < nk; kb += 2) {
-        store(S0);
-        __syncthreads();
-        if (kb + 2 < nk) S0 = load(k0 + kb + 2);
-        mfma_step();
-        __syncthreads();
-        if (kb + 1 < nk) {
-            store(S1);
-            __syncthreads();
-            if (kb + 3 < nk) S1 = load(k0 + kb + 3);
+    // this range's k-steps (at most kRtSteps: H <= 2048, H / 4 per range): every load is
+    // issued up front, then each k-step goes through LDS; the barriers are LDS-only, so that the
+    // loads of later k-steps stay in flight
+    const int nk = H / 64 / router_ksplit(H), k0 = blockIdx.z * nk;
+    St S[kRtSteps];
+#pragma unroll
+    for (int j = 0; j < kRtSteps; ++j) S[j] = load(k0 + min(j, nk - 1));
+#pragma unroll
+    for (int j = 0; j < kRtSteps; ++j) {
+        if (j < nk) {  // nk is uniform
+            store(S[j]);
+            lds_barrier();
             mfma_step();
-            __syncthreads();
+            lds_barrier();
         }
     }
     // lane l, register q -> token t0 + 16 th + 4 (l / 16) + q, row n0 + 16 nh + l % 16
@@ -146,7 +137,52 @@ __global__ void __launch_bounds__(kGemmThreads) router_gemm(BatchedParams p) {
     }
 }
 
-// ---- 2. top-k per token ------------------------------------------------------------------------
+// ---- 2. top-k per token, x as fp16 -------------------------------------------------------------
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+template <int BITS>
+__device__ void act16_to_pairs8(const uint4 r, int sh, half2_t *out);
+
+// x16[t] = x[t] * 2^-xe[t] in fp16, columns in pair order (see the grouped GEMMs), with xe[t] =
+// E - 15 for the token's largest magnitude in [2^(E-1), 2^E): the token's values fill fp16's range
+// up to 2^15 whatever their bf16 magnitude (only values more than 2^29 below the token's largest
+// become fp16 subnormals); the power-of-two scaling is exact and the gate|up epilogue multiplies
+// it back. One wave per token.
+template <int BITS>
+__device__ __forceinline__ void wave_x16(const BatchedParams &p, int t) {
+    const int lane = threadIdx.x % kWave, H = p.H;
+    const uint16_t *xr = p.x + (size_t)t * H;
+    constexpr int NC = 4;  // H <= 2048: at most 4 chunks of 8 columns per lane
+    uint4 v[NC];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int c = (i * kWave + lane) * 8;
+        v[i] = c < H ? *reinterpret_cast<const uint4 *>(xr + c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(w[k] & 0xFFFF)), fabsf(bf16_to_f32(w[k] >> 16))));
+    }
+    amax = __int_as_float((int)wave_max_u32(__float_as_uint(amax)));  // non-negative floats order as integers
+    int e = 0;
+    if (amax > 0.0f) {
+        frexpf(amax, &e);
+        e -= 15;
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int c = (i * kWave + lane) * 8;
+        if (c >= H) break;
+        half2_t hv[4];
+        act16_to_pairs8<BITS>(v[i], -e, hv);
+        *reinterpret_cast<uint4 *>(p.x16 + (size_t)t * H + c) = __builtin_bit_cast(uint4, hv);
+    }
+    if (lane == 0) p.xe[t] = e;
+}
+
 constexpr int kTopkWaves = 4;
 __global__ void __launch_bounds__(kTopkWaves * kWave) topk_kernel(BatchedParams p) {
     extern __shared__ __align__(16) char smem[];
@@ -159,12 +195,26 @@ __global__ void __launch_bounds__(kTopkWaves * kWave) topk_kernel(BatchedParams 
     const int N = E + (p.sgate ? 1 : 0), ks = router_ksplit(p.H);
     const float *part = p.lpart + (size_t)t * N;
     const size_t zs = (size_t)p.T * N;
-    for (int e = lane; e < E; e += kWave) {
-        float v = part[e];
-        for (int z = 1; z < ks; ++z) v += part[z * zs + e];
-        if (p.rbias) v += p.rbias[e];
-        lt[e] = v;
-        p.logits[(size_t)t * E + e] = v;
+    // every partial sum of this lane's logits in flight at once (E <= 1024, ks <= 4)
+    for (int e0 = 0; e0 < E; e0 += 4 * kWave) {
+        float v[4][kRouterSplitK];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int z = 0; z < kRouterSplitK; ++z) {
+                const int e = min(e0 + u * kWave + lane, E - 1);
+                v[u][z] = z < ks ? part[z * zs + e] : 0.0f;
+            }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = e0 + u * kWave + lane;
+            if (e >= E) break;
+            float a = v[u][0];
+            for (int z = 1; z < ks; ++z) a += v[u][z];
+            if (p.rbias) a += p.rbias[e];
+            lt[e] = a;
+            p.logits[(size_t)t * E + e] = a;
+        }
     }
     float gate = 0.0f;
     if (p.sgate) {
@@ -176,61 +226,98 @@ __global__ void __launch_bounds__(kTopkWaves * kWave) topk_kernel(BatchedParams 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     wave_topk(lt, E, K, p.idx + (size_t)t * K, p.w + (size_t)t * K);
     if (lane == 0 && p.gamma) p.gamma[t] = p.sgate ? 1.0f / (1.0f + expf(-gate)) : 0.0f;
+    if (p.x16) {
+        if (p.bits == 4) wave_x16<4>(p, t);
+        else wave_x16<8>(p, t);
+    }
 }
 
 // ---- 3. histogram, exclusive scan, stable scatter, tile list -------------------------------------
-// One workgroup of 512 threads. Tokens are taken in blocks of 64 (one lane each); for a block,
-// wave-private LDS holds one 64-bit mask per expert with bit l set when token (block, l) selected
-// that expert. popcount(mask) is the block's count for the expert and popcount(mask & lanes below)
-// the pair's rank among the block's pairs of the same expert. Per-expert exclusive prefixes over
-// blocks plus the expert offsets place every pair: pairs of one expert stay in token order, which
-// is pair order (a token selects an expert at most once).
-constexpr int kBucketThreads = 512;
-constexpr int kBucketWaves = kBucketThreads / kWave;
+// Two launches. bucket_count: one wave per block of 64 tokens (one lane each), four blocks per
+// workgroup; wave-private LDS holds one 64-bit mask per expert with bit l set when token (block, l)
+// selected that expert. popcount(mask) is the block's count for the expert and popcount(mask &
+// lanes below) the pair's rank among the block's pairs of the same expert. bucket_plan: one
+// workgroup: per-expert exclusive prefixes over blocks, the scans of the group sizes, tile counts
+// and work items, the tile list, the work lists, then every pair's place: expert offset + its
+// block's prefix + its rank, so pairs of one expert stay in token order, which is pair order (a
+// token selects an expert at most once). The shared expert is group E with one row per token.
+constexpr int kCountWaves = 4;
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / kWave;
+constexpr int kMaxGroups = 1025;  // experts (<= 1024) and the shared expert
 
-__global__ void __launch_bounds__(kBucketThreads) bucket_kernel(BatchedParams p) {
+__global__ void __launch_bounds__(kCountWaves * kWave) bucket_count(BatchedParams p) {
     extern __shared__ __align__(16) char smem[];
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int T = p.T, K = p.K, E = p.E;
+    const int blk = blockIdx.x * kCountWaves + wave;
+    if (blk * kWave >= T) return;  // whole wave leaves together; no workgroup barrier follows
+    unsigned long long *masks = reinterpret_cast<unsigned long long *>(smem) + (size_t)wave * E;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const int t = blk * kWave + lane;
+    const bool valid = t < T;
+    for (int e = lane; e < E; e += kWave) masks[e] = 0ull;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int ex[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ex[k] = k < K && valid ? min((unsigned)p.idx[(size_t)t * K + k], (unsigned)(E - 1)) : -1;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        if (ex[k] >= 0) atomicOr(&masks[ex[k]], 1ull << lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        if (ex[k] >= 0) p.rank[(size_t)t * K + k] = __popcll(masks[ex[k]] & below);
+    for (int e = lane; e < E; e += kWave) p.blkcnt[(size_t)blk * E + e] = __popcll(masks[e]);
+}
+
+// Inclusive sums over the workgroup of four per-thread values (v[0..3]); returns the exclusive
+// prefix of this thread and the totals (every thread). 16 waves: wave scans, then wave totals.
+__device__ __forceinline__ void block_scan4(int v[4], int excl[4], int total[4], int (*wsum)[4]) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    int inc[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int a = __shfl_up(inc[i], o, kWave);
+            if (lane >= o) inc[i] += a;
+        }
+    }
+    if (lane == kWave - 1)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wsum[wave][i] = inc[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int before = 0, all = 0;
+        for (int w = 0; w < kPlanWaves; ++w) {
+            const int s = wsum[w][i];
+            before += w < wave ? s : 0;
+            all += s;
+        }
+        excl[i] = before + inc[i] - v[i];
+        total[i] = all;
+    }
+    __syncthreads();
+}
+
+__global__ void __launch_bounds__(kPlanThreads) bucket_plan(BatchedParams p) {
+    __shared__ int gcnt[kMaxGroups], goff[kMaxGroups + 1], gtoff[kMaxGroups + 1];
+    __shared__ int wsum[kPlanWaves][4];
+    __shared__ int hgu[kBM + 1], hdn[kBM + 1];
+    const int tid = threadIdx.x;
     const int T = p.T, K = p.K, E = p.E;
     const int ng = E + (p.Is ? 1 : 0);  // groups: experts, then the shared expert
     const int nblk = (T + kWave - 1) / kWave;
-    unsigned long long *masks = reinterpret_cast<unsigned long long *>(smem) + (size_t)wave * E;
-    int *gcnt = reinterpret_cast<int *>(reinterpret_cast<unsigned long long *>(smem) + (size_t)kBucketWaves * E);
-    int *goff = gcnt + (E + 1);
-    int *gtoff = goff + (E + 2);
-    int *guoff = gtoff + (E + 2);  // first gate|up work item of each group
-    int *dnoff = guoff + (E + 2);  // first down work item of each group
-    const unsigned long long below = (1ull << lane) - 1ull;
-
-    for (int blk = wave; blk < nblk; blk += kBucketWaves) {
-        const int t = blk * kWave + lane;
-        const bool valid = t < T;
-        for (int e = lane; e < E; e += kWave) masks[e] = 0ull;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (valid)
-            for (int k = 0; k < K; ++k) {
-                const int e = min((unsigned)p.idx[(size_t)t * K + k], (unsigned)(E - 1));
-                atomicOr(&masks[e], 1ull << lane);
-            }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (valid)
-            for (int k = 0; k < K; ++k) {
-                const int e = min((unsigned)p.idx[(size_t)t * K + k], (unsigned)(E - 1));
-                p.rank[(size_t)t * K + k] = __popcll(masks[e] & below);
-            }
-        for (int e = lane; e < E; e += kWave) p.blkcnt[(size_t)blk * E + e] = __popcll(masks[e]);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    __syncthreads();
     // per expert: exclusive prefix over blocks (in place) and the total; the counts of eight blocks
     // are loaded before any is rewritten, so that a chunk costs one memory round trip
-    for (int e = tid; e < E; e += kBucketThreads) {
+    if (tid < E) {
+        const int e = tid;
         int run = 0;
         for (int b0 = 0; b0 < nblk; b0 += 8) {
             int c[8];
@@ -247,112 +334,136 @@ __global__ void __launch_bounds__(kBucketThreads) bucket_kernel(BatchedParams p)
     if (tid == 0 && p.Is) gcnt[E] = T;
     __syncthreads();
     // exclusive scans of the group sizes, their tile counts and their gate|up and down work items
-    // (tiles x column blocks), by wave 0: lane l owns a chunk
     const int ndn = p.H / kDnCols;
     auto ngu_of = [&](int g) { return (g < E ? p.I : p.Is) / kGuCols; };
-    if (wave == 0) {
-        const int chunk = (ng + kWave - 1) / kWave;
-        const int g0 = min(ng, lane * chunk), g1 = min(ng, g0 + chunk);
-        int s = 0, st = 0, su = 0, sd = 0;
-        for (int g = g0; g < g1; ++g) {
-            const int nt = (gcnt[g] + kBM - 1) / kBM;
-            s += gcnt[g];
-            st += nt;
-            su += nt * ngu_of(g);
-            sd += nt * ndn;
-        }
-        int is = s, ist = st, isu = su, isd = sd;  // inclusive wave scans
+    {
+        // thread tid: groups 2 tid and 2 tid + 1 (up to 2048 groups)
+        int v[4] = {0, 0, 0, 0}, first[2] = {0, 0}, tiles0 = 0;
 #pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int a = __shfl_up(is, o, kWave), b = __shfl_up(ist, o, kWave);
-            const int c = __shfl_up(isu, o, kWave), d = __shfl_up(isd, o, kWave);
-            if (lane >= o) { is += a; ist += b; isu += c; isd += d; }
+        for (int h = 0; h < 2; ++h) {
+            const int g = 2 * tid + h;
+            if (g < ng) {
+                const int nt = (gcnt[g] + kBM - 1) / kBM;
+                if (h == 0) {
+                    first[0] = gcnt[g];
+                    tiles0 = nt;
+                }
+                v[0] += gcnt[g];
+                v[1] += nt;
+                v[2] += nt * ngu_of(g);
+                v[3] += nt * ndn;
+            }
         }
-        int run = is - s, trun = ist - st, urun = isu - su, drun = isd - sd;
-        for (int g = g0; g < g1; ++g) {
-            const int nt = (gcnt[g] + kBM - 1) / kBM;
-            goff[g] = run;
-            gtoff[g] = trun;
-            guoff[g] = urun;
-            dnoff[g] = drun;
-            run += gcnt[g];
-            trun += nt;
-            urun += nt * ngu_of(g);
-            drun += nt * ndn;
+        int ex[4], tot[4];
+        block_scan4(v, ex, tot, wsum);
+        if (2 * tid < ng) {
+            goff[2 * tid] = ex[0];
+            gtoff[2 * tid] = ex[1];
         }
-        if (lane == kWave - 1) {
-            goff[ng] = is;
-            gtoff[ng] = ist;
-            guoff[ng] = isu;
-            dnoff[ng] = isd;
+        if (2 * tid + 1 < ng) {
+            goff[2 * tid + 1] = ex[0] + first[0];
+            gtoff[2 * tid + 1] = ex[1] + tiles0;
+        }
+        if (tid == 0) {
+            goff[ng] = tot[0];
+            gtoff[ng] = tot[1];
+            p.ntiles[0] = tot[1];
+            p.ntiles[1] = tot[2];
+            p.ntiles[2] = tot[3];
         }
     }
     __syncthreads();
-    for (int g = tid; g <= ng; g += kBucketThreads) {
+    for (int g = tid; g <= ng; g += kPlanThreads) {
         p.goff[g] = goff[g];
         if (g < ng) p.gcnt[g] = gcnt[g];
     }
-    if (tid == 0) {
-        p.ntiles[0] = gtoff[ng];
-        p.ntiles[1] = guoff[ng];
-        p.ntiles[2] = dnoff[ng];
-    }
-    for (int g = tid; g < ng; g += kBucketThreads) {
+    for (int g = tid; g < ng; g += kPlanThreads) {
         const int nt = (gcnt[g] + kBM - 1) / kBM;
         for (int i = 0; i < nt; ++i) p.tiles[gtoff[g] + i] = make_int2(g, i * kBM);
     }
-    // work items of the grouped GEMMs, longest first: bucketed by the tile's row count (a counting
-    // sort, 128 rows down to 1), so that the workgroups taken in list order fill the compute units
+    // work items of the grouped GEMMs, longest first: a counting sort of the tiles by row count
+    // (128 rows down to 1), so that the workgroups taken in list order fill the compute units
     // greedily and the heavy tiles do not form the tail. Within a bucket the order is arbitrary
     // (each item writes its own block of the output, so it does not change any result).
     if (p.wgu) {
-        int *hgu = dnoff + (E + 2), *hdn = hgu + (kBM + 1);  // [kBM + 1] each: counts, then cursors
-        for (int i = tid; i <= kBM; i += kBucketThreads) hgu[i] = hdn[i] = 0;
+        for (int i = tid; i <= kBM; i += kPlanThreads) hgu[i] = hdn[i] = 0;
         __syncthreads();
-        for (int g = tid; g < ng; g += kBucketThreads) {
-            const int nt = (gcnt[g] + kBM - 1) / kBM, ngu = ngu_of(g);
-            for (int i = 0; i < nt; ++i) {
-                const int rows = min(kBM, gcnt[g] - i * kBM);
-                atomicAdd(&hgu[rows], ngu);
-                atomicAdd(&hdn[rows], ndn);
+        const int ntile = gtoff[ng];
+        // tile i: its group by binary search over the tile offsets
+        auto tile_group = [&](int i) {
+            int lo = 0, hi = ng - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (gtoff[mid] <= i) lo = mid;
+                else hi = mid - 1;
+            }
+            return lo;
+        };
+        for (int i = tid; i < ntile; i += kPlanThreads) {
+            const int g = tile_group(i), m0 = (i - gtoff[g]) * kBM, rows = min(kBM, gcnt[g] - m0);
+            atomicAdd(&hgu[rows], ngu_of(g));
+            atomicAdd(&hdn[rows], ndn);
+        }
+        __syncthreads();
+        if (tid < kWave) {  // exclusive prefix from 128 rows down: lane l owns rows 128 - 2l, 127 - 2l
+            const int ra = kBM - 2 * tid, rb = kBM - 2 * tid - 1;
+            const int cu = hgu[ra] + (rb >= 1 ? hgu[rb] : 0), cd = hdn[ra] + (rb >= 1 ? hdn[rb] : 0);
+            int iu = cu, id = cd;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int a = __shfl_up(iu, o, kWave), b = __shfl_up(id, o, kWave);
+                if (tid >= o) {
+                    iu += a;
+                    id += b;
+                }
+            }
+            const int eu = iu - cu, ed = id - cd;
+            const int hua = hgu[ra], hda = hdn[ra];
+            hgu[ra] = eu;
+            hdn[ra] = ed;
+            if (rb >= 1) {
+                hgu[rb] = eu + hua;
+                hdn[rb] = ed + hda;
             }
         }
         __syncthreads();
-        if (tid == 0) {
-            int ru = 0, rd = 0;
-            for (int r = kBM; r >= 1; --r) {
-                const int cu = hgu[r], cd = hdn[r];
-                hgu[r] = ru;
-                hdn[r] = rd;
-                ru += cu;
-                rd += cd;
-            }
-        }
-        __syncthreads();
-        for (int g = wave; g < ng; g += kBucketWaves) {
-            const int nt = (gcnt[g] + kBM - 1) / kBM, ngu = ngu_of(g);
-            for (int i = lane; i < nt * max(ngu, ndn); i += kWave) {
-                const int mi = i % nt, col = i / nt, m0 = mi * kBM;
-                const int rows = min(kBM, gcnt[g] - m0);
-                if (col < ngu)
-                    p.wgu[atomicAdd(&hgu[rows], 1)] =
-                        make_int4(g, goff[g] + m0, rows | (col * kGuCols) << 16, gtoff[g] + mi);
-                if (col < ndn)
-                    p.wdn[atomicAdd(&hdn[rows], 1)] =
-                        make_int4(g, goff[g] + m0, rows | (col * kDnCols) << 16, gtoff[g] + mi);
-            }
+        for (int i = tid; i < ntile; i += kPlanThreads) {
+            const int g = tile_group(i), mi = i - gtoff[g], m0 = mi * kBM, rows = min(kBM, gcnt[g] - m0);
+            const int nu = ngu_of(g);
+            const int bu = atomicAdd(&hgu[rows], nu), bd = atomicAdd(&hdn[rows], ndn);
+            for (int c = 0; c < nu; ++c)
+                p.wgu[bu + c] = make_int4(g, goff[g] + m0, rows | (c * kGuCols) << 16, i);
+            for (int c = 0; c < ndn; ++c)
+                p.wdn[bd + c] = make_int4(g, goff[g] + m0, rows | (c * kDnCols) << 16, i);
         }
     }
-    // scatter
-    for (int q = tid; q < T * K; q += kBucketThreads) {
-        const int t = q / K;
-        const int e = min((unsigned)p.idx[q], (unsigned)(E - 1));
-        const int P = goff[e] + p.blkcnt[(size_t)(t / kWave) * E + e] + p.rank[q];
-        p.perm[P] = q;
-        p.pos[q] = P;
+    // scatter: four pairs per thread in flight at once
+    const int TK = T * K;
+    for (int q0 = tid; q0 < TK; q0 += 4 * kPlanThreads) {
+        int e[4], r[4], c[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = q0 + u * kPlanThreads;
+            e[u] = q < TK ? min((unsigned)p.idx[q], (unsigned)(E - 1)) : 0;
+            r[u] = q < TK ? p.rank[q] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = q0 + u * kPlanThreads;
+            c[u] = q < TK ? p.blkcnt[(size_t)(q / K / kWave) * E + e[u]] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = q0 + u * kPlanThreads;
+            if (q < TK) {
+                const int P = goff[e[u]] + c[u] + r[u];
+                p.perm[P] = q;
+                p.pos[q] = P;
+            }
+        }
     }
     if (p.Is)
-        for (int t = tid; t < T; t += kBucketThreads) p.perm[(size_t)T * K + t] = t * K;
+        for (int t = tid; t < T; t += kPlanThreads) p.perm[(size_t)TK + t] = t * K;
 }
 
 // ---- shared pieces of the grouped GEMMs -------------------------------------------------------------
@@ -415,8 +526,6 @@ __device__ __forceinline__ void flag_unsupported(int *status) {
 // (x for gate|up, h for down) hold their columns in the order the packed dequantisation produces
 // them: 4-bit (0,4,1,5,2,6,3,7), 8-bit (0,2,1,3). Both operands of every MFMA use the same order,
 // so each product and each k-sum is that of the natural order.
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
 template <int BITS>
 __device__ __forceinline__ int pair_pos(int c) {  // stored position of column c (blocks stay in place)
     if constexpr (BITS == 4) return (c & ~7) + 2 * (c & 3) + ((c >> 2) & 1);
@@ -426,7 +535,7 @@ __device__ __forceinline__ int pair_pos(int c) {  // stored position of column c
 // 8 bf16 activations (natural order) times 2^sh -> 8 fp16 in pair order (4-bit: one block of 8;
 // 8-bit: two blocks of 4).
 template <int BITS>
-__device__ __forceinline__ void act16_to_pairs8(const uint4 r, int sh, half2_t *out) {
+__device__ void act16_to_pairs8(const uint4 r, int sh, half2_t *out) {
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
     float v[8];
 #pragma unroll
@@ -443,44 +552,6 @@ __device__ __forceinline__ void act16_to_pairs8(const uint4 r, int sh, half2_t *
         out[2] = half2_t{(_Float16)v[4], (_Float16)v[6]};
         out[3] = half2_t{(_Float16)v[5], (_Float16)v[7]};
     }
-}
-
-// ---- x as fp16 -------------------------------------------------------------------------------------
-// x16[t] = x[t] * 2^-xe[t] in fp16, columns in pair order, with xe[t] = E - 15 for the token's
-// largest magnitude in [2^(E-1), 2^E): the token's values fill fp16's range up to 2^15 whatever
-// their bf16 magnitude (only values more than 2^29 below the token's largest become fp16
-// subnormals); the power-of-two scaling is exact and the gate|up epilogue multiplies it back. One
-// workgroup per token.
-constexpr int kX16Threads = 256;
-template <int BITS>
-__global__ void __launch_bounds__(kX16Threads) x16_kernel(BatchedParams p) {
-    __shared__ float red[kX16Threads / kWave];
-    const int t = blockIdx.x, H = p.H, tid = threadIdx.x;
-    const uint16_t *xr = p.x + (size_t)t * H;
-    float amax = 0.0f;
-    for (int c = tid * 8; c < H; c += kX16Threads * 8) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(xr + c);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(w[i] & 0xFFFF)), fabsf(bf16_to_f32(w[i] >> 16))));
-    }
-    amax = __int_as_float((int)wave_max_u32(__float_as_uint(amax)));  // non-negative floats order as integers
-    if (tid % kWave == 0) red[tid / kWave] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    int e = 0;
-    if (amax > 0.0f) {
-        frexpf(amax, &e);
-        e -= 15;
-    }
-    for (int c = tid * 8; c < H; c += kX16Threads * 8) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(xr + c);
-        half2_t hv[4];
-        act16_to_pairs8<BITS>(v, -e, hv);
-        *reinterpret_cast<uint4 *>(p.x16 + (size_t)t * H + c) = __builtin_bit_cast(uint4, hv);
-    }
-    if (tid == 0) p.xe[t] = e;
 }
 
 // ---- 4 / 5. grouped GEMMs --------------------------------------------------------------------------
@@ -1008,9 +1079,6 @@ __global__ void __launch_bounds__(256) combine_kernel(BatchedParams p) {
 // ---- launch sequence ---------------------------------------------------------------------------------
 hipError_t launch_router_topk(const BatchedParams &p, hipStream_t stream) {
     const int N = p.E + (p.sgate ? 1 : 0);
-    const size_t nsplit = ((size_t)N * p.H / 8 + kSplitThreads - 1) / kSplitThreads;
-    hipLaunchKernelGGL(router_split, dim3((unsigned)nsplit), dim3(kSplitThreads), 0, stream, p);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL(router_gemm, dim3((p.T + kRtT - 1) / kRtT, (N + kRtN - 1) / kRtN, router_ksplit(p.H)),
                        dim3(kGemmThreads), 0,
                        stream, p);
@@ -1022,16 +1090,19 @@ hipError_t launch_router_topk(const BatchedParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-size_t bucket_lds_bytes(int E) {
-    return 8 * (size_t)kBucketWaves * E + 4 * (size_t)(5 * E + 9 + 2 * (kBM + 1));
-}
+size_t bucket_lds_bytes(int E) { return 8 * (size_t)kCountWaves * E; }
 
 hipError_t launch_bucket(const BatchedParams &p, hipStream_t stream) {
+    if (p.E > kMaxGroups - 1 || p.K > 16) return hipErrorInvalidValue;
     const size_t blds = bucket_lds_bytes(p.E);
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&bucket_kernel),
+    const int nblk = (p.T + kWave - 1) / kWave;
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&bucket_count),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)blds);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), blds, stream, p);
+    hipLaunchKernelGGL(bucket_count, dim3((nblk + kCountWaves - 1) / kCountWaves), dim3(kCountWaves * kWave), blds,
+                       stream, p);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(bucket_plan, dim3(1), dim3(kPlanThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -1055,13 +1126,9 @@ hipError_t launch_batched(const BatchedParams &p, const BatchedWs &lay, hipStrea
     const int gu_lds4 = GCfg<4, false>::lds_bytes(p.H / 64), dn_lds4 = GCfg<4, true>::lds_bytes(p.Imax / 64);
     const int gu_lds8 = GCfg<8, false>::lds_bytes(p.H / 64), dn_lds8 = GCfg<8, true>::lds_bytes(p.Imax / 64);
     if (p.bits == 4) {
-        hipLaunchKernelGGL(x16_kernel<4>, dim3(p.T), dim3(kX16Threads), 0, stream, p);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
         if ((err = launch_gemm(gu_gemm<4>, ggu, gu_lds4, stream, p)) != hipSuccess) return err;
         if ((err = launch_gemm(dn_gemm<4>, gdn, dn_lds4, stream, p)) != hipSuccess) return err;
     } else {
-        hipLaunchKernelGGL(x16_kernel<8>, dim3(p.T), dim3(kX16Threads), 0, stream, p);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
         if ((err = launch_gemm(gu_gemm<8>, ggu, gu_lds8, stream, p)) != hipSuccess) return err;
         if ((err = launch_gemm(dn_gemm<8>, gdn, dn_lds8, stream, p)) != hipSuccess) return err;
     }
