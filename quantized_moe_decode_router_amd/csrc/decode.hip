@@ -156,16 +156,19 @@ __device__ bool ll_gather(const uint64_t *src, int n, uint32_t ep, float *dst, i
 // The LDS-DMA form of the global load writes lane l's 16 (or 4) bytes to LDS address
 // M0 + 16 l (4 l), M0 wave-uniform. It is issued from inline assembly so that the compiler does
 // not treat it as an LDS store it must wait for at every barrier; every consumer therefore waits
-// explicitly (dma_wait: all of this wave's vector-memory loads, then a workgroup barrier).
+// explicitly (dma_wait: all of this wave's vector-memory loads, then a workgroup barrier). The
+// issue itself carries no memory clobber, so that the LDS reads computing later DMAs' addresses
+// can be issued ahead of earlier DMAs; the waits (with a memory clobber) and the barriers keep
+// every read of the destination after its DMA lands and every earlier read of it before the DMA.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     // a generic pointer into LDS converted to its 32-bit LDS address (address space 3)
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char *)p));
 }
 __device__ __forceinline__ void dma16(const void *g, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "m0");
 }
 __device__ __forceinline__ void dma4(const void *g, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "m0");
 }
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most n of this wave's vector-memory loads are outstanding (n wave-uniform). Loads
