@@ -102,10 +102,9 @@ __device__ __forceinline__ void fail(int *ctrl) {
 // and its period -- the delay between a word's arrival and its detection -- with it. The values
 // go to LDS once at the end. Returns false on timeout or when any workgroup has failed.
 template <int NW>
-__device__ __forceinline__ bool gather_slots(const uint64_t *src, int m, uint32_t ep, float *dst, int *ctrl,
-                                             unsigned spin) {
+__device__ __forceinline__ bool poll_slots(const uint64_t *src, int m, uint32_t ep, uint64_t (&w)[NW], int *ctrl,
+                                           unsigned spin) {
     const int tid = threadIdx.x;
-    uint64_t w[NW];
     for (unsigned it = 0;; ++it) {
         // lanes past m read word m - 1 (it becomes current like any other), which keeps the loads
         // unpredicated
@@ -119,12 +118,32 @@ __device__ __forceinline__ bool gather_slots(const uint64_t *src, int m, uint32_
         if ((it & 31u) == 31u && status_of(ctrl) != 0) return false;
         __builtin_amdgcn_s_sleep(1);
     }
+    return true;
+}
+template <int NW>
+__device__ __forceinline__ bool gather_slots(const uint64_t *src, int m, uint32_t ep, float *dst, int *ctrl,
+                                             unsigned spin) {
+    const int tid = threadIdx.x;
+    uint64_t w[NW];
+    if (!poll_slots<NW>(src, m, ep, w, ctrl, spin)) return false;
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
         const int i = tid + k * kDecodeThreads;
         if (i < m) dst[i] = __uint_as_float(static_cast<uint32_t>(w[k]));
     }
     return true;
+}
+// Workgroup-wide AND of every thread's ok through LDS (slots written, read, then released again).
+__device__ __forceinline__ bool all_ok(bool ok) {
+    __shared__ int vote[kWaves];
+    const unsigned long long bad = __ballot(!ok);
+    if ((threadIdx.x % kWave) == 0) vote[threadIdx.x / kWave] = bad ? 0 : 1;
+    lds_barrier();
+    int all = 1;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) all &= vote[w];
+    lds_barrier();
+    return all != 0;
 }
 __device__ bool ll_gather(const uint64_t *src, int n, uint32_t ep, float *dst, int *ctrl, unsigned spin) {
     constexpr int kPass = kMaxGather * kDecodeThreads;
@@ -140,16 +159,7 @@ __device__ bool ll_gather(const uint64_t *src, int n, uint32_t ep, float *dst, i
         else if (kw <= 12) ok = gather_slots<12>(src + base, m, ep, dst + base, ctrl, spin);
         else ok = gather_slots<kMaxGather>(src + base, m, ep, dst + base, ctrl, spin);
     }
-    // workgroup-wide AND of ok through LDS (slots written, read, then released again)
-    __shared__ int vote[kWaves];
-    const unsigned long long bad = __ballot(!ok);
-    if ((threadIdx.x % kWave) == 0) vote[threadIdx.x / kWave] = bad ? 0 : 1;
-    lds_barrier();
-    int all = 1;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) all &= vote[w];
-    lds_barrier();
-    return all != 0;
+    return all_ok(ok);
 }
 
 // ---- LDS DMA ------------------------------------------------------------------------------------
@@ -642,6 +652,68 @@ __device__ __forceinline__ void build_limbs(const float (&v)[4], int8_t *dst, fl
 }
 
 // ---- layer input ---------------------------------------------------------------------------------
+// RMS glue of y_{l-1} for tokens t0 .. t0 + n - 1 (n <= TT) of H = 512 S columns, straight from
+// registers: their words are polled at once (slot u S + j of thread tid: y[t0 + u][tid + 512 j]);
+// per token the sum of squares adds the thread's words in column order, then the wave sum, then
+// the waves in order -- the order of a thread-strided loop over the row -- and x = bf16_rne(y /
+// sqrt(mean(y^2) + eps)) goes from the register holding y to its half of the pair table. One wait
+// for the exchange and one barrier per group of tokens.
+template <int BITS, int S, int TT>
+__device__ bool chained_group(const DecodeParams &p, const uint64_t *ysrc, int t0, int n, uint32_t ep,
+                              const Lds &s, unsigned spin) {
+    constexpr int NW = S * TT;
+    constexpr int H = 512 * S, nsl = H / 32;
+    static_assert(kDecodeThreads == 512 && NW <= kMaxGather, "slot layout");
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    uint64_t w[NW];
+    if (!all_ok(poll_slots<NW>(ysrc + (size_t)t0 * H, n * H, ep, w, p.ctrl, spin))) return false;
+#pragma unroll
+    for (int u = 0; u < TT; ++u) {
+        if (u < n) {
+            float ss = 0.0f;
+#pragma unroll
+            for (int j = 0; j < S; ++j) {
+                const float v = __uint_as_float(static_cast<uint32_t>(w[u * S + j]));
+                ss += v * v;
+            }
+            ss = wave_sum(ss);
+            if (lane == 0) s.red[u * kWaves + wave] = ss;  // TT * kWaves <= 64 slots
+        }
+    }
+    lds_barrier();
+    uint16_t *xp16 = reinterpret_cast<uint16_t *>(s.xp);
+#pragma unroll
+    for (int u = 0; u < TT; ++u) {
+        if (u < n) {
+            float ss = 0.0f;
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v) ss += s.red[u * kWaves + v];
+            const float inv = 1.0f / sqrtf(ss / (float)H + p.eps);
+#pragma unroll
+            for (int j = 0; j < S; ++j) {
+                const int h = tid + 512 * j, sl = h >> 5;
+                int q, half;
+                col_pair<BITS>(h & 31, q, half);
+                const float v = __uint_as_float(static_cast<uint32_t>(w[u * S + j]));
+                xp16[(((t0 + u) * nsl + sl) * 20 + q) * 2 + half] = static_cast<uint16_t>(f32_to_bf16_rne(v * inv));
+            }
+        }
+    }
+    lds_barrier();  // s.red is reused by the next group
+    return true;
+}
+// All T tokens in groups of TT (words per thread <= kMaxGather).
+template <int BITS, int S>
+__device__ bool chained_input(const DecodeParams &p, const uint64_t *ysrc, uint32_t ep, const Lds &s,
+                              unsigned spin) {
+    constexpr int TT = kMaxGather / S < 8 ? kMaxGather / S : 8;
+    const int T = p.T;
+    if (T == 1) return chained_group<BITS, S, 1>(p, ysrc, 0, 1, ep, s, spin);
+    for (int t0 = 0; t0 < T; t0 += TT)
+        if (!chained_group<BITS, S, TT>(p, ysrc, t0, min(TT, T - t0), ep, s, spin)) return false;
+    return true;
+}
+
 // x of every token into the pair table s.xp (and its slice constants): x_in for l == 0 (or
 // unchained), else the RMS glue of y_{l-1}: x = bf16_rne(y / sqrt(mean(y^2) + eps)); every
 // workgroup computes the same bits.
@@ -657,7 +729,15 @@ __device__ bool layer_input(const DecodeParams &p, int l, uint32_t ep, const Lds
             const uint32_t a = xr[pair_col_a<BITS>(q)], c = xr[pair_col_b<BITS>(q)];
             s.xp[(t * nsl + sl) * 20 + q] = a | (c << 16);
         }
+    } else if (H >= 512) {
+        const uint64_t *ysrc = p.ll_y + (size_t)(l - 1) * T * H;
+        bool ok;
+        if (H == 512) ok = chained_input<BITS, 1>(p, ysrc, ep, s, spin);
+        else if (H == 1024) ok = chained_input<BITS, 2>(p, ysrc, ep, s, spin);
+        else ok = chained_input<BITS, 4>(p, ysrc, ep, s, spin);  // H == 2048
+        if (!ok) return false;
     } else {
+        // H = 256: token by token through LDS
         const uint64_t *ysrc = p.ll_y + (size_t)(l - 1) * T * H;
         float *yb = reinterpret_cast<float *>(s.hp);
         for (int t = 0; t < T; ++t) {
