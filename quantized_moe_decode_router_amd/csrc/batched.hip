@@ -1,11 +1,12 @@
 // batched.hip -- one MoE layer for a batch of T tokens (prefill / batched decode) on gfx950.
 //
-// Six launches on one stream, no host synchronisation:
+// Seven launches on one stream, no host synchronisation:
 //   1. router_gemm   logits[T][E] (+ shared-gate logit) = x . R^T on v_mfma_f32_16x16x32_bf16, the
 //                    fp32 router split into bf16 hi + lo halves on its way into LDS (x is bf16,
 //                    exact)
-//   2. topk_kernel   one wave per token: top-k by (logit desc, index asc), renormalised weights
-//                    (softmax of the kept logits), gamma = sigmoid(gate logit); x as scaled fp16
+//   2. topk_kernel   per token one wave: top-k by (logit desc, index asc), renormalised weights
+//                    (softmax of the kept logits), gamma = sigmoid(gate logit); beside it another
+//                    wave: x as scaled fp16
 //   3. bucket_count  per block of 64 tokens: per-expert counts and every pair's rank in its block
 //      bucket_plan   one workgroup: exclusive scans, stable scatter (pairs of one expert stay in
 //                    pair order), the inverse map, the list of 128-row tiles of every group
@@ -183,14 +184,23 @@ __device__ __forceinline__ void wave_x16(const BatchedParams &p, int t) {
     if (lane == 0) p.xe[t] = e;
 }
 
-constexpr int kTopkWaves = 4;
-__global__ void __launch_bounds__(kTopkWaves * kWave) topk_kernel(BatchedParams p) {
+// kTopkTokens tokens per workgroup: wave w < kTopkTokens selects token w's experts while wave
+// kTopkTokens + w scales its x, so the two latency chains of a token run side by side.
+constexpr int kTopkTokens = 2;
+__global__ void __launch_bounds__(2 * kTopkTokens * kWave) topk_kernel(BatchedParams p) {
     extern __shared__ __align__(16) char smem[];
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int E = p.E, K = p.K;
-    const int t = blockIdx.x * kTopkWaves + wave;
-    float *lt = reinterpret_cast<float *>(smem) + (size_t)wave * E;
+    const int t = blockIdx.x * kTopkTokens + wave % kTopkTokens;
     if (t >= p.T) return;  // whole wave leaves together; no workgroup barrier follows
+    if (wave >= kTopkTokens) {
+        if (p.x16) {
+            if (p.bits == 4) wave_x16<4>(p, t);
+            else wave_x16<8>(p, t);
+        }
+        return;
+    }
+    float *lt = reinterpret_cast<float *>(smem) + (size_t)wave * E;
     // logits: the router GEMM's range partial sums added in range order, then the bias
     const int N = E + (p.sgate ? 1 : 0), ks = router_ksplit(p.H);
     const float *part = p.lpart + (size_t)t * N;
@@ -226,10 +236,6 @@ __global__ void __launch_bounds__(kTopkWaves * kWave) topk_kernel(BatchedParams 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     wave_topk(lt, E, K, p.idx + (size_t)t * K, p.w + (size_t)t * K);
     if (lane == 0 && p.gamma) p.gamma[t] = p.sgate ? 1.0f / (1.0f + expf(-gate)) : 0.0f;
-    if (p.x16) {
-        if (p.bits == 4) wave_x16<4>(p, t);
-        else wave_x16<8>(p, t);
-    }
 }
 
 // ---- 3. histogram, exclusive scan, stable scatter, tile list -------------------------------------
@@ -1084,9 +1090,9 @@ hipError_t launch_router_topk(const BatchedParams &p, hipStream_t stream) {
                        stream, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const size_t lds = sizeof(float) * (size_t)kTopkWaves * p.E;
-    hipLaunchKernelGGL(topk_kernel, dim3((p.T + kTopkWaves - 1) / kTopkWaves), dim3(kTopkWaves * kWave), lds, stream,
-                       p);
+    const size_t lds = sizeof(float) * (size_t)kTopkTokens * p.E;
+    hipLaunchKernelGGL(topk_kernel, dim3((p.T + kTopkTokens - 1) / kTopkTokens), dim3(2 * kTopkTokens * kWave), lds,
+                       stream, p);
     return hipGetLastError();
 }
 
