@@ -754,17 +754,48 @@ __device__ __forceinline__ void wdma_block(const WDma<BITS, DN> &d, const GroupW
 #pragma unroll
     for (int u = 0; u < C::NBC; ++u) dma16s(d.coff[u], base, lds_addr(buf + 1024 * u));
 }
-// The lane's fragments of k-step kb (slice kb % SB of the block in buf; f scales s and b).
-template <int BITS, bool DN>
-__device__ __forceinline__ BQ dequant_step(const char *buf, const char *sq, int ng, int kb, float f, int fi, int fj) {
+// The lane's scale and bias halves (bf16 bits) of one B block's SB k-steps for its two rows:
+// quarter k (scales of rows fi, 16 + fi, then biases), k-step j at bits 16 (j & 1) of w[k][j / 2].
+// One LDS read per quarter and block (SB halves at once) instead of one per k-step: a quarter's
+// 16 rows sit ng halves apart, so these reads conflict on the banks whatever their width.
+template <int SB>
+struct SBlk {
+    uint32_t w[4][(SB + 1) / 2];
+};
+template <int SB>
+__device__ __forceinline__ SBlk<SB> load_sblk(const char *sq, int ng, int kb0, int fi) {
+    SBlk<SB> b;
+    const int qb = 32 * ng;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const char *a = sq + k * qb + (fi * ng + kb0) * 2;  // kb0 % SB == 0: aligned to 2 SB bytes
+        if constexpr (SB == 4) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(a);
+            b.w[k][0] = v.x;
+            b.w[k][1] = v.y;
+        } else if constexpr (SB == 2) {
+            b.w[k][0] = *reinterpret_cast<const uint32_t *>(a);
+        } else {
+            b.w[k][0] = *reinterpret_cast<const uint16_t *>(a);
+        }
+    }
+    return b;
+}
+template <int SB, int J>
+__device__ __forceinline__ uint16_t sblk_half(const SBlk<SB> &b, int k) {
+    return static_cast<uint16_t>(b.w[k][J / 2] >> (16 * (J & 1)));
+}
+// The lane's fragments of k-step kb = J (mod SB) (slice J of the block in buf; f scales s and b).
+template <int BITS, bool DN, int J>
+__device__ __forceinline__ BQ dequant_step(const char *buf, const SBlk<GCfg<BITS, DN>::SB> &sb, float f, int fi,
+                                           int fj) {
     using C = GCfg<BITS, DN>;
     constexpr int m = C::BB / 16 - 1;
-    const int s = kb % C::SB, qb = 32 * ng;
-    const uint16_t *sg = reinterpret_cast<const uint16_t *>(sq);
-    const half2_t s0 = f16_splat(sg[fi * ng + kb], f);
-    const half2_t s1 = f16_splat(sg[qb / 2 + fi * ng + kb], f);
-    const half2_t b0 = f16_splat(sg[qb + fi * ng + kb], f);
-    const half2_t b1 = f16_splat(sg[3 * qb / 2 + fi * ng + kb], f);
+    constexpr int s = J;
+    const half2_t s0 = f16_splat(sblk_half<C::SB, J>(sb, 0), f);
+    const half2_t s1 = f16_splat(sblk_half<C::SB, J>(sb, 1), f);
+    const half2_t b0 = f16_splat(sblk_half<C::SB, J>(sb, 2), f);
+    const half2_t b1 = f16_splat(sblk_half<C::SB, J>(sb, 3), f);
     const int r0 = fi, r1 = 16 + fi;
     BQ q;
     if constexpr (BITS == 4) {
@@ -798,7 +829,8 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 // The k-loop shared by both GEMMs, unrolled by SB so that every wait count is a constant.
 // issue_a(kb): the A DMAs of k-step kb (NA per wave); mfma(stage, bq): the MFMAs of one k-step on
-// A stage `stage`; dq(kb, buf): the fragments of k-step kb from B buffer `buf`.
+// A stage `stage`; dq(kb, buf, j): the fragments of k-step kb from B buffer `buf`, j = kb % SB as an
+// integral constant.
 template <int BITS, bool DN, int NA, typename IssueA, typename IssueB, typename Mfma, typename Dq>
 __device__ __forceinline__ void kloop(int nk, IssueA issue_a, IssueB issue_b, Mfma mfma, Dq dq) {
     using C = GCfg<BITS, DN>;
@@ -810,7 +842,7 @@ __device__ __forceinline__ void kloop(int nk, IssueA issue_a, IssueB issue_b, Mf
         if ((t + 1 + L) % SB == 0) issue_b((t + 1 + L) / SB);
     }
     wait_step<L, SB, NA, NBC, 0>();
-    BQ bq = dq(0, 0);
+    BQ bq = dq(0, 0, std::integral_constant<int, 0>{});
     for (int kb0 = 0; kb0 < nk; kb0 += SB) {
         static_for<0, SB>([&](auto jc) __attribute__((always_inline)) {
             constexpr int j = decltype(jc)::value;
@@ -820,7 +852,7 @@ __device__ __forceinline__ void kloop(int nk, IssueA issue_a, IssueB issue_b, Mf
             issue_a(kb + L);
             if constexpr ((j + 1 + L) % SB == 0) issue_b((kb + 1 + L) / SB);
             mfma(kb % C::RA, bq);
-            bq = dq(kb + 1, ((kb + 1) / SB) % C::NBUF);
+            bq = dq(kb + 1, ((kb + 1) / SB) % C::NBUF, std::integral_constant<int, (j + 1) % SB>{});
         });
     }
     vm_wait<0>();  // no DMA may still write this workgroup's LDS once it leaves
@@ -877,8 +909,11 @@ __device__ __forceinline__ void gu_body(const BatchedParams &p, char *lds, int g
             }
         }
     };
-    auto dq = [&](int kb, int buf) __attribute__((always_inline)) {
-        return dequant_step<BITS, false>(bbuf + buf * C::B_BLOCK, sq, ng, min(kb, nk - 1), 1.0f, fi, fj);
+    SBlk<C::SB> sb;
+    auto dq = [&](int kb, int buf, auto jc) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
+        if constexpr (J == 0) sb = load_sblk<C::SB>(sq, ng, min(kb, nk - C::SB), fi);
+        return dequant_step<BITS, false, J>(bbuf + buf * C::B_BLOCK, sb, 1.0f, fi, fj);
     };
     kloop<BITS, false, NA>(nk, issue_a, issue_b, mfma, dq);
     // epilogue: lane l, register r of subtile i -> row 16 i + 4 (l / 16) + r, j = j0 + 16 w + l % 16.
@@ -1018,10 +1053,13 @@ __device__ __forceinline__ void dn_body(const BatchedParams &p, char *lds, int g
             }
         }
     };
-    auto dq = [&](int kb, int buf) __attribute__((always_inline)) {
+    SBlk<C::SB> sb;
+    auto dq = [&](int kb, int buf, auto jc) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
         const int k = min(kb, nk - 1);
         const float f = ldexpf(1.0f, __builtin_amdgcn_readlane(hexp_lane, k));
-        return dequant_step<BITS, true>(bbuf + buf * C::B_BLOCK, sq, ng, k, f, fi, fj);
+        if constexpr (J == 0) sb = load_sblk<C::SB>(sq, ng, min(kb, nk - C::SB), fi);
+        return dequant_step<BITS, true, J>(bbuf + buf * C::B_BLOCK, sb, f, fi, fj);
     };
     kloop<BITS, true, 2 * NA>(nk, issue_a, issue_b, mfma, dq);
     // epilogue: lane l, register r of subtile i, block nb -> row 16 i + 4 (l / 16) + r, output row
