@@ -472,6 +472,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--batched-steps", type=int, default=10,
                     help="steps of the batched leg (0 skips it)")
+    ap.add_argument("--batched-only", action="store_true",
+                    help="run only the batched leg (T = 512 per layer call) and print its result")
     ap.add_argument("--residency", action="store_true",
                     help="only the expert-residency sweep over pool sizes (one JSON line)")
     ap.add_argument("--residency-steps", type=int, default=100)
@@ -508,6 +510,9 @@ def main():
     if args.phases:
         print(json.dumps({"phases": phase_profile(stack, wl, T, warmup=args.warmup, steps=args.steps,
                                                   chained=not args.independent)}), flush=True)
+        return
+    if args.batched_only:
+        print(json.dumps({"batched": batched_leg(stack, max(args.batched_steps, 1), 2)}), flush=True)
         return
     if args.residency:
         print(json.dumps({"residency": residency_sweep(stack, wl, warmup=args.residency_warmup,

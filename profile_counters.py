@@ -7,6 +7,9 @@ the path).
              profiles/<kernel>_<workload>_counters.json: per-launch FETCH_SIZE and WRITE_SIZE, each
              scaled by (true bytes / counted bytes) of the copy, and the hash of the kernel sources
              they were taken on (bench.py reports the traffic only while that hash still matches).
+  table      per kernel, the mean per dispatch of every counter in the given CSVs as a markdown
+             table: FETCH_SIZE / WRITE_SIZE as calibrated bytes, MfmaUtil in percent,
+             SQ_INSTS_VALU_MFMA_MOPS_F16 as fp16 MFMA flops (512 per count), the rest raw.
 """
 import argparse
 import csv
@@ -82,6 +85,57 @@ def summarize(a) -> None:
     print(json.dumps(out))
 
 
+def table(a) -> None:
+    rows = []
+    for g in a.csv:
+        rows.extend(counter_rows(g))
+    ff = fw = None
+    if a.copy_fetch and a.copy_write:
+        cf, _ = per_dispatch(counter_rows(a.copy_fetch), a.copy_kernel, "FETCH_SIZE")
+        cw, _ = per_dispatch(counter_rows(a.copy_write), a.copy_kernel, "WRITE_SIZE")
+        ff, fw = a.copy_mib * 1024.0 / cf, a.copy_mib * 1024.0 / cw
+    # kernel -> counter -> dispatch -> summed value
+    acc = {}
+    for r in rows:
+        k = r.get("Kernel_Name", "")
+        if not any(s in k for s in a.kernels):
+            continue
+        short = next(s for s in a.kernels if s in k)
+        d = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        c = acc.setdefault(short, {}).setdefault(r["Counter_Name"], {})
+        c[d] = c.get(d, 0.0) + float(r["Counter_Value"])
+    counters = sorted({c for v in acc.values() for c in v})
+    head = ["kernel", "dispatches"]
+    for c in counters:
+        head.append({"FETCH_SIZE": "fetched MB", "WRITE_SIZE": "written MB", "MfmaUtil": "MFMA busy %",
+                     "SQ_INSTS_VALU_MFMA_MOPS_F16": "fp16 MFMA GFLOP"}.get(c, c))
+    print("| " + " | ".join(head) + " |")
+    print("|" + "---|" * len(head))
+    for k in a.kernels:
+        if k not in acc:
+            continue
+        cells = [k, str(max(len(v) for v in acc[k].values()))]
+        for c in counters:
+            vals = acc[k].get(c)
+            if not vals:
+                cells.append("")
+                continue
+            m = sum(vals.values()) / len(vals)
+            if c == "FETCH_SIZE" and ff:
+                cells.append(f"{m * ff * 1024 / 1e6:.1f}")
+            elif c == "WRITE_SIZE" and fw:
+                cells.append(f"{m * fw * 1024 / 1e6:.1f}")
+            elif c == "MfmaUtil":
+                cells.append(f"{m:.1f}")
+            elif c == "SQ_INSTS_VALU_MFMA_MOPS_F16":
+                cells.append(f"{m * 512 / 1e9:.2f}")
+            else:
+                cells.append(f"{m:.4g}")
+        print("| " + " | ".join(cells) + " |")
+    if ff:
+        print(f"\nCopy calibration: fetched bytes = {ff:.3f} x FETCH_SIZE KiB x 1024, written = {fw:.3f} x WRITE_SIZE.")
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -97,9 +151,18 @@ def main() -> None:
     s.add_argument("--copy-fetch", required=True)
     s.add_argument("--copy-write", required=True)
     s.add_argument("--copy-mib", type=int, default=COPY_MIB)
+    t = sub.add_parser("table")
+    t.add_argument("--csv", action="append", required=True, help="glob of counter CSV(s); repeatable")
+    t.add_argument("--kernels", nargs="+", required=True, help="kernel name substrings, in table order")
+    t.add_argument("--copy-kernel", default="copy")
+    t.add_argument("--copy-fetch")
+    t.add_argument("--copy-write")
+    t.add_argument("--copy-mib", type=int, default=COPY_MIB)
     a = ap.parse_args()
     if a.cmd == "copy":
         run_copy(a.mib, a.reps)
+    elif a.cmd == "table":
+        table(a)
     else:
         summarize(a)
 
