@@ -312,31 +312,15 @@ __device__ __forceinline__ void block_scan4(int v[4], int excl[4], int total[4],
     __syncthreads();
 }
 
-__global__ void __launch_bounds__(kPlanThreads) bucket_plan(BatchedParams p) {
-    __shared__ int gcnt[kMaxGroups], goff[kMaxGroups + 1], gtoff[kMaxGroups + 1];
-    __shared__ int wsum[kPlanWaves][4];
-    __shared__ int hgu[kBM + 1], hdn[kBM + 1];
+// From the group sizes gcnt[0..E) (per-block prefixes already in place): the shared group's size,
+// the scans of the group sizes, tile counts and work items (goff, gtoff, the totals in p.ntiles),
+// p.gcnt / p.goff, the tile list and, when p.wgu is set, both GEMMs' work lists, longest first.
+// Called by the whole workgroup of kPlanThreads; the arrays live in the caller's LDS.
+__device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *gtoff, int (*wsum)[4], int *hgu,
+                            int *hdn) {
     const int tid = threadIdx.x;
-    const int T = p.T, K = p.K, E = p.E;
+    const int T = p.T, E = p.E;
     const int ng = E + (p.Is ? 1 : 0);  // groups: experts, then the shared expert
-    const int nblk = (T + kWave - 1) / kWave;
-    // per expert: exclusive prefix over blocks (in place) and the total; the counts of eight blocks
-    // are loaded before any is rewritten, so that a chunk costs one memory round trip
-    if (tid < E) {
-        const int e = tid;
-        int run = 0;
-        for (int b0 = 0; b0 < nblk; b0 += 8) {
-            int c[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) c[i] = b0 + i < nblk ? p.blkcnt[(size_t)(b0 + i) * E + e] : 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (b0 + i < nblk) p.blkcnt[(size_t)(b0 + i) * E + e] = run;
-                run += c[i];
-            }
-        }
-        gcnt[e] = run;
-    }
     if (tid == 0 && p.Is) gcnt[E] = T;
     __syncthreads();
     // exclusive scans of the group sizes, their tile counts and their gate|up and down work items
@@ -443,6 +427,33 @@ __global__ void __launch_bounds__(kPlanThreads) bucket_plan(BatchedParams p) {
                 p.wdn[bd + c] = make_int4(g, goff[g] + m0, rows | (c * kDnCols) << 16, i);
         }
     }
+}
+
+__global__ void __launch_bounds__(kPlanThreads) bucket_plan(BatchedParams p) {
+    __shared__ int gcnt[kMaxGroups], goff[kMaxGroups + 1], gtoff[kMaxGroups + 1];
+    __shared__ int wsum[kPlanWaves][4];
+    __shared__ int hgu[kBM + 1], hdn[kBM + 1];
+    const int tid = threadIdx.x;
+    const int T = p.T, K = p.K, E = p.E;
+    const int nblk = (T + kWave - 1) / kWave;
+    // per expert: exclusive prefix over blocks (in place) and the total; the counts of eight blocks
+    // are loaded before any is rewritten, so that a chunk costs one memory round trip
+    if (tid < E) {
+        const int e = tid;
+        int run = 0;
+        for (int b0 = 0; b0 < nblk; b0 += 8) {
+            int c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = b0 + i < nblk ? p.blkcnt[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (b0 + i < nblk) p.blkcnt[(size_t)(b0 + i) * E + e] = run;
+                run += c[i];
+            }
+        }
+        gcnt[e] = run;
+    }
+    plan_groups(p, gcnt, goff, gtoff, wsum, hgu, hdn);
     // scatter: four pairs per thread in flight at once
     const int TK = T * K;
     for (int q0 = tid; q0 < TK; q0 += 4 * kPlanThreads) {
@@ -470,6 +481,67 @@ __global__ void __launch_bounds__(kPlanThreads) bucket_plan(BatchedParams p) {
     }
     if (p.Is)
         for (int t = tid; t < T; t += kPlanThreads) p.perm[(size_t)TK + t] = t * K;
+}
+
+// Both bucket steps in one workgroup, for T <= 64 kPlanWaves tokens and E <= kSmallBucketE: wave w
+// builds block w's lane masks as bucket_count does, but the counts and the per-block prefixes stay
+// in LDS and every pair's rank stays in the register of the lane that scatters it, so that no
+// count, rank or index goes back through memory between the steps. The results are those of the
+// two-launch form.
+constexpr int kSmallBucketE = 512;
+__host__ __device__ inline size_t bucket_small_lds_bytes(int E) { return 12 * (size_t)kPlanWaves * E; }
+__global__ void __launch_bounds__(kPlanThreads) bucket_small(BatchedParams p) {
+    extern __shared__ __align__(16) char smem[];
+    __shared__ int gcnt[kMaxGroups], goff[kMaxGroups + 1], gtoff[kMaxGroups + 1];
+    __shared__ int wsum[kPlanWaves][4];
+    __shared__ int hgu[kBM + 1], hdn[kBM + 1];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int T = p.T, K = p.K, E = p.E;
+    const int nblk = (T + kWave - 1) / kWave;  // <= kPlanWaves
+    unsigned long long *masks = reinterpret_cast<unsigned long long *>(smem) + (size_t)wave * E;
+    int *cnt = reinterpret_cast<int *>(smem + 8 * (size_t)kPlanWaves * E);  // [block][E]
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const int t = wave * kWave + lane;
+    const bool valid = wave < nblk && t < T;
+    for (int e = lane; e < E; e += kWave) masks[e] = 0ull;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int ex[16], rk[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ex[k] = k < K && valid ? min((unsigned)p.idx[(size_t)t * K + k], (unsigned)(E - 1)) : -1;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        if (ex[k] >= 0) atomicOr(&masks[ex[k]], 1ull << lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int k = 0; k < 16; ++k) rk[k] = ex[k] >= 0 ? __popcll(masks[ex[k]] & below) : 0;
+    if (wave < nblk)
+        for (int e = lane; e < E; e += kWave) cnt[wave * E + e] = __popcll(masks[e]);
+    __syncthreads();
+    // per expert: exclusive prefix over blocks (in place) and the total
+    for (int e = tid; e < E; e += kPlanThreads) {
+        int run = 0;
+        for (int b = 0; b < nblk; ++b) {
+            const int c = cnt[b * E + e];
+            cnt[b * E + e] = run;
+            run += c;
+        }
+        gcnt[e] = run;
+    }
+    plan_groups(p, gcnt, goff, gtoff, wsum, hgu, hdn);
+    // scatter by the lane that ranked the pair: expert offset + block prefix + rank
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        if (ex[k] >= 0) {
+            const int q = t * K + k, P = goff[ex[k]] + cnt[wave * E + ex[k]] + rk[k];
+            p.perm[P] = q;
+            p.pos[q] = P;
+        }
+    if (p.Is)
+        for (int u = tid; u < T; u += kPlanThreads) p.perm[(size_t)T * K + u] = u * K;
 }
 
 // ---- shared pieces of the grouped GEMMs -------------------------------------------------------------
@@ -1138,8 +1210,16 @@ size_t bucket_lds_bytes(int E) { return 8 * (size_t)kCountWaves * E; }
 
 hipError_t launch_bucket(const BatchedParams &p, hipStream_t stream) {
     if (p.E > kMaxGroups - 1 || p.K > 16) return hipErrorInvalidValue;
-    const size_t blds = bucket_lds_bytes(p.E);
     const int nblk = (p.T + kWave - 1) / kWave;
+    if (nblk <= kPlanWaves && p.E <= kSmallBucketE) {
+        const size_t lds = bucket_small_lds_bytes(p.E);
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&bucket_small),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(bucket_small, dim3(1), dim3(kPlanThreads), lds, stream, p);
+        return hipGetLastError();
+    }
+    const size_t blds = bucket_lds_bytes(p.E);
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&bucket_count),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)blds);
     if (err != hipSuccess) return err;

@@ -35,7 +35,8 @@ def run_batched(shape, layer, x, T, dev, ws=None):
 # ------------------------------------------------------------------------------ grouping (b2-b4)
 
 @pytest.mark.parametrize("T,K,E,seed", [(1, 1, 16, 0), (4, 2, 16, 1), (33, 8, 256, 2), (512, 8, 256, 3),
-                                        (130, 10, 512, 4), (2000, 4, 8, 5), (65, 16, 1024, 6)])
+                                        (130, 10, 512, 4), (2000, 4, 8, 5), (65, 16, 1024, 6),
+                                        (1024, 8, 512, 7), (1025, 2, 64, 8)])
 def test_group_pairs_bit_exact(T, K, E, seed):
     """Histogram, exclusive scan and stable scatter equal the oracle's plain definition exactly,
     for uniform and for heavily skewed (Zipf-like) selections."""
