@@ -633,17 +633,11 @@ def decode_step_bytes(shape, L: int, T: int, idx_steps=None) -> float:
 
 
 def run_metadata(seed: int) -> dict:
-    """What identifies the run: source revision, device, runtime versions, clocks, seed."""
-    import subprocess
-
+    """What identifies the run: source revision, device, runtime versions, clocks, seed. Read from
+    files only: this process has initialised the GPU, so it starts no other program."""
     import torch
-    meta = {"seed": seed, "kernel_source_hash": kernel_source_hash(), "git": None,
+    meta = {"seed": seed, "kernel_source_hash": kernel_source_hash(), "git": _git_head(),
             "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
-    try:
-        meta["git"] = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short", "HEAD"], capture_output=True,
-                                     text=True, timeout=10).stdout.strip() or None
-    except Exception:
-        pass
     try:
         props = torch.cuda.get_device_properties(0)
         meta["gpu"] = props.name
@@ -656,14 +650,39 @@ def run_metadata(seed: int) -> dict:
             meta["rocm"] = f.read().strip()
     except Exception:
         pass
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
-                             timeout=20).stdout
-        card = next(iter(json.loads(out).values()))
-        meta["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower() or "clk" in k.lower()}
-    except Exception:
-        pass
+    clocks = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    cur = [l.split(":", 1)[1].strip(" *\n") for l in f if l.rstrip().endswith("*")]
+                if cur:
+                    clocks[f"{os.path.basename(os.path.dirname(dev))}.{name[3:]}"] = cur[0]
+            except OSError:
+                pass
+    meta["clocks"] = clocks or None
     return meta
+
+
+def _git_head():
+    """The checked-out commit from .git (None where the tree was copied without it)."""
+    try:
+        with open(os.path.join(ROOT, ".git", "HEAD")) as f:
+            head = f.read().strip()
+        if not head.startswith("ref:"):
+            return head[:7]
+        ref = head.split(None, 1)[1]
+        p = os.path.join(ROOT, ".git", ref)
+        if os.path.exists(p):
+            with open(p) as f:
+                return f.read().strip()[:7]
+        with open(os.path.join(ROOT, ".git", "packed-refs")) as f:
+            for line in f:
+                if line.strip().endswith(ref):
+                    return line.split()[0][:7]
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":
