@@ -97,8 +97,6 @@ size_t forward_decode_part(const moe_shape *s) { return align_up(decode_ws_bytes
 moe_status decode_supported(const moe_shape *s, int T, int grid, bool xt = false) {
     if (s->hidden > 2048 || s->inter > 2048 || s->shared_inter > 2048) return MOE_ERR_UNSUPPORTED;
     if (s->inter < 128 || (s->shared_inter && s->shared_inter < 128)) return MOE_ERR_UNSUPPORTED;
-    // a grouped-GEMM workgroup stages every scale and bias of its rows in LDS (at most 32 groups)
-    if (s->hidden > 2048 || s->inter > 2048 || s->shared_inter > 2048) return MOE_ERR_UNSUPPORTED;
     if (decode_chunk(s, T, grid, xt) == 0) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }

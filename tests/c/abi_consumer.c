@@ -19,7 +19,10 @@ int main(void) {
     const moe_shape bad = {2048, 256, 8, 512, 512, 5, 64};
 
     CHECK(moe_layer_path(&s, 1, 0) == MOE_PATH_DECODE, "T=1 takes the decode path");
-    CHECK(moe_layer_path(&s, 8, 0) == MOE_PATH_DECODE, "T=8 takes the decode path");
+    CHECK(moe_layer_path(&s, MOE_DEFAULT_CROSSOVER, 0) == MOE_PATH_DECODE &&
+              moe_layer_path(&s, MOE_DEFAULT_CROSSOVER + 1, 0) == MOE_PATH_BATCHED,
+          "the default crossover splits the two paths");
+    CHECK(moe_layer_path(&s, 8, 8) == MOE_PATH_DECODE, "a crossover of 8 sends T=8 to the decode path");
     CHECK(moe_layer_path(&s, 9, 0) == MOE_PATH_BATCHED, "T=9 takes the batched path");
     CHECK(moe_layer_path(&s, 4, 2) == MOE_PATH_BATCHED, "a crossover of 2 sends T=4 to the batched path");
     CHECK(moe_layer_path(&s, 0, 0) == -1 && moe_layer_path(&bad, 1, 0) == -1, "invalid T or shape: -1");

@@ -45,7 +45,8 @@ def run_direct(shape, layer, x, T, dev, path):
     return y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy()
 
 
-@pytest.mark.parametrize("T,crossover", [(1, 0), (7, 0), (8, 0), (9, 0), (23, 0), (5, 4), (4, 4)])
+@pytest.mark.parametrize("T,crossover", [(1, 0), (2, 0), (3, 0), (8, 0), (9, 0), (23, 0), (5, 4), (4, 4),
+                                         (8, 8)])
 def test_forward_is_the_chosen_path(T, crossover):
     """moe_layer_forward returns exactly (bit for bit) what the path moe_layer_path names returns,
     and that is within the layer tolerance of the fp64 oracle."""
