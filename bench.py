@@ -30,11 +30,16 @@ HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
 FP16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, published
 
 
+# The sources the decode kernel is compiled from (its device code and the launch-plan header):
+# counter figures taken on the decode kernel stay valid while these are unchanged.
+DECODE_SOURCES = ("decode.hip", "moe_device.hpp", "moe_internal.hpp")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "quantized_moe_decode_router_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode() + f.read())
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "quantized_moe_decode_router_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 

@@ -1,13 +1,14 @@
 // batched.hip -- one MoE layer for a batch of T tokens (prefill / batched decode) on gfx950.
 //
-// Seven launches on one stream, no host synchronisation:
+// Six launches on one stream (seven when step 3 takes two), no host synchronisation:
 //   1. router_gemm   logits[T][E] (+ shared-gate logit) = x . R^T on v_mfma_f32_16x16x32_bf16, the
 //                    fp32 router split into bf16 hi + lo halves on its way into LDS (x is bf16,
 //                    exact)
 //   2. topk_kernel   per token one wave: top-k by (logit desc, index asc), renormalised weights
 //                    (softmax of the kept logits), gamma = sigmoid(gate logit); beside it another
 //                    wave: x as scaled fp16
-//   3. bucket_count  per block of 64 tokens: per-expert counts and every pair's rank in its block
+//   3. bucket_small  (T <= 1024, E <= 512) the two steps below in one workgroup, counts in LDS
+//      bucket_count  per block of 64 tokens: per-expert counts and every pair's rank in its block
 //      bucket_plan   one workgroup: exclusive scans, stable scatter (pairs of one expert stay in
 //                    pair order), the inverse map, the list of 128-row tiles of every group
 //                    (routed experts, then the shared expert as group E with one row per token)
@@ -656,7 +657,7 @@ __device__ void act16_to_pairs8(const uint4 r, int sh, half2_t *out) {
 //
 // The k-loop is compiled once per count MT of 16-row subtiles that hold rows of the tile, so that
 // a k-step has no branches inside and the MFMAs of one k-step interleave with the dequantisation of
-// the next. Block b runs work item b of a list ordered longest first (see bucket_kernel).
+// the next. Block b runs work item b of a list ordered longest first (see plan_groups).
 __device__ __forceinline__ int list_item(int n) { return (int)blockIdx.x < n ? (int)blockIdx.x : -1; }
 __device__ __forceinline__ int chunk_pos(int row, int c) { return c ^ (row & 7); }
 
