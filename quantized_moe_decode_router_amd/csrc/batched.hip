@@ -904,7 +904,9 @@ __device__ __forceinline__ void static_for(F &&f) {
 // issue_a(kb): the A DMAs of k-step kb (NA per wave); mfma(stage, bq): the MFMAs of one k-step on
 // A stage `stage`; dq(kb, buf, j): the fragments of k-step kb from B buffer `buf`, j = kb % SB as an
 // integral constant.
-template <int BITS, bool DN, int NA, typename IssueA, typename IssueB, typename Mfma, typename Dq>
+// BAR = false: every wave reads only LDS it filled itself (its own copy of the A rows), so its own
+// vmcnt waits suffice and the k-steps need no workgroup barrier.
+template <int BITS, bool DN, int NA, bool BAR, typename IssueA, typename IssueB, typename Mfma, typename Dq>
 __device__ __forceinline__ void kloop(int nk, IssueA issue_a, IssueB issue_b, Mfma mfma, Dq dq) {
     using C = GCfg<BITS, DN>;
     constexpr int L = C::L, SB = C::SB, NBC = C::NBC;
@@ -921,7 +923,8 @@ __device__ __forceinline__ void kloop(int nk, IssueA issue_a, IssueB issue_b, Mf
             constexpr int j = decltype(jc)::value;
             const int kb = kb0 + j;
             wait_step<L, SB, NA, NBC, j>();
-            lds_barrier();
+            if constexpr (BAR) lds_barrier();
+            else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own LDS reads done before the DMAs reuse a stage
             issue_a(kb + L);
             if constexpr ((j + 1 + L) % SB == 0) issue_b((kb + 1 + L) / SB);
             mfma(kb % C::RA, bq);
@@ -937,19 +940,24 @@ __device__ __forceinline__ void kloop(int nk, IssueA issue_a, IssueB issue_b, Mf
 template <int BITS, int MT>
 __device__ __forceinline__ void gu_body(const BatchedParams &p, char *lds, int g, int P0, int M, int j0, int tile) {
     using C = GCfg<BITS, false>;
-    constexpr int NA = (MT + 3) / 4;  // A DMAs per wave and k-step: 8 NA waves x 8 rows >= 16 MT
+    // one 16-row subtile: every wave stages its own copy of the 16 A rows (2 DMAs per k-step, RA
+    // stages of 2 KiB per wave fill the shared A region exactly) and the k-loop runs barrier-free
+    constexpr bool PRIV = MT == 1;
+    constexpr int NA = PRIV ? 2 : (MT + 3) / 4;  // A DMAs per wave and k-step: 8 NA waves x 8 rows >= 16 MT
     const GroupW W = group_w13(p, g);
     const int tid = threadIdx.x, lane = tid % kWave, wave = (int)uniform(tid / kWave), fi = lane % 16, fj = lane / 16;
     const int H = p.H, K = p.K, nk = H / 64, ng = nk;
     uint4(*As)[kBM][8] = reinterpret_cast<uint4(*)[kBM][8]>(lds);
+    uint4(*Ap)[16][8] = reinterpret_cast<uint4(*)[16][8]>(lds + wave * C::RA * 16 * 128);  // PRIV
+    static_assert(kGW * C::RA * 16 * 128 <= C::RA * C::A_STAGE, "private A stages");
     char *bbuf = lds + C::b_off() + wave * C::NBUF * C::B_BLOCK;
     char *sq = lds + C::s_off() + wave * 4 * 32 * ng;
-    // A DMA lanes: DMA u of wave w covers tile rows 8 d .. 8 d + 7, d = w + 8 u; lane l -> row
-    // 8 d + l / 8, LDS slot l % 8 = chunk (l % 8) ^ (row & 7). Rows past M read row 0's token.
+    // A DMA lanes: DMA u of wave w covers tile rows 8 d .. 8 d + 7, d = w + 8 u (PRIV: d = u); lane
+    // l -> row 8 d + l / 8, LDS slot l % 8 = chunk (l % 8) ^ (row & 7). Rows past M read row 0's token.
     uint32_t aoff[NA];
 #pragma unroll
     for (int u = 0; u < NA; ++u) {
-        const int d = wave + kGW * u, r = 8 * d + lane / 8, c = (lane % 8) ^ (r & 7);
+        const int d = PRIV ? u : wave + kGW * u, r = 8 * d + lane / 8, c = (lane % 8) ^ (r & 7);
         const int tok = gp(p.perm)[P0 + (r < M ? r : 0)] / K;
         aoff[u] = (uint32_t)(((size_t)tok * H + c * 8) * 2);
     }
@@ -961,7 +969,9 @@ __device__ __forceinline__ void gu_body(const BatchedParams &p, char *lds, int g
     auto issue_a = [&](int kb) __attribute__((always_inline)) {
         const _Float16 *base = p.x16 + (size_t)min(kb, nk - 1) * 64;
 #pragma unroll
-        for (int u = 0; u < NA; ++u) dma16s(aoff[u], base, lds_addr(&As[kb % C::RA][8 * (wave + kGW * u)][0]));
+        for (int u = 0; u < NA; ++u)
+            dma16s(aoff[u], base,
+                   lds_addr(PRIV ? &Ap[kb % C::RA][8 * u][0] : &As[kb % C::RA][8 * (wave + kGW * u)][0]));
     };
     auto issue_b = [&](int b) __attribute__((always_inline)) {
         wdma_block<BITS, false>(wd, W, min(b, nblk - 1), bbuf + (b % C::NBUF) * C::B_BLOCK);
@@ -976,7 +986,8 @@ __device__ __forceinline__ void gu_body(const BatchedParams &p, char *lds, int g
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
                 const int ra = 16 * i + fi;
-                const half8_t a = __builtin_bit_cast(half8_t, As[stage][ra][chunk_pos(ra, 2 * fj + q)]);
+                const uint4 av = PRIV ? Ap[stage][ra][chunk_pos(ra, 2 * fj + q)] : As[stage][ra][chunk_pos(ra, 2 * fj + q)];
+                const half8_t a = __builtin_bit_cast(half8_t, av);
                 ag[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bg, ag[i], 0, 0, 0);
                 au[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bu, au[i], 0, 0, 0);
             }
@@ -988,7 +999,7 @@ __device__ __forceinline__ void gu_body(const BatchedParams &p, char *lds, int g
         if constexpr (J == 0) sb = load_sblk<C::SB>(sq, ng, min(kb, nk - C::SB), fi);
         return dequant_step<BITS, false, J>(bbuf + buf * C::B_BLOCK, sb, 1.0f, fi, fj);
     };
-    kloop<BITS, false, NA>(nk, issue_a, issue_b, mfma, dq);
+    kloop<BITS, false, NA, !PRIV>(nk, issue_a, issue_b, mfma, dq);
     // epilogue: lane l, register r of subtile i -> row 16 i + 4 (l / 16) + r, j = j0 + 16 w + l % 16.
     // The accumulators are scaled back by the token's 2^xe, SwiGLU applied, and h stored as fp16
     // hi + lo halves of h * 2^-e, e = max(0, E - 15) for the largest |h| of the tile in this
@@ -1067,19 +1078,22 @@ __global__ void __launch_bounds__(kGT, 1) gu_gemm(BatchedParams p) {
 template <int BITS, int MT>
 __device__ __forceinline__ void dn_body(const BatchedParams &p, char *lds, int g, int P0, int M, int n0, int tile) {
     using C = GCfg<BITS, true>;
-    constexpr int NA = (MT + 3) / 4;
+    constexpr bool PRIV = MT == 1;  // as in gate|up: private A rows (hi and lo), barrier-free k-loop
+    constexpr int NA = PRIV ? 2 : (MT + 3) / 4;
     const GroupW W = group_w2(p, g);
     const int tid = threadIdx.x, lane = tid % kWave, wave = (int)uniform(tid / kWave), fi = lane % 16, fj = lane / 16;
     const int H = p.H, Imax = p.Imax, nk = W.inter / 64, ng = nk;
     // A stage s: hi tile at s * A_STAGE, lo tile 16 KiB after it
     uint4(*Ah)[kBM][8] = reinterpret_cast<uint4(*)[kBM][8]>(lds);
+    uint4(*Ahp)[2][16][8] = reinterpret_cast<uint4(*)[2][16][8]>(lds + wave * C::RA * 2 * 16 * 128);  // PRIV
+    static_assert(kGW * C::RA * 2 * 16 * 128 <= C::RA * C::A_STAGE, "private A stages");
     char *bbuf = lds + C::b_off() + wave * C::NBUF * C::B_BLOCK;
     char *sq = lds + C::s_off() + wave * 4 * 32 * ng;
     const int hexp0 = (int)((size_t)tile * (Imax / 64));
     uint32_t aoff[NA];
 #pragma unroll
     for (int u = 0; u < NA; ++u) {
-        const int d = wave + kGW * u, r = 8 * d + lane / 8, c = (lane % 8) ^ (r & 7);
+        const int d = PRIV ? u : wave + kGW * u, r = 8 * d + lane / 8, c = (lane % 8) ^ (r & 7);
         aoff[u] = (uint32_t)(((size_t)(P0 + (r < M ? r : 0)) * Imax + c * 8) * 2);
     }
     // the tile's h exponents of every group, in registers of lanes 0..ng-1 (read with readlane)
@@ -1093,9 +1107,9 @@ __device__ __forceinline__ void dn_body(const BatchedParams &p, char *lds, int g
         const size_t o = (size_t)min(kb, nk - 1) * 64;
 #pragma unroll
         for (int u = 0; u < NA; ++u) {
-            const int st = kb % C::RA, row = 8 * (wave + kGW * u);
-            dma16s(aoff[u], p.hh + o, lds_addr(&Ah[2 * st][row][0]));
-            dma16s(aoff[u], p.hl + o, lds_addr(&Ah[2 * st + 1][row][0]));
+            const int st = kb % C::RA, row = 8 * (PRIV ? u : wave + kGW * u);
+            dma16s(aoff[u], p.hh + o, lds_addr(PRIV ? &Ahp[st][0][row][0] : &Ah[2 * st][row][0]));
+            dma16s(aoff[u], p.hl + o, lds_addr(PRIV ? &Ahp[st][1][row][0] : &Ah[2 * st + 1][row][0]));
         }
     };
     auto issue_b = [&](int b) __attribute__((always_inline)) {
@@ -1105,8 +1119,8 @@ __device__ __forceinline__ void dn_body(const BatchedParams &p, char *lds, int g
 #pragma unroll
     for (int i = 0; i < MT; ++i) a0[i] = a1[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     auto mfma = [&](int stage, const BQ &bq) __attribute__((always_inline)) {
-        const uint4(*Hh)[8] = Ah[2 * stage];
-        const uint4(*Hl)[8] = Ah[2 * stage + 1];
+        const uint4(*Hh)[8] = PRIV ? Ahp[stage][0] : Ah[2 * stage];
+        const uint4(*Hl)[8] = PRIV ? Ahp[stage][1] : Ah[2 * stage + 1];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const half8_t b0 = q ? bq.r0q1 : bq.r0q0, b1 = q ? bq.r1q1 : bq.r1q0;
@@ -1134,7 +1148,7 @@ __device__ __forceinline__ void dn_body(const BatchedParams &p, char *lds, int g
         if constexpr (J == 0) sb = load_sblk<C::SB>(sq, ng, min(kb, nk - C::SB), fi);
         return dequant_step<BITS, true, J>(bbuf + buf * C::B_BLOCK, sb, f, fi, fj);
     };
-    kloop<BITS, true, 2 * NA>(nk, issue_a, issue_b, mfma, dq);
+    kloop<BITS, true, 2 * NA, !PRIV>(nk, issue_a, issue_b, mfma, dq);
     // epilogue: lane l, register r of subtile i, block nb -> row 16 i + 4 (l / 16) + r, output row
     // n0 + 32 w + 16 nb + l % 16; scaled by the routing weight (gamma for the shared group)
     bool finite = true;
