@@ -743,23 +743,29 @@ __device__ __forceinline__ half2_t f16_splat(uint16_t bf, float f) {
 //         block two (or three) ahead is issued into it
 //   RA    A stages (L + 1)
 //   NBC   DMAs per B block and wave (32 rows x BB bytes)
-template <int BITS, bool DN>
+//   LO    a lookahead other than the default L0 for some items (their k-loop only: the LDS layout,
+//         i.e. the A region, the per-wave B ring stride and the scale quarters, is the default's)
+template <int BITS, bool DN, int LO = 0>
 struct GCfg {
     static constexpr int BB = DN ? 64 : 128;
     static constexpr int SB = BB / (8 * BITS);
-    static constexpr int L = DN ? (BITS == 4 ? 2 : 1) : (BITS == 4 ? 3 : 2);
+    static constexpr int L0 = DN ? (BITS == 4 ? 2 : 1) : (BITS == 4 ? 3 : 2);
+    static constexpr int L = LO ? LO : L0;
+    static constexpr int NBUF0 = (L0 + SB - 1) / SB + 1;
     static constexpr int NBUF = (L + SB - 1) / SB + 1;
+    static constexpr int RA0 = L0 + 1;
     static constexpr int RA = L + 1;
     static constexpr int NBC = 32 * BB / 1024;
     static constexpr int A_STAGE = (DN ? 2 : 1) * kBM * 128;  // A bytes per stage (h: hi and lo)
     static constexpr int B_BLOCK = 32 * BB;                    // B bytes per block and wave
+    static_assert(NBUF <= NBUF0, "a B ring within the default's");
     // LDS bytes for ng groups per weight row: A stages, B buffers, then each wave's scale and bias
     // quarters (16 rows x ng groups x 2 bytes each)
     __host__ __device__ static constexpr int lds_bytes(int ng) {
-        return RA * A_STAGE + kGW * NBUF * B_BLOCK + kGW * 4 * 32 * ng;
+        return RA0 * A_STAGE + kGW * NBUF0 * B_BLOCK + kGW * 4 * 32 * ng;
     }
-    __host__ __device__ static constexpr int b_off() { return RA * A_STAGE; }
-    __host__ __device__ static constexpr int s_off() { return RA * A_STAGE + kGW * NBUF * B_BLOCK; }
+    __host__ __device__ static constexpr int b_off() { return RA0 * A_STAGE; }
+    __host__ __device__ static constexpr int s_off() { return RA0 * A_STAGE + kGW * NBUF0 * B_BLOCK; }
 };
 
 // Outstanding DMAs allowed at the top of k-step kb (kb % SB = j): those of the batches issued at
@@ -906,9 +912,8 @@ __device__ __forceinline__ void static_for(F &&f) {
 // integral constant.
 // BAR = false: every wave reads only LDS it filled itself (its own copy of the A rows), so its own
 // vmcnt waits suffice and the k-steps need no workgroup barrier.
-template <int BITS, bool DN, int NA, bool BAR, typename IssueA, typename IssueB, typename Mfma, typename Dq>
+template <typename C, int NA, bool BAR, typename IssueA, typename IssueB, typename Mfma, typename Dq>
 __device__ __forceinline__ void kloop(int nk, IssueA issue_a, IssueB issue_b, Mfma mfma, Dq dq) {
-    using C = GCfg<BITS, DN>;
     constexpr int L = C::L, SB = C::SB, NBC = C::NBC;
     // the batches of k-steps -1 - L .. -1 (A only from A(0) on)
 #pragma unroll
@@ -934,23 +939,36 @@ __device__ __forceinline__ void kloop(int nk, IssueA issue_a, IssueB issue_b, Mf
     vm_wait<0>();  // no DMA may still write this workgroup's LDS once it leaves
 }
 
+// Items of at most kPrivMT subtiles whose private A stages fit the shared A region take private A
+// rows and a barrier-free k-loop, with the lookahead priv_lookahead.
+constexpr int kPrivMT = 1;
+template <int BITS, bool DN>
+constexpr int priv_lookahead(int mt) {
+    return GCfg<BITS, DN>::L0;
+}
+template <int BITS, bool DN>
+constexpr bool priv_items(int mt) {
+    using C = GCfg<BITS, DN>;
+    return mt <= kPrivMT && kGW * (priv_lookahead<BITS, DN>(mt) + 1) * (DN ? 2 : 1) * mt * 16 * 128 <= C::RA0 * C::A_STAGE;
+}
+
 // gate|up + SwiGLU. Item: rows P0 .. P0+M-1 of group g against gate rows j0 .. j0+127 and up rows
 // inter + j0 .. +127. Wave w: gate rows j0 + 16 w + (0..15) (its first row block) and the up rows
 // of the same j (its second), so a lane's accumulators hold gate and up of the same (row, j).
 template <int BITS, int MT>
 __device__ __forceinline__ void gu_body(const BatchedParams &p, char *lds, int g, int P0, int M, int j0, int tile) {
-    using C = GCfg<BITS, false>;
-    // one 16-row subtile: every wave stages its own copy of the 16 A rows (2 DMAs per k-step, RA
-    // stages of 2 KiB per wave fill the shared A region exactly) and the k-loop runs barrier-free
-    constexpr bool PRIV = MT == 1;
-    constexpr int NA = PRIV ? 2 : (MT + 3) / 4;  // A DMAs per wave and k-step: 8 NA waves x 8 rows >= 16 MT
+    // few subtiles: every wave stages its own copy of the A rows (MT 16-row blocks per k-step, RA
+    // stages per wave within the shared A region) and the k-loop runs barrier-free
+    constexpr bool PRIV = priv_items<BITS, false>(MT);
+    using C = GCfg<BITS, false, PRIV ? priv_lookahead<BITS, false>(MT) : 0>;
+    constexpr int NA = PRIV ? 2 * MT : (MT + 3) / 4;  // A DMAs per wave and k-step: 8 NA waves x 8 rows >= 16 MT
     const GroupW W = group_w13(p, g);
     const int tid = threadIdx.x, lane = tid % kWave, wave = (int)uniform(tid / kWave), fi = lane % 16, fj = lane / 16;
     const int H = p.H, K = p.K, nk = H / 64, ng = nk;
     uint4(*As)[kBM][8] = reinterpret_cast<uint4(*)[kBM][8]>(lds);
-    uint4(*Ap)[16][8] = reinterpret_cast<uint4(*)[16][8]>(lds + wave * C::RA * 16 * 128);  // PRIV
-    static_assert(kGW * C::RA * 16 * 128 <= C::RA * C::A_STAGE, "private A stages");
-    char *bbuf = lds + C::b_off() + wave * C::NBUF * C::B_BLOCK;
+    uint4(*Ap)[16 * MT][8] = reinterpret_cast<uint4(*)[16 * MT][8]>(lds + wave * C::RA * MT * 16 * 128);  // PRIV
+    static_assert(!PRIV || kGW * C::RA * MT * 16 * 128 <= C::RA0 * C::A_STAGE, "private A stages");
+    char *bbuf = lds + C::b_off() + wave * C::NBUF0 * C::B_BLOCK;
     char *sq = lds + C::s_off() + wave * 4 * 32 * ng;
     // A DMA lanes: DMA u of wave w covers tile rows 8 d .. 8 d + 7, d = w + 8 u (PRIV: d = u); lane
     // l -> row 8 d + l / 8, LDS slot l % 8 = chunk (l % 8) ^ (row & 7). Rows past M read row 0's token.
@@ -999,7 +1017,7 @@ __device__ __forceinline__ void gu_body(const BatchedParams &p, char *lds, int g
         if constexpr (J == 0) sb = load_sblk<C::SB>(sq, ng, min(kb, nk - C::SB), fi);
         return dequant_step<BITS, false, J>(bbuf + buf * C::B_BLOCK, sb, 1.0f, fi, fj);
     };
-    kloop<BITS, false, NA, !PRIV>(nk, issue_a, issue_b, mfma, dq);
+    kloop<C, NA, !PRIV>(nk, issue_a, issue_b, mfma, dq);
     // epilogue: lane l, register r of subtile i -> row 16 i + 4 (l / 16) + r, j = j0 + 16 w + l % 16.
     // The accumulators are scaled back by the token's 2^xe, SwiGLU applied, and h stored as fp16
     // hi + lo halves of h * 2^-e, e = max(0, E - 15) for the largest |h| of the tile in this
@@ -1077,17 +1095,17 @@ __global__ void __launch_bounds__(kGT, 1) gu_gemm(BatchedParams p) {
 // h halves of this tile in this group, so that every product is the unscaled one.
 template <int BITS, int MT>
 __device__ __forceinline__ void dn_body(const BatchedParams &p, char *lds, int g, int P0, int M, int n0, int tile) {
-    using C = GCfg<BITS, true>;
-    constexpr bool PRIV = MT == 1;  // as in gate|up: private A rows (hi and lo), barrier-free k-loop
-    constexpr int NA = PRIV ? 2 : (MT + 3) / 4;
+    constexpr bool PRIV = priv_items<BITS, true>(MT);  // as in gate|up: private A rows (hi and lo), barrier-free k-loop
+    using C = GCfg<BITS, true, PRIV ? priv_lookahead<BITS, true>(MT) : 0>;
+    constexpr int NA = PRIV ? 2 * MT : (MT + 3) / 4;
     const GroupW W = group_w2(p, g);
     const int tid = threadIdx.x, lane = tid % kWave, wave = (int)uniform(tid / kWave), fi = lane % 16, fj = lane / 16;
     const int H = p.H, Imax = p.Imax, nk = W.inter / 64, ng = nk;
     // A stage s: hi tile at s * A_STAGE, lo tile 16 KiB after it
     uint4(*Ah)[kBM][8] = reinterpret_cast<uint4(*)[kBM][8]>(lds);
-    uint4(*Ahp)[2][16][8] = reinterpret_cast<uint4(*)[2][16][8]>(lds + wave * C::RA * 2 * 16 * 128);  // PRIV
-    static_assert(kGW * C::RA * 2 * 16 * 128 <= C::RA * C::A_STAGE, "private A stages");
-    char *bbuf = lds + C::b_off() + wave * C::NBUF * C::B_BLOCK;
+    uint4(*Ahp)[2][16 * MT][8] = reinterpret_cast<uint4(*)[2][16 * MT][8]>(lds + wave * C::RA * 2 * MT * 16 * 128);  // PRIV
+    static_assert(!PRIV || kGW * C::RA * 2 * MT * 16 * 128 <= C::RA0 * C::A_STAGE, "private A stages");
+    char *bbuf = lds + C::b_off() + wave * C::NBUF0 * C::B_BLOCK;
     char *sq = lds + C::s_off() + wave * 4 * 32 * ng;
     const int hexp0 = (int)((size_t)tile * (Imax / 64));
     uint32_t aoff[NA];
@@ -1148,7 +1166,7 @@ __device__ __forceinline__ void dn_body(const BatchedParams &p, char *lds, int g
         if constexpr (J == 0) sb = load_sblk<C::SB>(sq, ng, min(kb, nk - C::SB), fi);
         return dequant_step<BITS, true, J>(bbuf + buf * C::B_BLOCK, sb, f, fi, fj);
     };
-    kloop<BITS, true, 2 * NA, !PRIV>(nk, issue_a, issue_b, mfma, dq);
+    kloop<C, 2 * NA, !PRIV>(nk, issue_a, issue_b, mfma, dq);
     // epilogue: lane l, register r of subtile i, block nb -> row 16 i + 4 (l / 16) + r, output row
     // n0 + 32 w + 16 nb + l % 16; scaled by the routing weight (gamma for the shared group)
     bool finite = true;
