@@ -282,43 +282,11 @@ __global__ void __launch_bounds__(kCountWaves * kWave) bucket_count(BatchedParam
     for (int e = lane; e < E; e += kWave) p.blkcnt[(size_t)blk * E + e] = __popcll(masks[e]);
 }
 
-// Inclusive sums over the workgroup of four per-thread values (v[0..3]); returns the exclusive
-// prefix of this thread and the totals (every thread). 16 waves: wave scans, then wave totals.
-__device__ __forceinline__ void block_scan4(int v[4], int excl[4], int total[4], int (*wsum)[4]) {
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    int inc[4] = {v[0], v[1], v[2], v[3]};
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int a = __shfl_up(inc[i], o, kWave);
-            if (lane >= o) inc[i] += a;
-        }
-    }
-    if (lane == kWave - 1)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wsum[wave][i] = inc[i];
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int before = 0, all = 0;
-        for (int w = 0; w < kPlanWaves; ++w) {
-            const int s = wsum[w][i];
-            before += w < wave ? s : 0;
-            all += s;
-        }
-        excl[i] = before + inc[i] - v[i];
-        total[i] = all;
-    }
-    __syncthreads();
-}
-
 // From the group sizes gcnt[0..E) (per-block prefixes already in place): the shared group's size,
 // the scans of the group sizes, tile counts and work items (goff, gtoff, the totals in p.ntiles),
 // p.gcnt / p.goff, the tile list and, when p.wgu is set, both GEMMs' work lists, longest first.
 // Called by the whole workgroup of kPlanThreads; the arrays live in the caller's LDS.
-__device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *gtoff, int (*wsum)[4], int *hgu,
-                            int *hdn) {
+__device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *gtoff, int *hgu, int *hdn) {
     const int tid = threadIdx.x;
     const int T = p.T, E = p.E;
     const int ng = E + (p.Is ? 1 : 0);  // groups: experts, then the shared expert
@@ -327,40 +295,41 @@ __device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *g
     // exclusive scans of the group sizes, their tile counts and their gate|up and down work items
     const int ndn = p.H / kDnCols;
     auto ngu_of = [&](int g) { return (g < E ? p.I : p.Is) / kGuCols; };
-    {
-        // thread tid: groups 2 tid and 2 tid + 1 (up to 2048 groups)
-        int v[4] = {0, 0, 0, 0}, first[2] = {0, 0}, tiles0 = 0;
+    if (tid < kWave) {
+        // one wave: lane l sums the run of groups [l G, l G + G), G = ceil(ng / 64), in order; a wave
+        // scan of the runs' totals; then the run's exclusive offsets, group by group
+        const int G = (ng + kWave - 1) / kWave, g0 = tid * G, g1 = min(g0 + G, ng);
+        int v[4] = {0, 0, 0, 0};
+        for (int g = g0; g < g1; ++g) {
+            const int nt = (gcnt[g] + kBM - 1) / kBM;
+            v[0] += gcnt[g];
+            v[1] += nt;
+            v[2] += nt * ngu_of(g);
+            v[3] += nt * ndn;
+        }
+        int inc[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int g = 2 * tid + h;
-            if (g < ng) {
-                const int nt = (gcnt[g] + kBM - 1) / kBM;
-                if (h == 0) {
-                    first[0] = gcnt[g];
-                    tiles0 = nt;
-                }
-                v[0] += gcnt[g];
-                v[1] += nt;
-                v[2] += nt * ngu_of(g);
-                v[3] += nt * ndn;
+        for (int o = 1; o < kWave; o <<= 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int x = __shfl_up(inc[i], o, kWave);
+                if (tid >= o) inc[i] += x;
             }
         }
-        int ex[4], tot[4];
-        block_scan4(v, ex, tot, wsum);
-        if (2 * tid < ng) {
-            goff[2 * tid] = ex[0];
-            gtoff[2 * tid] = ex[1];
+        int e0 = inc[0] - v[0], e1 = inc[1] - v[1];
+        for (int g = g0; g < g1; ++g) {
+            const int c = gcnt[g];
+            goff[g] = e0;
+            gtoff[g] = e1;
+            e0 += c;
+            e1 += (c + kBM - 1) / kBM;
         }
-        if (2 * tid + 1 < ng) {
-            goff[2 * tid + 1] = ex[0] + first[0];
-            gtoff[2 * tid + 1] = ex[1] + tiles0;
-        }
-        if (tid == 0) {
-            goff[ng] = tot[0];
-            gtoff[ng] = tot[1];
-            p.ntiles[0] = tot[1];
-            p.ntiles[1] = tot[2];
-            p.ntiles[2] = tot[3];
+        if (tid == kWave - 1) {
+            goff[ng] = inc[0];
+            gtoff[ng] = inc[1];
+            p.ntiles[0] = inc[1];
+            p.ntiles[1] = inc[2];
+            p.ntiles[2] = inc[3];
         }
     }
     __syncthreads();
@@ -390,8 +359,9 @@ __device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *g
             }
             return lo;
         };
+        const int gfirst = tid < ntile ? tile_group(tid) : 0;  // this thread's first tile, used twice
         for (int i = tid; i < ntile; i += kPlanThreads) {
-            const int g = tile_group(i), m0 = (i - gtoff[g]) * kBM, rows = min(kBM, gcnt[g] - m0);
+            const int g = i == tid ? gfirst : tile_group(i), m0 = (i - gtoff[g]) * kBM, rows = min(kBM, gcnt[g] - m0);
             atomicAdd(&hgu[rows], ngu_of(g));
             atomicAdd(&hdn[rows], ndn);
         }
@@ -419,7 +389,8 @@ __device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *g
         }
         __syncthreads();
         for (int i = tid; i < ntile; i += kPlanThreads) {
-            const int g = tile_group(i), mi = i - gtoff[g], m0 = mi * kBM, rows = min(kBM, gcnt[g] - m0);
+            const int g = i == tid ? gfirst : tile_group(i), mi = i - gtoff[g], m0 = mi * kBM,
+                      rows = min(kBM, gcnt[g] - m0);
             const int nu = ngu_of(g);
             const int bu = atomicAdd(&hgu[rows], nu), bd = atomicAdd(&hdn[rows], ndn);
             for (int c = 0; c < nu; ++c)
@@ -432,7 +403,6 @@ __device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *g
 
 __global__ void __launch_bounds__(kPlanThreads) bucket_plan(BatchedParams p) {
     __shared__ int gcnt[kMaxGroups], goff[kMaxGroups + 1], gtoff[kMaxGroups + 1];
-    __shared__ int wsum[kPlanWaves][4];
     __shared__ int hgu[kBM + 1], hdn[kBM + 1];
     const int tid = threadIdx.x;
     const int T = p.T, K = p.K, E = p.E;
@@ -454,7 +424,7 @@ __global__ void __launch_bounds__(kPlanThreads) bucket_plan(BatchedParams p) {
         }
         gcnt[e] = run;
     }
-    plan_groups(p, gcnt, goff, gtoff, wsum, hgu, hdn);
+    plan_groups(p, gcnt, goff, gtoff, hgu, hdn);
     // scatter: four pairs per thread in flight at once
     const int TK = T * K;
     for (int q0 = tid; q0 < TK; q0 += 4 * kPlanThreads) {
@@ -494,7 +464,6 @@ __host__ __device__ inline size_t bucket_small_lds_bytes(int E) { return 12 * (s
 __global__ void __launch_bounds__(kPlanThreads) bucket_small(BatchedParams p) {
     extern __shared__ __align__(16) char smem[];
     __shared__ int gcnt[kMaxGroups], goff[kMaxGroups + 1], gtoff[kMaxGroups + 1];
-    __shared__ int wsum[kPlanWaves][4];
     __shared__ int hgu[kBM + 1], hdn[kBM + 1];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int T = p.T, K = p.K, E = p.E;
@@ -504,13 +473,14 @@ __global__ void __launch_bounds__(kPlanThreads) bucket_small(BatchedParams p) {
     const unsigned long long below = (1ull << lane) - 1ull;
     const int t = wave * kWave + lane;
     const bool valid = wave < nblk && t < T;
+    int ex[16], rk[16];
+    // the selections are loaded first, so that their latency covers the mask clearing
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ex[k] = k < K && valid ? min((unsigned)p.idx[(size_t)t * K + k], (unsigned)(E - 1)) : -1;
     for (int e = lane; e < E; e += kWave) masks[e] = 0ull;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    int ex[16], rk[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) ex[k] = k < K && valid ? min((unsigned)p.idx[(size_t)t * K + k], (unsigned)(E - 1)) : -1;
 #pragma unroll
     for (int k = 0; k < 16; ++k)
         if (ex[k] >= 0) atomicOr(&masks[ex[k]], 1ull << lane);
@@ -532,7 +502,7 @@ __global__ void __launch_bounds__(kPlanThreads) bucket_small(BatchedParams p) {
         }
         gcnt[e] = run;
     }
-    plan_groups(p, gcnt, goff, gtoff, wsum, hgu, hdn);
+    plan_groups(p, gcnt, goff, gtoff, hgu, hdn);
     // scatter by the lane that ranked the pair: expert offset + block prefix + rank
 #pragma unroll
     for (int k = 0; k < 16; ++k)
