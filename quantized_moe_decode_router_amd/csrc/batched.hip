@@ -1183,14 +1183,24 @@ __global__ void __launch_bounds__(256) combine_kernel(BatchedParams p) {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (long long)T * nq) return;
     const int t = (int)(i / nq), c = (int)(i - (long long)t * nq) * 4;
+    // every position, then every row, in flight at once (K <= 16); the sum keeps the order k = 0..K-1,
+    // then the shared row
+    int pk[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) pk[k] = k < K ? p.pos[(size_t)t * K + k] : 0;
+    float4 v[17];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        v[k] = k < K ? *reinterpret_cast<const float4 *>(p.out + (size_t)pk[k] * H + c) : make_float4(0, 0, 0, 0);
+    v[16] = p.Is ? *reinterpret_cast<const float4 *>(p.out + ((size_t)T * K + t) * H + c) : make_float4(0, 0, 0, 0);
     float4 acc = make_float4(0, 0, 0, 0);
-    for (int k = 0; k < K; ++k) {
-        const float4 v = *reinterpret_cast<const float4 *>(p.out + (size_t)p.pos[(size_t)t * K + k] * H + c);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        if (k < K) {
+            acc.x += v[k].x; acc.y += v[k].y; acc.z += v[k].z; acc.w += v[k].w;
+        }
     if (p.Is) {
-        const float4 v = *reinterpret_cast<const float4 *>(p.out + ((size_t)T * K + t) * H + c);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        acc.x += v[16].x; acc.y += v[16].y; acc.z += v[16].z; acc.w += v[16].w;
     }
     *reinterpret_cast<float4 *>(p.y + (size_t)t * H + c) = acc;
 }
