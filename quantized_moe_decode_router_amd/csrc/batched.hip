@@ -60,9 +60,9 @@ constexpr int kRtSteps = 8;  // k-steps per range: H / 64 / router_ksplit(H) <= 
 __host__ __device__ inline int router_ksplit(int H) { return H / 64 < kRouterSplitK ? H / 64 : kRouterSplitK; }
 
 __global__ void __launch_bounds__(kGemmThreads) router_gemm(BatchedParams p) {
-    __shared__ __align__(16) uint16_t xs[kRtT][kLdsK];
-    __shared__ __align__(16) uint16_t rh[kRtN][kLdsK];
-    __shared__ __align__(16) uint16_t rl[kRtN][kLdsK];
+    __shared__ __align__(16) uint16_t xs[2][kRtT][kLdsK];
+    __shared__ __align__(16) uint16_t rh[2][kRtN][kLdsK];
+    __shared__ __align__(16) uint16_t rl[2][kRtN][kLdsK];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int t0 = blockIdx.x * kRtT, n0 = blockIdx.y * kRtN;
     const int H = p.H, E = p.E, T = p.T;
@@ -85,8 +85,8 @@ __global__ void __launch_bounds__(kGemmThreads) router_gemm(BatchedParams p) {
         return st;
     };
     // the fp32 router weights split into bf16 hi = rne(R) and lo = rne(R - hi) on the way into LDS
-    auto store = [&](const St &st) {
-        *reinterpret_cast<uint4 *>(&xs[r][c]) = st.x;
+    auto store = [&](const St &st, int bf) {
+        *reinterpret_cast<uint4 *>(&xs[bf][r][c]) = st.x;
         auto split2 = [](float a, float b, uint32_t &hi, uint32_t &lo) __attribute__((always_inline)) {
             const uint16_t h0 = f32_to_bf16_rne(a), h1 = f32_to_bf16_rne(b);
             hi = h0 | (uint32_t)h1 << 16;
@@ -97,35 +97,37 @@ __global__ void __launch_bounds__(kGemmThreads) router_gemm(BatchedParams p) {
         split2(st.f0.z, st.f0.w, hi.y, lo.y);
         split2(st.f1.x, st.f1.y, hi.z, lo.z);
         split2(st.f1.z, st.f1.w, hi.w, lo.w);
-        *reinterpret_cast<uint4 *>(&rh[r][c]) = hi;
-        *reinterpret_cast<uint4 *>(&rl[r][c]) = lo;
+        *reinterpret_cast<uint4 *>(&rh[bf][r][c]) = hi;
+        *reinterpret_cast<uint4 *>(&rl[bf][r][c]) = lo;
     };
     float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     const int th = wave & 1, nh = wave >> 1;
-    auto mfma_step = [&]() {
+    auto mfma_step = [&](int bf) {
 #pragma unroll
         for (int ks = 0; ks < 64; ks += 32) {
             const int kc = ks + 8 * (lane / 16);
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&xs[16 * th + lane % 16][kc]);
-            const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&rh[16 * nh + lane % 16][kc]);
-            const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(&rl[16 * nh + lane % 16][kc]);
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&xs[bf][16 * th + lane % 16][kc]);
+            const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&rh[bf][16 * nh + lane % 16][kc]);
+            const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(&rl[bf][16 * nh + lane % 16][kc]);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc, 0, 0, 0);
         }
     };
     // this range's k-steps (at most kRtSteps: H <= 2048, H / 4 per range): every load is
-    // issued up front, then each k-step goes through LDS; the barriers are LDS-only, so that the
+    // issued up front, then each k-step goes through one of two LDS buffers (k-step j + 1 is stored
+    // while k-step j's MFMAs run: one barrier per k-step); the barriers are LDS-only, so that the
     // loads of later k-steps stay in flight
     const int nk = H / 64 / router_ksplit(H), k0 = blockIdx.z * nk;
     St S[kRtSteps];
 #pragma unroll
     for (int j = 0; j < kRtSteps; ++j) S[j] = load(k0 + min(j, nk - 1));
+    store(S[0], 0);
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < kRtSteps; ++j) {
         if (j < nk) {  // nk is uniform
-            store(S[j]);
-            lds_barrier();
-            mfma_step();
+            if (j + 1 < nk) store(S[j + 1], (j + 1) & 1);
+            mfma_step(j & 1);
             lds_barrier();
         }
     }
