@@ -208,31 +208,35 @@ __global__ void __launch_bounds__(2 * kTopkTokens * kWave) topk_kernel(BatchedPa
     const int N = E + (p.sgate ? 1 : 0), ks = router_ksplit(p.H);
     const float *part = p.lpart + (size_t)t * N;
     const size_t zs = (size_t)p.T * N;
-    // every partial sum of this lane's logits in flight at once (E <= 1024, ks <= 4)
+    // every partial sum of this lane's logits, their biases and the gate partials in flight at
+    // once (E <= 1024, ks <= 4)
+    float g[kRouterSplitK];
+#pragma unroll
+    for (int z = 0; z < kRouterSplitK; ++z) g[z] = p.sgate && z < ks ? part[z * zs + E] : 0.0f;
     for (int e0 = 0; e0 < E; e0 += 4 * kWave) {
-        float v[4][kRouterSplitK];
+        float v[4][kRouterSplitK], bias[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 4; ++u) {
+            const int e = min(e0 + u * kWave + lane, E - 1);
 #pragma unroll
-            for (int z = 0; z < kRouterSplitK; ++z) {
-                const int e = min(e0 + u * kWave + lane, E - 1);
-                v[u][z] = z < ks ? part[z * zs + e] : 0.0f;
-            }
+            for (int z = 0; z < kRouterSplitK; ++z) v[u][z] = z < ks ? part[z * zs + e] : 0.0f;
+            bias[u] = p.rbias ? p.rbias[e] : 0.0f;
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int e = e0 + u * kWave + lane;
             if (e >= E) break;
             float a = v[u][0];
             for (int z = 1; z < ks; ++z) a += v[u][z];
-            if (p.rbias) a += p.rbias[e];
+            if (p.rbias) a += bias[u];
             lt[e] = a;
             p.logits[(size_t)t * E + e] = a;
         }
     }
     float gate = 0.0f;
     if (p.sgate) {
-        gate = part[E];
-        for (int z = 1; z < ks; ++z) gate += part[z * zs + E];
+        gate = g[0];
+        for (int z = 1; z < ks; ++z) gate += g[z];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
