@@ -1090,9 +1090,23 @@ __device__ __forceinline__ void dn_body(const BatchedParams &p, char *lds, int g
         const int d = PRIV ? u : wave + kGW * u, r = 8 * d + lane / 8, c = (lane % 8) ^ (r & 7);
         aoff[u] = (uint32_t)(((size_t)(P0 + (r < M ? r : 0)) * Imax + c * 8) * 2);
     }
+    // the epilogue's routing weights of this lane's accumulator rows (rows past M repeat row M - 1):
+    // their pair indices load with the h exponents, the weights themselves stay in flight through
+    // the k-loop
+    int qr[MT][4];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) qr[i][r] = gp(p.perm)[P0 + min(16 * i + 4 * fj + r, M - 1)];
     // the tile's h exponents of every group, in registers of lanes 0..ng-1 (read with readlane)
     const int hexp_lane = lane < ng ? gp(p.hexp)[hexp0 + lane] : 0;
     asm volatile("" ::"v"(hexp_lane));  // the load completes here, before the first DMA is issued
+    float wsc[MT][4];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            wsc[i][r] = g < p.E ? gp(p.w)[qr[i][r]] : gp(p.gamma)[qr[i][r] / p.K];
     const WDma<BITS, true> wd =
         wdma_lanes<BITS, true>(W, ng, lane, [&](int r) { return (size_t)(n0 + 32 * wave + r); });
     wdma_scales<BITS, true>(wd, ng, lane, sq);
@@ -1153,8 +1167,7 @@ __device__ __forceinline__ void dn_body(const BatchedParams &p, char *lds, int g
         for (int r = 0; r < 4; ++r) {
             const int m = 16 * i + 4 * fj + r;
             if (m >= M) continue;
-            const int q = gp(p.perm)[P0 + m];
-            const float sc = g < p.E ? gp(p.w)[q] : gp(p.gamma)[q / p.K];
+            const float sc = wsc[i][r];
             finite &= __builtin_isfinite(a0[i][r]) && __builtin_isfinite(a1[i][r]);
             float *o = p.out + (size_t)(P0 + m) * H + n;
             o[0] = sc * a0[i][r];
