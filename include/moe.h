@@ -134,10 +134,11 @@ typedef struct {
 #define MOE_PATH_BATCHED 1
 /* Largest token count moe_layer_forward sends to the decode path when given crossover <= 0.
  * Measured on MI355X for one 35B-shaped 4-bit layer (H 2048, E 256, top-8, I = Is = 512): the
- * single-layer decode call is the faster one up to T = 2 (49 vs 53 us) and the batched one from
- * T = 3 on (56 vs 58 us; T = 8: 85 vs 111 us). A stack of layers in one moe_stack_decode call
- * pays the decode kernel's launch and first staging once, so there the decode path stays ahead. */
-#define MOE_DEFAULT_CROSSOVER 2
+ * single-layer decode call is the faster one at T = 1 (40 vs 46 us) and the batched one
+ * from T = 2 on (46 vs 49 us; T = 8: 77 vs 110 us). A stack of layers in one
+ * moe_stack_decode call pays the decode kernel's launch and first staging once, so there the decode
+ * path stays ahead. */
+#define MOE_DEFAULT_CROSSOVER 1
 
 /*
  * Router: logits, top-k selection and renormalised weights for T tokens (1 <= T <= 65536).

@@ -28,7 +28,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_ROUTE_LOGITS_IN = 1
 MOE_WS_DECODE, MOE_WS_BATCHED, MOE_WS_STACK, MOE_WS_FORWARD = 0, 1, 2, 3
 MOE_PATH_DECODE, MOE_PATH_BATCHED = 0, 1
-MOE_DEFAULT_CROSSOVER = 2
+MOE_DEFAULT_CROSSOVER = 1
 
 MOE_STACK_INDEPENDENT = 1
 MOE_STATIC_RESET = 2

@@ -119,23 +119,23 @@ def test_binding_refuses_host_tensors(L):
 
 
 def test_layer_path_boundary(L):
-    """moe_layer_path (host-only): decode for T up to the crossover (default 2, the measured
+    """moe_layer_path (host-only): decode for T up to the crossover (default 1, the measured
     boundary) when the decode call takes the shape, batched above it, above T = 8, or for shapes
     the decode kernel does not take."""
     path = lambda shape, T, c=0: binding.lib().moe_layer_path(ctypes.byref(shape), T, c)
     s = S()
-    assert moe.MOE_DEFAULT_CROSSOVER == 2
-    assert [path(s, T) for T in (1, 2)] == [moe.MOE_PATH_DECODE] * 2
-    assert [path(s, T) for T in (3, 8, 9, 16, 512, 65536)] == [moe.MOE_PATH_BATCHED] * 6
+    assert moe.MOE_DEFAULT_CROSSOVER == 1
+    assert path(s, 1) == moe.MOE_PATH_DECODE
+    assert [path(s, T) for T in (2, 3, 8, 9, 16, 512, 65536)] == [moe.MOE_PATH_BATCHED] * 7
     assert [path(s, T, 8) for T in (1, 7, 8)] == [moe.MOE_PATH_DECODE] * 3
     assert path(s, 3, 2) == moe.MOE_PATH_BATCHED and path(s, 2, 2) == moe.MOE_PATH_DECODE
     assert path(s, 9, 100) == moe.MOE_PATH_BATCHED  # the decode path takes at most 8 tokens
-    assert path(s, 2, -1) == moe.MOE_PATH_DECODE == path(s, moe.MOE_DEFAULT_CROSSOVER)
-    assert path(s, 3, -1) == moe.MOE_PATH_BATCHED
+    assert path(s, 1, -1) == moe.MOE_PATH_DECODE == path(s, moe.MOE_DEFAULT_CROSSOVER)
+    assert path(s, 2, -1) == moe.MOE_PATH_BATCHED
     assert path(S(hidden=4096), 1) == moe.MOE_PATH_BATCHED  # beyond the decode limits
     assert path(S(inter=64), 1) == moe.MOE_PATH_BATCHED
     assert path(s, 0) == -1 and path(s, 65537) == -1 and path(S(bits=3), 1) == -1
-    assert moe.moe_layer_path(synth_tiny_shape(), 2) == moe.MOE_PATH_DECODE
+    assert moe.moe_layer_path(synth_tiny_shape(), 1) == moe.MOE_PATH_DECODE
     assert moe.moe_layer_path(synth_tiny_shape(), 4, 8) == moe.MOE_PATH_DECODE
 
 
