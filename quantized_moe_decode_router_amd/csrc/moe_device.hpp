@@ -204,12 +204,75 @@ __device__ inline void wave_topk_n(const float *lt, int E, int K, int *idx, floa
     }
 }
 
+// The same selection with each lane's NJ keys sorted first (key descending; equal keys keep their
+// ascending expert order, the network exchanging only adjacent slots and only on a strictly larger
+// key), so that a lane competes with its head alone: a round is the wave maximum of the heads, the
+// lane holding it (lowest expert index among tied heads, by a wave minimum in that rare case)
+// records its head's expert and shifts its list up. Same result as wave_topk_n: the first key of
+// the global (value descending, index ascending) order is always some lane's head.
+template <int NJ>
+__device__ inline void wave_topk_sorted(const float *lt, int E, int K, int *idx, float *w) {
+    const int lane = threadIdx.x % kWave;
+    uint32_t key[NJ];
+    int ex[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int e = lane + kWave * j;
+        const float v = lt[min(e, E - 1)];
+        key[j] = e < E ? order_key(v) : 0u;
+        ex[j] = e;
+    }
+#pragma unroll
+    for (int a = 1; a < NJ; ++a) {
+#pragma unroll
+        for (int b = a; b > 0; --b) {
+            const bool sw = key[b] > key[b - 1];
+            const uint32_t k0 = key[b - 1], k1 = key[b];
+            const int e0 = ex[b - 1], e1 = ex[b];
+            key[b - 1] = sw ? k1 : k0;
+            key[b] = sw ? k0 : k1;
+            ex[b - 1] = sw ? e1 : e0;
+            ex[b] = sw ? e0 : e1;
+        }
+    }
+    int mine = 0;  // lane r < K ends with the rank-r winner
+    for (int r = 0; r < K; ++r) {
+        const uint32_t m = wave_max_vgpr(key[0]);
+        const unsigned long long holders = __ballot(key[0] == m);
+        int wl;  // the winning lane
+        if (__popcll(holders) == 1) {
+            wl = __builtin_amdgcn_readfirstlane(__ffsll(holders) - 1);
+        } else {
+            const uint32_t c = key[0] == m ? static_cast<uint32_t>(ex[0]) : 0xFFFFFFFFu;
+            wl = static_cast<int>(wave_min_vgpr(c)) & (kWave - 1);
+        }
+        const int win = __builtin_amdgcn_readlane(ex[0], wl);
+        if (lane == r) mine = win;
+        if (lane == wl) {
+#pragma unroll
+            for (int j = 0; j + 1 < NJ; ++j) {
+                key[j] = key[j + 1];
+                ex[j] = ex[j + 1];
+            }
+            key[NJ - 1] = 0u;
+        }
+    }
+    const float v = lt[lane < K ? mine : 0];
+    const float vmax = readlane_f32(v, 0);
+    const float pe = lane < K ? expf(v - vmax) : 0.0f;
+    const float z = wave_sum(pe);  // fixed reduction tree: the same bits every time
+    if (lane < K) {
+        idx[lane] = mine;
+        w[lane] = pe / z;
+    }
+}
+
 __device__ inline void wave_topk(const float *lt, int E, int K, int *idx, float *w) {
     const int nj = (E + kWave - 1) / kWave;
     if (nj <= 1) wave_topk_n<1>(lt, E, K, idx, w);
-    else if (nj <= 2) wave_topk_n<2>(lt, E, K, idx, w);
-    else if (nj <= 4) wave_topk_n<4>(lt, E, K, idx, w);
-    else if (nj <= 8) wave_topk_n<8>(lt, E, K, idx, w);
+    else if (nj <= 2) wave_topk_sorted<2>(lt, E, K, idx, w);
+    else if (nj <= 4) wave_topk_sorted<4>(lt, E, K, idx, w);
+    else if (nj <= 8) wave_topk_sorted<8>(lt, E, K, idx, w);
     else wave_topk_n<16>(lt, E, K, idx, w);
 }
 

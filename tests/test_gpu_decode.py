@@ -86,6 +86,33 @@ def test_route_adversarial_logits():
         assert list(idx[t].cpu().numpy()) == list(oracle.topk(lg[t].astype(np.float64), 4)), t
 
 
+@pytest.mark.parametrize("E,K", [(128, 8), (256, 8), (512, 10), (1024, 16)])
+def test_route_adversarial_logits_wide(E, K):
+    """Several keys per lane (E > 64): few distinct logit values, so a lane often holds equal
+    keys in several of its slots and several lanes tie at the maximum; +-0 rows; the selection is
+    the oracle's (logit desc, index asc) order exactly."""
+    import oracle
+    dev = need_gpu()
+    moe = _moe()
+    shape = synth.MoeShape(256, E, K, 128, 128, 4)
+    rng = np.random.default_rng(E + K)
+    rows = [np.zeros(E), np.where(np.arange(E) % 3 == 0, -0.0, 0.0)]
+    rows += [rng.integers(-2, 3, size=E).astype(float) for _ in range(20)]
+    rows += [np.where(rng.random(E) < 0.02, 1.0, 0.0) for _ in range(6)]
+    rows += [rng.standard_normal(E) for _ in range(4)]
+    lg = np.stack(rows).astype(np.float32)
+    T = lg.shape[0]
+    idx = torch.empty(T, K, dtype=torch.int32, device=dev)
+    w = torch.empty(T, K, dtype=torch.float32, device=dev)
+    moe.moe_route(shape, None, None, T, torch.from_numpy(lg).to(dev), idx, w, flags=moe.MOE_ROUTE_LOGITS_IN)
+    torch.cuda.synchronize()
+    for t in range(T):
+        want = oracle.topk(lg[t].astype(np.float64), K)
+        assert list(idx[t].cpu().numpy()) == list(want), t
+        np.testing.assert_allclose(w[t].cpu().numpy(), oracle.route_weights(lg[t].astype(np.float64), want),
+                                   rtol=0, atol=1e-6)
+
+
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("35b", 2), ("80b", 3)])
 def test_route_own_logits(name, T):
     import oracle
