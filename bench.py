@@ -397,8 +397,8 @@ def residency_sweep(stack, wl, warmup: int, steps: int, zipf_s):
 
 
 PHASE_NAMES = ["layer", "input", "router_rows", "logits_put", "x_limbs", "logits_got", "topk", "shared_gu",
-               "routed_issued", "routed_landed", "routed_done", "down_issued", "h_got", "down_done", "y_put",
-               "layer_end"]
+               "routed_issued", "routed_landed", "gu_units", "gu_barrier", "gu_put", "routed_done", "down_issued",
+               "h_polled", "h_got", "down_units", "down_done", "y_put", "layer_end"]
 REALTIME_HZ = 100e6  # s_memrealtime counts at 100 MHz
 
 

@@ -20,9 +20,11 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# MOE_AMD_PHASE_TIMER=1 loads the phase-timer build of the same sources (build.py, phase_timer)
-LIB_PATH = os.path.join(_HERE, "_lib", "libmoe_amd_phase.so" if os.environ.get("MOE_AMD_PHASE_TIMER") == "1"
-                        else "libmoe_amd.so")
+# MOE_AMD_PHASE_TIMER=1 loads the phase-timer build of the same sources (build.py, phase_timer);
+# MOE_AMD_LIB names another build of the library to load instead (an A/B comparison of kernel
+# variants built from other sources on one machine)
+LIB_PATH = os.environ.get("MOE_AMD_LIB") or os.path.join(
+    _HERE, "_lib", "libmoe_amd_phase.so" if os.environ.get("MOE_AMD_PHASE_TIMER") == "1" else "libmoe_amd.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_TIMEOUT = range(6)
 MOE_ROUTE_LOGITS_IN = 1

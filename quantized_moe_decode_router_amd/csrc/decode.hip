@@ -32,6 +32,8 @@
 namespace moe {
 
 constexpr int kWaves = kDecodeThreads / kWave;  // 8
+// Block-strided loops step by kDecodeThreads, the block size of every launch: blockDim.x would be a
+// scalar load from the kernel-argument segment inside the layer loop.
 constexpr int kMaxGather = 16;                  // exchange words one thread waits for at once
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -60,9 +62,14 @@ enum PhaseMark {
     kMarkSharedGu,       // shared gate|up done, routing published to the workgroup
     kMarkRoutedIssued,   // first chunk of routed gate|up rows issued
     kMarkRoutedLanded,   // first chunk landed
+    kMarkGuUnits,        // last chunk: wave 0's gate|up units done
+    kMarkGuBarrier,      // last chunk: every wave's units done
+    kMarkGuPut,          // last chunk: SwiGLU of the pairs and their h words stored
     kMarkRoutedDone,     // every routed gate|up pair computed, h published
     kMarkDownIssued,     // routed down rows (and next shared gate|up rows) issued
+    kMarkHPolled,        // every h word of token 0 current (before its limbs)
     kMarkHGot,           // every h of token 0 gathered, down rows landed
+    kMarkDownUnits,      // token T-1: wave 0's down tiles done
     kMarkDownDone,       // down projections of every token done
     kMarkYPut,           // y published
     kMarkLayerEnd        // next layer's shared down rows issued
@@ -95,7 +102,7 @@ __device__ __forceinline__ void fail(int *ctrl) {
 
 // Wait until words src[0..n) carry epoch ep and copy their values into LDS (word i to dst[i]).
 // Called by the whole workgroup; n may be any size (passes of kMaxGather words per thread). Thread
-// tid holds words tid + k * blockDim (slot k) of a pass in registers; a wave re-reads all its slots
+// tid holds words tid + k * kDecodeThreads (slot k) of a pass in registers; a wave re-reads all its slots
 // (every load of a poll in flight together) until one poll finds all of them current -- a current
 // word stays current, so re-reading words that were already there is harmless. The poll loop is
 // instantiated for the number of slots the wave has (rounded up to 1, 4, 12 or 16), so it stays short
@@ -346,19 +353,30 @@ __device__ __forceinline__ LayerPtrs layer_ptrs(const DecodeParams &p, int l) {
     return q;
 }
 
-// The kernel's parameter block, re-read from the kernel-argument segment (scalar loads) through a
-// pointer the compiler cannot prove invariant: without it every field would be hoisted out of
-// the layer loop and held in scalar registers for the whole kernel.
-__device__ __forceinline__ DecodeParams fresh_params() {
+// The kernel's parameter block: copied once into LDS at kernel start (params_to_lds) and re-read
+// from there at the top of every layer (fresh_params) through a pointer the compiler cannot prove
+// invariant -- without it every field would be hoisted out of the layer loop and held in scalar
+// registers for the whole kernel. Re-reading the kernel-argument segment itself inside the loop
+// (a scalar load per field group) measured 1 us per layer slower on the 40-layer stack.
+constexpr int kParamWords = sizeof(DecodeParams) / 4;
+static_assert(sizeof(DecodeParams) % 4 == 0, "parameter block is copied in 32-bit words");
+// the static LDS (this copy and the barrier votes) stays inside the 1 KiB the host keeps out of
+// the dynamic LDS plan
+static_assert(sizeof(DecodeParams) + 64 <= 1024, "static LDS");
+__device__ __forceinline__ void params_to_lds(uint32_t *dst) {
     typedef const __attribute__((address_space(4))) uint32_t *KP;
-    static_assert(sizeof(DecodeParams) % 4 == 0, "parameter block is copied in 32-bit words");
-    uint64_t a = reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr());
-    asm volatile("" : "+s"(a));
-    const KP src = reinterpret_cast<KP>(a);
+    const KP src = reinterpret_cast<KP>(reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr()));
+    for (int i = threadIdx.x; i < kParamWords; i += kDecodeThreads) dst[i] = src[i];
+}
+__device__ __forceinline__ DecodeParams fresh_params(const uint32_t *words) {
+    uint32_t a = lds_addr(words);
+    asm volatile("" : "+v"(a));
+    const __attribute__((address_space(3))) uint32_t *src =
+        reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>(static_cast<uintptr_t>(a));
     DecodeParams out;
     uint32_t *dst = reinterpret_cast<uint32_t *>(&out);
 #pragma unroll
-    for (size_t i = 0; i < sizeof(DecodeParams) / 4; ++i) dst[i] = src[i];
+    for (int i = 0; i < kParamWords; ++i) dst[i] = __builtin_amdgcn_readfirstlane(src[i]);
     return out;
 }
 
@@ -518,7 +536,7 @@ __device__ __forceinline__ void stage_routed_down(const DecodeParams &p, int l, 
 template <typename DstOf>
 __device__ __forceinline__ void wb_rows16(int n, int bytes, const char *lds, Swz swz, DstOf dst_of) {
     const int sh = __builtin_ctz(static_cast<unsigned>(bytes / 16)), total = n << sh;
-    for (int u = threadIdx.x; u < total; u += blockDim.x) {
+    for (int u = threadIdx.x; u < total; u += kDecodeThreads) {
         const int r = u >> sh, g = u & ((1 << sh) - 1);
         char *d = dst_of(r);
         if (!d) continue;
@@ -530,7 +548,7 @@ __device__ __forceinline__ void wb_rows16(int n, int bytes, const char *lds, Swz
 template <typename DstOf>
 __device__ __forceinline__ void wb_rows4(int n, int bytes, const char *lds, DstOf dst_of) {
     const int sh = __builtin_ctz(static_cast<unsigned>(bytes / 4)), total = n << sh;
-    for (int u = threadIdx.x; u < total; u += blockDim.x) {
+    for (int u = threadIdx.x; u < total; u += kDecodeThreads) {
         const int r = u >> sh, g = u & ((1 << sh) - 1);
         char *d = dst_of(r);
         if (!d) continue;
@@ -722,7 +740,7 @@ __device__ bool layer_input(const DecodeParams &p, int l, uint32_t ep, const Lds
     const int T = p.T, H = p.H, nsl = H / 32;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     if (l == 0 || !p.chained) {
-        for (int i = threadIdx.x; i < T * nsl * 16; i += blockDim.x) {
+        for (int i = threadIdx.x; i < T * nsl * 16; i += kDecodeThreads) {
             const int sh = __builtin_ctz(static_cast<unsigned>(nsl * 16));
             const int t = i >> sh, r = i & ((nsl * 16) - 1), sl = r >> 4, q = r & 15;
             const auto xr = G(p.x_in + (size_t)t * H + sl * 32);
@@ -743,7 +761,7 @@ __device__ bool layer_input(const DecodeParams &p, int l, uint32_t ep, const Lds
         for (int t = 0; t < T; ++t) {
             if (!ll_gather(ysrc + (size_t)t * H, H, ep, yb, p.ctrl, spin)) return false;
             float ss = 0.0f;
-            for (int h = threadIdx.x; h < H; h += blockDim.x) ss += yb[h] * yb[h];
+            for (int h = threadIdx.x; h < H; h += kDecodeThreads) ss += yb[h] * yb[h];
             ss = wave_sum(ss);
             if (lane == 0) s.red[wave] = ss;
             lds_barrier();
@@ -751,7 +769,7 @@ __device__ bool layer_input(const DecodeParams &p, int l, uint32_t ep, const Lds
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) ss += s.red[w];
             const float inv = 1.0f / sqrtf(ss / (float)H + p.eps);
-            for (int i = threadIdx.x; i < nsl * 16; i += blockDim.x) {
+            for (int i = threadIdx.x; i < nsl * 16; i += kDecodeThreads) {
                 const int sl = i >> 4, q = i & 15;
                 const float *yr = yb + sl * 32;
                 const uint32_t a = f32_to_bf16_rne(yr[pair_col_a<BITS>(q)] * inv);
@@ -763,7 +781,7 @@ __device__ bool layer_input(const DecodeParams &p, int l, uint32_t ep, const Lds
     }
     lds_barrier();
     if (p.x_all && blockIdx.x == 0)
-        for (int i = threadIdx.x; i < T * H; i += blockDim.x) {
+        for (int i = threadIdx.x; i < T * H; i += kDecodeThreads) {
             const int t = i >> __builtin_ctz(static_cast<unsigned>(H)), h = i & (H - 1), sl = h >> 5;
             int q, half;
             col_pair<BITS>(h & 31, q, half);
@@ -844,12 +862,14 @@ __device__ void router_logits(const DecodeParams &p, int l, const Lds &s, const 
 
 // ---- h of one token as limbs -------------------------------------------------------------------------
 template <int BITS>
-__device__ bool stage_hq(const DecodeParams &p, const Lds &s, const uint64_t *src, uint32_t ep, unsigned spin) {
+__device__ bool stage_hq(const DecodeParams &p, const Lds &s, const uint64_t *src, uint32_t ep, unsigned spin,
+                         int mark_l = -1) {
     const int n = p.K * p.I + p.Is;
     const float *hf = reinterpret_cast<const float *>(s.hp);
     if (!ll_gather(src, n, ep, reinterpret_cast<float *>(s.hp), p.ctrl, spin)) return false;
+    if (mark_l >= 0) phase_mark(p.phase, mark_l, kMarkHPolled);
     // 16 lanes per group; n / 4 and the block size are multiples of 16, so DPP rows stay whole
-    for (int it = threadIdx.x; it < n / 4; it += blockDim.x) {
+    for (int it = threadIdx.x; it < n / 4; it += kDecodeThreads) {
         const int gi = it >> 4, m = it & 15;
         float v[4];
 #pragma unroll
@@ -961,7 +981,7 @@ __device__ void down_all_mfma(const Lds &s, const Rows &rd, const Rows &sd, int 
 //   depend on busy).
 template <int BITS, bool ALL, typename TokOf, typename DstOf>
 __device__ void gate_up_mfma(const DecodeParams &p, const Lds &s, const Rows &R, int np, TokOf tok_of,
-                             DstOf dst_of, uint32_t ep, int busy = 0, int max_units = kWaves) {
+                             DstOf dst_of, uint32_t ep, int busy = 0, int max_units = kWaves, int mark_l = -1) {
     typedef CodeFmt<BITS> F;
     typedef typename F::lane_t qv_t;
     const int lane = threadIdx.x % kWave, i = lane % 16, kb = lane / 16;
@@ -1050,8 +1070,10 @@ __device__ void gate_up_mfma(const DecodeParams &p, const Lds &s, const Rows &R,
             }
         }
     }
+    if (mark_l >= 0) phase_mark(p.phase, mark_l, kMarkGuUnits);
     lds_barrier();
-    for (int e = threadIdx.x; e < np * nslot; e += blockDim.x) {
+    if (mark_l >= 0) phase_mark(p.phase, mark_l, kMarkGuBarrier);
+    for (int e = threadIdx.x; e < np * nslot; e += kDecodeThreads) {
         const int m = ALL ? div_by(e, p.tdiv) : e, t = ALL ? e - m * T : 0;
         float gsum = 0.0f, usum = 0.0f;
         for (int k = 0; k < ks; ++k) {
@@ -1060,6 +1082,7 @@ __device__ void gate_up_mfma(const DecodeParams &p, const Lds &s, const Rows &R,
         }
         ll_put(dst_of(m, t), silu(gsum) * usum, ep);
     }
+    if (mark_l >= 0) phase_mark(p.phase, mark_l, kMarkGuPut);
 }
 
 // ---- routing of every token (identical in every workgroup) ---------------------------------------
@@ -1068,7 +1091,7 @@ __device__ void gate_up_mfma(const DecodeParams &p, const Lds &s, const Rows &R,
 __device__ void route_tokens(const DecodeParams &p, const Lds &s) {
     const int T = p.T, E = p.E, K = p.K, wave = threadIdx.x / kWave;
     if (wave < T) wave_topk(s.lg + wave * (E + 1), E, K, s.sidx + wave * K, s.sw + wave * K);
-    for (int t = threadIdx.x; t < T; t += blockDim.x)
+    for (int t = threadIdx.x; t < T; t += kDecodeThreads)
         s.gam[t] = p.Is ? 1.0f / (1.0f + expf(-s.lg[t * (E + 1) + E])) : 0.0f;
 }
 
@@ -1078,6 +1101,9 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
     const int tid = threadIdx.x;
     const int nb = gridDim.x, b = blockIdx.x;
     if (p0.ctrl[0] != 0) return;  // sticky failure of an earlier call: do nothing
+    __shared__ __align__(16) uint32_t pwords[kParamWords];
+    params_to_lds(pwords);
+    lds_barrier();
     // bound on every wait: the workspace's control word 2 when the caller set one, else the default
     const unsigned spin = p0.ctrl[2] > 0 ? static_cast<unsigned>(p0.ctrl[2]) : p0.spin_limit;
     uint32_t ep = static_cast<uint32_t>(p0.ctrl[1]) + 1u;
@@ -1093,7 +1119,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
     }
     const int nlayers = p0.L;
     for (int l = 0; l < nlayers; ++l) {
-        const DecodeParams p = fresh_params();
+        const DecodeParams p = fresh_params(pwords);
         const Lds s = carve(p, smem);
         const int T = p.T, H = p.H, E = p.E, K = p.K, I = p.I, Is = p.Is, RB = p.rows_per_wg;
         const int KI = K * I, HW = KI + Is;  // h words per token
@@ -1142,11 +1168,11 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         if (b == 0) {
             const size_t base = (size_t)l * T;
             if (p.idx_all)
-                for (int i = tid; i < T * K; i += blockDim.x) G(p.idx_all)[base * K + i] = s.sidx[i];
+                for (int i = tid; i < T * K; i += kDecodeThreads) G(p.idx_all)[base * K + i] = s.sidx[i];
             if (p.w_all)
-                for (int i = tid; i < T * K; i += blockDim.x) G(p.w_all)[base * K + i] = s.sw[i];
+                for (int i = tid; i < T * K; i += kDecodeThreads) G(p.w_all)[base * K + i] = s.sw[i];
             if (p.logits_all)
-                for (int i = tid; i < T * E; i += blockDim.x)
+                for (int i = tid; i < T * E; i += kDecodeThreads)
                     G(p.logits_all)[base * E + i] = s.lg[(i / E) * (E + 1) + i % E];
         }
         // routed gate|up: this workgroup's pairs [q0, q1) of the flattened (token, slot, j) pairs,
@@ -1184,7 +1210,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
                         const int P = pb + i, t = div_by(P >> lgI, kdiv);
                         return ll_h + (size_t)t * HW + (P - t * KI);
                     },
-                    ep);
+                    ep, 0, kWaves, c0 + cp >= np ? l : -1);
                 if constexpr (XT) {
                     // the chunk's pairs belong to (token, slot)s tk_lo .. tk_hi; write through only
                     // if one of them is marked (wave-uniform test on LDS broadcasts)
@@ -1219,7 +1245,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
         }
         phase_mark(p.phase, l, kMarkDownIssued);
         for (int t = 0; t < T; ++t) {
-            if (!stage_hq<BITS>(p, s, ll_h + (size_t)t * HW, ep, spin)) { dma_wait(); return; }
+            if (!stage_hq<BITS>(p, s, ll_h + (size_t)t * HW, ep, spin, t == 0 ? l : -1)) { dma_wait(); return; }
             if (t == 0) dma_wait_but(later);
             else dma_wait();
             lds_barrier();
@@ -1227,6 +1253,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
             if (nr > 0) {
                 float *pt = s.part + (size_t)t * (K + 1) * RB;
                 down_all_mfma<BITS>(s, rd_rows(p, s), sd_rows(p, s), K, I, Is, nr, w.nrm, pt, RB);
+                if (t + 1 == T) phase_mark(p.phase, l, kMarkDownUnits);
                 if constexpr (XT) {
                     bool marked = false;
                     if (p.landing)
@@ -1247,7 +1274,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
             if (t + 1 < T) stage_routed_down<XT>(p, l, s, t + 1, r0, nr, w.nrm);
         }
         phase_mark(p.phase, l, kMarkDownDone);
-        for (int i = tid; i < T * nr; i += blockDim.x) {
+        for (int i = tid; i < T * nr; i += kDecodeThreads) {
             const int t = div_by(i, w.nrm), rl = i - t * nr;
             const float *pt = s.part + t * (K + 1) * RB;
             float acc = 0.0f;

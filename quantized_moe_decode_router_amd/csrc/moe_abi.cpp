@@ -72,7 +72,7 @@ size_t batched_ws_bytes(const moe_shape *s, int T) {
 
 // LDS available to the decode kernel's dynamic plan (the rest of the 160 KiB holds its small
 // static arrays).
-constexpr int kDecodeLdsBudget = 160 * 1024 - 256;
+constexpr int kDecodeLdsBudget = 160 * 1024 - 1024;
 
 int decode_chunk(const moe_shape *s, int T, int grid, bool xt = false) {
     return moe::decode_chunk_pairs(T, s->hidden, s->num_experts, s->top_k, s->inter, s->shared_inter, s->bits, grid,

@@ -94,7 +94,7 @@ struct DecodeWs {
     size_t phase, start, logits, h, y, total;
 };
 constexpr int kMaxGrid = 1024;
-constexpr int kPhaseMarks = 16;
+constexpr int kPhaseMarks = 21;
 __host__ __device__ inline DecodeWs decode_ws_layout(int L, int T, int H, int E, int K, int I, int Is) {
     DecodeWs w;
     size_t o = kCtrlBytes;
