@@ -39,7 +39,8 @@ namespace moe {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = kTileRows;   // pair rows per tile
+constexpr int kBM = 128;         // pair rows of an A stage in LDS
+static_assert(kTileRows <= kBM, "a tile's rows fit one A stage");
 constexpr int kGemmThreads = 256;
 constexpr int kLdsK = 72;        // fp16 per LDS tile row: 64 + 8 padding (16 bytes)
 
@@ -307,7 +308,7 @@ __device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *g
         const int G = (ng + kWave - 1) / kWave, g0 = tid * G, g1 = min(g0 + G, ng);
         int v[4] = {0, 0, 0, 0};
         for (int g = g0; g < g1; ++g) {
-            const int nt = (gcnt[g] + kBM - 1) / kBM;
+            const int nt = (gcnt[g] + kTileRows - 1) / kTileRows;
             v[0] += gcnt[g];
             v[1] += nt;
             v[2] += nt * ngu_of(g);
@@ -328,7 +329,7 @@ __device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *g
             goff[g] = e0;
             gtoff[g] = e1;
             e0 += c;
-            e1 += (c + kBM - 1) / kBM;
+            e1 += (c + kTileRows - 1) / kTileRows;
         }
         if (tid == kWave - 1) {
             goff[ng] = inc[0];
@@ -344,15 +345,15 @@ __device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *g
         if (g < ng) p.gcnt[g] = gcnt[g];
     }
     for (int g = tid; g < ng; g += kPlanThreads) {
-        const int nt = (gcnt[g] + kBM - 1) / kBM;
-        for (int i = 0; i < nt; ++i) p.tiles[gtoff[g] + i] = make_int2(g, i * kBM);
+        const int nt = (gcnt[g] + kTileRows - 1) / kTileRows;
+        for (int i = 0; i < nt; ++i) p.tiles[gtoff[g] + i] = make_int2(g, i * kTileRows);
     }
     // work items of the grouped GEMMs, longest first: a counting sort of the tiles by row count
     // (128 rows down to 1), so that the workgroups taken in list order fill the compute units
     // greedily and the heavy tiles do not form the tail. Within a bucket the order is arbitrary
     // (each item writes its own block of the output, so it does not change any result).
     if (p.wgu) {
-        for (int i = tid; i <= kBM; i += kPlanThreads) hgu[i] = hdn[i] = 0;
+        for (int i = tid; i <= kTileRows; i += kPlanThreads) hgu[i] = hdn[i] = 0;
         __syncthreads();
         const int ntile = gtoff[ng];
         // tile i: its group by binary search over the tile offsets
@@ -367,14 +368,21 @@ __device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *g
         };
         const int gfirst = tid < ntile ? tile_group(tid) : 0;  // this thread's first tile, used twice
         for (int i = tid; i < ntile; i += kPlanThreads) {
-            const int g = i == tid ? gfirst : tile_group(i), m0 = (i - gtoff[g]) * kBM, rows = min(kBM, gcnt[g] - m0);
+            const int g = i == tid ? gfirst : tile_group(i), m0 = (i - gtoff[g]) * kTileRows, rows = min(kTileRows, gcnt[g] - m0);
             atomicAdd(&hgu[rows], ngu_of(g));
             atomicAdd(&hdn[rows], ndn);
         }
         __syncthreads();
-        if (tid < kWave) {  // exclusive prefix from 128 rows down: lane l owns rows 128 - 2l, 127 - 2l
-            const int ra = kBM - 2 * tid, rb = kBM - 2 * tid - 1;
-            const int cu = hgu[ra] + (rb >= 1 ? hgu[rb] : 0), cd = hdn[ra] + (rb >= 1 ? hdn[rb] : 0);
+        if (tid < kWave) {  // exclusive prefix from kTileRows rows down: lane l owns rows kTileRows - RPL l - j
+            constexpr int RPL = kTileRows / kWave;  // row counts per lane, j = 0 .. RPL-1
+            static_assert(kTileRows % kWave == 0, "whole row counts per lane");
+            int cu = 0, cd = 0;
+#pragma unroll
+            for (int j = 0; j < RPL; ++j) {
+                const int r = kTileRows - RPL * tid - j;  // >= 1
+                cu += hgu[r];
+                cd += hdn[r];
+            }
             int iu = cu, id = cd;
 #pragma unroll
             for (int o = 1; o < kWave; o <<= 1) {
@@ -384,19 +392,21 @@ __device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *g
                     id += b;
                 }
             }
-            const int eu = iu - cu, ed = id - cd;
-            const int hua = hgu[ra], hda = hdn[ra];
-            hgu[ra] = eu;
-            hdn[ra] = ed;
-            if (rb >= 1) {
-                hgu[rb] = eu + hua;
-                hdn[rb] = ed + hda;
+            int eu = iu - cu, ed = id - cd;
+#pragma unroll
+            for (int j = 0; j < RPL; ++j) {
+                const int r = kTileRows - RPL * tid - j;
+                const int hu = hgu[r], hd = hdn[r];
+                hgu[r] = eu;
+                hdn[r] = ed;
+                eu += hu;
+                ed += hd;
             }
         }
         __syncthreads();
         for (int i = tid; i < ntile; i += kPlanThreads) {
-            const int g = i == tid ? gfirst : tile_group(i), mi = i - gtoff[g], m0 = mi * kBM,
-                      rows = min(kBM, gcnt[g] - m0);
+            const int g = i == tid ? gfirst : tile_group(i), mi = i - gtoff[g], m0 = mi * kTileRows,
+                      rows = min(kTileRows, gcnt[g] - m0);
             const int nu = ngu_of(g);
             const int bu = atomicAdd(&hgu[rows], nu), bd = atomicAdd(&hdn[rows], ndn);
             for (int c = 0; c < nu; ++c)
@@ -409,7 +419,7 @@ __device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *g
 
 __global__ void __launch_bounds__(kPlanThreads) bucket_plan(BatchedParams p) {
     __shared__ int gcnt[kMaxGroups], goff[kMaxGroups + 1], gtoff[kMaxGroups + 1];
-    __shared__ int hgu[kBM + 1], hdn[kBM + 1];
+    __shared__ int hgu[kTileRows + 1], hdn[kTileRows + 1];
     const int tid = threadIdx.x;
     const int T = p.T, K = p.K, E = p.E;
     const int nblk = (T + kWave - 1) / kWave;
@@ -470,7 +480,7 @@ __host__ __device__ inline size_t bucket_small_lds_bytes(int E) { return 12 * (s
 __global__ void __launch_bounds__(kPlanThreads) bucket_small(BatchedParams p) {
     extern __shared__ __align__(16) char smem[];
     __shared__ int gcnt[kMaxGroups], goff[kMaxGroups + 1], gtoff[kMaxGroups + 1];
-    __shared__ int hgu[kBM + 1], hdn[kBM + 1];
+    __shared__ int hgu[kTileRows + 1], hdn[kTileRows + 1];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int T = p.T, K = p.K, E = p.E;
     const int nblk = (T + kWave - 1) / kWave;  // <= kPlanWaves

@@ -1091,7 +1091,8 @@ __device__ void gate_up_mfma(const DecodeParams &p, const Lds &s, const Rows &R,
 __device__ void route_tokens(const DecodeParams &p, const Lds &s) {
     const int T = p.T, E = p.E, K = p.K, wave = threadIdx.x / kWave;
     if (wave < T) wave_topk(s.lg + wave * (E + 1), E, K, s.sidx + wave * K, s.sw + wave * K);
-    for (int t = threadIdx.x; t < T; t += kDecodeThreads)
+    // gamma by the last wave, so that wave 0 goes from its selection straight to the barrier
+    for (int t = threadIdx.x - (kWaves - 1) * kWave; t >= 0 && t < T; t += kDecodeThreads)
         s.gam[t] = p.Is ? 1.0f / (1.0f + expf(-s.lg[t * (E + 1) + E])) : 0.0f;
 }
 
