@@ -375,8 +375,13 @@ __device__ __forceinline__ DecodeParams fresh_params(const uint32_t *words) {
         reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>(static_cast<uintptr_t>(a));
     DecodeParams out;
     uint32_t *dst = reinterpret_cast<uint32_t *>(&out);
+    typedef const __attribute__((address_space(3))) u32x4_t *Q4;
+    const Q4 src4 = reinterpret_cast<Q4>(src);
+    u32x4_t q[(kParamWords + 3) / 4];
 #pragma unroll
-    for (int i = 0; i < kParamWords; ++i) dst[i] = __builtin_amdgcn_readfirstlane(src[i]);
+    for (int i = 0; i < (kParamWords + 3) / 4; ++i) q[i] = src4[i];  // every read in flight at once
+#pragma unroll
+    for (int i = 0; i < kParamWords; ++i) dst[i] = __builtin_amdgcn_readfirstlane(q[i / 4][i % 4]);
     return out;
 }
 
@@ -1102,7 +1107,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 1) decode_kernel(DecodeParams 
     const int tid = threadIdx.x;
     const int nb = gridDim.x, b = blockIdx.x;
     if (p0.ctrl[0] != 0) return;  // sticky failure of an earlier call: do nothing
-    __shared__ __align__(16) uint32_t pwords[kParamWords];
+    __shared__ __align__(16) uint32_t pwords[(kParamWords + 3) / 4 * 4];
     params_to_lds(pwords);
     lds_barrier();
     // bound on every wait: the workspace's control word 2 when the caller set one, else the default
