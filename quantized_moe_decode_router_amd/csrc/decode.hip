@@ -1095,7 +1095,13 @@ __device__ void gate_up_mfma(const DecodeParams &p, const Lds &s, const Rows &R,
 // Wave t < T selects token t's experts; the caller publishes the results with a barrier.
 __device__ void route_tokens(const DecodeParams &p, const Lds &s) {
     const int T = p.T, E = p.E, K = p.K, wave = threadIdx.x / kWave;
-    if (wave < T) wave_topk(s.lg + wave * (E + 1), E, K, s.sidx + wave * K, s.sw + wave * K);
+    if (wave < T) {
+        // the selection is one wave's dependent chain on the critical path; the wave sharing its
+        // SIMD runs the shared gate|up meanwhile, so the selecting wave issues first
+        __builtin_amdgcn_s_setprio(3);
+        wave_topk(s.lg + wave * (E + 1), E, K, s.sidx + wave * K, s.sw + wave * K);
+        __builtin_amdgcn_s_setprio(0);
+    }
     // gamma by the last wave, so that wave 0 goes from its selection straight to the barrier
     for (int t = threadIdx.x - (kWaves - 1) * kWave; t >= 0 && t < T; t += kDecodeThreads)
         s.gam[t] = p.Is ? 1.0f / (1.0f + expf(-s.lg[t * (E + 1) + E])) : 0.0f;
