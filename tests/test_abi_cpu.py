@@ -158,3 +158,20 @@ def test_forward_workspace_and_host_checks(L):
     assert f(ctypes.byref(s), ctypes.byref(lay), p, 4, 0, p, None, None, None, None, fwd, None) == moe.MOE_ERR_WORKSPACE
     assert f(ctypes.byref(S(bits=3)), ctypes.byref(lay), p, 4, 0, p, None, None, None, p, fwd, None) == \
         moe.MOE_ERR_UNSUPPORTED
+
+
+def test_library_override_selects_the_named_build(tmp_path):
+    """MOE_AMD_LIB names another build of the library (a same-machine A/B of kernel variants): the
+    binding loads that file, and MOE_AMD_PHASE_TIMER=1 alone selects the phase-timer build."""
+    import subprocess
+    import sys
+    code = "from quantized_moe_decode_router_amd import binding; print(binding.LIB_PATH)"
+    env = dict(os.environ)
+    env.pop("MOE_AMD_PHASE_TIMER", None)
+    env["MOE_AMD_LIB"] = str(tmp_path / "libvariant.so")
+    out = subprocess.run([sys.executable, "-c", code], env=env, cwd=ROOT, capture_output=True, text=True, check=True)
+    assert out.stdout.strip() == str(tmp_path / "libvariant.so")
+    env.pop("MOE_AMD_LIB")
+    env["MOE_AMD_PHASE_TIMER"] = "1"
+    out = subprocess.run([sys.executable, "-c", code], env=env, cwd=ROOT, capture_output=True, text=True, check=True)
+    assert out.stdout.strip().endswith(os.path.join("_lib", "libmoe_amd_phase.so"))
