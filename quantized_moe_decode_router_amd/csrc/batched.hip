@@ -298,6 +298,12 @@ __device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *g
     const int T = p.T, E = p.E;
     const int ng = E + (p.Is ? 1 : 0);  // groups: experts, then the shared expert
     if (tid == 0 && p.Is) gcnt[E] = T;
+    // every slot of both work lists starts as an empty item (rows = 0), the real items overwrite
+    // theirs below: a GEMM workgroup reads its slot directly, with no load of the item count first
+    if (p.wgu) {
+        for (int i = tid; i < p.max_wgu; i += kPlanThreads) p.wgu[i] = make_int4(0, 0, 0, 0);
+        for (int i = tid; i < p.max_wdn; i += kPlanThreads) p.wdn[i] = make_int4(0, 0, 0, 0);
+    }
     __syncthreads();
     // exclusive scans of the group sizes, their tile counts and their gate|up and down work items
     const int ndn = p.H / kDnCols;
@@ -643,8 +649,8 @@ __device__ void act16_to_pairs8(const uint4 r, int sh, half2_t *out) {
 //
 // The k-loop is compiled once per count MT of 16-row subtiles that hold rows of the tile, so that
 // a k-step has no branches inside and the MFMAs of one k-step interleave with the dequantisation of
-// the next. Block b runs work item b of a list ordered longest first (see plan_groups).
-__device__ __forceinline__ int list_item(int n) { return (int)blockIdx.x < n ? (int)blockIdx.x : -1; }
+// the next. Block b runs slot b of a work list ordered longest first (see plan_groups); the
+// slots past the list's items hold rows = 0, and their blocks return at once.
 __device__ __forceinline__ int chunk_pos(int row, int c) { return c ^ (row & 7); }
 
 constexpr int kGW = kGemmWavesG;           // waves per grouped-GEMM workgroup
@@ -1058,10 +1064,9 @@ __device__ __forceinline__ void gu_body(const BatchedParams &p, char *lds, int g
 template <int BITS>
 __global__ void __launch_bounds__(kGT, 1) gu_gemm(BatchedParams p) {
     extern __shared__ __align__(16) char smem[];
-    const int w = list_item(gp(p.ntiles)[1]);
-    if (w < 0) return;
-    const auto wq = gp(reinterpret_cast<const int *>(p.wgu + w));
+    const auto wq = gp(reinterpret_cast<const int *>(p.wgu + blockIdx.x));
     const int g = wq[0], P0 = wq[1], M = wq[2] & 0xFFFF, j0 = wq[2] >> 16, tile = wq[3];
+    if (M == 0) return;  // a slot past the list's items
     switch ((M + 15) / 16) {
         case 1: gu_body<BITS, 1>(p, smem, g, P0, M, j0, tile); break;
         case 2: gu_body<BITS, 2>(p, smem, g, P0, M, j0, tile); break;
@@ -1189,10 +1194,9 @@ __device__ __forceinline__ void dn_body(const BatchedParams &p, char *lds, int g
 template <int BITS>
 __global__ void __launch_bounds__(kGT, 1) dn_gemm(BatchedParams p) {
     extern __shared__ __align__(16) char smem[];
-    const int w = list_item(gp(p.ntiles)[2]);
-    if (w < 0) return;
-    const auto wq = gp(reinterpret_cast<const int *>(p.wdn + w));
+    const auto wq = gp(reinterpret_cast<const int *>(p.wdn + blockIdx.x));
     const int g = wq[0], P0 = wq[1], M = wq[2] & 0xFFFF, n0 = wq[2] >> 16, tile = wq[3];
+    if (M == 0) return;  // a slot past the list's items
     switch ((M + 15) / 16) {
         case 1: dn_body<BITS, 1>(p, smem, g, P0, M, n0, tile); break;
         case 2: dn_body<BITS, 2>(p, smem, g, P0, M, n0, tile); break;
@@ -1287,7 +1291,7 @@ hipError_t launch_batched(const BatchedParams &p, const BatchedWs &lay, hipStrea
     hipError_t err = launch_router_topk(p, stream);
     if (err != hipSuccess) return err;
     if ((err = launch_bucket(p, stream)) != hipSuccess) return err;
-    // grids cover the work lists' upper bounds (blocks past the list's length return at once)
+    // grids cover the work lists' capacities (blocks past the list's items find rows = 0 and return)
     const unsigned ggu = (unsigned)lay.max_wgu, gdn = (unsigned)lay.max_wdn;
     const int gu_lds4 = GCfg<4, false>::lds_bytes(p.H / 64), dn_lds4 = GCfg<4, true>::lds_bytes(p.Imax / 64);
     const int gu_lds8 = GCfg<8, false>::lds_bytes(p.H / 64), dn_lds8 = GCfg<8, true>::lds_bytes(p.Imax / 64);

@@ -407,6 +407,8 @@ moe_status batched_common(const moe_shape *s, const moe_layer *L, const uint16_t
     p.lpart = reinterpret_cast<float *>(w + lay.lpart);
     p.wgu = reinterpret_cast<int4 *>(w + lay.wgu);
     p.wdn = reinterpret_cast<int4 *>(w + lay.wdn);
+    p.max_wgu = lay.max_wgu;
+    p.max_wdn = lay.max_wdn;
     p.x16 = reinterpret_cast<_Float16 *>(w + lay.x16);
     p.xe = reinterpret_cast<int *>(w + lay.xe);
     p.hexp = reinterpret_cast<int *>(w + lay.hexp);

@@ -212,6 +212,7 @@ struct BatchedParams {
     int2 *tiles;        // [max_tiles] (group, first row in group)
     int4 *wgu, *wdn;    // work items of the grouped GEMMs: {group, first row P0, rows | first column << 16,
                         // tile index}, ordered by group, then column block, then row tile
+    int max_wgu, max_wdn;  // the lists' capacities (the GEMM grids); slots past the items hold rows = 0
     _Float16 *x16;      // [T][H] x as fp16 in pair order, scaled by 2^-xe[t]
     int *xe;            // [T] per-token exponent of that scaling
     int *hexp;          // [max_tiles][Imax/64] exponent e of h's fp16 halves in (tile, 64-column group):
