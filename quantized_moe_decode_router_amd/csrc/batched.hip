@@ -40,6 +40,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 128;         // pair rows of an A stage in LDS
+constexpr int kXcds = 8;         // XCDs of the device: workgroup b of a launch runs on XCD b mod 8
 static_assert(kTileRows <= kBM, "a tile's rows fit one A stage");
 constexpr int kGemmThreads = 256;
 constexpr int kLdsK = 72;        // fp16 per LDS tile row: 64 + 8 padding (16 bytes)
@@ -293,7 +294,8 @@ __global__ void __launch_bounds__(kCountWaves * kWave) bucket_count(BatchedParam
 // the scans of the group sizes, tile counts and work items (goff, gtoff, the totals in p.ntiles),
 // p.gcnt / p.goff, the tile list and, when p.wgu is set, both GEMMs' work lists, longest first.
 // Called by the whole workgroup of kPlanThreads; the arrays live in the caller's LDS.
-__device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *gtoff, int *hgu, int *hdn) {
+__device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *gtoff, int *hgu, int *hdn, int *hds,
+                            int *hdc) {
     const int tid = threadIdx.x;
     const int T = p.T, E = p.E;
     const int ng = E + (p.Is ? 1 : 0);  // groups: experts, then the shared expert
@@ -405,6 +407,8 @@ __device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *g
                 const int hu = hgu[r], hd = hdn[r];
                 hgu[r] = eu;
                 hdn[r] = ed;
+                hds[r] = ed;  // the down bucket's first slot and its item count
+                hdc[r] = hd;
                 eu += hu;
                 ed += hd;
             }
@@ -417,15 +421,22 @@ __device__ void plan_groups(const BatchedParams &p, int *gcnt, int *goff, int *g
             const int bu = atomicAdd(&hgu[rows], nu), bd = atomicAdd(&hdn[rows], ndn);
             for (int c = 0; c < nu; ++c)
                 p.wgu[bu + c] = make_int4(g, goff[g] + m0, rows | (c * kGuCols) << 16, i);
-            for (int c = 0; c < ndn; ++c)
-                p.wdn[bd + c] = make_int4(g, goff[g] + m0, rows | (c * kDnCols) << 16, i);
+            // The down items of one tile all read the tile's h rows: within each whole group of
+            // kXcds tiles of a bucket, tile q's items take the slots of one residue mod kXcds
+            // (workgroup b runs on XCD b mod kXcds), so they run on one XCD and share its L2's copy
+            // of those rows; the bucket's last, partial group keeps consecutive slots.
+            const int B = hds[rows], nb = hdc[rows] / ndn, q = (bd - B) / ndn, full = nb / kXcds * kXcds;
+            for (int c = 0; c < ndn; ++c) {
+                const int slot = q < full ? B + (q / kXcds) * kXcds * ndn + c * kXcds + q % kXcds : bd + c;
+                p.wdn[slot] = make_int4(g, goff[g] + m0, rows | (c * kDnCols) << 16, i);
+            }
         }
     }
 }
 
 __global__ void __launch_bounds__(kPlanThreads) bucket_plan(BatchedParams p) {
     __shared__ int gcnt[kMaxGroups], goff[kMaxGroups + 1], gtoff[kMaxGroups + 1];
-    __shared__ int hgu[kTileRows + 1], hdn[kTileRows + 1];
+    __shared__ int hgu[kTileRows + 1], hdn[kTileRows + 1], hds[kTileRows + 1], hdc[kTileRows + 1];
     const int tid = threadIdx.x;
     const int T = p.T, K = p.K, E = p.E;
     const int nblk = (T + kWave - 1) / kWave;
@@ -446,7 +457,7 @@ __global__ void __launch_bounds__(kPlanThreads) bucket_plan(BatchedParams p) {
         }
         gcnt[e] = run;
     }
-    plan_groups(p, gcnt, goff, gtoff, hgu, hdn);
+    plan_groups(p, gcnt, goff, gtoff, hgu, hdn, hds, hdc);
     // scatter: four pairs per thread in flight at once
     const int TK = T * K;
     for (int q0 = tid; q0 < TK; q0 += 4 * kPlanThreads) {
@@ -486,7 +497,7 @@ __host__ __device__ inline size_t bucket_small_lds_bytes(int E) { return 12 * (s
 __global__ void __launch_bounds__(kPlanThreads) bucket_small(BatchedParams p) {
     extern __shared__ __align__(16) char smem[];
     __shared__ int gcnt[kMaxGroups], goff[kMaxGroups + 1], gtoff[kMaxGroups + 1];
-    __shared__ int hgu[kTileRows + 1], hdn[kTileRows + 1];
+    __shared__ int hgu[kTileRows + 1], hdn[kTileRows + 1], hds[kTileRows + 1], hdc[kTileRows + 1];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int T = p.T, K = p.K, E = p.E;
     const int nblk = (T + kWave - 1) / kWave;  // <= kPlanWaves
@@ -524,7 +535,7 @@ __global__ void __launch_bounds__(kPlanThreads) bucket_small(BatchedParams p) {
         }
         gcnt[e] = run;
     }
-    plan_groups(p, gcnt, goff, gtoff, hgu, hdn);
+    plan_groups(p, gcnt, goff, gtoff, hgu, hdn, hds, hdc);
     // scatter by the lane that ranked the pair: expert offset + block prefix + rank
 #pragma unroll
     for (int k = 0; k < 16; ++k)
