@@ -318,3 +318,59 @@ def test_full_stack_chained(wl):
     assert torch.equal(out["y"], out["y_all"][-1])
     print(f"{wl.name}: {strict}/{wl.n_layers} chained layers on bitwise-identical inputs")
     assert strict >= 1
+
+
+# ------------------------------------------------------------------------------ the largest shapes
+
+# E = 1024 experts and top-16 are the library's limits. The decode kernel holds a token's h (K I + Is
+# words), the router rows and the routed rows of its share in LDS, so not every such shape fits it:
+# the candidates run from the largest down. A shape it cannot hold must be refused with
+# MOE_ERR_UNSUPPORTED (before any launch) and routed to the batched path, which computes it; the
+# largest shape it does take must match the oracle.
+MAX_CANDIDATES = [
+    (synth.MoeShape(2048, 1024, 16, 512, 512, 4), 8),
+    (synth.MoeShape(2048, 1024, 16, 512, 512, 4), 4),
+    (synth.MoeShape(2048, 1024, 16, 512, 512, 4), 1),
+    (synth.MoeShape(2048, 1024, 16, 256, 256, 4), 1),
+    (synth.MoeShape(1024, 1024, 16, 256, 256, 4), 1),
+]
+
+
+def test_decode_at_the_largest_shapes():
+    dev = need_gpu()
+    moe = _moe()
+    stacks = {}
+    refused, taken = [], None
+    for shape, T in MAX_CANDIDATES:
+        key = str(shape)
+        if key not in stacks:
+            stacks[key] = synth.make_stack(shape, 1, 4242, dev, zipf_s=None)
+        st = stacks[key]
+        x = synth.make_x(shape, T, 77, device=dev)
+        if moe.moe_layer_path(shape, T, 8) == moe.MOE_PATH_DECODE:
+            taken = (shape, T, st, x)
+            break
+        y = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
+        ws = moe.workspace(shape, T, moe.MOE_WS_DECODE, dev)
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_layer_decode(shape, st.layer(0), x, T, y, workspace=ws)
+        assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+        refused.append((shape, T, st, x))
+    assert taken is not None, "the decode kernel takes none of the candidate shapes"
+    shape, T, st, x = taken
+    Lh = host_layer(st, 0)
+    ref = oracle_layer(st, 0, bf16_bits(x))
+    y, idx, w, lg = run_decode(shape, st.layer(0), x, T, dev)
+    differ = check_routing_against_oracle(idx, w, lg, ref, bf16_bits(x), Lh, shape.top_k)
+    keep = [t for t in range(T) if t not in differ]
+    assert keep, "every token's routing is legitimately ambiguous; pick another seed"
+    err = check_y(y[keep], ref["y"][keep])
+    print(f"decode at {shape} T={T}: max|err|/RMS = {err:.2e}; refused: {[(str(s), t) for s, t, _, _ in refused]}")
+    if refused:  # the largest refused shape, through the routing entry point (batched path)
+        shape, T, st, x = refused[0]
+        y = torch.empty(T, shape.hidden, dtype=torch.float32, device=dev)
+        ws = moe.workspace(shape, T, moe.MOE_WS_FORWARD, dev)
+        moe.moe_layer_forward(shape, st.layer(0), x, T, y, crossover=8, workspace=ws)
+        ref = oracle_layer(st, 0, bf16_bits(x))
+        err = check_y(y.cpu().numpy(), ref["y"])
+        print(f"forward (batched) at {shape} T={T}: max|err|/RMS = {err:.2e}")
