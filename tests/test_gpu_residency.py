@@ -117,6 +117,7 @@ TABLE_CASES = [
     ("q35b_T1_mixed", synth.QWEN35B_4BIT.shape, 3, 1, "mixed"),
     ("q35b_T3_host", synth.QWEN35B_4BIT.shape, 2, 3, "host"),
     ("q35b_8bit_T2_mixed", synth.QWEN35B_8BIT.shape, 2, 2, "mixed"),
+    ("q35b_8bit_T1_host", synth.QWEN35B_8BIT.shape, 2, 1, "host"),
     ("q80b_T2_mixed", synth.QWEN80B_4BIT.shape, 2, 2, "mixed"),
     # an odd expert count stages the table row in 4-byte units
     ("odd_e15_T2_mixed", synth.MoeShape(256, 15, 3, 128, 128, 4), 3, 2, "mixed"),
